@@ -1,0 +1,324 @@
+"""The oracle: a plain, slow, CPU implementation of the Mamba-2 SSD forward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this package.  The product
+library (``libssd``) and its Python binding never import, link or call it, and
+the two share no code: the only module both sides use is the seeded input
+generator, which holds none of the method's arithmetic.
+
+Contents
+--------
+* ``ssd_fwd``            -- the fp64 sequential recurrence (``ssd_ref.c``),
+                            Mamba-3-Lite "SSD Reference", section "Math: the
+                            recurrence both functions implement", plus dt bias,
+                            groups, D skip, SiLU gate, initial/final states and
+                            packed sequences.
+* ``varlen_chunk_meta``  -- the sequence-aligned chunk table, pure Python ints.
+* ``chunk_cumsum``       -- within-chunk cumulative log-decay, SSD Reference
+                            section "Chunking and the discretized log-decay".
+* ``bmm_chunk``          -- C.B^T per chunk and group, SSD Reference
+                            "Algorithm and tensor-shape contract", step 4.
+* ``chunk_states``       -- each chunk's end state from a zero start, SSD
+                            Reference "Algorithm and tensor-shape contract",
+                            step 6 (computed by running the recurrence on the
+                            chunk alone).
+* ``carry_in_states``    -- the state entering every chunk, SSD Reference
+                            "Inter-chunk propagation" (computed as the
+                            recurrence's state at the chunk boundary).
+
+All floating-point work is fp64.  Every function here is pinned by the
+``-m "not gpu"`` tests against closed forms, special cases and brute force.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+from dataclasses import dataclass
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ssd_ref.c")
+_LIB = os.path.join(_HERE, "libssd_ref.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``ssd_ref.c`` into ``libssd_ref.so`` with gcc (fp64, OpenMP).
+
+    ``-ffp-contract=off`` keeps every multiply and add separately rounded, as
+    written; the portable ``-march=x86-64-v2`` lets the library built here run
+    on any x86-64 host it is copied to.
+    """
+    if not force and os.path.exists(_LIB):
+        return _LIB
+    tmp = _LIB + ".tmp"
+    cmd = ["gcc", "-O2", "-march=x86-64-v2", "-ffp-contract=off", "-fopenmp",
+           "-fPIC", "-shared", "-std=c99", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.POINTER
+        lib.ssd_ref_fwd.restype = ctypes.c_int
+        lib.ssd_ref_fwd.argtypes = [
+            ctypes.c_int64, ctypes.c_int, P(ctypes.c_int64),
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int,
+        ]
+        lib.ssd_ref_num_chunks.restype = ctypes.c_int64
+        lib.ssd_ref_num_chunks.argtypes = [ctypes.c_int, P(ctypes.c_int64), ctypes.c_int]
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _packed(a, lead):
+    """(b, T, ...) -> (b*T, ...) when the batch axis is present."""
+    if a is None:
+        return None
+    return a.reshape((-1,) + a.shape[lead:])
+
+
+@dataclass
+class FwdResult:
+    y: np.ndarray                 # same leading layout as x
+    final_states: np.ndarray      # (nseq or b, H, P, N)
+    chunk_end_states: np.ndarray | None  # (nchunks, H, P, N) or None
+
+
+def ssd_fwd(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=None,
+            cu_seqlens=None, dt_softplus=True, dt_limit=None, chunk_size=0,
+            threads=None) -> FwdResult:
+    """Run the fp64 recurrence.
+
+    Batch mode: x (b, T, H, P), B and C (b, T, G, N), dt (b, T, H), z like x,
+    initial_states (b, H, P, N).  Packed mode (``cu_seqlens`` given): the same
+    tensors without the batch axis, i.e. x (T, H, P), with sequence i owning
+    tokens [cu[i], cu[i+1]); initial_states (nseq, H, P, N).
+
+    ``dt_limit=(lo, hi)`` clamps the step size after softplus.  With
+    ``chunk_size > 0`` the state after the last token of every sequence-aligned
+    chunk is returned as ``chunk_end_states`` (logical chunk order:
+    sequence-major, in token order inside a sequence).
+    """
+    x = _f64(x)
+    if cu_seqlens is None:
+        b, T = x.shape[0], x.shape[1]
+        cu = np.arange(b + 1, dtype=np.int64) * T
+        lead = 2
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        lead = 1
+    H, P = x.shape[lead], x.shape[lead + 1]
+    Bf, Cf = _f64(B), _f64(C)
+    G, N = Bf.shape[lead], Bf.shape[lead + 1]
+    xs, Bs, Cs = _packed(x, lead), _packed(Bf, lead), _packed(Cf, lead)
+    dts = _packed(_f64(dt), lead)
+    zs = _packed(_f64(z), lead) if z is not None else None
+    ntok = xs.shape[0]
+    nseq = len(cu) - 1
+    A_ = _f64(np.broadcast_to(np.asarray(A, dtype=np.float64), (H,)))
+    bias = _f64(dt_bias)
+    D_ = _f64(D)
+    h0 = _f64(initial_states)
+    y = np.empty((ntok, H, P), dtype=np.float64)
+    hfin = np.empty((nseq, H, P, N), dtype=np.float64)
+    lib = _load()
+    cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    hch = None
+    if chunk_size > 0:
+        nck = lib.ssd_ref_num_chunks(nseq, cu_p, int(chunk_size))
+        hch = np.empty((nck, H, P, N), dtype=np.float64)
+    clamp = 0 if dt_limit is None else 1
+    lo, hi = (0.0, math.inf) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
+    rc = lib.ssd_ref_fwd(ntok, nseq, cu_p, H, P, N, G, _ptr(xs), _ptr(Bs), _ptr(Cs),
+                         _ptr(dts), _ptr(A_), _ptr(bias), _ptr(D_), _ptr(zs), _ptr(h0),
+                         1 if dt_softplus else 0, clamp, lo, hi,
+                         int(chunk_size), _ptr(y), _ptr(hfin), _ptr(hch),
+                         int(threads or 0))
+    if rc != 0:
+        raise ValueError(f"ssd_ref_fwd failed with code {rc}")
+    return FwdResult(y.reshape(x.shape), hfin, hch)
+
+
+# --------------------------------------------------------------------------
+# Sequence-aligned chunk table (pure Python integers).
+# --------------------------------------------------------------------------
+
+@dataclass
+class ChunkMeta:
+    nchunks: int                 # number of logical chunks K
+    seq: list                    # seq[j]   sequence that chunk j belongs to
+    start: list                  # start[j] first token of chunk j
+    length: list                 # length[j] tokens in chunk j (1..C)
+    first_chunk: list            # first_chunk[i] first chunk of sequence i; [nseq] = K
+
+
+def varlen_chunk_meta(cu_seqlens, chunk_size) -> ChunkMeta:
+    """Split every sequence of a packed batch into chunks of ``chunk_size``.
+
+    Sequence i (tokens [cu[i], cu[i+1])) of length L_i is cut at multiples of
+    the chunk size counted from its own first token, giving ceil(L_i / C)
+    chunks; an empty sequence gets none.  Chunks are numbered sequence by
+    sequence.  This is the chunk grid of the SSD Reference ("Padding rule",
+    "Chunking") applied to each sequence separately, so that no chunk straddles
+    a sequence boundary and the state can restart there (vLLM PR 27299,
+    continuous batching).
+    """
+    cu = [int(v) for v in cu_seqlens]
+    C = int(chunk_size)
+    seq, start, length, first = [], [], [], []
+    for i in range(len(cu) - 1):
+        first.append(len(seq))
+        L = cu[i + 1] - cu[i]
+        k = 0
+        while k * C < L:
+            seq.append(i)
+            start.append(cu[i] + k * C)
+            length.append(min(C, L - k * C))
+            k += 1
+    first.append(len(seq))
+    return ChunkMeta(len(seq), seq, start, length, first)
+
+
+def batch_chunk_meta(batch, seqlen, chunk_size) -> ChunkMeta:
+    """The chunk table of ``batch`` equal sequences of ``seqlen`` tokens."""
+    return varlen_chunk_meta([i * seqlen for i in range(batch + 1)], chunk_size)
+
+
+# --------------------------------------------------------------------------
+# Stage intermediates.  Tokens are addressed on the packed axis (b*T for
+# batch mode), and chunks by their logical id j from the chunk table.
+# --------------------------------------------------------------------------
+
+def softplus(u):
+    """log(1 + e^u) in the overflow-free form max(u,0) + log1p(exp(-|u|))."""
+    u = np.asarray(u, dtype=np.float64)
+    return np.maximum(u, 0.0) + np.log1p(np.exp(-np.abs(u)))
+
+
+def step_size(dt, dt_bias=None, dt_softplus=True, dt_limit=None):
+    """delta = softplus(dt + dt_bias), optionally clamped (per token, per head)."""
+    u = np.asarray(dt, dtype=np.float64)
+    if dt_bias is not None:
+        u = u + np.asarray(dt_bias, dtype=np.float64)
+    d = softplus(u) if dt_softplus else u
+    if dt_limit is not None:
+        d = np.minimum(np.maximum(d, dt_limit[0]), dt_limit[1])
+    return d
+
+
+def chunk_cumsum(dt, A, meta: ChunkMeta, chunk_size, dt_bias=None, dt_softplus=True,
+                 dt_limit=None):
+    """Within-chunk inclusive cumulative sum of the log-decay a = delta * A.
+
+    dt is (ntok, H) on the packed token axis.  Returns (K, H, C) fp64.  A chunk
+    shorter than C is treated as if the missing positions had a = 0, so those
+    positions repeat the value at the chunk's last token.
+    """
+    dt = np.asarray(dt, dtype=np.float64)
+    H = dt.shape[1]
+    C = int(chunk_size)
+    a = step_size(dt, dt_bias, dt_softplus, dt_limit) * np.asarray(A, dtype=np.float64)[None, :]
+    out = np.zeros((meta.nchunks, H, C), dtype=np.float64)
+    for j in range(meta.nchunks):
+        s, L = meta.start[j], meta.length[j]
+        seg = np.zeros((C, H), dtype=np.float64)
+        seg[:L] = a[s:s + L]
+        out[j] = np.cumsum(seg, axis=0).T
+    return out
+
+
+def bmm_chunk(Cm, Bm, meta: ChunkMeta, chunk_size):
+    """CB[j, g, l, s] = sum_n C[start_j + l, g, n] * B[start_j + s, g, n].
+
+    Cm, Bm are (ntok, G, N).  Returns (K, G, C, C) fp64; rows or columns past a
+    short chunk's end are zero.
+    """
+    Cm = np.asarray(Cm, dtype=np.float64)
+    Bm = np.asarray(Bm, dtype=np.float64)
+    G = Cm.shape[1]
+    Cs = int(chunk_size)
+    out = np.zeros((meta.nchunks, G, Cs, Cs), dtype=np.float64)
+    for j in range(meta.nchunks):
+        s, L = meta.start[j], meta.length[j]
+        for g in range(G):
+            out[j, g, :L, :L] = np.matmul(Cm[s:s + L, g, :], Bm[s:s + L, g, :].T)
+    return out
+
+
+def _chunk_cut(meta: ChunkMeta):
+    """cu_seqlens whose sequences are exactly the chunks of ``meta``."""
+    cuts = [meta.start[j] for j in range(meta.nchunks)]
+    if meta.nchunks:
+        cuts.append(meta.start[-1] + meta.length[-1])
+    else:
+        cuts.append(0)
+    return np.asarray(cuts, dtype=np.int64)
+
+
+def chunk_states(x, Bm, dt, A, meta: ChunkMeta, dt_bias=None, dt_softplus=True,
+                 dt_limit=None, threads=None):
+    """Each chunk's end state with a zero state entering the chunk: (K, H, P, N).
+
+    Computed by running the recurrence on every chunk as its own sequence; x is
+    (ntok, H, P), Bm (ntok, G, N), dt (ntok, H), all on the packed token axis.
+    Tokens that belong to no chunk (between packed sequences there are none)
+    are never read.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    H, P = x.shape[1], x.shape[2]
+    N = np.asarray(Bm).shape[2]
+    if meta.nchunks == 0:
+        return np.zeros((0, H, P, N))
+    cu = _chunk_cut(meta)
+    lo, hi = int(cu[0]), int(cu[-1])
+    Cz = np.zeros_like(np.asarray(Bm, dtype=np.float64)[lo:hi])
+    r = ssd_fwd(x[lo:hi], np.asarray(Bm)[lo:hi], Cz, np.asarray(dt)[lo:hi], A,
+                dt_bias=dt_bias, cu_seqlens=cu - lo, dt_softplus=dt_softplus,
+                dt_limit=dt_limit, threads=threads)
+    return r.final_states
+
+
+def carry_in_states(chunk_end_states, meta: ChunkMeta, initial_states=None):
+    """State entering every chunk: (K, H, P, N).
+
+    The first chunk of sequence i starts from initial_states[i] (or zero); every
+    other chunk starts from the state after the last token of the chunk before
+    it, i.e. ``chunk_end_states[j - 1]`` from a full recurrence run.
+    """
+    K = meta.nchunks
+    shp = chunk_end_states.shape[1:]
+    out = np.zeros((K,) + shp, dtype=np.float64)
+    for j in range(K):
+        i = meta.seq[j]
+        if j == meta.first_chunk[i]:
+            if initial_states is not None:
+                out[j] = np.asarray(initial_states, dtype=np.float64)[i]
+        else:
+            out[j] = chunk_end_states[j - 1]
+    return out

@@ -1,0 +1,60 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one slip in a private copy of the oracle's C source (never in
+the tree), rebuilds it in a temporary directory and runs the pin suite against
+that copy in a subprocess; the suite has to fail.  This shows the pins are
+strong enough that a wrong oracle would not pass them.
+"""
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+MUTANTS = {
+    "decay_after_add": ("row[n] = decay * row[n] + xp * bt[n];",
+                        "row[n] = decay * (row[n] + xp * bt[n]);"),
+    "wrong_group_of_head": ("const int g = h / hpg;", "const int g = h % G;"),
+    "dropped_skip": ("double yp = acc + (D ? D[h] * xp : 0.0);", "double yp = acc;"),
+    "readout_before_update": (
+        "for (int n = 0; n < N; ++n) row[n] = decay * row[n] + xp * bt[n];\n"
+        "        double acc = 0.0;\n"
+        "        for (int n = 0; n < N; ++n) acc += row[n] * ct[n];",
+        "double acc = 0.0;\n"
+        "        for (int n = 0; n < N; ++n) acc += row[n] * ct[n];\n"
+        "        for (int n = 0; n < N; ++n) row[n] = decay * row[n] + xp * bt[n];"),
+    "sign_of_A": ("exp(delta * A[h])", "exp(-delta * A[h])"),
+    "sign_of_bias": ("+ (dt_bias ? dt_bias[h] : 0.0)", "- (dt_bias ? dt_bias[h] : 0.0)"),
+    "B_read_from_C": ("const double* bt = Bm +", "const double* bt = Cm +"),
+    "gate_without_z": ("yp = yp * zz / (1.0 + exp(-zz));", "yp = yp / (1.0 + exp(-zz));"),
+    "initial_state_transposed": (
+        "memcpy(S, h0 + ((size_t)i * H + h) * (size_t)P * N,\n             sizeof(double) * (size_t)P * N);",
+        "for (int q = 0; q < P * N; ++q) S[q] = h0[((size_t)i * H + h) * (size_t)P * N + (q % P) * N + q / P];"),
+    "clamp_upper_ignored": ("if (delta > dt_max) delta = dt_max;", ""),
+    "chunk_end_off_by_one": ("(t - t0) % chunk == chunk - 1", "(t - t0) % chunk == 0"),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    src = open(os.path.join(ROOT, "oracle", "ssd_ref.c")).read()
+    before, after = MUTANTS[name]
+    assert before in src, f"mutation site for {name} no longer in the oracle"
+    work = tmp_path / "tree"
+    shutil.copytree(os.path.join(ROOT, "oracle"), work / "oracle",
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__", "*.tmp"))
+    shutil.copytree(os.path.join(ROOT, "tests"), work / "tests",
+                    ignore=shutil.ignore_patterns("__pycache__"))
+    (work / "oracle" / "ssd_ref.c").write_text(src.replace(before, after))
+    subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                    "-std=c99", str(work / "oracle" / "ssd_ref.c"), "-o",
+                    str(work / "oracle" / "libssd_ref.so"), "-lm"], check=True)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        "tests/test_oracle_pins.py"], cwd=work, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
+    assert "failed" in r.stdout
