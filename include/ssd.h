@@ -1,0 +1,276 @@
+/*
+ * ssd.h -- libssd: the Mamba-2 SSD chunked scan on AMD Instinct MI355X (gfx950).
+ *
+ * The library computes, for every sequence and head h (group g = h / (H/G)):
+ *
+ *     delta_t = softplus(dt_t + dt_bias_h)            (optionally clamped)
+ *     h_t     = exp(delta_t * A_h) * h_{t-1} + x_t (outer) B_t      (P x N state)
+ *     y_t     = h_t . C_t + D_h * x_t
+ *     out_t   = y_t * silu(z_t)                        (when z is given)
+ *
+ * Mamba-3-Lite "SSD Reference", section "Math: the recurrence both functions
+ * implement" (recurrence and closed form) and section "_discretise" (the step
+ * exp(softplus(dt) A)); the dt bias, groups, D skip, SiLU gate and initial /
+ * final states are those of the Mamba-2 SSD stages timed in mamba PR 1012 and
+ * cudnn-frontend PR 1133 ("optional skip/SiLU", "initial/final-state").
+ *
+ * It is evaluated chunkwise in the five stages vLLM PR 27299 ("Purpose")
+ * names -- chunk cumsum, BMM, chunk state, state passing, chunk scan -- each
+ * exported below, plus a forward call that runs them all.  The chunkwise
+ * algebra is the SSD Reference's: sections "Chunking and the discretized
+ * log-decay", "Intra-chunk outputs and per-chunk states", "Inter-chunk
+ * propagation" and "Readout".
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Symbols: b batch, T tokens per sequence (total tokens when packed),
+ *   H heads, P head dim, G groups, N state dim, C chunk size.
+ * - Batch mode: b sequences of T tokens, chunk c of sequence i covers tokens
+ *   [cC, min(cC + C, T)); logical chunk id j = i * ceil(T/C) + c.
+ * - Packed (varlen) mode (problem.nseq > 0, batch == 1): sequence i owns tokens
+ *   [cu[i], cu[i+1]) and is cut into chunks counted from its own first token,
+ *   so no chunk straddles a sequence boundary and the state restarts at every
+ *   sequence.  Logical chunk ids run sequence by sequence.  The chunk table is
+ *   built on the device by ssd_varlen_chunk_meta.
+ * - K = ssd_num_chunks(problem) logical chunks (an upper bound in packed mode;
+ *   entries past the real count are never read or written).
+ * - Tensors are strided views (ssd_tensor): strides are in ELEMENTS, the
+ *   innermost dimension (P or N) must be contiguous, every row start must be
+ *   16-byte aligned.  x, B, C may be views into one packed xBC buffer.
+ * - Intermediates are caller-owned, contiguous, in these layouts:
+ *     dA_cumsum  float32 (K, H, C): within-chunk inclusive cumsum of
+ *                delta * A; positions past a short chunk's end repeat the
+ *                value at its last token (their log-decay counts as 0).
+ *     CB         float32 (K, G, C, C): CB[j,g,l,s] = C_l . B_s; only s <= l
+ *                inside the chunk is defined, other entries are unspecified.
+ *     states     state_dtype (K, H, P, N).
+ * - Initial and final states are float32 (nseq or b, H, P, N), contiguous.
+ * - Ownership: the caller owns every buffer.  The library allocates nothing,
+ *   keeps no pointer after a call returns, never synchronises the host, and
+ *   holds no global state; calls on different streams may run concurrently.
+ *   Every device call is asynchronous on the stream it is given.
+ * - Errors: arguments are validated on the host before anything is launched,
+ *   so a call that returns an error has launched nothing (except SSD_ERR_HIP,
+ *   returned when a launch itself fails).  ssd_last_error_message() names the
+ *   offending argument (thread-local).
+ * - Determinism: no atomics in the forward pass; results are bitwise
+ *   identical run to run.
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_status {
+  SSD_OK = 0,
+  SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+  SSD_ERR_SHAPE = 2,       /* a dimension is out of range or inconsistent */
+  SSD_ERR_DTYPE = 3,       /* a tensor has a dtype this call does not take */
+  SSD_ERR_STRIDE = 4,      /* inner stride != 1 or a row is not 16-byte aligned */
+  SSD_ERR_UNSUPPORTED = 5, /* valid request this build does not implement */
+  SSD_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+  SSD_ERR_HIP = 7          /* a HIP launch failed; the message has HIP's text */
+} ssd_status;
+
+typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef enum ssd_algo {
+  SSD_ALGO_STAGED = 0, /* the five stage kernels in sequence */
+  SSD_ALGO_FUSED = 1   /* one launch for the whole forward pass */
+} ssd_algo;
+
+/* A strided tensor view.  Shape is implied by the argument's role. */
+typedef struct ssd_tensor {
+  void* data;          /* device pointer; NULL = optional argument absent */
+  ssd_dtype dtype;
+  int64_t stride[3];   /* outer strides in elements, outermost first */
+} ssd_tensor;
+
+typedef struct ssd_problem {
+  int32_t batch;       /* b (must be 1 in packed mode) */
+  int32_t seqlen;      /* T: tokens per sequence, or total packed tokens */
+  int32_t nheads;      /* H */
+  int32_t headdim;     /* P: multiple of 16, <= 256 */
+  int32_t ngroups;     /* G: divides H */
+  int32_t dstate;      /* N: multiple of 16, <= 256 */
+  int32_t chunk_size;  /* C: 32, 64, 128 or 256 */
+  int32_t nseq;        /* packed mode: number of sequences; 0 = batch mode */
+  const int32_t* cu_seqlens; /* packed mode: device, nseq + 1 offsets, cu[0] = 0,
+                                non-decreasing, cu[nseq] = seqlen */
+  const int32_t* chunk_meta; /* packed mode, stage calls: device chunk table
+                                written by ssd_varlen_chunk_meta */
+  int32_t dt_softplus; /* 1: delta = softplus(dt + dt_bias); 0: delta = dt + dt_bias */
+  int32_t dt_clamp;    /* 1: clamp delta to [dt_min, dt_max] */
+  float dt_min, dt_max;
+  ssd_dtype state_dtype; /* storage of the per-chunk states (F32 or BF16) */
+} ssd_problem;
+
+/* ---------------------------------------------------------------- queries */
+
+/* Validate a problem (host only, no HIP call).  Checks: positive dims,
+ * H % G == 0, P and N multiples of 16 in [16, 256], C in {32, 64, 128, 256},
+ * packed mode => batch == 1 and cu_seqlens != NULL.  On failure returns the
+ * status and sets the message naming the dimension. */
+ssd_status ssd_problem_check(const ssd_problem* p);
+
+/* K: logical chunks (batch mode: b * ceil(T/C); packed: ceil(T/C) + nseq, an
+ * upper bound on the real count).  Returns -1 for an invalid problem. */
+int64_t ssd_num_chunks(const ssd_problem* p);
+
+/* Number of int32 entries of the packed-mode chunk table:
+ * 4 + 3*K + (nseq + 1).  Layout:
+ *   [0] number of real chunks Kr, [1] nseq, [2] C, [3] K
+ *   [4 + 3j + 0] sequence of chunk j (-1 for j >= Kr)
+ *   [4 + 3j + 1] first token of chunk j (0 for j >= Kr)
+ *   [4 + 3j + 2] tokens in chunk j, 1..C (0 for j >= Kr)
+ *   [4 + 3K + i] first chunk of sequence i, i = 0..nseq ([nseq] = Kr)
+ * Returns 0 for an invalid problem. */
+size_t ssd_varlen_meta_len(const ssd_problem* p);
+
+/* Bytes of workspace ssd_forward needs for `algo` (0 is a valid answer). */
+ssd_status ssd_workspace_size(const ssd_problem* p, ssd_algo algo, size_t* bytes);
+
+/* ---------------------------------------------------------------- a6 */
+
+/* Build the packed-mode chunk table on the device from p->cu_seqlens (read
+ * on the device only, so the call can be captured in a HIP graph).
+ * meta: device int32, ssd_varlen_meta_len(p) entries, written entirely.
+ * Sequence-aligned chunking per the SSD Reference "Padding rule" applied to
+ * each packed sequence (vLLM PR 27299, continuous batching).  cu_seqlens
+ * must be valid (checked by the host twin, not on the device). */
+ssd_status ssd_varlen_chunk_meta(const ssd_problem* p, int32_t* meta, hipStream_t stream);
+
+/* Host twin of ssd_varlen_chunk_meta: cu_host is host memory with nseq + 1
+ * entries; validates it (cu[0] == 0, non-decreasing, cu[nseq] == seqlen) and
+ * writes the same table to meta_host (meta_len entries). */
+ssd_status ssd_varlen_chunk_meta_host(const ssd_problem* p, const int32_t* cu_host,
+                                      int32_t* meta_host, size_t meta_len);
+
+/* ---------------------------------------------------------------- a1 */
+
+/* Chunk cumsum.  delta = softplus(dt + dt_bias) (or without softplus, and
+ * clamped when asked), a = delta * A_h, dA_cumsum[j,h,l] = sum_{l' <= l} a
+ * within chunk j.  SSD Reference "Chunking and the discretized log-decay"
+ * (A_log = softplus(dt) A, A_cumsum = cumsum over the chunk).
+ *   dt        (b, T, H) F32 or BF16, strides {batch, token, head} (any)
+ *   A         float32 (H), device
+ *   dt_bias   float32 (H), device, or NULL for no bias
+ *   dA_cumsum float32 (K, H, C), written
+ *   dt_out    float32 (K, H, C) or NULL: delta per position (0 past a chunk's end)
+ */
+ssd_status ssd_chunk_cumsum(const ssd_problem* p, ssd_tensor dt, const float* A,
+                            const float* dt_bias, float* dA_cumsum, float* dt_out,
+                            hipStream_t stream);
+
+/* ---------------------------------------------------------------- a2 */
+
+/* BMM: CB[j,g,l,s] = sum_n C[t0+l, g, n] B[t0+s, g, n] for s <= l < len_j.
+ * SSD Reference "Algorithm and tensor-shape contract", step 4 (Cb = Cc Bc^T).
+ *   C, B  (b, T, G, N), same dtype (F32 or BF16), strides {batch, token, group}
+ *   CB    float32 (K, G, C, C), written (entries with s > l left unspecified)
+ */
+ssd_status ssd_bmm_chunk(const ssd_problem* p, ssd_tensor C, ssd_tensor B, float* CB,
+                         hipStream_t stream);
+
+/* ---------------------------------------------------------------- a3 */
+
+/* Chunk state: each chunk's end state from a zero start,
+ *   states[j,h,p,n] = sum_{s < len} exp(cs[last] - cs[s]) x[t0+s,h,p] B[t0+s,g,n]
+ * SSD Reference "Intra-chunk outputs and per-chunk states" (states einsum with
+ * decay_states = exp(A_cumsum[-1] - A_cumsum)).
+ *   x         (b, T, H, P), F32 or BF16 (same dtype as B)
+ *   B         (b, T, G, N)
+ *   dA_cumsum float32 (K, H, C) from ssd_chunk_cumsum
+ *   states    (K, H, P, N) in p->state_dtype, written
+ */
+ssd_status ssd_chunk_state(const ssd_problem* p, ssd_tensor x, ssd_tensor B,
+                           const float* dA_cumsum, void* states, hipStream_t stream);
+
+/* ---------------------------------------------------------------- a4 */
+
+/* State passing, the sequential scan over chunks of every sequence:
+ *   Hin[first] = initial_states[i] (or 0),  Hin[j+1] = exp(Lambda_j) Hin[j] + S_j,
+ *   final_states[i] = exp(Lambda_last) Hin[last] + S_last   (= initial state if empty)
+ * with Lambda_j = dA_cumsum[j, h, len_j - 1].  Equivalent to the SSD
+ * Reference's decay_chunk[z,c] = exp(CD[z-1] - CD[c]) 1[z>c] plus the initial
+ * state term exp(CD[z-1]) H_{-1} ("Inter-chunk propagation").
+ *   states         (K, H, P, N) state_dtype: chunk states S_j from ssd_chunk_state
+ *   dA_cumsum      float32 (K, H, C)
+ *   initial_states float32 (nseq or b, H, P, N) or NULL (zero)
+ *   states_out     (K, H, P, N) state_dtype: carry-in Hin[j]; may alias `states`
+ *   final_states   float32 (nseq or b, H, P, N) or NULL
+ * The recurrence runs in float32 registers; only stored copies are rounded.
+ */
+ssd_status ssd_state_passing(const ssd_problem* p, const void* states,
+                             const float* dA_cumsum, const float* initial_states,
+                             void* states_out, float* final_states, hipStream_t stream);
+
+/* ---------------------------------------------------------------- a5 */
+
+/* Chunk scan: the output of every position l < len_j of chunk j,
+ *   y[l] = exp(cs[l]) C_l . Hin[j]                                    (Y_off)
+ *        + sum_{s <= l} exp(cs[l] - cs[s]) CB[l,s] x_s                 (Y_diag)
+ *        + D_h x_l ;      out = y * silu(z)  if z is given
+ * SSD Reference "Intra-chunk outputs" (L = exp(segsum) masked to s <= l,
+ * Y_diag) and "Readout" (Y_off = C . state . exp(A_cumsum), Y = Y_diag + Y_off);
+ * gate as cudnn-frontend PR 1133 "optional skip/SiLU" (D added before gating).
+ *   CB        float32 (K, G, C, C) from ssd_bmm_chunk
+ *   x         (b, T, H, P); C (b, T, G, N); same dtype
+ *   dA_cumsum float32 (K, H, C)
+ *   states_in (K, H, P, N) state_dtype: carry-in states from ssd_state_passing
+ *   D         float32 (H) or NULL
+ *   z         (b, T, H, P) same dtype as x, or data == NULL
+ *   out       (b, T, H, P) F32 or BF16, written
+ */
+ssd_status ssd_chunk_scan(const ssd_problem* p, const float* CB, ssd_tensor x, ssd_tensor C,
+                          const float* dA_cumsum, const void* states_in, const float* D,
+                          ssd_tensor z, ssd_tensor out, hipStream_t stream);
+
+/* ---------------------------------------------------------------- forward */
+
+typedef struct ssd_fwd_args {
+  ssd_tensor x;               /* (b, T, H, P) */
+  ssd_tensor B;               /* (b, T, G, N) */
+  ssd_tensor C;               /* (b, T, G, N) */
+  ssd_tensor dt;              /* (b, T, H) */
+  const float* A;             /* (H) */
+  const float* dt_bias;       /* (H) or NULL */
+  const float* D;             /* (H) or NULL */
+  ssd_tensor z;               /* (b, T, H, P) or data == NULL */
+  const float* initial_states;/* (nseq or b, H, P, N) float32 or NULL */
+  ssd_tensor out;             /* (b, T, H, P) F32 or BF16 */
+  float* final_states;        /* (nseq or b, H, P, N) float32 or NULL */
+} ssd_fwd_args;
+
+/* The whole forward pass.  SSD_ALGO_STAGED runs chunk cumsum, BMM, chunk
+ * state, state passing and chunk scan (vLLM PR 27299 "Purpose", the five
+ * stages); SSD_ALGO_FUSED computes the same result in one launch (the same
+ * page: one fused kernel that reorders work and synchronises to avoid the
+ * intermediate round trips).  In packed mode the chunk table is built inside
+ * the workspace.  workspace: device memory of at least
+ * ssd_workspace_size(p, algo) bytes, 256-byte aligned, owned by the caller,
+ * contents need not be initialised; it must not be shared by calls that
+ * overlap in time. */
+ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* a,
+                       void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- errors */
+
+const char* ssd_status_string(ssd_status s);
+/* Message of the last failing call on this thread ("" if none). */
+const char* ssd_last_error_message(void);
+/* Library version string. */
+const char* ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_SSD_H */

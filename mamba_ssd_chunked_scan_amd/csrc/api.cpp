@@ -1,0 +1,411 @@
+// api.cpp -- the libssd C ABI: argument validation, workspace layout and the
+// launch sequence of each call.  Every check runs on the host before anything
+// is enqueued, so a call that fails validation has launched nothing.  No call
+// allocates, synchronises or keeps pointers; all state lives in the arguments.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/ssd.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local std::string g_msg;
+
+ssd_status fail(ssd_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_msg = buf;
+  return s;
+}
+
+ssd_status ok() {
+  g_msg.clear();
+  return SSD_OK;
+}
+
+ssd_status hip_fail(hipError_t e, const char* where) {
+  return fail(SSD_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+size_t dsize(ssd_dtype d) { return d == SSD_BF16 ? 2 : 4; }
+int dcode(ssd_dtype d) { return d == SSD_BF16 ? ssd::DT_BF16 : ssd::DT_F32; }
+bool valid_dtype(ssd_dtype d) { return d == SSD_F32 || d == SSD_BF16; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t num_chunks(const ssd_problem* p) {
+  const int64_t nc = cdiv(p->seqlen, p->chunk_size);
+  if (p->nseq > 0) return nc + p->nseq;
+  return (int64_t)p->batch * nc;
+}
+
+ssd_status check_problem(const ssd_problem* p) {
+  if (!p) return fail(SSD_ERR_NULL, "problem is NULL");
+  if (p->batch < 1) return fail(SSD_ERR_SHAPE, "batch = %d must be >= 1", p->batch);
+  if (p->seqlen < 0) return fail(SSD_ERR_SHAPE, "seqlen = %d must be >= 0", p->seqlen);
+  if (p->nheads < 1) return fail(SSD_ERR_SHAPE, "nheads = %d must be >= 1", p->nheads);
+  if (p->ngroups < 1) return fail(SSD_ERR_SHAPE, "ngroups = %d must be >= 1", p->ngroups);
+  if (p->nheads % p->ngroups != 0)
+    return fail(SSD_ERR_SHAPE, "nheads = %d is not a multiple of ngroups = %d", p->nheads,
+                p->ngroups);
+  if (p->headdim < 16 || p->headdim > 256 || p->headdim % 16 != 0)
+    return fail(SSD_ERR_UNSUPPORTED, "headdim = %d: must be a multiple of 16 in [16, 256]",
+                p->headdim);
+  if (p->dstate < 16 || p->dstate > 256 || p->dstate % 16 != 0)
+    return fail(SSD_ERR_UNSUPPORTED, "dstate = %d: must be a multiple of 16 in [16, 256]",
+                p->dstate);
+  const int C = p->chunk_size;
+  if (C != 32 && C != 64 && C != 128 && C != 256)
+    return fail(SSD_ERR_UNSUPPORTED, "chunk_size = %d: must be 32, 64, 128 or 256", C);
+  if (p->nseq < 0) return fail(SSD_ERR_SHAPE, "nseq = %d must be >= 0", p->nseq);
+  if (p->nseq > 0) {
+    if (p->batch != 1)
+      return fail(SSD_ERR_SHAPE, "packed mode (nseq = %d) requires batch == 1, got %d", p->nseq,
+                  p->batch);
+    if (!p->cu_seqlens) return fail(SSD_ERR_NULL, "packed mode requires cu_seqlens");
+  }
+  if (!valid_dtype(p->state_dtype)) return fail(SSD_ERR_DTYPE, "state_dtype is not F32 or BF16");
+  if (p->dt_clamp && !(p->dt_min <= p->dt_max))
+    return fail(SSD_ERR_SHAPE, "dt_min = %g > dt_max = %g", p->dt_min, p->dt_max);
+  if ((int64_t)p->batch * p->seqlen > INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "batch * seqlen exceeds 2^31 - 1 tokens");
+  return SSD_OK;
+}
+
+ssd::Geo make_geo(const ssd_problem* p, const int32_t* meta) {
+  ssd::Geo g;
+  g.b = p->batch;
+  g.T = p->seqlen;
+  g.H = p->nheads;
+  g.P = p->headdim;
+  g.G = p->ngroups;
+  g.N = p->dstate;
+  g.C = p->chunk_size;
+  g.nc = (int)cdiv(p->seqlen, p->chunk_size);
+  g.K = (int)num_chunks(p);
+  g.nseq = p->nseq > 0 ? p->nseq : p->batch;
+  g.hpg = p->nheads / p->ngroups;
+  g.meta = p->nseq > 0 ? meta : nullptr;
+  return g;
+}
+
+ssd::TArg targ(const ssd_tensor& t) {
+  ssd::TArg a;
+  a.p = t.data;
+  a.s0 = t.stride[0];
+  a.s1 = t.stride[1];
+  a.s2 = t.stride[2];
+  return a;
+}
+
+// A 16-byte-vector operand: every row (innermost dim contiguous) starts on a
+// 16-byte boundary.
+ssd_status check_vec_tensor(const ssd_tensor& t, const char* name, bool required,
+                            bool allow_f32 = true, bool allow_bf16 = true) {
+  if (!t.data) {
+    if (required) return fail(SSD_ERR_NULL, "%s is NULL", name);
+    return SSD_OK;
+  }
+  if (!valid_dtype(t.dtype) || (t.dtype == SSD_F32 && !allow_f32) ||
+      (t.dtype == SSD_BF16 && !allow_bf16))
+    return fail(SSD_ERR_DTYPE, "%s has an unsupported dtype", name);
+  const size_t es = dsize(t.dtype);
+  if (reinterpret_cast<uintptr_t>(t.data) % 16 != 0)
+    return fail(SSD_ERR_STRIDE, "%s: data pointer is not 16-byte aligned", name);
+  for (int i = 0; i < 3; ++i) {
+    if (t.stride[i] < 0) return fail(SSD_ERR_STRIDE, "%s: stride[%d] is negative", name, i);
+    if ((t.stride[i] * (int64_t)es) % 16 != 0)
+      return fail(SSD_ERR_STRIDE,
+                  "%s: stride[%d] = %lld elements does not keep rows 16-byte aligned", name, i,
+                  (long long)t.stride[i]);
+  }
+  return SSD_OK;
+}
+
+ssd_status check_dt(const ssd_tensor& t, bool required = true) {
+  if (!t.data) {
+    if (required) return fail(SSD_ERR_NULL, "dt is NULL");
+    return SSD_OK;
+  }
+  if (!valid_dtype(t.dtype)) return fail(SSD_ERR_DTYPE, "dt has an unsupported dtype");
+  if (reinterpret_cast<uintptr_t>(t.data) % dsize(t.dtype) != 0)
+    return fail(SSD_ERR_STRIDE, "dt: data pointer is not element aligned");
+  for (int i = 0; i < 3; ++i)
+    if (t.stride[i] < 0) return fail(SSD_ERR_STRIDE, "dt: stride[%d] is negative", i);
+  return SSD_OK;
+}
+
+#define SSD_TRY(expr)            \
+  do {                           \
+    ssd_status _s = (expr);      \
+    if (_s != SSD_OK) return _s; \
+  } while (0)
+
+#define SSD_HIP(expr, where)                       \
+  do {                                             \
+    hipError_t _e = (expr);                        \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+// With no tokens at all the token tensors may be empty (NULL data).
+bool has_tokens(const ssd_problem* p) { return (int64_t)p->batch * p->seqlen > 0; }
+
+ssd_status need_meta(const ssd_problem* p) {
+  if (p->nseq > 0 && !p->chunk_meta)
+    return fail(SSD_ERR_NULL, "packed mode: chunk_meta is NULL (build it with ssd_varlen_chunk_meta)");
+  return SSD_OK;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct StagedWs {
+  size_t meta, cs, cb, st, total;
+};
+
+StagedWs staged_layout(const ssd_problem* p) {
+  StagedWs w;
+  const int64_t K = num_chunks(p);
+  size_t off = 0;
+  w.meta = off;
+  if (p->nseq > 0) off += align256(ssd_varlen_meta_len(p) * sizeof(int32_t));
+  w.cs = off;
+  off += align256((size_t)K * p->nheads * p->chunk_size * sizeof(float));
+  w.cb = off;
+  off += align256((size_t)K * p->ngroups * p->chunk_size * p->chunk_size * sizeof(float));
+  w.st = off;
+  off += align256((size_t)K * p->nheads * p->headdim * p->dstate * dsize(p->state_dtype));
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_version(void) { return "libssd 0.1 (gfx950)"; }
+
+const char* ssd_status_string(ssd_status s) {
+  switch (s) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL: return "SSD_ERR_NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE";
+    case SSD_ERR_DTYPE: return "SSD_ERR_DTYPE";
+    case SSD_ERR_STRIDE: return "SSD_ERR_STRIDE";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP";
+  }
+  return "SSD_ERR_UNKNOWN";
+}
+
+const char* ssd_last_error_message(void) { return g_msg.c_str(); }
+
+ssd_status ssd_problem_check(const ssd_problem* p) {
+  SSD_TRY(check_problem(p));
+  return ok();
+}
+
+int64_t ssd_num_chunks(const ssd_problem* p) {
+  if (check_problem(p) != SSD_OK) return -1;
+  return num_chunks(p);
+}
+
+size_t ssd_varlen_meta_len(const ssd_problem* p) {
+  if (check_problem(p) != SSD_OK || p->nseq <= 0) return 0;
+  return (size_t)ssd::kMetaHeader + 3 * (size_t)num_chunks(p) + (size_t)p->nseq + 1;
+}
+
+ssd_status ssd_workspace_size(const ssd_problem* p, ssd_algo algo, size_t* bytes) {
+  SSD_TRY(check_problem(p));
+  if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
+  if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED)
+    return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
+  if (algo == SSD_ALGO_FUSED)
+    return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED is not available in this build");
+  *bytes = staged_layout(p).total;
+  return ok();
+}
+
+ssd_status ssd_varlen_chunk_meta(const ssd_problem* p, int32_t* meta, hipStream_t stream) {
+  SSD_TRY(check_problem(p));
+  if (p->nseq <= 0) return fail(SSD_ERR_SHAPE, "ssd_varlen_chunk_meta needs packed mode (nseq > 0)");
+  if (!meta) return fail(SSD_ERR_NULL, "meta is NULL");
+  ssd::Geo g = make_geo(p, meta);
+  SSD_HIP(ssd::launch_varlen_meta(g, p->cu_seqlens, meta, stream), "varlen_chunk_meta launch");
+  return ok();
+}
+
+ssd_status ssd_varlen_chunk_meta_host(const ssd_problem* p, const int32_t* cu, int32_t* meta,
+                                      size_t meta_len) {
+  SSD_TRY(check_problem(p));
+  if (p->nseq <= 0) return fail(SSD_ERR_SHAPE, "ssd_varlen_chunk_meta_host needs packed mode");
+  if (!cu || !meta) return fail(SSD_ERR_NULL, "cu_seqlens or meta is NULL");
+  const size_t need = ssd_varlen_meta_len(p);
+  if (meta_len < need)
+    return fail(SSD_ERR_SHAPE, "meta_len = %zu, need %zu", meta_len, need);
+  if (cu[0] != 0) return fail(SSD_ERR_SHAPE, "cu_seqlens[0] = %d, must be 0", cu[0]);
+  for (int i = 0; i < p->nseq; ++i)
+    if (cu[i + 1] < cu[i])
+      return fail(SSD_ERR_SHAPE, "cu_seqlens decreases at %d (%d -> %d)", i, cu[i], cu[i + 1]);
+  if (cu[p->nseq] != p->seqlen)
+    return fail(SSD_ERR_SHAPE, "cu_seqlens[nseq] = %d, must equal seqlen = %d", cu[p->nseq],
+                p->seqlen);
+  const int C = p->chunk_size;
+  const int64_t K = num_chunks(p);
+  int32_t* first = meta + ssd::kMetaHeader + 3 * K;
+  int32_t j = 0;
+  for (int i = 0; i < p->nseq; ++i) {
+    first[i] = j;
+    const int L = cu[i + 1] - cu[i];
+    for (int k = 0; k * C < L; ++k, ++j) {
+      int32_t* e = meta + ssd::kMetaHeader + 3 * j;
+      e[0] = i;
+      e[1] = cu[i] + k * C;
+      e[2] = L - k * C < C ? L - k * C : C;
+    }
+  }
+  first[p->nseq] = j;
+  for (int64_t r = j; r < K; ++r) {
+    int32_t* e = meta + ssd::kMetaHeader + 3 * r;
+    e[0] = -1; e[1] = 0; e[2] = 0;
+  }
+  meta[0] = j; meta[1] = p->nseq; meta[2] = C; meta[3] = (int32_t)K;
+  return ok();
+}
+
+ssd_status ssd_chunk_cumsum(const ssd_problem* p, ssd_tensor dt, const float* A,
+                            const float* dt_bias, float* dA_cumsum, float* dt_out,
+                            hipStream_t stream) {
+  SSD_TRY(check_problem(p));
+  SSD_TRY(need_meta(p));
+  SSD_TRY(check_dt(dt, has_tokens(p)));
+  if (!A) return fail(SSD_ERR_NULL, "A is NULL");
+  if (!dA_cumsum) return fail(SSD_ERR_NULL, "dA_cumsum is NULL");
+  ssd::Geo g = make_geo(p, p->chunk_meta);
+  SSD_HIP(ssd::launch_chunk_cumsum(g, targ(dt), dcode(dt.dtype), A, dt_bias, p->dt_softplus,
+                                   p->dt_clamp, p->dt_min, p->dt_max, dA_cumsum, dt_out, stream),
+          "chunk_cumsum launch");
+  return ok();
+}
+
+ssd_status ssd_bmm_chunk(const ssd_problem* p, ssd_tensor C, ssd_tensor B, float* CB,
+                         hipStream_t stream) {
+  SSD_TRY(check_problem(p));
+  SSD_TRY(need_meta(p));
+  SSD_TRY(check_vec_tensor(C, "C", has_tokens(p)));
+  SSD_TRY(check_vec_tensor(B, "B", has_tokens(p)));
+  if (C.dtype != B.dtype) return fail(SSD_ERR_DTYPE, "B and C must share a dtype");
+  if (!CB) return fail(SSD_ERR_NULL, "CB is NULL");
+  ssd::Geo g = make_geo(p, p->chunk_meta);
+  SSD_HIP(ssd::launch_bmm_chunk(g, targ(C), targ(B), dcode(C.dtype), CB, stream),
+          "bmm_chunk launch");
+  return ok();
+}
+
+ssd_status ssd_chunk_state(const ssd_problem* p, ssd_tensor x, ssd_tensor B,
+                           const float* dA_cumsum, void* states, hipStream_t stream) {
+  SSD_TRY(check_problem(p));
+  SSD_TRY(need_meta(p));
+  SSD_TRY(check_vec_tensor(x, "x", has_tokens(p)));
+  SSD_TRY(check_vec_tensor(B, "B", has_tokens(p)));
+  if (x.dtype != B.dtype) return fail(SSD_ERR_DTYPE, "x and B must share a dtype");
+  if (!dA_cumsum || !states) return fail(SSD_ERR_NULL, "dA_cumsum or states is NULL");
+  ssd::Geo g = make_geo(p, p->chunk_meta);
+  SSD_HIP(ssd::launch_chunk_state(g, targ(x), targ(B), dcode(x.dtype), dA_cumsum, states,
+                                  dcode(p->state_dtype), stream),
+          "chunk_state launch");
+  return ok();
+}
+
+ssd_status ssd_state_passing(const ssd_problem* p, const void* states, const float* dA_cumsum,
+                             const float* initial_states, void* states_out,
+                             float* final_states, hipStream_t stream) {
+  SSD_TRY(check_problem(p));
+  SSD_TRY(need_meta(p));
+  if (!states || !dA_cumsum || !states_out)
+    return fail(SSD_ERR_NULL, "states, dA_cumsum or states_out is NULL");
+  ssd::Geo g = make_geo(p, p->chunk_meta);
+  SSD_HIP(ssd::launch_state_passing(g, states, dcode(p->state_dtype), dA_cumsum, initial_states,
+                                    states_out, final_states, stream),
+          "state_passing launch");
+  return ok();
+}
+
+ssd_status ssd_chunk_scan(const ssd_problem* p, const float* CB, ssd_tensor x, ssd_tensor C,
+                          const float* dA_cumsum, const void* states_in, const float* D,
+                          ssd_tensor z, ssd_tensor out, hipStream_t stream) {
+  SSD_TRY(check_problem(p));
+  SSD_TRY(need_meta(p));
+  SSD_TRY(check_vec_tensor(x, "x", has_tokens(p)));
+  SSD_TRY(check_vec_tensor(C, "C", has_tokens(p)));
+  SSD_TRY(check_vec_tensor(z, "z", false));
+  SSD_TRY(check_vec_tensor(out, "out", has_tokens(p)));
+  if (x.dtype != C.dtype) return fail(SSD_ERR_DTYPE, "x and C must share a dtype");
+  if (z.data && z.dtype != x.dtype) return fail(SSD_ERR_DTYPE, "z must have x's dtype");
+  if (!CB || !dA_cumsum || !states_in)
+    return fail(SSD_ERR_NULL, "CB, dA_cumsum or states_in is NULL");
+  ssd::Geo g = make_geo(p, p->chunk_meta);
+  SSD_HIP(ssd::launch_chunk_scan(g, CB, targ(x), targ(C), dcode(x.dtype), dA_cumsum, states_in,
+                                 dcode(p->state_dtype), D, targ(z), targ(out), dcode(out.dtype),
+                                 stream),
+          "chunk_scan launch");
+  return ok();
+}
+
+ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* a,
+                       void* workspace, size_t ws_bytes, hipStream_t stream) {
+  SSD_TRY(check_problem(p));
+  if (!a) return fail(SSD_ERR_NULL, "args is NULL");
+  SSD_TRY(check_vec_tensor(a->x, "x", has_tokens(p)));
+  SSD_TRY(check_vec_tensor(a->B, "B", has_tokens(p)));
+  SSD_TRY(check_vec_tensor(a->C, "C", has_tokens(p)));
+  SSD_TRY(check_dt(a->dt, has_tokens(p)));
+  SSD_TRY(check_vec_tensor(a->z, "z", false));
+  SSD_TRY(check_vec_tensor(a->out, "out", has_tokens(p)));
+  if (has_tokens(p) && (a->x.dtype != a->B.dtype || a->x.dtype != a->C.dtype))
+    return fail(SSD_ERR_DTYPE, "x, B and C must share a dtype");
+  if (a->z.data && a->z.dtype != a->x.dtype) return fail(SSD_ERR_DTYPE, "z must have x's dtype");
+  if (!a->A) return fail(SSD_ERR_NULL, "A is NULL");
+  if (algo == SSD_ALGO_FUSED)
+    return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED is not available in this build");
+  if (algo != SSD_ALGO_STAGED) return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
+  const StagedWs w = staged_layout(p);
+  if (w.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < w.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, w.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  int32_t* meta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws + w.meta) : nullptr;
+  float* cs = reinterpret_cast<float*>(ws + w.cs);
+  float* cb = reinterpret_cast<float*>(ws + w.cb);
+  void* st = ws + w.st;
+  ssd::Geo g = make_geo(p, meta);
+  const int in = dcode(a->x.dtype), sd = dcode(p->state_dtype);
+  if (p->nseq > 0)
+    SSD_HIP(ssd::launch_varlen_meta(g, p->cu_seqlens, meta, stream), "varlen_chunk_meta launch");
+  SSD_HIP(ssd::launch_chunk_cumsum(g, targ(a->dt), dcode(a->dt.dtype), a->A, a->dt_bias,
+                                   p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, cs, nullptr,
+                                   stream),
+          "chunk_cumsum launch");
+  SSD_HIP(ssd::launch_bmm_chunk(g, targ(a->C), targ(a->B), in, cb, stream), "bmm_chunk launch");
+  SSD_HIP(ssd::launch_chunk_state(g, targ(a->x), targ(a->B), in, cs, st, sd, stream),
+          "chunk_state launch");
+  SSD_HIP(ssd::launch_state_passing(g, st, sd, cs, a->initial_states, st, a->final_states,
+                                    stream),
+          "state_passing launch");
+  SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, st, sd, a->D, targ(a->z),
+                                 targ(a->out), dcode(a->out.dtype), stream),
+          "chunk_scan launch");
+  return ok();
+}
+
+}  // extern "C"

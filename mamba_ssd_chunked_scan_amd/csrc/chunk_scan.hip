@@ -1,0 +1,291 @@
+// chunk_scan.hip -- stage 5: the output of every position of every chunk,
+//
+//   y[l] = exp(cs[l]) * C_l . Hin[j]                              (Y_off)
+//        + sum_{s <= l} exp(cs[l] - cs[s]) CB[l, s] x_s            (Y_diag)
+//        + D_h x_l;            out = y * silu(z)   when z is given
+//
+// SSD Reference: "Intra-chunk outputs and per-chunk states" (segment matrix
+// L[l, s] = exp(A_cumsum[l] - A_cumsum[s]) 1[l >= s], Y_diag = (L o CB) X) and
+// "Readout" (Y_off = C . state . exp(A_cumsum), Y = Y_diag + Y_off); the skip
+// and SiLU gate of cudnn-frontend PR 1133.  The mask is applied by selecting
+// before exponentiating, so exp never sees the positive exponents above the
+// diagonal (exp(large) * 0 would be inf * 0).
+//
+// One workgroup per (chunk, head, 64-wide slice of P).  LDS holds the chunk's
+// cumsum, x transposed ([p][s], the reduction axis contiguous for the Y_diag
+// B operand) and the carry-in state ([p][n], split into bf16 hi + lo when it is
+// stored in fp32).  Wave w owns the 16-row l-tiles w and 7 - w of every group
+// of 8 (balancing the causal triangle) and all four p-tiles.  The decay-weighted
+// CB fragment and the C fragment are built once per (l-tile, k-block) and reused
+// across p-tiles.  The epilogue goes through LDS so that x, z and out move in
+// coalesced 16-byte rows.
+#include "kernels.hpp"
+
+namespace ssd {
+
+// Carry-in state in LDS, per (input type, state type).
+template <typename T, typename ST> struct HinLds;
+template <> struct HinLds<bf16, float> {  // fp32 state -> bf16 hi + lo
+  static __host__ __device__ int ld(int N) { return N + 8; }
+  static __host__ __device__ size_t bytes(int N) { return 2ull * 64 * ld(N) * sizeof(bf16); }
+  static __device__ void stage(char* base, const float* src, int N, int prow, int n, f32x8 v) {
+    bf16* hi = reinterpret_cast<bf16*>(base);
+    bf16* lo = hi + 64 * ld(N);
+    FragSplit f = split_f32x8(v);
+    *reinterpret_cast<bf16x8*>(&hi[prow * ld(N) + n]) = f.hi;
+    *reinterpret_cast<bf16x8*>(&lo[prow * ld(N) + n]) = f.lo;
+  }
+  static __device__ FragSplit frag(const char* base, int N, int prow, int k) {
+    const bf16* hi = reinterpret_cast<const bf16*>(base);
+    const bf16* lo = hi + 64 * ld(N);
+    FragSplit f;
+    f.hi = *reinterpret_cast<const bf16x8*>(&hi[prow * ld(N) + k]);
+    f.lo = *reinterpret_cast<const bf16x8*>(&lo[prow * ld(N) + k]);
+    return f;
+  }
+};
+template <> struct HinLds<bf16, bf16> {  // bf16 state is exact
+  static __host__ __device__ int ld(int N) { return N + 8; }
+  static __host__ __device__ size_t bytes(int N) { return 64ull * ld(N) * sizeof(bf16); }
+  static __device__ void stage(char* base, const bf16*, int N, int prow, int n, f32x8 v) {
+    bf16* hi = reinterpret_cast<bf16*>(base);
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x8*>(&hi[prow * ld(N) + n]) = o;
+  }
+  static __device__ FragBF frag(const char* base, int N, int prow, int k) {
+    const bf16* hi = reinterpret_cast<const bf16*>(base);
+    FragBF f;
+    f.v = *reinterpret_cast<const bf16x8*>(&hi[prow * ld(N) + k]);
+    return f;
+  }
+};
+template <typename ST> struct HinLdsF32 {  // fp32 inputs: fp32 operands throughout
+  static __host__ __device__ int ld(int N) { return N + 4; }
+  static __host__ __device__ size_t bytes(int N) { return 64ull * ld(N) * sizeof(float); }
+  static __device__ void stage(char* base, const ST*, int N, int prow, int n, f32x8 v) {
+    Vec8<float>::store(reinterpret_cast<float*>(base) + prow * ld(N) + n, v);
+  }
+  static __device__ FragF32 frag(const char* base, int N, int prow, int k) {
+    FragF32 f;
+    f.v = Vec8<float>::load(reinterpret_cast<const float*>(base) + prow * ld(N) + k);
+    return f;
+  }
+};
+template <> struct HinLds<float, float> : HinLdsF32<float> {};
+template <> struct HinLds<float, bf16> : HinLdsF32<bf16> {};
+
+template <typename ST> struct StLoad;
+template <> struct StLoad<float> {
+  static __device__ f32x8 load(const float* p) { return Vec8<float>::load(p); }
+};
+template <> struct StLoad<bf16> {
+  static __device__ f32x8 load(const bf16* p) { return Vec8<bf16>::load(p); }
+};
+
+template <typename T> __host__ __device__ constexpr int xt_pad() { return sizeof(T) == 2 ? 8 : 4; }
+
+struct ScanLayout {
+  size_t off_x, off_h, bytes;
+  int ldx, ldy;
+};
+
+template <typename T, typename ST>
+__host__ __device__ inline ScanLayout scan_layout(int C, int N) {
+  ScanLayout L;
+  L.ldx = C + xt_pad<T>();
+  L.ldy = 64 + 4;
+  L.off_x = 1024;  // cs: up to 256 floats
+  const size_t xbytes = 64ull * L.ldx * sizeof(T);
+  L.off_h = (L.off_x + xbytes + 15) & ~size_t(15);
+  const size_t hb = HinLds<T, ST>::bytes(N);
+  const size_t yb = (size_t)C * L.ldy * sizeof(float);
+  L.bytes = L.off_h + (hb > yb ? hb : yb);
+  return L;
+}
+
+template <typename T, typename ST, typename TO>
+__global__ __launch_bounds__(256) void k_chunk_scan(Geo g, const float* __restrict__ CB, TArg x,
+                                                    TArg Cm, const float* __restrict__ cs,
+                                                    const ST* __restrict__ states,
+                                                    const float* __restrict__ D, TArg z,
+                                                    TArg out) {
+  using Pr = Prec<T>;
+  using HL = HinLds<T, ST>;
+  extern __shared__ __align__(16) char smem[];
+  const int j = blockIdx.x, h = blockIdx.y, p0 = blockIdx.z * 64;
+  Chunk c;
+  if (!get_chunk(g, j, c)) return;
+  const int C = g.C, N = g.N, P = g.P;
+  const int grp = h / g.hpg;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int r16 = lane % 16, q = lane / 16;
+  const ScanLayout lay = scan_layout<T, ST>(C, N);
+  float* s_cs = reinterpret_cast<float*>(smem);
+  T* s_xt = reinterpret_cast<T*>(smem + lay.off_x);
+  char* s_h = smem + lay.off_h;
+  float* s_y = reinterpret_cast<float*>(smem + lay.off_h);
+
+  // ---- stage cumsum, x^T and the carry-in state
+  const float* csr = cs + ((int64_t)j * g.H + h) * C;
+  for (int l = tid; l < C; l += 256) s_cs[l] = csr[l];
+  const int pw = min(64, P - p0);           // p columns in this block (multiple of 16)
+  const int nvec_x = C * 8;                 // C rows x 8 vectors of 8 p
+  for (int v = tid; v < nvec_x; v += 256) {
+    const int s = v / 8, pp = (v % 8) * 8;
+    f32x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (s < c.len && pp < pw) val = Vec8<T>::load(row_ptr<T>(x, c.b, c.t0 + s, h) + p0 + pp);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_xt[(pp + i) * lay.ldx + s] = from_f32<T>(val[i]);
+  }
+  const ST* hsrc = states + ((int64_t)j * g.H + h) * P * N;
+  const int nvec_h = 64 * (N / 8);
+  for (int v = tid; v < nvec_h; v += 256) {
+    const int pr = v / (N / 8), n = (v % (N / 8)) * 8;
+    f32x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (pr < pw) val = StLoad<ST>::load(hsrc + (int64_t)(p0 + pr) * N + n);
+    HL::stage(s_h, hsrc, N, pr, n, val);
+  }
+  __syncthreads();
+
+  // ---- matrix-core phase
+  const int nlt = C / 16;
+  const int npt = pw / 16;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = zero4();
+
+  const float* cbm = CB + ((int64_t)j * g.G + grp) * C * C;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int grp8 = u / 2;
+    const int lt = grp8 * 8 + ((u & 1) ? 7 - wave : wave);
+    if (lt >= nlt) continue;
+    const int lrow = lt * 16 + r16;               // A-operand row of this lane
+    const bool lok = lrow < c.len;
+    // Y_off = C_l . Hin^T over n
+    const T* crow = row_ptr<T>(Cm, c.b, c.t0 + (lok ? lrow : 0), grp);
+    for (int k0 = 0; k0 < N; k0 += 32) {
+      // lanes whose k-quad lies past N (N % 32 == 16) contribute zeros on both
+      // sides; the matrix instruction itself always runs wave-wide
+      const int k = k0 + q * 8;
+      const bool kok = k < N;
+      typename Pr::Exact a = (lok && kok) ? Pr::load_exact(crow + k) : Pr::zero_exact();
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        if (pt < npt) {
+          auto b = HL::frag(s_h, N, pt * 16 + r16, kok ? k : 0);
+          mma(acc[u][pt], a, b);
+        }
+      }
+    }
+    // scale rows by exp(cs[l])
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp(s_cs[lt * 16 + q * 4 + i]);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) acc[u][pt][i] *= e;
+    }
+    // Y_diag = (L o CB) x over s <= l
+    const float csl = s_cs[min(lrow, C - 1)];
+    const int kend = lt * 16 + 16;                 // s < kend covers the diagonal tile
+    for (int k0 = 0; k0 < kend; k0 += 32) {
+      const int s0 = k0 + q * 8;
+      f32x8 m;
+      if (lok) {
+        const f32x8 cb = Vec8<float>::load(cbm + (int64_t)lrow * C + s0);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int s = s0 + e;
+          const bool keep = (s <= lrow) && (s < c.len);
+          m[e] = keep ? fast_exp(csl - s_cs[s]) * cb[e] : 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] = 0.0f;
+      }
+      const auto mf = Pr::derive(m);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        if (pt < npt) {
+          typename Pr::Exact xb = Pr::load_exact(s_xt + (pt * 16 + r16) * lay.ldx + s0);
+          mma(acc[u][pt], mf, xb);
+        }
+      }
+    }
+  }
+  __syncthreads();  // everyone is done with x^T and the state; reuse the state area for y
+
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int lt = (u / 2) * 8 + ((u & 1) ? 7 - wave : wave);
+    if (lt >= nlt) continue;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      if (pt >= npt) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        s_y[(lt * 16 + q * 4 + i) * lay.ldy + pt * 16 + r16] = acc[u][pt][i];
+    }
+  }
+  __syncthreads();
+
+  // ---- epilogue: D skip, SiLU gate, store; coalesced 8-element rows
+  const float Dh = D ? D[h] : 0.0f;
+  const int vpr = pw / 8;  // vectors per row
+  for (int v = tid; v < c.len * vpr; v += 256) {
+    const int l = v / vpr, pp = (v % vpr) * 8;
+    f32x8 y = Vec8<float>::load(s_y + l * lay.ldy + pp);
+    const int t = c.t0 + l;
+    if (D) {
+      const f32x8 xv = Vec8<T>::load(row_ptr<T>(x, c.b, t, h) + p0 + pp);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] += Dh * xv[i];
+    }
+    if (z.p) {
+      const f32x8 zv = Vec8<T>::load(row_ptr<T>(z, c.b, t, h) + p0 + pp);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) y[i] *= silu(zv[i]);
+    }
+    Vec8<TO>::store(row_ptr_mut<TO>(out, c.b, t, h) + p0 + pp, y);
+  }
+}
+
+template <typename T, typename ST, typename TO>
+static hipError_t launch_scan_t(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
+                                const void* states, const float* D, TArg z, TArg out,
+                                hipStream_t s) {
+  const ScanLayout lay = scan_layout<T, ST>(g.C, g.N);
+  auto kern = k_chunk_scan<T, ST, TO>;
+  if (lay.bytes > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.bytes);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(g.K, g.H, (g.P + 63) / 64);
+  hipLaunchKernelGGL(kern, grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, (const ST*)states, D,
+                     z, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
+                             const float* cs, const void* states, int st_dtype,
+                             const float* D, TArg z, TArg out, int out_dtype, hipStream_t s) {
+  if (g.K == 0) return hipSuccess;
+  const bool ib = in_dtype == DT_BF16, sb = st_dtype == DT_BF16, ob = out_dtype == DT_BF16;
+  if (ib) {
+    if (sb) return ob ? launch_scan_t<bf16, bf16, bf16>(g, CB, x, C, cs, states, D, z, out, s)
+                      : launch_scan_t<bf16, bf16, float>(g, CB, x, C, cs, states, D, z, out, s);
+    return ob ? launch_scan_t<bf16, float, bf16>(g, CB, x, C, cs, states, D, z, out, s)
+              : launch_scan_t<bf16, float, float>(g, CB, x, C, cs, states, D, z, out, s);
+  }
+  if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, states, D, z, out, s)
+                    : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, states, D, z, out, s);
+  return ob ? launch_scan_t<float, float, bf16>(g, CB, x, C, cs, states, D, z, out, s)
+            : launch_scan_t<float, float, float>(g, CB, x, C, cs, states, D, z, out, s);
+}
+
+}  // namespace ssd

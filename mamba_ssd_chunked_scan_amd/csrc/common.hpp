@@ -1,0 +1,253 @@
+// common.hpp -- device helpers shared by the libssd kernels (gfx950 / CDNA4).
+//
+// Fragment convention for the 16x16 matrix-core tiles used everywhere:
+//   A operand (16 x K):  lane L holds row  L % 16, k = (L / 16) * 8 + 0..7
+//   B operand (K x 16):  lane L holds col  L % 16, k = (L / 16) * 8 + 0..7
+//   accumulator (16x16): lane L holds col  L % 16, rows (L / 16) * 4 + 0..3
+// i.e. one K-block of 32 per lane-quad of 8 consecutive k values.  For bf16
+// operands that is exactly one v_mfma_f32_16x16x32_bf16.  For fp32 operands the
+// same eight values feed eight v_mfma_f32_16x16x4_f32, instruction i taking the
+// i-th value of every lane: both operands use the same k assignment, so the
+// sum over k is unchanged.
+//
+// Precision: inputs x, B, C are exact in their storage type.  Operands derived
+// in fp32 (decay-weighted CB, decay-scaled x, carried states) are split into a
+// bf16 "hi" part and a bf16 "lo" remainder and multiplied in two passes, which
+// keeps ~16 significant bits instead of bf16's 8 (one pass would lose accuracy
+// the output's dynamic range cannot absorb).  Accumulation is always fp32.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ scalars
+
+__device__ __forceinline__ float bf16_to_f32(bf16 v) { return (float)v; }
+__device__ __forceinline__ bf16 f32_to_bf16(float v) { return (bf16)v; }  // round to nearest even
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<bf16>(bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// exp(x) through the hardware base-2 exponential.
+__device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+
+// softplus(u) = log(1 + e^u); for u > 20 the correction log1p(e^-u) is below
+// 2.1e-9 relative and u itself is returned.
+__device__ __forceinline__ float softplus_f32(float u) {
+  return u > 20.0f ? u : log1pf(__expf(u));
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// ------------------------------------------------------------------ vectors
+
+// Eight consecutive elements of type T from memory, widened to fp32.
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+  static __device__ __forceinline__ f32x8 load(const bf16* p) {
+    bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+    f32x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (float)v[i];
+    return r;
+  }
+  static __device__ __forceinline__ void store(bf16* p, f32x8 v) {
+    bf16x8 o;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (bf16)v[i];
+    *reinterpret_cast<bf16x8*>(p) = o;
+  }
+};
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ f32x8 load(const float* p) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    f32x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r[i] = a[i]; r[i + 4] = b[i]; }
+    return r;
+  }
+  static __device__ __forceinline__ void store(float* p, f32x8 v) {
+    f32x4 a, b;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { a[i] = v[i]; b[i] = v[i + 4]; }
+    *reinterpret_cast<f32x4*>(p) = a;
+    *reinterpret_cast<f32x4*>(p + 4) = b;
+  }
+};
+
+// ------------------------------------------------------------------ fragments
+
+// bf16 path: exact operand (one register quad) and split operand (hi + lo).
+struct FragBF { bf16x8 v; };
+struct FragSplit { bf16x8 hi, lo; };
+// fp32 path: eight fp32 values.
+struct FragF32 { f32x8 v; };
+
+__device__ __forceinline__ FragSplit split_f32x8(f32x8 a) {
+  FragSplit f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    bf16 h = (bf16)a[i];
+    f.hi[i] = h;
+    f.lo[i] = (bf16)(a[i] - (float)h);
+  }
+  return f;
+}
+
+__device__ __forceinline__ void mma(f32x4& acc, const FragBF& a, const FragBF& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const FragSplit& a, const FragBF& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.v, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const FragBF& a, const FragSplit& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.lo, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mma(f32x4& acc, const FragF32& a, const FragF32& b) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
+}
+
+// Operand policy per input type: how an exact input fragment and an fp32-derived
+// fragment are represented, loaded and built.
+template <typename T> struct Prec;
+template <> struct Prec<bf16> {
+  using Exact = FragBF;
+  using Derived = FragSplit;
+  static __device__ __forceinline__ Exact load_exact(const bf16* p) {
+    Exact f; f.v = *reinterpret_cast<const bf16x8*>(p); return f;
+  }
+  static __device__ __forceinline__ Exact zero_exact() {
+    Exact f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = (bf16)0.0f;
+    return f;
+  }
+  static __device__ __forceinline__ Derived derive(f32x8 v) { return split_f32x8(v); }
+};
+template <> struct Prec<float> {
+  using Exact = FragF32;
+  using Derived = FragF32;
+  static __device__ __forceinline__ Exact load_exact(const float* p) {
+    Exact f; f.v = Vec8<float>::load(p); return f;
+  }
+  static __device__ __forceinline__ Exact zero_exact() {
+    Exact f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f.v[i] = 0.0f;
+    return f;
+  }
+  static __device__ __forceinline__ Derived derive(f32x8 v) { Derived f; f.v = v; return f; }
+};
+
+__device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
+
+// ------------------------------------------------------------------ wave scan
+
+// Inclusive prefix sum over the 64 lanes of a wavefront.
+__device__ __forceinline__ float wave_inclusive_sum(float v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    float o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ double wave_inclusive_sum_f64(double v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    double o = __shfl_up(v, d, kWave);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// ------------------------------------------------------------------ geometry
+
+// Problem geometry passed by value to every kernel.
+struct Geo {
+  int b, T, H, P, G, N, C;
+  int nc;        // ceil(T / C) chunks per sequence (batch mode)
+  int K;         // logical chunk slots
+  int nseq;      // sequences (batch mode: b)
+  int hpg;       // heads per group
+  const int32_t* meta;  // packed-mode chunk table, NULL in batch mode
+};
+
+struct Chunk {
+  int b;      // batch row of the chunk's tokens
+  int t0;     // first token (within the batch row)
+  int len;    // tokens in the chunk (1..C)
+  int seq;    // sequence id (batch row in batch mode)
+};
+
+// Chunk table header size and accessors (see the layout in ssd.h).
+constexpr int kMetaHeader = 4;
+
+__device__ __forceinline__ bool get_chunk(const Geo& g, int j, Chunk& c) {
+  if (g.meta) {
+    if (j >= g.meta[0]) return false;
+    const int32_t* e = g.meta + kMetaHeader + 3 * j;
+    c.seq = e[0]; c.t0 = e[1]; c.len = e[2]; c.b = 0;
+    return true;
+  }
+  if (j >= g.K) return false;
+  c.b = j / g.nc;
+  const int cc = j - c.b * g.nc;
+  c.t0 = cc * g.C;
+  c.len = min(g.C, g.T - c.t0);
+  c.seq = c.b;
+  return true;
+}
+
+// Range of logical chunks [first, last) of sequence i.
+__device__ __forceinline__ void seq_chunks(const Geo& g, int i, int& first, int& last) {
+  if (g.meta) {
+    const int32_t* fc = g.meta + kMetaHeader + 3 * g.K;
+    first = fc[i]; last = fc[i + 1];
+  } else {
+    first = i * g.nc; last = first + g.nc;
+  }
+}
+
+// Strided tensor argument as the kernels see it.
+struct TArg {
+  const void* p;
+  int64_t s0, s1, s2;   // batch, token, head/group strides (elements)
+};
+
+template <typename T>
+__device__ __forceinline__ const T* row_ptr(const TArg& a, int b, int t, int hg) {
+  return reinterpret_cast<const T*>(a.p) + (int64_t)b * a.s0 + (int64_t)t * a.s1 +
+         (int64_t)hg * a.s2;
+}
+template <typename T>
+__device__ __forceinline__ T* row_ptr_mut(const TArg& a, int b, int t, int hg) {
+  return reinterpret_cast<T*>(const_cast<void*>(a.p)) + (int64_t)b * a.s0 +
+         (int64_t)t * a.s1 + (int64_t)hg * a.s2;
+}
+
+}  // namespace ssd

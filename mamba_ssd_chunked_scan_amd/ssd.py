@@ -1,0 +1,336 @@
+"""Thin Python binding of libssd (ctypes).
+
+Argument marshalling only: torch supplies device memory (``data_ptr()``),
+strides and the current stream; every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/ssd.h``.  There is no fallback:
+if ``libssd.so`` has not been built, or a call fails, an exception is raised.
+
+Function names follow the C calls: ``ssd_chunk_cumsum``, ``ssd_bmm_chunk``,
+``ssd_chunk_state``, ``ssd_state_passing``, ``ssd_chunk_scan``,
+``ssd_varlen_chunk_meta``, ``ssd_forward``.  Each takes torch tensors and
+returns the tensors it wrote.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libssd.so")
+
+SSD_OK = 0
+STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
+          4: "SSD_ERR_STRIDE", 5: "SSD_ERR_UNSUPPORTED", 6: "SSD_ERR_WORKSPACE", 7: "SSD_ERR_HIP"}
+F32, BF16 = 0, 1
+ALGO = {"staged": 0, "fused": 1}
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class SsdTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int),
+                ("stride", ctypes.c_int64 * 3)]
+
+
+class SsdProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
+                ("ngroups", ctypes.c_int32), ("dstate", ctypes.c_int32),
+                ("chunk_size", ctypes.c_int32), ("nseq", ctypes.c_int32),
+                ("cu_seqlens", ctypes.c_void_p), ("chunk_meta", ctypes.c_void_p),
+                ("dt_softplus", ctypes.c_int32), ("dt_clamp", ctypes.c_int32),
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
+                ("state_dtype", ctypes.c_int)]
+
+
+class SsdFwdArgs(ctypes.Structure):
+    _fields_ = [("x", SsdTensor), ("B", SsdTensor), ("C", SsdTensor), ("dt", SsdTensor),
+                ("A", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("D", ctypes.c_void_p),
+                ("z", SsdTensor), ("initial_states", ctypes.c_void_p), ("out", SsdTensor),
+                ("final_states", ctypes.c_void_p)]
+
+
+_lib = None
+EXPORTS = ("ssd_problem_check", "ssd_num_chunks", "ssd_varlen_meta_len", "ssd_workspace_size",
+           "ssd_varlen_chunk_meta", "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum",
+           "ssd_bmm_chunk", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
+           "ssd_forward", "ssd_status_string", "ssd_last_error_message", "ssd_version")
+
+
+def lib():
+    """The loaded libssd.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m mamba_ssd_chunked_scan_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp, st = ctypes.c_void_p, ctypes.c_int
+        L.ssd_problem_check.argtypes = [P(SsdProblem)]
+        L.ssd_num_chunks.argtypes = [P(SsdProblem)]
+        L.ssd_num_chunks.restype = ctypes.c_int64
+        L.ssd_varlen_meta_len.argtypes = [P(SsdProblem)]
+        L.ssd_varlen_meta_len.restype = ctypes.c_size_t
+        L.ssd_workspace_size.argtypes = [P(SsdProblem), ctypes.c_int, P(ctypes.c_size_t)]
+        L.ssd_varlen_chunk_meta.argtypes = [P(SsdProblem), vp, vp]
+        L.ssd_varlen_chunk_meta_host.argtypes = [P(SsdProblem), P(ctypes.c_int32),
+                                                 P(ctypes.c_int32), ctypes.c_size_t]
+        L.ssd_chunk_cumsum.argtypes = [P(SsdProblem), SsdTensor, vp, vp, vp, vp, vp]
+        L.ssd_bmm_chunk.argtypes = [P(SsdProblem), SsdTensor, SsdTensor, vp, vp]
+        L.ssd_chunk_state.argtypes = [P(SsdProblem), SsdTensor, SsdTensor, vp, vp, vp]
+        L.ssd_state_passing.argtypes = [P(SsdProblem), vp, vp, vp, vp, vp, vp]
+        L.ssd_chunk_scan.argtypes = [P(SsdProblem), vp, SsdTensor, SsdTensor, vp, vp, vp,
+                                     SsdTensor, SsdTensor, vp]
+        L.ssd_forward.argtypes = [P(SsdProblem), ctypes.c_int, P(SsdFwdArgs), vp,
+                                  ctypes.c_size_t, vp]
+        for name in ("ssd_problem_check", "ssd_workspace_size", "ssd_varlen_chunk_meta",
+                     "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum", "ssd_bmm_chunk",
+                     "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward"):
+            getattr(L, name).restype = st
+        L.ssd_status_string.argtypes = [ctypes.c_int]
+        L.ssd_status_string.restype = ctypes.c_char_p
+        L.ssd_last_error_message.restype = ctypes.c_char_p
+        L.ssd_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc):
+    if rc != SSD_OK:
+        raise SSDError(rc, lib().ssd_last_error_message().decode())
+
+
+# ------------------------------------------------------------------ marshalling
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise SSDError(3, f"unsupported dtype {t}")
+
+
+def tensor_arg(t: torch.Tensor | None, packed: bool = False) -> SsdTensor:
+    """ssd_tensor of a (b, T, X, Y) / (b, T, X) tensor, or (T, ...) when packed.
+
+    The innermost dimension must be contiguous for the 4-D roles; for the 3-D dt
+    role all three strides are passed.
+    """
+    s = SsdTensor()
+    if t is None or t.numel() == 0:
+        # absent, or empty (no tokens): no memory to point at
+        s.data = None
+        s.dtype = F32 if t is None else _dtype_code(t.dtype)
+        return s
+    s.data = t.data_ptr()
+    s.dtype = _dtype_code(t.dtype)
+    st = list(t.stride())
+    if packed:
+        st = [0] + st
+    if len(st) == 4:
+        if st[3] != 1 and t.shape[-1 - 0] > 1:
+            raise SSDError(4, "innermost dimension must be contiguous")
+        outer = st[:3]
+    elif len(st) == 3:
+        outer = st
+    else:
+        raise SSDError(2, f"expected a 3-D or 4-D tensor, got shape {tuple(t.shape)}")
+    for i, v in enumerate(outer):
+        s.stride[i] = int(v)
+    return s
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+@dataclass
+class Problem:
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    ngroups: int
+    dstate: int
+    chunk_size: int
+    nseq: int = 0
+    cu_seqlens: torch.Tensor | None = None     # device int32 (nseq + 1)
+    chunk_meta: torch.Tensor | None = None     # device int32 table
+    dt_softplus: bool = True
+    dt_limit: tuple | None = None
+    state_dtype: torch.dtype = torch.float32
+
+    def c(self) -> SsdProblem:
+        p = SsdProblem()
+        p.batch, p.seqlen, p.nheads, p.headdim = self.batch, self.seqlen, self.nheads, self.headdim
+        p.ngroups, p.dstate, p.chunk_size, p.nseq = self.ngroups, self.dstate, self.chunk_size, self.nseq
+        p.cu_seqlens = _ptr(self.cu_seqlens)
+        p.chunk_meta = _ptr(self.chunk_meta)
+        p.dt_softplus = 1 if self.dt_softplus else 0
+        if self.dt_limit is None:
+            p.dt_clamp, p.dt_min, p.dt_max = 0, 0.0, math.inf
+        else:
+            p.dt_clamp, p.dt_min, p.dt_max = 1, float(self.dt_limit[0]), float(self.dt_limit[1])
+        p.state_dtype = _dtype_code(self.state_dtype)
+        return p
+
+    @property
+    def packed(self) -> bool:
+        return self.nseq > 0
+
+    def check(self):
+        _check(lib().ssd_problem_check(ctypes.byref(self.c())))
+
+    def num_chunks(self) -> int:
+        k = lib().ssd_num_chunks(ctypes.byref(self.c()))
+        if k < 0:
+            self.check()
+        return int(k)
+
+    def meta_len(self) -> int:
+        return int(lib().ssd_varlen_meta_len(ctypes.byref(self.c())))
+
+    def workspace_size(self, algo="staged") -> int:
+        n = ctypes.c_size_t(0)
+        _check(lib().ssd_workspace_size(ctypes.byref(self.c()), ALGO[algo], ctypes.byref(n)))
+        return int(n.value)
+
+
+def problem_from(x, B, chunk_size, cu_seqlens=None, **kw) -> Problem:
+    """Problem of x (b, T, H, P) and B (b, T, G, N), or x (T, H, P) when packed."""
+    if cu_seqlens is not None:
+        T, H, P = x.shape
+        G, N = B.shape[1], B.shape[2]
+        return Problem(1, T, H, P, G, N, chunk_size, nseq=cu_seqlens.numel() - 1,
+                       cu_seqlens=cu_seqlens, **kw)
+    b, T, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return Problem(b, T, H, P, G, N, chunk_size, **kw)
+
+
+# ------------------------------------------------------------------ calls
+
+def ssd_varlen_chunk_meta(prob: Problem, meta: torch.Tensor | None = None, stream=None):
+    """Build the packed-mode chunk table on the device; returns the int32 tensor."""
+    if meta is None:
+        meta = torch.empty(prob.meta_len(), dtype=torch.int32, device=prob.cu_seqlens.device)
+    _check(lib().ssd_varlen_chunk_meta(ctypes.byref(prob.c()), meta.data_ptr(), _stream(stream)))
+    return meta
+
+
+def ssd_varlen_chunk_meta_host(prob: Problem, cu_host) -> list:
+    """Host twin of the chunk table (validates cu_seqlens); returns a list of ints."""
+    n = prob.meta_len()
+    cu = (ctypes.c_int32 * len(cu_host))(*[int(v) for v in cu_host])
+    out = (ctypes.c_int32 * n)()
+    _check(lib().ssd_varlen_chunk_meta_host(ctypes.byref(prob.c()), cu, out, n))
+    return list(out)
+
+
+def ssd_chunk_cumsum(prob: Problem, dt, A, dt_bias=None, dA_cumsum=None, dt_out=None,
+                     stream=None):
+    K = prob.num_chunks()
+    if dA_cumsum is None:
+        dA_cumsum = torch.empty((K, prob.nheads, prob.chunk_size), dtype=torch.float32,
+                                device=dt.device)
+    _check(lib().ssd_chunk_cumsum(ctypes.byref(prob.c()), tensor_arg(dt, packed=prob.packed),
+                                  A.data_ptr(), _ptr(dt_bias), dA_cumsum.data_ptr(),
+                                  _ptr(dt_out), _stream(stream)))
+    return dA_cumsum
+
+
+def ssd_bmm_chunk(prob: Problem, C, B, CB=None, stream=None):
+    K = prob.num_chunks()
+    if CB is None:
+        CB = torch.empty((K, prob.ngroups, prob.chunk_size, prob.chunk_size),
+                         dtype=torch.float32, device=C.device)
+    _check(lib().ssd_bmm_chunk(ctypes.byref(prob.c()), tensor_arg(C, prob.packed),
+                               tensor_arg(B, prob.packed), CB.data_ptr(), _stream(stream)))
+    return CB
+
+
+def ssd_chunk_state(prob: Problem, x, B, dA_cumsum, states=None, stream=None):
+    K = prob.num_chunks()
+    if states is None:
+        states = torch.empty((K, prob.nheads, prob.headdim, prob.dstate),
+                             dtype=prob.state_dtype, device=x.device)
+    _check(lib().ssd_chunk_state(ctypes.byref(prob.c()), tensor_arg(x, prob.packed),
+                                 tensor_arg(B, prob.packed), dA_cumsum.data_ptr(),
+                                 states.data_ptr(), _stream(stream)))
+    return states
+
+
+def ssd_state_passing(prob: Problem, states, dA_cumsum, initial_states=None, states_out=None,
+                      final_states=None, stream=None):
+    if states_out is None:
+        states_out = torch.empty_like(states)
+    if final_states is None:
+        nseq = prob.nseq if prob.packed else prob.batch
+        final_states = torch.empty((nseq, prob.nheads, prob.headdim, prob.dstate),
+                                   dtype=torch.float32, device=states.device)
+    _check(lib().ssd_state_passing(ctypes.byref(prob.c()), states.data_ptr(),
+                                   dA_cumsum.data_ptr(), _ptr(initial_states),
+                                   states_out.data_ptr(), _ptr(final_states), _stream(stream)))
+    return states_out, final_states
+
+
+def ssd_chunk_scan(prob: Problem, CB, x, C, dA_cumsum, states_in, D=None, z=None, out=None,
+                   out_dtype=None, stream=None):
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _check(lib().ssd_chunk_scan(ctypes.byref(prob.c()), CB.data_ptr(),
+                                tensor_arg(x, prob.packed), tensor_arg(C, prob.packed),
+                                dA_cumsum.data_ptr(), states_in.data_ptr(), _ptr(D),
+                                tensor_arg(z, prob.packed), tensor_arg(out, prob.packed),
+                                _stream(stream)))
+    return out
+
+
+def ssd_forward(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=None,
+                cu_seqlens=None, chunk_size=128, dt_softplus=True, dt_limit=None,
+                state_dtype=torch.float32, out=None, out_dtype=None, final_states=None,
+                algo="staged", workspace=None, stream=None):
+    """The whole forward pass; returns (out, final_states).
+
+    Batch mode: x (b, T, H, P), B and C (b, T, G, N), dt (b, T, H), z like x,
+    initial_states (b, H, P, N) float32.  Packed mode: the same without the batch
+    axis plus ``cu_seqlens`` (device int32, nseq + 1).
+    """
+    prob = problem_from(x, B, chunk_size, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
+                        dt_limit=dt_limit, state_dtype=state_dtype)
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    if final_states is None:
+        nseq = prob.nseq if prob.packed else prob.batch
+        final_states = torch.empty((nseq, prob.nheads, prob.headdim, prob.dstate),
+                                   dtype=torch.float32, device=x.device)
+    need = prob.workspace_size(algo)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    a = SsdFwdArgs()
+    pk = prob.packed
+    a.x, a.B, a.C = tensor_arg(x, pk), tensor_arg(B, pk), tensor_arg(C, pk)
+    a.dt = tensor_arg(dt, pk)
+    a.A, a.dt_bias, a.D = A.data_ptr(), _ptr(dt_bias), _ptr(D)
+    a.z = tensor_arg(z, pk)
+    a.initial_states = _ptr(initial_states)
+    a.out = tensor_arg(out, pk)
+    a.final_states = _ptr(final_states)
+    _check(lib().ssd_forward(ctypes.byref(prob.c()), ALGO[algo], ctypes.byref(a),
+                             workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out, final_states

@@ -25,6 +25,8 @@ Contents
 * ``carry_in_states``    -- the state entering every chunk, SSD Reference
                             "Inter-chunk propagation" (computed as the
                             recurrence's state at the chunk boundary).
+* ``state_passing``      -- the chunk-level recurrence applied to given chunk
+                            states, SSD Reference "Inter-chunk propagation".
 
 All floating-point work is fp64.  Every function here is pinned by the
 ``-m "not gpu"`` tests against closed forms, special cases and brute force.
@@ -322,3 +324,32 @@ def carry_in_states(chunk_end_states, meta: ChunkMeta, initial_states=None):
         else:
             out[j] = chunk_end_states[j - 1]
     return out
+
+
+def state_passing(S, cs, meta: ChunkMeta, initial_states=None):
+    """The inter-chunk recurrence on given chunk states (fp64).
+
+    SSD Reference, "Inter-chunk propagation": the state entering chunk z is the
+    sum over earlier chunks c of exp(CD[z-1] - CD[c]) S_c plus exp(CD[z-1])
+    times the initial state, which is the recurrence
+        Hin[first] = h_init (or 0),  Hin[j + 1] = exp(Lambda_j) Hin[j] + S_j
+    with Lambda_j = cs[j, :, len_j - 1], restarted at every sequence's first
+    chunk.  S is (K, H, P, N), cs (K, H, C).  Returns (Hin (K, H, P, N),
+    final (nseq, H, P, N)); an empty sequence's final state is its initial state.
+    """
+    S = np.asarray(S, dtype=np.float64)
+    cs = np.asarray(cs, dtype=np.float64)
+    K = meta.nchunks
+    nseq = len(meta.first_chunk) - 1
+    shp = S.shape[1:]
+    Hin = np.zeros((K,) + shp)
+    final = np.zeros((nseq,) + shp)
+    for i in range(nseq):
+        cur = (np.zeros(shp) if initial_states is None
+               else np.asarray(initial_states, dtype=np.float64)[i].copy())
+        for j in range(meta.first_chunk[i], meta.first_chunk[i + 1]):
+            Hin[j] = cur
+            lam = cs[j, :, meta.length[j] - 1]
+            cur = np.exp(lam)[:, None, None] * cur + S[j]
+        final[i] = cur
+    return Hin, final

@@ -1,0 +1,296 @@
+"""End-to-end parity of ssd_forward (through the C ABI) against the fp64 oracle.
+
+Small cases compare every element; the full-size workloads (the benchmark's
+launch configuration: bf16, x/B/C as views of one packed xBC buffer) compare
+sampled heads, which the oracle computes on their own, plus properties that
+hold at any size (finite, run-to-run bit equality, packed == unpacked).
+"""
+import numpy as np
+import pytest
+import torch
+
+from mamba_ssd_chunked_scan_amd import ssd
+from mamba_ssd_chunked_scan_amd.inputs import WORKLOADS, Inputs, edge_seqlens
+from helpers import (TOL_BF16, TOL_BF16_DESIGN, TOL_F32, bf16_out_ok, device_inputs, err,
+                     head_slice, in_dtype, make_inputs, oracle_run, small_workload, to_np,
+                     with_initial_states)
+
+pytestmark = pytest.mark.gpu
+
+ALGOS = ["staged"]
+
+
+def run_gpu(inp, w, algo="staged", out_dtype=torch.float32, packed_xbc=False, **kw):
+    dev = device_inputs(inp, in_dtype(w), packed_xbc=packed_xbc)
+    out, fin = ssd.ssd_forward(dev["x"], dev["B"], dev["C"], dev["dt"], dev["A"],
+                               dev["dt_bias"], dev["D"], dev["z"], dev["initial_states"],
+                               cu_seqlens=dev["cu_seqlens"], chunk_size=w.chunk_size,
+                               out_dtype=out_dtype, algo=algo, **kw)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def check(w, got_y, got_f, ref, out_dtype=torch.float32, tol=None):
+    if tol is None:
+        tol = TOL_F32 if w.dtype == "f32" else TOL_BF16_DESIGN
+    gy = to_np(got_y)
+    if out_dtype == torch.float32:
+        e = err(gy, ref.y)
+        assert e <= tol, f"output err {e:.3e} > {tol}"
+        if w.dtype != "f32":
+            assert e <= TOL_BF16
+    else:
+        okay, excess = bf16_out_ok(gy, ref.y, tol)
+        assert okay, f"bf16 output exceeds its bound by {excess:.3e}"
+    ef = err(to_np(got_f), ref.final_states)
+    assert ef <= tol, f"final state err {ef:.3e} > {tol}"
+
+
+# ------------------------------------------------------------------ small, every element
+
+SMALL = {
+    "tiny_f32": WORKLOADS["tiny"],
+    "ragged_batch2": small_workload("ragged_batch2", batch=2, seqlen=333, nheads=6, headdim=32,
+                                    ngroups=2, dstate=64, chunk_size=64),
+    "c128_g8": small_workload("c128_g8", seqlen=1000, nheads=16, headdim=64, ngroups=8,
+                              dstate=128, chunk_size=128),
+    "c256": small_workload("c256", seqlen=700, nheads=4, headdim=64, ngroups=1, dstate=128,
+                           chunk_size=256, has_z=False),
+    "odd_hpg": small_workload("odd_hpg", seqlen=200, nheads=6, headdim=16, ngroups=2, dstate=32,
+                              chunk_size=32),
+    "n16_p128": small_workload("n16_p128", seqlen=150, nheads=2, headdim=128, ngroups=1,
+                               dstate=16, chunk_size=64),
+    "n48_p48": small_workload("n48_p48", seqlen=190, nheads=2, headdim=48, ngroups=1,
+                              dstate=48, chunk_size=64),
+    "max_dims": small_workload("max_dims", seqlen=300, nheads=2, headdim=256, ngroups=1,
+                               dstate=256, chunk_size=256),
+    "max_dims_f32": small_workload("max_dims_f32", seqlen=270, nheads=1, headdim=256,
+                                   ngroups=1, dstate=256, chunk_size=256, dtype="f32"),
+    "packed_edges": small_workload("packed_edges", seqlen=1600, nheads=4, headdim=32, ngroups=2,
+                                   dstate=32, chunk_size=64, seqlens=edge_seqlens(64, 1600)),
+    "packed_random": small_workload("packed_random", seqlen=2000, nheads=4, headdim=64,
+                                    ngroups=4, dstate=64, chunk_size=128, nseq=5),
+    "f32_packed": small_workload("f32_packed", seqlen=500, nheads=2, headdim=16, ngroups=1,
+                                 dstate=16, chunk_size=32, dtype="f32",
+                                 seqlens=(31, 0, 33, 436)),
+}
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("name", sorted(SMALL))
+def test_small_fp32_out(name, algo):
+    w = SMALL[name]
+    inp = with_initial_states(make_inputs(w))
+    ref = oracle_run(inp)
+    y, f = run_gpu(inp, w, algo)
+    check(w, y, f, ref)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("name", ["ragged_batch2", "c128_g8", "packed_edges", "tiny_f32"])
+def test_small_bf16_out(name, algo):
+    w = SMALL[name]
+    inp = make_inputs(w)
+    ref = oracle_run(inp)
+    y, f = run_gpu(inp, w, algo, out_dtype=torch.bfloat16)
+    check(w, y, f, ref, out_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("C", [32, 64, 128, 256])
+def test_chunk_size_invariance(C, algo):
+    # the tiny fp32 workload at every chunk size matches the same oracle output
+    base = WORKLOADS["tiny"]
+    w = small_workload("inv", seqlen=base.seqlen, nheads=base.nheads, headdim=base.headdim,
+                       ngroups=base.ngroups, dstate=base.dstate, chunk_size=C, dtype="f32",
+                       has_z=False, seed=base.seed)
+    inp = make_inputs(w)
+    ref = oracle_run(inp)
+    y, f = run_gpu(inp, w, algo)
+    check(w, y, f, ref)
+
+
+OPTION_CASES = {
+    "no_D_no_z": dict(has_D=False, has_z=False),
+    "z_only": dict(has_D=False, has_z=True),
+    "no_bias": dict(bias=None),
+    "init_only": dict(has_D=False, has_z=False, init=True, zero_x=True),
+    "clamp": dict(dt_limit=(1e-3, 0.1)),
+    "no_softplus": dict(dt_softplus=False, dt_shift=0.05),
+    "strong_decay": dict(A=-1e4),
+    "zero_decay": dict(A=0.0),
+    "weak_positive": dict(A=0.01),
+    "softplus_linear_branch": dict(bias=21.0, A=-0.01),
+    "softplus_negative_tail": dict(bias=-30.0),
+}
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("case", sorted(OPTION_CASES))
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_options(case, dtype, algo):
+    o = OPTION_CASES[case]
+    w = small_workload(case, seqlen=260, nheads=4, headdim=32, ngroups=2, dstate=32,
+                       chunk_size=64, dtype=dtype, has_D=o.get("has_D", True),
+                       has_z=o.get("has_z", True))
+    inp = make_inputs(w)
+    if "bias" in o:
+        inp.dt_bias = None if o["bias"] is None else np.full(w.nheads, o["bias"], np.float32)
+    if "A" in o:
+        inp.A = np.full(w.nheads, o["A"], np.float32)
+    if o.get("init"):
+        with_initial_states(inp)
+    if o.get("zero_x"):
+        inp.x = np.zeros_like(inp.x)
+    kw = {}
+    okw = {}
+    if "dt_limit" in o:
+        lo, hi = o["dt_limit"]
+        kw["dt_limit"] = (lo, hi)
+        okw["dt_limit"] = (float(np.float32(lo)), float(np.float32(hi)))
+    if o.get("dt_softplus") is False:
+        kw["dt_softplus"] = False
+        okw["dt_softplus"] = False
+        inp.dt = (np.abs(inp.dt) * 0.01 + o["dt_shift"]).astype(np.float32)
+        if dtype == "bf16":
+            from mamba_ssd_chunked_scan_amd.inputs import round_bf16
+            inp.dt = round_bf16(inp.dt)
+        inp.dt_bias = np.zeros(w.nheads, np.float32)
+    ref = oracle_run(inp, **okw)
+    y, f = run_gpu(inp, w, algo, **kw)
+    assert np.all(np.isfinite(to_np(y)))
+    check(w, y, f, ref)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("T", [1, 63, 64, 65, 128])
+def test_short_sequences(T, algo):
+    w = small_workload("short", batch=3, seqlen=T, nheads=2, headdim=16, ngroups=1, dstate=16,
+                       chunk_size=64)
+    inp = with_initial_states(make_inputs(w))
+    ref = oracle_run(inp)
+    y, f = run_gpu(inp, w, algo)
+    check(w, y, f, ref)
+
+
+def test_zero_tokens_passes_initial_state_through():
+    w = small_workload("empty", batch=2, seqlen=0, nheads=2, headdim=16, ngroups=1, dstate=16,
+                       chunk_size=64)
+    inp = with_initial_states(make_inputs(w))
+    y, f = run_gpu(inp, w)
+    assert y.numel() == 0
+    assert np.array_equal(to_np(f), inp.initial_states.astype(np.float64))
+
+
+# ------------------------------------------------------------------ invariants on the GPU
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_run_to_run_bit_identical(algo):
+    w = SMALL["c128_g8"]
+    inp = make_inputs(w)
+    y1, f1 = run_gpu(inp, w, algo)
+    y2, f2 = run_gpu(inp, w, algo)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_packed_xbc_views_equal_contiguous(algo):
+    w = SMALL["c128_g8"]
+    inp = make_inputs(w)
+    y1, f1 = run_gpu(inp, w, algo, packed_xbc=True)
+    y2, f2 = run_gpu(inp, w, algo, packed_xbc=False)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_packed_equals_separate_sequences(algo):
+    w = SMALL["packed_edges"]
+    inp = with_initial_states(make_inputs(w))
+    yp, fp = run_gpu(inp, w, algo)
+    cu = inp.cu_seqlens
+    for i in range(len(cu) - 1):
+        s, e = int(cu[i]), int(cu[i + 1])
+        if e == s:
+            assert np.array_equal(to_np(fp[i]), inp.initial_states[i].astype(np.float64))
+            continue
+        one = Inputs(inp.x[None, s:e], inp.B[None, s:e], inp.C[None, s:e], inp.dt[None, s:e],
+                     inp.A, inp.dt_bias, inp.D, inp.z[None, s:e], None,
+                     inp.initial_states[i:i + 1])
+        wi = small_workload("one", seqlen=e - s, nheads=w.nheads, headdim=w.headdim,
+                            ngroups=w.ngroups, dstate=w.dstate, chunk_size=w.chunk_size)
+        yi, fi = run_gpu(one, wi, algo)
+        assert torch.equal(yp[s:e], yi[0])
+        assert torch.equal(fp[i], fi[0])
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_split_and_resume(algo):
+    w = SMALL["c128_g8"]
+    inp = make_inputs(w)
+    y, f = run_gpu(inp, w, algo)
+    for k in (512, 300):  # on a chunk boundary, and inside a chunk
+        cut = lambda a, sl: None if a is None else a[:, sl]
+        first = Inputs(*(cut(getattr(inp, n), slice(0, k)) if n in ("x", "B", "C", "dt", "z")
+                         else getattr(inp, n) for n in ("x", "B", "C", "dt", "A", "dt_bias",
+                                                        "D", "z", "cu_seqlens",
+                                                        "initial_states")))
+        w1 = small_workload("a", seqlen=k, nheads=w.nheads, headdim=w.headdim,
+                            ngroups=w.ngroups, dstate=w.dstate, chunk_size=w.chunk_size)
+        y1, f1 = run_gpu(first, w1, algo)
+        second = Inputs(*(cut(getattr(inp, n), slice(k, None)) if n in ("x", "B", "C", "dt", "z")
+                          else getattr(inp, n) for n in ("x", "B", "C", "dt", "A", "dt_bias",
+                                                         "D", "z", "cu_seqlens")),
+                        initial_states=to_np(f1).astype(np.float32))
+        w2 = small_workload("b", seqlen=w.seqlen - k, nheads=w.nheads, headdim=w.headdim,
+                            ngroups=w.ngroups, dstate=w.dstate, chunk_size=w.chunk_size)
+        y2, f2 = run_gpu(second, w2, algo)
+        ycat = torch.cat([y1, y2], dim=1)
+        if k % w.chunk_size == 0:
+            assert torch.equal(ycat, y) and torch.equal(f2, f)
+        else:
+            # a shifted chunk grid rounds differently; both runs sit within
+            # the design bound of the oracle, so of each other
+            assert err(to_np(ycat), to_np(y)) <= 2 * TOL_BF16_DESIGN
+            assert err(to_np(f2), to_np(f)) <= 2 * TOL_BF16_DESIGN
+
+
+# ------------------------------------------------------------------ full size, sampled heads
+
+def sample_heads(inp, w, n_extra=2, seed=0):
+    """One head per group (up to 8), the slowest-decaying head, and a few random ones."""
+    H, G = w.nheads, w.ngroups
+    hpg = H // G
+    heads = {g * hpg + (g % hpg) for g in range(min(G, 8))}
+    sp = np.log1p(np.exp(inp.dt_bias.astype(np.float64)))
+    heads.add(int(np.argmin(sp * np.abs(inp.A))))
+    rng = np.random.default_rng(seed)
+    heads.update(int(h) for h in rng.choice(H, n_extra, replace=False))
+    return sorted(heads)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("name", ["granite", "nemotron", "nemotron_varlen", "longctx"])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_full_size_sampled(name, out_dtype, algo):
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    y, f = run_gpu(inp, w, algo, out_dtype=out_dtype, packed_xbc=True)
+    packed = inp.cu_seqlens is not None
+    yn = to_np(y)
+    assert np.all(np.isfinite(yn))
+    heads = sample_heads(inp, w, n_extra=1 if name == "longctx" else 2)
+    sub = head_slice(inp, heads, packed=packed)
+    ref = oracle_run(sub, threads=len(heads))
+    ax = 1 if packed else 2
+    gy = np.take(yn, heads, axis=ax)
+    if out_dtype == torch.float32:
+        e = err(gy, ref.y)
+        assert e <= TOL_BF16_DESIGN, e
+    else:
+        okay, excess = bf16_out_ok(gy, ref.y, TOL_BF16_DESIGN)
+        assert okay, excess
+    gf = to_np(f)[:, heads]
+    assert err(gf, ref.final_states) <= TOL_BF16_DESIGN
+    # bitwise repeatable at full size
+    y2, f2 = run_gpu(inp, w, algo, out_dtype=out_dtype, packed_xbc=True)
+    assert torch.equal(y, y2) and torch.equal(f, f2)

@@ -374,6 +374,12 @@ def test_oracle_matches_pages_chunkwise_algorithm(T, Cs):
     assert rel(S, states) < 1e-12
     Hin = oracle.carry_in_states(r.chunk_end_states, meta, h0)
     assert rel(Hin, carry) < 1e-12
+    # the chunk-level recurrence on the isolated chunk states lands on the same
+    # carry-in and final states as the token-level recurrence
+    Hin2, fin2 = oracle.state_passing(S, oracle.chunk_cumsum(dt, A, meta, Cs, dt_bias=bias),
+                                      meta, h0)
+    assert rel(Hin2, carry) < 1e-12
+    assert rel(fin2[0], final) < 1e-12
     cs = oracle.chunk_cumsum(dt, A, meta, Cs, dt_bias=bias)
     a = plain_softplus(dt + bias) * A
     for j in range(meta.nchunks):
@@ -412,3 +418,21 @@ def test_wrong_propagation_window_is_detected():
                                                 chunk_size=Cs).chunk_end_states, meta)
     assert rel(wrong, Hin) > 1e-3
     del r
+
+
+def test_state_passing_packed_with_empty_sequence():
+    rng = np.random.default_rng(41)
+    lens = [7, 0, 12, 3]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    T, H, P, N, Cs = int(cu[-1]), 2, 2, 3, 4
+    x = rng.standard_normal((T, H, P)); B = rng.standard_normal((T, 1, N))
+    C = rng.standard_normal((T, 1, N)); dt = rng.standard_normal((T, H))
+    A = -np.exp(rng.uniform(-1, 1, H)); h0 = rng.standard_normal((4, H, P, N))
+    r = oracle.ssd_fwd(x, B, C, dt, A, initial_states=h0, cu_seqlens=cu, chunk_size=Cs)
+    meta = oracle.varlen_chunk_meta(cu, Cs)
+    S = oracle.chunk_states(x, B, dt, A, meta)
+    cs = oracle.chunk_cumsum(dt, A, meta, Cs)
+    Hin, fin = oracle.state_passing(S, cs, meta, h0)
+    assert rel(Hin, oracle.carry_in_states(r.chunk_end_states, meta, h0)) < 1e-12
+    assert rel(fin, r.final_states) < 1e-12
+    assert np.array_equal(fin[1], h0[1])
