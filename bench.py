@@ -1,0 +1,286 @@
+#!/usr/bin/env python3
+"""Benchmark: SSD forward tokens/s at Nemotron-Nano dims (seq 8192, bf16) on one MI355X.
+
+One step = one whole forward pass (chunk cumsum, BMM, chunk state, state
+passing, chunk scan -- or the single fused kernel) over one batch of synthetic
+inputs already resident in HBM.  Prints ONE JSON line (rank 0).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload nemotron]
+                    [--algo staged|fused|auto] [--no-cpu-baseline]
+
+Only one GPU is used: --gpus above 1 exits with a message.
+
+Timing: W untimed steps, then K steps bracketed by torch.cuda.synchronize();
+wall time over the K steps gives `value`.  Inside the same timed region every
+kernel is bracketed by HIP events on the stream it runs on, which gives each
+kernel's average duration; the dominant one is reported against its roofline
+(algorithmic bytes per launch / average duration vs 8 TB/s HBM).
+
+cpu_baseline: the fp64 oracle (C, OpenMP) on the host's cores over the same
+workload, timed separately (a reported baseline, not the target).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA, published
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="nemotron")
+    ap.add_argument("--algo", default="auto", choices=["auto", "staged", "fused"])
+    ap.add_argument("--state-dtype", default="f32", choices=["f32", "bf16"])
+    ap.add_argument("--out-dtype", default="bf16", choices=["f32", "bf16"])
+    ap.add_argument("--layout", default="xbc", choices=["xbc", "contiguous"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-repeats", type=int, default=3)
+    return ap.parse_args()
+
+
+def stage_bytes(w, K, state_bytes, out_bytes, in_bytes=2):
+    """Algorithmic HBM bytes each kernel must move per launch (one forward).
+
+    b*T tokens, H heads, P head dim, G groups, N state, C chunk, K chunk slots.
+    Each input is read once, each output written once; CB is fp32 and only its
+    causal half (s <= l) is written and read; the cumsum is fp32.
+    """
+    T = w.batch * w.seqlen
+    H, P, G, N, C = w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk_size
+    e = in_bytes
+    x = T * H * P * e
+    bc = T * G * N * e
+    dt = T * H * e
+    cs = 4 * K * H * C
+    cb = 4 * K * G * C * (C + 1) // 2
+    st = K * H * P * N * state_bytes
+    fin = 4 * (w.nseq or w.batch) * H * P * N
+    z = x if w.has_z else 0
+    out = T * H * P * out_bytes
+    return {
+        "chunk_cumsum": dt + cs,
+        "bmm_chunk": 2 * bc + cb,
+        "chunk_state": x + bc + cs + st,
+        "state_passing": 2 * st + 4 * K * H + fin,
+        "chunk_scan": cb + x + bc + cs + st + z + out,
+        "fused_fwd": x + 2 * bc + dt + z + out + fin,
+    }
+
+
+def stage_flops(w, K):
+    """Useful matrix flops per launch (causal half only, no hi/lo second pass)."""
+    H, P, G, N, C = w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk_size
+    return {
+        "chunk_cumsum": 0,
+        "bmm_chunk": K * G * C * (C + 1) * N,
+        "chunk_state": 2 * K * H * C * P * N,
+        "state_passing": 2 * K * H * P * N,
+        "chunk_scan": 2 * K * H * C * N * P + K * H * C * (C + 1) * P,
+    }
+
+
+def cpu_baseline(w, inp, repeats):
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    times = []
+    oracle.ssd_fwd(inp.x, inp.B, inp.C, inp.dt, inp.A, inp.dt_bias, inp.D, inp.z,
+                   cu_seqlens=inp.cu_seqlens, threads=threads)  # warm-up (page-in)
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        oracle.ssd_fwd(inp.x, inp.B, inp.C, inp.dt, inp.A, inp.dt_bias, inp.D, inp.z,
+                       cu_seqlens=inp.cu_seqlens, threads=threads)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": w.tokens / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"the whole {w.name} workload ({w.tokens} tokens, all {w.nheads} heads), "
+                       f"fp64 sequential recurrence, median of {repeats} runs after 1 warm-up"),
+            "seconds": t, "cpu": platform.processor() or platform.machine()}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (--gpus {args.gpus} requested). "
+              "The path would shard over heads/groups with no communication; see the design "
+              "notes.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mamba_ssd_chunked_scan_amd import ssd
+    from mamba_ssd_chunked_scan_amd.inputs import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(w)
+    dev = torch.device("cuda:0")
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    sdt = torch.float32 if args.state_dtype == "f32" else torch.bfloat16
+    odt = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
+
+    def up(a, dt=tdt):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+
+    if args.layout == "xbc":
+        lead = inp.x.shape[:-2]
+        H, P, G, N = w.nheads, w.headdim, w.ngroups, w.dstate
+        buf = up(np.concatenate([inp.x.reshape(lead + (H * P,)), inp.B.reshape(lead + (G * N,)),
+                                 inp.C.reshape(lead + (G * N,))], axis=-1))
+        x = buf[..., :H * P].unflatten(-1, (H, P))
+        B = buf[..., H * P:H * P + G * N].unflatten(-1, (G, N))
+        C = buf[..., H * P + G * N:].unflatten(-1, (G, N))
+    else:
+        x, B, C = up(inp.x), up(inp.B), up(inp.C)
+    dt, z = up(inp.dt), up(inp.z)
+    A, bias = up(inp.A, torch.float32), up(inp.dt_bias, torch.float32)
+    D = up(inp.D, torch.float32)
+    cu = (torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
+          if inp.cu_seqlens is not None else None)
+
+    prob = ssd.problem_from(x, B, w.chunk_size, cu_seqlens=cu, state_dtype=sdt)
+    algo = args.algo
+    if algo == "auto":
+        try:
+            prob.workspace_size("fused")
+            algo = "fused"
+        except ssd.SSDError:
+            algo = "staged"
+    K = prob.num_chunks()
+    out = torch.empty(x.shape, dtype=odt, device=dev)
+    nseq = prob.nseq if prob.packed else prob.batch
+    fin = torch.empty((nseq, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(prob.workspace_size(algo), 1), dtype=torch.uint8, device=dev)
+
+    # stage buffers for the instrumented staged step (same kernels ssd_forward launches)
+    cs = torch.empty((K, w.nheads, w.chunk_size), dtype=torch.float32, device=dev)
+    cb = torch.empty((K, w.ngroups, w.chunk_size, w.chunk_size), dtype=torch.float32, device=dev)
+    st = torch.empty((K, w.nheads, w.headdim, w.dstate), dtype=sdt, device=dev)
+    if prob.packed:
+        prob.chunk_meta = torch.empty(prob.meta_len(), dtype=torch.int32, device=dev)
+
+    if algo == "staged":
+        names = (["varlen_meta"] if prob.packed else []) + [
+            "chunk_cumsum", "bmm_chunk", "chunk_state", "state_passing", "chunk_scan"]
+
+        def launches():
+            if prob.packed:
+                yield "varlen_meta", lambda: ssd.ssd_varlen_chunk_meta(prob, prob.chunk_meta)
+            yield "chunk_cumsum", lambda: ssd.ssd_chunk_cumsum(prob, dt, A, bias, cs)
+            yield "bmm_chunk", lambda: ssd.ssd_bmm_chunk(prob, C, B, cb)
+            yield "chunk_state", lambda: ssd.ssd_chunk_state(prob, x, B, cs, st)
+            yield "state_passing", lambda: ssd.ssd_state_passing(prob, st, cs, None, st, fin)
+            yield "chunk_scan", lambda: ssd.ssd_chunk_scan(prob, cb, x, C, cs, st, D, z, out)
+    else:
+        names = ["fused_fwd"]
+
+        def launches():
+            yield "fused_fwd", lambda: ssd.ssd_forward(x, B, C, dt, A, bias, D, z, None, cu,
+                                                       w.chunk_size, state_dtype=sdt, out=out,
+                                                       final_states=fin, algo="fused",
+                                                       workspace=ws)
+
+    def step(events=None):
+        for name, fn in launches():
+            if events is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                events.setdefault(name, []).append((e0, e1))
+            else:
+                fn()
+
+    # correctness smoke of the timed configuration against ssd_forward (same kernels)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_kernel_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in events[n]])) for n in names}
+    ms_per_step = wall * 1e3 / args.steps
+    tokens = w.tokens
+    value = tokens * args.steps / wall
+
+    sbytes = 4 if sdt == torch.float32 else 2
+    obytes = 2 if odt == torch.bfloat16 else 4
+    ibytes = 2 if w.dtype == "bf16" else 4
+    nb = stage_bytes(w, K, sbytes, obytes, ibytes)
+    nf = stage_flops(w, K)
+    dom = max((n for n in names if n in nb), key=lambda n: per_kernel_ms[n])
+    achieved = nb[dom] / (per_kernel_ms[dom] * 1e-3) / 1e9
+    stages = {n: {"ms": round(per_kernel_ms[n], 5),
+                  "GBps": (round(nb[n] / (per_kernel_ms[n] * 1e-3) / 1e9, 1) if n in nb else None),
+                  "hbm_frac": (round(nb[n] / (per_kernel_ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                               if n in nb else None),
+                  "mfma_TFLOPs": (round(nf[n] / (per_kernel_ms[n] * 1e-3) / 1e12, 1)
+                                  if nf.get(n) else None)}
+              for n in names}
+    roof_time_ms = sum(nb[n] for n in names if n in nb) / (HBM_PEAK_GBS * 1e9) * 1e3
+
+    result = {
+        "metric": "SSD fwd tokens/s at Nemotron-Nano dims, seq 8192 bf16; % of stage roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: SSD forward, batch {w.batch}, seq {w.seqlen}, "
+                        f"{w.nheads} heads x {w.headdim}, d_state {w.dstate}, "
+                        f"{w.ngroups} groups, chunk {w.chunk_size}"
+                        + (f", {w.nseq} packed sequences" if w.nseq else "")
+                        + (", D" if w.has_D else "") + (", z gate" if w.has_z else ""),
+            "global_batch": w.batch, "seq_len": w.seqlen, "parallelism": "none (1 GPU)",
+            "algo": algo, "state_dtype": args.state_dtype, "out_dtype": args.out_dtype,
+            "layout": args.layout,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": dom,
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": nb[dom],
+            "avg_launch_ms": round(per_kernel_ms[dom], 5),
+        },
+        "stages": stages,
+        "path_roofline_frac": round(roof_time_ms / ms_per_step, 4),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_repeats)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
