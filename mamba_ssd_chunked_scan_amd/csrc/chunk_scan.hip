@@ -106,7 +106,7 @@ __host__ __device__ inline ScanLayout scan_layout(int C, int N) {
 }
 
 template <typename T, typename ST, typename TO>
-__global__ __launch_bounds__(256) void k_chunk_scan(Geo g, const float* __restrict__ CB, TArg x,
+__global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* __restrict__ CB, TArg x,
                                                     TArg Cm, const float* __restrict__ cs,
                                                     const ST* __restrict__ states,
                                                     const float* __restrict__ D, TArg z,
@@ -254,12 +254,300 @@ __global__ __launch_bounds__(256) void k_chunk_scan(Geo g, const float* __restri
   }
 }
 
+// ------------------------------------------------------------------ bf16 fast path
+//
+// Same math, organised to keep many loads in flight and LDS traffic free of
+// bank conflicts:
+//   * prologue: every thread issues all of its x and carry-in-state loads at
+//     once; x is written transposed as packed token pairs (a wave covers one
+//     8-column group and the chunk's token pairs, so every LDS write hits one
+//     row's consecutive dwords), the state as bf16 hi + lo;
+//   * the z tile for the epilogue is prefetched into registers before the
+//     matrix-core phase and consumed after it;
+//   * per 16-row l-tile, all C and CB fragment loads are issued before the
+//     matrix instructions that use them;
+//   * the D skip is added in the accumulator layout from x^T in LDS (no second
+//     read of x from memory), then y goes through LDS once for a coalesced,
+//     gated, 16-byte-row store.
+
+template <int C> struct ScanCfg {
+  static constexpr int NPAIR = C / 2;
+  static constexpr int LDW = (C + 8) / 2;                  // dwords per x^T row
+  static constexpr int XU = (8 * NPAIR + 255) / 256;       // x units (2 tokens x 8 p) / thread
+  static constexpr int ZV = (C * 8 + 255) / 256;           // epilogue 8-vectors / thread
+  static constexpr int NLT = C / 16;                       // l-tiles
+  static constexpr int LTW = NLT >= 8 ? NLT / 4 : 1;       // l-tiles per wave
+};
+
+template <typename ST>
+__host__ __device__ inline ScanLayout scan_layout_bf16(int C, int N) {
+  ScanLayout L;
+  L.ldx = (C + 8) / 2;  // dwords
+  L.ldy = 64 + 4;
+  L.off_x = 1024;
+  const size_t xbytes = 64ull * L.ldx * 4;
+  L.off_h = (L.off_x + xbytes + 15) & ~size_t(15);
+  const size_t hb = HinLds<bf16, ST>::bytes(N);
+  const size_t yb = (size_t)C * L.ldy * sizeof(float);
+  L.bytes = L.off_h + (hb > yb ? hb : yb);
+  return L;
+}
+
+template <typename ST, typename TO, int C>
+__global__ __launch_bounds__(256) void k_chunk_scan_bf16(Geo g, const float* __restrict__ CB,
+                                                         TArg x, TArg Cm,
+                                                         const float* __restrict__ cs,
+                                                         const ST* __restrict__ states,
+                                                         const float* __restrict__ D, TArg z,
+                                                         TArg out) {
+  using Cfg = ScanCfg<C>;
+  using HL = HinLds<bf16, ST>;
+  constexpr int NPAIR = Cfg::NPAIR, LDW = Cfg::LDW;
+  extern __shared__ __align__(16) char smem[];
+  const int j = blockIdx.x, h = blockIdx.y, p0 = blockIdx.z * 64;
+  Chunk c;
+  if (!get_chunk(g, j, c)) return;
+  const int N = g.N, P = g.P;
+  const int grp = h / g.hpg;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int r16 = lane % 16, q = lane / 16;
+  const ScanLayout lay = scan_layout_bf16<ST>(C, N);
+  float* s_cs = reinterpret_cast<float*>(smem);
+  uint32_t* s_xt = reinterpret_cast<uint32_t*>(smem + lay.off_x);
+  char* s_h = smem + lay.off_h;
+  float* s_y = reinterpret_cast<float*>(smem + lay.off_h);
+  const int pw = min(64, P - p0);
+
+  // ---- prologue: x pairs and the carry-in state, all loads first
+  u32x4 xr[Cfg::XU][2];
+#pragma unroll
+  for (int k = 0; k < Cfg::XU; ++k) {
+    const int u = tid + 256 * k;
+    const int grp8 = u / NPAIR, pr = u % NPAIR;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      const int s = 2 * pr + t;
+      if (u < 8 * NPAIR && s < c.len && grp8 * 8 < pw)
+        v = *reinterpret_cast<const u32x4*>(row_ptr<bf16>(x, c.b, c.t0 + s, h) + p0 + grp8 * 8);
+      xr[k][t] = v;
+    }
+  }
+  const ST* hsrc = states + ((int64_t)j * g.H + h) * P * N;
+  const int nvec_h = 64 * (N / 8);
+  constexpr int HB = 8;  // state 8-vectors per thread per batch
+  for (int v0 = 0; v0 < nvec_h; v0 += 256 * HB) {
+    f32x8 hv[HB];
+#pragma unroll
+    for (int b = 0; b < HB; ++b) {
+      const int v = v0 + tid + 256 * b;
+      const int pr = v / (N / 8), n = (v % (N / 8)) * 8;
+      f32x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (v < nvec_h && pr < pw) val = StLoad<ST>::load(hsrc + (int64_t)(p0 + pr) * N + n);
+      hv[b] = val;
+    }
+#pragma unroll
+    for (int b = 0; b < HB; ++b) {
+      const int v = v0 + tid + 256 * b;
+      if (v < nvec_h) HL::stage(s_h, hsrc, N, v / (N / 8), (v % (N / 8)) * 8, hv[b]);
+    }
+  }
+  const float* csr = cs + ((int64_t)j * g.H + h) * C;
+  for (int l = tid; l < C; l += 256) s_cs[l] = csr[l];
+#pragma unroll
+  for (int k = 0; k < Cfg::XU; ++k) {
+    const int u = tid + 256 * k;
+    if (u >= 8 * NPAIR) continue;
+    const int grp8 = u / NPAIR, pr = u % NPAIR;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const int row = grp8 * 8 + 2 * d;
+      s_xt[row * LDW + pr] = pack_lo(xr[k][0][d], xr[k][1][d]);
+      s_xt[(row + 1) * LDW + pr] = pack_hi(xr[k][0][d], xr[k][1][d]);
+    }
+  }
+  __syncthreads();
+
+  // ---- prefetch z for the epilogue (row-major 8-vectors)
+  const int vpr = pw / 8;
+  u32x4 zr[Cfg::ZV];
+  if (z.p) {
+#pragma unroll
+    for (int k = 0; k < Cfg::ZV; ++k) {
+      const int v = tid + 256 * k;
+      const int l = v / vpr, pp = (v % vpr) * 8;
+      u32x4 val = {0u, 0u, 0u, 0u};
+      if (l < c.len) val = *reinterpret_cast<const u32x4*>(row_ptr<bf16>(z, c.b, c.t0 + l, h) + p0 + pp);
+      zr[k] = val;
+    }
+  }
+
+  // ---- matrix-core phase.  All four p-tiles run even when fewer than 64
+  // columns are in range: x^T and state rows past P were staged as zeros.
+  f32x4 acc[Cfg::LTW][4];
+#pragma unroll
+  for (int a = 0; a < Cfg::LTW; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = zero4();
+  const float* cbm = CB + ((int64_t)j * g.G + grp) * C * C;
+  const int nkb = (N + 31) / 32;
+
+#pragma unroll
+  for (int u = 0; u < Cfg::LTW; ++u) {
+    const int lt = (u / 2) * 8 + ((u & 1) ? 7 - wave : wave);
+    if (lt >= Cfg::NLT) continue;
+    const int lrow = lt * 16 + r16;
+    const bool lok = lrow < c.len;
+    const bf16* crow = row_ptr<bf16>(Cm, c.b, c.t0 + (lok ? lrow : 0), grp);
+    // Y_off: C_l . Hin^T, four k-blocks of 32 per batch.  Every matrix
+    // instruction runs unconditionally; operands past N or past the chunk are
+    // zero, so no accumulator is ever updated under a data-dependent branch.
+    for (int k0 = 0; k0 < nkb; k0 += 4) {
+      FragBF cf[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k = (k0 + kk) * 32 + q * 8;
+        const bool ok = lok && k < N;
+        const FragBF v = Prec<bf16>::load_exact(crow + (k < N ? k : 0));
+        cf[kk] = ok ? v : Prec<bf16>::zero_exact();
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k = (k0 + kk) * 32 + q * 8;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          auto b = HL::frag(s_h, N, pt * 16 + r16, k < N ? k : 0);
+          mma(acc[u][pt], cf[kk], b);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp(s_cs[lt * 16 + q * 4 + i]);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) acc[u][pt][i] *= e;
+    }
+    // Y_diag: (L o CB) x over s <= l, four k-blocks per batch.  The CB tile is
+    // allocated for every (l, s) of the chunk, so its loads need no guard; the
+    // causal/length mask is a select applied after the exponential (the
+    // exponent itself is zeroed where masked, so exp never overflows).
+    const float csl = s_cs[lrow];
+    const int nkd = (lt * 16 + 16 + 31) / 32;
+    for (int k0 = 0; k0 < nkd; k0 += 4) {
+      f32x8 cb[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int kb = min(k0 + kk, nkd - 1);
+        cb[kk] = Vec8<float>::load(cbm + (int64_t)lrow * C + kb * 32 + q * 8);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (k0 + kk >= nkd) break;
+        const int s0 = (k0 + kk) * 32 + q * 8;
+        const f32x8 csv = Vec8<float>::load(s_cs + s0);
+        f32x8 m;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int s = s0 + e;
+          const bool keep = lok && (s <= lrow) && (s < c.len);
+          const float ex = fast_exp(keep ? csl - csv[e] : 0.0f);
+          m[e] = keep ? ex * cb[kk][e] : 0.0f;
+        }
+        const FragSplit mf = split_f32x8(m);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          FragBF xb;
+          xb.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                &s_xt[(pt * 16 + r16) * LDW + s0 / 2]));
+          mma(acc[u][pt], mf, xb);
+        }
+      }
+    }
+  }
+
+  // ---- D skip in the accumulator layout, from x^T in LDS
+  if (D) {
+    const float Dh = D[h];
+#pragma unroll
+    for (int u = 0; u < Cfg::LTW; ++u) {
+      const int lt = (u / 2) * 8 + ((u & 1) ? 7 - wave : wave);
+      if (lt >= Cfg::NLT) continue;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const u32x2 xv = *reinterpret_cast<const u32x2*>(
+            &s_xt[(pt * 16 + r16) * LDW + (lt * 16 + q * 4) / 2]);
+        acc[u][pt][0] += Dh * bf16_lo_f32(xv[0]);
+        acc[u][pt][1] += Dh * bf16_hi_f32(xv[0]);
+        acc[u][pt][2] += Dh * bf16_lo_f32(xv[1]);
+        acc[u][pt][3] += Dh * bf16_hi_f32(xv[1]);
+      }
+    }
+  }
+  __syncthreads();  // all waves are done with the state; reuse its area for y
+#pragma unroll
+  for (int u = 0; u < Cfg::LTW; ++u) {
+    const int lt = (u / 2) * 8 + ((u & 1) ? 7 - wave : wave);
+    if (lt >= Cfg::NLT) continue;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s_y[(lt * 16 + q * 4 + i) * lay.ldy + pt * 16 + r16] = acc[u][pt][i];
+    }
+  }
+  __syncthreads();
+
+  // ---- epilogue: gate and store, coalesced 8-element rows
+#pragma unroll
+  for (int k = 0; k < Cfg::ZV; ++k) {
+    const int v = tid + 256 * k;
+    const int l = v / vpr, pp = (v % vpr) * 8;
+    if (l >= c.len) continue;
+    f32x8 y = Vec8<float>::load(s_y + l * lay.ldy + pp);
+    if (z.p) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        y[2 * d] *= silu(bf16_lo_f32(zr[k][d]));
+        y[2 * d + 1] *= silu(bf16_hi_f32(zr[k][d]));
+      }
+    }
+    Vec8<TO>::store(row_ptr_mut<TO>(out, c.b, c.t0 + l, h) + p0 + pp, y);
+  }
+}
+
+template <typename ST, typename TO>
+static hipError_t launch_scan_bf16(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
+                                   const void* states, const float* D, TArg z, TArg out,
+                                   hipStream_t s) {
+  const ScanLayout lay = scan_layout_bf16<ST>(g.C, g.N);
+  const void* kern;
+  switch (g.C) {
+    case 32: kern = (const void*)k_chunk_scan_bf16<ST, TO, 32>; break;
+    case 64: kern = (const void*)k_chunk_scan_bf16<ST, TO, 64>; break;
+    case 128: kern = (const void*)k_chunk_scan_bf16<ST, TO, 128>; break;
+    default: kern = (const void*)k_chunk_scan_bf16<ST, TO, 256>; break;
+  }
+  if (lay.bytes > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)lay.bytes);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(g.K, g.H, (g.P + 63) / 64);
+  const ST* st = (const ST*)states;
+  switch (g.C) {
+    case 32: hipLaunchKernelGGL((k_chunk_scan_bf16<ST, TO, 32>), grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, st, D, z, out); break;
+    case 64: hipLaunchKernelGGL((k_chunk_scan_bf16<ST, TO, 64>), grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, st, D, z, out); break;
+    case 128: hipLaunchKernelGGL((k_chunk_scan_bf16<ST, TO, 128>), grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, st, D, z, out); break;
+    default: hipLaunchKernelGGL((k_chunk_scan_bf16<ST, TO, 256>), grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, st, D, z, out); break;
+  }
+  return hipGetLastError();
+}
+
 template <typename T, typename ST, typename TO>
 static hipError_t launch_scan_t(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
                                 const void* states, const float* D, TArg z, TArg out,
                                 hipStream_t s) {
   const ScanLayout lay = scan_layout<T, ST>(g.C, g.N);
-  auto kern = k_chunk_scan<T, ST, TO>;
+  auto kern = k_chunk_scan_generic<T, ST, TO>;
   if (lay.bytes > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.bytes);
@@ -277,10 +565,10 @@ hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int 
   if (g.K == 0) return hipSuccess;
   const bool ib = in_dtype == DT_BF16, sb = st_dtype == DT_BF16, ob = out_dtype == DT_BF16;
   if (ib) {
-    if (sb) return ob ? launch_scan_t<bf16, bf16, bf16>(g, CB, x, C, cs, states, D, z, out, s)
-                      : launch_scan_t<bf16, bf16, float>(g, CB, x, C, cs, states, D, z, out, s);
-    return ob ? launch_scan_t<bf16, float, bf16>(g, CB, x, C, cs, states, D, z, out, s)
-              : launch_scan_t<bf16, float, float>(g, CB, x, C, cs, states, D, z, out, s);
+    if (sb) return ob ? launch_scan_bf16<bf16, bf16>(g, CB, x, C, cs, states, D, z, out, s)
+                      : launch_scan_bf16<bf16, float>(g, CB, x, C, cs, states, D, z, out, s);
+    return ob ? launch_scan_bf16<float, bf16>(g, CB, x, C, cs, states, D, z, out, s)
+              : launch_scan_bf16<float, float>(g, CB, x, C, cs, states, D, z, out, s);
   }
   if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, states, D, z, out, s)
                     : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, states, D, z, out, s);

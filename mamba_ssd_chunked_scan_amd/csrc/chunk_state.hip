@@ -9,200 +9,307 @@
 // page, the decay weight is folded into x rather than B: x is the per-head
 // operand, B is shared by the heads of a group.
 //
-// Matrix-core formulation: S (P x N) = Xw^T (P x s) * B (s x N) with the
-// reduction over tokens s.  Tokens are the strided axis in memory, so each
-// 32-token slab of x and B is staged through LDS transposed ([p][s] and [n][s],
-// s contiguous), the weighted x split into bf16 hi + lo on the way in.  One
-// workgroup covers up to 64 (p) x 128 (n) of one (chunk, head): wave w owns
-// p-tile w and all n-tiles, accumulating 8 16x16 fp32 tiles in registers.
+// Matrix-core formulation: S (P x N) = Xw^T (P x s) * B (s x N), reducing over
+// tokens s.  Tokens are the strided axis in memory while the 16x16x32 MFMA
+// wants eight consecutive tokens per lane, so x and B pass through LDS
+// transposed ([p][s], [n][s]).
+//
+// bf16 inputs (the fast path).  One workgroup covers 64 (p) x 128 (n) of one
+// (chunk, head); wave w owns p-tile w and all eight n-tiles (8 fp32 16x16
+// accumulators).  Tokens are processed in slabs of up to 64 (~38 KB of LDS,
+// four workgroups per CU):
+//   * every load of a slab is issued at once into registers (2 x 16 B of x and
+//     4 x 16 B of B per thread), and the next slab's loads are issued before the
+//     current slab's MFMAs, so a workgroup waits on memory about once per slab;
+//   * the transpose is written as packed token pairs: a thread holds tokens
+//     (s, s+1) for 8 columns and writes 8 dwords (x[s][c], x[s+1][c]); half a
+//     wave covers one 8-column group's 32 token pairs, so each LDS write
+//     instruction touches two runs of 32 consecutive dwords;
+//   * the weighted x is split into bf16 hi + lo on the way in;
+//   * the finished tile goes through LDS so the state is stored in coalesced
+//     16-byte rows.
+// fp32 inputs use a simpler slab loop with fp32 MFMA (small problems only).
 #include "kernels.hpp"
 
 namespace ssd {
 
-constexpr int kSlab = 32;
+// ------------------------------------------------------------------ bf16 path
 
-template <typename T> struct StateLds;
-template <> struct StateLds<bf16> {
-  static constexpr int LD = kSlab + 8;  // 80-byte rows
-  bf16 xh[64 * LD];
-  bf16 xl[64 * LD];
-  bf16 bt[128 * LD];
-  float w[256];
-};
-template <> struct StateLds<float> {
-  static constexpr int LD = kSlab + 4;  // 144-byte rows
-  float x[64 * LD];
-  float bt[128 * LD];
-  float w[256];
+template <int C> struct StateCfg {
+  static constexpr int SL = C < 64 ? C : 64;       // tokens per slab
+  static constexpr int NSL = C / SL;
+  static constexpr int NPAIR = SL / 2;
+  static constexpr int LD = SL + 8;                // bf16 elements per transposed row
+  static constexpr int LDW = LD / 2;               // the same in dwords
+  static constexpr int XU = (8 * NPAIR + 255) / 256;   // x units (2 tokens x 8 p) per thread
+  static constexpr int BU = (16 * NPAIR + 255) / 256;  // B units (2 tokens x 8 n) per thread
+  static constexpr int LDS_T = (2 * 64 + 128) * LDW;   // dwords: x hi, x lo, B
+  static constexpr int LDS_S = 64 * (128 + 4);         // floats: output tile
+  static constexpr int LDS = LDS_T > LDS_S ? LDS_T : LDS_S;
 };
 
-// Stage tokens [s0, s0 + 32) of x (weighted, transposed) and B (transposed).
-__device__ __forceinline__ void stage_slab(StateLds<bf16>& L, const Geo& g, const Chunk& c,
-                                           const TArg& x, const TArg& B, int h, int grp, int p0,
-                                           int n0, int s0) {
-  constexpr int LD = StateLds<bf16>::LD;
-  const int tid = threadIdx.x;
-  {  // x: 32 tokens x 64 p = 256 vectors of 8
-    const int s = tid / 8, pp = (tid % 8) * 8;
-    f32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int p = p0 + pp;
-    if (s0 + s < c.len && p < g.P) {
-      v = Vec8<bf16>::load(row_ptr<bf16>(x, c.b, c.t0 + s0 + s, h) + p);
-      const float ws = L.w[s0 + s];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] *= ws;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bf16 hi = (bf16)v[i];
-      L.xh[(pp + i) * LD + s] = hi;
-      L.xl[(pp + i) * LD + s] = (bf16)(v[i] - (float)hi);
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {  // B: 32 tokens x 128 n = 512 vectors of 8
-    const int v8 = tid + r * 256;
-    const int s = v8 / 16, nn = (v8 % 16) * 8;
-    const int n = n0 + nn;
-    bf16x8 v;
-    if (s0 + s < c.len && n < g.N) {
-      v = *reinterpret_cast<const bf16x8*>(row_ptr<bf16>(B, c.b, c.t0 + s0 + s, grp) + n);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = (bf16)0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) L.bt[(nn + i) * LD + s] = v[i];
-  }
-}
+template <typename ST, int C>
+__global__ __launch_bounds__(256, 4) void k_chunk_state_bf16(Geo g, TArg x, TArg B,
+                                                          const float* __restrict__ cs,
+                                                          ST* __restrict__ states) {
+  using Cfg = StateCfg<C>;
+  constexpr int SL = Cfg::SL, NPAIR = Cfg::NPAIR, LDW = Cfg::LDW, XU = Cfg::XU, BU = Cfg::BU;
+  __shared__ __align__(16) uint32_t lds[Cfg::LDS];
+  __shared__ float w[C];
+  uint32_t* xh = lds;
+  uint32_t* xl = lds + 64 * LDW;
+  uint32_t* bt = lds + 128 * LDW;
 
-__device__ __forceinline__ void stage_slab(StateLds<float>& L, const Geo& g, const Chunk& c,
-                                           const TArg& x, const TArg& B, int h, int grp, int p0,
-                                           int n0, int s0) {
-  constexpr int LD = StateLds<float>::LD;
-  const int tid = threadIdx.x;
-  {
-    const int s = tid / 8, pp = (tid % 8) * 8;
-    f32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    const int p = p0 + pp;
-    if (s0 + s < c.len && p < g.P) {
-      v = Vec8<float>::load(row_ptr<float>(x, c.b, c.t0 + s0 + s, h) + p);
-      const float ws = L.w[s0 + s];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] *= ws;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) L.x[(pp + i) * LD + s] = v[i];
-  }
-#pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int v8 = tid + r * 256;
-    const int s = v8 / 16, nn = (v8 % 16) * 8;
-    const int n = n0 + nn;
-    f32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (s0 + s < c.len && n < g.N) v = Vec8<float>::load(row_ptr<float>(B, c.b, c.t0 + s0 + s, grp) + n);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) L.bt[(nn + i) * LD + s] = v[i];
-  }
-}
-
-__device__ __forceinline__ FragSplit frag_a(const StateLds<bf16>& L, int p, int q) {
-  constexpr int LD = StateLds<bf16>::LD;
-  FragSplit f;
-  f.hi = *reinterpret_cast<const bf16x8*>(&L.xh[p * LD + q * 8]);
-  f.lo = *reinterpret_cast<const bf16x8*>(&L.xl[p * LD + q * 8]);
-  return f;
-}
-__device__ __forceinline__ FragBF frag_b(const StateLds<bf16>& L, int n, int q) {
-  constexpr int LD = StateLds<bf16>::LD;
-  FragBF f;
-  f.v = *reinterpret_cast<const bf16x8*>(&L.bt[n * LD + q * 8]);
-  return f;
-}
-__device__ __forceinline__ FragF32 frag_a(const StateLds<float>& L, int p, int q) {
-  constexpr int LD = StateLds<float>::LD;
-  FragF32 f;
-  f.v = Vec8<float>::load(&L.x[p * LD + q * 8]);
-  return f;
-}
-__device__ __forceinline__ FragF32 frag_b(const StateLds<float>& L, int n, int q) {
-  constexpr int LD = StateLds<float>::LD;
-  FragF32 f;
-  f.v = Vec8<float>::load(&L.bt[n * LD + q * 8]);
-  return f;
-}
-
-template <typename T, typename ST>
-__global__ __launch_bounds__(256) void k_chunk_state(Geo g, TArg x, TArg B,
-                                                     const float* __restrict__ cs,
-                                                     ST* __restrict__ states) {
-  __shared__ StateLds<T> L;
   const int j = blockIdx.x, h = blockIdx.y;
   Chunk c;
   if (!get_chunk(g, j, c)) return;
   const int nzn = (g.N + 127) / 128;
   const int p0 = (blockIdx.z / nzn) * 64, n0 = (blockIdx.z % nzn) * 128;
   const int grp = h / g.hpg;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int r16 = lane % 16, q = lane / 16;
 
-  const float* csr = cs + ((int64_t)j * g.H + h) * g.C;
-  const float last = csr[c.len - 1];
-  for (int s = threadIdx.x; s < g.C; s += blockDim.x)
-    L.w[s] = s < c.len ? fast_exp(last - csr[s]) : 0.0f;
+  u32x4 xr[XU][2], br[BU][2];
+  auto load_slab = [&](int sl) {
+#pragma unroll
+    for (int k = 0; k < XU; ++k) {
+      const int u = tid + 256 * k;
+      const int grp8 = u / NPAIR, pr = u % NPAIR;
+      const int s = sl * SL + 2 * pr, p = p0 + grp8 * 8;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (u < 8 * NPAIR && s + t < c.len && p < g.P)
+          v = *reinterpret_cast<const u32x4*>(row_ptr<bf16>(x, c.b, c.t0 + s + t, h) + p);
+        xr[k][t] = v;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < BU; ++k) {
+      const int u = tid + 256 * k;
+      const int grp8 = u / NPAIR, pr = u % NPAIR;
+      const int s = sl * SL + 2 * pr, n = n0 + grp8 * 8;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (u < 16 * NPAIR && s + t < c.len && n < g.N)
+          v = *reinterpret_cast<const u32x4*>(row_ptr<bf16>(B, c.b, c.t0 + s + t, grp) + n);
+        br[k][t] = v;
+      }
+    }
+  };
+  auto write_slab = [&](int sl) {
+#pragma unroll
+    for (int k = 0; k < XU; ++k) {
+      const int u = tid + 256 * k;
+      if (u >= 8 * NPAIR) continue;
+      const int grp8 = u / NPAIR, pr = u % NPAIR;
+      const float wa = w[sl * SL + 2 * pr], wb = w[sl * SL + 2 * pr + 1];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t ua = xr[k][0][d], ub = xr[k][1][d];
+          const float fa = __uint_as_float(half ? (ua & 0xffff0000u) : (ua << 16)) * wa;
+          const float fb = __uint_as_float(half ? (ub & 0xffff0000u) : (ub << 16)) * wb;
+          const bf16 ha = (bf16)fa, hb = (bf16)fb;
+          const bf16 la = (bf16)(fa - (float)ha), lb = (bf16)(fb - (float)hb);
+          const int row = grp8 * 8 + 2 * d + half;
+          xh[row * LDW + pr] = pack2(ha, hb);
+          xl[row * LDW + pr] = pack2(la, lb);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < BU; ++k) {
+      const int u = tid + 256 * k;
+      if (u >= 16 * NPAIR) continue;
+      const int grp8 = u / NPAIR, pr = u % NPAIR;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        const int row = grp8 * 8 + 2 * d;
+        bt[row * LDW + pr] = pack_lo(br[k][0][d], br[k][1][d]);
+        bt[(row + 1) * LDW + pr] = pack_hi(br[k][0][d], br[k][1][d]);
+      }
+    }
+  };
+
+  load_slab(0);
+  {
+    const float* csr = cs + ((int64_t)j * g.H + h) * g.C;
+    const float last = csr[c.len - 1];
+    for (int s = tid; s < C; s += 256) w[s] = s < c.len ? fast_exp(last - csr[s]) : 0.0f;
+  }
   __syncthreads();
 
-  const int pt0 = p0 + wave * 16;       // this wave's p-tile
+  const int pt0 = p0 + wave * 16;
   const bool active = pt0 < g.P;
   const int ntn = min(8, (g.N - n0) / 16);
   f32x4 acc[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) acc[t] = zero4();
 
-  for (int s0 = 0; s0 < c.len; s0 += kSlab) {
-    stage_slab(L, g, c, x, B, h, grp, p0, n0, s0);
+#pragma unroll
+  for (int sl = 0; sl < Cfg::NSL; ++sl) {
+    if (sl * SL >= c.len) break;
+    write_slab(sl);
+    __syncthreads();
+    if (sl + 1 < Cfg::NSL && (sl + 1) * SL < c.len) load_slab(sl + 1);
+    if (active) {
+#pragma unroll
+      for (int kb = 0; kb < SL / 32; ++kb) {
+        const int off = kb * 16 + q * 4;  // dword offset of this lane's 8 tokens
+        FragSplit a;
+        a.hi = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                              &xh[(wave * 16 + r16) * LDW + off]));
+        a.lo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                              &xl[(wave * 16 + r16) * LDW + off]));
+        // all eight n-tiles run unconditionally: LDS rows past N hold zeros,
+        // and a data-dependent guard around the matrix instructions would make
+        // the compiler keep conditional copies of every accumulator
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          FragBF b;
+          b.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                               &bt[(t * 16 + r16) * LDW + off]));
+          mma(acc[t], a, b);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // stage the 64 x 128 tile through LDS, then coalesced 16-byte stores
+  float* so = reinterpret_cast<float*>(lds);
+  constexpr int LDO = 128 + 4;
+  if (active) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      if (t >= ntn) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) so[(wave * 16 + q * 4 + i) * LDO + t * 16 + r16] = acc[t][i];
+    }
+  }
+  __syncthreads();
+  const int prows = min(64, g.P - p0), ncols = ntn * 16;
+  const int vpr = ncols / 8;
+  ST* out = states + ((int64_t)j * g.H + h) * g.P * g.N;
+  for (int v = tid; v < prows * vpr; v += 256) {
+    const int pr = v / vpr, nn = (v % vpr) * 8;
+    const f32x8 val = Vec8<float>::load(so + pr * LDO + nn);
+    Vec8<ST>::store(out + (int64_t)(p0 + pr) * g.N + n0 + nn, val);
+  }
+}
+
+// ------------------------------------------------------------------ fp32 path
+
+constexpr int kSlabF = 32;
+struct StateLdsF32 {
+  static constexpr int LD = kSlabF + 4;  // 144-byte rows
+  float x[64 * LD];
+  float bt[128 * LD];
+  float w[256];
+};
+
+__global__ __launch_bounds__(256) void k_chunk_state_f32(Geo g, TArg x, TArg B,
+                                                         const float* __restrict__ cs,
+                                                         float* __restrict__ states_f,
+                                                         bf16* __restrict__ states_b) {
+  __shared__ StateLdsF32 L;
+  constexpr int LD = StateLdsF32::LD;
+  const int j = blockIdx.x, h = blockIdx.y;
+  Chunk c;
+  if (!get_chunk(g, j, c)) return;
+  const int nzn = (g.N + 127) / 128;
+  const int p0 = (blockIdx.z / nzn) * 64, n0 = (blockIdx.z % nzn) * 128;
+  const int grp = h / g.hpg;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int r16 = lane % 16, q = lane / 16;
+  const float* csr = cs + ((int64_t)j * g.H + h) * g.C;
+  const float last = csr[c.len - 1];
+  for (int s = tid; s < g.C; s += blockDim.x) L.w[s] = s < c.len ? fast_exp(last - csr[s]) : 0.0f;
+  __syncthreads();
+  const int pt0 = p0 + wave * 16;
+  const bool active = pt0 < g.P;
+  const int ntn = min(8, (g.N - n0) / 16);
+  f32x4 acc[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) acc[t] = zero4();
+  for (int s0 = 0; s0 < c.len; s0 += kSlabF) {
+    {
+      const int s = tid / 8, pp = (tid % 8) * 8, p = p0 + pp;
+      f32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (s0 + s < c.len && p < g.P) {
+        v = Vec8<float>::load(row_ptr<float>(x, c.b, c.t0 + s0 + s, h) + p);
+        const float ws = L.w[s0 + s];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] *= ws;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) L.x[(pp + i) * LD + s] = v[i];
+    }
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int v8 = tid + r * 256;
+      const int s = v8 / 16, nn = (v8 % 16) * 8, n = n0 + nn;
+      f32x8 v = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (s0 + s < c.len && n < g.N) v = Vec8<float>::load(row_ptr<float>(B, c.b, c.t0 + s0 + s, grp) + n);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) L.bt[(nn + i) * LD + s] = v[i];
+    }
     __syncthreads();
     if (active) {
-      const auto a = frag_a(L, wave * 16 + r16, q);
+      FragF32 a;
+      a.v = Vec8<float>::load(&L.x[(wave * 16 + r16) * LD + q * 8]);
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-        if (t < ntn) mma(acc[t], a, frag_b(L, t * 16 + r16, q));
+      for (int t = 0; t < 8; ++t) {
+        if (t < ntn) {
+          FragF32 b;
+          b.v = Vec8<float>::load(&L.bt[(t * 16 + r16) * LD + q * 8]);
+          mma(acc[t], a, b);
+        }
+      }
     }
     __syncthreads();
   }
   if (!active) return;
-  ST* out = states + ((int64_t)j * g.H + h) * g.P * g.N;
+  const int64_t base = ((int64_t)j * g.H + h) * g.P * g.N;
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     if (t >= ntn) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int p = pt0 + q * 4 + i;
-      const int n = n0 + t * 16 + r16;
-      out[(int64_t)p * g.N + n] = from_f32<ST>(acc[t][i]);
+      const int64_t o = base + (int64_t)(pt0 + q * 4 + i) * g.N + n0 + t * 16 + r16;
+      if (states_f) states_f[o] = acc[t][i];
+      else states_b[o] = (bf16)acc[t][i];
     }
   }
+}
+
+template <typename ST>
+static hipError_t launch_state_bf16(const Geo& g, TArg x, TArg B, const float* cs, ST* st,
+                                    hipStream_t s) {
+  dim3 grid(g.K, g.H, ((g.P + 63) / 64) * ((g.N + 127) / 128));
+  switch (g.C) {
+    case 32: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 32>), grid, dim3(256), 0, s, g, x, B, cs, st); break;
+    case 64: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 64>), grid, dim3(256), 0, s, g, x, B, cs, st); break;
+    case 128: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 128>), grid, dim3(256), 0, s, g, x, B, cs, st); break;
+    default: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 256>), grid, dim3(256), 0, s, g, x, B, cs, st); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_chunk_state(const Geo& g, TArg x, TArg B, int in_dtype, const float* cs,
                               void* states, int st_dtype, hipStream_t s) {
   if (g.K == 0) return hipSuccess;
-  dim3 grid(g.K, g.H, ((g.P + 63) / 64) * ((g.N + 127) / 128));
   if (in_dtype == DT_BF16) {
-    if (st_dtype == DT_BF16)
-      hipLaunchKernelGGL((k_chunk_state<bf16, bf16>), grid, dim3(256), 0, s, g, x, B, cs,
-                         (bf16*)states);
-    else
-      hipLaunchKernelGGL((k_chunk_state<bf16, float>), grid, dim3(256), 0, s, g, x, B, cs,
-                         (float*)states);
-  } else {
-    if (st_dtype == DT_BF16)
-      hipLaunchKernelGGL((k_chunk_state<float, bf16>), grid, dim3(256), 0, s, g, x, B, cs,
-                         (bf16*)states);
-    else
-      hipLaunchKernelGGL((k_chunk_state<float, float>), grid, dim3(256), 0, s, g, x, B, cs,
-                         (float*)states);
+    if (st_dtype == DT_BF16) return launch_state_bf16<bf16>(g, x, B, cs, (bf16*)states, s);
+    return launch_state_bf16<float>(g, x, B, cs, (float*)states, s);
   }
+  dim3 grid(g.K, g.H, ((g.P + 63) / 64) * ((g.N + 127) / 128));
+  hipLaunchKernelGGL(k_chunk_state_f32, grid, dim3(256), 0, s, g, x, B, cs,
+                     st_dtype == DT_BF16 ? nullptr : (float*)states,
+                     st_dtype == DT_BF16 ? (bf16*)states : nullptr);
   return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@ __device__ __forceinline__ float softplus_f32(float u) {
   return u > 20.0f ? u : log1pf(__expf(u));
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // ------------------------------------------------------------------ vectors
 
@@ -91,6 +91,24 @@ template <> struct Vec8<float> {
     *reinterpret_cast<f32x4*>(p + 4) = b;
   }
 };
+
+// Packed bf16 pairs: a dword holds two bf16, element 2i in the low half.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {  // (a.lo16, b.lo16)
+  return (a & 0xffffu) | (b << 16);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {  // (a.hi16, b.hi16)
+  return (a >> 16) | (b & 0xffff0000u);
+}
+__device__ __forceinline__ uint32_t bf16_bits(bf16 v) {
+  return (uint32_t)__builtin_bit_cast(unsigned short, v);
+}
+__device__ __forceinline__ uint32_t pack2(bf16 a, bf16 b) {
+  return bf16_bits(a) | (bf16_bits(b) << 16);
+}
+__device__ __forceinline__ float bf16_lo_f32(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t d) { return __uint_as_float(d & 0xffff0000u); }
 
 // ------------------------------------------------------------------ fragments
 
