@@ -9,7 +9,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/ssd.h"
+#include "ssd.h"
 #include "kernels.hpp"
 
 namespace {
@@ -228,8 +228,6 @@ ssd_status ssd_workspace_size(const ssd_problem* p, ssd_algo algo, size_t* bytes
   if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
   if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
-  if (algo == SSD_ALGO_FUSED)
-    return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED is not available in this build");
   *bytes = staged_layout(p).total;
   return ok();
 }
@@ -374,9 +372,10 @@ ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* 
     return fail(SSD_ERR_DTYPE, "x, B and C must share a dtype");
   if (a->z.data && a->z.dtype != a->x.dtype) return fail(SSD_ERR_DTYPE, "z must have x's dtype");
   if (!a->A) return fail(SSD_ERR_NULL, "A is NULL");
-  if (algo == SSD_ALGO_FUSED)
-    return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED is not available in this build");
-  if (algo != SSD_ALGO_STAGED) return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
+  if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED)
+    return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
+  if (algo == SSD_ALGO_FUSED && has_tokens(p) && a->x.dtype != SSD_BF16)
+    return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED takes bf16 x, B, C (use SSD_ALGO_STAGED)");
   const StagedWs w = staged_layout(p);
   if (w.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < w.total)
@@ -397,11 +396,17 @@ ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* 
                                    stream),
           "chunk_cumsum launch");
   SSD_HIP(ssd::launch_bmm_chunk(g, targ(a->C), targ(a->B), in, cb, stream), "bmm_chunk launch");
-  SSD_HIP(ssd::launch_chunk_state(g, targ(a->x), targ(a->B), in, cs, st, sd, stream),
-          "chunk_state launch");
-  SSD_HIP(ssd::launch_state_passing(g, st, sd, cs, a->initial_states, st, a->final_states,
-                                    stream),
-          "state_passing launch");
+  if (algo == SSD_ALGO_FUSED) {
+    SSD_HIP(ssd::launch_state_scan(g, targ(a->x), targ(a->B), cs, a->initial_states, st, sd,
+                                   a->final_states, stream),
+            "state_scan launch");
+  } else {
+    SSD_HIP(ssd::launch_chunk_state(g, targ(a->x), targ(a->B), in, cs, st, sd, stream),
+            "chunk_state launch");
+    SSD_HIP(ssd::launch_state_passing(g, st, sd, cs, a->initial_states, st, a->final_states,
+                                      stream),
+            "state_passing launch");
+  }
   SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, st, sd, a->D, targ(a->z),
                                  targ(a->out), dcode(a->out.dtype), stream),
           "chunk_scan launch");

@@ -293,8 +293,15 @@ __host__ __device__ inline ScanLayout scan_layout_bf16(int C, int N) {
   return L;
 }
 
+// Fragments one wave needs for one 16-row l-tile: the first four k-blocks of
+// C (Y_off A operand) and of the CB row block (Y_diag).  Loaded ahead of use.
+struct ScanFrags {
+  u32x4 cf[4];
+  f32x8 cb[4];
+};
+
 template <typename ST, typename TO, int C>
-__global__ __launch_bounds__(256) void k_chunk_scan_bf16(Geo g, const float* __restrict__ CB,
+__global__ __launch_bounds__(256, C <= 128 ? 3 : 2) void k_chunk_scan_bf16(Geo g, const float* __restrict__ CB,
                                                          TArg x, TArg Cm,
                                                          const float* __restrict__ cs,
                                                          const ST* __restrict__ states,
@@ -317,22 +324,44 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bf16(Geo g, const float* __r
   char* s_h = smem + lay.off_h;
   float* s_y = reinterpret_cast<float*>(smem + lay.off_h);
   const int pw = min(64, P - p0);
+  const float* cbm = CB + ((int64_t)j * g.G + grp) * C * C;
+  const int nkb = (N + 31) / 32;
 
-  // ---- prologue: x pairs and the carry-in state, all loads first
+  // l-tile of the wave's u-th slot: w and 7 - w of every group of eight
+  auto lt_of = [&](int u) { return (u / 2) * 8 + ((u & 1) ? 7 - wave : wave); };
+  // Loads for one l-tile, issued before they are needed.  Addresses are always
+  // inside the tensors (rows clamped into the chunk, columns into N, the CB tile
+  // covers every (l, s) of the chunk); values that must not count are zeroed
+  // where they are consumed.
+  auto load_frags = [&](int u, ScanFrags& f) {
+    const int lt = lt_of(u);
+    const int lrow = lt * 16 + r16;
+    const int nkd = (lt * 16 + 16 + 31) / 32;  // k-blocks the causal row block needs
+    const bf16* crow = row_ptr<bf16>(Cm, c.b, c.t0 + min(lrow, c.len - 1), grp);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const int k = min(kk * 32 + q * 8, N - 8);
+      f.cf[kk] = *reinterpret_cast<const u32x4*>(crow + k);
+      // past the causal block: repeat the last needed address (a cache hit)
+      f.cb[kk] = Vec8<float>::load(cbm + (int64_t)lrow * C + min(kk, nkd - 1) * 32 + q * 8);
+    }
+  };
+
+  // ---- prologue: every load of the tile's first phase at once
   u32x4 xr[Cfg::XU][2];
 #pragma unroll
   for (int k = 0; k < Cfg::XU; ++k) {
-    const int u = tid + 256 * k;
+    const int u = min(tid + 256 * k, 8 * NPAIR - 1);
     const int grp8 = u / NPAIR, pr = u % NPAIR;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      u32x4 v = {0u, 0u, 0u, 0u};
       const int s = 2 * pr + t;
-      if (u < 8 * NPAIR && s < c.len && grp8 * 8 < pw)
-        v = *reinterpret_cast<const u32x4*>(row_ptr<bf16>(x, c.b, c.t0 + s, h) + p0 + grp8 * 8);
-      xr[k][t] = v;
+      xr[k][t] = *reinterpret_cast<const u32x4*>(
+          row_ptr<bf16>(x, c.b, c.t0 + min(s, c.len - 1), h) + p0 + min(grp8 * 8, pw - 8));
     }
   }
+  ScanFrags fr;
+  if (lt_of(0) < Cfg::NLT) load_frags(0, fr);
   const ST* hsrc = states + ((int64_t)j * g.H + h) * P * N;
   const int nvec_h = 64 * (N / 8);
   constexpr int HB = 8;  // state 8-vectors per thread per batch
@@ -340,16 +369,22 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bf16(Geo g, const float* __r
     f32x8 hv[HB];
 #pragma unroll
     for (int b = 0; b < HB; ++b) {
-      const int v = v0 + tid + 256 * b;
-      const int pr = v / (N / 8), n = (v % (N / 8)) * 8;
-      f32x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (v < nvec_h && pr < pw) val = StLoad<ST>::load(hsrc + (int64_t)(p0 + pr) * N + n);
-      hv[b] = val;
+      const int v = min(v0 + tid + 256 * b, nvec_h - 1);
+      const int pr = min(v / (N / 8), pw - 1), n = (v % (N / 8)) * 8;
+      hv[b] = StLoad<ST>::load(hsrc + (int64_t)(p0 + pr) * N + n);
     }
 #pragma unroll
     for (int b = 0; b < HB; ++b) {
       const int v = v0 + tid + 256 * b;
-      if (v < nvec_h) HL::stage(s_h, hsrc, N, v / (N / 8), (v % (N / 8)) * 8, hv[b]);
+      if (v < nvec_h) {
+        const int pr = v / (N / 8);
+        f32x8 val = hv[b];
+        if (pr >= pw) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) val[e] = 0.0f;
+        }
+        HL::stage(s_h, hsrc, N, pr, (v % (N / 8)) * 8, val);
+      }
     }
   }
   const float* csr = cs + ((int64_t)j * g.H + h) * C;
@@ -359,11 +394,14 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bf16(Geo g, const float* __r
     const int u = tid + 256 * k;
     if (u >= 8 * NPAIR) continue;
     const int grp8 = u / NPAIR, pr = u % NPAIR;
+    const bool col_ok = grp8 * 8 < pw;
+    const bool k0 = col_ok && 2 * pr < c.len, k1 = col_ok && 2 * pr + 1 < c.len;
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
       const int row = grp8 * 8 + 2 * d;
-      s_xt[row * LDW + pr] = pack_lo(xr[k][0][d], xr[k][1][d]);
-      s_xt[(row + 1) * LDW + pr] = pack_hi(xr[k][0][d], xr[k][1][d]);
+      const uint32_t a = k0 ? xr[k][0][d] : 0u, b = k1 ? xr[k][1][d] : 0u;
+      s_xt[row * LDW + pr] = pack_lo(a, b);
+      s_xt[(row + 1) * LDW + pr] = pack_hi(a, b);
     }
   }
   __syncthreads();
@@ -375,10 +413,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bf16(Geo g, const float* __r
 #pragma unroll
     for (int k = 0; k < Cfg::ZV; ++k) {
       const int v = tid + 256 * k;
-      const int l = v / vpr, pp = (v % vpr) * 8;
-      u32x4 val = {0u, 0u, 0u, 0u};
-      if (l < c.len) val = *reinterpret_cast<const u32x4*>(row_ptr<bf16>(z, c.b, c.t0 + l, h) + p0 + pp);
-      zr[k] = val;
+      const int l = min(v / vpr, c.len - 1), pp = (v % vpr) * 8;
+      zr[k] = *reinterpret_cast<const u32x4*>(row_ptr<bf16>(z, c.b, c.t0 + l, h) + p0 + pp);
     }
   }
 
@@ -389,27 +425,24 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bf16(Geo g, const float* __r
   for (int a = 0; a < Cfg::LTW; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = zero4();
-  const float* cbm = CB + ((int64_t)j * g.G + grp) * C * C;
-  const int nkb = (N + 31) / 32;
 
 #pragma unroll
   for (int u = 0; u < Cfg::LTW; ++u) {
-    const int lt = (u / 2) * 8 + ((u & 1) ? 7 - wave : wave);
+    const int lt = lt_of(u);
     if (lt >= Cfg::NLT) continue;
     const int lrow = lt * 16 + r16;
     const bool lok = lrow < c.len;
-    const bf16* crow = row_ptr<bf16>(Cm, c.b, c.t0 + (lok ? lrow : 0), grp);
-    // Y_off: C_l . Hin^T, four k-blocks of 32 per batch.  Every matrix
-    // instruction runs unconditionally; operands past N or past the chunk are
-    // zero, so no accumulator is ever updated under a data-dependent branch.
+    const bf16* crow = row_ptr<bf16>(Cm, c.b, c.t0 + min(lrow, c.len - 1), grp);
+    // Y_off: C_l . Hin^T.  The first four k-blocks come from the prefetch.
     for (int k0 = 0; k0 < nkb; k0 += 4) {
       FragBF cf[4];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int k = (k0 + kk) * 32 + q * 8;
-        const bool ok = lok && k < N;
-        const FragBF v = Prec<bf16>::load_exact(crow + (k < N ? k : 0));
-        cf[kk] = ok ? v : Prec<bf16>::zero_exact();
+        const u32x4 raw = k0 == 0 ? fr.cf[kk]
+                                  : *reinterpret_cast<const u32x4*>(crow + min(k, N - 8));
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        cf[kk].v = __builtin_bit_cast(bf16x8, (lok && k < N) ? raw : zero);
       }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -427,18 +460,21 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bf16(Geo g, const float* __r
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[u][pt][i] *= e;
     }
-    // Y_diag: (L o CB) x over s <= l, four k-blocks per batch.  The CB tile is
-    // allocated for every (l, s) of the chunk, so its loads need no guard; the
-    // causal/length mask is a select applied after the exponential (the
-    // exponent itself is zeroed where masked, so exp never overflows).
+    // Y_diag: (L o CB) x over s <= l.  The first four k-blocks come from the
+    // prefetch; the mask is a select after the exponential (whose argument is
+    // zeroed where masked, so it never overflows).
     const float csl = s_cs[lrow];
     const int nkd = (lt * 16 + 16 + 31) / 32;
-    for (int k0 = 0; k0 < nkd; k0 += 4) {
-      f32x8 cb[4];
+    f32x8 cbv[4];
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int kb = min(k0 + kk, nkd - 1);
-        cb[kk] = Vec8<float>::load(cbm + (int64_t)lrow * C + kb * 32 + q * 8);
+    for (int kk = 0; kk < 4; ++kk) cbv[kk] = fr.cb[kk];
+    // the prefetch buffer is free again: start loading the next l-tile
+    if (u + 1 < Cfg::LTW && lt_of(u + 1) < Cfg::NLT) load_frags(u + 1, fr);
+    for (int k0 = 0; k0 < nkd; k0 += 4) {
+      if (k0 > 0) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          cbv[kk] = Vec8<float>::load(cbm + (int64_t)lrow * C + min(k0 + kk, nkd - 1) * 32 + q * 8);
       }
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
@@ -451,7 +487,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bf16(Geo g, const float* __r
           const int s = s0 + e;
           const bool keep = lok && (s <= lrow) && (s < c.len);
           const float ex = fast_exp(keep ? csl - csv[e] : 0.0f);
-          m[e] = keep ? ex * cb[kk][e] : 0.0f;
+          m[e] = keep ? ex * cbv[kk][e] : 0.0f;
         }
         const FragSplit mf = split_f32x8(m);
 #pragma unroll
@@ -470,7 +506,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bf16(Geo g, const float* __r
     const float Dh = D[h];
 #pragma unroll
     for (int u = 0; u < Cfg::LTW; ++u) {
-      const int lt = (u / 2) * 8 + ((u & 1) ? 7 - wave : wave);
+      const int lt = lt_of(u);
       if (lt >= Cfg::NLT) continue;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
@@ -486,7 +522,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_bf16(Geo g, const float* __r
   __syncthreads();  // all waves are done with the state; reuse its area for y
 #pragma unroll
   for (int u = 0; u < Cfg::LTW; ++u) {
-    const int lt = (u / 2) * 8 + ((u & 1) ? 7 - wave : wave);
+    const int lt = lt_of(u);
     if (lt >= Cfg::NLT) continue;
 #pragma unroll
     for (int pt = 0; pt < 4; ++pt) {

@@ -203,6 +203,20 @@ __device__ __forceinline__ double wave_inclusive_sum_f64(double v) {
   return v;
 }
 
+// ------------------------------------------------------------------ XCD placement
+
+// MI355X has 8 accelerator complex dies (XCDs), each with its own L2.  The
+// dispatcher hands consecutive workgroup ids to the XCDs in turn, so a linear
+// block id L runs on XCD L % 8.  This maps L to a logical work item such that
+// consecutive logical items share an XCD (and its L2): items [x * per, (x+1) *
+// per) run on XCD x.  Ids of an incomplete last round keep their own number.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int xcd_remap(int L, int total) {
+  const int per = total / kNumXcd;
+  if (L >= per * kNumXcd) return L;
+  return (L % kNumXcd) * per + L / kNumXcd;
+}
+
 // ------------------------------------------------------------------ geometry
 
 // Problem geometry passed by value to every kernel.

@@ -29,6 +29,11 @@ hipError_t launch_state_passing(const Geo& g, const void* states, int st_dtype,
                                 const float* cs, const float* h0, void* states_out,
                                 float* hfinal, hipStream_t s);
 
+// Chunk states and the inter-chunk scan in one pass (bf16 inputs): writes the
+// carry-in states (K, H, P, N) in the state dtype and the final states.
+hipError_t launch_state_scan(const Geo& g, TArg x, TArg B, const float* cs, const float* h0,
+                             void* hin, int st_dtype, float* hfinal, hipStream_t s);
+
 hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
                              const float* cs, const void* states, int st_dtype,
                              const float* D, TArg z, TArg out, int out_dtype, hipStream_t s);

@@ -17,10 +17,12 @@ from helpers import (TOL_BF16, TOL_BF16_DESIGN, TOL_F32, bf16_out_ok, device_inp
 
 pytestmark = pytest.mark.gpu
 
-ALGOS = ["staged"]
+ALGOS = ["staged", "fused"]
 
 
 def run_gpu(inp, w, algo="staged", out_dtype=torch.float32, packed_xbc=False, **kw):
+    if algo == "fused" and w.dtype == "f32":
+        pytest.skip("the fused forward takes bf16 inputs (fp32 is rejected, tested below)")
     dev = device_inputs(inp, in_dtype(w), packed_xbc=packed_xbc)
     out, fin = ssd.ssd_forward(dev["x"], dev["B"], dev["C"], dev["dt"], dev["A"],
                                dev["dt_bias"], dev["D"], dev["z"], dev["initial_states"],
@@ -294,3 +296,24 @@ def test_full_size_sampled(name, out_dtype, algo):
     # bitwise repeatable at full size
     y2, f2 = run_gpu(inp, w, algo, out_dtype=out_dtype, packed_xbc=True)
     assert torch.equal(y, y2) and torch.equal(f, f2)
+
+
+def test_fused_rejects_fp32_inputs():
+    w = SMALL["tiny_f32"]
+    inp = make_inputs(w)
+    dev = device_inputs(inp, torch.float32)
+    with pytest.raises(ssd.SSDError) as e:
+        ssd.ssd_forward(dev["x"], dev["B"], dev["C"], dev["dt"], dev["A"], dev["dt_bias"],
+                        dev["D"], dev["z"], chunk_size=w.chunk_size, algo="fused")
+    assert e.value.status == 5
+
+
+@pytest.mark.parametrize("name", ["c128_g8", "packed_edges", "ragged_batch2", "c256"])
+def test_fused_matches_staged(name):
+    # two different schedules of the same math agree to within their rounding
+    w = SMALL[name]
+    inp = with_initial_states(make_inputs(w))
+    ys, fs = run_gpu(inp, w, "staged")
+    yf, ff = run_gpu(inp, w, "fused")
+    assert err(to_np(yf), to_np(ys)) <= TOL_BF16_DESIGN
+    assert err(to_np(ff), to_np(fs)) <= TOL_BF16_DESIGN
