@@ -1,0 +1,74 @@
+// stage_bmm.hpp -- stage 2: CB[j, g, l, s] = sum_n C[t0 + l, g, n] B[t0 + s, g, n].
+//
+// SSD Reference, "Algorithm and tensor-shape contract" step 4 (Cb = Cc Bc^T),
+// the BMM stage of vLLM PR 27299 "Purpose".  Only the causal half s <= l is
+// ever consumed, so only 16x16 tiles on or below the diagonal are computed.
+//
+// Both operands are read with the reduction index n contiguous in memory, the
+// layout the matrix-core fragments want, so fragments come straight from
+// global memory (16 B per lane for bf16).  One wavefront per (chunk, group,
+// 16-row l-tile) computes the l-tile's causal s-tiles four at a time: all
+// fragment loads of a batch are issued together (one memory round trip per
+// batch and 128 columns of N), rows past the chunk's end and columns past N are
+// zeroed by select when used, and every matrix instruction runs unconditionally.
+// Inputs are exact in their storage type, so the products need no hi/lo split.
+#pragma once
+#include "common.hpp"
+
+namespace ssd {
+
+// One wavefront computes the causal tiles of l-tile lt of (chunk j, group grp).
+template <typename T>
+__device__ __forceinline__ void bmm_wave(const Geo& g, const TArg& Cm, const TArg& Bm, float* CB,
+                                         int j, int grp, int lt) {
+  using Pr = Prec<T>;
+  using Ex = typename Pr::Exact;
+  Chunk c;
+  if (!get_chunk(g, j, c)) return;
+  const int lane = threadIdx.x % kWave;
+  const int C = g.C, N = g.N;
+  if (lt >= C / 16) return;
+  const int r16 = lane % 16, q = lane / 16;
+  const int lrow = lt * 16 + r16;
+  const T* crow = row_ptr<T>(Cm, c.b, c.t0 + min(lrow, c.len - 1), grp);
+  const bool lok = lrow < c.len;
+  float* out = CB + ((int64_t)j * g.G + grp) * C * C;
+
+  for (int st0 = 0; st0 <= lt; st0 += 4) {
+    f32x4 acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = zero4();
+    for (int n0 = 0; n0 < N; n0 += 128) {
+      Ex a[4], bf[4][4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k = n0 + kk * 32 + q * 8;
+        a[kk] = Pr::load_exact(crow + min(k, N - 8));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int srow = min((st0 + b) * 16 + r16, c.len - 1);
+          bf[b][kk] = Pr::load_exact(row_ptr<T>(Bm, c.b, c.t0 + srow, grp) + min(k, N - 8));
+        }
+      }
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k = n0 + kk * 32 + q * 8;
+        const Ex av = (lok && k < N) ? a[kk] : Pr::zero_exact();
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const bool sok = (st0 + b) * 16 + r16 < c.len && k < N;
+          mma(acc[b], av, sok ? bf[b][kk] : Pr::zero_exact());
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      if (st0 + b > lt) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        out[(int64_t)(lt * 16 + q * 4 + i) * C + (st0 + b) * 16 + r16] = acc[b][i];
+    }
+  }
+}
+
+}  // namespace ssd
