@@ -95,7 +95,7 @@ def stage_flops(w, K):
 
 KERNEL_SOURCES = {"chunk_cumsum": "chunk_cumsum.hip", "bmm_chunk": "bmm_chunk.hip",
                   "chunk_state": "chunk_state.hip", "state_passing": "state_passing.hip",
-                  "chunk_scan": "chunk_scan.hip", "state_scan": "state_scan.hip"}
+                  "chunk_scan": "chunk_scan.hip", "fused_fwd": "fused_fwd.hip"}
 
 
 def measured_traffic(stage, key):

@@ -186,6 +186,85 @@ StagedWs staged_layout(const ssd_problem* p) {
   return w;
 }
 
+struct FusedWs {
+  ssd::FusedPlan plan;
+  int64_t K;  // 128-token chunk slots
+  size_t meta, sync, edec, agg, total;
+};
+
+// Chunk slots at the fused pass's own chunk length.
+int64_t fused_chunks(const ssd_problem* p) {
+  const int64_t nc = cdiv(p->seqlen, ssd::kFusedChunk);
+  if (p->nseq > 0) return nc + p->nseq;
+  return (int64_t)p->batch * nc;
+}
+
+FusedWs fused_layout(const ssd_problem* p) {
+  FusedWs w;
+  w.K = fused_chunks(p);
+  w.plan = ssd::fused_plan(w.K, p->nheads, p->headdim, p->dstate);
+  const int64_t slots = (int64_t)w.plan.nr * w.plan.U;
+  size_t off = 0;
+  w.meta = off;
+  if (p->nseq > 0)
+    off += align256((size_t)(ssd::kMetaHeader + 3 * w.K + p->nseq + 1) * sizeof(int32_t));
+  w.sync = off;
+  off += align256((size_t)(2 + slots) * sizeof(uint32_t));
+  w.edec = off;
+  off += align256((size_t)slots * sizeof(float));
+  w.agg = off;
+  off += align256((size_t)slots * 64 * 16 * w.plan.NT * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+ssd_status check_state_ptr(const float* ptr, const char* name) {
+  if (ptr && reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+    return fail(SSD_ERR_STRIDE, "%s: data pointer is not 16-byte aligned", name);
+  return SSD_OK;
+}
+
+// The single-pass forward (SSD_ALGO_FUSED); arguments common to both paths
+// were validated by ssd_forward.
+ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* workspace,
+                         size_t ws_bytes, hipStream_t stream) {
+  if (has_tokens(p) && a->x.dtype != SSD_BF16)
+    return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED takes bf16 x, B, C (use SSD_ALGO_STAGED)");
+  if (p->dstate > 128)
+    return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED supports dstate <= 128, got %d (use SSD_ALGO_STAGED)",
+                p->dstate);
+  SSD_TRY(check_state_ptr(a->initial_states, "initial_states"));
+  SSD_TRY(check_state_ptr(a->final_states, "final_states"));
+  const FusedWs w = fused_layout(p);
+  if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < w.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, w.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  ssd::FusedLaunch f;
+  f.meta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws + w.meta) : nullptr;
+  f.g = make_geo(p, f.meta);
+  f.g.C = ssd::kFusedChunk;
+  f.g.nc = (int)cdiv(p->seqlen, ssd::kFusedChunk);
+  f.g.K = (int)w.K;
+  f.cu = p->nseq > 0 ? p->cu_seqlens : nullptr;
+  f.x = targ(a->x); f.B = targ(a->B); f.C = targ(a->C); f.dt = targ(a->dt);
+  f.z = targ(a->z); f.out = targ(a->out);
+  f.dt_dtype = dcode(a->dt.dtype);
+  f.out_dtype = dcode(a->out.dtype);
+  f.A = a->A; f.dt_bias = a->dt_bias; f.D = a->D;
+  f.h0 = a->initial_states; f.hfinal = a->final_states;
+  f.softplus = p->dt_softplus; f.clamp = p->dt_clamp;
+  f.dt_min = p->dt_min; f.dt_max = p->dt_max;
+  f.plan = w.plan;
+  f.sync = reinterpret_cast<uint32_t*>(ws + w.sync);
+  f.edec = reinterpret_cast<float*>(ws + w.edec);
+  f.agg = reinterpret_cast<float*>(ws + w.agg);
+  SSD_HIP(ssd::launch_fused_fwd(f, stream), "fused forward launch");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -228,7 +307,7 @@ ssd_status ssd_workspace_size(const ssd_problem* p, ssd_algo algo, size_t* bytes
   if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
   if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
-  *bytes = staged_layout(p).total;
+  *bytes = algo == SSD_ALGO_FUSED ? fused_layout(p).total : staged_layout(p).total;
   return ok();
 }
 
@@ -374,8 +453,7 @@ ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* 
   if (!a->A) return fail(SSD_ERR_NULL, "A is NULL");
   if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
-  if (algo == SSD_ALGO_FUSED && has_tokens(p) && a->x.dtype != SSD_BF16)
-    return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED takes bf16 x, B, C (use SSD_ALGO_STAGED)");
+  if (algo == SSD_ALGO_FUSED) return fused_forward(p, a, workspace, ws_bytes, stream);
   const StagedWs w = staged_layout(p);
   if (w.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < w.total)
@@ -396,17 +474,11 @@ ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* 
                                    stream),
           "chunk_cumsum launch");
   SSD_HIP(ssd::launch_bmm_chunk(g, targ(a->C), targ(a->B), in, cb, stream), "bmm_chunk launch");
-  if (algo == SSD_ALGO_FUSED) {
-    SSD_HIP(ssd::launch_state_scan(g, targ(a->x), targ(a->B), cs, a->initial_states, st, sd,
-                                   a->final_states, stream),
-            "state_scan launch");
-  } else {
-    SSD_HIP(ssd::launch_chunk_state(g, targ(a->x), targ(a->B), in, cs, st, sd, stream),
-            "chunk_state launch");
-    SSD_HIP(ssd::launch_state_passing(g, st, sd, cs, a->initial_states, st, a->final_states,
-                                      stream),
-            "state_passing launch");
-  }
+  SSD_HIP(ssd::launch_chunk_state(g, targ(a->x), targ(a->B), in, cs, st, sd, stream),
+          "chunk_state launch");
+  SSD_HIP(ssd::launch_state_passing(g, st, sd, cs, a->initial_states, st, a->final_states,
+                                    stream),
+          "state_passing launch");
   SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, st, sd, a->D, targ(a->z),
                                  targ(a->out), dcode(a->out.dtype), stream),
           "chunk_scan launch");

@@ -29,13 +29,41 @@ hipError_t launch_state_passing(const Geo& g, const void* states, int st_dtype,
                                 const float* cs, const float* h0, void* states_out,
                                 float* hfinal, hipStream_t s);
 
-// Chunk states and the inter-chunk scan in one pass (bf16 inputs): writes the
-// carry-in states (K, H, P, N) in the state dtype and the final states.
-hipError_t launch_state_scan(const Geo& g, TArg x, TArg B, const float* cs, const float* h0,
-                             void* hin, int st_dtype, float* hfinal, hipStream_t s);
-
 hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
                              const float* cs, const void* states, int st_dtype,
                              const float* D, TArg z, TArg out, int out_dtype, hipStream_t s);
+
+// ---- fused forward (fused_fwd.hip)
+constexpr int kFusedChunk = 128;             // internal chunk length of the fused pass
+constexpr int kFusedTargetWorkgroups = 512;  // (unit, range) workgroups aimed for
+
+// Work decomposition of the fused pass: P slabs of 64 rows per head, units =
+// heads x slabs, n-tiles of the d_state capacity, chunks per range, ranges.
+struct FusedPlan {
+  int PS, U, NT, R, nr;
+};
+FusedPlan fused_plan(int64_t K, int H, int P, int N);
+
+struct FusedLaunch {
+  Geo g;                   // 128-token chunk geometry (meta = the fused chunk table)
+  const int32_t* cu;       // cu_seqlens of a packed batch, NULL in batch mode
+  int32_t* meta;           // chunk table to build (packed batch only)
+  TArg x, B, C, dt, z, out;
+  int dt_dtype, out_dtype;
+  const float* A;
+  const float* dt_bias;
+  const float* D;
+  const float* h0;
+  float* hfinal;
+  int softplus, clamp;
+  float dt_min, dt_max;
+  FusedPlan plan;
+  uint32_t* sync;          // 2 + nr * U words
+  float* edec;             // nr * U
+  float* agg;              // nr * U * 64 * 16 * NT
+};
+
+// Two launches: a small reset/table kernel, then the fused forward.
+hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s);
 
 }  // namespace ssd

@@ -23,6 +23,9 @@ ALGOS = ["staged", "fused"]
 def run_gpu(inp, w, algo="staged", out_dtype=torch.float32, packed_xbc=False, **kw):
     if algo == "fused" and w.dtype == "f32":
         pytest.skip("the fused forward takes bf16 inputs (fp32 is rejected, tested below)")
+    if algo == "fused" and w.dstate > 128:
+        pytest.skip("the fused forward takes dstate <= 128 (larger is rejected, tested in "
+                    "test_gpu_fused.py)")
     dev = device_inputs(inp, in_dtype(w), packed_xbc=packed_xbc)
     out, fin = ssd.ssd_forward(dev["x"], dev["B"], dev["C"], dev["dt"], dev["A"],
                                dev["dt_bias"], dev["D"], dev["z"], dev["initial_states"],
@@ -175,16 +178,29 @@ def test_short_sequences(T, algo):
     check(w, y, f, ref)
 
 
-def test_zero_tokens_passes_initial_state_through():
+@pytest.mark.parametrize("algo", ALGOS)
+def test_zero_tokens_passes_initial_state_through(algo):
     w = small_workload("empty", batch=2, seqlen=0, nheads=2, headdim=16, ngroups=1, dstate=16,
                        chunk_size=64)
     inp = with_initial_states(make_inputs(w))
-    y, f = run_gpu(inp, w)
+    y, f = run_gpu(inp, w, algo)
     assert y.numel() == 0
     assert np.array_equal(to_np(f), inp.initial_states.astype(np.float64))
 
 
 # ------------------------------------------------------------------ invariants on the GPU
+
+def same(a, b, algo):
+    """Equal results of two decompositions of one problem.  The staged path
+    reproduces them bit for bit.  The fused path cuts the chunks into ranges
+    whose aggregates are combined in a different association when the problem
+    size changes; the carry-in enters the matrix cores as bf16 hi + lo (about
+    16 significant bits), so a last-bit difference of the fp32 state can move
+    an output by ~2^-16 of its scale.  There the two agree to 1e-4."""
+    if algo == "staged":
+        assert torch.equal(a, b)
+    else:
+        assert err(to_np(a), to_np(b)) <= 1e-4
 
 @pytest.mark.parametrize("algo", ALGOS)
 def test_run_to_run_bit_identical(algo):
@@ -221,8 +237,8 @@ def test_packed_equals_separate_sequences(algo):
         wi = small_workload("one", seqlen=e - s, nheads=w.nheads, headdim=w.headdim,
                             ngroups=w.ngroups, dstate=w.dstate, chunk_size=w.chunk_size)
         yi, fi = run_gpu(one, wi, algo)
-        assert torch.equal(yp[s:e], yi[0])
-        assert torch.equal(fp[i], fi[0])
+        same(yp[s:e], yi[0], algo)
+        same(fp[i], fi[0], algo)
 
 
 @pytest.mark.parametrize("algo", ALGOS)
@@ -248,7 +264,8 @@ def test_split_and_resume(algo):
         y2, f2 = run_gpu(second, w2, algo)
         ycat = torch.cat([y1, y2], dim=1)
         if k % w.chunk_size == 0:
-            assert torch.equal(ycat, y) and torch.equal(f2, f)
+            same(ycat, y, algo)
+            same(f2, f, algo)
         else:
             # a shifted chunk grid rounds differently; both runs sit within
             # the design bound of the oracle, so of each other
