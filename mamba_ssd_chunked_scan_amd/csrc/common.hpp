@@ -180,6 +180,35 @@ template <> struct Prec<float> {
 
 __device__ __forceinline__ f32x4 zero4() { f32x4 z = {0.f, 0.f, 0.f, 0.f}; return z; }
 
+// ------------------------------------------------------------------ LDS transpose reads
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane 4a + b receives element b of the 8-byte words addressed by lanes
+// a, a + 4, a + 8 and a + 12 of the group (in that order; layout checked on
+// the hardware).  So if lane l of a group addresses row k0 + l / 4, columns
+// col0 + 4 (l % 4) .. + 3 of a row-major [k][col] bf16 tile, lane c of the
+// group receives column col0 + c of rows k0 .. k0 + 3: four consecutive k of
+// one column, half of a 16x16x32 matrix-core operand fragment.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const bf16* p) {
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(const_cast<bf16*>(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Operand fragment (8 bf16 along k for column col0 + lane % 16) from a
+// row-major [k][col] bf16 tile in LDS with row pitch ld (elements, a multiple
+// of 4): k = k0 .. k0 + 3, then k1 .. k1 + 3 (k0, k1 chosen per lane group).
+__device__ __forceinline__ bf16x8 lds_frag_tr(const bf16* tile, int ld, int k0, int k1,
+                                              int col0) {
+  const int l = threadIdx.x % 16;
+  const bf16* c = tile + col0 + 4 * (l % 4);
+  const u32x2 lo = lds_read_tr16(c + (k0 + l / 4) * ld);
+  const u32x2 hi = lds_read_tr16(c + (k1 + l / 4) * ld);
+  const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // ------------------------------------------------------------------ wave scan
 
 // Inclusive prefix sum over the 64 lanes of a wavefront.

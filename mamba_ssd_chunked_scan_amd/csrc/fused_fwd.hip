@@ -34,17 +34,31 @@
 // owns: no residency assumption, no deadlock.  Every wait is bounded; on
 // timeout an error bit is set in the workspace and the kernel still finishes.
 //
-// Per chunk, per workgroup (4 waves, wave w):
+// Hand-off.  Aggregates, decays and flags are written and read with
+// agent-scope atomic accesses, which on gfx950 are plain loads and stores that
+// go to the level of the memory system all XCDs share (the L2 of each XCD is
+// not coherent with the others).  A publisher stores its aggregate, waits
+// until all its stores have completed (s_waitcnt), passes a workgroup barrier
+// and only then stores the flag; a reader polls the flag and issues its
+// aggregate loads only after it has seen it.  Release/acquire fences would do
+// the same job through a write-back and an invalidation of the whole L2 of the
+// XCD, which costs far more than the few aggregates involved.
+//
+// Per chunk, per workgroup (4 waves, wave w).  x and B are staged in LDS in
+// their natural layout (tokens x columns); operands that need the token axis
+// as the reduction axis are read with the gfx950 LDS transpose read, so no
+// thread ever transposes data itself.
 //   * S_j^T (n x p) = B^T (n x s) . (w_s x_s) (s x p): wave w owns p-tile w
 //     and all n-tiles; the carried state uses this accumulator layout (lane:
 //     one p, four consecutive n per n-tile), which is also the layout of the
 //     carry-in rows the Y_off operand reads from LDS;
 //   * C.B^T: wave w computes the tiles (s-tile, l-tile) of its l-tiles w and
-//     7 - w (balanced causal work) with B and C fragments read straight from
-//     global memory (n contiguous).  The accumulator layout of a C.B^T tile
-//     (lane: one l, four consecutive s) is used directly as the A operand of
-//     Y_diag = M . x with the k (token) order permuted to match; the x operand
-//     is read from x^T in LDS in the same permuted order, so M never goes
+//     7 - w (balanced causal work), B rows from the LDS tile and C fragments
+//     from global memory (n contiguous in both), while the B tile is still in
+//     LDS; the tiles stay in registers.  The accumulator layout of a C.B^T
+//     tile (lane: one l, four consecutive s) is used directly as the A operand
+//     of Y_diag = M . x with the k (token) order permuted to match; the x
+//     operand is read from the x tile in that same order, so M never goes
 //     through LDS.
 // Precision is that of the staged path: exact bf16 inputs, fp32-derived
 // operands (decay-weighted x, M = L o CB, the carried state) split into bf16
@@ -57,11 +71,21 @@ namespace ssd {
 namespace {
 
 constexpr int FC = 128;                 // internal chunk length
-constexpr int FNP = FC / 2;             // token pairs per chunk
-constexpr int FLDW = (FC + 8) / 2;      // dwords per transposed (token-pair) row
-constexpr int FXU = (8 * FNP) / 256;    // x staging units per thread (token pair x 8 p)
-constexpr int FZV = (FC * 8) / 256;     // epilogue 8-vectors per thread
-constexpr int FYLD = 64 + 4;            // floats per staged output row
+#ifndef SSD_FUSED_XPAD
+#define SSD_FUSED_XPAD 8
+#endif
+#ifndef SSD_FUSED_BPAD
+#define SSD_FUSED_BPAD 8
+#endif
+#ifndef SSD_FUSED_HPAD
+#define SSD_FUSED_HPAD 8
+#endif
+#ifndef SSD_FUSED_YPAD
+#define SSD_FUSED_YPAD 4
+#endif
+constexpr int FXLD = 64 + SSD_FUSED_XPAD;   // bf16 per row of the x tile in LDS
+constexpr int FXV = (FC * 8) / 256;     // 16-byte x (and z, out) vectors per thread
+constexpr int FYLD = 64 + SSD_FUSED_YPAD;  // floats per staged output row
 constexpr uint32_t kFlagAgg = 1;        // aggregate of a range that continues a sequence
 constexpr uint32_t kFlagReset = 2;      // aggregate of a range where the sequence starts
 constexpr int kSpinLimit = 1 << 18;     // polls (~1 us each) before giving up
@@ -69,19 +93,20 @@ constexpr int kSpinLimit = 1 << 18;     // polls (~1 us each) before giving up
 template <int NT> struct FCfg {
   static constexpr int NMAX = 16 * NT;         // d_state capacity
   static constexpr int NKB = NT / 2;           // 32-wide k-blocks over n
-  static constexpr int BU = NT / 2;            // B staging units per thread
-  static constexpr int HLD = NMAX + 8;         // bf16 per carry-in row in LDS
+  static constexpr int BV = FC * NMAX / 8 / 256;   // 16-byte B vectors per thread
+  static constexpr int BLD = NMAX + SSD_FUSED_BPAD;  // bf16 per row of the B tile in LDS
+  static constexpr int HLD = NMAX + SSD_FUSED_HPAD;  // bf16 per carry-in row in LDS
   static constexpr int OFF_CS = 0;             // cs[128]
   static constexpr int OFF_W = 512;            // w[128] = exp(Lambda - cs)
   static constexpr int OFF_MISC = 1024;        // broadcast words
-  static constexpr int OFF_XT = 1088;          // x^T [64 p][FLDW]
-  static constexpr int XT_BYTES = 64 * FLDW * 4;
-  static constexpr int OFF_R = OFF_XT + XT_BYTES;   // B^T, then carry-in, then y
-  static constexpr int BT_BYTES = NMAX * FLDW * 4;
+  static constexpr int OFF_X = 1088;           // x [128 s][FXLD]
+  static constexpr int X_BYTES = FC * FXLD * 2;
+  static constexpr int OFF_R = OFF_X + X_BYTES;     // B, then carry-in, then y
+  static constexpr int B_BYTES = FC * BLD * 2;
   static constexpr int H_BYTES = 2 * 64 * HLD * 2;
   static constexpr int Y_BYTES = FC * FYLD * 4;
-  static constexpr int R_BYTES = BT_BYTES > H_BYTES ? (BT_BYTES > Y_BYTES ? BT_BYTES : Y_BYTES)
-                                                    : (H_BYTES > Y_BYTES ? H_BYTES : Y_BYTES);
+  static constexpr int R_BYTES = B_BYTES > H_BYTES ? (B_BYTES > Y_BYTES ? B_BYTES : Y_BYTES)
+                                                  : (H_BYTES > Y_BYTES ? H_BYTES : Y_BYTES);
   static constexpr int LDS = OFF_R + R_BYTES;
 };
 
@@ -90,7 +115,6 @@ template <int NT> struct FCfg {
 struct FusedArgs {
   Geo g;                  // 128-token chunk geometry; meta = the fused chunk table
   TArg x, B, C, dt, z, out;
-  int dt_bf16;
   const float* A;
   const float* dt_bias;
   const float* D;
@@ -104,16 +128,16 @@ struct FusedArgs {
   float* agg;             // [r * U + u][64][NMAX] aggregates
 };
 
-template <typename TO, int NT>
+template <typename TO, typename TDt, int NT>
 __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   using Cfg = FCfg<NT>;
-  constexpr int NMAX = Cfg::NMAX, NKB = Cfg::NKB, BU = Cfg::BU, HLD = Cfg::HLD;
+  constexpr int NMAX = Cfg::NMAX, NKB = Cfg::NKB, BV = Cfg::BV, BLD = Cfg::BLD, HLD = Cfg::HLD;
   __shared__ __align__(16) char smem[Cfg::LDS];
   float* s_cs = reinterpret_cast<float*>(smem + Cfg::OFF_CS);
   float* s_w = reinterpret_cast<float*>(smem + Cfg::OFF_W);
   uint32_t* s_misc = reinterpret_cast<uint32_t*>(smem + Cfg::OFF_MISC);
-  uint32_t* s_xt = reinterpret_cast<uint32_t*>(smem + Cfg::OFF_XT);
-  uint32_t* s_bt = reinterpret_cast<uint32_t*>(smem + Cfg::OFF_R);
+  bf16* s_x = reinterpret_cast<bf16*>(smem + Cfg::OFF_X);
+  bf16* s_b = reinterpret_cast<bf16*>(smem + Cfg::OFF_R);
   bf16* s_hh = reinterpret_cast<bf16*>(smem + Cfg::OFF_R);
   bf16* s_hl = s_hh + 64 * HLD;
   float* s_y = reinterpret_cast<float*>(smem + Cfg::OFF_R);
@@ -151,51 +175,58 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
 
   const float Ah = a.A[h];
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
-  u32x4 xr[FXU][2], br[BU][2], zr[FZV];
-  float dtv[2];
+  // registers a chunk's x, B and dt are loaded into before they go to LDS:
+  // 16-byte row pieces, 8 (x) or NMAX / 8 (B) consecutive threads per row
+  struct Stage {
+    u32x4 x[FXV], b[BV];
+    float dt[2];
+  };
+  u32x4 zr[FXV];
 
-  // ---- issue every global load of chunk c (x, B, dt; z when gating)
-  auto load_chunk = [&](const Chunk& c, bool with_z) {
+  // Tile loads: a uniform base pointer (the chunk's first row) plus a 32-bit
+  // per-lane element offset (at most 127 rows of the tensor), so addresses
+  // stay in scalar registers.
+  auto load_z = [&](const Chunk& c) {
+    const bf16* base = row_ptr<bf16>(a.z, c.b, c.t0, h) + p0;
 #pragma unroll
-    for (int k = 0; k < FXU; ++k) {
-      const int uu = tid + 256 * k, grp8 = uu / FNP, pr = uu % FNP;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        xr[k][t] = *reinterpret_cast<const u32x4*>(
-            row_ptr<bf16>(a.x, c.b, c.t0 + min(2 * pr + t, c.len - 1), h) + p0 +
-            min(grp8 * 8, pw - 8));
+    for (int k = 0; k < FXV; ++k) {
+      const int v = tid + 256 * k, row = v / 8, col = (v % 8) * 8;
+      const uint32_t off = (uint32_t)(min(row, c.len - 1) * a.z.s1 + min(col, pw - 8));
+      zr[k] = *reinterpret_cast<const u32x4*>(base + off);
     }
+  };
+  // ---- issue every global load of chunk c (x, B, dt into st; z when gating)
+  auto load_chunk = [&](Stage& st, const Chunk& c, bool with_z) {
+    const bf16* xbase = row_ptr<bf16>(a.x, c.b, c.t0, h) + p0;
 #pragma unroll
-    for (int k = 0; k < BU; ++k) {
-      const int uu = tid + 256 * k, grp8 = uu / FNP, pr = uu % FNP;
+    for (int k = 0; k < FXV; ++k) {
+      const int v = tid + 256 * k, row = v / 8, col = (v % 8) * 8;
+      const uint32_t off = (uint32_t)(min(row, c.len - 1) * a.x.s1 + min(col, pw - 8));
+      st.x[k] = *reinterpret_cast<const u32x4*>(xbase + off);
+    }
+    const bf16* bbase = row_ptr<bf16>(a.B, c.b, c.t0, grp);
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        br[k][t] = *reinterpret_cast<const u32x4*>(
-            row_ptr<bf16>(a.B, c.b, c.t0 + min(2 * pr + t, c.len - 1), grp) +
-            min(grp8 * 8, g.N - 8));
+    for (int k = 0; k < BV; ++k) {
+      const int v = tid + 256 * k, row = v / (NMAX / 8), col = (v % (NMAX / 8)) * 8;
+      const uint32_t off = (uint32_t)(min(row, c.len - 1) * a.B.s1 + min(col, g.N - 8));
+      st.b[k] = *reinterpret_cast<const u32x4*>(bbase + off);
     }
     if (wave == 0) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int t = c.t0 + min(2 * lane + e, c.len - 1);
-        dtv[e] = a.dt_bf16 ? to_f32<bf16>(*row_ptr<bf16>(a.dt, c.b, t, h))
-                           : *row_ptr<float>(a.dt, c.b, t, h);
+        // (a branch on the dt type here would make the compiler wait for every
+        // outstanding load right after it)
+        st.dt[e] = to_f32<TDt>(*row_ptr<TDt>(a.dt, c.b, t, h));
       }
     }
-    if (with_z && a.z.p) {
-#pragma unroll
-      for (int k = 0; k < FZV; ++k) {
-        const int v = tid + 256 * k, l = v / 8, pp = (v % 8) * 8;
-        zr[k] = *reinterpret_cast<const u32x4*>(
-            row_ptr<bf16>(a.z, c.b, c.t0 + min(l, c.len - 1), h) + p0 + min(pp, pw - 8));
-      }
-    }
+    if (with_z && a.z.p) load_z(c);
   };
 
-  // ---- LDS: cumsum, decay weights, x^T and B^T as packed token pairs.
-  // Tokens past the chunk's end (loaded as copies of its last token), columns
-  // past P and rows past N are zeroed here.
-  auto stage_chunk = [&](const Chunk& c) {
+  // ---- LDS: cumsum, decay weights, and x and B in their natural row-major
+  // layout (tokens x columns).  Tokens past the chunk's end (loaded as copies
+  // of its last token), columns past P and past N are zeroed here.
+  auto stage_cs = [&](const Stage& st, const Chunk& c) {
     if (wave == 0) {
       double av[2], run = 0.0;
 #pragma unroll
@@ -203,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
         const int l = 2 * lane + e;
         float aa = 0.0f;
         if (l < c.len) {
-          const float uu = dtv[e] + bias;
+          const float uu = st.dt[e] + bias;
           float d = a.softplus ? softplus_f32(uu) : uu;
           if (a.clamp) d = fminf(fmaxf(d, a.dt_min), a.dt_max);
           aa = d * Ah;
@@ -222,44 +253,32 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       s_w[2 * lane + 1] = 2 * lane + 1 < c.len ? fast_exp(lam - c1) : 0.0f;
       if (lane == 0) s_misc[1] = __float_as_uint(lam);
     }
+  };
+  auto stage_xb = [&](const Stage& st, const Chunk& c) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int k = 0; k < FXU; ++k) {
-      const int uu = tid + 256 * k, grp8 = uu / FNP, pr = uu % FNP;
-      const bool col_ok = grp8 * 8 < pw;
-      const bool k0 = col_ok && 2 * pr < c.len, k1 = col_ok && 2 * pr + 1 < c.len;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int row = grp8 * 8 + 2 * d;
-        const uint32_t va = k0 ? xr[k][0][d] : 0u, vb = k1 ? xr[k][1][d] : 0u;
-        s_xt[row * FLDW + pr] = pack_lo(va, vb);
-        s_xt[(row + 1) * FLDW + pr] = pack_hi(va, vb);
-      }
+    for (int k = 0; k < FXV; ++k) {
+      const int v = tid + 256 * k, row = v / 8, col = (v % 8) * 8;
+      *reinterpret_cast<u32x4*>(&s_x[row * FXLD + col]) =
+          (row < c.len && col < pw) ? st.x[k] : zero;
     }
 #pragma unroll
-    for (int k = 0; k < BU; ++k) {
-      const int uu = tid + 256 * k, grp8 = uu / FNP, pr = uu % FNP;
-      const bool n_ok = grp8 * 8 < g.N;
-      const bool k0 = n_ok && 2 * pr < c.len, k1 = n_ok && 2 * pr + 1 < c.len;
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        const int row = grp8 * 8 + 2 * d;
-        const uint32_t va = k0 ? br[k][0][d] : 0u, vb = k1 ? br[k][1][d] : 0u;
-        s_bt[row * FLDW + pr] = pack_lo(va, vb);
-        s_bt[(row + 1) * FLDW + pr] = pack_hi(va, vb);
-      }
+    for (int k = 0; k < BV; ++k) {
+      const int v = tid + 256 * k, row = v / (NMAX / 8), col = (v % (NMAX / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&s_b[row * BLD + col]) =
+          (row < c.len && col < g.N) ? st.b[k] : zero;
     }
   };
 
-  // ---- S_j^T = B^T (w x): wave w owns p-tile w, all n-tiles
+  // ---- acc += S_j^T = B^T (w x): wave w owns p-tile w, all n-tiles.  Both
+  // operands come from the natural-layout tiles through transpose reads.
   auto state_mma = [&](f32x4 (&acc)[NT]) {
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = zero4();
-#pragma unroll
     for (int kb = 0; kb < FC / 32; ++kb) {
-      const int off = kb * 16 + q * 4;  // dwords of tokens 32 kb + 8 q .. + 7
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(&s_xt[pl * FLDW + off]);
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&s_w[kb * 32 + q * 8]);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&s_w[kb * 32 + q * 8 + 4]);
+      const int k0 = kb * 32 + q * 8;  // this lane group's 8 tokens
+      const u32x4 xv = __builtin_bit_cast(u32x4, lds_frag_tr(s_x, FXLD, k0, k0 + 4, wave * 16));
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&s_w[k0]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&s_w[k0 + 4]);
       f32x8 xw;
 #pragma unroll
       for (int d = 0; d < 2; ++d) {
@@ -272,10 +291,10 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         FragBF av;
-        av.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                              &s_bt[(nt * 16 + r16) * FLDW + off]));
+        av.v = lds_frag_tr(s_b, BLD, k0, k0 + 4, nt * 16);
         mma(acc[nt], av, b);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -301,85 +320,162 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       for (int nt = 0; nt < NT; ++nt) carry[nt] = zero4();
     }
     float E = 1.0f;
-    for (int j = js; j < j1; ++j) {
-      Chunk c;
-      get_chunk(g, j, c);
-      load_chunk(c, false);
+    // two register sets alternate, so chunk j + 2 is in flight while chunk j
+    // is multiplied
+    Stage sa, sb;
+    Chunk ca, cb;
+    get_chunk(g, js, ca);
+    load_chunk(sa, ca, false);
+    if (js + 1 < j1) {
+      get_chunk(g, js + 1, cb);
+      load_chunk(sb, cb, false);
+    }
+    auto step = [&](Stage& st, Chunk& c, int j) {
+      __syncthreads();  // the previous chunk's matrix phase is done with LDS
+      stage_cs(st, c);
+      stage_xb(st, c);
+      if (j + 2 < j1) {  // the registers are in LDS now: refill them
+        get_chunk(g, j + 2, c);
+        load_chunk(st, c, false);
+      }
       __syncthreads();
-      stage_chunk(c);
-      __syncthreads();
-      f32x4 S[NT];
-      state_mma(S);
       const float e = fast_exp(__uint_as_float(s_misc[1]));
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(e, carry[nt][i], S[nt][i]);
+      for (int nt = 0; nt < NT; ++nt) carry[nt] *= e;
+      state_mma(carry);
       E *= e;
+    };
+    for (int j = js; j < j1; j += 2) {
+      step(sa, ca, j);
+      if (j + 1 < j1) step(sb, cb, j + 1);
     }
+    // Publish: agent-coherent stores, wait until every one has completed, then
+    // raise the flag.  The aggregate never sits in a non-coherent cache, so no
+    // cache-wide write-back is needed (see "Hand-off" above).
     float* dst = a.agg + slot(r);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) *reinterpret_cast<f32x4*>(dst + nt * 16) = carry[nt];
-    if (tid == 0) a.edec[r * a.U + u] = E;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        __hip_atomic_store(dst + nt * 16 + i, carry[nt][i], __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0)
+      __hip_atomic_store(a.edec + r * a.U + u, E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
       __hip_atomic_store(a.sync + 2 + r * a.U + u, reset ? kFlagReset : kFlagAgg,
-                         __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+
+  // the first chunk's loads go out before the wait for the carry-in
+  Chunk c;
+  get_chunk(g, j0, c);
+  Stage st;
+  load_chunk(st, c, true);
 
   // ---- carry-in: the decayed sum of the preceding ranges' aggregates, back
   // to the range where the sequence starts
   if (need_lb) {
+    if (wave == 0) {
+      // Lane k watches range r - 1 - base - k.  The ranges to sum are r - 1
+      // down to the nearest one flagged "reset"; every one of them must have
+      // published.  Flags are read once per round by all lanes together.
+      int base = 0, spins = 0, rstop = 0;
+      while (true) {
+        const int rr = r - 1 - base - lane;
+        const uint32_t f = rr >= 0 ? __hip_atomic_load(a.sync + 2 + rr * a.U + u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)
+                                   : kFlagReset;
+        const uint64_t resets = __ballot(f == kFlagReset);
+        const uint64_t missing = __ballot(f == 0);
+        const int kr = resets ? __builtin_ctzll(resets) : 64;
+        const uint64_t needed = kr >= 63 ? ~0ull : ((1ull << (kr + 1)) - 1);
+        if ((missing & needed) == 0) {
+          if (kr < 64) {
+            rstop = max(r - 1 - base - kr, 0);
+            break;
+          }
+          base += 64;  // a full window of continuing ranges: look further back
+          continue;
+        }
+        if (++spins > kSpinLimit) {
+          if (lane == 0)
+            __hip_atomic_fetch_or(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          rstop = max(r - 1 - base - (kr < 64 ? kr : 63), 0);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (lane == 0) s_misc[2] = (uint32_t)rstop;
+    }
+    __syncthreads();
+    const int rstop = (int)s_misc[2];
+    // carry = sum over rr = r-1 .. rstop of (prod of E over r-1 .. rr+1) agg_rr,
+    // accumulated newest first (a fixed order); agent-coherent loads see the
+    // published values.  Two aggregates are loaded per round trip.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) carry[nt] = zero4();
     float dec = 1.0f;
-    for (int rr = r - 1; rr >= 0; --rr) {
-      if (tid == 0) {
-        uint32_t f;
-        int spins = 0;
-        while ((f = __hip_atomic_load(a.sync + 2 + rr * a.U + u, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT)) == 0) {
-          if (++spins > kSpinLimit) {
-            __hip_atomic_fetch_or(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            f = kFlagReset;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        s_misc[2] = f;
+    auto ld = [&](const float* p) {
+      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+    int rr = r - 1;
+    for (; rr - 1 >= rstop; rr -= 2) {
+      float v[2][NT][4], e[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const float* src = a.agg + slot(rr - m);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[m][nt][i] = ld(src + nt * 16 + i);
+        e[m] = ld(a.edec + (rr - m) * a.U + u);
       }
-      __syncthreads();
-      const uint32_t f = s_misc[2];
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(dec, v[m][nt][i], carry[nt][i]);
+        dec *= e[m];
+      }
+    }
+    for (; rr >= rstop; --rr) {
       const float* src = a.agg + slot(rr);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(src + nt * 16);
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(dec, v[i], carry[nt][i]);
-      }
-      const float e = a.edec[rr * a.U + u];
-      __syncthreads();
-      if (f == kFlagReset) break;
-      dec *= e;
+        for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(dec, ld(src + nt * 16 + i), carry[nt][i]);
+      dec *= ld(a.edec + rr * a.U + u);
     }
   }
 
-  // ---- pass 2: outputs, chunk by chunk
+  // ---- pass 2: outputs, chunk by chunk.  Per chunk:
+  //   A  cumsum; the carry-in H_j to LDS as bf16 hi + lo
+  //   B  Y_off = exp(cs_l) C_l . H_j
+  //   C  x and B tiles to LDS; the next chunk's x, B, dt loads go out
+  //   D  carry = exp(Lambda) carry + S_j (accumulated in place); per k-block,
+  //      C.B^T tiles -> M -> Y_diag; the next chunk's C fragments go out
+  //   E  y through LDS; D skip, gate, store; the next chunk's z goes out
+  const int ltA = wave, ltB = 7 - wave;   // this wave's l-tiles
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  u32x4 cfr[2][NKB];
+  auto load_cfr = [&](const Chunk& cc) {
+#pragma unroll
+    for (int ui = 0; ui < 2; ++ui) {
+      const int lrow = (ui ? ltB : ltA) * 16 + r16;
+      const bf16* cbase = row_ptr<bf16>(a.C, cc.b, cc.t0, grp);
+      const uint32_t roff = (uint32_t)(min(lrow, cc.len - 1) * a.C.s1);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        cfr[ui][kb] = *reinterpret_cast<const u32x4*>(cbase + roff + min(kb * 32 + q * 8, g.N - 8));
+    }
+  };
+  load_cfr(c);
   for (int j = j0; j < j1; ++j) {
-    Chunk c;
-    get_chunk(g, j, c);
-    load_chunk(c, true);
-    __syncthreads();  // the previous chunk's epilogue is done with LDS
-    stage_chunk(c);
-    __syncthreads();
-    f32x4 S[NT];
-    state_mma(S);
-    const float lam = __uint_as_float(s_misc[1]);
-    __syncthreads();  // B^T is dead: its space takes the carry-in state
-
+    // ---- A
+    stage_cs(st, c);
     int fj, lj;
     seq_chunks(g, c.seq, fj, lj);
     if (j == fj) load_h0(carry, c.seq);
@@ -395,42 +491,27 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       *reinterpret_cast<bf16x4*>(&s_hh[pl * HLD + nt * 16 + q * 4]) = hi;
       *reinterpret_cast<bf16x4*>(&s_hl[pl * HLD + nt * 16 + q * 4]) = lo;
     }
-    const float e = fast_exp(lam);
+    // C rows past the chunk and columns past N contribute nothing
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+    for (int ui = 0; ui < 2; ++ui) {
+      const bool lok = (ui ? ltB : ltA) * 16 + r16 < c.len;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(e, carry[nt][i], S[nt][i]);
-    if (j == lj - 1 && a.hfinal && p_ok) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        if (nt * 16 < g.N)
-          *reinterpret_cast<f32x4*>(a.hfinal + state_row(c.seq) + nt * 16 + q * 4) = carry[nt];
+      for (int kb = 0; kb < NKB; ++kb)
+        cfr[ui][kb] = (lok && kb * 32 + q * 8 < g.N) ? cfr[ui][kb] : zero;
     }
     __syncthreads();
 
-    // ---- Y for l-tiles w and 7 - w, all four p-tiles, one l-tile at a time
+    // ---- B
     f32x4 acc[2][4];
-    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int ui = 0; ui < 2; ++ui) {
-      const int lt = ui ? 7 - wave : wave;
-      const int lrow = lt * 16 + r16;
-      const bool lok = lrow < c.len;
-      // C fragments: the A operand of Y_off and the B operand of C.B^T
-      u32x4 cfr[NKB];
-      const bf16* crow = row_ptr<bf16>(a.C, c.b, c.t0 + min(lrow, c.len - 1), grp);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        cfr[kb] = *reinterpret_cast<const u32x4*>(crow + min(kb * 32 + q * 8, g.N - 8));
+      const int lt = ui ? ltB : ltA;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[ui][pt] = zero4();
-      // Y_off = exp(cs_l) C_l . H_j
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const bool nok = kb * 32 + q * 8 < g.N;
-        cfr[kb] = (lok && nok) ? cfr[kb] : zero;
         FragBF cf;
-        cf.v = __builtin_bit_cast(bf16x8, cfr[kb]);
+        cf.v = __builtin_bit_cast(bf16x8, cfr[ui][kb]);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
           FragSplit hs;
@@ -438,6 +519,8 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
           hs.lo = *reinterpret_cast<const bf16x8*>(&s_hl[(pt * 16 + r16) * HLD + kb * 32 + q * 8]);
           mma(acc[ui][pt], cf, hs);
         }
+        // keep the scheduler from hoisting every k-block's reads at once
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -445,32 +528,53 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) acc[ui][pt][i] *= ex;
       }
-      // Y_diag = (L o C.B^T) x, two s-tiles (one 32-token k-block) at a time
+    }
+    __syncthreads();  // the carry-in rows are dead: the B tile takes their space
+
+    // ---- C
+    stage_xb(st, c);
+    Chunk cn = c;
+    const bool more = j + 1 < j1;
+    if (more) {
+      get_chunk(g, j + 1, cn);
+      load_chunk(st, cn, false);
+    }
+    __syncthreads();
+
+    // ---- D
+    const float e = fast_exp(__uint_as_float(s_misc[1]));
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) carry[nt] *= e;
+    state_mma(carry);
+    if (j == lj - 1 && a.hfinal && p_ok) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        if (nt * 16 < g.N)
+          *reinterpret_cast<f32x4*>(a.hfinal + state_row(c.seq) + nt * 16 + q * 4) = carry[nt];
+    }
+#pragma unroll
+    for (int ui = 0; ui < 2; ++ui) {
+      const int lt = ui ? ltB : ltA;
+      const int lrow = lt * 16 + r16;
+      const bool lok = lrow < c.len;
       const float csl = s_cs[lrow];
       for (int kp = 0; kp <= lt / 2; ++kp) {
+        // C.B^T tiles (s-tile sa / sb, l-tile lt): B rows (n contiguous) from
+        // the B tile as the A operand, the C fragments as the B operand
         const int sa = 2 * kp, sb = 2 * kp + 1;
-        const int rowa = sa * 16 + r16, rowb = sb * 16 + r16;
-        const bf16* pa = row_ptr<bf16>(a.B, c.b, c.t0 + min(rowa, c.len - 1), grp);
-        const bf16* pb = row_ptr<bf16>(a.B, c.b, c.t0 + min(rowb, c.len - 1), grp);
-        u32x4 ba[NKB], bb[NKB];
+        f32x4 va = zero4(), vb = zero4();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          const int n = min(kb * 32 + q * 8, g.N - 8);
-          ba[kb] = *reinterpret_cast<const u32x4*>(pa + n);
-          bb[kb] = *reinterpret_cast<const u32x4*>(pb + n);
+          FragBF ba, bb, cf;
+          ba.v = *reinterpret_cast<const bf16x8*>(&s_b[(sa * 16 + r16) * BLD + kb * 32 + q * 8]);
+          bb.v = *reinterpret_cast<const bf16x8*>(&s_b[(sb * 16 + r16) * BLD + kb * 32 + q * 8]);
+          cf.v = __builtin_bit_cast(bf16x8, cfr[ui][kb]);
+          mma(va, ba, cf);
+          mma(vb, bb, cf);
         }
-        // rows past the chunk only reach M entries the token mask removes,
-        // and columns past N meet zeros in the C operand
-        f32x4 cba = zero4(), cbb = zero4();
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          FragBF A0, A1, Bc;
-          A0.v = __builtin_bit_cast(bf16x8, ba[kb]);
-          A1.v = __builtin_bit_cast(bf16x8, bb[kb]);
-          Bc.v = __builtin_bit_cast(bf16x8, cfr[kb]);
-          mma(cba, A0, Bc);
-          mma(cbb, A1, Bc);
-        }
+        // M = L o C.B^T in the accumulator layout (lane: one l, tokens 4 q +
+        // 0..3 of each s-tile), used as the A operand with the tokens in that
+        // order; x is read from the x tile in the same order
         const f32x4 csa = *reinterpret_cast<const f32x4*>(&s_cs[sa * 16 + q * 4]);
         const f32x4 csb = *reinterpret_cast<const f32x4*>(&s_cs[sb * 16 + q * 4]);
         f32x8 m;
@@ -480,43 +584,25 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
           const bool kb2 = lok && sb * 16 + q * 4 + e4 <= lrow;
           const float xa = fast_exp(ka ? csl - csa[e4] : 0.0f);
           const float xb = fast_exp(kb2 ? csl - csb[e4] : 0.0f);
-          m[e4] = ka ? xa * cba[e4] : 0.0f;
-          m[4 + e4] = kb2 ? xb * cbb[e4] : 0.0f;
+          m[e4] = ka ? xa * va[e4] : 0.0f;
+          m[4 + e4] = kb2 ? xb * vb[e4] : 0.0f;
         }
         const FragSplit mf = split_f32x8(m);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) {
-          const uint32_t* xrow = &s_xt[(pt * 16 + r16) * FLDW];
-          const u32x2 xa = *reinterpret_cast<const u32x2*>(xrow + sa * 8 + q * 2);
-          const u32x2 xb = *reinterpret_cast<const u32x2*>(xrow + sb * 8 + q * 2);
-          const u32x4 xv = {xa[0], xa[1], xb[0], xb[1]};
           FragBF xf;
-          xf.v = __builtin_bit_cast(bf16x8, xv);
+          xf.v = lds_frag_tr(s_x, FXLD, sa * 16 + q * 4, sb * 16 + q * 4, pt * 16);
           mma(acc[ui][pt], mf, xf);
         }
       }
     }
-    // D skip from x^T
-    if (a.D) {
-      const float Dh = a.D[h];
-#pragma unroll
-      for (int ui = 0; ui < 2; ++ui) {
-        const int lt = ui ? 7 - wave : wave;
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          const u32x2 xv =
-              *reinterpret_cast<const u32x2*>(&s_xt[(pt * 16 + r16) * FLDW + lt * 8 + q * 2]);
-          acc[ui][pt][0] += Dh * bf16_lo_f32(xv[0]);
-          acc[ui][pt][1] += Dh * bf16_hi_f32(xv[0]);
-          acc[ui][pt][2] += Dh * bf16_lo_f32(xv[1]);
-          acc[ui][pt][3] += Dh * bf16_hi_f32(xv[1]);
-        }
-      }
-    }
-    __syncthreads();  // every wave is done with the carry-in rows
+    if (more) load_cfr(cn);
+    __syncthreads();  // the B tile is dead: its space takes y
+
+    // ---- E
 #pragma unroll
     for (int ui = 0; ui < 2; ++ui) {
-      const int lt = ui ? 7 - wave : wave;
+      const int lt = ui ? ltB : ltA;
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt)
 #pragma unroll
@@ -524,12 +610,19 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
           s_y[(lt * 16 + q * 4 + i) * FYLD + pt * 16 + r16] = acc[ui][pt][i];
     }
     __syncthreads();
-    // ---- epilogue: gate and store, coalesced 8-element rows
+    const float Dh = a.D ? a.D[h] : 0.0f;
+    TO* obase = row_ptr_mut<TO>(a.out, c.b, c.t0, h) + p0;
 #pragma unroll
-    for (int k = 0; k < FZV; ++k) {
+    for (int k = 0; k < FXV; ++k) {
       const int v = tid + 256 * k, l = v / 8, pp = (v % 8) * 8;
       if (l >= c.len || pp >= pw) continue;
       f32x8 y = Vec8<float>::load(s_y + l * FYLD + pp);
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(&s_x[l * FXLD + pp]);
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        y[2 * d] = fmaf(Dh, bf16_lo_f32(xv[d]), y[2 * d]);
+        y[2 * d + 1] = fmaf(Dh, bf16_hi_f32(xv[d]), y[2 * d + 1]);
+      }
       if (a.z.p) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -537,8 +630,13 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
           y[2 * d + 1] *= silu(bf16_hi_f32(zr[k][d]));
         }
       }
-      Vec8<TO>::store(row_ptr_mut<TO>(a.out, c.b, c.t0 + l, h) + p0 + pp, y);
+      Vec8<TO>::store(obase + (uint32_t)(l * a.out.s1 + pp), y);
     }
+    if (more) {
+      c = cn;
+      if (a.z.p) load_z(c);
+    }
+    __syncthreads();  // y and x are dead before the next chunk's staging
   }
 }
 
@@ -604,14 +702,17 @@ hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s) {
   FusedArgs a;
   a.g = g;
   a.x = f.x; a.B = f.B; a.C = f.C; a.dt = f.dt; a.z = f.z; a.out = f.out;
-  a.dt_bf16 = f.dt_dtype == DT_BF16;
   a.A = f.A; a.dt_bias = f.dt_bias; a.D = f.D; a.h0 = f.h0; a.hfinal = f.hfinal;
   a.softplus = f.softplus; a.clamp = f.clamp; a.dt_min = f.dt_min; a.dt_max = f.dt_max;
   a.U = pl.U; a.PS = pl.PS; a.R = pl.R;
   a.sync = f.sync; a.edec = f.edec; a.agg = f.agg;
   const dim3 grid((unsigned)(pl.nr * pl.U));
-  const bool ob = f.out_dtype == DT_BF16;
-#define SSD_FUSED(TO, NT) hipLaunchKernelGGL((k_fused_fwd<TO, NT>), grid, dim3(256), 0, s, a)
+  const bool ob = f.out_dtype == DT_BF16, db = f.dt_dtype == DT_BF16;
+#define SSD_FUSED(TO, NT)                                                                   \
+  do {                                                                                      \
+    if (db) hipLaunchKernelGGL((k_fused_fwd<TO, bf16, NT>), grid, dim3(256), 0, s, a);       \
+    else hipLaunchKernelGGL((k_fused_fwd<TO, float, NT>), grid, dim3(256), 0, s, a);         \
+  } while (0)
   switch (pl.NT) {
     case 2: if (ob) SSD_FUSED(bf16, 2); else SSD_FUSED(float, 2); break;
     case 4: if (ob) SSD_FUSED(bf16, 4); else SSD_FUSED(float, 4); break;
