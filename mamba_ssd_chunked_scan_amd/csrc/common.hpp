@@ -209,6 +209,16 @@ __device__ __forceinline__ bf16x8 lds_frag_tr(const bf16* tile, int ld, int k0, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// threadIdx.x passed through an empty asm statement, so that the per-lane
+// addresses derived from it are recomputed where they are used instead of
+// being hoisted out of a long loop and kept live across all of it (which can
+// exhaust the register file and force spills).  Emits no instruction.
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
 // ------------------------------------------------------------------ wave scan
 
 // Inclusive prefix sum over the 64 lanes of a wavefront.
@@ -219,6 +229,26 @@ __device__ __forceinline__ float wave_inclusive_sum(float v) {
     float o = __shfl_up(v, d, kWave);
     if (lane >= d) v += o;
   }
+  return v;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wavefront with DPP lane moves
+// (row shifts within each 16-lane row, then row broadcasts across rows); no
+// LDS traffic.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf,
+                                                    false));
+}
+__device__ __forceinline__ float wave_inclusive_sum_dpp(float v) {
+  // row_shr:1, 2, 4, 8 (lanes without a source receive 0)
+  v += dpp_f32<0x111, 0xf>(v);
+  v += dpp_f32<0x112, 0xf>(v);
+  v += dpp_f32<0x114, 0xf>(v);
+  v += dpp_f32<0x118, 0xf>(v);
+  // row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3
+  v += dpp_f32<0x142, 0xa>(v);
+  v += dpp_f32<0x143, 0xc>(v);
   return v;
 }
 

@@ -187,6 +187,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   // per-lane element offset (at most 127 rows of the tensor), so addresses
   // stay in scalar registers.
   auto load_z = [&](const Chunk& c) {
+    const int tid = opaque_tid();
     const bf16* base = row_ptr<bf16>(a.z, c.b, c.t0, h) + p0;
 #pragma unroll
     for (int k = 0; k < FXV; ++k) {
@@ -197,6 +198,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   };
   // ---- issue every global load of chunk c (x, B, dt into st; z when gating)
   auto load_chunk = [&](Stage& st, const Chunk& c, bool with_z) {
+    const int tid = opaque_tid();
     const bf16* xbase = row_ptr<bf16>(a.x, c.b, c.t0, h) + p0;
 #pragma unroll
     for (int k = 0; k < FXV; ++k) {
@@ -226,35 +228,36 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   // ---- LDS: cumsum, decay weights, and x and B in their natural row-major
   // layout (tokens x columns).  Tokens past the chunk's end (loaded as copies
   // of its last token), columns past P and past N are zeroed here.
+  // Within-chunk cumsum by wave 0, branch-free: lane l holds positions 2l and
+  // 2l + 1.  fp32 with a DPP wave scan (the bf16 inputs of this path leave
+  // ample room for fp32 rounding of cs; no LDS round trips).  softplus as
+  // max(u, 0) + log(1 + exp(-|u|)) with the hardware exp/log.
   auto stage_cs = [&](const Stage& st, const Chunk& c) {
     if (wave == 0) {
-      double av[2], run = 0.0;
+      float av[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const int l = 2 * lane + e;
-        float aa = 0.0f;
-        if (l < c.len) {
-          const float uu = st.dt[e] + bias;
-          float d = a.softplus ? softplus_f32(uu) : uu;
-          if (a.clamp) d = fminf(fmaxf(d, a.dt_min), a.dt_max);
-          aa = d * Ah;
-        }
-        run += (double)aa;
-        av[e] = run;
+        const float uu = st.dt[e] + bias;
+        float d = uu;
+        if (a.softplus) d = fmaxf(uu, 0.0f) + __logf(1.0f + __expf(-fabsf(uu)));
+        if (a.clamp) d = fminf(fmaxf(d, a.dt_min), a.dt_max);
+        av[e] = 2 * lane + e < c.len ? d * Ah : 0.0f;
       }
-      const double incl = wave_inclusive_sum_f64(run);
-      const double excl = incl - run;
-      const float c0 = (float)(excl + av[0]), c1 = (float)(excl + av[1]);
+      const float pair = av[0] + av[1];
+      const float incl = wave_inclusive_sum_dpp(pair);
+      const float c0 = incl - pair + av[0], c1 = incl;
       s_cs[2 * lane] = c0;
       s_cs[2 * lane + 1] = c1;
       const int ll = c.len - 1;
-      const float lam = __shfl((ll & 1) ? c1 : c0, ll >> 1, kWave);
+      const float lam = __int_as_float(
+          __builtin_amdgcn_readlane(__float_as_int((ll & 1) ? c1 : c0), ll >> 1));
       s_w[2 * lane] = 2 * lane < c.len ? fast_exp(lam - c0) : 0.0f;
       s_w[2 * lane + 1] = 2 * lane + 1 < c.len ? fast_exp(lam - c1) : 0.0f;
       if (lane == 0) s_misc[1] = __float_as_uint(lam);
     }
   };
   auto stage_xb = [&](const Stage& st, const Chunk& c) {
+    const int tid = opaque_tid();
     const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < FXV; ++k) {
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   Chunk c;
   get_chunk(g, j0, c);
   Stage st;
-  load_chunk(st, c, true);
+  load_chunk(st, c, false);
 
   // ---- carry-in: the decayed sum of the preceding ranges' aggregates, back
   // to the range where the sequence starts
@@ -452,12 +455,14 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   }
 
   // ---- pass 2: outputs, chunk by chunk.  Per chunk:
-  //   A  cumsum; the carry-in H_j to LDS as bf16 hi + lo
+  //   A  the carry-in H_j to LDS as bf16 hi + lo (the cumsum was staged at
+  //      the end of the previous chunk)
   //   B  Y_off = exp(cs_l) C_l . H_j
-  //   C  x and B tiles to LDS; the next chunk's x, B, dt loads go out
+  //   C  x and B tiles to LDS; this chunk's z and the next chunk's x, B, dt
+  //      loads go out
   //   D  carry = exp(Lambda) carry + S_j (accumulated in place); per k-block,
   //      C.B^T tiles -> M -> Y_diag; the next chunk's C fragments go out
-  //   E  y through LDS; D skip, gate, store; the next chunk's z goes out
+  //   E  y through LDS; D skip, gate, store; the next chunk's cumsum
   const int ltA = wave, ltB = 7 - wave;   // this wave's l-tiles
   const u32x4 zero = {0u, 0u, 0u, 0u};
   u32x4 cfr[2][NKB];
@@ -473,11 +478,11 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     }
   };
   load_cfr(c);
+  int fj, lj;  // the current chunk's sequence: chunks [fj, lj)
+  seq_chunks(g, c.seq, fj, lj);
+  stage_cs(st, c);
   for (int j = j0; j < j1; ++j) {
     // ---- A
-    stage_cs(st, c);
-    int fj, lj;
-    seq_chunks(g, c.seq, fj, lj);
     if (j == fj) load_h0(carry, c.seq);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -533,11 +538,18 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
 
     // ---- C
     stage_xb(st, c);
+    // Loads complete in issue order as far as the wait counter is concerned, so
+    // z (needed in this chunk's epilogue) goes out before the next chunk's x,
+    // B and dt (needed one chunk later): waiting for z then never waits for
+    // the prefetch.
+    if (a.z.p) load_z(c);
     Chunk cn = c;
+    int fn = fj, ln = lj;
     const bool more = j + 1 < j1;
     if (more) {
       get_chunk(g, j + 1, cn);
       load_chunk(st, cn, false);
+      if (cn.seq != c.seq) seq_chunks(g, cn.seq, fn, ln);
     }
     __syncthreads();
 
@@ -612,10 +624,12 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     __syncthreads();
     const float Dh = a.D ? a.D[h] : 0.0f;
     TO* obase = row_ptr_mut<TO>(a.out, c.b, c.t0, h) + p0;
+    const int etid = opaque_tid();
 #pragma unroll
     for (int k = 0; k < FXV; ++k) {
-      const int v = tid + 256 * k, l = v / 8, pp = (v % 8) * 8;
-      if (l >= c.len || pp >= pw) continue;
+      // computed for every row (rows past the chunk hold finite values), only
+      // the store is conditional: straight-line code keeps the waits precise
+      const int v = etid + 256 * k, l = v / 8, pp = (v % 8) * 8;
       f32x8 y = Vec8<float>::load(s_y + l * FYLD + pp);
       const u32x4 xv = *reinterpret_cast<const u32x4*>(&s_x[l * FXLD + pp]);
 #pragma unroll
@@ -630,11 +644,13 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
           y[2 * d + 1] *= silu(bf16_hi_f32(zr[k][d]));
         }
       }
-      Vec8<TO>::store(obase + (uint32_t)(l * a.out.s1 + pp), y);
+      if (l < c.len && pp < pw) Vec8<TO>::store(obase + (uint32_t)(l * a.out.s1 + pp), y);
     }
     if (more) {
       c = cn;
-      if (a.z.p) load_z(c);
+      fj = fn;
+      lj = ln;
+      stage_cs(st, c);  // cs is free: nothing reads it after the matrix phase
     }
     __syncthreads();  // y and x are dead before the next chunk's staging
   }
