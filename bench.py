@@ -183,8 +183,9 @@ def main():
     prob = ssd.problem_from(x, B, w.chunk_size, cu_seqlens=cu, state_dtype=sdt)
     algo = args.algo
     if algo == "auto":
-        # the staged path is the faster one at present (see the design notes)
-        algo = "staged"
+        # the single-pass forward where it applies (bf16 inputs, d_state <= 128),
+        # the staged one otherwise
+        algo = "fused" if (w.dtype == "bf16" and w.dstate <= 128) else "staged"
     K = prob.num_chunks()
     out = torch.empty(x.shape, dtype=odt, device=dev)
     nseq = prob.nseq if prob.packed else prob.batch

@@ -34,12 +34,12 @@
 // owns: no residency assumption, no deadlock.  Every wait is bounded; on
 // timeout an error bit is set in the workspace and the kernel still finishes.
 //
-// Hand-off.  Aggregates, decays and flags are written and read with
-// agent-scope atomic accesses, which on gfx950 are plain loads and stores that
-// go to the level of the memory system all XCDs share (the L2 of each XCD is
-// not coherent with the others).  A publisher stores its aggregate, waits
-// until all its stores have completed (s_waitcnt), passes a workgroup barrier
-// and only then stores the flag; a reader polls the flag and issues its
+// Hand-off.  Aggregates, decays and flags are written with agent-scope atomic
+// stores, which on gfx950 are plain stores that go through to the level of
+// the memory system all XCDs share (the L2 of each XCD is not coherent with
+// the others).  A publisher stores its aggregate, waits until all its stores
+// have completed (s_waitcnt), passes a workgroup barrier and only then stores
+// the flag; a reader polls the flag with agent-scope loads and issues its
 // aggregate loads only after it has seen it.  Release/acquire fences would do
 // the same job through a write-back and an invalidation of the whole L2 of the
 // XCD, which costs far more than the few aggregates involved.
@@ -415,8 +415,12 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     __syncthreads();
     const int rstop = (int)s_misc[2];
     // carry = sum over rr = r-1 .. rstop of (prod of E over r-1 .. rr+1) agg_rr,
-    // accumulated newest first (a fixed order); agent-coherent loads see the
-    // published values.  Two aggregates are loaded per round trip.
+    // accumulated newest first (a fixed order).  Two aggregates are loaded per
+    // round trip.  The aggregate data is read with ordinary (cacheable)
+    // loads: its lines are read only after their flag was seen, so no cache
+    // can hold an older copy from this launch, and launch boundaries leave no
+    // stale lines behind; each aggregate occupies whole cache lines.  The
+    // decays share cache lines across ranges, so they are read coherently.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) carry[nt] = zero4();
     float dec = 1.0f;
@@ -432,7 +436,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[m][nt][i] = ld(src + nt * 16 + i);
+          for (int i = 0; i < 4; ++i) v[m][nt][i] = src[nt * 16 + i];
         e[m] = ld(a.edec + (rr - m) * a.U + u);
       }
 #pragma unroll
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(dec, ld(src + nt * 16 + i), carry[nt][i]);
+        for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(dec, src[nt * 16 + i], carry[nt][i]);
       dec *= ld(a.edec + rr * a.U + u);
     }
   }
