@@ -16,8 +16,15 @@ kernel is bracketed by HIP events on the stream it runs on, which gives each
 kernel's average duration; the dominant one is reported against its roofline
 (algorithmic bytes per launch / average duration vs 8 TB/s HBM).
 
+Cold: after the timed region, --cold-steps forwards are timed one by one with
+HIP events, each preceded (outside the events) by a 512 MB write that evicts
+the inputs from L2 and the 256 MB MALL; their median is reported as `cold`.
+
 cpu_baseline: the fp64 oracle (C, OpenMP) on the host's cores over the same
 workload, timed separately (a reported baseline, not the target).
+
+--copy-calibration makes the program start with one 512 MiB device-to-device
+copy, the reference transfer that HBM byte counters are scaled against.
 """
 from __future__ import annotations
 
@@ -48,7 +55,12 @@ def parse():
     ap.add_argument("--out-dtype", default="bf16", choices=["f32", "bf16"])
     ap.add_argument("--layout", default="xbc", choices=["xbc", "contiguous"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-repeats", type=int, default=3)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="repeat the oracle until this much CPU time has been spent (min 3 runs)")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="event-timed forwards each preceded by a 512 MB cache flush")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="copy a 512 MiB device buffer once first (HBM counter calibration)")
     return ap.parse_args()
 
 
@@ -84,13 +96,15 @@ def stage_bytes(w, K, state_bytes, out_bytes, in_bytes=2):
 def stage_flops(w, K):
     """Useful matrix flops per launch (causal half only, no hi/lo second pass)."""
     H, P, G, N, C = w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk_size
-    return {
+    f = {
         "chunk_cumsum": 0,
         "bmm_chunk": K * G * C * (C + 1) * N,
         "chunk_state": 2 * K * H * C * P * N,
         "state_passing": 2 * K * H * P * N,
         "chunk_scan": 2 * K * H * C * N * P + K * H * C * (C + 1) * P,
     }
+    f["fused_fwd"] = f["bmm_chunk"] + f["chunk_state"] + f["chunk_scan"]
+    return f
 
 
 KERNEL_SOURCES = {"chunk_cumsum": "chunk_cumsum.hip", "bmm_chunk": "bmm_chunk.hip",
@@ -122,13 +136,13 @@ def measured_traffic(stage, key):
     return rec["fetch_bytes"] + rec["write_bytes"]
 
 
-def cpu_baseline(w, inp, repeats):
+def cpu_baseline(w, inp, seconds):
     import oracle
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
     times = []
     oracle.ssd_fwd(inp.x, inp.B, inp.C, inp.dt, inp.A, inp.dt_bias, inp.D, inp.z,
                    cu_seqlens=inp.cu_seqlens, threads=threads)  # warm-up (page-in)
-    for _ in range(repeats):
+    while len(times) < 3 or (sum(times) < seconds and len(times) < 1000):
         t0 = time.perf_counter()
         oracle.ssd_fwd(inp.x, inp.B, inp.C, inp.dt, inp.A, inp.dt_bias, inp.D, inp.z,
                        cu_seqlens=inp.cu_seqlens, threads=threads)
@@ -136,7 +150,8 @@ def cpu_baseline(w, inp, repeats):
     t = float(np.median(times))
     return {"value": w.tokens / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": (f"the whole {w.name} workload ({w.tokens} tokens, all {w.nheads} heads), "
-                       f"fp64 sequential recurrence, median of {repeats} runs after 1 warm-up"),
+                       f"fp64 sequential recurrence, median of {len(times)} runs "
+                       f"({sum(times):.1f} s) after 1 warm-up"),
             "seconds": t, "cpu": platform.processor() or platform.machine()}
 
 
@@ -157,6 +172,12 @@ def main():
     w = WORKLOADS[args.workload]
     inp = make_inputs(w)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     sdt = torch.float32 if args.state_dtype == "f32" else torch.bfloat16
     odt = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
@@ -246,6 +267,22 @@ def main():
     wall = time.perf_counter() - t0
 
     per_kernel_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in events[n]])) for n in names}
+
+    # cold: a 512 MB write before each forward evicts L2 and the MALL
+    cold_ms = []
+    if args.cold_steps > 0:
+        flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        for _ in range(args.cold_steps):
+            flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _name, fn in launches():
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            cold_ms.append(e0.elapsed_time(e1))
+        del flush
     ms_per_step = wall * 1e3 / args.steps
     tokens = w.tokens
     value = tokens * args.steps / wall
@@ -303,10 +340,15 @@ def main():
         },
         "stages": stages,
         "path_roofline_frac": round(roof_time_ms / ms_per_step, 4),
+        "cold": ({"ms_median": round(float(np.median(cold_ms)), 5),
+                  "value": round(tokens / (float(np.median(cold_ms)) * 1e-3), 1),
+                  "steps": len(cold_ms),
+                  "note": "median of event-timed forwards, each after a 512 MB cache flush"}
+                 if cold_ms else None),
         "gpu": torch.cuda.get_device_name(0),
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_repeats)
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 
