@@ -83,7 +83,7 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
 typedef enum ssd_algo {
   SSD_ALGO_STAGED = 0, /* the five stage kernels in sequence */
-  SSD_ALGO_FUSED = 1   /* one launch for the whole forward pass */
+  SSD_ALGO_FUSED = 1   /* one pass over the inputs: a reset kernel + one fused kernel */
 } ssd_algo;
 
 /* A strided tensor view.  Shape is implied by the argument's role. */
@@ -251,13 +251,20 @@ typedef struct ssd_fwd_args {
 
 /* The whole forward pass.  SSD_ALGO_STAGED runs chunk cumsum, BMM, chunk
  * state, state passing and chunk scan (vLLM PR 27299 "Purpose", the five
- * stages); SSD_ALGO_FUSED computes the same result in one launch (the same
- * page: one fused kernel that reorders work and synchronises to avoid the
- * intermediate round trips).  In packed mode the chunk table is built inside
- * the workspace.  workspace: device memory of at least
- * ssd_workspace_size(p, algo) bytes, 256-byte aligned, owned by the caller,
- * contents need not be initialised; it must not be shared by calls that
- * overlap in time. */
+ * stages).  SSD_ALGO_FUSED computes the same result in one fused kernel (the
+ * same page: one kernel that recomputes the cumsum and C.B^T per tile and
+ * hands the chunk state between workgroups instead of storing the
+ * intermediates), preceded by a small reset kernel; it always works on
+ * 128-token chunks (the result does not depend on the chunk length), takes
+ * bf16 x, B, C (and z) and dstate <= 128, and returns SSD_ERR_UNSUPPORTED
+ * otherwise.  initial_states and final_states must be 16-byte aligned for
+ * it.  Its results are bit-identical run to run for a given problem shape;
+ * two different shapes of one computation (e.g. a sequence split in two and
+ * resumed from the final state) agree to fp32 rounding of the states.
+ * In packed mode the chunk table is built inside the workspace.  workspace:
+ * device memory of at least ssd_workspace_size(p, algo) bytes, 256-byte
+ * aligned, owned by the caller, contents need not be initialised; it must not
+ * be shared by calls that overlap in time. */
 ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* a,
                        void* workspace, size_t ws_bytes, hipStream_t stream);
 
