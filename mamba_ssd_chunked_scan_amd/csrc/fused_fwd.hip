@@ -186,32 +186,59 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   // Tile loads: a uniform base pointer (the chunk's first row) plus a 32-bit
   // per-lane element offset (at most 127 rows of the tensor), so addresses
   // stay in scalar registers.
-  auto load_z = [&](const Chunk& c) {
+  // Tile geometry of the 16-byte row pieces: x, z and out rows hold 8 pieces
+  // (64 columns), B rows NMAX / 8.  A full chunk with a full P slab and N ==
+  // NMAX (the common case) needs no clamping: each lane computes one base
+  // offset and every further piece adds a uniform stride.  Other chunks take
+  // the clamped path.
+  constexpr int BPR = NMAX / 8;           // B pieces per row
+  constexpr int BROWS = 256 / BPR;        // B rows per pass of the workgroup
+  const bool dims_full = pw == 64 && g.N == NMAX;
+  auto x_offsets = [&](const Chunk& c, int64_t s1, uint32_t (&off)[FXV]) {
     const int tid = opaque_tid();
-    const bf16* base = row_ptr<bf16>(a.z, c.b, c.t0, h) + p0;
+    const int row0 = tid / 8, col = (tid % 8) * 8;
+    if (dims_full && c.len == FC) {
+      const uint32_t o = (uint32_t)(row0 * s1 + col), step = (uint32_t)(32 * s1);
 #pragma unroll
-    for (int k = 0; k < FXV; ++k) {
-      const int v = tid + 256 * k, row = v / 8, col = (v % 8) * 8;
-      const uint32_t off = (uint32_t)(min(row, c.len - 1) * a.z.s1 + min(col, pw - 8));
-      zr[k] = *reinterpret_cast<const u32x4*>(base + off);
+      for (int k = 0; k < FXV; ++k) off[k] = o + k * step;
+    } else {
+#pragma unroll
+      for (int k = 0; k < FXV; ++k)
+        off[k] = (uint32_t)(min(row0 + 32 * k, c.len - 1) * s1 + min(col, pw - 8));
     }
+  };
+  auto load_z = [&](const Chunk& c) {
+    const bf16* base = row_ptr<bf16>(a.z, c.b, c.t0, h) + p0;
+    uint32_t off[FXV];
+    x_offsets(c, a.z.s1, off);
+#pragma unroll
+    for (int k = 0; k < FXV; ++k) zr[k] = *reinterpret_cast<const u32x4*>(base + off[k]);
   };
   // ---- issue every global load of chunk c (x, B, dt into st; z when gating)
   auto load_chunk = [&](Stage& st, const Chunk& c, bool with_z) {
-    const int tid = opaque_tid();
     const bf16* xbase = row_ptr<bf16>(a.x, c.b, c.t0, h) + p0;
+    {
+      uint32_t off[FXV];
+      x_offsets(c, a.x.s1, off);
 #pragma unroll
-    for (int k = 0; k < FXV; ++k) {
-      const int v = tid + 256 * k, row = v / 8, col = (v % 8) * 8;
-      const uint32_t off = (uint32_t)(min(row, c.len - 1) * a.x.s1 + min(col, pw - 8));
-      st.x[k] = *reinterpret_cast<const u32x4*>(xbase + off);
+      for (int k = 0; k < FXV; ++k) st.x[k] = *reinterpret_cast<const u32x4*>(xbase + off[k]);
     }
     const bf16* bbase = row_ptr<bf16>(a.B, c.b, c.t0, grp);
+    {
+      const int tid = opaque_tid();
+      const int row0 = tid / BPR, col = (tid % BPR) * 8;
+      uint32_t off[BV];
+      if (dims_full && c.len == FC) {
+        const uint32_t o = (uint32_t)(row0 * a.B.s1 + col), step = (uint32_t)(BROWS * a.B.s1);
 #pragma unroll
-    for (int k = 0; k < BV; ++k) {
-      const int v = tid + 256 * k, row = v / (NMAX / 8), col = (v % (NMAX / 8)) * 8;
-      const uint32_t off = (uint32_t)(min(row, c.len - 1) * a.B.s1 + min(col, g.N - 8));
-      st.b[k] = *reinterpret_cast<const u32x4*>(bbase + off);
+        for (int k = 0; k < BV; ++k) off[k] = o + k * step;
+      } else {
+#pragma unroll
+        for (int k = 0; k < BV; ++k)
+          off[k] = (uint32_t)(min(row0 + BROWS * k, c.len - 1) * a.B.s1 + min(col, g.N - 8));
+      }
+#pragma unroll
+      for (int k = 0; k < BV; ++k) st.b[k] = *reinterpret_cast<const u32x4*>(bbase + off[k]);
     }
     if (wave == 0) {
 #pragma unroll
@@ -259,17 +286,24 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   auto stage_xb = [&](const Stage& st, const Chunk& c) {
     const int tid = opaque_tid();
     const u32x4 zero = {0u, 0u, 0u, 0u};
+    const int xrow = tid / 8, xcol = (tid % 8) * 8;
+    const int brow = tid / BPR, bcol = (tid % BPR) * 8;
+    bf16* xd = &s_x[xrow * FXLD + xcol];
+    bf16* bd = &s_b[brow * BLD + bcol];
+    if (dims_full && c.len == FC) {
 #pragma unroll
-    for (int k = 0; k < FXV; ++k) {
-      const int v = tid + 256 * k, row = v / 8, col = (v % 8) * 8;
-      *reinterpret_cast<u32x4*>(&s_x[row * FXLD + col]) =
-          (row < c.len && col < pw) ? st.x[k] : zero;
-    }
+      for (int k = 0; k < FXV; ++k) *reinterpret_cast<u32x4*>(xd + 32 * k * FXLD) = st.x[k];
 #pragma unroll
-    for (int k = 0; k < BV; ++k) {
-      const int v = tid + 256 * k, row = v / (NMAX / 8), col = (v % (NMAX / 8)) * 8;
-      *reinterpret_cast<u32x4*>(&s_b[row * BLD + col]) =
-          (row < c.len && col < g.N) ? st.b[k] : zero;
+      for (int k = 0; k < BV; ++k) *reinterpret_cast<u32x4*>(bd + BROWS * k * BLD) = st.b[k];
+    } else {
+#pragma unroll
+      for (int k = 0; k < FXV; ++k)
+        *reinterpret_cast<u32x4*>(xd + 32 * k * FXLD) =
+            (xrow + 32 * k < c.len && xcol < pw) ? st.x[k] : zero;
+#pragma unroll
+      for (int k = 0; k < BV; ++k)
+        *reinterpret_cast<u32x4*>(bd + BROWS * k * BLD) =
+            (brow + BROWS * k < c.len && bcol < g.N) ? st.b[k] : zero;
     }
   };
 
@@ -629,11 +663,14 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     const float Dh = a.D ? a.D[h] : 0.0f;
     TO* obase = row_ptr_mut<TO>(a.out, c.b, c.t0, h) + p0;
     const int etid = opaque_tid();
+    const int erow = etid / 8, ecol = (etid % 8) * 8;
+    const uint32_t eoff = (uint32_t)(erow * a.out.s1 + ecol), estep = (uint32_t)(32 * a.out.s1);
+    const bool efull = dims_full && c.len == FC;
 #pragma unroll
     for (int k = 0; k < FXV; ++k) {
       // computed for every row (rows past the chunk hold finite values), only
       // the store is conditional: straight-line code keeps the waits precise
-      const int v = etid + 256 * k, l = v / 8, pp = (v % 8) * 8;
+      const int l = erow + 32 * k, pp = ecol;
       f32x8 y = Vec8<float>::load(s_y + l * FYLD + pp);
       const u32x4 xv = *reinterpret_cast<const u32x4*>(&s_x[l * FXLD + pp]);
 #pragma unroll
@@ -648,7 +685,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
           y[2 * d + 1] *= silu(bf16_hi_f32(zr[k][d]));
         }
       }
-      if (l < c.len && pp < pw) Vec8<TO>::store(obase + (uint32_t)(l * a.out.s1 + pp), y);
+      if (efull || (l < c.len && pp < pw)) Vec8<TO>::store(obase + eoff + k * estep, y);
     }
     if (more) {
       c = cn;
