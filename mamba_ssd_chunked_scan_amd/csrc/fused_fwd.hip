@@ -535,12 +535,14 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       *reinterpret_cast<bf16x4*>(&s_hl[pl * HLD + nt * 16 + q * 4]) = lo;
     }
     // C rows past the chunk and columns past N contribute nothing
+    if (!(dims_full && c.len == FC)) {
 #pragma unroll
-    for (int ui = 0; ui < 2; ++ui) {
-      const bool lok = (ui ? ltB : ltA) * 16 + r16 < c.len;
+      for (int ui = 0; ui < 2; ++ui) {
+        const bool lok = (ui ? ltB : ltA) * 16 + r16 < c.len;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-        cfr[ui][kb] = (lok && kb * 32 + q * 8 < g.N) ? cfr[ui][kb] : zero;
+        for (int kb = 0; kb < NKB; ++kb)
+          cfr[ui][kb] = (lok && kb * 32 + q * 8 < g.N) ? cfr[ui][kb] : zero;
+      }
     }
     __syncthreads();
 

@@ -2,7 +2,8 @@
 shapes and sequence structures its work split depends on: partial 64-row P
 slabs, every d_state tile width, long look-back chains, ranges of several
 chunks, packed batches whose sequences start and end inside ranges (and empty
-sequences and empty ranges), and a workspace that starts out as garbage.
+sequences and empty ranges), a workspace that starts out as garbage, and HIP
+graph capture (both paths).
 """
 import numpy as np
 import pytest
@@ -136,3 +137,47 @@ def test_rejects_large_dstate():
     with pytest.raises(ssd.SSDError) as e:
         run(inp, w)
     assert e.value.status == 5
+
+
+@pytest.mark.parametrize("algo", ["staged", "fused"])
+def test_graph_capture_replays_match_eager(algo):
+    # every ssd_* call is stream-ordered device work with no host
+    # synchronisation or allocation, so a whole forward can be captured in a
+    # HIP graph; each replay (with eager work in between) must reproduce the
+    # eager result exactly
+    w = small_workload("graph", seqlen=700, nheads=8, headdim=64, ngroups=2, dstate=64,
+                       chunk_size=128, seqlens=(300, 0, 1, 399))
+    inp = with_initial_states(make_inputs(w))
+    dev = device_inputs(inp, torch.bfloat16)
+    prob = ssd.problem_from(dev["x"], dev["B"], 128, cu_seqlens=dev["cu_seqlens"])
+    ws = torch.empty(prob.workspace_size(algo), dtype=torch.uint8, device="cuda")
+    out = torch.empty(dev["x"].shape, dtype=torch.float32, device="cuda")
+    fin = torch.empty(dev["initial_states"].shape, dtype=torch.float32, device="cuda")
+
+    def fwd():
+        ssd.ssd_forward(dev["x"], dev["B"], dev["C"], dev["dt"], dev["A"], dev["dt_bias"],
+                        dev["D"], dev["z"], dev["initial_states"], cu_seqlens=dev["cu_seqlens"],
+                        chunk_size=128, out=out, final_states=fin, algo=algo, workspace=ws)
+
+    fwd()
+    torch.cuda.synchronize()
+    ref_out, ref_fin = out.clone(), fin.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fwd()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd()
+    for _ in range(4):
+        out.fill_(float("nan"))
+        fin.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out) and torch.equal(fin, ref_fin)
+        fwd()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out)
