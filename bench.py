@@ -107,9 +107,12 @@ def stage_flops(w, K):
     return f
 
 
-KERNEL_SOURCES = {"chunk_cumsum": "chunk_cumsum.hip", "bmm_chunk": "bmm_chunk.hip",
-                  "chunk_state": "chunk_state.hip", "state_passing": "state_passing.hip",
-                  "chunk_scan": "chunk_scan.hip", "fused_fwd": "fused_fwd.hip"}
+KERNEL_SOURCES = {"chunk_cumsum": ("chunk_cumsum.hip", "stage_cumsum.hpp"),
+                  "bmm_chunk": ("bmm_chunk.hip", "stage_bmm.hpp"),
+                  "chunk_state": ("chunk_state.hip", "stage_state.hpp"),
+                  "state_passing": ("state_passing.hip", "stage_passing.hpp"),
+                  "chunk_scan": ("chunk_scan.hip", "stage_scan.hpp"),
+                  "fused_fwd": ("fused_fwd.hip", "stage_varlen.hpp")}
 
 
 def measured_traffic(stage, key):
@@ -129,7 +132,7 @@ def measured_traffic(stage, key):
         return None
     csrc = os.path.join(ROOT, "mamba_ssd_chunked_scan_amd", "csrc")
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCES[stage], "common.hpp", "kernels.hpp"):
+    for f in (*KERNEL_SOURCES[stage], "common.hpp", "kernels.hpp"):
         h.update(open(os.path.join(csrc, f), "rb").read())
     if h.hexdigest()[:16] != rec["source_sha256_16"]:
         return None

@@ -25,6 +25,8 @@ namespace ssd {
 typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
@@ -40,12 +42,23 @@ template <typename T> __device__ __forceinline__ float to_f32(T v);
 template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ float to_f32<bf16>(bf16 v) { return (float)v; }
 
+// A value's bits in a 32-bit register (bf16 zero-extended) and back to fp32.
+__device__ __forceinline__ uint32_t raw_bits(float v) { return __float_as_uint(v); }
+__device__ __forceinline__ uint32_t raw_bits(bf16 v) {
+  return (uint32_t)__builtin_bit_cast(unsigned short, v);
+}
+template <typename T> __device__ __forceinline__ float from_bits(uint32_t r);
+template <> __device__ __forceinline__ float from_bits<float>(uint32_t r) { return __uint_as_float(r); }
+template <> __device__ __forceinline__ float from_bits<bf16>(uint32_t r) { return __uint_as_float(r << 16); }
+
 template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
 
 // exp(x) through the hardware base-2 exponential.
 __device__ __forceinline__ float fast_exp(float x) { return __expf(x); }
+// 2^x: the hardware exponential itself.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // softplus(u) = log(1 + e^u); for u > 20 the correction log1p(e^-u) is below
 // 2.1e-9 relative and u itself is returned.
@@ -118,14 +131,31 @@ struct FragSplit { bf16x8 hi, lo; };
 // fp32 path: eight fp32 values.
 struct FragF32 { f32x8 v; };
 
+// Two fp32 values rounded (to nearest even) to a packed bf16 pair in one
+// conversion: the first in the low half.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// hi = bf16(a), lo = bf16(a - hi), per pair of elements.
+__device__ __forceinline__ void split_pair(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - bf16_lo_f32(hi), b - bf16_hi_f32(hi));
+}
+
 __device__ __forceinline__ FragSplit split_f32x8(f32x8 a) {
-  FragSplit f;
+  u32x4 hi, lo;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    bf16 h = (bf16)a[i];
-    f.hi[i] = h;
-    f.lo[i] = (bf16)(a[i] - (float)h);
+  for (int i = 0; i < 4; ++i) {
+    uint32_t h, l;
+    split_pair(a[2 * i], a[2 * i + 1], h, l);
+    hi[i] = h;
+    lo[i] = l;
   }
+  FragSplit f;
+  f.hi = __builtin_bit_cast(bf16x8, hi);
+  f.lo = __builtin_bit_cast(bf16x8, lo);
   return f;
 }
 
@@ -298,11 +328,21 @@ struct Chunk {
 // Chunk table header size and accessors (see the layout in ssd.h).
 constexpr int kMetaHeader = 4;
 
+// The chunk table is built by an earlier kernel and only read by the kernels
+// that walk it, so it is read through the constant address space: at uniform
+// indices these are scalar loads, which do not queue behind the vector loads a
+// kernel has in flight.
+typedef __attribute__((address_space(4))) const int32_t MetaWord;
+__device__ __forceinline__ int32_t meta_word(const int32_t* meta, int i) {
+  return ((const MetaWord*)meta)[i];
+}
+
 __device__ __forceinline__ bool get_chunk(const Geo& g, int j, Chunk& c) {
   if (g.meta) {
-    if (j >= g.meta[0]) return false;
-    const int32_t* e = g.meta + kMetaHeader + 3 * j;
-    c.seq = e[0]; c.t0 = e[1]; c.len = e[2]; c.b = 0;
+    if (j >= meta_word(g.meta, 0)) return false;
+    const int e = kMetaHeader + 3 * j;
+    c.seq = meta_word(g.meta, e); c.t0 = meta_word(g.meta, e + 1); c.len = meta_word(g.meta, e + 2);
+    c.b = 0;
     return true;
   }
   if (j >= g.K) return false;
@@ -317,8 +357,8 @@ __device__ __forceinline__ bool get_chunk(const Geo& g, int j, Chunk& c) {
 // Range of logical chunks [first, last) of sequence i.
 __device__ __forceinline__ void seq_chunks(const Geo& g, int i, int& first, int& last) {
   if (g.meta) {
-    const int32_t* fc = g.meta + kMetaHeader + 3 * g.K;
-    first = fc[i]; last = fc[i + 1];
+    const int fc = kMetaHeader + 3 * g.K;
+    first = meta_word(g.meta, fc + i); last = meta_word(g.meta, fc + i + 1);
   } else {
     first = i * g.nc; last = first + g.nc;
   }
@@ -329,6 +369,19 @@ struct TArg {
   const void* p;
   int64_t s0, s1, s2;   // batch, token, head/group strides (elements)
 };
+
+// base + off elements with the offset in 32-bit arithmetic: a uniform base
+// stays in scalar registers and the per-lane part is one 32-bit vector
+// register (the scalar-base form of the global loads and stores).  The byte
+// offset must fit in 32 bits.
+template <typename T>
+__device__ __forceinline__ const T* at(const T* base, uint32_t off) {
+  return reinterpret_cast<const T*>(reinterpret_cast<const char*>(base) + off * (uint32_t)sizeof(T));
+}
+template <typename T>
+__device__ __forceinline__ T* at(T* base, uint32_t off) {
+  return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off * (uint32_t)sizeof(T));
+}
 
 template <typename T>
 __device__ __forceinline__ const T* row_ptr(const TArg& a, int b, int t, int hg) {

@@ -27,7 +27,8 @@
 //      run to run);
 //   3. (pass 2) walks its chunks: cumsum from dt, chunk state S_j, the carry-in
 //      H_j of the chunk staged in LDS as bf16 hi + lo, C.B^T tile by tile,
-//      Y_off + Y_diag + D x, SiLU gate, store; then H_{j+1} = exp(Lambda_j)
+//      Y_off + Y_diag (with the D skip on its diagonal), SiLU gate, store;
+//      then H_{j+1} = exp(Lambda_j)
 //      H_j + S_j in registers, and the final state at a sequence's last chunk.
 // Workgroups take (unit, range) in order from an atomic ticket counter, so a
 // workgroup only ever waits for work that a running or finished workgroup
@@ -59,10 +60,11 @@
 //     tile (lane: one l, four consecutive s) is used directly as the A operand
 //     of Y_diag = M . x with the k (token) order permuted to match; the x
 //     operand is read from the x tile in that same order, so M never goes
-//     through LDS.
-// Precision is that of the staged path: exact bf16 inputs, fp32-derived
-// operands (decay-weighted x, M = L o CB, the carried state) split into bf16
-// hi + lo, fp32 accumulation, fp64 within-chunk cumsum rounded once.
+//     through LDS.  D x is folded into the same product: M gets D added on
+//     its diagonal (y_l = sum_s M_ls x_s + D x_l).
+// Precision: exact bf16 inputs, fp32-derived operands (decay-weighted x,
+// M = L o CB + D I, the carried state) split into bf16 hi + lo, fp32
+// accumulation, and an fp32 within-chunk cumsum (bf16 inputs only).
 #include "kernels.hpp"
 #include "stage_varlen.hpp"
 
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   const int h = u / a.PS, p0 = (u % a.PS) * 64;
   const int grp = h / g.hpg;
   const int pw = min(64, g.P - p0);
-  const int Kr = g.meta ? g.meta[0] : g.K;
+  const int Kr = g.meta ? meta_word(g.meta, 0) : g.K;
   const int j0 = r * a.R, j1 = min(j0 + a.R, Kr);
   if (j0 >= j1) return;
 
@@ -162,24 +164,35 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   const int pl = wave * 16 + r16;
   const bool p_ok = pl < pw;
   const int64_t PN = (int64_t)g.P * g.N;
-  auto state_row = [&](int seq) { return ((int64_t)seq * g.H + h) * PN + (int64_t)(p0 + pl) * g.N; };
+  // uniform part of a state offset, and the per-lane part (this lane's row and
+  // first column; recomputed at each use so that it is never held across the
+  // loops)
+  auto state_base = [&](int seq) { return ((int64_t)seq * g.H + h) * PN + (int64_t)p0 * g.N; };
+  auto lane_off = [&]() {
+    const int t = opaque_tid();
+    return (uint32_t)((((t / kWave) * 16 + t % 16) * g.N) + (t % kWave) / 16 * 4);
+  };
   auto slot = [&](int rr) { return ((int64_t)rr * a.U + u) * 64 * NMAX + pl * NMAX + q * 4; };
   auto load_h0 = [&](f32x4 (&v)[NT], int seq) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       v[nt] = zero4();
       if (a.h0 && p_ok && nt * 16 < g.N)
-        v[nt] = *reinterpret_cast<const f32x4*>(a.h0 + state_row(seq) + nt * 16 + q * 4);
+        v[nt] = *reinterpret_cast<const f32x4*>(at(a.h0 + state_base(seq), lane_off() + nt * 16));
     }
   };
 
-  const float Ah = a.A[h];
+  const float Ah2 = a.A[h] * 1.4426950408889634f;  // A_h in base-2 units
+  const float Dh = a.D ? a.D[h] : 0.0f;
   const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
   // registers a chunk's x, B and dt are loaded into before they go to LDS:
   // 16-byte row pieces, 8 (x) or NMAX / 8 (B) consecutive threads per row
   struct Stage {
     u32x4 x[FXV], b[BV];
-    float dt[2];
+    // raw bits of dt (bf16 zero-extended, or fp32), converted only where the
+    // cumsum uses them: converting at the load would make the wave wait for
+    // the load, and with it for every load issued before it
+    uint32_t dt[2];
   };
   u32x4 zr[FXV];
 
@@ -212,16 +225,27 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     uint32_t off[FXV];
     x_offsets(c, a.z.s1, off);
 #pragma unroll
-    for (int k = 0; k < FXV; ++k) zr[k] = *reinterpret_cast<const u32x4*>(base + off[k]);
+    for (int k = 0; k < FXV; ++k) zr[k] = *reinterpret_cast<const u32x4*>(at(base, off[k]));
   };
-  // ---- issue every global load of chunk c (x, B, dt into st; z when gating)
+  // ---- issue every global load of chunk c (dt, x, B into st; z when gating).
+  // dt goes first: its wait (for the cumsum) then covers no x or B load
   auto load_chunk = [&](Stage& st, const Chunk& c, bool with_z) {
+    {
+      // (every wave loads dt, though only wave 0 uses it: loads under a
+      // branch would leave the compiler's wait counts conservative)
+      const TDt* dbase = row_ptr<TDt>(a.dt, c.b, c.t0, h);
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const uint32_t off = (uint32_t)(min(2 * lane + e, c.len - 1) * a.dt.s1);
+        st.dt[e] = raw_bits(*at(dbase, off));
+      }
+    }
     const bf16* xbase = row_ptr<bf16>(a.x, c.b, c.t0, h) + p0;
     {
       uint32_t off[FXV];
       x_offsets(c, a.x.s1, off);
 #pragma unroll
-      for (int k = 0; k < FXV; ++k) st.x[k] = *reinterpret_cast<const u32x4*>(xbase + off[k]);
+      for (int k = 0; k < FXV; ++k) st.x[k] = *reinterpret_cast<const u32x4*>(at(xbase, off[k]));
     }
     const bf16* bbase = row_ptr<bf16>(a.B, c.b, c.t0, grp);
     {
@@ -238,16 +262,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
           off[k] = (uint32_t)(min(row0 + BROWS * k, c.len - 1) * a.B.s1 + min(col, g.N - 8));
       }
 #pragma unroll
-      for (int k = 0; k < BV; ++k) st.b[k] = *reinterpret_cast<const u32x4*>(bbase + off[k]);
-    }
-    if (wave == 0) {
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int t = c.t0 + min(2 * lane + e, c.len - 1);
-        // (a branch on the dt type here would make the compiler wait for every
-        // outstanding load right after it)
-        st.dt[e] = to_f32<TDt>(*row_ptr<TDt>(a.dt, c.b, t, h));
-      }
+      for (int k = 0; k < BV; ++k) st.b[k] = *reinterpret_cast<const u32x4*>(at(bbase, off[k]));
     }
     if (with_z && a.z.p) load_z(c);
   };
@@ -258,17 +273,19 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   // Within-chunk cumsum by wave 0, branch-free: lane l holds positions 2l and
   // 2l + 1.  fp32 with a DPP wave scan (the bf16 inputs of this path leave
   // ample room for fp32 rounding of cs; no LDS round trips).  softplus as
-  // max(u, 0) + log(1 + exp(-|u|)) with the hardware exp/log.
+  // max(u, 0) + log(1 + exp(-|u|)) with the hardware exp/log.  The cumsum is
+  // kept in base-2 units (cs * log2 e), so every decay factor below is one
+  // hardware 2^x of a difference.
   auto stage_cs = [&](const Stage& st, const Chunk& c) {
     if (wave == 0) {
       float av[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const float uu = st.dt[e] + bias;
+        const float uu = from_bits<TDt>(st.dt[e]) + bias;
         float d = uu;
         if (a.softplus) d = fmaxf(uu, 0.0f) + __logf(1.0f + __expf(-fabsf(uu)));
         if (a.clamp) d = fminf(fmaxf(d, a.dt_min), a.dt_max);
-        av[e] = 2 * lane + e < c.len ? d * Ah : 0.0f;
+        av[e] = 2 * lane + e < c.len ? d * Ah2 : 0.0f;
       }
       const float pair = av[0] + av[1];
       const float incl = wave_inclusive_sum_dpp(pair);
@@ -278,8 +295,8 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       const int ll = c.len - 1;
       const float lam = __int_as_float(
           __builtin_amdgcn_readlane(__float_as_int((ll & 1) ? c1 : c0), ll >> 1));
-      s_w[2 * lane] = 2 * lane < c.len ? fast_exp(lam - c0) : 0.0f;
-      s_w[2 * lane + 1] = 2 * lane + 1 < c.len ? fast_exp(lam - c1) : 0.0f;
+      s_w[2 * lane] = 2 * lane < c.len ? fast_exp2(lam - c0) : 0.0f;
+      s_w[2 * lane + 1] = 2 * lane + 1 < c.len ? fast_exp2(lam - c1) : 0.0f;
       if (lane == 0) s_misc[1] = __float_as_uint(lam);
     }
   };
@@ -361,22 +378,23 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     // is multiplied
     Stage sa, sb;
     Chunk ca, cb;
+    // Every prefetch below is unconditional: with loads under a branch the
+    // compiler can no longer count which loads a wait has to cover, and waits
+    // for all of them.  Past the range's end they re-read its last chunk,
+    // which is never used.
     get_chunk(g, js, ca);
     load_chunk(sa, ca, false);
-    if (js + 1 < j1) {
-      get_chunk(g, js + 1, cb);
-      load_chunk(sb, cb, false);
-    }
+    get_chunk(g, min(js + 1, j1 - 1), cb);
+    load_chunk(sb, cb, false);
     auto step = [&](Stage& st, Chunk& c, int j) {
       __syncthreads();  // the previous chunk's matrix phase is done with LDS
       stage_cs(st, c);
       stage_xb(st, c);
-      if (j + 2 < j1) {  // the registers are in LDS now: refill them
-        get_chunk(g, j + 2, c);
-        load_chunk(st, c, false);
-      }
+      // the registers are in LDS now: refill them with chunk j + 2
+      get_chunk(g, min(j + 2, j1 - 1), c);
+      load_chunk(st, c, false);
       __syncthreads();
-      const float e = fast_exp(__uint_as_float(s_misc[1]));
+      const float e = fast_exp2(__uint_as_float(s_misc[1]));
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) carry[nt] *= e;
       state_mma(carry);
@@ -493,14 +511,16 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   }
 
   // ---- pass 2: outputs, chunk by chunk.  Per chunk:
-  //   A  the carry-in H_j to LDS as bf16 hi + lo (the cumsum was staged at
-  //      the end of the previous chunk)
+  //   A  the carry-in H_j (the initial state at a sequence's first chunk,
+  //      loaded during the previous chunk) to LDS as bf16 hi + lo (the cumsum
+  //      was staged at the end of the previous chunk)
   //   B  Y_off = exp(cs_l) C_l . H_j
   //   C  x and B tiles to LDS; this chunk's z and the next chunk's x, B, dt
   //      loads go out
-  //   D  carry = exp(Lambda) carry + S_j (accumulated in place); per k-block,
-  //      C.B^T tiles -> M -> Y_diag; the next chunk's C fragments go out
-  //   E  y through LDS; D skip, gate, store; the next chunk's cumsum
+  //   D  carry = exp(Lambda) carry + S_j (accumulated in place); per s-tile
+  //      pair, C.B^T tiles -> M (+ D on the diagonal) -> Y_diag; the next
+  //      chunk's C fragments go out
+  //   E  y through LDS; gate, store; the next chunk's cumsum
   const int ltA = wave, ltB = 7 - wave;   // this wave's l-tiles
   const u32x4 zero = {0u, 0u, 0u, 0u};
   u32x4 cfr[2][NKB];
@@ -512,27 +532,24 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       const uint32_t roff = (uint32_t)(min(lrow, cc.len - 1) * a.C.s1);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
-        cfr[ui][kb] = *reinterpret_cast<const u32x4*>(cbase + roff + min(kb * 32 + q * 8, g.N - 8));
+        cfr[ui][kb] = *reinterpret_cast<const u32x4*>(
+            at(cbase, roff + (uint32_t)min(kb * 32 + q * 8, g.N - 8)));
     }
   };
-  load_cfr(c);
   int fj, lj;  // the current chunk's sequence: chunks [fj, lj)
   seq_chunks(g, c.seq, fj, lj);
+  if (fj == j0) load_h0(carry, c.seq);  // (before the C fragments, as below)
+  load_cfr(c);
   stage_cs(st, c);
   for (int j = j0; j < j1; ++j) {
     // ---- A
-    if (j == fj) load_h0(carry, c.seq);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      bf16x4 hi, lo;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bf16 hv = (bf16)carry[nt][i];
-        hi[i] = hv;
-        lo[i] = (bf16)(carry[nt][i] - (float)hv);
-      }
-      *reinterpret_cast<bf16x4*>(&s_hh[pl * HLD + nt * 16 + q * 4]) = hi;
-      *reinterpret_cast<bf16x4*>(&s_hl[pl * HLD + nt * 16 + q * 4]) = lo;
+      uint2 hi, lo;
+      split_pair(carry[nt][0], carry[nt][1], hi.x, lo.x);
+      split_pair(carry[nt][2], carry[nt][3], hi.y, lo.y);
+      *reinterpret_cast<uint2*>(&s_hh[pl * HLD + nt * 16 + q * 4]) = hi;
+      *reinterpret_cast<uint2*>(&s_hl[pl * HLD + nt * 16 + q * 4]) = lo;
     }
     // C rows past the chunk and columns past N contribute nothing
     if (!(dims_full && c.len == FC)) {
@@ -546,30 +563,35 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     }
     __syncthreads();
 
-    // ---- B
+    // ---- B  (each carry-in fragment is read from LDS once and serves both
+    // l-tiles)
     f32x4 acc[2][4];
+#pragma unroll
+    for (int ui = 0; ui < 2; ++ui)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) acc[ui][pt] = zero4();
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      FragBF cf0, cf1;
+      cf0.v = __builtin_bit_cast(bf16x8, cfr[0][kb]);
+      cf1.v = __builtin_bit_cast(bf16x8, cfr[1][kb]);
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        FragSplit hs;
+        hs.hi = *reinterpret_cast<const bf16x8*>(&s_hh[(pt * 16 + r16) * HLD + kb * 32 + q * 8]);
+        hs.lo = *reinterpret_cast<const bf16x8*>(&s_hl[(pt * 16 + r16) * HLD + kb * 32 + q * 8]);
+        mma(acc[0][pt], cf0, hs);
+        mma(acc[1][pt], cf1, hs);
+      }
+      // keep the scheduler from hoisting every k-block's reads at once
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int ui = 0; ui < 2; ++ui) {
       const int lt = ui ? ltB : ltA;
 #pragma unroll
-      for (int pt = 0; pt < 4; ++pt) acc[ui][pt] = zero4();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        FragBF cf;
-        cf.v = __builtin_bit_cast(bf16x8, cfr[ui][kb]);
-#pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          FragSplit hs;
-          hs.hi = *reinterpret_cast<const bf16x8*>(&s_hh[(pt * 16 + r16) * HLD + kb * 32 + q * 8]);
-          hs.lo = *reinterpret_cast<const bf16x8*>(&s_hl[(pt * 16 + r16) * HLD + kb * 32 + q * 8]);
-          mma(acc[ui][pt], cf, hs);
-        }
-        // keep the scheduler from hoisting every k-block's reads at once
-        __builtin_amdgcn_sched_barrier(0);
-      }
-#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float ex = fast_exp(s_cs[lt * 16 + q * 4 + i]);
+        const float ex = fast_exp2(s_cs[lt * 16 + q * 4 + i]);
 #pragma unroll
         for (int pt = 0; pt < 4; ++pt) acc[ui][pt][i] *= ex;
       }
@@ -588,13 +610,13 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     const bool more = j + 1 < j1;
     if (more) {
       get_chunk(g, j + 1, cn);
-      load_chunk(st, cn, false);
       if (cn.seq != c.seq) seq_chunks(g, cn.seq, fn, ln);
     }
+    load_chunk(st, cn, false);  // unconditional, as in pass 1
     __syncthreads();
 
     // ---- D
-    const float e = fast_exp(__uint_as_float(s_misc[1]));
+    const float e = fast_exp2(__uint_as_float(s_misc[1]));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) carry[nt] *= e;
     state_mma(carry);
@@ -602,15 +624,21 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
         if (nt * 16 < g.N)
-          *reinterpret_cast<f32x4*>(a.hfinal + state_row(c.seq) + nt * 16 + q * 4) = carry[nt];
+          *reinterpret_cast<f32x4*>(at(a.hfinal + state_base(c.seq), lane_off() + nt * 16)) = carry[nt];
     }
+    // Y_diag = (L o C.B^T + D I) x, one s-tile pair (kp) at a time; the
+    // diagonal pair (the last) masks s > l and adds the skip D on s == l.
+    // Rows past the chunk compute finite or discarded values: the epilogue
+    // never stores them.  (A separate unmasked loop for the pairs below the
+    // diagonal measured slower: its extra code costs more registers than the
+    // selects it saves.)
 #pragma unroll
     for (int ui = 0; ui < 2; ++ui) {
       const int lt = ui ? ltB : ltA;
       const int lrow = lt * 16 + r16;
-      const bool lok = lrow < c.len;
       const float csl = s_cs[lrow];
       for (int kp = 0; kp <= lt / 2; ++kp) {
+        const bool diag = kp == lt / 2;
         // C.B^T tiles (s-tile sa / sb, l-tile lt): B rows (n contiguous) from
         // the B tile as the A operand, the C fragments as the B operand
         const int sa = 2 * kp, sb = 2 * kp + 1;
@@ -624,20 +652,24 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
           mma(va, ba, cf);
           mma(vb, bb, cf);
         }
-        // M = L o C.B^T in the accumulator layout (lane: one l, tokens 4 q +
-        // 0..3 of each s-tile), used as the A operand with the tokens in that
-        // order; x is read from the x tile in the same order
+        // M in the accumulator layout (lane: one l, tokens 4 q + 0..3 of each
+        // s-tile), used as the A operand with the tokens in that order; x is
+        // read from the x tile in the same order
         const f32x4 csa = *reinterpret_cast<const f32x4*>(&s_cs[sa * 16 + q * 4]);
         const f32x4 csb = *reinterpret_cast<const f32x4*>(&s_cs[sb * 16 + q * 4]);
         f32x8 m;
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
-          const bool ka = lok && sa * 16 + q * 4 + e4 <= lrow;
-          const bool kb2 = lok && sb * 16 + q * 4 + e4 <= lrow;
-          const float xa = fast_exp(ka ? csl - csa[e4] : 0.0f);
-          const float xb = fast_exp(kb2 ? csl - csb[e4] : 0.0f);
-          m[e4] = ka ? xa * va[e4] : 0.0f;
-          m[4 + e4] = kb2 ? xb * vb[e4] : 0.0f;
+          const float ma = fast_exp2(csl - csa[e4]) * va[e4];
+          const float mb = fast_exp2(csl - csb[e4]) * vb[e4];
+          if (diag) {
+            const int s_a = sa * 16 + q * 4 + e4, s_b2 = sb * 16 + q * 4 + e4;
+            m[e4] = s_a < lrow ? ma : (s_a == lrow ? ma + Dh : 0.0f);
+            m[4 + e4] = s_b2 < lrow ? mb : (s_b2 == lrow ? mb + Dh : 0.0f);
+          } else {
+            m[e4] = ma;
+            m[4 + e4] = mb;
+          }
         }
         const FragSplit mf = split_f32x8(m);
 #pragma unroll
@@ -648,7 +680,11 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
         }
       }
     }
-    if (more) load_cfr(cn);
+    // A sequence that starts at the next chunk starts from its initial
+    // state (carry is dead here: its final state was stored above).  Issued
+    // before the C fragments, so that waiting for it does not wait for them.
+    if (more && fn == j + 1) load_h0(carry, cn.seq);
+    load_cfr(cn);  // unconditional, as in pass 1
     __syncthreads();  // the B tile is dead: its space takes y
 
     // ---- E
@@ -662,7 +698,11 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
           s_y[(lt * 16 + q * 4 + i) * FYLD + pt * 16 + r16] = acc[ui][pt][i];
     }
     __syncthreads();
-    const float Dh = a.D ? a.D[h] : 0.0f;
+    // The next chunk's cumsum (cs is free: nothing reads it after the matrix
+    // phase) goes before the stores below, whose completion a later wait for
+    // its dt would also wait for.  Past the range's end it stages this chunk
+    // again, unused.
+    stage_cs(st, cn);
     TO* obase = row_ptr_mut<TO>(a.out, c.b, c.t0, h) + p0;
     const int etid = opaque_tid();
     const int erow = etid / 8, ecol = (etid % 8) * 8;
@@ -674,12 +714,6 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       // the store is conditional: straight-line code keeps the waits precise
       const int l = erow + 32 * k, pp = ecol;
       f32x8 y = Vec8<float>::load(s_y + l * FYLD + pp);
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(&s_x[l * FXLD + pp]);
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        y[2 * d] = fmaf(Dh, bf16_lo_f32(xv[d]), y[2 * d]);
-        y[2 * d + 1] = fmaf(Dh, bf16_hi_f32(xv[d]), y[2 * d + 1]);
-      }
       if (a.z.p) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
@@ -687,14 +721,11 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
           y[2 * d + 1] *= silu(bf16_hi_f32(zr[k][d]));
         }
       }
-      if (efull || (l < c.len && pp < pw)) Vec8<TO>::store(obase + eoff + k * estep, y);
+      if (efull || (l < c.len && pp < pw)) Vec8<TO>::store(at(obase, eoff + k * estep), y);
     }
-    if (more) {
-      c = cn;
-      fj = fn;
-      lj = ln;
-      stage_cs(st, c);  // cs is free: nothing reads it after the matrix phase
-    }
+    c = cn;
+    fj = fn;
+    lj = ln;
     __syncthreads();  // y and x are dead before the next chunk's staging
   }
 }
