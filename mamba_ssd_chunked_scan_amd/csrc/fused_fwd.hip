@@ -73,6 +73,12 @@ namespace ssd {
 namespace {
 
 constexpr int FC = 128;                 // internal chunk length
+constexpr int kLookback = 3;            // aggregates loaded per look-back round trip
+// buffer resource word 3 for raw (untyped, 32-bit format) buffer access
+constexpr int kBufWord3 = 0x00020000;
+// cache-policy operand of the buffer builtins: sc1, the policy of an
+// agent-scope atomic store
+constexpr int kCachePolicySc1 = 16;
 #ifndef SSD_FUSED_XPAD
 #define SSD_FUSED_XPAD 8
 #endif
@@ -172,7 +178,12 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     const int t = opaque_tid();
     return (uint32_t)((((t / kWave) * 16 + t % 16) * g.N) + (t % kWave) / 16 * 4);
   };
-  auto slot = [&](int rr) { return ((int64_t)rr * a.U + u) * 64 * NMAX + pl * NMAX + q * 4; };
+  // aggregate of range rr: uniform base, and this lane's offset in it
+  auto slot_base = [&](int rr) { return a.agg + ((int64_t)rr * a.U + u) * 64 * NMAX; };
+  auto slot_lane = [&]() {
+    const int t = opaque_tid();
+    return (uint32_t)(((t / kWave) * 16 + t % 16) * NMAX + (t % kWave) / 16 * 4);
+  };
   auto load_h0 = [&](f32x4 (&v)[NT], int seq) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -407,13 +418,17 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     // Publish: agent-coherent stores, wait until every one has completed, then
     // raise the flag.  The aggregate never sits in a non-coherent cache, so no
     // cache-wide write-back is needed (see "Hand-off" above).
-    float* dst = a.agg + slot(r);
+    // 16-byte stores with the cache policy of an agent-scope atomic store
+    // (sc1: written through to the level all XCDs share).
+    {
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(slot_base(r), 0, 64 * NMAX * 4, kBufWord3);
+      const uint32_t lo = slot_lane();
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        __hip_atomic_store(dst + nt * 16 + i, carry[nt][i], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+      for (int nt = 0; nt < NT; ++nt)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, carry[nt]), rs,
+                                               (lo + nt * 16) * 4, 0, kCachePolicySc1);
+    }
     if (tid == 0)
       __hip_atomic_store(a.edec + r * a.U + u, E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
@@ -429,84 +444,67 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   Stage st;
   load_chunk(st, c, false);
 
-  // ---- carry-in: the decayed sum of the preceding ranges' aggregates, back
-  // to the range where the sequence starts
+  // ---- carry-in: the aggregates of the preceding ranges back to the one
+  // where the sequence starts (rstop, whose aggregate starts from the
+  // initial state), folded oldest first: carry = E_rr carry + agg_rr.  Each
+  // wave polls the flags itself (one lane per range) and folds every
+  // aggregate as soon as it and all older ones are published, kLookback per
+  // round trip to memory.  The folds happen in the same order whatever the
+  // timing, so results are bit-identical run to run.  Aggregate data is read
+  // with ordinary (cacheable) loads, issued only after this wave has seen the
+  // flag: no cache can hold an older copy from this launch, launch boundaries
+  // leave no stale lines behind, and each aggregate occupies whole cache
+  // lines.  The decays share cache lines across ranges and the flags change
+  // during the launch, so both are read coherently.
   if (need_lb) {
-    if (wave == 0) {
-      // Lane k watches range r - 1 - base - k.  The ranges to sum are r - 1
-      // down to the nearest one flagged "reset"; every one of them must have
-      // published.  Flags are read once per round by all lanes together.
-      int base = 0, spins = 0, rstop = 0;
-      while (true) {
-        const int rr = r - 1 - base - lane;
-        const uint32_t f = rr >= 0 ? __hip_atomic_load(a.sync + 2 + rr * a.U + u, __ATOMIC_RELAXED,
-                                                       __HIP_MEMORY_SCOPE_AGENT)
-                                   : kFlagReset;
-        const uint64_t resets = __ballot(f == kFlagReset);
-        const uint64_t missing = __ballot(f == 0);
-        const int kr = resets ? __builtin_ctzll(resets) : 64;
-        const uint64_t needed = kr >= 63 ? ~0ull : ((1ull << (kr + 1)) - 1);
-        if ((missing & needed) == 0) {
-          if (kr < 64) {
-            rstop = max(r - 1 - base - kr, 0);
-            break;
-          }
-          base += 64;  // a full window of continuing ranges: look further back
-          continue;
-        }
-        if (++spins > kSpinLimit) {
-          if (lane == 0)
-            __hip_atomic_fetch_or(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          rstop = max(r - 1 - base - (kr < 64 ? kr : 63), 0);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-      }
-      if (lane == 0) s_misc[2] = (uint32_t)rstop;
-    }
-    __syncthreads();
-    const int rstop = (int)s_misc[2];
-    // carry = sum over rr = r-1 .. rstop of (prod of E over r-1 .. rr+1) agg_rr,
-    // accumulated newest first (a fixed order).  Two aggregates are loaded per
-    // round trip.  The aggregate data is read with ordinary (cacheable)
-    // loads: its lines are read only after their flag was seen, so no cache
-    // can hold an older copy from this launch, and launch boundaries leave no
-    // stale lines behind; each aggregate occupies whole cache lines.  The
-    // decays share cache lines across ranges, so they are read coherently.
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) carry[nt] = zero4();
-    float dec = 1.0f;
     auto ld = [&](const float* p) {
       return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     };
-    int rr = r - 1;
-    for (; rr - 1 >= rstop; rr -= 2) {
-      float v[2][NT][4], e[2];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const float* src = a.agg + slot(rr - m);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[m][nt][i] = src[nt * 16 + i];
-        e[m] = ld(a.edec + (rr - m) * a.U + u);
+    for (int nt = 0; nt < NT; ++nt) carry[nt] = zero4();
+    int next = f0 / a.R, spins = 0;
+    while (next < r) {
+      const int rr = next + lane;
+      const uint32_t f = rr < r ? __hip_atomic_load(a.sync + 2 + rr * a.U + u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT)
+                                : 1u;
+      const uint64_t waiting = ~__ballot(f != 0u);
+      const int n = min(waiting ? (int)__builtin_ctzll(waiting) : 64, r - next);
+      if (n == 0) {
+        if (++spins > kSpinLimit) {
+          if (lane == 0)
+            __hip_atomic_fetch_or(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+        continue;
       }
+      for (int b = 0; b < n; b += kLookback) {
+        // (loads past the n available repeat the last one, unused: loads
+        // under a branch would leave the compiler's wait counts conservative)
+        f32x4 v[kLookback][NT];
+        float e[kLookback];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+        for (int m = 0; m < kLookback; ++m) {
+          const int rm = next + min(b + m, n - 1);
+          const float* src = slot_base(rm);
+          const uint32_t lo = slot_lane();
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
+          for (int nt = 0; nt < NT; ++nt) v[m][nt] = *reinterpret_cast<const f32x4*>(at(src, lo + nt * 16));
+          e[m] = ld(a.edec + rm * a.U + u);
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(dec, v[m][nt][i], carry[nt][i]);
-        dec *= e[m];
+        for (int m = 0; m < kLookback; ++m) {
+          // an unused term folds as carry * 1 + 0, which leaves carry as it is
+          const bool ok = b + m < n;
+          const float em = ok ? e[m] : 1.0f, wm = ok ? 1.0f : 0.0f;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(em, carry[nt][i], wm * v[m][nt][i]);
+        }
       }
-    }
-    for (; rr >= rstop; --rr) {
-      const float* src = a.agg + slot(rr);
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(dec, src[nt * 16 + i], carry[nt][i]);
-      dec *= ld(a.edec + rr * a.U + u);
+      next += n;
     }
   }
 
