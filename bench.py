@@ -83,7 +83,11 @@ def stage_bytes(w, K, state_bytes, out_bytes, in_bytes=2):
     fin = 4 * (w.nseq or w.batch) * H * P * N
     z = x if w.has_z else 0
     out = T * H * P * out_bytes
+    nseq = w.nseq or w.batch
     return {
+        # cu_seqlens in; the chunk table (4-word header, 3 words per chunk,
+        # first chunk per sequence) out
+        "varlen_meta": 4 * (nseq + 1) + 4 * (4 + 3 * K + nseq + 1),
         "chunk_cumsum": dt + cs,
         "bmm_chunk": 2 * bc + cb,
         "chunk_state": x + bc + cs + st,
@@ -97,6 +101,7 @@ def stage_flops(w, K):
     """Useful matrix flops per launch (causal half only, no hi/lo second pass)."""
     H, P, G, N, C = w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk_size
     f = {
+        "varlen_meta": 0,
         "chunk_cumsum": 0,
         "bmm_chunk": K * G * C * (C + 1) * N,
         "chunk_state": 2 * K * H * C * P * N,
