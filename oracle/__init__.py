@@ -27,6 +27,12 @@ Contents
                             recurrence's state at the chunk boundary).
 * ``state_passing``      -- the chunk-level recurrence applied to given chunk
                             states, SSD Reference "Inter-chunk propagation".
+* ``ssd_bwd``            -- the reverse-mode gradient of ``ssd_fwd`` (every input,
+                            the initial state included), the adjoint recurrence
+                            taken token by token in reverse (``ssd_ref.c``,
+                            ``ssd_ref_bwd``); the backward stages of mamba PR 1012
+                            "Measurements", SSD Reference section 6 "The autograd
+                            backward contract".
 
 All floating-point work is fp64.  Every function here is pinned by the
 ``-m "not gpu"`` tests against closed forms, special cases and brute force.
@@ -81,6 +87,19 @@ def _load():
             ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int,
+        ]
+        lib.ssd_ref_bwd.restype = ctypes.c_int
+        lib.ssd_ref_bwd.argtypes = [
+            ctypes.c_int64, ctypes.c_int, P(ctypes.c_int64),
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p,
+            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+            ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_void_p, ctypes.c_int,
         ]
         lib.ssd_ref_num_chunks.restype = ctypes.c_int64
         lib.ssd_ref_num_chunks.argtypes = [ctypes.c_int, P(ctypes.c_int64), ctypes.c_int]
@@ -165,6 +184,74 @@ def ssd_fwd(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=None,
     if rc != 0:
         raise ValueError(f"ssd_ref_fwd failed with code {rc}")
     return FwdResult(y.reshape(x.shape), hfin, hch)
+
+
+@dataclass
+class BwdResult:
+    dx: np.ndarray                # like x
+    dB: np.ndarray                # like B (summed over the heads of each group)
+    dC: np.ndarray                # like C (summed over the heads of each group)
+    ddt: np.ndarray               # like dt: gradient w.r.t. the raw dt
+    dA: np.ndarray                # (H,)
+    ddt_bias: np.ndarray          # (H,)
+    dD: np.ndarray | None         # (H,), None without D
+    dz: np.ndarray | None         # like z, None without z
+    dinitial_states: np.ndarray   # (nseq or b, H, P, N)
+
+
+def ssd_bwd(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_states=None,
+            dfinal_states=None, cu_seqlens=None, dt_softplus=True, dt_limit=None,
+            threads=None) -> BwdResult:
+    """Gradient of L = sum(dout * y) + sum(dfinal_states * final_states).
+
+    Arguments as ``ssd_fwd``; ``dout`` is shaped like x and ``dfinal_states``
+    like the final states (None = zero).  ``ddt`` is the gradient with respect
+    to the raw dt (before bias and softplus); where the clamp of ``dt_limit``
+    is active it is zero.  A missing initial state is a zero one, and its
+    gradient is still returned.
+    """
+    x = _f64(x)
+    if cu_seqlens is None:
+        b, T = x.shape[0], x.shape[1]
+        cu = np.arange(b + 1, dtype=np.int64) * T
+        lead = 2
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        lead = 1
+    H, P = x.shape[lead], x.shape[lead + 1]
+    Bf, Cf = _f64(B), _f64(C)
+    G, N = Bf.shape[lead], Bf.shape[lead + 1]
+    xs, Bs, Cs = _packed(x, lead), _packed(Bf, lead), _packed(Cf, lead)
+    dts = _packed(_f64(dt), lead)
+    zs = _packed(_f64(z), lead) if z is not None else None
+    dos = _packed(_f64(dout), lead)
+    ntok = xs.shape[0]
+    nseq = len(cu) - 1
+    A_ = _f64(np.broadcast_to(np.asarray(A, dtype=np.float64), (H,)))
+    bias, D_, h0, dfin = _f64(dt_bias), _f64(D), _f64(initial_states), _f64(dfinal_states)
+    dx = np.empty((ntok, H, P))
+    dB = np.empty((ntok, G, N))
+    dC = np.empty((ntok, G, N))
+    ddt = np.empty((ntok, H))
+    dA = np.empty(H)
+    dbias = np.empty(H)
+    dD = np.empty(H) if D is not None else None
+    dz = np.empty((ntok, H, P)) if z is not None else None
+    dh0 = np.empty((nseq, H, P, N))
+    clamp = 0 if dt_limit is None else 1
+    lo, hi = (0.0, math.inf) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
+    lib = _load()
+    cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+    rc = lib.ssd_ref_bwd(ntok, nseq, cu_p, H, P, N, G, _ptr(xs), _ptr(Bs), _ptr(Cs),
+                         _ptr(dts), _ptr(A_), _ptr(bias), _ptr(D_), _ptr(zs), _ptr(h0),
+                         1 if dt_softplus else 0, clamp, lo, hi, _ptr(dos), _ptr(dfin),
+                         _ptr(dx), _ptr(dB), _ptr(dC), _ptr(ddt), _ptr(dA), _ptr(dbias),
+                         _ptr(dD), _ptr(dz), _ptr(dh0), int(threads or 0))
+    if rc != 0:
+        raise ValueError(f"ssd_ref_bwd failed with code {rc}")
+    shp = lambda a, like: a.reshape(np.shape(like))
+    return BwdResult(shp(dx, x), shp(dB, Bf), shp(dC, Cf), shp(ddt, dt), dA, dbias, dD,
+                     None if dz is None else shp(dz, z), dh0)
 
 
 # --------------------------------------------------------------------------

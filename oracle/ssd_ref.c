@@ -1,5 +1,6 @@
 /*
- * ssd_ref.c -- the fp64 sequential oracle for the Mamba-2 SSD forward pass.
+ * ssd_ref.c -- the fp64 sequential oracle for the Mamba-2 SSD forward pass and
+ * its reverse-mode gradient (ssd_ref_bwd, at the end of the file).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing in the product library links, includes
  * or calls this file; only the tests, the package's smoke check and the CPU
@@ -184,4 +185,224 @@ int64_t ssd_ref_num_chunks(int nseq, const int64_t* cu, int chunk) {
   int64_t k = 0;
   for (int i = 0; i < nseq; ++i) k += (cu[i + 1] - cu[i] + chunk - 1) / chunk;
   return k;
+}
+
+/*
+ * ssd_ref_bwd -- reverse-mode gradient of ssd_ref_fwd, in fp64.
+ *
+ * The backward pass the pages describe (mamba PR 1012, "Measurements": the
+ * dx/ddt, dB, dC, dA-cumsum, state-passing and dstates backward stages;
+ * cudnn-frontend PR 1133: first-order backward checked against fp64 gradients;
+ * SSD Reference, section 6 "The autograd backward contract": exact gradients
+ * of every input) is here the adjoint of the recurrence above, taken one
+ * token at a time in reverse:
+ *
+ *   G      := dL/dS_t, starting from dL/dS_final (dfinal, or zero)
+ *   per token t, newest first, with S_t and S_{t-1} recomputed:
+ *     y_t    = S_t . C_t + D x_t              (before the gate)
+ *     dy_t   = dout_t * silu(z_t)             (dout_t without a gate)
+ *     dz_t   = dout_t * y_t * silu'(z_t),     silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
+ *     G     += dy_t (outer) C_t               (now dL/dS_t, all paths)
+ *     dC_t  += S_t^T dy_t                     (summed over the heads of the group)
+ *     dx_t   = G B_t + D dy_t
+ *     dB_t  += G^T x_t                        (summed over the heads of the group)
+ *     dD    += dy_t . x_t
+ *     da_t   = exp(a_t) <G, S_{t-1}>          (a_t = delta_t A)
+ *     G      = exp(a_t) G                     (dL/dS_{t-1})
+ *     dA    += da_t delta_t;  ddelta = da_t A
+ *     ddt_t  = ddelta * sigmoid(u_t)          (softplus' = sigmoid; ddelta itself
+ *                                              without softplus; 0 where the
+ *                                              clamp is active)
+ *     ddt_bias += ddt_t
+ *   dh0 = G after the sequence's first token.
+ *
+ * The loss this differentiates is L = sum(dout * y) + sum(dfinal * S_final).
+ * States are recomputed from checkpoints taken every kCheck tokens, so memory
+ * stays O(kCheck P N) per (sequence, head).  Work is split by group: one
+ * thread owns every head of a group (all sequences), so the group-summed dB
+ * and dC and the per-head dA, ddt_bias, dD need no atomics, and the order of
+ * every sum is fixed.
+ *
+ *   dout   (ntok, H, P)      gradient of y (after the gate)
+ *   dfinal (nseq, H, P, N) or NULL
+ *   dx (ntok,H,P), dB and dC (ntok,G,N), ddt (ntok,H), dA (H), ddt_bias (H),
+ *   dD (H) (may be NULL when D is NULL), dz (ntok,H,P) (NULL when z is NULL),
+ *   dh0 (nseq,H,P,N) or NULL -- all written (not accumulated into).
+ *
+ * Returns 0 on success, -1 on an inconsistent argument, -2 when out of memory.
+ */
+enum { kCheck = 64 };
+
+static void ref_step_size(double u, int dt_softplus, int clamp, double dt_min,
+                          double dt_max, double* delta, double* ddelta_du) {
+  double d = dt_softplus ? ref_softplus(u) : u;
+  double g = dt_softplus ? 1.0 / (1.0 + exp(-u)) : 1.0;
+  if (clamp) {
+    if (d < dt_min) { d = dt_min; g = 0.0; }
+    if (d > dt_max) { d = dt_max; g = 0.0; }
+  }
+  *delta = d;
+  *ddelta_du = g;
+}
+
+int ssd_ref_bwd(int64_t ntok, int nseq, const int64_t* cu, int H, int P, int N,
+                int G, const double* x, const double* Bm, const double* Cm,
+                const double* dt, const double* A, const double* dt_bias,
+                const double* D, const double* z, const double* h0,
+                int dt_softplus, int clamp, double dt_min, double dt_max,
+                const double* dout, const double* dfinal,
+                double* dx, double* dB, double* dC, double* ddt, double* dA,
+                double* ddt_bias, double* dD, double* dz, double* dh0,
+                int nthreads) {
+  if (ntok < 0 || nseq < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return -1;
+  if (H % G != 0) return -1;
+  if (nseq > 0 && (cu == NULL || cu[0] != 0 || cu[nseq] != ntok)) return -1;
+  for (int i = 0; i < nseq; ++i)
+    if (cu[i + 1] < cu[i]) return -1;
+  if (!dout || !dx || !dB || !dC || !ddt || !dA || !ddt_bias) return -1;
+  if (z && !dz) return -1;
+
+  const int hpg = H / G;
+  const size_t PN = (size_t)P * N;
+  memset(dB, 0, sizeof(double) * (size_t)ntok * G * N);
+  memset(dC, 0, sizeof(double) * (size_t)ntok * G * N);
+  int err = 0;
+
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+  for (int g = 0; g < G; ++g) {
+    /* states of one checkpoint block (kCheck + 1 of them: the one entering
+     * the block first), the running adjoint, and the block's checkpoints */
+    double* blk = (double*)malloc(sizeof(double) * (size_t)(kCheck + 1) * PN);
+    double* Gs = (double*)malloc(sizeof(double) * PN);
+    double* ck = NULL;
+    int64_t ck_cap = 0;
+    if (!blk || !Gs) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+      err = -2;
+      free(blk); free(Gs);
+      continue;
+    }
+    for (int hh = 0; hh < hpg; ++hh) {
+      const int h = g * hpg + hh;
+      double sA = 0.0, sBias = 0.0, sD = 0.0;
+      for (int i = 0; i < nseq && !err; ++i) {
+        const int64_t t0 = cu[i], t1 = cu[i + 1], L = t1 - t0;
+        const int64_t nblk = (L + kCheck - 1) / kCheck;
+        if (nblk > ck_cap) {
+          free(ck);
+          ck = (double*)malloc(sizeof(double) * (size_t)nblk * PN);
+          ck_cap = ck ? nblk : 0;
+          if (!ck) {
+#ifdef _OPENMP
+#pragma omp atomic write
+#endif
+            err = -2;
+            break;
+          }
+        }
+        /* forward sweep: the state entering every block */
+        double* S = blk;
+        if (h0)
+          memcpy(S, h0 + ((size_t)i * H + h) * PN, sizeof(double) * PN);
+        else
+          memset(S, 0, sizeof(double) * PN);
+        for (int64_t t = t0; t < t1; ++t) {
+          if ((t - t0) % kCheck == 0)
+            memcpy(ck + (size_t)((t - t0) / kCheck) * PN, S, sizeof(double) * PN);
+          double delta, gd;
+          ref_step_size(dt[t * H + h] + (dt_bias ? dt_bias[h] : 0.0), dt_softplus, clamp,
+                        dt_min, dt_max, &delta, &gd);
+          const double decay = exp(delta * A[h]);
+          const double* xt = x + ((size_t)t * H + h) * P;
+          const double* bt = Bm + ((size_t)t * G + g) * N;
+          for (int p = 0; p < P; ++p)
+            for (int n = 0; n < N; ++n)
+              S[(size_t)p * N + n] = decay * S[(size_t)p * N + n] + xt[p] * bt[n];
+        }
+        /* reverse sweep */
+        if (dfinal)
+          memcpy(Gs, dfinal + ((size_t)i * H + h) * PN, sizeof(double) * PN);
+        else
+          memset(Gs, 0, sizeof(double) * PN);
+        for (int64_t b = nblk - 1; b >= 0; --b) {
+          const int64_t ta = t0 + b * kCheck;
+          const int64_t tb = ta + kCheck < t1 ? ta + kCheck : t1;
+          /* blk[k] = state before token ta + k, blk[k + 1] = after it */
+          memcpy(blk, ck + (size_t)b * PN, sizeof(double) * PN);
+          for (int64_t t = ta; t < tb; ++t) {
+            double delta, gd;
+            ref_step_size(dt[t * H + h] + (dt_bias ? dt_bias[h] : 0.0), dt_softplus, clamp,
+                          dt_min, dt_max, &delta, &gd);
+            const double decay = exp(delta * A[h]);
+            const double* xt = x + ((size_t)t * H + h) * P;
+            const double* bt = Bm + ((size_t)t * G + g) * N;
+            const double* Sp = blk + (size_t)(t - ta) * PN;
+            double* Sn = blk + (size_t)(t - ta + 1) * PN;
+            for (int p = 0; p < P; ++p)
+              for (int n = 0; n < N; ++n)
+                Sn[(size_t)p * N + n] = decay * Sp[(size_t)p * N + n] + xt[p] * bt[n];
+          }
+          for (int64_t t = tb - 1; t >= ta; --t) {
+            const double u = dt[t * H + h] + (dt_bias ? dt_bias[h] : 0.0);
+            double delta, gd;
+            ref_step_size(u, dt_softplus, clamp, dt_min, dt_max, &delta, &gd);
+            const double decay = exp(delta * A[h]);
+            const double* xt = x + ((size_t)t * H + h) * P;
+            const double* bt = Bm + ((size_t)t * G + g) * N;
+            const double* ct = Cm + ((size_t)t * G + g) * N;
+            const double* dot = dout + ((size_t)t * H + h) * P;
+            const double* St = blk + (size_t)(t - ta + 1) * PN;
+            const double* Sp = blk + (size_t)(t - ta) * PN;
+            double* dxt = dx + ((size_t)t * H + h) * P;
+            double* dbt = dB + ((size_t)t * G + g) * N;
+            double* dct = dC + ((size_t)t * G + g) * N;
+            double da = 0.0;
+            for (int p = 0; p < P; ++p) {
+              const double* srow = St + (size_t)p * N;
+              double* grow = Gs + (size_t)p * N;
+              double dy = dot[p];
+              if (z) {
+                double y = 0.0;
+                for (int n = 0; n < N; ++n) y += srow[n] * ct[n];
+                y += D ? D[h] * xt[p] : 0.0;
+                const double zz = z[((size_t)t * H + h) * P + p];
+                const double sg = 1.0 / (1.0 + exp(-zz));
+                dz[((size_t)t * H + h) * P + p] = dy * y * (sg * (1.0 + zz * (1.0 - sg)));
+                dy = dy * zz * sg;
+              }
+              sD += dy * xt[p];
+              double acc = 0.0;
+              for (int n = 0; n < N; ++n) {
+                dct[n] += srow[n] * dy;
+                grow[n] += dy * ct[n];
+                acc += grow[n] * bt[n];
+                dbt[n] += grow[n] * xt[p];
+                da += grow[n] * Sp[(size_t)p * N + n];
+              }
+              dxt[p] = acc + (D ? D[h] * dy : 0.0);
+            }
+            da *= decay;
+            for (size_t q = 0; q < PN; ++q) Gs[q] *= decay;
+            sA += da * delta;
+            const double du = da * A[h] * gd;
+            ddt[t * H + h] = du;
+            sBias += du;
+          }
+        }
+        if (dh0) memcpy(dh0 + ((size_t)i * H + h) * PN, Gs, sizeof(double) * PN);
+      }
+      dA[h] = sA;
+      ddt_bias[h] = sBias;
+      if (dD) dD[h] = sD;
+    }
+    free(ck);
+    free(blk);
+    free(Gs);
+  }
+  return err;
 }

@@ -37,12 +37,35 @@ MUTANTS = {
     "chunk_end_off_by_one": ("(t - t0) % chunk == chunk - 1", "(t - t0) % chunk == 0"),
 }
 
+# slips in the backward (ssd_ref_bwd), caught by tests/test_oracle_bwd_pins.py
+BWD_MUTANTS = {
+    "bwd_dx_without_skip": ("dxt[p] = acc + (D ? D[h] * dy : 0.0);", "dxt[p] = acc;"),
+    "bwd_silu_derivative_sign": ("(sg * (1.0 + zz * (1.0 - sg)))", "(sg * (1.0 - zz * (1.0 - sg)))"),
+    "bwd_dB_before_adjoint_update": (
+        "grow[n] += dy * ct[n];\n                acc += grow[n] * bt[n];\n                dbt[n] += grow[n] * xt[p];",
+        "dbt[n] += grow[n] * xt[p];\n                grow[n] += dy * ct[n];\n                acc += grow[n] * bt[n];"),
+    "bwd_dC_from_previous_state": ("dct[n] += srow[n] * dy;", "dct[n] += Sp[(size_t)p * N + n] * dy;"),
+    "bwd_da_from_current_state": ("da += grow[n] * Sp[(size_t)p * N + n];", "da += grow[n] * srow[n];"),
+    "bwd_da_not_decayed": ("da *= decay;", ""),
+    "bwd_adjoint_not_decayed": ("for (size_t q = 0; q < PN; ++q) Gs[q] *= decay;", ""),
+    "bwd_softplus_derivative": ("double g = dt_softplus ? 1.0 / (1.0 + exp(-u)) : 1.0;",
+                                "double g = dt_softplus ? 1.0 / (1.0 + exp(u)) : 1.0;"),
+    "bwd_clamp_passes_gradient": ("if (d < dt_min) { d = dt_min; g = 0.0; }", "if (d < dt_min) { d = dt_min; }"),
+    "bwd_dA_times_A": ("sA += da * delta;", "sA += da * A[h];"),
+    "bwd_bias_not_summed": ("sBias += du;", "sBias = du;"),
+    "bwd_gate_uses_y_after_gate": ("dy = dy * zz * sg;", "dy = dy * zz;"),
+}
+
+
+CASES = [(n, MUTANTS[n], "tests/test_oracle_pins.py") for n in sorted(MUTANTS)] + \
+        [(n, BWD_MUTANTS[n], "tests/test_oracle_bwd_pins.py") for n in sorted(BWD_MUTANTS)]
+
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_reject_mutant(name, tmp_path):
+@pytest.mark.parametrize("name,mutation,pins", CASES, ids=[c[0] for c in CASES])
+def test_pins_reject_mutant(name, mutation, pins, tmp_path):
     src = open(os.path.join(ROOT, "oracle", "ssd_ref.c")).read()
-    before, after = MUTANTS[name]
+    before, after = mutation
     assert before in src, f"mutation site for {name} no longer in the oracle"
     work = tmp_path / "tree"
     shutil.copytree(os.path.join(ROOT, "oracle"), work / "oracle",
@@ -54,7 +77,7 @@ def test_pins_reject_mutant(name, tmp_path):
                     "-std=c99", str(work / "oracle" / "ssd_ref.c"), "-o",
                     str(work / "oracle" / "libssd_ref.so"), "-lm"], check=True)
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "tests/test_oracle_pins.py"], cwd=work, capture_output=True, text=True,
+                        pins], cwd=work, capture_output=True, text=True,
                        timeout=300)
     assert r.returncode != 0, f"pins did not catch mutant {name}:\n{r.stdout[-2000:]}"
     assert "failed" in r.stdout
