@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--out-dtype", default="bf16", choices=["f32", "bf16"])
     ap.add_argument("--layout", default="xbc", choices=["xbc", "contiguous"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time ssd_backward (upstream gradient ~ N(0,1)) and report the "
+                         "forward+backward rate in a 'fwd_bwd' object")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle until this much CPU time has been spent (min 3 runs)")
     ap.add_argument("--cold-steps", type=int, default=10,
@@ -355,9 +358,47 @@ def main():
                  if cold_ms else None),
         "gpu": torch.cuda.get_device_name(0),
     }
+    if args.backward:
+        result["fwd_bwd"] = time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu,
+                                          ms_per_step)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu, fwd_ms):
+    """HIP-event time of ssd_backward (all gradients) on the same inputs, with
+    an upstream gradient drawn from N(0, 1); the forward+backward rate adds
+    the forward step time measured above."""
+    import torch
+    g = torch.Generator(device=x.device).manual_seed(4)
+    dout = torch.randn(x.shape, generator=g, device=x.device, dtype=torch.float32)
+    prob = ssd.problem_from(x, B, w.chunk_size, cu_seqlens=cu)
+    ws = torch.empty(prob.backward_workspace_size(), dtype=torch.uint8, device=x.device)
+
+    def bwd():
+        return ssd.ssd_backward(x, B, C, dt, A, dout, dt_bias=bias, D=D, z=z, cu_seqlens=cu,
+                                chunk_size=w.chunk_size, workspace=ws)
+
+    for _ in range(max(2, args.warmup // 5)):
+        bwd()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(max(5, args.steps // 5)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        bwd()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    bms = float(np.median(times))
+    return {"bwd_ms": round(bms, 5), "fwd_ms": round(fwd_ms, 5),
+            "fwd_bwd_ms": round(bms + fwd_ms, 5),
+            "tokens_per_s": round(w.tokens / ((bms + fwd_ms) * 1e-3), 1),
+            "workspace_MB": round(ws.numel() / 1e6, 1), "steps": len(times),
+            "note": "median of event-timed backward calls (fp32 staged scans), plus the "
+                    "timed forward step"}
 
 
 if __name__ == "__main__":

@@ -53,8 +53,8 @@
  *   so a call that returns an error has launched nothing (except SSD_ERR_HIP,
  *   returned when a launch itself fails).  ssd_last_error_message() names the
  *   offending argument (thread-local).
- * - Determinism: no atomics in the forward pass; results are bitwise
- *   identical run to run.
+ * - Determinism: no atomics in the forward or backward pass; results are
+ *   bitwise identical run to run.
  */
 #ifndef LIBSSD_SSD_H
 #define LIBSSD_SSD_H
@@ -267,6 +267,54 @@ typedef struct ssd_fwd_args {
  * be shared by calls that overlap in time. */
 ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* a,
                        void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- backward */
+
+typedef struct ssd_bwd_args {
+  /* the forward's inputs, as in ssd_fwd_args */
+  ssd_tensor x, B, C, dt;
+  const float* A;
+  const float* dt_bias;       /* (H) or NULL */
+  const float* D;             /* (H) or NULL */
+  ssd_tensor z;               /* (b, T, H, P) or data == NULL */
+  const float* initial_states;/* (nseq or b, H, P, N) float32 or NULL (zero) */
+  /* incoming gradients */
+  ssd_tensor dout;            /* (b, T, H, P) F32 or BF16: gradient of out */
+  const float* dfinal_states; /* (nseq or b, H, P, N) float32 or NULL (zero) */
+  /* gradients, written; all float32 */
+  ssd_tensor dx;              /* (b, T, H, P) */
+  ssd_tensor dB, dC;          /* (b, T, G, N), summed over the heads of each group */
+  ssd_tensor ddt;             /* (b, T, H): gradient w.r.t. the raw dt (0 where clamped) */
+  ssd_tensor dz;              /* (b, T, H, P); required when z is given */
+  float* dA;                  /* (H) */
+  float* ddt_bias;            /* (H): ddt summed over all tokens */
+  float* dD;                  /* (H) or NULL (written only when D is given) */
+  float* dinitial_states;     /* (nseq or b, H, P, N) or NULL */
+} ssd_bwd_args;
+
+/* Bytes of workspace ssd_backward needs. */
+ssd_status ssd_backward_workspace_size(const ssd_problem* p, size_t* bytes);
+
+/* The gradient of L = sum(dout * out) + sum(dfinal_states * final_states)
+ * with respect to every input of ssd_forward (the backward stages timed in
+ * mamba PR 1012 "Measurements"; SSD Reference section 6 "The autograd
+ * backward contract": gradients of every input, exact for the forward).
+ * The adjoint of the recurrence, dL/dh_t = exp(delta_{t+1} A) dL/dh_{t+1} +
+ * dy_t (outer) C_t, is itself an SSD scan run backwards in time; the call
+ * runs the staged forward four times on operands it prepares (the forward
+ * recompute, then the adjoint read with B for dx and with x for dB, and the
+ * forward state read with dy for dC), and the step-size gradient in closed
+ * form: dL/d(delta_t A) = <dfinal, h_final> + sum_{l >= t} (u_l - v_l) with
+ * u_l = dy_l . (y_l - D x_l) and v_l = x_l . (dx_l - D dy_l), y before the
+ * gate.  Everything after the inputs is fp32 (fp32 chunk states, fp32 matrix
+ * products), so gradients are accurate to fp32 whatever the input dtype.
+ * Packed mode is supported (each sequence runs backwards on its own).
+ * Results are bit-identical run to run (no atomics, fixed sum orders).
+ * workspace: at least ssd_backward_workspace_size(p) bytes, 256-byte
+ * aligned, contents need not be initialised; calls that overlap in time must
+ * not share it. */
+ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* workspace,
+                        size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- errors */
 

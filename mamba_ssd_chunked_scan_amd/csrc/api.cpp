@@ -265,6 +265,106 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
   return ok();
 }
 
+
+// ---------------------------------------------------------------- backward
+
+// The problems of the forward recompute and the three backward scans (see
+// bwd.hip): fwd and dC keep the step definition (softplus, clamp) of the
+// caller's problem, dx and dB take precomputed steps; dB and dC run on the
+// transposed state (head dim N, state dim P, one group per head).  All keep
+// fp32 chunk states.
+struct BwdProblems {
+  ssd_problem fwd, dx, dB, dC;
+};
+
+BwdProblems bwd_problems(const ssd_problem* p) {
+  BwdProblems q;
+  q.fwd = *p;
+  q.fwd.state_dtype = SSD_F32;
+  q.fwd.chunk_meta = nullptr;
+  q.dx = q.fwd;
+  q.dx.dt_softplus = 0;
+  q.dx.dt_clamp = 0;
+  q.dB = q.dx;
+  q.dB.headdim = p->dstate;
+  q.dB.dstate = p->headdim;
+  q.dB.ngroups = p->nheads;
+  q.dC = q.fwd;
+  q.dC.headdim = p->dstate;
+  q.dC.dstate = p->headdim;
+  q.dC.ngroups = p->nheads;
+  return q;
+}
+
+struct BwdWs {
+  size_t yf, sfin, dy, dyr, Cr, Br, Cf, Bf, Cer, Be, xr, xf, delta, gd, dtr, w, dyx, gx, gb, gc, gfirst,
+      dfT, h0T, run, run_bytes, total;
+};
+
+int64_t bwd_tokens(const ssd_problem* p) { return (int64_t)p->batch * p->seqlen; }
+int bwd_nseq(const ssd_problem* p) { return p->nseq > 0 ? p->nseq : p->batch; }
+
+BwdWs bwd_layout(const ssd_problem* p) {
+  BwdWs w;
+  const size_t nt = (size_t)bwd_tokens(p), H = p->nheads, P = p->headdim, N = p->dstate,
+               G = p->ngroups, ns = (size_t)bwd_nseq(p);
+  size_t off = 0;
+  auto take = [&](size_t floats) {
+    const size_t o = off;
+    off += align256(floats * sizeof(float));
+    return o;
+  };
+  w.yf = take(nt * H * P);
+  w.sfin = take(ns * H * P * N);
+  w.dy = take(nt * H * P);
+  w.dyr = take(nt * H * P);
+  w.Cr = take(nt * G * N);
+  w.Br = take(nt * G * N);
+  w.Cf = take(nt * G * N);
+  w.Bf = take(nt * G * N);
+  w.Cer = take(nt * H * N);
+  w.Be = take(nt * H * N);
+  w.xr = take(nt * H * P);
+  w.xf = take(nt * H * P);
+  w.delta = take(nt * H);
+  w.gd = take(nt * H);
+  w.dtr = take(nt * H);
+  w.w = take(nt * H);
+  w.dyx = take(nt * H);
+  w.gx = take(nt * H * P);
+  w.gb = take(nt * H * N);
+  w.gc = take(nt * H * N);
+  w.gfirst = take(ns * H * P * N);
+  w.dfT = take(ns * H * P * N);
+  w.h0T = take(ns * H * P * N);
+  const BwdProblems q = bwd_problems(p);
+  w.run_bytes = 0;
+  for (const ssd_problem* r : {&q.fwd, &q.dx, &q.dB, &q.dC}) {
+    const size_t b = staged_layout(r).total;
+    if (b > w.run_bytes) w.run_bytes = b;
+  }
+  w.run = off;
+  off += align256(w.run_bytes);
+  w.total = off;
+  return w;
+}
+
+// (b, T, rows, width) contiguous fp32 view of a scratch buffer
+ssd_tensor scratch_view(void* ptr, const ssd_problem* p, int rows, int width) {
+  ssd_tensor t;
+  t.data = ptr;
+  t.dtype = SSD_F32;
+  t.stride[0] = (int64_t)p->seqlen * rows * width;
+  t.stride[1] = (int64_t)rows * width;
+  t.stride[2] = width;
+  return t;
+}
+
+ssd_status check_grad_tensor(const ssd_tensor& t, const char* name, bool required) {
+  SSD_TRY(check_vec_tensor(t, name, required, true, false));
+  return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -482,6 +582,148 @@ ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* 
   SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, st, sd, a->D, targ(a->z),
                                  targ(a->out), dcode(a->out.dtype), stream),
           "chunk_scan launch");
+  return ok();
+}
+
+ssd_status ssd_backward_workspace_size(const ssd_problem* p, size_t* bytes) {
+  SSD_TRY(check_problem(p));
+  if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
+  *bytes = bwd_layout(p).total;
+  return ok();
+}
+
+ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  SSD_TRY(check_problem(p));
+  if (!a) return fail(SSD_ERR_NULL, "args is NULL");
+  const bool tok = has_tokens(p);
+  SSD_TRY(check_vec_tensor(a->x, "x", tok));
+  SSD_TRY(check_vec_tensor(a->B, "B", tok));
+  SSD_TRY(check_vec_tensor(a->C, "C", tok));
+  SSD_TRY(check_dt(a->dt, tok));
+  SSD_TRY(check_vec_tensor(a->z, "z", false));
+  SSD_TRY(check_vec_tensor(a->dout, "dout", tok));
+  if (tok && (a->x.dtype != a->B.dtype || a->x.dtype != a->C.dtype))
+    return fail(SSD_ERR_DTYPE, "x, B and C must share a dtype");
+  if (a->z.data && a->z.dtype != a->x.dtype) return fail(SSD_ERR_DTYPE, "z must have x's dtype");
+  if (!a->A) return fail(SSD_ERR_NULL, "A is NULL");
+  SSD_TRY(check_grad_tensor(a->dx, "dx", tok));
+  SSD_TRY(check_grad_tensor(a->dB, "dB", tok));
+  SSD_TRY(check_grad_tensor(a->dC, "dC", tok));
+  SSD_TRY(check_grad_tensor(a->dz, "dz", tok && a->z.data));
+  SSD_TRY(check_dt(a->ddt, tok));
+  if (a->ddt.data && a->ddt.dtype != SSD_F32) return fail(SSD_ERR_DTYPE, "ddt must be F32");
+  if (!a->dA || !a->ddt_bias) return fail(SSD_ERR_NULL, "dA or ddt_bias is NULL");
+  const BwdWs w = bwd_layout(p);
+  if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < w.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, w.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+
+  char* ws = static_cast<char*>(workspace);
+  auto f = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const BwdProblems q = bwd_problems(p);
+  const int H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups;
+  const int ns = bwd_nseq(p);
+  ssd::BwdGeo bg;
+  bg.ntok = (int)bwd_tokens(p);
+  bg.T = p->seqlen;
+  bg.nseq = ns;
+  bg.H = H;
+  bg.P = P;
+  bg.G = G;
+  bg.N = N;
+  bg.hpg = H / G;
+  bg.cu = p->nseq > 0 ? p->cu_seqlens : nullptr;
+  const ssd_tensor none = {nullptr, SSD_F32, {0, 0, 0}};
+  void* run_ws = ws + w.run;
+
+  // 1. fp32 copies of the operands (mirrored in time for the backward scans;
+  // B and C repeated for each head where a scan's head dim is N)
+  const int in = dcode(a->x.dtype);
+  struct Copy { ssd_tensor src; int R, W, rep, rev; size_t dst; };
+  const Copy copies[] = {{a->C, G, N, 1, 1, w.Cr},     {a->B, G, N, 1, 1, w.Br},
+                         {a->C, G, N, 1, 0, w.Cf},     {a->B, G, N, 1, 0, w.Bf},
+                         {a->C, H, N, H / G, 1, w.Cer}, {a->B, H, N, H / G, 0, w.Be},
+                         {a->x, H, P, 1, 1, w.xr},     {a->x, H, P, 1, 0, w.xf}};
+  for (const Copy& c : copies)
+    SSD_HIP(ssd::launch_bwd_gather(bg, targ(c.src), in, c.R, c.W, c.rep, c.rev, f(c.dst), stream),
+            "backward gather launch");
+
+  // 2. forward recompute in fp32 (the step-size gradient below differences
+  // long sums of y-dependent terms, so y is needed to fp32 accuracy): y before
+  // the gate, and the final states
+  ssd_fwd_args fa;
+  fa.x = scratch_view(f(w.xf), p, H, P);
+  fa.B = scratch_view(f(w.Bf), p, G, N);
+  fa.C = scratch_view(f(w.Cf), p, G, N);
+  fa.dt = a->dt;
+  fa.A = a->A; fa.dt_bias = a->dt_bias; fa.D = a->D; fa.z = none;
+  fa.initial_states = a->initial_states;
+  fa.out = scratch_view(f(w.yf), p, H, P);
+  fa.final_states = f(w.sfin);
+  SSD_TRY(ssd_forward(&q.fwd, SSD_ALGO_STAGED, &fa, run_ws, w.run_bytes, stream));
+
+  // 3. gate, steps, transposed states
+  SSD_HIP(ssd::launch_bwd_gate(bg, targ(a->dout), dcode(a->dout.dtype), targ(a->z), in, f(w.yf),
+                               f(w.dy), f(w.dyr), targ(a->dz), stream),
+          "backward gate launch");
+  SSD_HIP(ssd::launch_bwd_steps(bg, targ(a->dt), dcode(a->dt.dtype), a->A, a->dt_bias,
+                                p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, f(w.delta),
+                                f(w.gd), f(w.dtr), stream),
+          "backward steps launch");
+  if (a->dfinal_states)
+    SSD_HIP(ssd::launch_bwd_transpose_states(ns * H, P, N, a->dfinal_states, f(w.dfT), stream),
+            "backward transpose launch");
+  if (a->initial_states)
+    SSD_HIP(ssd::launch_bwd_transpose_states(ns * H, P, N, a->initial_states, f(w.h0T), stream),
+            "backward transpose launch");
+
+  // 4. the three scans: dx and dB backwards in time (mirrored operands,
+  // shifted steps), dC forwards
+  ssd_tensor dtr;
+  dtr.data = f(w.dtr);
+  dtr.dtype = SSD_F32;
+  dtr.stride[0] = (int64_t)p->seqlen * H;
+  dtr.stride[1] = H;
+  dtr.stride[2] = 1;
+  ssd_fwd_args ra;
+  ra.x = scratch_view(f(w.dyr), p, H, P);
+  ra.B = scratch_view(f(w.Cr), p, G, N);
+  ra.C = scratch_view(f(w.Br), p, G, N);
+  ra.dt = dtr; ra.A = a->A; ra.dt_bias = nullptr; ra.D = nullptr; ra.z = none;
+  ra.initial_states = a->dfinal_states;
+  ra.out = scratch_view(f(w.gx), p, H, P);
+  ra.final_states = f(w.gfirst);
+  SSD_TRY(ssd_forward(&q.dx, SSD_ALGO_STAGED, &ra, run_ws, w.run_bytes, stream));
+  ra.x = scratch_view(f(w.Cer), p, H, N);
+  ra.B = scratch_view(f(w.dyr), p, H, P);
+  ra.C = scratch_view(f(w.xr), p, H, P);
+  ra.initial_states = a->dfinal_states ? f(w.dfT) : nullptr;
+  ra.out = scratch_view(f(w.gb), p, H, N);
+  ra.final_states = nullptr;
+  SSD_TRY(ssd_forward(&q.dB, SSD_ALGO_STAGED, &ra, run_ws, w.run_bytes, stream));
+  ra.x = scratch_view(f(w.Be), p, H, N);
+  ra.B = scratch_view(f(w.xf), p, H, P);
+  ra.C = scratch_view(f(w.dy), p, H, P);
+  ra.dt = a->dt;
+  ra.dt_bias = a->dt_bias;
+  ra.initial_states = a->initial_states ? f(w.h0T) : nullptr;
+  ra.out = scratch_view(f(w.gc), p, H, N);
+  SSD_TRY(ssd_forward(&q.dC, SSD_ALGO_STAGED, &ra, run_ws, w.run_bytes, stream));
+
+  // 5. gradients
+  SSD_HIP(ssd::launch_bwd_tokens(bg, targ(a->x), in, a->D, f(w.dy), f(w.yf), f(w.gx),
+                                 targ(a->dx), f(w.w), f(w.dyx), stream),
+          "backward tokens launch");
+  SSD_HIP(ssd::launch_bwd_group_sums(bg, f(w.gb), f(w.gc), targ(a->dB), targ(a->dC), stream),
+          "backward group sums launch");
+  SSD_HIP(ssd::launch_bwd_steps_grad(bg, f(w.w), f(w.dyx), f(w.delta), f(w.gd), a->A,
+                                     a->dfinal_states, f(w.sfin), f(w.gfirst), targ(a->ddt),
+                                     a->dA, a->ddt_bias, a->D ? a->dD : nullptr,
+                                     a->dinitial_states, stream),
+          "backward steps gradient launch");
   return ok();
 }
 

@@ -1,0 +1,373 @@
+// bwd.hip -- the kernels of the SSD backward pass that are not scans.
+//
+// The backward of the recurrence (mamba PR 1012, "Measurements": the dx/ddt,
+// dB, dC, dA-cumsum and dstates backward stages; SSD Reference, section 6 "The
+// autograd backward contract") is run as three more SSD forward scans on
+// operands this file prepares, plus the pieces below:
+//
+//   dL/dS_t = G_t obeys G_t = exp(a_{t+1}) G_{t+1} + dy_t (outer) C_t, a scan
+//   backwards in time.  Read with B it gives dx, read with x (state
+//   transposed) it gives the head's share of dB; the forward state S_t read
+//   with dy (state transposed) gives the head's share of dC.  Run on reversed
+//   sequences, each is an ordinary forward scan with the step sizes shifted by
+//   one token (the decay between t and t+1 belongs to token t+1) and the final
+//   state's gradient as the initial state.
+//
+//   For the step sizes, with u_t = dy_t . (y_t - D x_t) and
+//   v_t = x_t . (dx_t - D dy_t) (y before the gate), telescoping
+//   <G_t, S_t> = <G_{t+1}, S_{t+1}> - v_{t+1} + u_t gives
+//     dL/da_t = exp(a_t) <G_t, S_{t-1}> = <dfinal, S_final> + sum_{l >= t} (u_l - v_l)
+//   over the token's own sequence, so ddt needs one reverse scan of a scalar
+//   per token and head.
+//
+// Everything here is fp32 and deterministic: every sum has a fixed order.
+#include "kernels.hpp"
+#include "stage_varlen.hpp"
+
+namespace ssd {
+
+namespace {
+
+// ---- tokens on the packed axis (b * T in batch mode)
+
+// Sequence span [s0, s1) of packed token tp.
+__device__ __forceinline__ void seq_of(const BwdGeo& q, int tp, int& s0, int& s1) {
+  if (!q.cu) {
+    s0 = (tp / q.T) * q.T;
+    s1 = s0 + q.T;
+    return;
+  }
+  int lo = 0, hi = q.nseq;  // find the last i with cu[i] <= tp
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) / 2;
+    if (clamp_tok(q.cu[mid], q.T) <= tp) lo = mid; else hi = mid;
+  }
+  s0 = clamp_tok(q.cu[lo], q.T);
+  s1 = max(clamp_tok(q.cu[lo + 1], q.T), s0);
+  if (tp < s0 || tp >= s1) {  // a token outside every sequence stands alone
+    s0 = tp;
+    s1 = tp + 1;
+  }
+}
+
+// The token at the mirrored position of tp inside its sequence.
+__device__ __forceinline__ int mirror(const BwdGeo& q, int tp) {
+  int s0, s1;
+  seq_of(q, tp, s0, s1);
+  return s0 + s1 - 1 - tp;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* tok_row(const TArg& a, const BwdGeo& q, int tp, int hg) {
+  return q.cu ? row_ptr<T>(a, 0, tp, hg) : row_ptr<T>(a, tp / q.T, tp % q.T, hg);
+}
+__device__ __forceinline__ float* tok_row_f32(const TArg& a, const BwdGeo& q, int tp, int hg) {
+  return q.cu ? row_ptr_mut<float>(a, 0, tp, hg) : row_ptr_mut<float>(a, tp / q.T, tp % q.T, hg);
+}
+
+template <typename T>
+__device__ __forceinline__ float load_f32(const TArg& a, const BwdGeo& q, int tp, int hg, int i) {
+  return to_f32<T>(tok_row<T>(a, q, tp, hg)[i]);
+}
+__device__ __forceinline__ float load_any(const TArg& a, int dtype, const BwdGeo& q, int tp, int hg,
+                                          int i) {
+  return dtype == DT_BF16 ? load_f32<bf16>(a, q, tp, hg, i) : load_f32<float>(a, q, tp, hg, i);
+}
+
+__device__ __forceinline__ float sigmoid(float v) { return 1.0f / (1.0f + __expf(-v)); }
+
+// Step size and d(step)/du of one token: softplus (or identity), clamp.
+__device__ __forceinline__ void step_size(float u, int softplus, int clamp, float dt_min,
+                                          float dt_max, float& delta, float& gd) {
+  float d = u, g = 1.0f;
+  if (softplus) {
+    d = u > 20.0f ? u : log1pf(__expf(u));
+    g = sigmoid(u);
+  }
+  if (clamp) {
+    if (d < dt_min) { d = dt_min; g = 0.0f; }
+    if (d > dt_max) { d = dt_max; g = 0.0f; }
+  }
+  delta = d;
+  gd = g;
+}
+
+// ---- dst (ntok, R, W) fp32 = rows of src, optionally mirrored in time and
+// with dst row r reading src row r / rep (a group's row for each of its heads)
+__global__ __launch_bounds__(256) void k_gather(BwdGeo q, TArg src, int dtype, int R, int W,
+                                                int rep, int reverse, float* dst) {
+  const int64_t total = (int64_t)q.ntok * R * W;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int w = (int)(i % W);
+    const int r = (int)((i / W) % R);
+    const int tp = (int)(i / ((int64_t)W * R));
+    const int ts = reverse ? mirror(q, tp) : tp;
+    dst[i] = load_any(src, dtype, q, ts, r / rep, w);
+  }
+}
+
+// ---- the gate: dy = dout silu(z), dz = dout y silu'(z) (dy = dout without a
+// gate); dy is written in token order and mirrored
+__global__ __launch_bounds__(256) void k_gate(BwdGeo q, TArg dout, int dout_dtype, TArg z,
+                                              int z_dtype, const float* y, float* dy,
+                                              float* dy_rev, TArg dz) {
+  const int64_t total = (int64_t)q.ntok * q.H * q.P;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int p = (int)(i % q.P);
+    const int h = (int)((i / q.P) % q.H);
+    const int tp = (int)(i / ((int64_t)q.P * q.H));
+    const float go = load_any(dout, dout_dtype, q, tp, h, p);
+    float g = go;
+    if (z.p) {
+      const float zz = load_any(z, z_dtype, q, tp, h, p);
+      const float s = sigmoid(zz);
+      g = go * zz * s;
+      tok_row_f32(dz, q, tp, h)[p] = go * y[i] * (s * (1.0f + zz * (1.0f - s)));
+    }
+    dy[i] = g;
+    dy_rev[((int64_t)mirror(q, tp) * q.H + h) * q.P + p] = g;
+  }
+}
+
+// ---- per (token, head): step size, d(step)/du, and the mirrored, shifted
+// step of the backward scans (the next token's step; 0 at a sequence's end)
+__global__ __launch_bounds__(256) void k_steps(BwdGeo q, TArg dt, int dt_dtype, const float* A,
+                                               const float* dt_bias, int softplus, int clamp,
+                                               float dt_min, float dt_max, float* delta,
+                                               float* gd, float* dt_rev) {
+  const int64_t total = (int64_t)q.ntok * q.H;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int h = (int)(i % q.H);
+    const int tp = (int)(i / q.H);
+    const float bias = dt_bias ? dt_bias[h] : 0.0f;
+    float d, g;
+    step_size(load_any(dt, dt_dtype, q, tp, h, 0) + bias, softplus, clamp, dt_min, dt_max, d, g);
+    delta[i] = d;
+    gd[i] = g;
+    int s0, s1;
+    seq_of(q, tp, s0, s1);
+    float dn = 0.0f;
+    if (tp + 1 < s1)
+      step_size(load_any(dt, dt_dtype, q, tp + 1, h, 0) + bias, softplus, clamp, dt_min, dt_max,
+                dn, g);
+    dt_rev[(int64_t)(s0 + s1 - 1 - tp) * q.H + h] = dn;
+  }
+}
+
+// ---- (nseq, H, P, N) -> (nseq, H, N, P)
+__global__ __launch_bounds__(256) void k_transpose_states(int nsh, int P, int N, const float* src,
+                                                          float* dst) {
+  const int64_t total = (int64_t)nsh * P * N;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int n = (int)(i % N);
+    const int p = (int)((i / N) % P);
+    const int64_t m = i / ((int64_t)N * P);
+    dst[(m * N + n) * P + p] = src[i];
+  }
+}
+
+// ---- per (token, head), one wavefront each: dx = mirrored dx-scan output +
+// D dy, w = u - v (see the header), and dy . x for dD
+__global__ __launch_bounds__(256) void k_tokens(BwdGeo q, TArg x, int x_dtype, const float* D,
+                                                const float* dy, const float* y,
+                                                const float* gx_rev, TArg dx, float* w,
+                                                float* dyx) {
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int64_t item = blockIdx.x * 4ll + wave;
+  if (item >= (int64_t)q.ntok * q.H) return;
+  const int h = (int)(item % q.H);
+  const int tp = (int)(item / q.H);
+  const int tm = mirror(q, tp);
+  const float Dh = D ? D[h] : 0.0f;
+  // u and v nearly cancel in the telescoped sums: both in fp64
+  double su = 0.0, sv = 0.0, sx = 0.0;
+  for (int p = lane; p < q.P; p += kWave) {
+    const int64_t o = item * q.P + p;
+    const float xv = load_any(x, x_dtype, q, tp, h, p);
+    const float g = gx_rev[((int64_t)tm * q.H + h) * q.P + p];
+    tok_row_f32(dx, q, tp, h)[p] = g + Dh * dy[o];
+    su += (double)dy[o] * ((double)y[o] - (double)Dh * xv);
+    sv += (double)xv * g;
+    sx += (double)dy[o] * xv;
+  }
+  su = wave_inclusive_sum_f64(su);
+  sv = wave_inclusive_sum_f64(sv);
+  sx = wave_inclusive_sum_f64(sx);
+  if (lane == kWave - 1) {
+    w[item] = su - sv;
+    dyx[item] = sx;
+  }
+}
+
+// ---- per (token, group, n): dB and dC summed over the group's heads (dB's
+// scan ran mirrored)
+__global__ __launch_bounds__(256) void k_group_sums(BwdGeo q, const float* gb_rev,
+                                                    const float* gc, TArg dB, TArg dC) {
+  const int64_t total = (int64_t)q.ntok * q.G * q.N;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int n = (int)(i % q.N);
+    const int g = (int)((i / q.N) % q.G);
+    const int tp = (int)(i / ((int64_t)q.N * q.G));
+    const int tm = mirror(q, tp);
+    float sb = 0.0f, sc = 0.0f;
+    for (int k = 0; k < q.hpg; ++k) {
+      const int h = g * q.hpg + k;
+      sb += gb_rev[((int64_t)tm * q.H + h) * q.N + n];
+      sc += gc[((int64_t)tp * q.H + h) * q.N + n];
+    }
+    tok_row_f32(dB, q, tp, g)[n] = sb;
+    tok_row_f32(dC, q, tp, g)[n] = sc;
+  }
+}
+
+__device__ __forceinline__ double block_sum(double v, double* lds) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  v = wave_inclusive_sum_f64(v);
+  if (lane == kWave - 1) lds[wave] = v;
+  __syncthreads();
+  const double t = lds[0] + lds[1] + lds[2] + lds[3];
+  __syncthreads();
+  return t;
+}
+
+// ---- one workgroup per head: ddt (reverse scan of w per sequence, seeded
+// with <dfinal, S_final>), dA, ddt_bias, dD, and the initial-state gradient
+// exp(a_first) G_first (G_first = the final state of the mirrored dx scan)
+__global__ __launch_bounds__(256) void k_steps_grad(BwdGeo q, const float* w, const float* dyx,
+                                                    const float* delta, const float* gd,
+                                                    const float* A, const float* dfinal,
+                                                    const float* sfinal, const float* gfirst,
+                                                    TArg ddt, float* dA, float* ddt_bias,
+                                                    float* dD, float* dh0) {
+  // every running sum in fp64: the scan below adds up to a sequence's length
+  // of terms that largely cancel
+  __shared__ double lds[4];
+  __shared__ double seg[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const float Ah = A[h];
+  const int64_t PN = (int64_t)q.P * q.N;
+  double accA = 0.0, accB = 0.0, accD = 0.0;
+  for (int i = 0; i < q.nseq; ++i) {
+    int s0, s1;
+    if (q.cu) {
+      s0 = clamp_tok(q.cu[i], q.T);
+      s1 = max(clamp_tok(q.cu[i + 1], q.T), s0);
+    } else {
+      s0 = i * q.T;
+      s1 = s0 + q.T;
+    }
+    const int64_t so = ((int64_t)i * q.H + h) * PN;
+    double c0 = 0.0;
+    if (dfinal) {
+      double part = 0.0;
+      for (int64_t k = tid; k < PN; k += 256) part += (double)dfinal[so + k] * sfinal[so + k];
+      c0 = block_sum(part, lds);
+    }
+    // thread k owns the contiguous segment [a, b) of the sequence
+    const int L = s1 - s0;
+    const int per = (L + 255) / 256;
+    const int a = s0 + min(tid * per, L), b = s0 + min((tid + 1) * per, L);
+    double tot = 0.0;
+    for (int t = a; t < b; ++t) tot += w[(int64_t)t * q.H + h];
+    seg[tid] = tot;
+    __syncthreads();
+    double after = c0;  // c0 + sum of w over the segments after this one
+    for (int k = tid + 1; k < 256; ++k) after += seg[k];
+    __syncthreads();
+    double run = after;
+    for (int t = b - 1; t >= a; --t) {
+      const int64_t it = (int64_t)t * q.H + h;
+      run += w[it];
+      const double g = run * Ah * gd[it];
+      tok_row_f32(ddt, q, t, h)[0] = (float)g;
+      accA += run * delta[it];
+      accB += g;
+      accD += dyx[it];
+    }
+    if (dh0) {
+      const float e = L > 0 ? __expf(delta[(int64_t)s0 * q.H + h] * Ah) : 1.0f;
+      for (int64_t k = tid; k < PN; k += 256) dh0[so + k] = e * gfirst[so + k];
+    }
+  }
+  accA = block_sum(accA, lds);
+  accB = block_sum(accB, lds);
+  accD = block_sum(accD, lds);
+  if (tid == 0) {
+    dA[h] = (float)accA;
+    ddt_bias[h] = (float)accB;
+    if (dD) dD[h] = (float)accD;
+  }
+}
+
+int grid_for(int64_t n) {
+  const int64_t g = (n + 255) / 256;
+  return (int)(g < 8192 ? g : 8192);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_gather(const BwdGeo& q, TArg src, int dtype, int R, int W, int rep,
+                             int reverse, float* dst, hipStream_t s) {
+  const int64_t n = (int64_t)q.ntok * R * W;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gather, dim3(grid_for(n)), dim3(256), 0, s, q, src, dtype, R, W, rep,
+                     reverse, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_gate(const BwdGeo& q, TArg dout, int dout_dtype, TArg z, int z_dtype,
+                           const float* y, float* dy, float* dy_rev, TArg dz, hipStream_t s) {
+  const int64_t n = (int64_t)q.ntok * q.H * q.P;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gate, dim3(grid_for(n)), dim3(256), 0, s, q, dout, dout_dtype, z, z_dtype,
+                     y, dy, dy_rev, dz);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_steps(const BwdGeo& q, TArg dt, int dt_dtype, const float* A,
+                            const float* dt_bias, int softplus, int clamp, float dt_min,
+                            float dt_max, float* delta, float* gd, float* dt_rev, hipStream_t s) {
+  const int64_t n = (int64_t)q.ntok * q.H;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_steps, dim3(grid_for(n)), dim3(256), 0, s, q, dt, dt_dtype, A, dt_bias,
+                     softplus, clamp, dt_min, dt_max, delta, gd, dt_rev);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_transpose_states(int nsh, int P, int N, const float* src, float* dst,
+                                       hipStream_t s) {
+  const int64_t n = (int64_t)nsh * P * N;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_transpose_states, dim3(grid_for(n)), dim3(256), 0, s, nsh, P, N, src, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_tokens(const BwdGeo& q, TArg x, int x_dtype, const float* D,
+                             const float* dy, const float* y, const float* gx_rev, TArg dx,
+                             float* w, float* dyx, hipStream_t s) {
+  const int64_t items = (int64_t)q.ntok * q.H;
+  if (items == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tokens, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, q, x, x_dtype,
+                     D, dy, y, gx_rev, dx, w, dyx);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_group_sums(const BwdGeo& q, const float* gb_rev, const float* gc, TArg dB,
+                                 TArg dC, hipStream_t s) {
+  const int64_t n = (int64_t)q.ntok * q.G * q.N;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_group_sums, dim3(grid_for(n)), dim3(256), 0, s, q, gb_rev, gc, dB, dC);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_steps_grad(const BwdGeo& q, const float* w, const float* dyx,
+                                 const float* delta, const float* gd, const float* A,
+                                 const float* dfinal, const float* sfinal, const float* gfirst,
+                                 TArg ddt, float* dA, float* ddt_bias, float* dD, float* dh0,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(k_steps_grad, dim3(q.H), dim3(256), 0, s, q, w, dyx, delta, gd, A, dfinal,
+                     sfinal, gfirst, ddt, dA, ddt_bias, dD, dh0);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

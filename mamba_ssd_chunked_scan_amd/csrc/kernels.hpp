@@ -66,4 +66,30 @@ struct FusedLaunch {
 // Two launches: a small reset/table kernel, then the fused forward.
 hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s);
 
+// ---- backward (bwd.hip): tokens on the packed axis, ntok = b * T (batch) or
+// T (packed, cu != NULL); scratch tensors are contiguous fp32 (ntok, rows, width)
+struct BwdGeo {
+  int ntok, T, nseq, H, P, G, N, hpg;
+  const int32_t* cu;
+};
+hipError_t launch_bwd_gather(const BwdGeo& q, TArg src, int dtype, int R, int W, int rep,
+                             int reverse, float* dst, hipStream_t s);
+hipError_t launch_bwd_gate(const BwdGeo& q, TArg dout, int dout_dtype, TArg z, int z_dtype,
+                           const float* y, float* dy, float* dy_rev, TArg dz, hipStream_t s);
+hipError_t launch_bwd_steps(const BwdGeo& q, TArg dt, int dt_dtype, const float* A,
+                            const float* dt_bias, int softplus, int clamp, float dt_min,
+                            float dt_max, float* delta, float* gd, float* dt_rev, hipStream_t s);
+hipError_t launch_bwd_transpose_states(int nsh, int P, int N, const float* src, float* dst,
+                                       hipStream_t s);
+hipError_t launch_bwd_tokens(const BwdGeo& q, TArg x, int x_dtype, const float* D,
+                             const float* dy, const float* y, const float* gx_rev, TArg dx,
+                             float* w, float* dyx, hipStream_t s);
+hipError_t launch_bwd_group_sums(const BwdGeo& q, const float* gb_rev, const float* gc, TArg dB,
+                                 TArg dC, hipStream_t s);
+hipError_t launch_bwd_steps_grad(const BwdGeo& q, const float* w, const float* dyx,
+                                 const float* delta, const float* gd, const float* A,
+                                 const float* dfinal, const float* sfinal, const float* gfirst,
+                                 TArg ddt, float* dA, float* ddt_bias, float* dD, float* dh0,
+                                 hipStream_t s);
+
 }  // namespace ssd

@@ -7,8 +7,8 @@ if ``libssd.so`` has not been built, or a call fails, an exception is raised.
 
 Function names follow the C calls: ``ssd_chunk_cumsum``, ``ssd_bmm_chunk``,
 ``ssd_chunk_state``, ``ssd_state_passing``, ``ssd_chunk_scan``,
-``ssd_varlen_chunk_meta``, ``ssd_forward``.  Each takes torch tensors and
-returns the tensors it wrote.
+``ssd_varlen_chunk_meta``, ``ssd_forward``, ``ssd_backward``.  Each takes torch
+tensors and returns the tensors it wrote.
 """
 from __future__ import annotations
 
@@ -58,11 +58,22 @@ class SsdFwdArgs(ctypes.Structure):
                 ("final_states", ctypes.c_void_p)]
 
 
+class SsdBwdArgs(ctypes.Structure):
+    _fields_ = [("x", SsdTensor), ("B", SsdTensor), ("C", SsdTensor), ("dt", SsdTensor),
+                ("A", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p), ("D", ctypes.c_void_p),
+                ("z", SsdTensor), ("initial_states", ctypes.c_void_p),
+                ("dout", SsdTensor), ("dfinal_states", ctypes.c_void_p),
+                ("dx", SsdTensor), ("dB", SsdTensor), ("dC", SsdTensor), ("ddt", SsdTensor),
+                ("dz", SsdTensor), ("dA", ctypes.c_void_p), ("ddt_bias", ctypes.c_void_p),
+                ("dD", ctypes.c_void_p), ("dinitial_states", ctypes.c_void_p)]
+
+
 _lib = None
 EXPORTS = ("ssd_problem_check", "ssd_num_chunks", "ssd_varlen_meta_len", "ssd_workspace_size",
            "ssd_varlen_chunk_meta", "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum",
            "ssd_bmm_chunk", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
-           "ssd_forward", "ssd_status_string", "ssd_last_error_message", "ssd_version")
+           "ssd_forward", "ssd_backward_workspace_size", "ssd_backward",
+           "ssd_status_string", "ssd_last_error_message", "ssd_version")
 
 
 def lib():
@@ -92,9 +103,12 @@ def lib():
                                      SsdTensor, SsdTensor, vp]
         L.ssd_forward.argtypes = [P(SsdProblem), ctypes.c_int, P(SsdFwdArgs), vp,
                                   ctypes.c_size_t, vp]
+        L.ssd_backward_workspace_size.argtypes = [P(SsdProblem), P(ctypes.c_size_t)]
+        L.ssd_backward.argtypes = [P(SsdProblem), P(SsdBwdArgs), vp, ctypes.c_size_t, vp]
         for name in ("ssd_problem_check", "ssd_workspace_size", "ssd_varlen_chunk_meta",
                      "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum", "ssd_bmm_chunk",
-                     "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward"):
+                     "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
+                     "ssd_backward_workspace_size", "ssd_backward"):
             getattr(L, name).restype = st
         L.ssd_status_string.argtypes = [ctypes.c_int]
         L.ssd_status_string.restype = ctypes.c_char_p
@@ -208,6 +222,11 @@ class Problem:
     def workspace_size(self, algo="staged") -> int:
         n = ctypes.c_size_t(0)
         _check(lib().ssd_workspace_size(ctypes.byref(self.c()), ALGO[algo], ctypes.byref(n)))
+        return int(n.value)
+
+    def backward_workspace_size(self) -> int:
+        n = ctypes.c_size_t(0)
+        _check(lib().ssd_backward_workspace_size(ctypes.byref(self.c()), ctypes.byref(n)))
         return int(n.value)
 
 
@@ -334,3 +353,57 @@ def ssd_forward(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=Non
     _check(lib().ssd_forward(ctypes.byref(prob.c()), ALGO[algo], ctypes.byref(a),
                              workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return out, final_states
+
+
+@dataclass
+class Grads:
+    dx: torch.Tensor
+    dB: torch.Tensor
+    dC: torch.Tensor
+    ddt: torch.Tensor
+    dA: torch.Tensor
+    ddt_bias: torch.Tensor
+    dD: torch.Tensor | None
+    dz: torch.Tensor | None
+    dinitial_states: torch.Tensor
+
+
+def ssd_backward(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_states=None,
+                 dfinal_states=None, cu_seqlens=None, chunk_size=128, dt_softplus=True,
+                 dt_limit=None, workspace=None, stream=None) -> Grads:
+    """Gradients of sum(dout * out) + sum(dfinal_states * final_states) with
+    respect to every input of ``ssd_forward`` (same arguments and layouts);
+    all gradients are float32."""
+    prob = problem_from(x, B, chunk_size, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
+                        dt_limit=dt_limit)
+    dev, f32 = x.device, torch.float32
+    nseq = prob.nseq if prob.packed else prob.batch
+    g = Grads(dx=torch.empty(x.shape, dtype=f32, device=dev),
+              dB=torch.empty(B.shape, dtype=f32, device=dev),
+              dC=torch.empty(C.shape, dtype=f32, device=dev),
+              ddt=torch.empty(dt.shape, dtype=f32, device=dev),
+              dA=torch.empty(prob.nheads, dtype=f32, device=dev),
+              ddt_bias=torch.empty(prob.nheads, dtype=f32, device=dev),
+              dD=torch.empty(prob.nheads, dtype=f32, device=dev) if D is not None else None,
+              dz=torch.empty(x.shape, dtype=f32, device=dev) if z is not None else None,
+              dinitial_states=torch.empty((nseq, prob.nheads, prob.headdim, prob.dstate),
+                                          dtype=f32, device=dev))
+    need = prob.backward_workspace_size()
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    a = SsdBwdArgs()
+    pk = prob.packed
+    a.x, a.B, a.C = tensor_arg(x, pk), tensor_arg(B, pk), tensor_arg(C, pk)
+    a.dt = tensor_arg(dt, pk)
+    a.A, a.dt_bias, a.D = A.data_ptr(), _ptr(dt_bias), _ptr(D)
+    a.z = tensor_arg(z, pk)
+    a.initial_states = _ptr(initial_states)
+    a.dout = tensor_arg(dout, pk)
+    a.dfinal_states = _ptr(dfinal_states)
+    a.dx, a.dB, a.dC = tensor_arg(g.dx, pk), tensor_arg(g.dB, pk), tensor_arg(g.dC, pk)
+    a.ddt, a.dz = tensor_arg(g.ddt, pk), tensor_arg(g.dz, pk)
+    a.dA, a.ddt_bias, a.dD = g.dA.data_ptr(), g.ddt_bias.data_ptr(), _ptr(g.dD)
+    a.dinitial_states = g.dinitial_states.data_ptr()
+    _check(lib().ssd_backward(ctypes.byref(prob.c()), ctypes.byref(a), workspace.data_ptr(),
+                              workspace.numel(), _stream(stream)))
+    return g
