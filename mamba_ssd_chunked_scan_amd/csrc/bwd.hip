@@ -92,18 +92,46 @@ __device__ __forceinline__ void step_size(float u, int softplus, int clamp, floa
   gd = g;
 }
 
+// ---- rows of width W (a multiple of 4): W / 4 threads per row, each on 4
+// consecutive elements; 256 / (W / 4) rows per workgroup.  Indices stay 32-bit
+// (the host checks that the row counts fit).
+struct Row {
+  int row, c, tpr;
+  bool ok;
+};
+__device__ __forceinline__ Row row_of(int W, int nrows) {
+  Row r;
+  r.tpr = W / 4;
+  const int rpb = 256 / r.tpr;
+  const int k = threadIdx.x / r.tpr;
+  r.row = blockIdx.x * rpb + k;
+  r.c = (threadIdx.x % r.tpr) * 4;
+  r.ok = k < rpb && r.row < nrows;
+  return r;
+}
+
+__device__ __forceinline__ f32x4 load4(const TArg& a, int dtype, const BwdGeo& q, int tp, int hg,
+                                       int c) {
+  f32x4 v;
+  if (dtype == DT_BF16) {
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(tok_row<bf16>(a, q, tp, hg) + c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (float)b[i];
+  } else {
+    v = *reinterpret_cast<const f32x4*>(tok_row<float>(a, q, tp, hg) + c);
+  }
+  return v;
+}
+
 // ---- dst (ntok, R, W) fp32 = rows of src, optionally mirrored in time and
 // with dst row r reading src row r / rep (a group's row for each of its heads)
 __global__ __launch_bounds__(256) void k_gather(BwdGeo q, TArg src, int dtype, int R, int W,
                                                 int rep, int reverse, float* dst) {
-  const int64_t total = (int64_t)q.ntok * R * W;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int w = (int)(i % W);
-    const int r = (int)((i / W) % R);
-    const int tp = (int)(i / ((int64_t)W * R));
-    const int ts = reverse ? mirror(q, tp) : tp;
-    dst[i] = load_any(src, dtype, q, ts, r / rep, w);
-  }
+  const Row rw = row_of(W, q.ntok * R);
+  if (!rw.ok) return;
+  const int tp = rw.row / R, r = rw.row % R;
+  const int ts = reverse ? mirror(q, tp) : tp;
+  *reinterpret_cast<f32x4*>(dst + (int64_t)rw.row * W + rw.c) = load4(src, dtype, q, ts, r / rep, rw.c);
 }
 
 // ---- the gate: dy = dout silu(z), dz = dout y silu'(z) (dy = dout without a
@@ -111,22 +139,26 @@ __global__ __launch_bounds__(256) void k_gather(BwdGeo q, TArg src, int dtype, i
 __global__ __launch_bounds__(256) void k_gate(BwdGeo q, TArg dout, int dout_dtype, TArg z,
                                               int z_dtype, const float* y, float* dy,
                                               float* dy_rev, TArg dz) {
-  const int64_t total = (int64_t)q.ntok * q.H * q.P;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int p = (int)(i % q.P);
-    const int h = (int)((i / q.P) % q.H);
-    const int tp = (int)(i / ((int64_t)q.P * q.H));
-    const float go = load_any(dout, dout_dtype, q, tp, h, p);
-    float g = go;
-    if (z.p) {
-      const float zz = load_any(z, z_dtype, q, tp, h, p);
-      const float s = sigmoid(zz);
-      g = go * zz * s;
-      tok_row_f32(dz, q, tp, h)[p] = go * y[i] * (s * (1.0f + zz * (1.0f - s)));
+  const Row rw = row_of(q.P, q.ntok * q.H);
+  if (!rw.ok) return;
+  const int tp = rw.row / q.H, h = rw.row % q.H;
+  const int64_t o = (int64_t)rw.row * q.P + rw.c;
+  const f32x4 go = load4(dout, dout_dtype, q, tp, h, rw.c);
+  f32x4 g = go;
+  if (z.p) {
+    const f32x4 zz = load4(z, z_dtype, q, tp, h, rw.c);
+    const f32x4 yy = *reinterpret_cast<const f32x4*>(y + o);
+    f32x4 d;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float s = sigmoid(zz[i]);
+      g[i] = go[i] * zz[i] * s;
+      d[i] = go[i] * yy[i] * (s * (1.0f + zz[i] * (1.0f - s)));
     }
-    dy[i] = g;
-    dy_rev[((int64_t)mirror(q, tp) * q.H + h) * q.P + p] = g;
+    *reinterpret_cast<f32x4*>(tok_row_f32(dz, q, tp, h) + rw.c) = d;
   }
+  *reinterpret_cast<f32x4*>(dy + o) = g;
+  *reinterpret_cast<f32x4*>(dy_rev + ((int64_t)mirror(q, tp) * q.H + h) * q.P + rw.c) = g;
 }
 
 // ---- per (token, head): step size, d(step)/du, and the mirrored, shifted
@@ -166,58 +198,67 @@ __global__ __launch_bounds__(256) void k_transpose_states(int nsh, int P, int N,
   }
 }
 
-// ---- per (token, head), one wavefront each: dx = mirrored dx-scan output +
-// D dy, w = u - v (see the header), and dy . x for dD
+// ---- per (token, head) row: dx = mirrored dx-scan output + D dy, w = u - v
+// (see the header) and dy . x for dD; the row's partial sums meet in LDS and
+// its first thread adds them in order
 __global__ __launch_bounds__(256) void k_tokens(BwdGeo q, TArg x, int x_dtype, const float* D,
                                                 const float* dy, const float* y,
                                                 const float* gx_rev, TArg dx, float* w,
                                                 float* dyx) {
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  const int64_t item = blockIdx.x * 4ll + wave;
-  if (item >= (int64_t)q.ntok * q.H) return;
-  const int h = (int)(item % q.H);
-  const int tp = (int)(item / q.H);
-  const int tm = mirror(q, tp);
-  const float Dh = D ? D[h] : 0.0f;
-  // u and v nearly cancel in the telescoped sums: both in fp64
+  __shared__ double part[3][256];
+  const Row rw = row_of(q.P, q.ntok * q.H);
   double su = 0.0, sv = 0.0, sx = 0.0;
-  for (int p = lane; p < q.P; p += kWave) {
-    const int64_t o = item * q.P + p;
-    const float xv = load_any(x, x_dtype, q, tp, h, p);
-    const float g = gx_rev[((int64_t)tm * q.H + h) * q.P + p];
-    tok_row_f32(dx, q, tp, h)[p] = g + Dh * dy[o];
-    su += (double)dy[o] * ((double)y[o] - (double)Dh * xv);
-    sv += (double)xv * g;
-    sx += (double)dy[o] * xv;
+  if (rw.ok) {
+    const int tp = rw.row / q.H, h = rw.row % q.H;
+    const int64_t o = (int64_t)rw.row * q.P + rw.c;
+    const float Dh = D ? D[h] : 0.0f;
+    const f32x4 xv = load4(x, x_dtype, q, tp, h, rw.c);
+    const f32x4 g = *reinterpret_cast<const f32x4*>(gx_rev + ((int64_t)mirror(q, tp) * q.H + h) * q.P + rw.c);
+    const f32x4 d = *reinterpret_cast<const f32x4*>(dy + o);
+    const f32x4 yy = *reinterpret_cast<const f32x4*>(y + o);
+    f32x4 out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[i] = g[i] + Dh * d[i];
+      // u and v nearly cancel in the telescoped sums: both in fp64
+      su += (double)d[i] * ((double)yy[i] - (double)Dh * xv[i]);
+      sv += (double)xv[i] * g[i];
+      sx += (double)d[i] * xv[i];
+    }
+    *reinterpret_cast<f32x4*>(tok_row_f32(dx, q, tp, h) + rw.c) = out;
   }
-  su = wave_inclusive_sum_f64(su);
-  sv = wave_inclusive_sum_f64(sv);
-  sx = wave_inclusive_sum_f64(sx);
-  if (lane == kWave - 1) {
-    w[item] = su - sv;
-    dyx[item] = sx;
+  part[0][threadIdx.x] = su;
+  part[1][threadIdx.x] = sv;
+  part[2][threadIdx.x] = sx;
+  __syncthreads();
+  if (rw.ok && rw.c == 0) {
+    double a = 0.0, b = 0.0, c = 0.0;
+    for (int k = 0; k < rw.tpr; ++k) {
+      a += part[0][threadIdx.x + k];
+      b += part[1][threadIdx.x + k];
+      c += part[2][threadIdx.x + k];
+    }
+    w[rw.row] = (float)(a - b);
+    dyx[rw.row] = (float)c;
   }
 }
 
-// ---- per (token, group, n): dB and dC summed over the group's heads (dB's
+// ---- per (token, group) row: dB and dC summed over the group's heads (dB's
 // scan ran mirrored)
 __global__ __launch_bounds__(256) void k_group_sums(BwdGeo q, const float* gb_rev,
                                                     const float* gc, TArg dB, TArg dC) {
-  const int64_t total = (int64_t)q.ntok * q.G * q.N;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int n = (int)(i % q.N);
-    const int g = (int)((i / q.N) % q.G);
-    const int tp = (int)(i / ((int64_t)q.N * q.G));
-    const int tm = mirror(q, tp);
-    float sb = 0.0f, sc = 0.0f;
-    for (int k = 0; k < q.hpg; ++k) {
-      const int h = g * q.hpg + k;
-      sb += gb_rev[((int64_t)tm * q.H + h) * q.N + n];
-      sc += gc[((int64_t)tp * q.H + h) * q.N + n];
-    }
-    tok_row_f32(dB, q, tp, g)[n] = sb;
-    tok_row_f32(dC, q, tp, g)[n] = sc;
+  const Row rw = row_of(q.N, q.ntok * q.G);
+  if (!rw.ok) return;
+  const int tp = rw.row / q.G, g = rw.row % q.G;
+  const int tm = mirror(q, tp);
+  f32x4 sb = {0.0f, 0.0f, 0.0f, 0.0f}, sc = sb;
+  for (int k = 0; k < q.hpg; ++k) {
+    const int h = g * q.hpg + k;
+    sb += *reinterpret_cast<const f32x4*>(gb_rev + ((int64_t)tm * q.H + h) * q.N + rw.c);
+    sc += *reinterpret_cast<const f32x4*>(gc + ((int64_t)tp * q.H + h) * q.N + rw.c);
   }
+  *reinterpret_cast<f32x4*>(tok_row_f32(dB, q, tp, g) + rw.c) = sb;
+  *reinterpret_cast<f32x4*>(tok_row_f32(dC, q, tp, g) + rw.c) = sc;
 }
 
 __device__ __forceinline__ double block_sum(double v, double* lds) {
@@ -299,6 +340,12 @@ __global__ __launch_bounds__(256) void k_steps_grad(BwdGeo q, const float* w, co
   }
 }
 
+// workgroups for `rows` rows of width W (see row_of)
+unsigned row_blocks(int rows, int W) {
+  const int rpb = 256 / (W / 4);
+  return (unsigned)((rows + rpb - 1) / rpb);
+}
+
 int grid_for(int64_t n) {
   const int64_t g = (n + 255) / 256;
   return (int)(g < 8192 ? g : 8192);
@@ -308,19 +355,19 @@ int grid_for(int64_t n) {
 
 hipError_t launch_bwd_gather(const BwdGeo& q, TArg src, int dtype, int R, int W, int rep,
                              int reverse, float* dst, hipStream_t s) {
-  const int64_t n = (int64_t)q.ntok * R * W;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gather, dim3(grid_for(n)), dim3(256), 0, s, q, src, dtype, R, W, rep,
-                     reverse, dst);
+  const int rows = q.ntok * R;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gather, dim3(row_blocks(rows, W)), dim3(256), 0, s, q, src, dtype, R, W,
+                     rep, reverse, dst);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_gate(const BwdGeo& q, TArg dout, int dout_dtype, TArg z, int z_dtype,
                            const float* y, float* dy, float* dy_rev, TArg dz, hipStream_t s) {
-  const int64_t n = (int64_t)q.ntok * q.H * q.P;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_gate, dim3(grid_for(n)), dim3(256), 0, s, q, dout, dout_dtype, z, z_dtype,
-                     y, dy, dy_rev, dz);
+  const int rows = q.ntok * q.H;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_gate, dim3(row_blocks(rows, q.P)), dim3(256), 0, s, q, dout, dout_dtype,
+                     z, z_dtype, y, dy, dy_rev, dz);
   return hipGetLastError();
 }
 
@@ -345,18 +392,19 @@ hipError_t launch_bwd_transpose_states(int nsh, int P, int N, const float* src, 
 hipError_t launch_bwd_tokens(const BwdGeo& q, TArg x, int x_dtype, const float* D,
                              const float* dy, const float* y, const float* gx_rev, TArg dx,
                              float* w, float* dyx, hipStream_t s) {
-  const int64_t items = (int64_t)q.ntok * q.H;
-  if (items == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_tokens, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, q, x, x_dtype,
-                     D, dy, y, gx_rev, dx, w, dyx);
+  const int rows = q.ntok * q.H;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tokens, dim3(row_blocks(rows, q.P)), dim3(256), 0, s, q, x, x_dtype, D,
+                     dy, y, gx_rev, dx, w, dyx);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_group_sums(const BwdGeo& q, const float* gb_rev, const float* gc, TArg dB,
                                  TArg dC, hipStream_t s) {
-  const int64_t n = (int64_t)q.ntok * q.G * q.N;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_group_sums, dim3(grid_for(n)), dim3(256), 0, s, q, gb_rev, gc, dB, dC);
+  const int rows = q.ntok * q.G;
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_group_sums, dim3(row_blocks(rows, q.N)), dim3(256), 0, s, q, gb_rev, gc,
+                     dB, dC);
   return hipGetLastError();
 }
 
