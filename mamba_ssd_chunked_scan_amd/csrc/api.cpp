@@ -4,6 +4,7 @@
 // allocates, synchronises or keeps pointers; all state lives in the arguments.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -175,7 +176,10 @@ StagedWs staged_layout(const ssd_problem* p) {
   const int64_t K = num_chunks(p);
   size_t off = 0;
   w.meta = off;
-  if (p->nseq > 0) off += align256(ssd_varlen_meta_len(p) * sizeof(int32_t));
+  // (the chunk table's length, for a problem already validated)
+  if (p->nseq > 0)
+    off += align256(((size_t)ssd::kMetaHeader + 3 * (size_t)num_chunks(p) + p->nseq + 1) *
+                    sizeof(int32_t));
   w.cs = off;
   off += align256((size_t)K * p->nheads * p->chunk_size * sizeof(float));
   w.cb = off;
@@ -266,6 +270,42 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
 }
 
 
+// The staged forward: a6 (packed mode, unless `meta_in` gives a prebuilt
+// chunk table), a1-a5 in sequence.  Arguments were validated by the caller.
+ssd_status staged_run(const ssd_problem* p, const ssd_fwd_args* a, const int32_t* meta_in,
+                      void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const StagedWs w = staged_layout(p);
+  if (w.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < w.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, w.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  int32_t* meta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws + w.meta) : nullptr;
+  if (meta_in) meta = const_cast<int32_t*>(meta_in);
+  float* cs = reinterpret_cast<float*>(ws + w.cs);
+  float* cb = reinterpret_cast<float*>(ws + w.cb);
+  void* st = ws + w.st;
+  ssd::Geo g = make_geo(p, meta);
+  const int in = dcode(a->x.dtype), sd = dcode(p->state_dtype);
+  if (p->nseq > 0 && !meta_in)
+    SSD_HIP(ssd::launch_varlen_meta(g, p->cu_seqlens, meta, stream), "varlen_chunk_meta launch");
+  SSD_HIP(ssd::launch_chunk_cumsum(g, targ(a->dt), dcode(a->dt.dtype), a->A, a->dt_bias,
+                                   p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, cs, nullptr,
+                                   stream),
+          "chunk_cumsum launch");
+  SSD_HIP(ssd::launch_bmm_chunk(g, targ(a->C), targ(a->B), in, cb, stream), "bmm_chunk launch");
+  SSD_HIP(ssd::launch_chunk_state(g, targ(a->x), targ(a->B), in, cs, st, sd, stream),
+          "chunk_state launch");
+  SSD_HIP(ssd::launch_state_passing(g, st, sd, cs, a->initial_states, st, a->final_states,
+                                    stream),
+          "state_passing launch");
+  SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, st, sd, a->D, targ(a->z),
+                                 targ(a->out), dcode(a->out.dtype), stream),
+          "chunk_scan launch");
+  return ok();
+}
+
 // ---------------------------------------------------------------- backward
 
 // The problems of the forward recompute and the three backward scans (see
@@ -276,6 +316,17 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
 struct BwdProblems {
   ssd_problem fwd, dx, dB, dC;
 };
+
+// The mirrored scans run in packed form (batch rows become sequences) with
+// their own chunk table, whose boundaries mirror the forward ones.
+ssd_problem mirrored(const ssd_problem& q, const ssd_problem* p) {
+  ssd_problem m = q;
+  m.batch = 1;
+  m.seqlen = (int32_t)((int64_t)p->batch * p->seqlen);
+  m.nseq = p->nseq > 0 ? p->nseq : p->batch;
+  m.chunk_meta = nullptr;
+  return m;
+}
 
 BwdProblems bwd_problems(const ssd_problem* p) {
   BwdProblems q;
@@ -297,8 +348,8 @@ BwdProblems bwd_problems(const ssd_problem* p) {
 }
 
 struct BwdWs {
-  size_t yf, sfin, dy, dyr, Cr, Br, Cf, Bf, Cer, Be, xr, xf, delta, gd, dtr, w, dyx, gx, gb, gc, gfirst,
-      dfT, h0T, run, run_bytes, total;
+  size_t yf, dy, dyr, Cr, Br, Cf, Bf, Cer, Be, xr, xf, delta, gd, dtr, w, dyx, gx, gb, gc, gfirst,
+      dfT, h0T, mmeta, mcu, part, run_fwd, run_dx, run_rest, fwd_bytes, dx_bytes, rest_bytes, total;
 };
 
 int64_t bwd_tokens(const ssd_problem* p) { return (int64_t)p->batch * p->seqlen; }
@@ -315,7 +366,6 @@ BwdWs bwd_layout(const ssd_problem* p) {
     return o;
   };
   w.yf = take(nt * H * P);
-  w.sfin = take(ns * H * P * N);
   w.dy = take(nt * H * P);
   w.dyr = take(nt * H * P);
   w.Cr = take(nt * G * N);
@@ -338,13 +388,25 @@ BwdWs bwd_layout(const ssd_problem* p) {
   w.dfT = take(ns * H * P * N);
   w.h0T = take(ns * H * P * N);
   const BwdProblems q = bwd_problems(p);
-  w.run_bytes = 0;
-  for (const ssd_problem* r : {&q.fwd, &q.dx, &q.dB, &q.dC}) {
-    const size_t b = staged_layout(r).total;
-    if (b > w.run_bytes) w.run_bytes = b;
-  }
-  w.run = off;
-  off += align256(w.run_bytes);
+  const ssd_problem mdx = mirrored(q.dx, p), mdB = mirrored(q.dB, p);
+  w.mmeta = off;
+  off += align256(((size_t)ssd::kMetaHeader + 3 * (size_t)num_chunks(&mdx) + mdx.nseq + 1) *
+                  sizeof(int32_t));
+  w.mcu = off;
+  off += align256((ns + 1) * sizeof(int32_t));
+  w.part = off;
+  off += align256((size_t)num_chunks(p) * H * 3 * sizeof(double));
+  // the forward recompute and the mirrored dx scan keep their chunk states
+  // (the step-size anchors); the other two scans share one workspace
+  w.fwd_bytes = staged_layout(&q.fwd).total;
+  w.dx_bytes = staged_layout(&mdx).total;
+  w.rest_bytes = std::max(staged_layout(&mdB).total, staged_layout(&q.dC).total);
+  w.run_fwd = off;
+  off += align256(w.fwd_bytes);
+  w.run_dx = off;
+  off += align256(w.dx_bytes);
+  w.run_rest = off;
+  off += align256(w.rest_bytes);
   w.total = off;
   return w;
 }
@@ -554,35 +616,7 @@ ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* 
   if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
   if (algo == SSD_ALGO_FUSED) return fused_forward(p, a, workspace, ws_bytes, stream);
-  const StagedWs w = staged_layout(p);
-  if (w.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
-  if (ws_bytes < w.total)
-    return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, w.total);
-  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
-    return fail(SSD_ERR_WORKSPACE, "workspace is not 256-byte aligned");
-  char* ws = static_cast<char*>(workspace);
-  int32_t* meta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws + w.meta) : nullptr;
-  float* cs = reinterpret_cast<float*>(ws + w.cs);
-  float* cb = reinterpret_cast<float*>(ws + w.cb);
-  void* st = ws + w.st;
-  ssd::Geo g = make_geo(p, meta);
-  const int in = dcode(a->x.dtype), sd = dcode(p->state_dtype);
-  if (p->nseq > 0)
-    SSD_HIP(ssd::launch_varlen_meta(g, p->cu_seqlens, meta, stream), "varlen_chunk_meta launch");
-  SSD_HIP(ssd::launch_chunk_cumsum(g, targ(a->dt), dcode(a->dt.dtype), a->A, a->dt_bias,
-                                   p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, cs, nullptr,
-                                   stream),
-          "chunk_cumsum launch");
-  SSD_HIP(ssd::launch_bmm_chunk(g, targ(a->C), targ(a->B), in, cb, stream), "bmm_chunk launch");
-  SSD_HIP(ssd::launch_chunk_state(g, targ(a->x), targ(a->B), in, cs, st, sd, stream),
-          "chunk_state launch");
-  SSD_HIP(ssd::launch_state_passing(g, st, sd, cs, a->initial_states, st, a->final_states,
-                                    stream),
-          "state_passing launch");
-  SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, st, sd, a->D, targ(a->z),
-                                 targ(a->out), dcode(a->out.dtype), stream),
-          "chunk_scan launch");
-  return ok();
+  return staged_run(p, a, nullptr, workspace, ws_bytes, stream);
 }
 
 ssd_status ssd_backward_workspace_size(const ssd_problem* p, size_t* bytes) {
@@ -639,7 +673,9 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   bg.hpg = H / G;
   bg.cu = p->nseq > 0 ? p->cu_seqlens : nullptr;
   const ssd_tensor none = {nullptr, SSD_F32, {0, 0, 0}};
-  void* run_ws = ws + w.run;
+  char* ws_fwd = ws + w.run_fwd;
+  char* ws_dx = ws + w.run_dx;
+  char* ws_rest = ws + w.run_rest;
 
   // 1. fp32 copies of the operands (mirrored in time for the backward scans;
   // B and C repeated for each head where a scan's head dim is N)
@@ -653,9 +689,9 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
     SSD_HIP(ssd::launch_bwd_gather(bg, targ(c.src), in, c.R, c.W, c.rep, c.rev, f(c.dst), stream),
             "backward gather launch");
 
-  // 2. forward recompute in fp32 (the step-size gradient below differences
-  // long sums of y-dependent terms, so y is needed to fp32 accuracy): y before
-  // the gate, and the final states
+  // 2. forward recompute in fp32 (the step-size gradients difference sums of
+  // y-dependent terms, so y is needed to fp32 accuracy): y before the gate,
+  // and the carry-in state of every chunk, kept in its workspace
   ssd_fwd_args fa;
   fa.x = scratch_view(f(w.xf), p, H, P);
   fa.B = scratch_view(f(w.Bf), p, G, N);
@@ -664,10 +700,10 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   fa.A = a->A; fa.dt_bias = a->dt_bias; fa.D = a->D; fa.z = none;
   fa.initial_states = a->initial_states;
   fa.out = scratch_view(f(w.yf), p, H, P);
-  fa.final_states = f(w.sfin);
-  SSD_TRY(ssd_forward(&q.fwd, SSD_ALGO_STAGED, &fa, run_ws, w.run_bytes, stream));
+  fa.final_states = nullptr;
+  SSD_TRY(staged_run(&q.fwd, &fa, nullptr, ws_fwd, w.fwd_bytes, stream));
 
-  // 3. gate, steps, transposed states
+  // 3. gate, steps, transposed states, the mirrored chunk table
   SSD_HIP(ssd::launch_bwd_gate(bg, targ(a->dout), dcode(a->dout.dtype), targ(a->z), in, f(w.yf),
                                f(w.dy), f(w.dyr), targ(a->dz), stream),
           "backward gate launch");
@@ -681,31 +717,40 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   if (a->initial_states)
     SSD_HIP(ssd::launch_bwd_transpose_states(ns * H, P, N, a->initial_states, f(w.h0T), stream),
             "backward transpose launch");
+  ssd_problem mdx = mirrored(q.dx, p), mdB = mirrored(q.dB, p);
+  int32_t* mmeta = reinterpret_cast<int32_t*>(ws + w.mmeta);
+  int32_t* mcu = p->nseq > 0 ? const_cast<int32_t*>(p->cu_seqlens)
+                             : reinterpret_cast<int32_t*>(ws + w.mcu);
+  SSD_HIP(ssd::launch_bwd_mirror_meta(bg, p->chunk_size, (int)num_chunks(&mdx), mmeta,
+                                      p->nseq > 0 ? nullptr : mcu, stream),
+          "backward chunk table launch");
+  mdx.cu_seqlens = mcu;
+  mdB.cu_seqlens = mcu;
 
   // 4. the three scans: dx and dB backwards in time (mirrored operands,
-  // shifted steps), dC forwards
+  // shifted steps, mirrored chunk table), dC forwards
   ssd_tensor dtr;
   dtr.data = f(w.dtr);
   dtr.dtype = SSD_F32;
-  dtr.stride[0] = (int64_t)p->seqlen * H;
+  dtr.stride[0] = (int64_t)mdx.seqlen * H;
   dtr.stride[1] = H;
   dtr.stride[2] = 1;
   ssd_fwd_args ra;
-  ra.x = scratch_view(f(w.dyr), p, H, P);
-  ra.B = scratch_view(f(w.Cr), p, G, N);
-  ra.C = scratch_view(f(w.Br), p, G, N);
+  ra.x = scratch_view(f(w.dyr), &mdx, H, P);
+  ra.B = scratch_view(f(w.Cr), &mdx, G, N);
+  ra.C = scratch_view(f(w.Br), &mdx, G, N);
   ra.dt = dtr; ra.A = a->A; ra.dt_bias = nullptr; ra.D = nullptr; ra.z = none;
   ra.initial_states = a->dfinal_states;
-  ra.out = scratch_view(f(w.gx), p, H, P);
+  ra.out = scratch_view(f(w.gx), &mdx, H, P);
   ra.final_states = f(w.gfirst);
-  SSD_TRY(ssd_forward(&q.dx, SSD_ALGO_STAGED, &ra, run_ws, w.run_bytes, stream));
-  ra.x = scratch_view(f(w.Cer), p, H, N);
-  ra.B = scratch_view(f(w.dyr), p, H, P);
-  ra.C = scratch_view(f(w.xr), p, H, P);
+  SSD_TRY(staged_run(&mdx, &ra, mmeta, ws_dx, w.dx_bytes, stream));
+  ra.x = scratch_view(f(w.Cer), &mdB, H, N);
+  ra.B = scratch_view(f(w.dyr), &mdB, H, P);
+  ra.C = scratch_view(f(w.xr), &mdB, H, P);
   ra.initial_states = a->dfinal_states ? f(w.dfT) : nullptr;
-  ra.out = scratch_view(f(w.gb), p, H, N);
+  ra.out = scratch_view(f(w.gb), &mdB, H, N);
   ra.final_states = nullptr;
-  SSD_TRY(ssd_forward(&q.dB, SSD_ALGO_STAGED, &ra, run_ws, w.run_bytes, stream));
+  SSD_TRY(staged_run(&mdB, &ra, mmeta, ws_rest, w.rest_bytes, stream));
   ra.x = scratch_view(f(w.Be), p, H, N);
   ra.B = scratch_view(f(w.xf), p, H, P);
   ra.C = scratch_view(f(w.dy), p, H, P);
@@ -713,7 +758,7 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   ra.dt_bias = a->dt_bias;
   ra.initial_states = a->initial_states ? f(w.h0T) : nullptr;
   ra.out = scratch_view(f(w.gc), p, H, N);
-  SSD_TRY(ssd_forward(&q.dC, SSD_ALGO_STAGED, &ra, run_ws, w.run_bytes, stream));
+  SSD_TRY(staged_run(&q.dC, &ra, nullptr, ws_rest, w.rest_bytes, stream));
 
   // 5. gradients
   SSD_HIP(ssd::launch_bwd_tokens(bg, targ(a->x), in, a->D, f(w.dy), f(w.yf), f(w.gx),
@@ -721,11 +766,16 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
           "backward tokens launch");
   SSD_HIP(ssd::launch_bwd_group_sums(bg, f(w.gb), f(w.gc), targ(a->dB), targ(a->dC), stream),
           "backward group sums launch");
-  SSD_HIP(ssd::launch_bwd_steps_grad(bg, f(w.w), f(w.dyx), f(w.delta), f(w.gd), a->A,
-                                     a->dfinal_states, f(w.sfin), f(w.gfirst), targ(a->ddt),
-                                     a->dA, a->ddt_bias, a->D ? a->dD : nullptr,
-                                     a->dinitial_states, stream),
-          "backward steps gradient launch");
+  const StagedWs lf = staged_layout(&q.fwd), lx = staged_layout(&mdx);
+  const int32_t* fwd_meta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws_fwd + lf.meta) : nullptr;
+  const ssd::Geo gf = make_geo(&q.fwd, fwd_meta);
+  SSD_HIP(ssd::launch_bwd_step_grads(bg, gf, f(w.w), f(w.dyx), f(w.delta), f(w.gd), a->A,
+                                     reinterpret_cast<float*>(ws_fwd + lf.st),
+                                     reinterpret_cast<float*>(ws_dx + lx.st), f(w.gfirst),
+                                     targ(a->ddt), reinterpret_cast<double*>(ws + w.part), a->dA,
+                                     a->ddt_bias, a->D ? a->dD : nullptr, a->dinitial_states,
+                                     stream),
+          "backward step gradients launch");
   return ok();
 }
 

@@ -13,12 +13,17 @@
 //   one token (the decay between t and t+1 belongs to token t+1) and the final
 //   state's gradient as the initial state.
 //
-//   For the step sizes, with u_t = dy_t . (y_t - D x_t) and
-//   v_t = x_t . (dx_t - D dy_t) (y before the gate), telescoping
-//   <G_t, S_t> = <G_{t+1}, S_{t+1}> - v_{t+1} + u_t gives
-//     dL/da_t = exp(a_t) <G_t, S_{t-1}> = <dfinal, S_final> + sum_{l >= t} (u_l - v_l)
-//   over the token's own sequence, so ddt needs one reverse scan of a scalar
-//   per token and head.
+//   For the step sizes, dL/da_t = exp(a_t) <G_t, S_{t-1}>.  At the first
+//   token f of every chunk both states are at hand: S_{f-1} is the forward
+//   scan's carry-in, and G_f the mirrored dx scan's carry-in, because that
+//   scan cuts each mirrored sequence so that its chunk boundaries fall on the
+//   forward ones (a short first chunk of L mod C tokens).  Inside the chunk,
+//   with u_t = dy_t . (y_t - D x_t) and v_t = x_t . (dx_t - D dy_t) (y before
+//   the gate), <G_t, S_t> = <G_{t+1}, S_{t+1}> - v_{t+1} + u_t telescopes to
+//     dL/da_t = dL/da_{t-1} + v_{t-1} - u_{t-1},
+//   so each step-size gradient is an exact inner product at the chunk start
+//   plus a sum of at most C - 1 terms (the terms largely cancel, so the sums
+//   are kept short and in fp64).
 //
 // Everything here is fp32 and deterministic: every sum has a fixed order.
 #include "kernels.hpp"
@@ -271,72 +276,166 @@ __device__ __forceinline__ double block_sum(double v, double* lds) {
   return t;
 }
 
-// ---- one workgroup per head: ddt (reverse scan of w per sequence, seeded
-// with <dfinal, S_final>), dA, ddt_bias, dD, and the initial-state gradient
-// exp(a_first) G_first (G_first = the final state of the mirrored dx scan)
-__global__ __launch_bounds__(256) void k_steps_grad(BwdGeo q, const float* w, const float* dyx,
-                                                    const float* delta, const float* gd,
-                                                    const float* A, const float* dfinal,
-                                                    const float* sfinal, const float* gfirst,
-                                                    TArg ddt, float* dA, float* ddt_bias,
-                                                    float* dD, float* dh0) {
-  // every running sum in fp64: the scan below adds up to a sequence's length
-  // of terms that largely cancel
-  __shared__ double lds[4];
-  __shared__ double seg[256];
-  const int h = blockIdx.x, tid = threadIdx.x;
-  const float Ah = A[h];
-  const int64_t PN = (int64_t)q.P * q.N;
-  double accA = 0.0, accB = 0.0, accD = 0.0;
-  for (int i = 0; i < q.nseq; ++i) {
-    int s0, s1;
-    if (q.cu) {
-      s0 = clamp_tok(q.cu[i], q.T);
-      s1 = max(clamp_tok(q.cu[i + 1], q.T), s0);
-    } else {
-      s0 = i * q.T;
-      s1 = s0 + q.T;
-    }
-    const int64_t so = ((int64_t)i * q.H + h) * PN;
-    double c0 = 0.0;
-    if (dfinal) {
-      double part = 0.0;
-      for (int64_t k = tid; k < PN; k += 256) part += (double)dfinal[so + k] * sfinal[so + k];
-      c0 = block_sum(part, lds);
-    }
-    // thread k owns the contiguous segment [a, b) of the sequence
-    const int L = s1 - s0;
-    const int per = (L + 255) / 256;
-    const int a = s0 + min(tid * per, L), b = s0 + min((tid + 1) * per, L);
-    double tot = 0.0;
-    for (int t = a; t < b; ++t) tot += w[(int64_t)t * q.H + h];
-    seg[tid] = tot;
-    __syncthreads();
-    double after = c0;  // c0 + sum of w over the segments after this one
-    for (int k = tid + 1; k < 256; ++k) after += seg[k];
-    __syncthreads();
-    double run = after;
-    for (int t = b - 1; t >= a; --t) {
-      const int64_t it = (int64_t)t * q.H + h;
-      run += w[it];
-      const double g = run * Ah * gd[it];
-      tok_row_f32(ddt, q, t, h)[0] = (float)g;
-      accA += run * delta[it];
-      accB += g;
-      accD += dyx[it];
-    }
-    if (dh0) {
-      const float e = L > 0 ? __expf(delta[(int64_t)s0 * q.H + h] * Ah) : 1.0f;
-      for (int64_t k = tid; k < PN; k += 256) dh0[so + k] = e * gfirst[so + k];
-    }
+// Sequence i's span on the packed axis (batch mode: cu == NULL, length T each).
+__device__ __forceinline__ void span_of(const BwdGeo& q, int i, int& s0, int& L) {
+  if (q.cu) {
+    seq_span(q.cu, i, q.T, s0, L);
+  } else {
+    s0 = i * q.T;
+    L = q.T;
   }
-  accA = block_sum(accA, lds);
-  accB = block_sum(accB, lds);
-  accD = block_sum(accD, lds);
+}
+
+// ---- the chunk table of the mirrored scans (layout of ssd_varlen_meta_len):
+// sequence i of length L is cut into the same number of chunks as forward,
+// ceil(L / C), but shifted so that its boundaries mirror the forward ones:
+// chunk k covers positions [max(0, kC - s), min(L, (k+1)C - s)) with
+// s = (C - L mod C) mod C.  In batch mode it also writes cu = {0, T, 2T, ..}.
+__global__ __launch_bounds__(256) void k_mirror_meta(BwdGeo q, int C, int K, int32_t* meta,
+                                                     int32_t* cu_out) {
+  __shared__ int lds_waves[4];
+  int32_t* first = meta + kMetaHeader + 3 * K;
+  int base = 0;
+  for (int i0 = 0; i0 < q.nseq; i0 += blockDim.x) {
+    const int i = i0 + threadIdx.x;
+    int n = 0;
+    if (i < q.nseq) {
+      int st, L;
+      span_of(q, i, st, L);
+      n = (L + C - 1) / C;
+      if (cu_out) cu_out[i] = st;
+    }
+    int tot;
+    const int ex = block_exclusive_scan(n, lds_waves, tot);
+    if (i < q.nseq) first[i] = min(base + ex, K);
+    base = min(base + tot, K);
+  }
+  if (threadIdx.x == 0) {
+    first[q.nseq] = base;
+    meta[0] = base;
+    meta[1] = q.nseq;
+    meta[2] = C;
+    meta[3] = K;
+    if (cu_out) cu_out[q.nseq] = q.ntok;
+  }
+  __syncthreads();
+  const int Kr = base;
+  for (int j = threadIdx.x; j < K; j += blockDim.x) {
+    int32_t* e = meta + kMetaHeader + 3 * j;
+    if (j >= Kr) {
+      e[0] = -1; e[1] = 0; e[2] = 0;
+      continue;
+    }
+    int lo = 0, hi = q.nseq - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (first[mid] <= j) lo = mid; else hi = mid - 1;
+    }
+    const int k = j - first[lo];
+    int st, L;
+    span_of(q, lo, st, L);
+    const int sh = (C - L % C) % C;
+    const int a = max(0, k * C - sh), b = min(L, (k + 1) * C - sh);
+    e[0] = lo;
+    e[1] = st + a;
+    e[2] = b - a;
+  }
+}
+
+// ---- one workgroup per (forward chunk j, head h): the step-size gradients of
+// the chunk's tokens (see the header) and the chunk's shares of dA, ddt_bias
+// and dD; at a sequence's first chunk also dh0 = exp(a_first) G_first.
+//   fwd_st:  forward scan's carry-in states, by forward chunk
+//   mir_st:  mirrored dx scan's carry-in states, by mirrored chunk
+//   gfirst:  mirrored dx scan's final states (G at each sequence's first token)
+__global__ __launch_bounds__(256) void k_step_anchor(BwdGeo q, Geo gf, const float* w,
+                                                     const float* dyx, const float* delta,
+                                                     const float* gd, const float* A,
+                                                     const float* fwd_st, const float* mir_st,
+                                                     const float* gfirst, TArg ddt,
+                                                     double* part, float* dh0) {
+  __shared__ double lds[4];
+  __shared__ double sw[256];
+  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  Chunk c;
+  const bool live = get_chunk(gf, j, c);
+  double* pj = part + ((int64_t)j * q.H + h) * 3;
+  if (!live) {
+    if (tid == 0) pj[0] = pj[1] = pj[2] = 0.0;
+    return;
+  }
+  int fi, li;
+  seq_chunks(gf, c.seq, fi, li);
+  const int jl = j - fi;
+  const int64_t PN = (int64_t)q.P * q.N;
+  const float* Gf = jl == 0 ? gfirst + ((int64_t)c.seq * q.H + h) * PN
+                            : mir_st + ((int64_t)(fi + (li - fi) - jl) * q.H + h) * PN;
+  const float* Hin = fwd_st + ((int64_t)j * q.H + h) * PN;
+  double part_ip = 0.0;
+  for (int64_t k = tid; k < PN; k += 256) part_ip += (double)Gf[k] * Hin[k];
+  const double ip = block_sum(part_ip, lds);
+  const float Ah = A[h];
+  const int tp0 = c.b * q.T + c.t0;  // the chunk's first token on the packed axis
+  const int64_t i0 = (int64_t)tp0 * q.H + h;
+  const double da0 = ip * exp((double)delta[i0] * Ah);
+  // exclusive prefix of w over the chunk's tokens (one token per thread)
+  const bool tok = tid < c.len;
+  const int64_t it = (int64_t)(tp0 + tid) * q.H + h;
+  const double wv = tok ? (double)w[it] : 0.0;
+  sw[tid] = wv;
+  __syncthreads();
+  double pre = 0.0;
+  for (int k = 0; k < tid; ++k) pre += sw[k];
+  double sa = 0.0, sb = 0.0, sx = 0.0;
+  if (tok) {
+    const double da = da0 - pre;
+    const double g = da * Ah * gd[it];
+    tok_row_f32(ddt, q, tp0 + tid, h)[0] = (float)g;
+    sa = da * delta[it];
+    sb = g;
+    sx = dyx[it];
+  }
+  sa = block_sum(sa, lds);
+  sb = block_sum(sb, lds);
+  sx = block_sum(sx, lds);
   if (tid == 0) {
-    dA[h] = (float)accA;
-    ddt_bias[h] = (float)accB;
-    if (dD) dD[h] = (float)accD;
+    pj[0] = sa;
+    pj[1] = sb;
+    pj[2] = sx;
+  }
+  if (jl == 0 && dh0) {
+    const float e = __expf(delta[i0] * Ah);
+    float* dst = dh0 + ((int64_t)c.seq * q.H + h) * PN;
+    for (int64_t k = tid; k < PN; k += 256) dst[k] = e * Gf[k];
+  }
+}
+
+// ---- per head: dA, ddt_bias, dD from the chunks' shares (in chunk order),
+// and dh0 = G_first for sequences without tokens
+__global__ __launch_bounds__(256) void k_step_heads(BwdGeo q, int K, const double* part,
+                                                    const float* gfirst, float* dA,
+                                                    float* ddt_bias, float* dD, float* dh0) {
+  const int h = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0) {
+    double a = 0.0, b = 0.0, x = 0.0;
+    for (int j = 0; j < K; ++j) {
+      const double* pj = part + ((int64_t)j * q.H + h) * 3;
+      a += pj[0];
+      b += pj[1];
+      x += pj[2];
+    }
+    dA[h] = (float)a;
+    ddt_bias[h] = (float)b;
+    if (dD) dD[h] = (float)x;
+  }
+  if (!dh0) return;
+  const int64_t PN = (int64_t)q.P * q.N;
+  for (int i = 0; i < q.nseq; ++i) {
+    int s0, L;
+    span_of(q, i, s0, L);
+    if (L > 0) continue;
+    const int64_t o = ((int64_t)i * q.H + h) * PN;
+    for (int64_t k = tid; k < PN; k += 256) dh0[o + k] = gfirst[o + k];
   }
 }
 
@@ -408,13 +507,25 @@ hipError_t launch_bwd_group_sums(const BwdGeo& q, const float* gb_rev, const flo
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_steps_grad(const BwdGeo& q, const float* w, const float* dyx,
-                                 const float* delta, const float* gd, const float* A,
-                                 const float* dfinal, const float* sfinal, const float* gfirst,
-                                 TArg ddt, float* dA, float* ddt_bias, float* dD, float* dh0,
+hipError_t launch_bwd_mirror_meta(const BwdGeo& q, int C, int K, int32_t* meta, int32_t* cu_out,
                                  hipStream_t s) {
-  hipLaunchKernelGGL(k_steps_grad, dim3(q.H), dim3(256), 0, s, q, w, dyx, delta, gd, A, dfinal,
-                     sfinal, gfirst, ddt, dA, ddt_bias, dD, dh0);
+  hipLaunchKernelGGL(k_mirror_meta, dim3(1), dim3(256), 0, s, q, C, K, meta, cu_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* w,
+                                 const float* dyx, const float* delta, const float* gd,
+                                 const float* A, const float* fwd_st, const float* mir_st,
+                                 const float* gfirst, TArg ddt, double* part, float* dA,
+                                 float* ddt_bias, float* dD, float* dh0, hipStream_t s) {
+  if (gf.K > 0) {
+    hipLaunchKernelGGL(k_step_anchor, dim3(gf.K, q.H), dim3(256), 0, s, q, gf, w, dyx, delta, gd,
+                       A, fwd_st, mir_st, gfirst, ddt, part, dh0);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_step_heads, dim3(q.H), dim3(256), 0, s, q, gf.K, part, gfirst, dA,
+                     ddt_bias, dD, dh0);
   return hipGetLastError();
 }
 

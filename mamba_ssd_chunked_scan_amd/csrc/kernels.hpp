@@ -86,10 +86,15 @@ hipError_t launch_bwd_tokens(const BwdGeo& q, TArg x, int x_dtype, const float* 
                              float* w, float* dyx, hipStream_t s);
 hipError_t launch_bwd_group_sums(const BwdGeo& q, const float* gb_rev, const float* gc, TArg dB,
                                  TArg dC, hipStream_t s);
-hipError_t launch_bwd_steps_grad(const BwdGeo& q, const float* w, const float* dyx,
-                                 const float* delta, const float* gd, const float* A,
-                                 const float* dfinal, const float* sfinal, const float* gfirst,
-                                 TArg ddt, float* dA, float* ddt_bias, float* dD, float* dh0,
+// the mirrored scans' chunk table (and, in batch mode, cu = {0, T, 2T, ..})
+hipError_t launch_bwd_mirror_meta(const BwdGeo& q, int C, int K, int32_t* meta, int32_t* cu_out,
                                  hipStream_t s);
+// step-size gradients anchored at the forward chunks (gf: the forward chunk
+// geometry); part: 3 doubles per (chunk, head)
+hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* w,
+                                 const float* dyx, const float* delta, const float* gd,
+                                 const float* A, const float* fwd_st, const float* mir_st,
+                                 const float* gfirst, TArg ddt, double* part, float* dA,
+                                 float* ddt_bias, float* dD, float* dh0, hipStream_t s);
 
 }  // namespace ssd
