@@ -40,24 +40,43 @@ __device__ __forceinline__ void bmm_wave(const Geo& g, const TArg& Cm, const TAr
     for (int b = 0; b < 4; ++b) acc[b] = zero4();
     for (int n0 = 0; n0 < N; n0 += 128) {
       Ex a[4], bf[4][4];
+      if (N - n0 >= 128) {
+        // a full 128-wide block: four k-blocks
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int k = n0 + kk * 32 + q * 8;
-        a[kk] = Pr::load_exact(crow + min(k, N - 8));
+        for (int kk = 0; kk < 4; ++kk) {
+          const int k = n0 + kk * 32 + q * 8;
+          a[kk] = Pr::load_exact(crow + k);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int srow = min((st0 + b) * 16 + r16, c.len - 1);
-          bf[b][kk] = Pr::load_exact(row_ptr<T>(Bm, c.b, c.t0 + srow, grp) + min(k, N - 8));
+          for (int b = 0; b < 4; ++b) {
+            const int srow = min((st0 + b) * 16 + r16, c.len - 1);
+            bf[b][kk] = Pr::load_exact(row_ptr<T>(Bm, c.b, c.t0 + srow, grp) + k);
+          }
         }
-      }
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int k = n0 + kk * 32 + q * 8;
-        const Ex av = (lok && k < N) ? a[kk] : Pr::zero_exact();
+        for (int kk = 0; kk < 4; ++kk) {
+          const Ex av = lok ? a[kk] : Pr::zero_exact();
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const bool sok = (st0 + b) * 16 + r16 < c.len && k < N;
-          mma(acc[b], av, sok ? bf[b][kk] : Pr::zero_exact());
+          for (int b = 0; b < 4; ++b) {
+            const bool sok = (st0 + b) * 16 + r16 < c.len;
+            mma(acc[b], av, sok ? bf[b][kk] : Pr::zero_exact());
+          }
+        }
+      } else {
+        // the tail of N (a multiple of 16 below 128): only its k-blocks, a
+        // uniform trip count, so no matrix instruction sits under a
+        // data-dependent branch
+        const int nk = (N - n0 + 31) / 32;
+        for (int kk = 0; kk < nk; ++kk) {
+          const int k = n0 + kk * 32 + q * 8;
+          const Ex av0 = Pr::load_exact(crow + min(k, N - 8));
+          const Ex av = (lok && k < N) ? av0 : Pr::zero_exact();
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int srow = min((st0 + b) * 16 + r16, c.len - 1);
+            const Ex bv = Pr::load_exact(row_ptr<T>(Bm, c.b, c.t0 + srow, grp) + min(k, N - 8));
+            const bool sok = (st0 + b) * 16 + r16 < c.len && k < N;
+            mma(acc[b], av, sok ? bv : Pr::zero_exact());
+          }
         }
       }
     }
