@@ -273,7 +273,8 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
 // The staged forward: a6 (packed mode, unless `meta_in` gives a prebuilt
 // chunk table), a1-a5 in sequence.  Arguments were validated by the caller.
 ssd_status staged_run(const ssd_problem* p, const ssd_fwd_args* a, const int32_t* meta_in,
-                      void* workspace, size_t ws_bytes, hipStream_t stream) {
+                      void* workspace, size_t ws_bytes, hipStream_t stream,
+                      float* yoff = nullptr) {
   const StagedWs w = staged_layout(p);
   if (w.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < w.total)
@@ -301,7 +302,7 @@ ssd_status staged_run(const ssd_problem* p, const ssd_fwd_args* a, const int32_t
                                     stream),
           "state_passing launch");
   SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, st, sd, a->D, targ(a->z),
-                                 targ(a->out), dcode(a->out.dtype), stream),
+                                 targ(a->out), dcode(a->out.dtype), stream, yoff),
           "chunk_scan launch");
   return ok();
 }
@@ -348,7 +349,7 @@ BwdProblems bwd_problems(const ssd_problem* p) {
 }
 
 struct BwdWs {
-  size_t yf, dy, dyr, Cr, Br, Cf, Bf, Cer, Be, xr, xf, delta, gd, dtr, w, dyx, gx, gb, gc, gfirst,
+  size_t yf, yo, dy, dyr, Cr, Br, Cf, Bf, Cer, Be, xr, xf, delta, gd, dtr, dyx, gx, gb, gc, gfirst,
       dfT, h0T, mmeta, mcu, part, run_fwd, run_dx, run_rest, fwd_bytes, dx_bytes, rest_bytes, total;
 };
 
@@ -366,6 +367,7 @@ BwdWs bwd_layout(const ssd_problem* p) {
     return o;
   };
   w.yf = take(nt * H * P);
+  w.yo = take(nt * H * P);
   w.dy = take(nt * H * P);
   w.dyr = take(nt * H * P);
   w.Cr = take(nt * G * N);
@@ -379,7 +381,6 @@ BwdWs bwd_layout(const ssd_problem* p) {
   w.delta = take(nt * H);
   w.gd = take(nt * H);
   w.dtr = take(nt * H);
-  w.w = take(nt * H);
   w.dyx = take(nt * H);
   w.gx = take(nt * H * P);
   w.gb = take(nt * H * N);
@@ -396,8 +397,9 @@ BwdWs bwd_layout(const ssd_problem* p) {
   off += align256((ns + 1) * sizeof(int32_t));
   w.part = off;
   off += align256((size_t)num_chunks(p) * H * 3 * sizeof(double));
-  // the forward recompute and the mirrored dx scan keep their chunk states
-  // (the step-size anchors); the other two scans share one workspace
+  // the forward recompute and the mirrored dx scan keep their workspaces (the
+  // step-size gradients read their chunk states and the forward's C.B^T); the
+  // dB and dC scans share one, dC last (its C.B^T, dy.x^T, is read too)
   w.fwd_bytes = staged_layout(&q.fwd).total;
   w.dx_bytes = staged_layout(&mdx).total;
   w.rest_bytes = std::max(staged_layout(&mdB).total, staged_layout(&q.dC).total);
@@ -689,9 +691,9 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
     SSD_HIP(ssd::launch_bwd_gather(bg, targ(c.src), in, c.R, c.W, c.rep, c.rev, f(c.dst), stream),
             "backward gather launch");
 
-  // 2. forward recompute in fp32 (the step-size gradients difference sums of
-  // y-dependent terms, so y is needed to fp32 accuracy): y before the gate,
-  // and the carry-in state of every chunk, kept in its workspace
+  // 2. forward recompute in fp32: y before the gate (for dz), its inter-chunk
+  // part exp(cs_l) C_l . h_in (for the step sizes), and the carry-in state of
+  // every chunk, kept in its workspace
   ssd_fwd_args fa;
   fa.x = scratch_view(f(w.xf), p, H, P);
   fa.B = scratch_view(f(w.Bf), p, G, N);
@@ -701,7 +703,7 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   fa.initial_states = a->initial_states;
   fa.out = scratch_view(f(w.yf), p, H, P);
   fa.final_states = nullptr;
-  SSD_TRY(staged_run(&q.fwd, &fa, nullptr, ws_fwd, w.fwd_bytes, stream));
+  SSD_TRY(staged_run(&q.fwd, &fa, nullptr, ws_fwd, w.fwd_bytes, stream, f(w.yo)));
 
   // 3. gate, steps, transposed states, the mirrored chunk table
   SSD_HIP(ssd::launch_bwd_gate(bg, targ(a->dout), dcode(a->dout.dtype), targ(a->z), in, f(w.yf),
@@ -743,7 +745,8 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   ra.initial_states = a->dfinal_states;
   ra.out = scratch_view(f(w.gx), &mdx, H, P);
   ra.final_states = f(w.gfirst);
-  SSD_TRY(staged_run(&mdx, &ra, mmeta, ws_dx, w.dx_bytes, stream));
+  // (its inter-chunk part goes to yf, free since the gate)
+  SSD_TRY(staged_run(&mdx, &ra, mmeta, ws_dx, w.dx_bytes, stream, f(w.yf)));
   ra.x = scratch_view(f(w.Cer), &mdB, H, N);
   ra.B = scratch_view(f(w.dyr), &mdB, H, P);
   ra.C = scratch_view(f(w.xr), &mdB, H, P);
@@ -761,20 +764,22 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   SSD_TRY(staged_run(&q.dC, &ra, nullptr, ws_rest, w.rest_bytes, stream));
 
   // 5. gradients
-  SSD_HIP(ssd::launch_bwd_tokens(bg, targ(a->x), in, a->D, f(w.dy), f(w.yf), f(w.gx),
-                                 targ(a->dx), f(w.w), f(w.dyx), stream),
+  SSD_HIP(ssd::launch_bwd_tokens(bg, targ(a->x), in, a->D, f(w.dy), f(w.gx), targ(a->dx),
+                                 f(w.dyx), stream),
           "backward tokens launch");
   SSD_HIP(ssd::launch_bwd_group_sums(bg, f(w.gb), f(w.gc), targ(a->dB), targ(a->dC), stream),
           "backward group sums launch");
-  const StagedWs lf = staged_layout(&q.fwd), lx = staged_layout(&mdx);
+  const StagedWs lf = staged_layout(&q.fwd), lx = staged_layout(&mdx), lc = staged_layout(&q.dC);
   const int32_t* fwd_meta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws_fwd + lf.meta) : nullptr;
   const ssd::Geo gf = make_geo(&q.fwd, fwd_meta);
-  SSD_HIP(ssd::launch_bwd_step_grads(bg, gf, f(w.w), f(w.dyx), f(w.delta), f(w.gd), a->A,
-                                     reinterpret_cast<float*>(ws_fwd + lf.st),
-                                     reinterpret_cast<float*>(ws_dx + lx.st), f(w.gfirst),
-                                     targ(a->ddt), reinterpret_cast<double*>(ws + w.part), a->dA,
-                                     a->ddt_bias, a->D ? a->dD : nullptr, a->dinitial_states,
-                                     stream),
+  // (the dC scan's C.B^T is dy . x^T per head, and it ran last in ws_rest)
+  SSD_HIP(ssd::launch_bwd_step_grads(
+              bg, gf, reinterpret_cast<float*>(ws_fwd + lf.cb),
+              reinterpret_cast<float*>(ws_rest + lc.cb), f(w.yo), f(w.yf), f(w.xf), f(w.dy),
+              f(w.dyx), f(w.delta), f(w.gd), a->A,
+              reinterpret_cast<float*>(ws_fwd + lf.st), reinterpret_cast<float*>(ws_dx + lx.st),
+              f(w.gfirst), a->dfinal_states, targ(a->ddt), reinterpret_cast<double*>(ws + w.part),
+              a->dA, a->ddt_bias, a->D ? a->dD : nullptr, a->dinitial_states, stream),
           "backward step gradients launch");
   return ok();
 }

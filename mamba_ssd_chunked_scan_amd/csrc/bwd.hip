@@ -13,19 +13,16 @@
 //   one token (the decay between t and t+1 belongs to token t+1) and the final
 //   state's gradient as the initial state.
 //
-//   For the step sizes, dL/da_t = exp(a_t) <G_t, S_{t-1}>.  At the first
-//   token f of every chunk both states are at hand: S_{f-1} is the forward
-//   scan's carry-in, and G_f the mirrored dx scan's carry-in, because that
-//   scan cuts each mirrored sequence so that its chunk boundaries fall on the
-//   forward ones (a short first chunk of L mod C tokens).  Inside the chunk,
-//   with u_t = dy_t . (y_t - D x_t) and v_t = x_t . (dx_t - D dy_t) (y before
-//   the gate), <G_t, S_t> = <G_{t+1}, S_{t+1}> - v_{t+1} + u_t telescopes to
-//     dL/da_t = dL/da_{t-1} + v_{t-1} - u_{t-1},
-//   so each step-size gradient is an exact inner product at the chunk start
-//   plus a sum of at most C - 1 terms (the terms largely cancel, so the sums
-//   are kept short and in fp64).
+//   For the step sizes, dL/da_t is the sum over the chunk's later tokens of
+//   dL/dcs (see k_step_dcs): row and column sums of the strictly lower
+//   triangle of M = exp(segsum) o (C.B^T) o (dy.x^T), plus the terms of the
+//   states entering and leaving the chunk.  The state leaving a chunk gets its
+//   gradient from the mirrored dx scan's carry-in states, because that scan
+//   cuts each mirrored sequence so that its chunk boundaries fall on the
+//   forward ones (a short first chunk of L mod C tokens).
 //
-// Everything here is fp32 and deterministic: every sum has a fixed order.
+// Products are fp32; sums that accumulate many terms are fp64.  Every sum has a
+// fixed order, so the results are deterministic.
 #include "kernels.hpp"
 #include "stage_varlen.hpp"
 
@@ -203,16 +200,15 @@ __global__ __launch_bounds__(256) void k_transpose_states(int nsh, int P, int N,
   }
 }
 
-// ---- per (token, head) row: dx = mirrored dx-scan output + D dy, w = u - v
-// (see the header) and dy . x for dD; the row's partial sums meet in LDS and
-// its first thread adds them in order
+// ---- per (token, head) row: dx = mirrored dx-scan output + D dy, and dy . x
+// for dD; the row's partial sums meet in LDS and its first thread adds them in
+// order
 __global__ __launch_bounds__(256) void k_tokens(BwdGeo q, TArg x, int x_dtype, const float* D,
-                                                const float* dy, const float* y,
-                                                const float* gx_rev, TArg dx, float* w,
+                                                const float* dy, const float* gx_rev, TArg dx,
                                                 float* dyx) {
-  __shared__ double part[3][256];
+  __shared__ double part[256];
   const Row rw = row_of(q.P, q.ntok * q.H);
-  double su = 0.0, sv = 0.0, sx = 0.0;
+  double sx = 0.0;
   if (rw.ok) {
     const int tp = rw.row / q.H, h = rw.row % q.H;
     const int64_t o = (int64_t)rw.row * q.P + rw.c;
@@ -220,30 +216,19 @@ __global__ __launch_bounds__(256) void k_tokens(BwdGeo q, TArg x, int x_dtype, c
     const f32x4 xv = load4(x, x_dtype, q, tp, h, rw.c);
     const f32x4 g = *reinterpret_cast<const f32x4*>(gx_rev + ((int64_t)mirror(q, tp) * q.H + h) * q.P + rw.c);
     const f32x4 d = *reinterpret_cast<const f32x4*>(dy + o);
-    const f32x4 yy = *reinterpret_cast<const f32x4*>(y + o);
     f32x4 out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       out[i] = g[i] + Dh * d[i];
-      // u and v nearly cancel in the telescoped sums: both in fp64
-      su += (double)d[i] * ((double)yy[i] - (double)Dh * xv[i]);
-      sv += (double)xv[i] * g[i];
       sx += (double)d[i] * xv[i];
     }
     *reinterpret_cast<f32x4*>(tok_row_f32(dx, q, tp, h) + rw.c) = out;
   }
-  part[0][threadIdx.x] = su;
-  part[1][threadIdx.x] = sv;
-  part[2][threadIdx.x] = sx;
+  part[threadIdx.x] = sx;
   __syncthreads();
   if (rw.ok && rw.c == 0) {
-    double a = 0.0, b = 0.0, c = 0.0;
-    for (int k = 0; k < rw.tpr; ++k) {
-      a += part[0][threadIdx.x + k];
-      b += part[1][threadIdx.x + k];
-      c += part[2][threadIdx.x + k];
-    }
-    w[rw.row] = (float)(a - b);
+    double c = 0.0;
+    for (int k = 0; k < rw.tpr; ++k) c += part[threadIdx.x + k];
     dyx[rw.row] = (float)c;
   }
 }
@@ -343,20 +328,60 @@ __global__ __launch_bounds__(256) void k_mirror_meta(BwdGeo q, int C, int K, int
 }
 
 // ---- one workgroup per (forward chunk j, head h): the step-size gradients of
-// the chunk's tokens (see the header) and the chunk's shares of dA, ddt_bias
-// and dD; at a sequence's first chunk also dh0 = exp(a_first) G_first.
+// the chunk's tokens and the chunk's shares of dA, ddt_bias and dD; at a
+// sequence's first chunk also dh0 = exp(a_first) G_first.
+//
+// dL/da_t = sum over l >= t in the chunk of dL/dcs_l, with cs the chunk's
+// inclusive cumsum of a and Lambda = cs at its last token:
+//   dL/dcs_l = sum_{s<l} M_ls - sum_{l'>l} M_l'l + Q_l - R_l  (+ at the last
+//              token: exp(Lambda) <dS, Hin> + sum_s R_s)
+//   M_ls = exp(cs_l - cs_s) (C_l . B_s) (dy_l . x_s)       (s < l: the diagonal
+//          terms of the two sums are equal and cancel, so neither holds them)
+//   Q_l  = exp(cs_l) dy_l . (Hin C_l),   R_l = exp(Lambda - cs_l) x_l . (dS B_l)
+// Hin is the state entering the chunk (forward scan's carry-in), dS the
+// gradient of the state leaving it through later tokens: exp(a_next) G_next
+// (G_next the mirrored dx scan's carry-in for the next chunk) or dfinal at a
+// sequence's last chunk.  Every term decays as it should, so nothing cancels
+// however strong the decay.  The vectors in Q and R are the inter-chunk parts
+// of the forward scan's output (Hin C_l, scaled by exp(cs_l)) and of the
+// mirrored dx scan's output at the mirrored token (dS B_l, scaled by
+// exp(Lambda - cs_l): that scan's chunk cumsum at token l), so only their dot
+// products with dy_l and x_l are left here.  cs itself is summed in fp64 from
+// the step sizes: with strong decay it reaches |cs| ~ 1e4 while the segments
+// that still matter span |cs_l - cs_s| < ~100, and an fp32 sum would leave
+// each such segment an absolute error of |cs| 2^-24.
+//   CB:      forward scan's C.B^T (K, G, C, C)
+//   DX:      dy.x^T per head (K, H, C, C), the dC scan's C.B^T
+//   yo_f:    forward scan's inter-chunk output, (tokens, H, P)
+//   yo_r:    mirrored dx scan's inter-chunk output, (tokens, H, P), mirrored
 //   fwd_st:  forward scan's carry-in states, by forward chunk
 //   mir_st:  mirrored dx scan's carry-in states, by mirrored chunk
 //   gfirst:  mirrored dx scan's final states (G at each sequence's first token)
-__global__ __launch_bounds__(256) void k_step_anchor(BwdGeo q, Geo gf, const float* w,
-                                                     const float* dyx, const float* delta,
-                                                     const float* gd, const float* A,
-                                                     const float* fwd_st, const float* mir_st,
-                                                     const float* gfirst, TArg ddt,
-                                                     double* part, float* dh0) {
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+  return v;  // (the same in every lane: each level adds the same two numbers)
+}
+
+__global__ __launch_bounds__(256) void k_step_dcs(BwdGeo q, Geo gf, const float* CB,
+                                                  const float* DX, const float* yo_f,
+                                                  const float* yo_r, const float* xf,
+                                                  const float* dy, const float* dyx,
+                                                  const float* delta, const float* gd,
+                                                  const float* A, const float* fwd_st,
+                                                  const float* mir_st, const float* gfirst,
+                                                  const float* dfinal, TArg ddt, double* part,
+                                                  float* dh0) {
   __shared__ double lds[4];
-  __shared__ double sw[256];
+  __shared__ float s_a[256];
+  __shared__ double s_cs[256];
+  __shared__ double s_col[4][256];  // per-wave column sums of M
+  __shared__ double s_row[256];     // row sums of M
+  __shared__ double s_qr[2][256];   // per-thread partial dot products: Q, R
+  __shared__ double s_r[256];       // R per row (for the Lambda term)
+  __shared__ double s_dcs[256];
   const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int wave = tid / kWave, lane = tid % kWave;
   Chunk c;
   const bool live = get_chunk(gf, j, c);
   double* pj = part + ((int64_t)j * q.H + h) * 3;
@@ -366,45 +391,125 @@ __global__ __launch_bounds__(256) void k_step_anchor(BwdGeo q, Geo gf, const flo
   }
   int fi, li;
   seq_chunks(gf, c.seq, fi, li);
-  const int jl = j - fi;
+  const int jl = j - fi, len = c.len, C = gf.C, g = h / q.hpg;
   const int64_t PN = (int64_t)q.P * q.N;
-  const float* Gf = jl == 0 ? gfirst + ((int64_t)c.seq * q.H + h) * PN
-                            : mir_st + ((int64_t)(fi + (li - fi) - jl) * q.H + h) * PN;
-  const float* Hin = fwd_st + ((int64_t)j * q.H + h) * PN;
-  double part_ip = 0.0;
-  for (int64_t k = tid; k < PN; k += 256) part_ip += (double)Gf[k] * Hin[k];
-  const double ip = block_sum(part_ip, lds);
   const float Ah = A[h];
   const int tp0 = c.b * q.T + c.t0;  // the chunk's first token on the packed axis
-  const int64_t i0 = (int64_t)tp0 * q.H + h;
-  const double da0 = ip * exp((double)delta[i0] * Ah);
-  // exclusive prefix of w over the chunk's tokens (one token per thread)
-  const bool tok = tid < c.len;
-  const int64_t it = (int64_t)(tp0 + tid) * q.H + h;
-  const double wv = tok ? (double)w[it] : 0.0;
-  sw[tid] = wv;
+  int s0, s1;
+  seq_of(q, tp0, s0, s1);
+  if (tid < len) s_a[tid] = delta[(int64_t)(tp0 + tid) * q.H + h] * Ah;
   __syncthreads();
-  double pre = 0.0;
-  for (int k = 0; k < tid; ++k) pre += sw[k];
-  double sa = 0.0, sb = 0.0, sx = 0.0;
-  if (tok) {
-    const double da = da0 - pre;
-    const double g = da * Ah * gd[it];
-    tok_row_f32(ddt, q, tp0 + tid, h)[0] = (float)g;
+  if (tid < len) {
+    double acc = 0.0;
+    for (int k = 0; k <= tid; ++k) acc += (double)s_a[k];
+    s_cs[tid] = acc;
+  }
+  __syncthreads();
+  const double lam = s_cs[len - 1];
+
+  // the states at the chunk's two ends (for the Lambda term)
+  const float* Hin = fwd_st + ((int64_t)j * q.H + h) * PN;
+  const bool last = j == li - 1;
+  const float* dS = nullptr;
+  float dscale = 1.0f;
+  if (!last) {
+    dS = mir_st + ((int64_t)(li - (jl + 1)) * q.H + h) * PN;
+    dscale = __expf(delta[(int64_t)(tp0 + len) * q.H + h] * Ah);
+  } else if (dfinal) {
+    dS = dfinal + ((int64_t)c.seq * q.H + h) * PN;
+  }
+
+  // row and column sums of M: wave w takes rows l = w, w + 4, ..; lane k the
+  // columns k, k + 64, ..  (coalesced rows of CB and DX); every M_ls is
+  // formed once and added to both sums, in fp64
+  {
+    const float* cbm = CB + ((int64_t)j * q.G + g) * C * C;
+    const float* dxm = DX + ((int64_t)j * q.H + h) * C * C;
+    double col[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int l = wave; l < len; l += 4) {
+      const double csl = s_cs[l];
+      double rp = 0.0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int sc = lane + kWave * i;
+        if (sc < l) {
+          const float m = __expf((float)(csl - s_cs[sc])) * cbm[l * C + sc] * dxm[l * C + sc];
+          rp += (double)m;
+          col[i] += (double)m;
+        }
+      }
+      rp = wave_sum_f64(rp);
+      if (lane == 0) s_row[l] = rp;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + kWave * i < C) s_col[wave][lane + kWave * i] = col[i];
+  }
+
+  // Q and R: tpr threads per row, each over an interleaved share of p
+  const int tpr = 256 / C, l = tid / tpr, part_k = tid % tpr;
+  double qs = 0.0, rs = 0.0;
+  if (l < len) {
+    const int64_t rf = ((int64_t)(tp0 + l) * q.H + h) * q.P;
+    const int64_t rr = ((int64_t)(s0 + s1 - 1 - (tp0 + l)) * q.H + h) * q.P;
+    for (int p = part_k * 4; p < q.P; p += tpr * 4) {
+      const f32x4 d = *reinterpret_cast<const f32x4*>(dy + rf + p);
+      const f32x4 yf = *reinterpret_cast<const f32x4*>(yo_f + rf + p);
+      const f32x4 xv = *reinterpret_cast<const f32x4*>(xf + rf + p);
+      const f32x4 yr = *reinterpret_cast<const f32x4*>(yo_r + rr + p);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qs += (double)(d[i] * yf[i]);
+        rs += (double)(xv[i] * yr[i]);
+      }
+    }
+  }
+  s_qr[0][tid] = qs;
+  s_qr[1][tid] = rs;
+  // <dS, Hin> for the last token's Lambda term
+  double ip = 0.0;
+  if (dS)
+    for (int64_t k = tid; k < PN; k += 256) ip += (double)dS[k] * Hin[k];
+  ip = block_sum(ip, lds);  // (its barrier publishes s_row, s_col and s_qr)
+  if (tid < len) {
+    double qq = 0.0, r = 0.0;
+    for (int k = 0; k < tpr; ++k) {
+      qq += s_qr[0][tid * tpr + k];
+      r += s_qr[1][tid * tpr + k];
+    }
+    const double b = s_col[0][tid] + s_col[1][tid] + s_col[2][tid] + s_col[3][tid];
+    s_dcs[tid] = s_row[tid] - b + qq - r;
+    s_r[tid] = r;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double sr = 0.0;
+    for (int k = 0; k < len; ++k) sr += s_r[k];
+    s_dcs[len - 1] += (double)dscale * __expf((float)lam) * ip + sr;
+  }
+  __syncthreads();
+  double sa = 0.0, sb2 = 0.0, sx = 0.0;
+  if (tid < len) {
+    double da = 0.0;
+    for (int k = len - 1; k >= tid; --k) da += s_dcs[k];
+    const int64_t it = (int64_t)(tp0 + tid) * q.H + h;
+    const double gg = da * Ah * gd[it];
+    tok_row_f32(ddt, q, tp0 + tid, h)[0] = (float)gg;
     sa = da * delta[it];
-    sb = g;
+    sb2 = gg;
     sx = dyx[it];
   }
   sa = block_sum(sa, lds);
-  sb = block_sum(sb, lds);
+  sb2 = block_sum(sb2, lds);
   sx = block_sum(sx, lds);
   if (tid == 0) {
     pj[0] = sa;
-    pj[1] = sb;
+    pj[1] = sb2;
     pj[2] = sx;
   }
   if (jl == 0 && dh0) {
-    const float e = __expf(delta[i0] * Ah);
+    const float* Gf = gfirst + ((int64_t)c.seq * q.H + h) * PN;
+    const float e = __expf(delta[(int64_t)tp0 * q.H + h] * Ah);
     float* dst = dh0 + ((int64_t)c.seq * q.H + h) * PN;
     for (int64_t k = tid; k < PN; k += 256) dst[k] = e * Gf[k];
   }
@@ -489,12 +594,11 @@ hipError_t launch_bwd_transpose_states(int nsh, int P, int N, const float* src, 
 }
 
 hipError_t launch_bwd_tokens(const BwdGeo& q, TArg x, int x_dtype, const float* D,
-                             const float* dy, const float* y, const float* gx_rev, TArg dx,
-                             float* w, float* dyx, hipStream_t s) {
+                             const float* dy, const float* gx_rev, TArg dx, float* dyx, hipStream_t s) {
   const int rows = q.ntok * q.H;
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(k_tokens, dim3(row_blocks(rows, q.P)), dim3(256), 0, s, q, x, x_dtype, D,
-                     dy, y, gx_rev, dx, w, dyx);
+                     dy, gx_rev, dx, dyx);
   return hipGetLastError();
 }
 
@@ -513,14 +617,17 @@ hipError_t launch_bwd_mirror_meta(const BwdGeo& q, int C, int K, int32_t* meta, 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* w,
+hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* CB,
+                                 const float* DX, const float* yo_f, const float* yo_r,
+                                 const float* xf, const float* dy,
                                  const float* dyx, const float* delta, const float* gd,
                                  const float* A, const float* fwd_st, const float* mir_st,
-                                 const float* gfirst, TArg ddt, double* part, float* dA,
-                                 float* ddt_bias, float* dD, float* dh0, hipStream_t s) {
+                                 const float* gfirst, const float* dfinal, TArg ddt,
+                                 double* part, float* dA, float* ddt_bias, float* dD, float* dh0,
+                                 hipStream_t s) {
   if (gf.K > 0) {
-    hipLaunchKernelGGL(k_step_anchor, dim3(gf.K, q.H), dim3(256), 0, s, q, gf, w, dyx, delta, gd,
-                       A, fwd_st, mir_st, gfirst, ddt, part, dh0);
+    hipLaunchKernelGGL(k_step_dcs, dim3(gf.K, q.H), dim3(256), 0, s, q, gf, CB, DX, yo_f, yo_r,
+                       xf, dy, dyx, delta, gd, A, fwd_st, mir_st, gfirst, dfinal, ddt, part, dh0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -11,7 +11,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
                                                     TArg Cm, const float* __restrict__ cs,
                                                     const ST* __restrict__ states,
                                                     const float* __restrict__ D, TArg z,
-                                                    TArg out) {
+                                                    TArg out, float* __restrict__ yoff) {
   using Pr = Prec<T>;
   using HL = HinLds<T, ST>;
   extern __shared__ __align__(16) char smem[];
@@ -89,6 +89,18 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
       const float e = fast_exp(s_cs[lt * 16 + q * 4 + i]);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[u][pt][i] *= e;
+    }
+    // optionally keep Y_off on its own, (tokens, H, P) fp32 on the packed axis
+    if (yoff) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int l = lt * 16 + q * 4 + i;
+        if (l >= c.len) continue;
+        float* yr = yoff + ((int64_t)(c.b * g.T + c.t0 + l) * g.H + h) * P + p0;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          if (pt < npt) yr[pt * 16 + r16] = acc[u][pt][i];
+      }
     }
     // Y_diag = (L o CB) x over s <= l
     const float csl = s_cs[min(lrow, C - 1)];
@@ -198,7 +210,7 @@ static hipError_t launch_scan_bf16(const Geo& g, const float* CB, TArg x, TArg C
 template <typename T, typename ST, typename TO>
 static hipError_t launch_scan_t(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
                                 const void* states, const float* D, TArg z, TArg out,
-                                hipStream_t s) {
+                                float* yoff, hipStream_t s) {
   const ScanLayout lay = scan_layout<T, ST>(g.C, g.N);
   auto kern = k_chunk_scan_generic<T, ST, TO>;
   if (lay.bytes > 64 * 1024) {
@@ -208,25 +220,27 @@ static hipError_t launch_scan_t(const Geo& g, const float* CB, TArg x, TArg C, c
   }
   dim3 grid(g.K, g.H, (g.P + 63) / 64);
   hipLaunchKernelGGL(kern, grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, (const ST*)states, D,
-                     z, out);
+                     z, out, yoff);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
                              const float* cs, const void* states, int st_dtype,
-                             const float* D, TArg z, TArg out, int out_dtype, hipStream_t s) {
+                             const float* D, TArg z, TArg out, int out_dtype, hipStream_t s,
+                             float* yoff) {
   if (g.K == 0) return hipSuccess;
   const bool ib = in_dtype == DT_BF16, sb = st_dtype == DT_BF16, ob = out_dtype == DT_BF16;
   if (ib) {
+    if (yoff) return hipErrorInvalidValue;  // only the fp32 kernel keeps Y_off
     if (sb) return ob ? launch_scan_bf16<bf16, bf16>(g, CB, x, C, cs, states, D, z, out, s)
                       : launch_scan_bf16<bf16, float>(g, CB, x, C, cs, states, D, z, out, s);
     return ob ? launch_scan_bf16<float, bf16>(g, CB, x, C, cs, states, D, z, out, s)
               : launch_scan_bf16<float, float>(g, CB, x, C, cs, states, D, z, out, s);
   }
-  if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, states, D, z, out, s)
-                    : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, states, D, z, out, s);
-  return ob ? launch_scan_t<float, float, bf16>(g, CB, x, C, cs, states, D, z, out, s)
-            : launch_scan_t<float, float, float>(g, CB, x, C, cs, states, D, z, out, s);
+  if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, states, D, z, out, yoff, s)
+                    : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, states, D, z, out, yoff, s);
+  return ob ? launch_scan_t<float, float, bf16>(g, CB, x, C, cs, states, D, z, out, yoff, s)
+            : launch_scan_t<float, float, float>(g, CB, x, C, cs, states, D, z, out, yoff, s);
 }
 
 }  // namespace ssd

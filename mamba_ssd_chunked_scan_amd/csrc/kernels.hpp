@@ -29,9 +29,13 @@ hipError_t launch_state_passing(const Geo& g, const void* states, int st_dtype,
                                 const float* cs, const float* h0, void* states_out,
                                 float* hfinal, hipStream_t s);
 
+// yoff (fp32 inputs only; NULL to skip): also writes the inter-chunk part of
+// the output, exp(cs_l) C_l . h_in, before the skip and the gate, as (tokens,
+// H, P) fp32 on the packed axis
 hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
                              const float* cs, const void* states, int st_dtype,
-                             const float* D, TArg z, TArg out, int out_dtype, hipStream_t s);
+                             const float* D, TArg z, TArg out, int out_dtype, hipStream_t s,
+                             float* yoff = nullptr);
 
 // ---- fused forward (fused_fwd.hip)
 constexpr int kFusedChunk = 128;             // internal chunk length of the fused pass
@@ -82,19 +86,21 @@ hipError_t launch_bwd_steps(const BwdGeo& q, TArg dt, int dt_dtype, const float*
 hipError_t launch_bwd_transpose_states(int nsh, int P, int N, const float* src, float* dst,
                                        hipStream_t s);
 hipError_t launch_bwd_tokens(const BwdGeo& q, TArg x, int x_dtype, const float* D,
-                             const float* dy, const float* y, const float* gx_rev, TArg dx,
-                             float* w, float* dyx, hipStream_t s);
+                             const float* dy, const float* gx_rev, TArg dx, float* dyx, hipStream_t s);
 hipError_t launch_bwd_group_sums(const BwdGeo& q, const float* gb_rev, const float* gc, TArg dB,
                                  TArg dC, hipStream_t s);
 // the mirrored scans' chunk table (and, in batch mode, cu = {0, T, 2T, ..})
 hipError_t launch_bwd_mirror_meta(const BwdGeo& q, int C, int K, int32_t* meta, int32_t* cu_out,
                                  hipStream_t s);
-// step-size gradients anchored at the forward chunks (gf: the forward chunk
-// geometry); part: 3 doubles per (chunk, head)
-hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* w,
+// step-size gradients per forward chunk (gf: the forward chunk geometry);
+// part: 3 doubles per (chunk, head)
+hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* CB,
+                                 const float* DX, const float* yo_f, const float* yo_r,
+                                 const float* xf, const float* dy,
                                  const float* dyx, const float* delta, const float* gd,
                                  const float* A, const float* fwd_st, const float* mir_st,
-                                 const float* gfirst, TArg ddt, double* part, float* dA,
-                                 float* ddt_bias, float* dD, float* dh0, hipStream_t s);
+                                 const float* gfirst, const float* dfinal, TArg ddt,
+                                 double* part, float* dA, float* ddt_bias, float* dD, float* dh0,
+                                 hipStream_t s);
 
 }  // namespace ssd
