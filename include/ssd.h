@@ -303,12 +303,16 @@ ssd_status ssd_backward_workspace_size(const ssd_problem* p, size_t* bytes);
  * dy_t (outer) C_t, is itself an SSD scan run backwards in time; the call
  * runs the staged forward four times on operands it prepares (the forward
  * recompute, then the adjoint read with B for dx and with x for dB, and the
- * forward state read with dy for dC), and the step-size gradient in closed
- * form: dL/d(delta_t A) = <dfinal, h_final> + sum_{l >= t} (u_l - v_l) with
- * u_l = dy_l . (y_l - D x_l) and v_l = x_l . (dx_l - D dy_l), y before the
- * gate.  Everything after the inputs is fp32 (fp32 chunk states, fp32 matrix
- * products), so gradients are accurate to fp32 whatever the input dtype.
- * Packed mode is supported (each sequence runs backwards on its own).
+ * forward state read with dy for dC).  The step-size gradient of a token is
+ * the sum, over the later tokens of its chunk, of dL/dcs_l (cs the chunk's
+ * cumulative log-decay): row minus column sums of the strictly lower triangle
+ * of exp(cs_l - cs_s) (C_l . B_s) (dy_l . x_s), plus the terms of the states
+ * entering and leaving the chunk; no two terms of it cancel, so it stays
+ * accurate under strong decay.  Everything after the inputs is fp32 (fp32
+ * chunk states, fp32 matrix products, fp64 sums where many terms meet), so
+ * gradients are accurate to fp32 whatever the input dtype.  Packed mode is
+ * supported (each sequence runs backwards on its own).  initial_states,
+ * dfinal_states and dinitial_states must be 16-byte aligned.
  * Results are bit-identical run to run (no atomics, fixed sum orders).
  * workspace: at least ssd_backward_workspace_size(p) bytes, 256-byte
  * aligned, contents need not be initialised; calls that overlap in time must

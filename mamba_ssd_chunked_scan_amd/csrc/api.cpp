@@ -650,6 +650,9 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   SSD_TRY(check_dt(a->ddt, tok));
   if (a->ddt.data && a->ddt.dtype != SSD_F32) return fail(SSD_ERR_DTYPE, "ddt must be F32");
   if (!a->dA || !a->ddt_bias) return fail(SSD_ERR_NULL, "dA or ddt_bias is NULL");
+  SSD_TRY(check_state_ptr(a->initial_states, "initial_states"));
+  SSD_TRY(check_state_ptr(a->dfinal_states, "dfinal_states"));
+  SSD_TRY(check_state_ptr(a->dinitial_states, "dinitial_states"));
   if (bwd_tokens(p) * (p->nheads > p->ngroups ? p->nheads : p->ngroups) > INT32_MAX)
     return fail(SSD_ERR_UNSUPPORTED, "backward: tokens x heads exceeds 2^31 - 1");
   const BwdWs w = bwd_layout(p);

@@ -363,6 +363,7 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   return v;  // (the same in every lane: each level adds the same two numbers)
 }
 
+template <int C>
 __global__ __launch_bounds__(256) void k_step_dcs(BwdGeo q, Geo gf, const float* CB,
                                                   const float* DX, const float* yo_f,
                                                   const float* yo_r, const float* xf,
@@ -391,7 +392,7 @@ __global__ __launch_bounds__(256) void k_step_dcs(BwdGeo q, Geo gf, const float*
   }
   int fi, li;
   seq_chunks(gf, c.seq, fi, li);
-  const int jl = j - fi, len = c.len, C = gf.C, g = h / q.hpg;
+  const int jl = j - fi, len = c.len, g = h / q.hpg;
   const int64_t PN = (int64_t)q.P * q.N;
   const float Ah = A[h];
   const int tp0 = c.b * q.T + c.t0;  // the chunk's first token on the packed axis
@@ -421,37 +422,58 @@ __global__ __launch_bounds__(256) void k_step_dcs(BwdGeo q, Geo gf, const float*
 
   // row and column sums of M: wave w takes rows l = w, w + 4, ..; lane k the
   // columns k, k + 64, ..  (coalesced rows of CB and DX); every M_ls is
-  // formed once and added to both sums, in fp64
+  // formed once and added to both sums, in fp64.  Four rows per pass, their
+  // loads issued together (clamped in bounds, masked after).
   {
+    constexpr int NI = C >= kWave ? C / kWave : 1;
     const float* cbm = CB + ((int64_t)j * q.G + g) * C * C;
     const float* dxm = DX + ((int64_t)j * q.H + h) * C * C;
-    double col[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int l = wave; l < len; l += 4) {
-      const double csl = s_cs[l];
-      double rp = 0.0;
+    double col[NI];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int sc = lane + kWave * i;
-        if (sc < l) {
-          const float m = __expf((float)(csl - s_cs[sc])) * cbm[l * C + sc] * dxm[l * C + sc];
-          rp += (double)m;
-          col[i] += (double)m;
+    for (int i = 0; i < NI; ++i) col[i] = 0.0;
+    for (int l0 = wave; l0 < len; l0 += 16) {
+      float cb[4][NI], dx[4][NI];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lr = min(l0 + 4 * r, len - 1);
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int sc = min(lane + kWave * i, C - 1);
+          cb[r][i] = cbm[lr * C + sc];
+          dx[r][i] = dxm[lr * C + sc];
         }
       }
-      rp = wave_sum_f64(rp);
-      if (lane == 0) s_row[l] = rp;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int l = l0 + 4 * r;
+        const double csl = s_cs[min(l, len - 1)];
+        double rp = 0.0;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int sc = lane + kWave * i;
+          if (sc < l && l < len) {
+            const float m = __expf((float)(csl - s_cs[sc])) * cb[r][i] * dx[r][i];
+            rp += (double)m;
+            col[i] += (double)m;
+          }
+        }
+        rp = wave_sum_f64(rp);
+        if (lane == 0 && l < len) s_row[l] = rp;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
       if (lane + kWave * i < C) s_col[wave][lane + kWave * i] = col[i];
   }
 
   // Q and R: tpr threads per row, each over an interleaved share of p
-  const int tpr = 256 / C, l = tid / tpr, part_k = tid % tpr;
+  constexpr int tpr = 256 / C;
+  const int l = tid / tpr, part_k = tid % tpr;
   double qs = 0.0, rs = 0.0;
   if (l < len) {
     const int64_t rf = ((int64_t)(tp0 + l) * q.H + h) * q.P;
     const int64_t rr = ((int64_t)(s0 + s1 - 1 - (tp0 + l)) * q.H + h) * q.P;
+#pragma unroll 2
     for (int p = part_k * 4; p < q.P; p += tpr * 4) {
       const f32x4 d = *reinterpret_cast<const f32x4*>(dy + rf + p);
       const f32x4 yf = *reinterpret_cast<const f32x4*>(yo_f + rf + p);
@@ -468,8 +490,15 @@ __global__ __launch_bounds__(256) void k_step_dcs(BwdGeo q, Geo gf, const float*
   s_qr[1][tid] = rs;
   // <dS, Hin> for the last token's Lambda term
   double ip = 0.0;
-  if (dS)
-    for (int64_t k = tid; k < PN; k += 256) ip += (double)dS[k] * Hin[k];
+  if (dS) {
+#pragma unroll 4
+    for (int64_t k = tid * 4; k < PN; k += 256 * 4) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(dS + k);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(Hin + k);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ip += (double)a[i] * b[i];
+    }
+  }
   ip = block_sum(ip, lds);  // (its barrier publishes s_row, s_col and s_qr)
   if (tid < len) {
     double qq = 0.0, r = 0.0;
@@ -626,8 +655,10 @@ hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* CB
                                  double* part, float* dA, float* ddt_bias, float* dD, float* dh0,
                                  hipStream_t s) {
   if (gf.K > 0) {
-    hipLaunchKernelGGL(k_step_dcs, dim3(gf.K, q.H), dim3(256), 0, s, q, gf, CB, DX, yo_f, yo_r,
-                       xf, dy, dyx, delta, gd, A, fwd_st, mir_st, gfirst, dfinal, ddt, part, dh0);
+    auto kern = gf.C == 32 ? k_step_dcs<32> : gf.C == 64 ? k_step_dcs<64>
+              : gf.C == 128 ? k_step_dcs<128> : k_step_dcs<256>;
+    hipLaunchKernelGGL(kern, dim3(gf.K, q.H), dim3(256), 0, s, q, gf, CB, DX, yo_f, yo_r, xf, dy,
+                       dyx, delta, gd, A, fwd_st, mir_st, gfirst, dfinal, ddt, part, dh0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
