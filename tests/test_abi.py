@@ -148,6 +148,45 @@ def test_forward_validation_workspace_and_algo():
     assert L.ssd_forward(ctypes.byref(p), 0, ctypes.byref(a), 4096, 1 << 40, None) == 1
 
 
+def test_backward_validation_before_launch():
+    # fake device addresses: every case fails on the host before any launch
+    L = ssd.lib()
+    p = prob().c()
+    tok = (8192 * 4096, 4096, 64)
+    grp = (8192 * 1024, 1024, 128)
+    steps = (8192 * 64, 64, 1)
+    a = ssd.SsdBwdArgs()
+    a.x = fake_tensor(strides=tok)
+    a.B = fake_tensor(strides=grp)
+    a.C = fake_tensor(strides=grp)
+    a.dt = fake_tensor(strides=steps)
+    a.dout = fake_tensor(dtype=ssd.F32, strides=tok)
+    a.dx = fake_tensor(dtype=ssd.F32, strides=tok)
+    a.dB = fake_tensor(dtype=ssd.F32, strides=grp)
+    a.dC = fake_tensor(dtype=ssd.F32, strides=grp)
+    a.ddt = fake_tensor(dtype=ssd.F32, strides=steps)
+    a.A = a.dA = a.ddt_bias = 4096
+    n = ctypes.c_size_t()
+    assert L.ssd_backward_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    big = n.value
+    assert L.ssd_backward(ctypes.byref(p), ctypes.byref(a), 4096, big - 1, None) == 6
+    assert b"need" in L.ssd_last_error_message()
+    assert L.ssd_backward(ctypes.byref(p), ctypes.byref(a), 4096 + 16, big, None) == 6
+    for name in ("initial_states", "dfinal_states", "dinitial_states"):
+        setattr(a, name, 4096 + 4)
+        assert L.ssd_backward(ctypes.byref(p), ctypes.byref(a), 4096, big, None) == 4, name
+        assert name.encode() in L.ssd_last_error_message()
+        setattr(a, name, None)
+    a.z = fake_tensor(strides=tok)  # a gate needs dz
+    assert L.ssd_backward(ctypes.byref(p), ctypes.byref(a), 4096, big, None) == 1
+    a.z = ssd.SsdTensor()
+    a.ddt = fake_tensor(strides=steps)  # ddt must be fp32
+    assert L.ssd_backward(ctypes.byref(p), ctypes.byref(a), 4096, big, None) == 3
+    a.ddt = fake_tensor(dtype=ssd.F32, strides=steps)
+    a.dA = None
+    assert L.ssd_backward(ctypes.byref(p), ctypes.byref(a), 4096, big, None) == 1
+
+
 def host_meta(cu, C):
     T = int(cu[-1])
     p = ssd.Problem(1, T, 4, 16, 1, 16, C, nseq=len(cu) - 1)
