@@ -84,7 +84,7 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p,
-            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_int,
             ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_int,
         ]
@@ -95,7 +95,7 @@ def _load():
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p,
-            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+            ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_int,
             ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -133,7 +133,7 @@ class FwdResult:
 
 def ssd_fwd(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=None,
             cu_seqlens=None, dt_softplus=True, dt_limit=None, chunk_size=0,
-            threads=None) -> FwdResult:
+            threads=None, input_dt=False) -> FwdResult:
     """Run the fp64 recurrence.
 
     Batch mode: x (b, T, H, P), B and C (b, T, G, N), dt (b, T, H), z like x,
@@ -141,7 +141,9 @@ def ssd_fwd(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=None,
     tensors without the batch axis, i.e. x (T, H, P), with sequence i owning
     tokens [cu[i], cu[i+1]); initial_states (nseq, H, P, N).
 
-    ``dt_limit=(lo, hi)`` clamps the step size after softplus.  With
+    ``dt_limit=(lo, hi)`` clamps the step size after softplus.
+    ``input_dt=True`` scales the input term by the step size,
+    S = exp(delta A) S + delta x (outer) B (the D skip keeps the raw x).  With
     ``chunk_size > 0`` the state after the last token of every sequence-aligned
     chunk is returned as ``chunk_end_states`` (logical chunk order:
     sequence-major, in token order inside a sequence).
@@ -178,7 +180,7 @@ def ssd_fwd(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=None,
     lo, hi = (0.0, math.inf) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
     rc = lib.ssd_ref_fwd(ntok, nseq, cu_p, H, P, N, G, _ptr(xs), _ptr(Bs), _ptr(Cs),
                          _ptr(dts), _ptr(A_), _ptr(bias), _ptr(D_), _ptr(zs), _ptr(h0),
-                         1 if dt_softplus else 0, clamp, lo, hi,
+                         1 if dt_softplus else 0, clamp, lo, hi, 1 if input_dt else 0,
                          int(chunk_size), _ptr(y), _ptr(hfin), _ptr(hch),
                          int(threads or 0))
     if rc != 0:
@@ -201,7 +203,7 @@ class BwdResult:
 
 def ssd_bwd(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_states=None,
             dfinal_states=None, cu_seqlens=None, dt_softplus=True, dt_limit=None,
-            threads=None) -> BwdResult:
+            threads=None, input_dt=False) -> BwdResult:
     """Gradient of L = sum(dout * y) + sum(dfinal_states * final_states).
 
     Arguments as ``ssd_fwd``; ``dout`` is shaped like x and ``dfinal_states``
@@ -244,7 +246,8 @@ def ssd_bwd(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_states=N
     cu_p = cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
     rc = lib.ssd_ref_bwd(ntok, nseq, cu_p, H, P, N, G, _ptr(xs), _ptr(Bs), _ptr(Cs),
                          _ptr(dts), _ptr(A_), _ptr(bias), _ptr(D_), _ptr(zs), _ptr(h0),
-                         1 if dt_softplus else 0, clamp, lo, hi, _ptr(dos), _ptr(dfin),
+                         1 if dt_softplus else 0, clamp, lo, hi, 1 if input_dt else 0,
+                         _ptr(dos), _ptr(dfin),
                          _ptr(dx), _ptr(dB), _ptr(dC), _ptr(ddt), _ptr(dA), _ptr(dbias),
                          _ptr(dD), _ptr(dz), _ptr(dh0), int(threads or 0))
     if rc != 0:
@@ -371,7 +374,7 @@ def _chunk_cut(meta: ChunkMeta):
 
 
 def chunk_states(x, Bm, dt, A, meta: ChunkMeta, dt_bias=None, dt_softplus=True,
-                 dt_limit=None, threads=None):
+                 dt_limit=None, threads=None, input_dt=False):
     """Each chunk's end state with a zero state entering the chunk: (K, H, P, N).
 
     Computed by running the recurrence on every chunk as its own sequence; x is
@@ -389,7 +392,7 @@ def chunk_states(x, Bm, dt, A, meta: ChunkMeta, dt_bias=None, dt_softplus=True,
     Cz = np.zeros_like(np.asarray(Bm, dtype=np.float64)[lo:hi])
     r = ssd_fwd(x[lo:hi], np.asarray(Bm)[lo:hi], Cz, np.asarray(dt)[lo:hi], A,
                 dt_bias=dt_bias, cu_seqlens=cu - lo, dt_softplus=dt_softplus,
-                dt_limit=dt_limit, threads=threads)
+                dt_limit=dt_limit, threads=threads, input_dt=input_dt)
     return r.final_states
 
 

@@ -24,14 +24,20 @@
  *     (SSD Reference, "Inter-chunk propagation": the initial-state term;
  *     cudnn-frontend PR 1133: "initial/final-state");
  *   - packed variable-length batches, where the state restarts at every
- *     sequence boundary (vLLM PR 27299 "Test Plan": continuous batching).
+ *     sequence boundary (vLLM PR 27299 "Test Plan": continuous batching);
+ *   - optionally (input_dt = 1) the step size on the input term as well,
+ *     S = exp(a) S + delta x (outer) B, the discretisation the Mamba-2 models
+ *     timed on these pages use (vLLM PR 27299 "Purpose": the Mamba-2 SSD
+ *     stages of production models); the pages write the recurrence without it,
+ *     so it is an option, off by default.  The D skip keeps the raw x.
  *
  * The state of one (sequence, head) is a P x N matrix S[p][n] (head dim
  * before state dim, SSD Reference "Shape contract").  Per token:
  *   u     = dt[t,h] + dt_bias[h]
  *   delta = softplus(u) if dt_softplus else u;   clamp to [dt_min, dt_max] if asked
  *   a     = delta * A[h]
- *   S     = exp(a) * S + x[t,h,:] (outer) B[t,g,:]      (decay first, then add)
+ *   S     = exp(a) * S + xs (outer) B[t,g,:]      (decay first, then add)
+ *           with xs = delta * x[t,h,:] if input_dt, else x[t,h,:]
  *   y     = S . C[t,g,:] + D[h] * x[t,h,:]
  *   out   = y * z / (1 + exp(-z))   if z is given, else y
  *
@@ -73,6 +79,7 @@ static double ref_softplus(double u) {
  *   h0     (nseq, H, P, N) or NULL (NULL = zero initial state)
  *   dt_softplus: 1 = apply softplus to u, 0 = use u as the step size
  *   clamp: 1 = clamp the step size to [dt_min, dt_max] after softplus
+ *   input_dt: 1 = scale the input term by the step size (see above)
  *   chunk: if > 0 and hchunk != NULL, the state after the last token of every
  *          sequence-aligned chunk is stored to hchunk.  Chunks of sequence i
  *          start at cu[i] + k*chunk and hold min(chunk, L_i - k*chunk) tokens;
@@ -90,7 +97,7 @@ int ssd_ref_fwd(int64_t ntok, int nseq, const int64_t* cu, int H, int P, int N,
                 int G, const double* x, const double* Bm, const double* Cm,
                 const double* dt, const double* A, const double* dt_bias,
                 const double* D, const double* z, const double* h0,
-                int dt_softplus, int clamp, double dt_min, double dt_max,
+                int dt_softplus, int clamp, double dt_min, double dt_max, int input_dt,
                 int chunk, double* y, double* hfinal, double* hchunk,
                 int nthreads) {
   if (ntok < 0 || nseq < 0 || H <= 0 || P <= 0 || N <= 0 || G <= 0) return -1;
@@ -152,7 +159,8 @@ int ssd_ref_fwd(int64_t ntok, int nseq, const int64_t* cu, int H, int P, int N,
       for (int p = 0; p < P; ++p) {
         double* row = S + (size_t)p * N;
         const double xp = xt[p];
-        for (int n = 0; n < N; ++n) row[n] = decay * row[n] + xp * bt[n];
+        const double xs = input_dt ? delta * xp : xp;
+        for (int n = 0; n < N; ++n) row[n] = decay * row[n] + xs * bt[n];
         double acc = 0.0;
         for (int n = 0; n < N; ++n) acc += row[n] * ct[n];
         double yp = acc + (D ? D[h] * xp : 0.0);
@@ -204,12 +212,12 @@ int64_t ssd_ref_num_chunks(int nseq, const int64_t* cu, int chunk) {
  *     dz_t   = dout_t * y_t * silu'(z_t),     silu'(z) = s (1 + z (1 - s)), s = sigmoid(z)
  *     G     += dy_t (outer) C_t               (now dL/dS_t, all paths)
  *     dC_t  += S_t^T dy_t                     (summed over the heads of the group)
- *     dx_t   = G B_t + D dy_t
- *     dB_t  += G^T x_t                        (summed over the heads of the group)
+ *     dx_t   = f G B_t + D dy_t               (f = delta_t with input_dt, else 1)
+ *     dB_t  += f G^T x_t                      (summed over the heads of the group)
  *     dD    += dy_t . x_t
  *     da_t   = exp(a_t) <G, S_{t-1}>          (a_t = delta_t A)
  *     G      = exp(a_t) G                     (dL/dS_{t-1})
- *     dA    += da_t delta_t;  ddelta = da_t A
+ *     dA    += da_t delta_t;  ddelta = da_t A (+ x_t . G B_t with input_dt)
  *     ddt_t  = ddelta * sigmoid(u_t)          (softplus' = sigmoid; ddelta itself
  *                                              without softplus; 0 where the
  *                                              clamp is active)
@@ -249,7 +257,7 @@ int ssd_ref_bwd(int64_t ntok, int nseq, const int64_t* cu, int H, int P, int N,
                 int G, const double* x, const double* Bm, const double* Cm,
                 const double* dt, const double* A, const double* dt_bias,
                 const double* D, const double* z, const double* h0,
-                int dt_softplus, int clamp, double dt_min, double dt_max,
+                int dt_softplus, int clamp, double dt_min, double dt_max, int input_dt,
                 const double* dout, const double* dfinal,
                 double* dx, double* dB, double* dC, double* ddt, double* dA,
                 double* ddt_bias, double* dD, double* dz, double* dh0,
@@ -318,11 +326,12 @@ int ssd_ref_bwd(int64_t ntok, int nseq, const int64_t* cu, int H, int P, int N,
           ref_step_size(dt[t * H + h] + (dt_bias ? dt_bias[h] : 0.0), dt_softplus, clamp,
                         dt_min, dt_max, &delta, &gd);
           const double decay = exp(delta * A[h]);
+          const double f = input_dt ? delta : 1.0;
           const double* xt = x + ((size_t)t * H + h) * P;
           const double* bt = Bm + ((size_t)t * G + g) * N;
           for (int p = 0; p < P; ++p)
             for (int n = 0; n < N; ++n)
-              S[(size_t)p * N + n] = decay * S[(size_t)p * N + n] + xt[p] * bt[n];
+              S[(size_t)p * N + n] = decay * S[(size_t)p * N + n] + (f * xt[p]) * bt[n];
         }
         /* reverse sweep */
         if (dfinal)
@@ -339,13 +348,14 @@ int ssd_ref_bwd(int64_t ntok, int nseq, const int64_t* cu, int H, int P, int N,
             ref_step_size(dt[t * H + h] + (dt_bias ? dt_bias[h] : 0.0), dt_softplus, clamp,
                           dt_min, dt_max, &delta, &gd);
             const double decay = exp(delta * A[h]);
+            const double f = input_dt ? delta : 1.0;
             const double* xt = x + ((size_t)t * H + h) * P;
             const double* bt = Bm + ((size_t)t * G + g) * N;
             const double* Sp = blk + (size_t)(t - ta) * PN;
             double* Sn = blk + (size_t)(t - ta + 1) * PN;
             for (int p = 0; p < P; ++p)
               for (int n = 0; n < N; ++n)
-                Sn[(size_t)p * N + n] = decay * Sp[(size_t)p * N + n] + xt[p] * bt[n];
+                Sn[(size_t)p * N + n] = decay * Sp[(size_t)p * N + n] + (f * xt[p]) * bt[n];
           }
           for (int64_t t = tb - 1; t >= ta; --t) {
             const double u = dt[t * H + h] + (dt_bias ? dt_bias[h] : 0.0);
@@ -361,7 +371,8 @@ int ssd_ref_bwd(int64_t ntok, int nseq, const int64_t* cu, int H, int P, int N,
             double* dxt = dx + ((size_t)t * H + h) * P;
             double* dbt = dB + ((size_t)t * G + g) * N;
             double* dct = dC + ((size_t)t * G + g) * N;
-            double da = 0.0;
+            const double f = input_dt ? delta : 1.0;
+            double da = 0.0, din = 0.0;
             for (int p = 0; p < P; ++p) {
               const double* srow = St + (size_t)p * N;
               double* grow = Gs + (size_t)p * N;
@@ -381,15 +392,16 @@ int ssd_ref_bwd(int64_t ntok, int nseq, const int64_t* cu, int H, int P, int N,
                 dct[n] += srow[n] * dy;
                 grow[n] += dy * ct[n];
                 acc += grow[n] * bt[n];
-                dbt[n] += grow[n] * xt[p];
+                dbt[n] += grow[n] * (f * xt[p]);
                 da += grow[n] * Sp[(size_t)p * N + n];
               }
-              dxt[p] = acc + (D ? D[h] * dy : 0.0);
+              din += xt[p] * acc;
+              dxt[p] = f * acc + (D ? D[h] * dy : 0.0);
             }
             da *= decay;
             for (size_t q = 0; q < PN; ++q) Gs[q] *= decay;
             sA += da * delta;
-            const double du = da * A[h] * gd;
+            const double du = (da * A[h] + (input_dt ? din : 0.0)) * gd;
             ddt[t * H + h] = du;
             sBias += du;
           }

@@ -9,7 +9,10 @@
   state and (for a zero initial state) linear in B, so a finite step of any
   size must change it by exactly <gradient, step> (up to rounding).
 * A closed form: with A = 0, N = 1 and B = C = 1 the output is a prefix sum, so
-  dx is the reverse cumulative sum of dout plus D dout.
+  dx is the reverse cumulative sum of dout plus D dout (with the step size on
+  the input term, delta times it, and the raw dt gets x . that sum through
+  softplus').
+* The same checks with the step size on the input term (``input_dt``).
 * Structure: grouped B/C gradients equal the per-head gradients summed over
   the group, and a packed batch equals its sequences run one by one.
 """
@@ -100,6 +103,28 @@ def test_fd_without_softplus():
     check_fd(p, w, cu, dt_softplus=False)
 
 
+@pytest.mark.parametrize("kw", [dict(), dict(cu=np.array([0, 4, 4, 5, 11, 11], dtype=np.int64)),
+                                dict(z=False, D=False, h0=False, dfinal=False)],
+                         ids=["batch", "packed", "plain"])
+def test_fd_input_dt(kw):
+    check_fd(*problem(13, **kw), input_dt=True)
+
+
+def test_fd_input_dt_clamp_and_no_softplus():
+    p, w, cu = problem(14, T=12)
+    delta = oracle.step_size(p["dt"], p["dt_bias"])
+    lo, hi = np.quantile(delta, [0.25, 0.75])
+    for v in (lo, hi):
+        assert not (np.abs(delta - v) < 1e-4).any()
+    g = grads(p, w, cu, dt_limit=(lo, hi), input_dt=True)
+    assert np.all(g.ddt[(delta < lo) | (delta > hi)] == 0.0)
+    check_fd(p, w, cu, dt_limit=(lo, hi), input_dt=True)
+    q, w2, cu2 = problem(15)
+    q["dt"] = np.abs(q["dt"]) * 0.3 + 0.05
+    q["dt_bias"] = np.zeros_like(q["dt_bias"])
+    check_fd(q, w2, cu2, dt_softplus=False, input_dt=True)
+
+
 def test_fd_clamp_active():
     p, w, cu = problem(6, T=12)
     delta = oracle.step_size(p["dt"], p["dt_bias"])
@@ -149,6 +174,14 @@ def test_prefix_sum_closed_form():
     assert np.allclose(g.dx, rev + D[None, None, :, None] * dout, rtol=0, atol=1e-13)
     # A = 0: nothing depends on dt
     assert np.all(g.ddt == 0.0) and np.all(g.ddt_bias == 0.0)
+    # with the step size on the input: y_t = sum_{s<=t} delta_s x_s + D x_t
+    delta = np.log1p(np.exp(dt))
+    gi = oracle.ssd_bwd(x, ones, ones, dt, np.zeros(H), dout, D=D, input_dt=True)
+    assert np.allclose(gi.dx, delta[..., None] * rev + D[None, None, :, None] * dout,
+                       rtol=0, atol=1e-13)
+    sig = 1.0 / (1.0 + np.exp(-dt))
+    assert np.allclose(gi.ddt, np.sum(x * rev, axis=-1) * sig, rtol=0, atol=1e-13)
+    assert np.allclose(gi.ddt_bias, gi.ddt.sum(axis=(0, 1)), rtol=0, atol=1e-13)
 
 
 def test_group_gradients_are_head_sums():

@@ -15,17 +15,17 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 MUTANTS = {
-    "decay_after_add": ("row[n] = decay * row[n] + xp * bt[n];",
-                        "row[n] = decay * (row[n] + xp * bt[n]);"),
+    "decay_after_add": ("row[n] = decay * row[n] + xs * bt[n];",
+                        "row[n] = decay * (row[n] + xs * bt[n]);"),
     "wrong_group_of_head": ("const int g = h / hpg;", "const int g = h % G;"),
     "dropped_skip": ("double yp = acc + (D ? D[h] * xp : 0.0);", "double yp = acc;"),
     "readout_before_update": (
-        "for (int n = 0; n < N; ++n) row[n] = decay * row[n] + xp * bt[n];\n"
+        "for (int n = 0; n < N; ++n) row[n] = decay * row[n] + xs * bt[n];\n"
         "        double acc = 0.0;\n"
         "        for (int n = 0; n < N; ++n) acc += row[n] * ct[n];",
         "double acc = 0.0;\n"
         "        for (int n = 0; n < N; ++n) acc += row[n] * ct[n];\n"
-        "        for (int n = 0; n < N; ++n) row[n] = decay * row[n] + xp * bt[n];"),
+        "        for (int n = 0; n < N; ++n) row[n] = decay * row[n] + xs * bt[n];"),
     "sign_of_A": ("exp(delta * A[h])", "exp(-delta * A[h])"),
     "sign_of_bias": ("+ (dt_bias ? dt_bias[h] : 0.0)", "- (dt_bias ? dt_bias[h] : 0.0)"),
     "B_read_from_C": ("const double* bt = Bm +", "const double* bt = Cm +"),
@@ -35,15 +35,26 @@ MUTANTS = {
         "for (int q = 0; q < P * N; ++q) S[q] = h0[((size_t)i * H + h) * (size_t)P * N + (q % P) * N + q / P];"),
     "clamp_upper_ignored": ("if (delta > dt_max) delta = dt_max;", ""),
     "chunk_end_off_by_one": ("(t - t0) % chunk == chunk - 1", "(t - t0) % chunk == 0"),
+    "input_dt_ignored": ("const double xs = input_dt ? delta * xp : xp;", "const double xs = xp;"),
+    "input_dt_scales_skip": ("double yp = acc + (D ? D[h] * xp : 0.0);",
+                             "double yp = acc + (D ? D[h] * xs : 0.0);"),
 }
 
 # slips in the backward (ssd_ref_bwd), caught by tests/test_oracle_bwd_pins.py
 BWD_MUTANTS = {
-    "bwd_dx_without_skip": ("dxt[p] = acc + (D ? D[h] * dy : 0.0);", "dxt[p] = acc;"),
+    "bwd_dx_without_skip": ("dxt[p] = f * acc + (D ? D[h] * dy : 0.0);", "dxt[p] = f * acc;"),
+    "bwd_input_dt_dx_unscaled": ("dxt[p] = f * acc + (D ? D[h] * dy : 0.0);",
+                                 "dxt[p] = acc + (D ? D[h] * dy : 0.0);"),
+    "bwd_input_dt_dB_unscaled": ("dbt[n] += grow[n] * (f * xt[p]);", "dbt[n] += grow[n] * xt[p];"),
+    "bwd_input_dt_no_step_term": ("(da * A[h] + (input_dt ? din : 0.0)) * gd",
+                                  "(da * A[h]) * gd"),
+    "bwd_input_dt_recompute_unscaled": (
+        "Sn[(size_t)p * N + n] = decay * Sp[(size_t)p * N + n] + (f * xt[p]) * bt[n];",
+        "Sn[(size_t)p * N + n] = decay * Sp[(size_t)p * N + n] + xt[p] * bt[n];"),
     "bwd_silu_derivative_sign": ("(sg * (1.0 + zz * (1.0 - sg)))", "(sg * (1.0 - zz * (1.0 - sg)))"),
     "bwd_dB_before_adjoint_update": (
-        "grow[n] += dy * ct[n];\n                acc += grow[n] * bt[n];\n                dbt[n] += grow[n] * xt[p];",
-        "dbt[n] += grow[n] * xt[p];\n                grow[n] += dy * ct[n];\n                acc += grow[n] * bt[n];"),
+        "grow[n] += dy * ct[n];\n                acc += grow[n] * bt[n];\n                dbt[n] += grow[n] * (f * xt[p]);",
+        "dbt[n] += grow[n] * (f * xt[p]);\n                grow[n] += dy * ct[n];\n                acc += grow[n] * bt[n];"),
     "bwd_dC_from_previous_state": ("dct[n] += srow[n] * dy;", "dct[n] += Sp[(size_t)p * N + n] * dy;"),
     "bwd_da_from_current_state": ("da += grow[n] * Sp[(size_t)p * N + n];", "da += grow[n] * srow[n];"),
     "bwd_da_not_decayed": ("da *= decay;", ""),

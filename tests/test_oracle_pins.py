@@ -40,14 +40,16 @@ def plain_softplus(u):
     return np.log(1.0 + np.exp(u))
 
 
-def closed_form(x, B, C, dt, A, dt_bias, D=None, z=None, initial_states=None):
+def closed_form(x, B, C, dt, A, dt_bias, D=None, z=None, initial_states=None, input_dt=False):
     """y_t = sum_{s<=t} C_t^T (prod_{u=s+1..t} abar_u) B_s x_s
            + C_t^T (prod_{u<=t} abar_u) h_init  + D x_t,  then the SiLU gate.
 
     SSD Reference, section "Math": the closed form with the empty product = 1;
     the initial-state term decays through every token up to t (section
     "Inter-chunk propagation", the init term).  Brute force, O(T^2), explicit
-    products of per-token decays (no cumulative sums).
+    products of per-token decays (no cumulative sums).  With ``input_dt`` the
+    input of token s enters as delta_s x_s (Mamba-2's discretised input);
+    the skip still reads x_t.
     """
     b, T, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
@@ -56,11 +58,14 @@ def closed_form(x, B, C, dt, A, dt_bias, D=None, z=None, initial_states=None):
     for bi in range(b):
         for h in range(H):
             g = h // hpg
-            abar = np.exp(plain_softplus(dt[bi, :, h] + dt_bias[h]) * A[h])
+            delta = plain_softplus(dt[bi, :, h] + dt_bias[h])
+            abar = np.exp(delta * A[h])
             for t in range(T):
                 acc = np.zeros(P)
                 for s in range(t + 1):
                     w = np.prod(abar[s + 1:t + 1])  # empty product is 1
+                    if input_dt:
+                        w = w * delta[s]
                     acc += w * np.dot(C[bi, t, g], B[bi, s, g]) * x[bi, s, h]
                 if initial_states is not None:
                     w0 = np.prod(abar[:t + 1])
@@ -114,6 +119,32 @@ def test_closed_form_odd_groups_and_long_memory():
     assert rel(r.y, closed_form(**pr)) < 1e-12
 
 
+@pytest.mark.parametrize("gated,with_D,h0", [(False, False, False), (True, True, True)])
+def test_closed_form_input_dt(gated, with_D, h0):
+    rng = np.random.default_rng(17)
+    pr = rand_problem(rng, gated=gated, with_D=with_D, h0=h0)
+    r = oracle.ssd_fwd(**pr, input_dt=True)
+    ref = closed_form(**pr, input_dt=True)
+    assert rel(r.y, ref) < 1e-12
+    # and it is a different function: the plain recurrence misses by O(1)
+    assert rel(oracle.ssd_fwd(**pr).y, ref) > 1e-2
+
+
+def test_input_dt_is_the_plain_recurrence_on_scaled_input():
+    # the input term delta x (outer) B is the plain one with x replaced by
+    # delta x; outputs and final states agree when the skip is left out, and
+    # the skip adds D x (the raw x) on top
+    rng = np.random.default_rng(19)
+    pr = rand_problem(rng, gated=False, with_D=False)
+    delta = oracle.step_size(pr["dt"], pr["dt_bias"])
+    a = oracle.ssd_fwd(**pr, input_dt=True)
+    b = oracle.ssd_fwd(**dict(pr, x=pr["x"] * delta[..., None]))
+    assert rel(a.y, b.y) < 1e-13 and rel(a.final_states, b.final_states) < 1e-13
+    D = rng.standard_normal(pr["x"].shape[2])
+    c = oracle.ssd_fwd(**dict(pr, D=D), input_dt=True)
+    np.testing.assert_allclose(c.y - a.y, D[None, None, :, None] * pr["x"], rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------- special cases
 
 def test_zero_decay_is_prefix_sum():
@@ -129,6 +160,11 @@ def test_zero_decay_is_prefix_sum():
     ref = np.cumsum(x, axis=1) + D[None, None, :, None] * x
     np.testing.assert_allclose(r.y, ref, rtol=0, atol=1e-13)
     np.testing.assert_allclose(r.final_states[:, :, :, 0], x.sum(axis=1), rtol=0, atol=1e-13)
+    # with the step size on the input term the sum is of delta x
+    ri = oracle.ssd_fwd(x, ones, ones, dt, np.zeros(H), D=D, input_dt=True)
+    dx = plain_softplus(dt)[..., None] * x
+    np.testing.assert_allclose(ri.y, np.cumsum(dx, axis=1) + D[None, None, :, None] * x,
+                               rtol=0, atol=1e-13)
 
 
 def test_zero_decay_general_BC():
