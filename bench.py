@@ -6,7 +6,11 @@ passing, chunk scan -- or the single fused kernel) over one batch of synthetic
 inputs already resident in HBM.  Prints ONE JSON line (rank 0).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload nemotron]
-                    [--algo staged|fused|auto] [--no-cpu-baseline]
+                    [--algo staged|fused|auto] [--no-cpu-baseline] [--input-dt]
+
+--input-dt puts the step size on the input term as well (delta x (outer) B,
+the discretised input of the Mamba-2 models); the default is the recurrence
+as the pages write it.
 
 Only one GPU is used: --gpus above 1 exits with a message.
 
@@ -55,6 +59,8 @@ def parse():
     ap.add_argument("--out-dtype", default="bf16", choices=["f32", "bf16"])
     ap.add_argument("--layout", default="xbc", choices=["xbc", "contiguous"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--input-dt", action="store_true",
+                    help="step size on the input term too (Mamba-2's discretised input)")
     ap.add_argument("--backward", action="store_true",
                     help="also time ssd_backward (upstream gradient ~ N(0,1)) and report the "
                          "forward+backward rate in a 'fwd_bwd' object")
@@ -67,12 +73,13 @@ def parse():
     return ap.parse_args()
 
 
-def stage_bytes(w, K, state_bytes, out_bytes, in_bytes=2):
+def stage_bytes(w, K, state_bytes, out_bytes, in_bytes=2, input_dt=False):
     """Algorithmic HBM bytes each kernel must move per launch (one forward).
 
     b*T tokens, H heads, P head dim, G groups, N state, C chunk, K chunk slots.
     Each input is read once, each output written once; CB is fp32 and only its
-    causal half (s <= l) is written and read; the cumsum is fp32.
+    causal half (s <= l) is written and read; the cumsum is fp32, and so are
+    the per-position step sizes the staged path passes on with input_dt.
     """
     T = w.batch * w.seqlen
     H, P, G, N, C = w.nheads, w.headdim, w.ngroups, w.dstate, w.chunk_size
@@ -81,6 +88,7 @@ def stage_bytes(w, K, state_bytes, out_bytes, in_bytes=2):
     bc = T * G * N * e
     dt = T * H * e
     cs = 4 * K * H * C
+    dtc = 4 * K * H * C if input_dt else 0
     cb = 4 * K * G * C * (C + 1) // 2
     st = K * H * P * N * state_bytes
     fin = 4 * (w.nseq or w.batch) * H * P * N
@@ -91,11 +99,11 @@ def stage_bytes(w, K, state_bytes, out_bytes, in_bytes=2):
         # cu_seqlens in; the chunk table (4-word header, 3 words per chunk,
         # first chunk per sequence) out
         "varlen_meta": 4 * (nseq + 1) + 4 * (4 + 3 * K + nseq + 1),
-        "chunk_cumsum": dt + cs,
+        "chunk_cumsum": dt + cs + dtc,
         "bmm_chunk": 2 * bc + cb,
-        "chunk_state": x + bc + cs + st,
+        "chunk_state": x + bc + cs + dtc + st,
         "state_passing": 2 * st + 4 * K * H + fin,
-        "chunk_scan": cb + x + bc + cs + st + z + out,
+        "chunk_scan": cb + x + bc + cs + dtc + st + z + out,
         "fused_fwd": x + 2 * bc + dt + z + out + fin,
     }
 
@@ -212,7 +220,8 @@ def main():
     cu = (torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
           if inp.cu_seqlens is not None else None)
 
-    prob = ssd.problem_from(x, B, w.chunk_size, cu_seqlens=cu, state_dtype=sdt)
+    prob = ssd.problem_from(x, B, w.chunk_size, cu_seqlens=cu, state_dtype=sdt,
+                            input_dt=args.input_dt)
     algo = args.algo
     if algo == "auto":
         # the single-pass forward where it applies (bf16 inputs, d_state <= 128),
@@ -226,6 +235,7 @@ def main():
 
     # stage buffers for the instrumented staged step (same kernels ssd_forward launches)
     cs = torch.empty((K, w.nheads, w.chunk_size), dtype=torch.float32, device=dev)
+    dtc = torch.empty_like(cs) if args.input_dt else None
     cb = torch.empty((K, w.ngroups, w.chunk_size, w.chunk_size), dtype=torch.float32, device=dev)
     st = torch.empty((K, w.nheads, w.headdim, w.dstate), dtype=sdt, device=dev)
     if prob.packed:
@@ -238,11 +248,12 @@ def main():
         def launches():
             if prob.packed:
                 yield "varlen_meta", lambda: ssd.ssd_varlen_chunk_meta(prob, prob.chunk_meta)
-            yield "chunk_cumsum", lambda: ssd.ssd_chunk_cumsum(prob, dt, A, bias, cs)
+            yield "chunk_cumsum", lambda: ssd.ssd_chunk_cumsum(prob, dt, A, bias, cs, dtc)
             yield "bmm_chunk", lambda: ssd.ssd_bmm_chunk(prob, C, B, cb)
-            yield "chunk_state", lambda: ssd.ssd_chunk_state(prob, x, B, cs, st)
+            yield "chunk_state", lambda: ssd.ssd_chunk_state(prob, x, B, cs, st, dt_chunk=dtc)
             yield "state_passing", lambda: ssd.ssd_state_passing(prob, st, cs, None, st, fin)
-            yield "chunk_scan", lambda: ssd.ssd_chunk_scan(prob, cb, x, C, cs, st, D, z, out)
+            yield "chunk_scan", lambda: ssd.ssd_chunk_scan(prob, cb, x, C, cs, st, D, z, out,
+                                                           dt_chunk=dtc)
     else:
         names = ["fused_fwd"]
 
@@ -250,7 +261,7 @@ def main():
             yield "fused_fwd", lambda: ssd.ssd_forward(x, B, C, dt, A, bias, D, z, None, cu,
                                                        w.chunk_size, state_dtype=sdt, out=out,
                                                        final_states=fin, algo="fused",
-                                                       workspace=ws)
+                                                       workspace=ws, input_dt=args.input_dt)
 
     def step(events=None):
         for name, fn in launches():
@@ -301,7 +312,7 @@ def main():
     sbytes = 4 if sdt == torch.float32 else 2
     obytes = 2 if odt == torch.bfloat16 else 4
     ibytes = 2 if w.dtype == "bf16" else 4
-    nb = stage_bytes(w, K, sbytes, obytes, ibytes)
+    nb = stage_bytes(w, K, sbytes, obytes, ibytes, args.input_dt)
     nf = stage_flops(w, K)
     dom = max((n for n in names if n in nb), key=lambda n: per_kernel_ms[n])
     achieved = nb[dom] / (per_kernel_ms[dom] * 1e-3) / 1e9
@@ -314,7 +325,8 @@ def main():
               for n in names}
     roof_time_ms = sum(nb[n] for n in names if n in nb) / (HBM_PEAK_GBS * 1e9) * 1e3
 
-    traffic_key = f"{w.name}_{algo}_{args.state_dtype}state_{args.out_dtype}out_{args.layout}"
+    traffic_key = (f"{w.name}_{algo}_{args.state_dtype}state_{args.out_dtype}out_{args.layout}"
+                   + ("_inputdt" if args.input_dt else ""))
     result = {
         "metric": "SSD fwd tokens/s at Nemotron-Nano dims, seq 8192 bf16; % of stage roofline",
         "value": round(value, 1),
@@ -333,10 +345,11 @@ def main():
                         f"{w.nheads} heads x {w.headdim}, d_state {w.dstate}, "
                         f"{w.ngroups} groups, chunk {w.chunk_size}"
                         + (f", {w.nseq} packed sequences" if w.nseq else "")
-                        + (", D" if w.has_D else "") + (", z gate" if w.has_z else ""),
+                        + (", D" if w.has_D else "") + (", z gate" if w.has_z else "")
+                        + (", step size on the input term" if args.input_dt else ""),
             "global_batch": w.batch, "seq_len": w.seqlen, "parallelism": "none (1 GPU)",
             "algo": algo, "state_dtype": args.state_dtype, "out_dtype": args.out_dtype,
-            "layout": args.layout,
+            "layout": args.layout, "input_dt": bool(args.input_dt),
         },
         "roofline": {
             "bound": "hbm",
@@ -373,12 +386,12 @@ def time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu, fwd_ms):
     import torch
     g = torch.Generator(device=x.device).manual_seed(4)
     dout = torch.randn(x.shape, generator=g, device=x.device, dtype=torch.float32)
-    prob = ssd.problem_from(x, B, w.chunk_size, cu_seqlens=cu)
+    prob = ssd.problem_from(x, B, w.chunk_size, cu_seqlens=cu, input_dt=args.input_dt)
     ws = torch.empty(prob.backward_workspace_size(), dtype=torch.uint8, device=x.device)
 
     def bwd():
         return ssd.ssd_backward(x, B, C, dt, A, dout, dt_bias=bias, D=D, z=z, cu_seqlens=cu,
-                                chunk_size=w.chunk_size, workspace=ws)
+                                chunk_size=w.chunk_size, workspace=ws, input_dt=args.input_dt)
 
     for _ in range(max(2, args.warmup // 5)):
         bwd()

@@ -110,6 +110,11 @@ typedef struct ssd_problem {
   int32_t dt_clamp;    /* 1: clamp delta to [dt_min, dt_max] */
   float dt_min, dt_max;
   ssd_dtype state_dtype; /* storage of the per-chunk states (F32 or BF16) */
+  int32_t input_dt;    /* 1: the input term is delta_t x_t (outer) B_t, the way
+                          Mamba-2 implementations discretise the input (not
+                          written on the pages); 0: x_t (outer) B_t, the
+                          recurrence as the SSD Reference writes it ("Math").
+                          The skip D x_t uses the raw x either way. */
 } ssd_problem;
 
 /* ---------------------------------------------------------------- queries */
@@ -182,16 +187,20 @@ ssd_status ssd_bmm_chunk(const ssd_problem* p, ssd_tensor C, ssd_tensor B, float
 /* ---------------------------------------------------------------- a3 */
 
 /* Chunk state: each chunk's end state from a zero start,
- *   states[j,h,p,n] = sum_{s < len} exp(cs[last] - cs[s]) x[t0+s,h,p] B[t0+s,g,n]
- * SSD Reference "Intra-chunk outputs and per-chunk states" (states einsum with
- * decay_states = exp(A_cumsum[-1] - A_cumsum)).
+ *   states[j,h,p,n] = sum_{s < len} exp(cs[last] - cs[s]) f_s x[t0+s,h,p] B[t0+s,g,n]
+ * with f_s = delta_s when p->input_dt, else 1.  SSD Reference "Intra-chunk
+ * outputs and per-chunk states" (states einsum with decay_states =
+ * exp(A_cumsum[-1] - A_cumsum)).
  *   x         (b, T, H, P), F32 or BF16 (same dtype as B)
  *   B         (b, T, G, N)
  *   dA_cumsum float32 (K, H, C) from ssd_chunk_cumsum
+ *   dt_chunk  float32 (K, H, C): delta per position, ssd_chunk_cumsum's dt_out;
+ *             required when p->input_dt, otherwise ignored (may be NULL)
  *   states    (K, H, P, N) in p->state_dtype, written
  */
 ssd_status ssd_chunk_state(const ssd_problem* p, ssd_tensor x, ssd_tensor B,
-                           const float* dA_cumsum, void* states, hipStream_t stream);
+                           const float* dA_cumsum, const float* dt_chunk, void* states,
+                           hipStream_t stream);
 
 /* ---------------------------------------------------------------- a4 */
 
@@ -216,22 +225,25 @@ ssd_status ssd_state_passing(const ssd_problem* p, const void* states,
 
 /* Chunk scan: the output of every position l < len_j of chunk j,
  *   y[l] = exp(cs[l]) C_l . Hin[j]                                    (Y_off)
- *        + sum_{s <= l} exp(cs[l] - cs[s]) CB[l,s] x_s                 (Y_diag)
+ *        + sum_{s <= l} exp(cs[l] - cs[s]) CB[l,s] f_s x_s             (Y_diag)
  *        + D_h x_l ;      out = y * silu(z)  if z is given
+ * (f_s = delta_s when p->input_dt, else 1)
  * SSD Reference "Intra-chunk outputs" (L = exp(segsum) masked to s <= l,
  * Y_diag) and "Readout" (Y_off = C . state . exp(A_cumsum), Y = Y_diag + Y_off);
  * gate as cudnn-frontend PR 1133 "optional skip/SiLU" (D added before gating).
  *   CB        float32 (K, G, C, C) from ssd_bmm_chunk
  *   x         (b, T, H, P); C (b, T, G, N); same dtype
  *   dA_cumsum float32 (K, H, C)
+ *   dt_chunk  float32 (K, H, C) as for ssd_chunk_state (input_dt only)
  *   states_in (K, H, P, N) state_dtype: carry-in states from ssd_state_passing
  *   D         float32 (H) or NULL
  *   z         (b, T, H, P) same dtype as x, or data == NULL
  *   out       (b, T, H, P) F32 or BF16, written
  */
 ssd_status ssd_chunk_scan(const ssd_problem* p, const float* CB, ssd_tensor x, ssd_tensor C,
-                          const float* dA_cumsum, const void* states_in, const float* D,
-                          ssd_tensor z, ssd_tensor out, hipStream_t stream);
+                          const float* dA_cumsum, const float* dt_chunk,
+                          const void* states_in, const float* D, ssd_tensor z,
+                          ssd_tensor out, hipStream_t stream);
 
 /* ---------------------------------------------------------------- forward */
 
@@ -257,7 +269,9 @@ typedef struct ssd_fwd_args {
  * intermediates), preceded by a small reset kernel; it always works on
  * 128-token chunks (the result does not depend on the chunk length), takes
  * bf16 x, B, C (and z) and dstate <= 128, and returns SSD_ERR_UNSUPPORTED
- * otherwise.  initial_states and final_states must be 16-byte aligned for
+ * otherwise; with input_dt it also needs delta > 0 by construction (softplus,
+ * or a clamp with dt_min >= 0), since it folds log2(delta) into the decay
+ * exponent.  initial_states and final_states must be 16-byte aligned for
  * it.  Its results are bit-identical run to run for a given problem shape;
  * two different shapes of one computation (e.g. a sequence split in two and
  * resumed from the final state) agree to fp32 rounding of the states.

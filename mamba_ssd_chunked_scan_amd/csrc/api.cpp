@@ -76,6 +76,8 @@ ssd_status check_problem(const ssd_problem* p) {
   if (!valid_dtype(p->state_dtype)) return fail(SSD_ERR_DTYPE, "state_dtype is not F32 or BF16");
   if (p->dt_clamp && !(p->dt_min <= p->dt_max))
     return fail(SSD_ERR_SHAPE, "dt_min = %g > dt_max = %g", p->dt_min, p->dt_max);
+  if (p->input_dt != 0 && p->input_dt != 1)
+    return fail(SSD_ERR_SHAPE, "input_dt = %d: must be 0 or 1", p->input_dt);
   if ((int64_t)p->batch * p->seqlen > INT32_MAX)
     return fail(SSD_ERR_UNSUPPORTED, "batch * seqlen exceeds 2^31 - 1 tokens");
   return SSD_OK;
@@ -168,7 +170,7 @@ ssd_status need_meta(const ssd_problem* p) {
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct StagedWs {
-  size_t meta, cs, cb, st, total;
+  size_t meta, cs, dtc, cb, st, total;
 };
 
 StagedWs staged_layout(const ssd_problem* p) {
@@ -182,6 +184,8 @@ StagedWs staged_layout(const ssd_problem* p) {
                     sizeof(int32_t));
   w.cs = off;
   off += align256((size_t)K * p->nheads * p->chunk_size * sizeof(float));
+  w.dtc = off;  // step size per position, when it scales the input term
+  if (p->input_dt) off += align256((size_t)K * p->nheads * p->chunk_size * sizeof(float));
   w.cb = off;
   off += align256((size_t)K * p->ngroups * p->chunk_size * p->chunk_size * sizeof(float));
   w.st = off;
@@ -237,6 +241,10 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
   if (p->dstate > 128)
     return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED supports dstate <= 128, got %d (use SSD_ALGO_STAGED)",
                 p->dstate);
+  if (p->input_dt && !p->dt_softplus && !(p->dt_clamp && p->dt_min >= 0.0f))
+    return fail(SSD_ERR_UNSUPPORTED,
+                "SSD_ALGO_FUSED with input_dt needs delta >= 0 (softplus, or a clamp with "
+                "dt_min >= 0); use SSD_ALGO_STAGED");
   SSD_TRY(check_state_ptr(a->initial_states, "initial_states"));
   SSD_TRY(check_state_ptr(a->final_states, "final_states"));
   const FusedWs w = fused_layout(p);
@@ -259,7 +267,7 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
   f.out_dtype = dcode(a->out.dtype);
   f.A = a->A; f.dt_bias = a->dt_bias; f.D = a->D;
   f.h0 = a->initial_states; f.hfinal = a->final_states;
-  f.softplus = p->dt_softplus; f.clamp = p->dt_clamp;
+  f.softplus = p->dt_softplus; f.clamp = p->dt_clamp; f.input_dt = p->input_dt;
   f.dt_min = p->dt_min; f.dt_max = p->dt_max;
   f.plan = w.plan;
   f.sync = reinterpret_cast<uint32_t*>(ws + w.sync);
@@ -285,6 +293,7 @@ ssd_status staged_run(const ssd_problem* p, const ssd_fwd_args* a, const int32_t
   int32_t* meta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws + w.meta) : nullptr;
   if (meta_in) meta = const_cast<int32_t*>(meta_in);
   float* cs = reinterpret_cast<float*>(ws + w.cs);
+  float* dtc = p->input_dt ? reinterpret_cast<float*>(ws + w.dtc) : nullptr;
   float* cb = reinterpret_cast<float*>(ws + w.cb);
   void* st = ws + w.st;
   ssd::Geo g = make_geo(p, meta);
@@ -292,16 +301,17 @@ ssd_status staged_run(const ssd_problem* p, const ssd_fwd_args* a, const int32_t
   if (p->nseq > 0 && !meta_in)
     SSD_HIP(ssd::launch_varlen_meta(g, p->cu_seqlens, meta, stream), "varlen_chunk_meta launch");
   SSD_HIP(ssd::launch_chunk_cumsum(g, targ(a->dt), dcode(a->dt.dtype), a->A, a->dt_bias,
-                                   p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, cs, nullptr,
+                                   p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, cs, dtc,
                                    stream),
           "chunk_cumsum launch");
   SSD_HIP(ssd::launch_bmm_chunk(g, targ(a->C), targ(a->B), in, cb, stream), "bmm_chunk launch");
-  SSD_HIP(ssd::launch_chunk_state(g, targ(a->x), targ(a->B), in, cs, st, sd, stream),
+  SSD_HIP(ssd::launch_chunk_state(g, targ(a->x), targ(a->B), in, cs, dtc, st, sd, stream),
           "chunk_state launch");
   SSD_HIP(ssd::launch_state_passing(g, st, sd, cs, a->initial_states, st, a->final_states,
                                     stream),
           "state_passing launch");
-  SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, st, sd, a->D, targ(a->z),
+  SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, dtc, st, sd, a->D,
+                                 targ(a->z),
                                  targ(a->out), dcode(a->out.dtype), stream, yoff),
           "chunk_scan launch");
   return ok();
@@ -337,6 +347,7 @@ BwdProblems bwd_problems(const ssd_problem* p) {
   q.dx = q.fwd;
   q.dx.dt_softplus = 0;
   q.dx.dt_clamp = 0;
+  q.dx.input_dt = 0;  // the adjoint's input dy (outer) C carries no step size
   q.dB = q.dx;
   q.dB.headdim = p->dstate;
   q.dB.dstate = p->headdim;
@@ -349,8 +360,9 @@ BwdProblems bwd_problems(const ssd_problem* p) {
 }
 
 struct BwdWs {
-  size_t yf, yo, dy, dyr, Cr, Br, Cf, Bf, Cer, Be, xr, xf, delta, gd, dtr, dyx, gx, gb, gc, gfirst,
-      dfT, h0T, mmeta, mcu, part, run_fwd, run_dx, run_rest, fwd_bytes, dx_bytes, rest_bytes, total;
+  size_t yf, yo, dy, dyr, Cr, Br, Cf, Bf, Cer, Be, xr, xf, delta, gd, dtr, dyx, xg, gx, gb, gc,
+      gfirst, dfT, h0T, mmeta, mcu, part, run_fwd, run_dx, run_rest, fwd_bytes, dx_bytes,
+      rest_bytes, total;
 };
 
 int64_t bwd_tokens(const ssd_problem* p) { return (int64_t)p->batch * p->seqlen; }
@@ -382,6 +394,7 @@ BwdWs bwd_layout(const ssd_problem* p) {
   w.gd = take(nt * H);
   w.dtr = take(nt * H);
   w.dyx = take(nt * H);
+  w.xg = take(p->input_dt ? nt * H : 0);
   w.gx = take(nt * H * P);
   w.gb = take(nt * H * N);
   w.gc = take(nt * H * N);
@@ -552,15 +565,18 @@ ssd_status ssd_bmm_chunk(const ssd_problem* p, ssd_tensor C, ssd_tensor B, float
 }
 
 ssd_status ssd_chunk_state(const ssd_problem* p, ssd_tensor x, ssd_tensor B,
-                           const float* dA_cumsum, void* states, hipStream_t stream) {
+                           const float* dA_cumsum, const float* dt_chunk, void* states,
+                           hipStream_t stream) {
   SSD_TRY(check_problem(p));
   SSD_TRY(need_meta(p));
   SSD_TRY(check_vec_tensor(x, "x", has_tokens(p)));
   SSD_TRY(check_vec_tensor(B, "B", has_tokens(p)));
   if (x.dtype != B.dtype) return fail(SSD_ERR_DTYPE, "x and B must share a dtype");
   if (!dA_cumsum || !states) return fail(SSD_ERR_NULL, "dA_cumsum or states is NULL");
+  if (p->input_dt && !dt_chunk) return fail(SSD_ERR_NULL, "input_dt: dt_chunk is NULL");
   ssd::Geo g = make_geo(p, p->chunk_meta);
-  SSD_HIP(ssd::launch_chunk_state(g, targ(x), targ(B), dcode(x.dtype), dA_cumsum, states,
+  SSD_HIP(ssd::launch_chunk_state(g, targ(x), targ(B), dcode(x.dtype), dA_cumsum,
+                                  p->input_dt ? dt_chunk : nullptr, states,
                                   dcode(p->state_dtype), stream),
           "chunk_state launch");
   return ok();
@@ -581,8 +597,9 @@ ssd_status ssd_state_passing(const ssd_problem* p, const void* states, const flo
 }
 
 ssd_status ssd_chunk_scan(const ssd_problem* p, const float* CB, ssd_tensor x, ssd_tensor C,
-                          const float* dA_cumsum, const void* states_in, const float* D,
-                          ssd_tensor z, ssd_tensor out, hipStream_t stream) {
+                          const float* dA_cumsum, const float* dt_chunk,
+                          const void* states_in, const float* D, ssd_tensor z,
+                          ssd_tensor out, hipStream_t stream) {
   SSD_TRY(check_problem(p));
   SSD_TRY(need_meta(p));
   SSD_TRY(check_vec_tensor(x, "x", has_tokens(p)));
@@ -593,8 +610,10 @@ ssd_status ssd_chunk_scan(const ssd_problem* p, const float* CB, ssd_tensor x, s
   if (z.data && z.dtype != x.dtype) return fail(SSD_ERR_DTYPE, "z must have x's dtype");
   if (!CB || !dA_cumsum || !states_in)
     return fail(SSD_ERR_NULL, "CB, dA_cumsum or states_in is NULL");
+  if (p->input_dt && !dt_chunk) return fail(SSD_ERR_NULL, "input_dt: dt_chunk is NULL");
   ssd::Geo g = make_geo(p, p->chunk_meta);
-  SSD_HIP(ssd::launch_chunk_scan(g, CB, targ(x), targ(C), dcode(x.dtype), dA_cumsum, states_in,
+  SSD_HIP(ssd::launch_chunk_scan(g, CB, targ(x), targ(C), dcode(x.dtype), dA_cumsum,
+                                 p->input_dt ? dt_chunk : nullptr, states_in,
                                  dcode(p->state_dtype), D, targ(z), targ(out), dcode(out.dtype),
                                  stream),
           "chunk_scan launch");
@@ -767,10 +786,15 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   SSD_TRY(staged_run(&q.dC, &ra, nullptr, ws_rest, w.rest_bytes, stream));
 
   // 5. gradients
-  SSD_HIP(ssd::launch_bwd_tokens(bg, targ(a->x), in, a->D, f(w.dy), f(w.gx), targ(a->dx),
-                                 f(w.dyx), stream),
+  // (with the step size on the input term, dx and dB carry it and its
+  // gradient gains x . G B)
+  float* dlt = p->input_dt ? f(w.delta) : nullptr;
+  float* xg = p->input_dt ? f(w.xg) : nullptr;
+  SSD_HIP(ssd::launch_bwd_tokens(bg, targ(a->x), in, a->D, f(w.dy), f(w.gx), dlt, targ(a->dx),
+                                 f(w.dyx), xg, stream),
           "backward tokens launch");
-  SSD_HIP(ssd::launch_bwd_group_sums(bg, f(w.gb), f(w.gc), targ(a->dB), targ(a->dC), stream),
+  SSD_HIP(ssd::launch_bwd_group_sums(bg, f(w.gb), f(w.gc), dlt, targ(a->dB), targ(a->dC),
+                                     stream),
           "backward group sums launch");
   const StagedWs lf = staged_layout(&q.fwd), lx = staged_layout(&mdx), lc = staged_layout(&q.dC);
   const int32_t* fwd_meta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws_fwd + lf.meta) : nullptr;
@@ -781,7 +805,8 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
               reinterpret_cast<float*>(ws_rest + lc.cb), f(w.yo), f(w.yf), f(w.xf), f(w.dy),
               f(w.dyx), f(w.delta), f(w.gd), a->A,
               reinterpret_cast<float*>(ws_fwd + lf.st), reinterpret_cast<float*>(ws_dx + lx.st),
-              f(w.gfirst), a->dfinal_states, targ(a->ddt), reinterpret_cast<double*>(ws + w.part),
+              f(w.gfirst), a->dfinal_states, xg, targ(a->ddt),
+              reinterpret_cast<double*>(ws + w.part),
               a->dA, a->ddt_bias, a->D ? a->dD : nullptr, a->dinitial_states, stream),
           "backward step gradients launch");
   return ok();

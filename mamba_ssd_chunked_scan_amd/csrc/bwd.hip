@@ -200,43 +200,53 @@ __global__ __launch_bounds__(256) void k_transpose_states(int nsh, int P, int N,
   }
 }
 
-// ---- per (token, head) row: dx = mirrored dx-scan output + D dy, and dy . x
-// for dD; the row's partial sums meet in LDS and its first thread adds them in
-// order
+// ---- per (token, head) row: dx = f (mirrored dx-scan output G B) + D dy, dy .
+// x for dD and, when the step size f = delta scales the input term, x . G B
+// for its gradient; the row's partial sums meet in LDS and its first thread
+// adds them in order
 __global__ __launch_bounds__(256) void k_tokens(BwdGeo q, TArg x, int x_dtype, const float* D,
-                                                const float* dy, const float* gx_rev, TArg dx,
-                                                float* dyx) {
-  __shared__ double part[256];
+                                                const float* dy, const float* gx_rev,
+                                                const float* delta, TArg dx, float* dyx,
+                                                float* xg) {
+  __shared__ double part[2][256];
   const Row rw = row_of(q.P, q.ntok * q.H);
-  double sx = 0.0;
+  double sx = 0.0, sg = 0.0;
   if (rw.ok) {
     const int tp = rw.row / q.H, h = rw.row % q.H;
     const int64_t o = (int64_t)rw.row * q.P + rw.c;
     const float Dh = D ? D[h] : 0.0f;
+    const float f = delta ? delta[rw.row] : 1.0f;
     const f32x4 xv = load4(x, x_dtype, q, tp, h, rw.c);
     const f32x4 g = *reinterpret_cast<const f32x4*>(gx_rev + ((int64_t)mirror(q, tp) * q.H + h) * q.P + rw.c);
     const f32x4 d = *reinterpret_cast<const f32x4*>(dy + o);
     f32x4 out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      out[i] = g[i] + Dh * d[i];
+      out[i] = f * g[i] + Dh * d[i];
       sx += (double)d[i] * xv[i];
+      sg += (double)xv[i] * g[i];
     }
     *reinterpret_cast<f32x4*>(tok_row_f32(dx, q, tp, h) + rw.c) = out;
   }
-  part[threadIdx.x] = sx;
+  part[0][threadIdx.x] = sx;
+  part[1][threadIdx.x] = sg;
   __syncthreads();
   if (rw.ok && rw.c == 0) {
-    double c = 0.0;
-    for (int k = 0; k < rw.tpr; ++k) c += part[threadIdx.x + k];
+    double c = 0.0, e = 0.0;
+    for (int k = 0; k < rw.tpr; ++k) {
+      c += part[0][threadIdx.x + k];
+      e += part[1][threadIdx.x + k];
+    }
     dyx[rw.row] = (float)c;
+    if (xg) xg[rw.row] = (float)e;
   }
 }
 
 // ---- per (token, group) row: dB and dC summed over the group's heads (dB's
 // scan ran mirrored)
 __global__ __launch_bounds__(256) void k_group_sums(BwdGeo q, const float* gb_rev,
-                                                    const float* gc, TArg dB, TArg dC) {
+                                                    const float* gc, const float* delta,
+                                                    TArg dB, TArg dC) {
   const Row rw = row_of(q.N, q.ntok * q.G);
   if (!rw.ok) return;
   const int tp = rw.row / q.G, g = rw.row % q.G;
@@ -244,7 +254,8 @@ __global__ __launch_bounds__(256) void k_group_sums(BwdGeo q, const float* gb_re
   f32x4 sb = {0.0f, 0.0f, 0.0f, 0.0f}, sc = sb;
   for (int k = 0; k < q.hpg; ++k) {
     const int h = g * q.hpg + k;
-    sb += *reinterpret_cast<const f32x4*>(gb_rev + ((int64_t)tm * q.H + h) * q.N + rw.c);
+    const float f = delta ? delta[(int64_t)tp * q.H + h] : 1.0f;  // (input term's step)
+    sb += f * *reinterpret_cast<const f32x4*>(gb_rev + ((int64_t)tm * q.H + h) * q.N + rw.c);
     sc += *reinterpret_cast<const f32x4*>(gc + ((int64_t)tp * q.H + h) * q.N + rw.c);
   }
   *reinterpret_cast<f32x4*>(tok_row_f32(dB, q, tp, g) + rw.c) = sb;
@@ -335,9 +346,12 @@ __global__ __launch_bounds__(256) void k_mirror_meta(BwdGeo q, int C, int K, int
 // inclusive cumsum of a and Lambda = cs at its last token:
 //   dL/dcs_l = sum_{s<l} M_ls - sum_{l'>l} M_l'l + Q_l - R_l  (+ at the last
 //              token: exp(Lambda) <dS, Hin> + sum_s R_s)
-//   M_ls = exp(cs_l - cs_s) (C_l . B_s) (dy_l . x_s)       (s < l: the diagonal
+//   M_ls = exp(cs_l - cs_s) (C_l . B_s) (dy_l . x_s) f_s   (s < l: the diagonal
 //          terms of the two sums are equal and cancel, so neither holds them)
-//   Q_l  = exp(cs_l) dy_l . (Hin C_l),   R_l = exp(Lambda - cs_l) x_l . (dS B_l)
+//   Q_l  = exp(cs_l) dy_l . (Hin C_l),   R_l = exp(Lambda - cs_l) f_l x_l . (dS B_l)
+// with f the step size where it scales the input term (xg != NULL), else 1;
+// there the step size also reaches the loss through the input, and its
+// gradient gains x_t . G_t B_t (xg, from k_tokens).
 // Hin is the state entering the chunk (forward scan's carry-in), dS the
 // gradient of the state leaving it through later tokens: exp(a_next) G_next
 // (G_next the mirrored dx scan's carry-in for the next chunk) or dfinal at a
@@ -371,10 +385,11 @@ __global__ __launch_bounds__(256) void k_step_dcs(BwdGeo q, Geo gf, const float*
                                                   const float* delta, const float* gd,
                                                   const float* A, const float* fwd_st,
                                                   const float* mir_st, const float* gfirst,
-                                                  const float* dfinal, TArg ddt, double* part,
-                                                  float* dh0) {
+                                                  const float* dfinal, const float* xg, TArg ddt,
+                                                  double* part, float* dh0) {
   __shared__ double lds[4];
   __shared__ float s_a[256];
+  __shared__ float s_f[256];
   __shared__ double s_cs[256];
   __shared__ double s_col[4][256];  // per-wave column sums of M
   __shared__ double s_row[256];     // row sums of M
@@ -398,7 +413,11 @@ __global__ __launch_bounds__(256) void k_step_dcs(BwdGeo q, Geo gf, const float*
   const int tp0 = c.b * q.T + c.t0;  // the chunk's first token on the packed axis
   int s0, s1;
   seq_of(q, tp0, s0, s1);
-  if (tid < len) s_a[tid] = delta[(int64_t)(tp0 + tid) * q.H + h] * Ah;
+  if (tid < len) {
+    const float d = delta[(int64_t)(tp0 + tid) * q.H + h];
+    s_a[tid] = d * Ah;
+    s_f[tid] = xg ? d : 1.0f;
+  }
   __syncthreads();
   if (tid < len) {
     double acc = 0.0;
@@ -452,7 +471,7 @@ __global__ __launch_bounds__(256) void k_step_dcs(BwdGeo q, Geo gf, const float*
         for (int i = 0; i < NI; ++i) {
           const int sc = lane + kWave * i;
           if (sc < l && l < len) {
-            const float m = __expf((float)(csl - s_cs[sc])) * cb[r][i] * dx[r][i];
+            const float m = __expf((float)(csl - s_cs[sc])) * cb[r][i] * dx[r][i] * s_f[sc];
             rp += (double)m;
             col[i] += (double)m;
           }
@@ -507,6 +526,7 @@ __global__ __launch_bounds__(256) void k_step_dcs(BwdGeo q, Geo gf, const float*
       r += s_qr[1][tid * tpr + k];
     }
     const double b = s_col[0][tid] + s_col[1][tid] + s_col[2][tid] + s_col[3][tid];
+    r *= s_f[tid];
     s_dcs[tid] = s_row[tid] - b + qq - r;
     s_r[tid] = r;
   }
@@ -522,7 +542,7 @@ __global__ __launch_bounds__(256) void k_step_dcs(BwdGeo q, Geo gf, const float*
     double da = 0.0;
     for (int k = len - 1; k >= tid; --k) da += s_dcs[k];
     const int64_t it = (int64_t)(tp0 + tid) * q.H + h;
-    const double gg = da * Ah * gd[it];
+    const double gg = (da * Ah + (xg ? (double)xg[it] : 0.0)) * gd[it];
     tok_row_f32(ddt, q, tp0 + tid, h)[0] = (float)gg;
     sa = da * delta[it];
     sb2 = gg;
@@ -623,20 +643,21 @@ hipError_t launch_bwd_transpose_states(int nsh, int P, int N, const float* src, 
 }
 
 hipError_t launch_bwd_tokens(const BwdGeo& q, TArg x, int x_dtype, const float* D,
-                             const float* dy, const float* gx_rev, TArg dx, float* dyx, hipStream_t s) {
+                             const float* dy, const float* gx_rev, const float* delta, TArg dx,
+                             float* dyx, float* xg, hipStream_t s) {
   const int rows = q.ntok * q.H;
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(k_tokens, dim3(row_blocks(rows, q.P)), dim3(256), 0, s, q, x, x_dtype, D,
-                     dy, gx_rev, dx, dyx);
+                     dy, gx_rev, delta, dx, dyx, xg);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_group_sums(const BwdGeo& q, const float* gb_rev, const float* gc, TArg dB,
-                                 TArg dC, hipStream_t s) {
+hipError_t launch_bwd_group_sums(const BwdGeo& q, const float* gb_rev, const float* gc,
+                                 const float* delta, TArg dB, TArg dC, hipStream_t s) {
   const int rows = q.ntok * q.G;
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(k_group_sums, dim3(row_blocks(rows, q.N)), dim3(256), 0, s, q, gb_rev, gc,
-                     dB, dC);
+                     delta, dB, dC);
   return hipGetLastError();
 }
 
@@ -651,14 +672,14 @@ hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* CB
                                  const float* xf, const float* dy,
                                  const float* dyx, const float* delta, const float* gd,
                                  const float* A, const float* fwd_st, const float* mir_st,
-                                 const float* gfirst, const float* dfinal, TArg ddt,
-                                 double* part, float* dA, float* ddt_bias, float* dD, float* dh0,
-                                 hipStream_t s) {
+                                 const float* gfirst, const float* dfinal, const float* xg,
+                                 TArg ddt, double* part, float* dA, float* ddt_bias, float* dD,
+                                 float* dh0, hipStream_t s) {
   if (gf.K > 0) {
     auto kern = gf.C == 32 ? k_step_dcs<32> : gf.C == 64 ? k_step_dcs<64>
               : gf.C == 128 ? k_step_dcs<128> : k_step_dcs<256>;
     hipLaunchKernelGGL(kern, dim3(gf.K, q.H), dim3(256), 0, s, q, gf, CB, DX, yo_f, yo_r, xf, dy,
-                       dyx, delta, gd, A, fwd_st, mir_st, gfirst, dfinal, ddt, part, dh0);
+                       dyx, delta, gd, A, fwd_st, mir_st, gfirst, dfinal, xg, ddt, part, dh0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -1,14 +1,16 @@
 // chunk_scan.hip -- the standalone chunk-scan kernels.  The bf16 body and the
-// LDS helpers live in stage_scan.hpp (shared with the fused forward); fp32
-// inputs use the generic kernel below (fp32 matrix instructions throughout).
+// LDS helpers live in stage_scan.hpp; fp32 inputs use the generic kernel below
+// (fp32 matrix instructions throughout).
 #include "kernels.hpp"
 #include "stage_scan.hpp"
 
 namespace ssd {
 
-template <typename T, typename ST, typename TO>
+// F: the step size scales the input term (dtc is read), compiled in only then.
+template <typename T, typename ST, typename TO, bool F>
 __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* __restrict__ CB, TArg x,
                                                     TArg Cm, const float* __restrict__ cs,
+                                                    const float* __restrict__ dtc,
                                                     const ST* __restrict__ states,
                                                     const float* __restrict__ D, TArg z,
                                                     TArg out, float* __restrict__ yoff) {
@@ -24,13 +26,18 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
   const int r16 = lane % 16, q = lane / 16;
   const ScanLayout lay = scan_layout<T, ST>(C, N);
   float* s_cs = reinterpret_cast<float*>(smem);
+  float* s_f = s_cs + 256;
   T* s_xt = reinterpret_cast<T*>(smem + lay.off_x);
   char* s_h = smem + lay.off_h;
   float* s_y = reinterpret_cast<float*>(smem + lay.off_h);
 
   // ---- stage cumsum, x^T and the carry-in state
   const float* csr = cs + ((int64_t)j * g.H + h) * C;
-  for (int l = tid; l < C; l += 256) s_cs[l] = csr[l];
+  const float* dtr = dtc ? dtc + ((int64_t)j * g.H + h) * C : nullptr;
+  for (int l = tid; l < C; l += 256) {
+    s_cs[l] = csr[l];
+    s_f[l] = dtr ? dtr[l] : 1.0f;
+  }
   const int pw = min(64, P - p0);           // p columns in this block (multiple of 16)
   const int nvec_x = C * 8;                 // C rows x 8 vectors of 8 p
   for (int v = tid; v < nvec_x; v += 256) {
@@ -114,7 +121,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
         for (int e = 0; e < 8; ++e) {
           const int s = s0 + e;
           const bool keep = (s <= lrow) && (s < c.len);
-          m[e] = keep ? fast_exp(csl - s_cs[s]) * cb[e] : 0.0f;
+          m[e] = keep ? fast_exp(csl - s_cs[s]) * cb[e] * (F ? s_f[s] : 1.0f) : 0.0f;
         }
       } else {
 #pragma unroll
@@ -167,80 +174,98 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
   }
 }
 
-template <typename ST, typename TO, int C>
+template <typename ST, typename TO, int C, bool F>
 __global__ __launch_bounds__(256, C <= 128 ? 3 : 2) void k_chunk_scan_bf16(Geo g, const float* __restrict__ CB,
                                                          TArg x, TArg Cm,
                                                          const float* __restrict__ cs,
+                                                         const float* __restrict__ dtc,
                                                          const ST* __restrict__ states,
                                                          const float* __restrict__ D, TArg z,
                                                          TArg out) {
   extern __shared__ __align__(16) char smem[];
-  chunk_scan_block<ST, TO, C>(g, CB, x, Cm, cs, states, D, z, out, blockIdx.x, blockIdx.y,
-                              blockIdx.z, smem);
+  chunk_scan_block<ST, TO, C, F>(g, CB, x, Cm, cs, dtc, states, D, z, out, blockIdx.x,
+                                 blockIdx.y, blockIdx.z, smem);
 }
 
-template <typename ST, typename TO>
-static hipError_t launch_scan_bf16(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
-                                   const void* states, const float* D, TArg z, TArg out,
-                                   hipStream_t s) {
-  const ScanLayout lay = scan_layout_bf16<ST>(g.C, g.N);
-  const void* kern;
-  switch (g.C) {
-    case 32: kern = (const void*)k_chunk_scan_bf16<ST, TO, 32>; break;
-    case 64: kern = (const void*)k_chunk_scan_bf16<ST, TO, 64>; break;
-    case 128: kern = (const void*)k_chunk_scan_bf16<ST, TO, 128>; break;
-    default: kern = (const void*)k_chunk_scan_bf16<ST, TO, 256>; break;
-  }
-  if (lay.bytes > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lay.bytes);
-    if (e != hipSuccess) return e;
-  }
-  dim3 grid(g.K, g.H, (g.P + 63) / 64);
-  const ST* st = (const ST*)states;
-  switch (g.C) {
-    case 32: hipLaunchKernelGGL((k_chunk_scan_bf16<ST, TO, 32>), grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, st, D, z, out); break;
-    case 64: hipLaunchKernelGGL((k_chunk_scan_bf16<ST, TO, 64>), grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, st, D, z, out); break;
-    case 128: hipLaunchKernelGGL((k_chunk_scan_bf16<ST, TO, 128>), grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, st, D, z, out); break;
-    default: hipLaunchKernelGGL((k_chunk_scan_bf16<ST, TO, 256>), grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, st, D, z, out); break;
-  }
-  return hipGetLastError();
-}
-
-template <typename T, typename ST, typename TO>
-static hipError_t launch_scan_t(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
-                                const void* states, const float* D, TArg z, TArg out,
-                                float* yoff, hipStream_t s) {
-  const ScanLayout lay = scan_layout<T, ST>(g.C, g.N);
-  auto kern = k_chunk_scan_generic<T, ST, TO>;
+template <typename ST, typename TO, int C, bool F>
+static hipError_t launch_scan_bf16_c(const Geo& g, const float* CB, TArg x, TArg Cm,
+                                     const float* cs, const float* dtc, const ST* st,
+                                     const float* D, TArg z, TArg out, hipStream_t s) {
+  const ScanLayout lay = scan_layout_bf16<ST>(C, g.N);
+  auto kern = k_chunk_scan_bf16<ST, TO, C, F>;
   if (lay.bytes > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.bytes);
     if (e != hipSuccess) return e;
   }
   dim3 grid(g.K, g.H, (g.P + 63) / 64);
-  hipLaunchKernelGGL(kern, grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, (const ST*)states, D,
-                     z, out, yoff);
+  hipLaunchKernelGGL(kern, grid, dim3(256), lay.bytes, s, g, CB, x, Cm, cs, dtc, st, D, z, out);
   return hipGetLastError();
 }
 
+template <typename ST, typename TO, bool F>
+static hipError_t launch_scan_bf16_f(const Geo& g, const float* CB, TArg x, TArg Cm,
+                                     const float* cs, const float* dtc, const void* states,
+                                     const float* D, TArg z, TArg out, hipStream_t s) {
+  const ST* st = (const ST*)states;
+  switch (g.C) {
+    case 32: return launch_scan_bf16_c<ST, TO, 32, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, s);
+    case 64: return launch_scan_bf16_c<ST, TO, 64, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, s);
+    case 128: return launch_scan_bf16_c<ST, TO, 128, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, s);
+    default: return launch_scan_bf16_c<ST, TO, 256, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, s);
+  }
+}
+
+template <typename ST, typename TO>
+static hipError_t launch_scan_bf16(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
+                                   const float* dtc, const void* states, const float* D, TArg z,
+                                   TArg out, hipStream_t s) {
+  return dtc ? launch_scan_bf16_f<ST, TO, true>(g, CB, x, C, cs, dtc, states, D, z, out, s)
+             : launch_scan_bf16_f<ST, TO, false>(g, CB, x, C, cs, dtc, states, D, z, out, s);
+}
+
+template <typename T, typename ST, typename TO, bool F>
+static hipError_t launch_scan_tf(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
+                                 const float* dtc, const void* states, const float* D, TArg z,
+                                 TArg out, float* yoff, hipStream_t s) {
+  const ScanLayout lay = scan_layout<T, ST>(g.C, g.N);
+  auto kern = k_chunk_scan_generic<T, ST, TO, F>;
+  if (lay.bytes > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.bytes);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid(g.K, g.H, (g.P + 63) / 64);
+  hipLaunchKernelGGL(kern, grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, dtc, (const ST*)states,
+                     D, z, out, yoff);
+  return hipGetLastError();
+}
+
+template <typename T, typename ST, typename TO>
+static hipError_t launch_scan_t(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
+                                const float* dtc, const void* states, const float* D, TArg z,
+                                TArg out, float* yoff, hipStream_t s) {
+  return dtc ? launch_scan_tf<T, ST, TO, true>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
+             : launch_scan_tf<T, ST, TO, false>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
+}
+
 hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
-                             const float* cs, const void* states, int st_dtype,
+                             const float* cs, const float* dtc, const void* states, int st_dtype,
                              const float* D, TArg z, TArg out, int out_dtype, hipStream_t s,
                              float* yoff) {
   if (g.K == 0) return hipSuccess;
   const bool ib = in_dtype == DT_BF16, sb = st_dtype == DT_BF16, ob = out_dtype == DT_BF16;
   if (ib) {
     if (yoff) return hipErrorInvalidValue;  // only the fp32 kernel keeps Y_off
-    if (sb) return ob ? launch_scan_bf16<bf16, bf16>(g, CB, x, C, cs, states, D, z, out, s)
-                      : launch_scan_bf16<bf16, float>(g, CB, x, C, cs, states, D, z, out, s);
-    return ob ? launch_scan_bf16<float, bf16>(g, CB, x, C, cs, states, D, z, out, s)
-              : launch_scan_bf16<float, float>(g, CB, x, C, cs, states, D, z, out, s);
+    if (sb) return ob ? launch_scan_bf16<bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, s)
+                      : launch_scan_bf16<bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, s);
+    return ob ? launch_scan_bf16<float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, s)
+              : launch_scan_bf16<float, float>(g, CB, x, C, cs, dtc, states, D, z, out, s);
   }
-  if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, states, D, z, out, yoff, s)
-                    : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, states, D, z, out, yoff, s);
-  return ob ? launch_scan_t<float, float, bf16>(g, CB, x, C, cs, states, D, z, out, yoff, s)
-            : launch_scan_t<float, float, float>(g, CB, x, C, cs, states, D, z, out, yoff, s);
+  if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
+                    : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
+  return ob ? launch_scan_t<float, float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
+            : launch_scan_t<float, float, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
 }
 
 }  // namespace ssd

@@ -1,6 +1,7 @@
 // chunk_state.hip -- the standalone chunk-state kernels.  The bf16 body lives in
-// stage_state.hpp (shared with the fused forward); fp32 inputs use a simpler
-// slab loop with fp32 matrix instructions (small problems only).
+// stage_state.hpp; fp32 inputs use a simpler slab loop with fp32 matrix
+// instructions.  With the step size on the input term (dtc != NULL) each
+// token's decay weight is multiplied by its step size.
 #include "kernels.hpp"
 #include "stage_state.hpp"
 
@@ -9,9 +10,10 @@ namespace ssd {
 template <typename ST, int C>
 __global__ __launch_bounds__(256, 4) void k_chunk_state_bf16(Geo g, TArg x, TArg B,
                                                           const float* __restrict__ cs,
+                                                          const float* __restrict__ dtc,
                                                           ST* __restrict__ states) {
   __shared__ __align__(16) char smem[chunk_state_lds_bytes<C>()];
-  chunk_state_block<ST, C>(g, x, B, cs, states, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+  chunk_state_block<ST, C>(g, x, B, cs, dtc, states, blockIdx.x, blockIdx.y, blockIdx.z, smem);
 }
 
 // ------------------------------------------------------------------ fp32 path
@@ -26,6 +28,7 @@ struct StateLdsF32 {
 
 __global__ __launch_bounds__(256) void k_chunk_state_f32(Geo g, TArg x, TArg B,
                                                          const float* __restrict__ cs,
+                                                         const float* __restrict__ dtc,
                                                          float* __restrict__ states_f,
                                                          bf16* __restrict__ states_b) {
   __shared__ StateLdsF32 L;
@@ -39,8 +42,10 @@ __global__ __launch_bounds__(256) void k_chunk_state_f32(Geo g, TArg x, TArg B,
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int r16 = lane % 16, q = lane / 16;
   const float* csr = cs + ((int64_t)j * g.H + h) * g.C;
+  const float* dtr = dtc ? dtc + ((int64_t)j * g.H + h) * g.C : nullptr;
   const float last = csr[c.len - 1];
-  for (int s = tid; s < g.C; s += blockDim.x) L.w[s] = s < c.len ? fast_exp(last - csr[s]) : 0.0f;
+  for (int s = tid; s < g.C; s += blockDim.x)
+    L.w[s] = s < c.len ? fast_exp(last - csr[s]) * (dtr ? dtr[s] : 1.0f) : 0.0f;
   __syncthreads();
   const int pt0 = p0 + wave * 16;
   const bool active = pt0 < g.P;
@@ -100,27 +105,27 @@ __global__ __launch_bounds__(256) void k_chunk_state_f32(Geo g, TArg x, TArg B,
 }
 
 template <typename ST>
-static hipError_t launch_state_bf16(const Geo& g, TArg x, TArg B, const float* cs, ST* st,
-                                    hipStream_t s) {
+static hipError_t launch_state_bf16(const Geo& g, TArg x, TArg B, const float* cs,
+                                    const float* dtc, ST* st, hipStream_t s) {
   dim3 grid(g.K, g.H, ((g.P + 63) / 64) * ((g.N + 127) / 128));
   switch (g.C) {
-    case 32: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 32>), grid, dim3(256), 0, s, g, x, B, cs, st); break;
-    case 64: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 64>), grid, dim3(256), 0, s, g, x, B, cs, st); break;
-    case 128: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 128>), grid, dim3(256), 0, s, g, x, B, cs, st); break;
-    default: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 256>), grid, dim3(256), 0, s, g, x, B, cs, st); break;
+    case 32: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 32>), grid, dim3(256), 0, s, g, x, B, cs, dtc, st); break;
+    case 64: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 64>), grid, dim3(256), 0, s, g, x, B, cs, dtc, st); break;
+    case 128: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 128>), grid, dim3(256), 0, s, g, x, B, cs, dtc, st); break;
+    default: hipLaunchKernelGGL((k_chunk_state_bf16<ST, 256>), grid, dim3(256), 0, s, g, x, B, cs, dtc, st); break;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_state(const Geo& g, TArg x, TArg B, int in_dtype, const float* cs,
-                              void* states, int st_dtype, hipStream_t s) {
+                              const float* dtc, void* states, int st_dtype, hipStream_t s) {
   if (g.K == 0) return hipSuccess;
   if (in_dtype == DT_BF16) {
-    if (st_dtype == DT_BF16) return launch_state_bf16<bf16>(g, x, B, cs, (bf16*)states, s);
-    return launch_state_bf16<float>(g, x, B, cs, (float*)states, s);
+    if (st_dtype == DT_BF16) return launch_state_bf16<bf16>(g, x, B, cs, dtc, (bf16*)states, s);
+    return launch_state_bf16<float>(g, x, B, cs, dtc, (float*)states, s);
   }
   dim3 grid(g.K, g.H, ((g.P + 63) / 64) * ((g.N + 127) / 128));
-  hipLaunchKernelGGL(k_chunk_state_f32, grid, dim3(256), 0, s, g, x, B, cs,
+  hipLaunchKernelGGL(k_chunk_state_f32, grid, dim3(256), 0, s, g, x, B, cs, dtc,
                      st_dtype == DT_BF16 ? nullptr : (float*)states,
                      st_dtype == DT_BF16 ? (bf16*)states : nullptr);
   return hipGetLastError();

@@ -105,9 +105,10 @@ template <int NT> struct FCfg {
   static constexpr int BLD = NMAX + SSD_FUSED_BPAD;  // bf16 per row of the B tile in LDS
   static constexpr int HLD = NMAX + SSD_FUSED_HPAD;  // bf16 per carry-in row in LDS
   static constexpr int OFF_CS = 0;             // cs[128]
-  static constexpr int OFF_W = 512;            // w[128] = exp(Lambda - cs)
-  static constexpr int OFF_MISC = 1024;        // broadcast words
-  static constexpr int OFF_X = 1088;           // x [128 s][FXLD]
+  static constexpr int OFF_W = 512;            // w[128] = exp(Lambda - cs) (times delta)
+  static constexpr int OFF_CSC = 1024;         // csc[128]: cs as a column (source) index
+  static constexpr int OFF_MISC = 1536;        // broadcast words
+  static constexpr int OFF_X = 1600;           // x [128 s][FXLD]
   static constexpr int X_BYTES = FC * FXLD * 2;
   static constexpr int OFF_R = OFF_X + X_BYTES;     // B, then carry-in, then y
   static constexpr int B_BYTES = FC * BLD * 2;
@@ -128,7 +129,7 @@ struct FusedArgs {
   const float* D;
   const float* h0;
   float* hfinal;
-  int softplus, clamp;
+  int softplus, clamp, input_dt;
   float dt_min, dt_max;
   int U, PS, R;           // units, P slabs per head, chunks per range
   uint32_t* sync;         // [0] ticket counter, [1] error bits, [2 + r * U + u] flags
@@ -143,6 +144,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   __shared__ __align__(16) char smem[Cfg::LDS];
   float* s_cs = reinterpret_cast<float*>(smem + Cfg::OFF_CS);
   float* s_w = reinterpret_cast<float*>(smem + Cfg::OFF_W);
+  float* s_csc = reinterpret_cast<float*>(smem + Cfg::OFF_CSC);
   uint32_t* s_misc = reinterpret_cast<uint32_t*>(smem + Cfg::OFF_MISC);
   bf16* s_x = reinterpret_cast<bf16*>(smem + Cfg::OFF_X);
   bf16* s_b = reinterpret_cast<bf16*>(smem + Cfg::OFF_R);
@@ -289,14 +291,16 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   // hardware 2^x of a difference.
   auto stage_cs = [&](const Stage& st, const Chunk& c) {
     if (wave == 0) {
-      float av[2];
+      float av[2], dv[2];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const float uu = from_bits<TDt>(st.dt[e]) + bias;
         float d = uu;
         if (a.softplus) d = fmaxf(uu, 0.0f) + __logf(1.0f + __expf(-fabsf(uu)));
         if (a.clamp) d = fminf(fmaxf(d, a.dt_min), a.dt_max);
-        av[e] = 2 * lane + e < c.len ? d * Ah2 : 0.0f;
+        const bool in = 2 * lane + e < c.len;
+        av[e] = in ? d * Ah2 : 0.0f;
+        dv[e] = in && a.input_dt ? d : 1.0f;
       }
       const float pair = av[0] + av[1];
       const float incl = wave_inclusive_sum_dpp(pair);
@@ -306,8 +310,13 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       const int ll = c.len - 1;
       const float lam = __int_as_float(
           __builtin_amdgcn_readlane(__float_as_int((ll & 1) ? c1 : c0), ll >> 1));
-      s_w[2 * lane] = 2 * lane < c.len ? fast_exp2(lam - c0) : 0.0f;
-      s_w[2 * lane + 1] = 2 * lane + 1 < c.len ? fast_exp2(lam - c1) : 0.0f;
+      s_w[2 * lane] = 2 * lane < c.len ? fast_exp2(lam - c0) * dv[0] : 0.0f;
+      s_w[2 * lane + 1] = 2 * lane + 1 < c.len ? fast_exp2(lam - c1) * dv[1] : 0.0f;
+      // the source side of the decay exponent: with the step size on the input
+      // term, exp2(cs_l - cs_s) delta_s = exp2(cs_l - (cs_s - log2 delta_s))
+      // (delta >= 0 here; log2(0) = -inf gives the weight 0)
+      s_csc[2 * lane] = a.input_dt ? c0 - __log2f(dv[0]) : c0;
+      s_csc[2 * lane + 1] = a.input_dt ? c1 - __log2f(dv[1]) : c1;
       if (lane == 0) s_misc[1] = __float_as_uint(lam);
     }
   };
@@ -653,8 +662,8 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
         // M in the accumulator layout (lane: one l, tokens 4 q + 0..3 of each
         // s-tile), used as the A operand with the tokens in that order; x is
         // read from the x tile in the same order
-        const f32x4 csa = *reinterpret_cast<const f32x4*>(&s_cs[sa * 16 + q * 4]);
-        const f32x4 csb = *reinterpret_cast<const f32x4*>(&s_cs[sb * 16 + q * 4]);
+        const f32x4 csa = *reinterpret_cast<const f32x4*>(&s_csc[sa * 16 + q * 4]);
+        const f32x4 csb = *reinterpret_cast<const f32x4*>(&s_csc[sb * 16 + q * 4]);
         f32x8 m;
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
@@ -792,6 +801,7 @@ hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s) {
   a.x = f.x; a.B = f.B; a.C = f.C; a.dt = f.dt; a.z = f.z; a.out = f.out;
   a.A = f.A; a.dt_bias = f.dt_bias; a.D = f.D; a.h0 = f.h0; a.hfinal = f.hfinal;
   a.softplus = f.softplus; a.clamp = f.clamp; a.dt_min = f.dt_min; a.dt_max = f.dt_max;
+  a.input_dt = f.input_dt;
   a.U = pl.U; a.PS = pl.PS; a.R = pl.R;
   a.sync = f.sync; a.edec = f.edec; a.agg = f.agg;
   const dim3 grid((unsigned)(pl.nr * pl.U));

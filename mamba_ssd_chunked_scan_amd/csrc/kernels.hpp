@@ -22,8 +22,9 @@ hipError_t launch_chunk_cumsum(const Geo& g, TArg dt, int dt_dtype, const float*
 hipError_t launch_bmm_chunk(const Geo& g, TArg C, TArg B, int in_dtype, float* CB,
                             hipStream_t s);
 
+// dtc: step size per position (K, H, C) when it scales the input term, or NULL
 hipError_t launch_chunk_state(const Geo& g, TArg x, TArg B, int in_dtype, const float* cs,
-                              void* states, int st_dtype, hipStream_t s);
+                              const float* dtc, void* states, int st_dtype, hipStream_t s);
 
 hipError_t launch_state_passing(const Geo& g, const void* states, int st_dtype,
                                 const float* cs, const float* h0, void* states_out,
@@ -33,7 +34,7 @@ hipError_t launch_state_passing(const Geo& g, const void* states, int st_dtype,
 // the output, exp(cs_l) C_l . h_in, before the skip and the gate, as (tokens,
 // H, P) fp32 on the packed axis
 hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
-                             const float* cs, const void* states, int st_dtype,
+                             const float* cs, const float* dtc, const void* states, int st_dtype,
                              const float* D, TArg z, TArg out, int out_dtype, hipStream_t s,
                              float* yoff = nullptr);
 
@@ -59,7 +60,7 @@ struct FusedLaunch {
   const float* D;
   const float* h0;
   float* hfinal;
-  int softplus, clamp;
+  int softplus, clamp, input_dt;
   float dt_min, dt_max;
   FusedPlan plan;
   uint32_t* sync;          // 2 + nr * U words
@@ -86,9 +87,10 @@ hipError_t launch_bwd_steps(const BwdGeo& q, TArg dt, int dt_dtype, const float*
 hipError_t launch_bwd_transpose_states(int nsh, int P, int N, const float* src, float* dst,
                                        hipStream_t s);
 hipError_t launch_bwd_tokens(const BwdGeo& q, TArg x, int x_dtype, const float* D,
-                             const float* dy, const float* gx_rev, TArg dx, float* dyx, hipStream_t s);
-hipError_t launch_bwd_group_sums(const BwdGeo& q, const float* gb_rev, const float* gc, TArg dB,
-                                 TArg dC, hipStream_t s);
+                             const float* dy, const float* gx_rev, const float* delta, TArg dx,
+                             float* dyx, float* xg, hipStream_t s);
+hipError_t launch_bwd_group_sums(const BwdGeo& q, const float* gb_rev, const float* gc,
+                                 const float* delta, TArg dB, TArg dC, hipStream_t s);
 // the mirrored scans' chunk table (and, in batch mode, cu = {0, T, 2T, ..})
 hipError_t launch_bwd_mirror_meta(const BwdGeo& q, int C, int K, int32_t* meta, int32_t* cu_out,
                                  hipStream_t s);
@@ -99,8 +101,8 @@ hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* CB
                                  const float* xf, const float* dy,
                                  const float* dyx, const float* delta, const float* gd,
                                  const float* A, const float* fwd_st, const float* mir_st,
-                                 const float* gfirst, const float* dfinal, TArg ddt,
-                                 double* part, float* dA, float* ddt_bias, float* dD, float* dh0,
-                                 hipStream_t s);
+                                 const float* gfirst, const float* dfinal, const float* xg,
+                                 TArg ddt, double* part, float* dA, float* ddt_bias, float* dD,
+                                 float* dh0, hipStream_t s);
 
 }  // namespace ssd

@@ -1,18 +1,19 @@
 // stage_scan.hpp -- stage 5: the output of every position of every chunk,
 //
 //   y[l] = exp(cs[l]) * C_l . Hin[j]                              (Y_off)
-//        + sum_{s <= l} exp(cs[l] - cs[s]) CB[l, s] x_s            (Y_diag)
+//        + sum_{s <= l} exp(cs[l] - cs[s]) CB[l, s] f_s x_s        (Y_diag)
 //        + D_h x_l;            out = y * silu(z)   when z is given
 //
 // SSD Reference: "Intra-chunk outputs and per-chunk states" (segment matrix
 // L[l, s] = exp(A_cumsum[l] - A_cumsum[s]) 1[l >= s], Y_diag = (L o CB) X) and
 // "Readout" (Y_off = C . state . exp(A_cumsum), Y = Y_diag + Y_off); the skip
-// and SiLU gate of cudnn-frontend PR 1133.  The mask is applied by selecting
+// and SiLU gate of cudnn-frontend PR 1133.  f_s is the step size of token s
+// when it scales the input term (dtc != NULL), else 1.  The mask is applied by selecting
 // before exponentiating, so exp never sees the positive exponents above the
 // diagonal (exp(large) * 0 would be inf * 0).
 //
 // One workgroup per (chunk, head, 64-wide slice of P).  LDS holds the chunk's
-// cumsum, x transposed ([p][s], the reduction axis contiguous for the Y_diag
+// cumsum and f, x transposed ([p][s], the reduction axis contiguous for the Y_diag
 // B operand) and the carry-in state ([p][n], split into bf16 hi + lo when it is
 // stored in fp32).  Wave w owns the 16-row l-tiles w and 7 - w of every group
 // of 8 (balancing the causal triangle) and all four p-tiles.  The decay-weighted
@@ -97,7 +98,7 @@ __host__ __device__ inline ScanLayout scan_layout(int C, int N) {
   ScanLayout L;
   L.ldx = C + xt_pad<T>();
   L.ldy = 64 + 4;
-  L.off_x = 1024;  // cs: up to 256 floats
+  L.off_x = 2048;  // cs, then f: up to 256 floats each
   const size_t xbytes = 64ull * L.ldx * sizeof(T);
   L.off_h = (L.off_x + xbytes + 15) & ~size_t(15);
   const size_t hb = HinLds<T, ST>::bytes(N);
@@ -136,7 +137,7 @@ __host__ __device__ inline ScanLayout scan_layout_bf16(int C, int N) {
   ScanLayout L;
   L.ldx = (C + 8) / 2;  // dwords
   L.ldy = 64 + 4;
-  L.off_x = 1024;
+  L.off_x = 2048;  // cs, then f
   const size_t xbytes = 64ull * L.ldx * 4;
   L.off_h = (L.off_x + xbytes + 15) & ~size_t(15);
   const size_t hb = HinLds<bf16, ST>::bytes(N);
@@ -154,10 +155,12 @@ struct ScanFrags {
 
 // One workgroup computes the outputs of (chunk j, head h, columns [64 pz,
 // 64 pz + 64) of P); smem holds scan_layout_bf16<ST>(C, N).bytes bytes.
-template <typename ST, typename TO, int C>
+// F: the step size scales the input term (dtc is read), compiled in only then.
+template <typename ST, typename TO, int C, bool F>
 __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, const TArg& x,
                                                  const TArg& Cm, const float* cs,
-                                                 const ST* states, const float* D, const TArg& z,
+                                                 const float* dtc, const ST* states,
+                                                 const float* D, const TArg& z,
                                                  const TArg& out, int j, int h, int pz,
                                                  char* smem) {
   using Cfg = ScanCfg<C>;
@@ -172,6 +175,7 @@ __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, 
   const int r16 = lane % 16, q = lane / 16;
   const ScanLayout lay = scan_layout_bf16<ST>(C, N);
   float* s_cs = reinterpret_cast<float*>(smem);
+  float* s_f = s_cs + 256;
   uint32_t* s_xt = reinterpret_cast<uint32_t*>(smem + lay.off_x);
   char* s_h = smem + lay.off_h;
   float* s_y = reinterpret_cast<float*>(smem + lay.off_h);
@@ -240,7 +244,11 @@ __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, 
     }
   }
   const float* csr = cs + ((int64_t)j * g.H + h) * C;
-  for (int l = tid; l < C; l += 256) s_cs[l] = csr[l];
+  const float* dtr = dtc ? dtc + ((int64_t)j * g.H + h) * C : nullptr;
+  for (int l = tid; l < C; l += 256) {
+    s_cs[l] = csr[l];
+    s_f[l] = dtr ? dtr[l] : 1.0f;
+  }
 #pragma unroll
   for (int k = 0; k < Cfg::XU; ++k) {
     const int u = tid + 256 * k;
@@ -340,6 +348,11 @@ __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, 
           const bool keep = lok && (s <= lrow) && (s < c.len);
           const float ex = fast_exp(keep ? csl - csv[e] : 0.0f);
           m[e] = keep ? ex * cbv[kk][e] : 0.0f;
+        }
+        if constexpr (F) {
+          const f32x8 fv = Vec8<float>::load(s_f + s0);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) m[e] *= fv[e];
         }
         const FragSplit mf = split_f32x8(m);
 #pragma unroll

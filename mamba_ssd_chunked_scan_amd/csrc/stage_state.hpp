@@ -58,8 +58,8 @@ template <int C> __host__ __device__ constexpr size_t chunk_state_lds_bytes() {
 // (chunk j, head h); smem holds chunk_state_lds_bytes<C>() bytes.
 template <typename ST, int C>
 __device__ __forceinline__ void chunk_state_block(const Geo& g, const TArg& x, const TArg& B,
-                                                  const float* cs, ST* states, int j, int h,
-                                                  int z, char* smem) {
+                                                  const float* cs, const float* dtc, ST* states,
+                                                  int j, int h, int z, char* smem) {
   using Cfg = StateCfg<C>;
   constexpr int SL = Cfg::SL, NPAIR = Cfg::NPAIR, LDW = Cfg::LDW, XU = Cfg::XU, BU = Cfg::BU;
   uint32_t* lds = reinterpret_cast<uint32_t*>(smem);
@@ -144,8 +144,10 @@ __device__ __forceinline__ void chunk_state_block(const Geo& g, const TArg& x, c
   load_slab(0);
   {
     const float* csr = cs + ((int64_t)j * g.H + h) * g.C;
+    const float* dtr = dtc ? dtc + ((int64_t)j * g.H + h) * g.C : nullptr;
     const float last = csr[c.len - 1];
-    for (int s = tid; s < C; s += 256) w[s] = s < c.len ? fast_exp(last - csr[s]) : 0.0f;
+    for (int s = tid; s < C; s += 256)
+      w[s] = s < c.len ? fast_exp(last - csr[s]) * (dtr ? dtr[s] : 1.0f) : 0.0f;
   }
   __syncthreads();
 

@@ -48,7 +48,7 @@ class SsdProblem(ctypes.Structure):
                 ("cu_seqlens", ctypes.c_void_p), ("chunk_meta", ctypes.c_void_p),
                 ("dt_softplus", ctypes.c_int32), ("dt_clamp", ctypes.c_int32),
                 ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float),
-                ("state_dtype", ctypes.c_int)]
+                ("state_dtype", ctypes.c_int), ("input_dt", ctypes.c_int32)]
 
 
 class SsdFwdArgs(ctypes.Structure):
@@ -97,9 +97,9 @@ def lib():
                                                  P(ctypes.c_int32), ctypes.c_size_t]
         L.ssd_chunk_cumsum.argtypes = [P(SsdProblem), SsdTensor, vp, vp, vp, vp, vp]
         L.ssd_bmm_chunk.argtypes = [P(SsdProblem), SsdTensor, SsdTensor, vp, vp]
-        L.ssd_chunk_state.argtypes = [P(SsdProblem), SsdTensor, SsdTensor, vp, vp, vp]
+        L.ssd_chunk_state.argtypes = [P(SsdProblem), SsdTensor, SsdTensor, vp, vp, vp, vp]
         L.ssd_state_passing.argtypes = [P(SsdProblem), vp, vp, vp, vp, vp, vp]
-        L.ssd_chunk_scan.argtypes = [P(SsdProblem), vp, SsdTensor, SsdTensor, vp, vp, vp,
+        L.ssd_chunk_scan.argtypes = [P(SsdProblem), vp, SsdTensor, SsdTensor, vp, vp, vp, vp,
                                      SsdTensor, SsdTensor, vp]
         L.ssd_forward.argtypes = [P(SsdProblem), ctypes.c_int, P(SsdFwdArgs), vp,
                                   ctypes.c_size_t, vp]
@@ -188,6 +188,7 @@ class Problem:
     dt_softplus: bool = True
     dt_limit: tuple | None = None
     state_dtype: torch.dtype = torch.float32
+    input_dt: bool = False                     # step size on the input term too
 
     def c(self) -> SsdProblem:
         p = SsdProblem()
@@ -201,6 +202,7 @@ class Problem:
         else:
             p.dt_clamp, p.dt_min, p.dt_max = 1, float(self.dt_limit[0]), float(self.dt_limit[1])
         p.state_dtype = _dtype_code(self.state_dtype)
+        p.input_dt = 1 if self.input_dt else 0
         return p
 
     @property
@@ -283,14 +285,15 @@ def ssd_bmm_chunk(prob: Problem, C, B, CB=None, stream=None):
     return CB
 
 
-def ssd_chunk_state(prob: Problem, x, B, dA_cumsum, states=None, stream=None):
+def ssd_chunk_state(prob: Problem, x, B, dA_cumsum, states=None, dt_chunk=None, stream=None):
+    """dt_chunk: ssd_chunk_cumsum's dt_out, required when prob.input_dt."""
     K = prob.num_chunks()
     if states is None:
         states = torch.empty((K, prob.nheads, prob.headdim, prob.dstate),
                              dtype=prob.state_dtype, device=x.device)
     _check(lib().ssd_chunk_state(ctypes.byref(prob.c()), tensor_arg(x, prob.packed),
                                  tensor_arg(B, prob.packed), dA_cumsum.data_ptr(),
-                                 states.data_ptr(), _stream(stream)))
+                                 _ptr(dt_chunk), states.data_ptr(), _stream(stream)))
     return states
 
 
@@ -309,12 +312,14 @@ def ssd_state_passing(prob: Problem, states, dA_cumsum, initial_states=None, sta
 
 
 def ssd_chunk_scan(prob: Problem, CB, x, C, dA_cumsum, states_in, D=None, z=None, out=None,
-                   out_dtype=None, stream=None):
+                   out_dtype=None, dt_chunk=None, stream=None):
+    """dt_chunk: ssd_chunk_cumsum's dt_out, required when prob.input_dt."""
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     _check(lib().ssd_chunk_scan(ctypes.byref(prob.c()), CB.data_ptr(),
                                 tensor_arg(x, prob.packed), tensor_arg(C, prob.packed),
-                                dA_cumsum.data_ptr(), states_in.data_ptr(), _ptr(D),
+                                dA_cumsum.data_ptr(), _ptr(dt_chunk), states_in.data_ptr(),
+                                _ptr(D),
                                 tensor_arg(z, prob.packed), tensor_arg(out, prob.packed),
                                 _stream(stream)))
     return out
@@ -323,15 +328,16 @@ def ssd_chunk_scan(prob: Problem, CB, x, C, dA_cumsum, states_in, D=None, z=None
 def ssd_forward(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=None,
                 cu_seqlens=None, chunk_size=128, dt_softplus=True, dt_limit=None,
                 state_dtype=torch.float32, out=None, out_dtype=None, final_states=None,
-                algo="staged", workspace=None, stream=None):
+                algo="staged", workspace=None, stream=None, input_dt=False):
     """The whole forward pass; returns (out, final_states).
 
     Batch mode: x (b, T, H, P), B and C (b, T, G, N), dt (b, T, H), z like x,
     initial_states (b, H, P, N) float32.  Packed mode: the same without the batch
-    axis plus ``cu_seqlens`` (device int32, nseq + 1).
+    axis plus ``cu_seqlens`` (device int32, nseq + 1).  ``input_dt`` puts the
+    step size on the input term as well (delta x (outer) B).
     """
     prob = problem_from(x, B, chunk_size, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
-                        dt_limit=dt_limit, state_dtype=state_dtype)
+                        dt_limit=dt_limit, state_dtype=state_dtype, input_dt=input_dt)
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
     if final_states is None:
@@ -370,12 +376,12 @@ class Grads:
 
 def ssd_backward(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_states=None,
                  dfinal_states=None, cu_seqlens=None, chunk_size=128, dt_softplus=True,
-                 dt_limit=None, workspace=None, stream=None) -> Grads:
+                 dt_limit=None, workspace=None, stream=None, input_dt=False) -> Grads:
     """Gradients of sum(dout * out) + sum(dfinal_states * final_states) with
     respect to every input of ``ssd_forward`` (same arguments and layouts);
     all gradients are float32."""
     prob = problem_from(x, B, chunk_size, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
-                        dt_limit=dt_limit)
+                        dt_limit=dt_limit, input_dt=input_dt)
     dev, f32 = x.device, torch.float32
     nseq = prob.nseq if prob.packed else prob.batch
     g = Grads(dx=torch.empty(x.shape, dtype=f32, device=dev),

@@ -26,10 +26,9 @@
  *   - packed variable-length batches, where the state restarts at every
  *     sequence boundary (vLLM PR 27299 "Test Plan": continuous batching);
  *   - optionally (input_dt = 1) the step size on the input term as well,
- *     S = exp(a) S + delta x (outer) B, the discretisation the Mamba-2 models
- *     timed on these pages use (vLLM PR 27299 "Purpose": the Mamba-2 SSD
- *     stages of production models); the pages write the recurrence without it,
- *     so it is an option, off by default.  The D skip keeps the raw x.
+ *     S = exp(a) S + delta x (outer) B, the way Mamba-2 implementations
+ *     discretise the input; the pages write the recurrence without it, so it
+ *     is an option, off by default.  The D skip keeps the raw x.
  *
  * The state of one (sequence, head) is a P x N matrix S[p][n] (head dim
  * before state dim, SSD Reference "Shape contract").  Per token:

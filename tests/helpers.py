@@ -90,10 +90,12 @@ def device_inputs(inp: Inputs, dtype, packed_xbc=False, device="cuda"):
     return d
 
 
-def oracle_run(inp: Inputs, chunk_size=0, dt_limit=None, dt_softplus=True, threads=None):
+def oracle_run(inp: Inputs, chunk_size=0, dt_limit=None, dt_softplus=True, threads=None,
+               input_dt=False):
     return oracle.ssd_fwd(inp.x, inp.B, inp.C, inp.dt, inp.A, inp.dt_bias, inp.D, inp.z,
                           inp.initial_states, cu_seqlens=inp.cu_seqlens, dt_softplus=dt_softplus,
-                          dt_limit=dt_limit, chunk_size=chunk_size, threads=threads)
+                          dt_limit=dt_limit, chunk_size=chunk_size, threads=threads,
+                          input_dt=input_dt)
 
 
 def small_workload(name="small", batch=1, seqlen=300, nheads=4, headdim=32, ngroups=2,
