@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
   const int r16 = lane % 16, q = lane / 16;
   const ScanLayout lay = scan_layout<T, ST>(C, N);
   float* s_cs = reinterpret_cast<float*>(smem);
-  float* s_f = s_cs + 256;
+  float* s_f = s_cs + C;
   T* s_xt = reinterpret_cast<T*>(smem + lay.off_x);
   char* s_h = smem + lay.off_h;
   float* s_y = reinterpret_cast<float*>(smem + lay.off_h);

@@ -98,7 +98,7 @@ __host__ __device__ inline ScanLayout scan_layout(int C, int N) {
   ScanLayout L;
   L.ldx = C + xt_pad<T>();
   L.ldy = 64 + 4;
-  L.off_x = 2048;  // cs, then f: up to 256 floats each
+  L.off_x = 8 * C;  // cs, then f: C floats each
   const size_t xbytes = 64ull * L.ldx * sizeof(T);
   L.off_h = (L.off_x + xbytes + 15) & ~size_t(15);
   const size_t hb = HinLds<T, ST>::bytes(N);
@@ -137,7 +137,9 @@ __host__ __device__ inline ScanLayout scan_layout_bf16(int C, int N) {
   ScanLayout L;
   L.ldx = (C + 8) / 2;  // dwords
   L.ldy = 64 + 4;
-  L.off_x = 2048;  // cs, then f
+  // cs, then f: C floats each (at C = 128 this keeps three workgroups' LDS
+  // within a CU's 160 KB)
+  L.off_x = 8 * C;
   const size_t xbytes = 64ull * L.ldx * 4;
   L.off_h = (L.off_x + xbytes + 15) & ~size_t(15);
   const size_t hb = HinLds<bf16, ST>::bytes(N);
@@ -175,7 +177,7 @@ __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, 
   const int r16 = lane % 16, q = lane / 16;
   const ScanLayout lay = scan_layout_bf16<ST>(C, N);
   float* s_cs = reinterpret_cast<float*>(smem);
-  float* s_f = s_cs + 256;
+  float* s_f = s_cs + C;
   uint32_t* s_xt = reinterpret_cast<uint32_t*>(smem + lay.off_x);
   char* s_h = smem + lay.off_h;
   float* s_y = reinterpret_cast<float*>(smem + lay.off_h);
