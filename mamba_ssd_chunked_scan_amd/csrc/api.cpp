@@ -319,6 +319,22 @@ ssd_status staged_run(const ssd_problem* p, const ssd_fwd_args* a, const int32_t
 
 // ---------------------------------------------------------------- backward
 
+// The chunk scan of a backward run whose chunk states are another run's
+// carry-in states, stored transposed, and whose cumsum is that run's too:
+// C.B^T, then the chunk scan reading the states transposed.  fp32 operands.
+ssd_status transposed_scan(const ssd_problem* p, const ssd_fwd_args* a, const int32_t* meta,
+                           const float* cs, const float* dtc, const float* states, float* cb,
+                           hipStream_t stream) {
+  const ssd::Geo g = make_geo(p, meta);
+  const int in = dcode(a->x.dtype);
+  SSD_HIP(ssd::launch_bmm_chunk(g, targ(a->C), targ(a->B), in, cb, stream), "bmm_chunk launch");
+  SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, dtc, states,
+                                 dcode(SSD_F32), nullptr, targ(a->z), targ(a->out),
+                                 dcode(a->out.dtype), stream, nullptr, 1),
+          "chunk_scan launch");
+  return ok();
+}
+
 // The problems of the forward recompute and the three backward scans (see
 // bwd.hip): fwd and dC keep the step definition (softplus, clamp) of the
 // caller's problem, dx and dB take precomputed steps; dB and dC run on the
@@ -360,9 +376,8 @@ BwdProblems bwd_problems(const ssd_problem* p) {
 }
 
 struct BwdWs {
-  size_t yf, yo, dy, dyr, Cr, Br, Cf, Bf, Cer, Be, xr, xf, delta, gd, dtr, dyx, xg, gx, gb, gc,
-      gfirst, dfT, h0T, mmeta, mcu, part, run_fwd, run_dx, run_rest, fwd_bytes, dx_bytes,
-      rest_bytes, total;
+  size_t yf, yo, dy, dyr, Cr, Br, Cer, Be, xr, xf, delta, gd, dtr, dyx, xg, gx, gb, gc,
+      gfirst, mmeta, mcu, part, run_fwd, run_dx, run_rest, fwd_bytes, dx_bytes, rest_bytes, total;
 };
 
 int64_t bwd_tokens(const ssd_problem* p) { return (int64_t)p->batch * p->seqlen; }
@@ -384,8 +399,6 @@ BwdWs bwd_layout(const ssd_problem* p) {
   w.dyr = take(nt * H * P);
   w.Cr = take(nt * G * N);
   w.Br = take(nt * G * N);
-  w.Cf = take(nt * G * N);
-  w.Bf = take(nt * G * N);
   w.Cer = take(nt * H * N);
   w.Be = take(nt * H * N);
   w.xr = take(nt * H * P);
@@ -399,8 +412,6 @@ BwdWs bwd_layout(const ssd_problem* p) {
   w.gb = take(nt * H * N);
   w.gc = take(nt * H * N);
   w.gfirst = take(ns * H * P * N);
-  w.dfT = take(ns * H * P * N);
-  w.h0T = take(ns * H * P * N);
   const BwdProblems q = bwd_problems(p);
   const ssd_problem mdx = mirrored(q.dx, p), mdB = mirrored(q.dB, p);
   w.mmeta = off;
@@ -411,11 +422,16 @@ BwdWs bwd_layout(const ssd_problem* p) {
   w.part = off;
   off += align256((size_t)num_chunks(p) * H * 3 * sizeof(double));
   // the forward recompute and the mirrored dx scan keep their workspaces (the
-  // step-size gradients read their chunk states and the forward's C.B^T); the
-  // dB and dC scans share one, dC last (its C.B^T, dy.x^T, is read too)
+  // dB and dC scans read their cumsums and chunk states, the step-size
+  // gradients their chunk states and the forward's C.B^T); the dB and dC
+  // scans need only a C.B^T buffer, shared, dC last (its C.B^T, dy.x^T, is
+  // read by the step-size gradients too)
   w.fwd_bytes = staged_layout(&q.fwd).total;
   w.dx_bytes = staged_layout(&mdx).total;
-  w.rest_bytes = std::max(staged_layout(&mdB).total, staged_layout(&q.dC).total);
+  auto cb_bytes = [](const ssd_problem* r) {
+    return (size_t)num_chunks(r) * r->ngroups * r->chunk_size * r->chunk_size * sizeof(float);
+  };
+  w.rest_bytes = std::max(cb_bytes(&mdB), cb_bytes(&q.dC));
   w.run_fwd = off;
   off += align256(w.fwd_bytes);
   w.run_dx = off;
@@ -706,20 +722,21 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   const int in = dcode(a->x.dtype);
   struct Copy { ssd_tensor src; int R, W, rep, rev; size_t dst; };
   const Copy copies[] = {{a->C, G, N, 1, 1, w.Cr},     {a->B, G, N, 1, 1, w.Br},
-                         {a->C, G, N, 1, 0, w.Cf},     {a->B, G, N, 1, 0, w.Bf},
                          {a->C, H, N, H / G, 1, w.Cer}, {a->B, H, N, H / G, 0, w.Be},
                          {a->x, H, P, 1, 1, w.xr},     {a->x, H, P, 1, 0, w.xf}};
   for (const Copy& c : copies)
     SSD_HIP(ssd::launch_bwd_gather(bg, targ(c.src), in, c.R, c.W, c.rep, c.rev, f(c.dst), stream),
             "backward gather launch");
 
-  // 2. forward recompute in fp32: y before the gate (for dz), its inter-chunk
-  // part exp(cs_l) C_l . h_in (for the step sizes), and the carry-in state of
-  // every chunk, kept in its workspace
+  // 2. forward recompute on the caller's operands (bf16 inputs take the bf16
+  // kernels, whose derived operands are split hi + lo: fp32-accurate), with
+  // fp32 states and output: y before the gate (for dz), its inter-chunk part
+  // exp(cs_l) C_l . h_in (for the step sizes), and the carry-in state of every
+  // chunk, kept in its workspace
   ssd_fwd_args fa;
-  fa.x = scratch_view(f(w.xf), p, H, P);
-  fa.B = scratch_view(f(w.Bf), p, G, N);
-  fa.C = scratch_view(f(w.Cf), p, G, N);
+  fa.x = a->x;
+  fa.B = a->B;
+  fa.C = a->C;
   fa.dt = a->dt;
   fa.A = a->A; fa.dt_bias = a->dt_bias; fa.D = a->D; fa.z = none;
   fa.initial_states = a->initial_states;
@@ -735,12 +752,6 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
                                 p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, f(w.delta),
                                 f(w.gd), f(w.dtr), stream),
           "backward steps launch");
-  if (a->dfinal_states)
-    SSD_HIP(ssd::launch_bwd_transpose_states(ns * H, P, N, a->dfinal_states, f(w.dfT), stream),
-            "backward transpose launch");
-  if (a->initial_states)
-    SSD_HIP(ssd::launch_bwd_transpose_states(ns * H, P, N, a->initial_states, f(w.h0T), stream),
-            "backward transpose launch");
   ssd_problem mdx = mirrored(q.dx, p), mdB = mirrored(q.dB, p);
   int32_t* mmeta = reinterpret_cast<int32_t*>(ws + w.mmeta);
   int32_t* mcu = p->nseq > 0 ? const_cast<int32_t*>(p->cu_seqlens)
@@ -769,21 +780,26 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   ra.final_states = f(w.gfirst);
   // (its inter-chunk part goes to yf, free since the gate)
   SSD_TRY(staged_run(&mdx, &ra, mmeta, ws_dx, w.dx_bytes, stream, f(w.yf)));
+  // dB and dC: the chunk states these scans would compute are the dx and
+  // forward scans' carry-in states transposed (G^T and S^T, with the initial
+  // states already folded in), and their cumsums are those scans' own; so
+  // only C.B^T and the chunk scan run, reading the states transposed
+  const StagedWs lf = staged_layout(&q.fwd), lx = staged_layout(&mdx);
+  const int32_t* fwd_meta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws_fwd + lf.meta) : nullptr;
+  float* cb_rest = reinterpret_cast<float*>(ws_rest);
   ra.x = scratch_view(f(w.Cer), &mdB, H, N);
   ra.B = scratch_view(f(w.dyr), &mdB, H, P);
   ra.C = scratch_view(f(w.xr), &mdB, H, P);
-  ra.initial_states = a->dfinal_states ? f(w.dfT) : nullptr;
   ra.out = scratch_view(f(w.gb), &mdB, H, N);
-  ra.final_states = nullptr;
-  SSD_TRY(staged_run(&mdB, &ra, mmeta, ws_rest, w.rest_bytes, stream));
+  SSD_TRY(transposed_scan(&mdB, &ra, mmeta, reinterpret_cast<float*>(ws_dx + lx.cs), nullptr,
+                          reinterpret_cast<float*>(ws_dx + lx.st), cb_rest, stream));
   ra.x = scratch_view(f(w.Be), p, H, N);
   ra.B = scratch_view(f(w.xf), p, H, P);
   ra.C = scratch_view(f(w.dy), p, H, P);
-  ra.dt = a->dt;
-  ra.dt_bias = a->dt_bias;
-  ra.initial_states = a->initial_states ? f(w.h0T) : nullptr;
   ra.out = scratch_view(f(w.gc), p, H, N);
-  SSD_TRY(staged_run(&q.dC, &ra, nullptr, ws_rest, w.rest_bytes, stream));
+  SSD_TRY(transposed_scan(&q.dC, &ra, fwd_meta, reinterpret_cast<float*>(ws_fwd + lf.cs),
+                          p->input_dt ? reinterpret_cast<float*>(ws_fwd + lf.dtc) : nullptr,
+                          reinterpret_cast<float*>(ws_fwd + lf.st), cb_rest, stream));
 
   // 5. gradients
   // (with the step size on the input term, dx and dB carry it and its
@@ -796,13 +812,11 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   SSD_HIP(ssd::launch_bwd_group_sums(bg, f(w.gb), f(w.gc), dlt, targ(a->dB), targ(a->dC),
                                      stream),
           "backward group sums launch");
-  const StagedWs lf = staged_layout(&q.fwd), lx = staged_layout(&mdx), lc = staged_layout(&q.dC);
-  const int32_t* fwd_meta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws_fwd + lf.meta) : nullptr;
   const ssd::Geo gf = make_geo(&q.fwd, fwd_meta);
   // (the dC scan's C.B^T is dy . x^T per head, and it ran last in ws_rest)
   SSD_HIP(ssd::launch_bwd_step_grads(
-              bg, gf, reinterpret_cast<float*>(ws_fwd + lf.cb),
-              reinterpret_cast<float*>(ws_rest + lc.cb), f(w.yo), f(w.yf), f(w.xf), f(w.dy),
+              bg, gf, reinterpret_cast<float*>(ws_fwd + lf.cb), cb_rest, f(w.yo), f(w.yf),
+              f(w.xf), f(w.dy),
               f(w.dyx), f(w.delta), f(w.gd), a->A,
               reinterpret_cast<float*>(ws_fwd + lf.st), reinterpret_cast<float*>(ws_dx + lx.st),
               f(w.gfirst), a->dfinal_states, xg, targ(a->ddt),

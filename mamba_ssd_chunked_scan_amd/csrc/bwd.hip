@@ -188,18 +188,6 @@ __global__ __launch_bounds__(256) void k_steps(BwdGeo q, TArg dt, int dt_dtype, 
   }
 }
 
-// ---- (nseq, H, P, N) -> (nseq, H, N, P)
-__global__ __launch_bounds__(256) void k_transpose_states(int nsh, int P, int N, const float* src,
-                                                          float* dst) {
-  const int64_t total = (int64_t)nsh * P * N;
-  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int n = (int)(i % N);
-    const int p = (int)((i / N) % P);
-    const int64_t m = i / ((int64_t)N * P);
-    dst[(m * N + n) * P + p] = src[i];
-  }
-}
-
 // ---- per (token, head) row: dx = f (mirrored dx-scan output G B) + D dy, dy .
 // x for dD and, when the step size f = delta scales the input term, x . G B
 // for its gradient; the row's partial sums meet in LDS and its first thread
@@ -631,14 +619,6 @@ hipError_t launch_bwd_steps(const BwdGeo& q, TArg dt, int dt_dtype, const float*
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(k_steps, dim3(grid_for(n)), dim3(256), 0, s, q, dt, dt_dtype, A, dt_bias,
                      softplus, clamp, dt_min, dt_max, delta, gd, dt_rev);
-  return hipGetLastError();
-}
-
-hipError_t launch_bwd_transpose_states(int nsh, int P, int N, const float* src, float* dst,
-                                       hipStream_t s) {
-  const int64_t n = (int64_t)nsh * P * N;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_transpose_states, dim3(grid_for(n)), dim3(256), 0, s, nsh, P, N, src, dst);
   return hipGetLastError();
 }
 

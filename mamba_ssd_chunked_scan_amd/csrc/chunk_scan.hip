@@ -7,13 +7,16 @@
 namespace ssd {
 
 // F: the step size scales the input term (dtc is read), compiled in only then.
+// st_trans: the carry-in states are stored transposed, (K, H, N, P) -- the
+// chunk states of a scan whose head and state dims are this one's swapped.
 template <typename T, typename ST, typename TO, bool F>
 __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* __restrict__ CB, TArg x,
                                                     TArg Cm, const float* __restrict__ cs,
                                                     const float* __restrict__ dtc,
                                                     const ST* __restrict__ states,
                                                     const float* __restrict__ D, TArg z,
-                                                    TArg out, float* __restrict__ yoff) {
+                                                    TArg out, float* __restrict__ yoff,
+                                                    int st_trans) {
   using Pr = Prec<T>;
   using HL = HinLds<T, ST>;
   extern __shared__ __align__(16) char smem[];
@@ -48,12 +51,23 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
     for (int i = 0; i < 8; ++i) s_xt[(pp + i) * lay.ldx + s] = from_f32<T>(val[i]);
   }
   const ST* hsrc = states + ((int64_t)j * g.H + h) * P * N;
-  const int nvec_h = 64 * (N / 8);
-  for (int v = tid; v < nvec_h; v += 256) {
-    const int pr = v / (N / 8), n = (v % (N / 8)) * 8;
-    f32x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (pr < pw) val = StLoad<ST>::load(hsrc + (int64_t)(p0 + pr) * N + n);
-    HL::stage(s_h, hsrc, N, pr, n, val);
+  if (!st_trans) {
+    const int nvec_h = 64 * (N / 8);
+    for (int v = tid; v < nvec_h; v += 256) {
+      const int pr = v / (N / 8), n = (v % (N / 8)) * 8;
+      f32x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (pr < pw) val = StLoad<ST>::load(hsrc + (int64_t)(p0 + pr) * N + n);
+      HL::stage(s_h, hsrc, N, pr, n, val);
+    }
+  } else {
+    // row n of the stored state holds this block's 64 p columns contiguously
+    for (int v = tid; v < N * 8; v += 256) {
+      const int n = v / 8, pp = (v % 8) * 8;
+      f32x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
+      if (pp < pw) val = StLoad<ST>::load(hsrc + (int64_t)n * P + p0 + pp);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) HL::stage1(s_h, N, pp + i, n, val[i]);
+    }
   }
   __syncthreads();
 
@@ -181,16 +195,17 @@ __global__ __launch_bounds__(256, C <= 128 ? 3 : 2) void k_chunk_scan_bf16(Geo g
                                                          const float* __restrict__ dtc,
                                                          const ST* __restrict__ states,
                                                          const float* __restrict__ D, TArg z,
-                                                         TArg out) {
+                                                         TArg out, float* __restrict__ yoff) {
   extern __shared__ __align__(16) char smem[];
-  chunk_scan_block<ST, TO, C, F>(g, CB, x, Cm, cs, dtc, states, D, z, out, blockIdx.x,
+  chunk_scan_block<ST, TO, C, F>(g, CB, x, Cm, cs, dtc, states, D, z, out, yoff, blockIdx.x,
                                  blockIdx.y, blockIdx.z, smem);
 }
 
 template <typename ST, typename TO, int C, bool F>
 static hipError_t launch_scan_bf16_c(const Geo& g, const float* CB, TArg x, TArg Cm,
                                      const float* cs, const float* dtc, const ST* st,
-                                     const float* D, TArg z, TArg out, hipStream_t s) {
+                                     const float* D, TArg z, TArg out, float* yoff,
+                                     hipStream_t s) {
   const ScanLayout lay = scan_layout_bf16<ST>(C, g.N);
   auto kern = k_chunk_scan_bf16<ST, TO, C, F>;
   if (lay.bytes > 64 * 1024) {
@@ -199,35 +214,38 @@ static hipError_t launch_scan_bf16_c(const Geo& g, const float* CB, TArg x, TArg
     if (e != hipSuccess) return e;
   }
   dim3 grid(g.K, g.H, (g.P + 63) / 64);
-  hipLaunchKernelGGL(kern, grid, dim3(256), lay.bytes, s, g, CB, x, Cm, cs, dtc, st, D, z, out);
+  hipLaunchKernelGGL(kern, grid, dim3(256), lay.bytes, s, g, CB, x, Cm, cs, dtc, st, D, z, out,
+                     yoff);
   return hipGetLastError();
 }
 
 template <typename ST, typename TO, bool F>
 static hipError_t launch_scan_bf16_f(const Geo& g, const float* CB, TArg x, TArg Cm,
                                      const float* cs, const float* dtc, const void* states,
-                                     const float* D, TArg z, TArg out, hipStream_t s) {
+                                     const float* D, TArg z, TArg out, float* yoff,
+                                     hipStream_t s) {
   const ST* st = (const ST*)states;
   switch (g.C) {
-    case 32: return launch_scan_bf16_c<ST, TO, 32, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, s);
-    case 64: return launch_scan_bf16_c<ST, TO, 64, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, s);
-    case 128: return launch_scan_bf16_c<ST, TO, 128, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, s);
-    default: return launch_scan_bf16_c<ST, TO, 256, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, s);
+    case 32: return launch_scan_bf16_c<ST, TO, 32, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, yoff, s);
+    case 64: return launch_scan_bf16_c<ST, TO, 64, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, yoff, s);
+    case 128: return launch_scan_bf16_c<ST, TO, 128, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, yoff, s);
+    default: return launch_scan_bf16_c<ST, TO, 256, F>(g, CB, x, Cm, cs, dtc, st, D, z, out, yoff, s);
   }
 }
 
 template <typename ST, typename TO>
 static hipError_t launch_scan_bf16(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
                                    const float* dtc, const void* states, const float* D, TArg z,
-                                   TArg out, hipStream_t s) {
-  return dtc ? launch_scan_bf16_f<ST, TO, true>(g, CB, x, C, cs, dtc, states, D, z, out, s)
-             : launch_scan_bf16_f<ST, TO, false>(g, CB, x, C, cs, dtc, states, D, z, out, s);
+                                   TArg out, float* yoff, hipStream_t s) {
+  return dtc ? launch_scan_bf16_f<ST, TO, true>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
+             : launch_scan_bf16_f<ST, TO, false>(g, CB, x, C, cs, dtc, states, D, z, out, yoff,
+                                                 s);
 }
 
 template <typename T, typename ST, typename TO, bool F>
 static hipError_t launch_scan_tf(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
                                  const float* dtc, const void* states, const float* D, TArg z,
-                                 TArg out, float* yoff, hipStream_t s) {
+                                 TArg out, float* yoff, int st_trans, hipStream_t s) {
   const ScanLayout lay = scan_layout<T, ST>(g.C, g.N);
   auto kern = k_chunk_scan_generic<T, ST, TO, F>;
   if (lay.bytes > 64 * 1024) {
@@ -237,35 +255,37 @@ static hipError_t launch_scan_tf(const Geo& g, const float* CB, TArg x, TArg C, 
   }
   dim3 grid(g.K, g.H, (g.P + 63) / 64);
   hipLaunchKernelGGL(kern, grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, dtc, (const ST*)states,
-                     D, z, out, yoff);
+                     D, z, out, yoff, st_trans);
   return hipGetLastError();
 }
 
 template <typename T, typename ST, typename TO>
 static hipError_t launch_scan_t(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
                                 const float* dtc, const void* states, const float* D, TArg z,
-                                TArg out, float* yoff, hipStream_t s) {
-  return dtc ? launch_scan_tf<T, ST, TO, true>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
-             : launch_scan_tf<T, ST, TO, false>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
+                                TArg out, float* yoff, int st_trans, hipStream_t s) {
+  return dtc ? launch_scan_tf<T, ST, TO, true>(g, CB, x, C, cs, dtc, states, D, z, out, yoff,
+                                               st_trans, s)
+             : launch_scan_tf<T, ST, TO, false>(g, CB, x, C, cs, dtc, states, D, z, out, yoff,
+                                                st_trans, s);
 }
 
 hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
                              const float* cs, const float* dtc, const void* states, int st_dtype,
                              const float* D, TArg z, TArg out, int out_dtype, hipStream_t s,
-                             float* yoff) {
+                             float* yoff, int st_trans) {
   if (g.K == 0) return hipSuccess;
   const bool ib = in_dtype == DT_BF16, sb = st_dtype == DT_BF16, ob = out_dtype == DT_BF16;
   if (ib) {
-    if (yoff) return hipErrorInvalidValue;  // only the fp32 kernel keeps Y_off
-    if (sb) return ob ? launch_scan_bf16<bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, s)
-                      : launch_scan_bf16<bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, s);
-    return ob ? launch_scan_bf16<float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, s)
-              : launch_scan_bf16<float, float>(g, CB, x, C, cs, dtc, states, D, z, out, s);
+    if (st_trans) return hipErrorInvalidValue;  // only the fp32 kernel reads transposed states
+    if (sb) return ob ? launch_scan_bf16<bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
+                      : launch_scan_bf16<bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
+    return ob ? launch_scan_bf16<float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
+              : launch_scan_bf16<float, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
   }
-  if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
-                    : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
-  return ob ? launch_scan_t<float, float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
-            : launch_scan_t<float, float, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
+  if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, s)
+                    : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, s);
+  return ob ? launch_scan_t<float, float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, s)
+            : launch_scan_t<float, float, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, s);
 }
 
 }  // namespace ssd

@@ -30,13 +30,14 @@ hipError_t launch_state_passing(const Geo& g, const void* states, int st_dtype,
                                 const float* cs, const float* h0, void* states_out,
                                 float* hfinal, hipStream_t s);
 
-// yoff (fp32 inputs only; NULL to skip): also writes the inter-chunk part of
+// yoff (NULL to skip): also writes the inter-chunk part of
 // the output, exp(cs_l) C_l . h_in, before the skip and the gate, as (tokens,
-// H, P) fp32 on the packed axis
+// H, P) fp32 on the packed axis.  st_trans (fp32 inputs only): the carry-in
+// states are stored (K, H, N, P).
 hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
                              const float* cs, const float* dtc, const void* states, int st_dtype,
                              const float* D, TArg z, TArg out, int out_dtype, hipStream_t s,
-                             float* yoff = nullptr);
+                             float* yoff = nullptr, int st_trans = 0);
 
 // ---- fused forward (fused_fwd.hip)
 constexpr int kFusedChunk = 128;             // internal chunk length of the fused pass
@@ -84,8 +85,6 @@ hipError_t launch_bwd_gate(const BwdGeo& q, TArg dout, int dout_dtype, TArg z, i
 hipError_t launch_bwd_steps(const BwdGeo& q, TArg dt, int dt_dtype, const float* A,
                             const float* dt_bias, int softplus, int clamp, float dt_min,
                             float dt_max, float* delta, float* gd, float* dt_rev, hipStream_t s);
-hipError_t launch_bwd_transpose_states(int nsh, int P, int N, const float* src, float* dst,
-                                       hipStream_t s);
 hipError_t launch_bwd_tokens(const BwdGeo& q, TArg x, int x_dtype, const float* D,
                              const float* dy, const float* gx_rev, const float* delta, TArg dx,
                              float* dyx, float* xg, hipStream_t s);

@@ -69,6 +69,9 @@ template <typename ST> struct HinLdsF32 {  // fp32 inputs: fp32 operands through
   static __device__ void stage(char* base, const ST*, int N, int prow, int n, f32x8 v) {
     Vec8<float>::store(reinterpret_cast<float*>(base) + prow * ld(N) + n, v);
   }
+  static __device__ void stage1(char* base, int N, int prow, int n, float v) {
+    reinterpret_cast<float*>(base)[prow * ld(N) + n] = v;
+  }
   static __device__ FragF32 frag(const char* base, int N, int prow, int k) {
     FragF32 f;
     f.v = Vec8<float>::load(reinterpret_cast<const float*>(base) + prow * ld(N) + k);
@@ -163,8 +166,8 @@ __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, 
                                                  const TArg& Cm, const float* cs,
                                                  const float* dtc, const ST* states,
                                                  const float* D, const TArg& z,
-                                                 const TArg& out, int j, int h, int pz,
-                                                 char* smem) {
+                                                 const TArg& out, float* yoff, int j, int h,
+                                                 int pz, char* smem) {
   using Cfg = ScanCfg<C>;
   using HL = HinLds<bf16, ST>;
   constexpr int NPAIR = Cfg::NPAIR, LDW = Cfg::LDW;
@@ -321,6 +324,18 @@ __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, 
       const float e = fast_exp(s_cs[lt * 16 + q * 4 + i]);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[u][pt][i] *= e;
+    }
+    // optionally keep Y_off on its own, (tokens, H, P) fp32 on the packed axis
+    if (yoff) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int l = lt * 16 + q * 4 + i;
+        if (l >= c.len) continue;
+        float* yr = yoff + ((int64_t)(c.b * g.T + c.t0 + l) * g.H + h) * P + p0;
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          if (pt * 16 + r16 < pw) yr[pt * 16 + r16] = acc[u][pt][i];
+      }
     }
     // Y_diag: (L o CB) x over s <= l.  The first four k-blocks come from the
     // prefetch; the mask is a select after the exponential (whose argument is
