@@ -321,16 +321,17 @@ ssd_status staged_run(const ssd_problem* p, const ssd_fwd_args* a, const int32_t
 
 // The chunk scan of a backward run whose chunk states are another run's
 // carry-in states, stored transposed, and whose cumsum is that run's too:
-// C.B^T, then the chunk scan reading the states transposed.  fp32 operands.
+// C.B^T, then the chunk scan reading the states transposed.  fp32 operands;
+// the run's x is per group of x_div heads.
 ssd_status transposed_scan(const ssd_problem* p, const ssd_fwd_args* a, const int32_t* meta,
                            const float* cs, const float* dtc, const float* states, float* cb,
-                           hipStream_t stream) {
+                           int x_div, hipStream_t stream) {
   const ssd::Geo g = make_geo(p, meta);
   const int in = dcode(a->x.dtype);
   SSD_HIP(ssd::launch_bmm_chunk(g, targ(a->C), targ(a->B), in, cb, stream), "bmm_chunk launch");
   SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, dtc, states,
                                  dcode(SSD_F32), nullptr, targ(a->z), targ(a->out),
-                                 dcode(a->out.dtype), stream, nullptr, 1),
+                                 dcode(a->out.dtype), stream, nullptr, 1, x_div),
           "chunk_scan launch");
   return ok();
 }
@@ -376,7 +377,7 @@ BwdProblems bwd_problems(const ssd_problem* p) {
 }
 
 struct BwdWs {
-  size_t yf, yo, dy, dyr, Cr, Br, Cer, Be, xr, xf, delta, gd, dtr, dyx, xg, gx, gb, gc,
+  size_t yf, yo, dy, dyr, Cr, Br, Bf, xr, xf, delta, gd, dtr, dyx, xg, gx, gb, gc,
       gfirst, mmeta, mcu, part, run_fwd, run_dx, run_rest, fwd_bytes, dx_bytes, rest_bytes, total;
 };
 
@@ -399,8 +400,7 @@ BwdWs bwd_layout(const ssd_problem* p) {
   w.dyr = take(nt * H * P);
   w.Cr = take(nt * G * N);
   w.Br = take(nt * G * N);
-  w.Cer = take(nt * H * N);
-  w.Be = take(nt * H * N);
+  w.Bf = take(nt * G * N);
   w.xr = take(nt * H * P);
   w.xf = take(nt * H * P);
   w.delta = take(nt * H);
@@ -717,12 +717,12 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   char* ws_dx = ws + w.run_dx;
   char* ws_rest = ws + w.run_rest;
 
-  // 1. fp32 copies of the operands (mirrored in time for the backward scans;
-  // B and C repeated for each head where a scan's head dim is N)
+  // 1. fp32 copies of the operands the fp32 scans read (mirrored in time for
+  // the backward ones)
   const int in = dcode(a->x.dtype);
   struct Copy { ssd_tensor src; int R, W, rep, rev; size_t dst; };
   const Copy copies[] = {{a->C, G, N, 1, 1, w.Cr},     {a->B, G, N, 1, 1, w.Br},
-                         {a->C, H, N, H / G, 1, w.Cer}, {a->B, H, N, H / G, 0, w.Be},
+                         {a->B, G, N, 1, 0, w.Bf},
                          {a->x, H, P, 1, 1, w.xr},     {a->x, H, P, 1, 0, w.xf}};
   for (const Copy& c : copies)
     SSD_HIP(ssd::launch_bwd_gather(bg, targ(c.src), in, c.R, c.W, c.rep, c.rev, f(c.dst), stream),
@@ -787,19 +787,19 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   const StagedWs lf = staged_layout(&q.fwd), lx = staged_layout(&mdx);
   const int32_t* fwd_meta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws_fwd + lf.meta) : nullptr;
   float* cb_rest = reinterpret_cast<float*>(ws_rest);
-  ra.x = scratch_view(f(w.Cer), &mdB, H, N);
+  ra.x = scratch_view(f(w.Cr), &mdB, G, N);  // (each group's row serves its heads)
   ra.B = scratch_view(f(w.dyr), &mdB, H, P);
   ra.C = scratch_view(f(w.xr), &mdB, H, P);
   ra.out = scratch_view(f(w.gb), &mdB, H, N);
   SSD_TRY(transposed_scan(&mdB, &ra, mmeta, reinterpret_cast<float*>(ws_dx + lx.cs), nullptr,
-                          reinterpret_cast<float*>(ws_dx + lx.st), cb_rest, stream));
-  ra.x = scratch_view(f(w.Be), p, H, N);
+                          reinterpret_cast<float*>(ws_dx + lx.st), cb_rest, H / G, stream));
+  ra.x = scratch_view(f(w.Bf), p, G, N);
   ra.B = scratch_view(f(w.xf), p, H, P);
   ra.C = scratch_view(f(w.dy), p, H, P);
   ra.out = scratch_view(f(w.gc), p, H, N);
   SSD_TRY(transposed_scan(&q.dC, &ra, fwd_meta, reinterpret_cast<float*>(ws_fwd + lf.cs),
                           p->input_dt ? reinterpret_cast<float*>(ws_fwd + lf.dtc) : nullptr,
-                          reinterpret_cast<float*>(ws_fwd + lf.st), cb_rest, stream));
+                          reinterpret_cast<float*>(ws_fwd + lf.st), cb_rest, H / G, stream));
 
   // 5. gradients
   // (with the step size on the input term, dx and dB carry it and its

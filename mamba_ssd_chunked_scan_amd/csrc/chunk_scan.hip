@@ -9,6 +9,7 @@ namespace ssd {
 // F: the step size scales the input term (dtc is read), compiled in only then.
 // st_trans: the carry-in states are stored transposed, (K, H, N, P) -- the
 // chunk states of a scan whose head and state dims are this one's swapped.
+// x_div: head h reads row h / x_div of x (x shared by groups of heads).
 template <typename T, typename ST, typename TO, bool F>
 __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* __restrict__ CB, TArg x,
                                                     TArg Cm, const float* __restrict__ cs,
@@ -16,7 +17,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
                                                     const ST* __restrict__ states,
                                                     const float* __restrict__ D, TArg z,
                                                     TArg out, float* __restrict__ yoff,
-                                                    int st_trans) {
+                                                    int st_trans, int x_div) {
   using Pr = Prec<T>;
   using HL = HinLds<T, ST>;
   extern __shared__ __align__(16) char smem[];
@@ -46,7 +47,8 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
   for (int v = tid; v < nvec_x; v += 256) {
     const int s = v / 8, pp = (v % 8) * 8;
     f32x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (s < c.len && pp < pw) val = Vec8<T>::load(row_ptr<T>(x, c.b, c.t0 + s, h) + p0 + pp);
+    if (s < c.len && pp < pw)
+      val = Vec8<T>::load(row_ptr<T>(x, c.b, c.t0 + s, h / x_div) + p0 + pp);
 #pragma unroll
     for (int i = 0; i < 8; ++i) s_xt[(pp + i) * lay.ldx + s] = from_f32<T>(val[i]);
   }
@@ -245,7 +247,7 @@ static hipError_t launch_scan_bf16(const Geo& g, const float* CB, TArg x, TArg C
 template <typename T, typename ST, typename TO, bool F>
 static hipError_t launch_scan_tf(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
                                  const float* dtc, const void* states, const float* D, TArg z,
-                                 TArg out, float* yoff, int st_trans, hipStream_t s) {
+                                 TArg out, float* yoff, int st_trans, int x_div, hipStream_t s) {
   const ScanLayout lay = scan_layout<T, ST>(g.C, g.N);
   auto kern = k_chunk_scan_generic<T, ST, TO, F>;
   if (lay.bytes > 64 * 1024) {
@@ -255,37 +257,38 @@ static hipError_t launch_scan_tf(const Geo& g, const float* CB, TArg x, TArg C, 
   }
   dim3 grid(g.K, g.H, (g.P + 63) / 64);
   hipLaunchKernelGGL(kern, grid, dim3(256), lay.bytes, s, g, CB, x, C, cs, dtc, (const ST*)states,
-                     D, z, out, yoff, st_trans);
+                     D, z, out, yoff, st_trans, x_div);
   return hipGetLastError();
 }
 
 template <typename T, typename ST, typename TO>
 static hipError_t launch_scan_t(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
                                 const float* dtc, const void* states, const float* D, TArg z,
-                                TArg out, float* yoff, int st_trans, hipStream_t s) {
+                                TArg out, float* yoff, int st_trans, int x_div, hipStream_t s) {
   return dtc ? launch_scan_tf<T, ST, TO, true>(g, CB, x, C, cs, dtc, states, D, z, out, yoff,
-                                               st_trans, s)
+                                               st_trans, x_div, s)
              : launch_scan_tf<T, ST, TO, false>(g, CB, x, C, cs, dtc, states, D, z, out, yoff,
-                                                st_trans, s);
+                                                st_trans, x_div, s);
 }
 
 hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
                              const float* cs, const float* dtc, const void* states, int st_dtype,
                              const float* D, TArg z, TArg out, int out_dtype, hipStream_t s,
-                             float* yoff, int st_trans) {
+                             float* yoff, int st_trans, int x_div) {
   if (g.K == 0) return hipSuccess;
   const bool ib = in_dtype == DT_BF16, sb = st_dtype == DT_BF16, ob = out_dtype == DT_BF16;
   if (ib) {
-    if (st_trans) return hipErrorInvalidValue;  // only the fp32 kernel reads transposed states
+    // only the fp32 kernel reads transposed states or shares x between heads
+    if (st_trans || x_div != 1) return hipErrorInvalidValue;
     if (sb) return ob ? launch_scan_bf16<bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
                       : launch_scan_bf16<bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
     return ob ? launch_scan_bf16<float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
               : launch_scan_bf16<float, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
   }
-  if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, s)
-                    : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, s);
-  return ob ? launch_scan_t<float, float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, s)
-            : launch_scan_t<float, float, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, s);
+  if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, s)
+                    : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, s);
+  return ob ? launch_scan_t<float, float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, s)
+            : launch_scan_t<float, float, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, s);
 }
 
 }  // namespace ssd
