@@ -282,7 +282,7 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
 // chunk table), a1-a5 in sequence.  Arguments were validated by the caller.
 ssd_status staged_run(const ssd_problem* p, const ssd_fwd_args* a, const int32_t* meta_in,
                       void* workspace, size_t ws_bytes, hipStream_t stream,
-                      float* yoff = nullptr) {
+                      float* yoff = nullptr, int split = 0) {
   const StagedWs w = staged_layout(p);
   if (w.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < w.total)
@@ -311,8 +311,8 @@ ssd_status staged_run(const ssd_problem* p, const ssd_fwd_args* a, const int32_t
                                     stream),
           "state_passing launch");
   SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, dtc, st, sd, a->D,
-                                 targ(a->z),
-                                 targ(a->out), dcode(a->out.dtype), stream, yoff),
+                                 targ(a->z), targ(a->out), dcode(a->out.dtype), stream, yoff, 0,
+                                 1, split),
           "chunk_scan launch");
   return ok();
 }
@@ -325,13 +325,13 @@ ssd_status staged_run(const ssd_problem* p, const ssd_fwd_args* a, const int32_t
 // the run's x is per group of x_div heads.
 ssd_status transposed_scan(const ssd_problem* p, const ssd_fwd_args* a, const int32_t* meta,
                            const float* cs, const float* dtc, const float* states, float* cb,
-                           int x_div, hipStream_t stream) {
+                           int x_div, int split, hipStream_t stream) {
   const ssd::Geo g = make_geo(p, meta);
   const int in = dcode(a->x.dtype);
   SSD_HIP(ssd::launch_bmm_chunk(g, targ(a->C), targ(a->B), in, cb, stream), "bmm_chunk launch");
   SSD_HIP(ssd::launch_chunk_scan(g, cb, targ(a->x), targ(a->C), in, cs, dtc, states,
                                  dcode(SSD_F32), nullptr, targ(a->z), targ(a->out),
-                                 dcode(a->out.dtype), stream, nullptr, 1, x_div),
+                                 dcode(a->out.dtype), stream, nullptr, 1, x_div, split),
           "chunk_scan launch");
   return ok();
 }
@@ -763,7 +763,11 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   mdB.cu_seqlens = mcu;
 
   // 4. the three scans: dx and dB backwards in time (mirrored operands,
-  // shifted steps, mirrored chunk table), dC forwards
+  // shifted steps, mirrored chunk table), dC forwards.  Their chunk scans
+  // multiply fp32 operands; for bf16 inputs (held to the bf16 tolerance) the
+  // operands are split into bf16 hi + lo, three bf16 matrix instructions per
+  // product, ~16 significant bits per operand
+  const int split = in == ssd::DT_BF16 ? 1 : 0;
   ssd_tensor dtr;
   dtr.data = f(w.dtr);
   dtr.dtype = SSD_F32;
@@ -779,7 +783,7 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   ra.out = scratch_view(f(w.gx), &mdx, H, P);
   ra.final_states = f(w.gfirst);
   // (its inter-chunk part goes to yf, free since the gate)
-  SSD_TRY(staged_run(&mdx, &ra, mmeta, ws_dx, w.dx_bytes, stream, f(w.yf)));
+  SSD_TRY(staged_run(&mdx, &ra, mmeta, ws_dx, w.dx_bytes, stream, f(w.yf), split));
   // dB and dC: the chunk states these scans would compute are the dx and
   // forward scans' carry-in states transposed (G^T and S^T, with the initial
   // states already folded in), and their cumsums are those scans' own; so
@@ -792,14 +796,16 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   ra.C = scratch_view(f(w.xr), &mdB, H, P);
   ra.out = scratch_view(f(w.gb), &mdB, H, N);
   SSD_TRY(transposed_scan(&mdB, &ra, mmeta, reinterpret_cast<float*>(ws_dx + lx.cs), nullptr,
-                          reinterpret_cast<float*>(ws_dx + lx.st), cb_rest, H / G, stream));
+                          reinterpret_cast<float*>(ws_dx + lx.st), cb_rest, H / G, split,
+                          stream));
   ra.x = scratch_view(f(w.Bf), p, G, N);
   ra.B = scratch_view(f(w.xf), p, H, P);
   ra.C = scratch_view(f(w.dy), p, H, P);
   ra.out = scratch_view(f(w.gc), p, H, N);
   SSD_TRY(transposed_scan(&q.dC, &ra, fwd_meta, reinterpret_cast<float*>(ws_fwd + lf.cs),
                           p->input_dt ? reinterpret_cast<float*>(ws_fwd + lf.dtc) : nullptr,
-                          reinterpret_cast<float*>(ws_fwd + lf.st), cb_rest, H / G, stream));
+                          reinterpret_cast<float*>(ws_fwd + lf.st), cb_rest, H / G, split,
+                          stream));
 
   // 5. gradients
   // (with the step size on the input term, dx and dB carry it and its

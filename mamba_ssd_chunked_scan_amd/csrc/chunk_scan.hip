@@ -1,6 +1,9 @@
 // chunk_scan.hip -- the standalone chunk-scan kernels.  The bf16 body and the
-// LDS helpers live in stage_scan.hpp; fp32 inputs use the generic kernel below
-// (fp32 matrix instructions throughout).
+// LDS helpers live in stage_scan.hpp; fp32 inputs use the generic kernel below,
+// with fp32 matrix instructions, or (SP) every operand split into bf16 hi + lo
+// and three bf16 matrix instructions per product.
+#include <type_traits>
+
 #include "kernels.hpp"
 #include "stage_scan.hpp"
 
@@ -10,7 +13,7 @@ namespace ssd {
 // st_trans: the carry-in states are stored transposed, (K, H, N, P) -- the
 // chunk states of a scan whose head and state dims are this one's swapped.
 // x_div: head h reads row h / x_div of x (x shared by groups of heads).
-template <typename T, typename ST, typename TO, bool F>
+template <typename T, typename ST, typename TO, bool F, bool SP>
 __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* __restrict__ CB, TArg x,
                                                     TArg Cm, const float* __restrict__ cs,
                                                     const float* __restrict__ dtc,
@@ -19,7 +22,7 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
                                                     TArg out, float* __restrict__ yoff,
                                                     int st_trans, int x_div) {
   using Pr = Prec<T>;
-  using HL = HinLds<T, ST>;
+  using HL = typename std::conditional<SP, HinLds<bf16, ST>, HinLds<T, ST>>::type;
   extern __shared__ __align__(16) char smem[];
   const int j = blockIdx.x, h = blockIdx.y, p0 = blockIdx.z * 64;
   Chunk c;
@@ -28,10 +31,12 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
   const int grp = h / g.hpg;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int r16 = lane % 16, q = lane / 16;
-  const ScanLayout lay = scan_layout<T, ST>(C, N);
+  const ScanLayout lay = SP ? scan_layout_split<ST>(C, N) : scan_layout<T, ST>(C, N);
   float* s_cs = reinterpret_cast<float*>(smem);
   float* s_f = s_cs + C;
   T* s_xt = reinterpret_cast<T*>(smem + lay.off_x);
+  bf16* s_xh = reinterpret_cast<bf16*>(smem + lay.off_x);  // (SP: hi and lo planes)
+  bf16* s_xl = s_xh + 64 * lay.ldx;
   char* s_h = smem + lay.off_h;
   float* s_y = reinterpret_cast<float*>(smem + lay.off_h);
 
@@ -49,8 +54,17 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
     f32x8 val = {0, 0, 0, 0, 0, 0, 0, 0};
     if (s < c.len && pp < pw)
       val = Vec8<T>::load(row_ptr<T>(x, c.b, c.t0 + s, h / x_div) + p0 + pp);
+    if constexpr (SP) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s_xt[(pp + i) * lay.ldx + s] = from_f32<T>(val[i]);
+      for (int i = 0; i < 8; ++i) {
+        const bf16 hv = (bf16)val[i];
+        s_xh[(pp + i) * lay.ldx + s] = hv;
+        s_xl[(pp + i) * lay.ldx + s] = (bf16)(val[i] - (float)hv);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s_xt[(pp + i) * lay.ldx + s] = from_f32<T>(val[i]);
+    }
   }
   const ST* hsrc = states + ((int64_t)j * g.H + h) * P * N;
   if (!st_trans) {
@@ -92,17 +106,26 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
     const bool lok = lrow < c.len;
     // Y_off = C_l . Hin^T over n
     const T* crow = row_ptr<T>(Cm, c.b, c.t0 + (lok ? lrow : 0), grp);
+    // each k-block's C fragment is loaded one block ahead (the address clamped
+    // into N; past the end it re-reads the last block, unused)
+    typename Pr::Exact anext = Pr::load_exact(crow + min(q * 8, N - 8));
     for (int k0 = 0; k0 < N; k0 += 32) {
       // lanes whose k-quad lies past N (N % 32 == 16) contribute zeros on both
       // sides; the matrix instruction itself always runs wave-wide
       const int k = k0 + q * 8;
       const bool kok = k < N;
-      typename Pr::Exact a = (lok && kok) ? Pr::load_exact(crow + k) : Pr::zero_exact();
+      const typename Pr::Exact araw = anext;
+      anext = Pr::load_exact(crow + min(k + 32, N - 8));
+      const typename Pr::Exact a = (lok && kok) ? araw : Pr::zero_exact();
+      auto as = [&] {
+        if constexpr (SP) return split_f32x8(a.v);
+        else return a;
+      }();
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
         if (pt < npt) {
           auto b = HL::frag(s_h, N, pt * 16 + r16, kok ? k : 0);
-          mma(acc[u][pt], a, b);
+          mma(acc[u][pt], as, b);
         }
       }
     }
@@ -128,27 +151,40 @@ __global__ __launch_bounds__(256) void k_chunk_scan_generic(Geo g, const float* 
     // Y_diag = (L o CB) x over s <= l
     const float csl = s_cs[min(lrow, C - 1)];
     const int kend = lt * 16 + 16;                 // s < kend covers the diagonal tile
+    // the C.B^T row fragment one block ahead, as above (rows past the chunk
+    // read a row of the tile and are discarded)
+    const float* cbr = cbm + (int64_t)min(lrow, C - 1) * C;
+    f32x8 cbnext = Vec8<float>::load(cbr + q * 8);
     for (int k0 = 0; k0 < kend; k0 += 32) {
       const int s0 = k0 + q * 8;
+      const f32x8 cb = cbnext;
+      cbnext = Vec8<float>::load(cbr + min(s0 + 32, C - 8));
       f32x8 m;
-      if (lok) {
-        const f32x8 cb = Vec8<float>::load(cbm + (int64_t)lrow * C + s0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int s = s0 + e;
-          const bool keep = (s <= lrow) && (s < c.len);
-          m[e] = keep ? fast_exp(csl - s_cs[s]) * cb[e] * (F ? s_f[s] : 1.0f) : 0.0f;
+      for (int e = 0; e < 8; ++e) {
+        const int s = s0 + e;
+        const bool keep = lok && (s <= lrow) && (s < c.len);
+        m[e] = keep ? fast_exp(csl - s_cs[s]) * cb[e] * (F ? s_f[s] : 1.0f) : 0.0f;
+      }
+      if constexpr (SP) {
+        const FragSplit mf = split_f32x8(m);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          if (pt < npt) {
+            FragSplit xb;
+            xb.hi = *reinterpret_cast<const bf16x8*>(&s_xh[(pt * 16 + r16) * lay.ldx + s0]);
+            xb.lo = *reinterpret_cast<const bf16x8*>(&s_xl[(pt * 16 + r16) * lay.ldx + s0]);
+            mma(acc[u][pt], mf, xb);
+          }
         }
       } else {
+        const auto mf = Pr::derive(m);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m[e] = 0.0f;
-      }
-      const auto mf = Pr::derive(m);
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        if (pt < npt) {
-          typename Pr::Exact xb = Pr::load_exact(s_xt + (pt * 16 + r16) * lay.ldx + s0);
-          mma(acc[u][pt], mf, xb);
+        for (int pt = 0; pt < 4; ++pt) {
+          if (pt < npt) {
+            typename Pr::Exact xb = Pr::load_exact(s_xt + (pt * 16 + r16) * lay.ldx + s0);
+            mma(acc[u][pt], mf, xb);
+          }
         }
       }
     }
@@ -244,12 +280,12 @@ static hipError_t launch_scan_bf16(const Geo& g, const float* CB, TArg x, TArg C
                                                  s);
 }
 
-template <typename T, typename ST, typename TO, bool F>
+template <typename T, typename ST, typename TO, bool F, bool SP>
 static hipError_t launch_scan_tf(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
                                  const float* dtc, const void* states, const float* D, TArg z,
                                  TArg out, float* yoff, int st_trans, int x_div, hipStream_t s) {
-  const ScanLayout lay = scan_layout<T, ST>(g.C, g.N);
-  auto kern = k_chunk_scan_generic<T, ST, TO, F>;
+  const ScanLayout lay = SP ? scan_layout_split<ST>(g.C, g.N) : scan_layout<T, ST>(g.C, g.N);
+  auto kern = k_chunk_scan_generic<T, ST, TO, F, SP>;
   if (lay.bytes > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)kern,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lay.bytes);
@@ -264,31 +300,38 @@ static hipError_t launch_scan_tf(const Geo& g, const float* CB, TArg x, TArg C, 
 template <typename T, typename ST, typename TO>
 static hipError_t launch_scan_t(const Geo& g, const float* CB, TArg x, TArg C, const float* cs,
                                 const float* dtc, const void* states, const float* D, TArg z,
-                                TArg out, float* yoff, int st_trans, int x_div, hipStream_t s) {
-  return dtc ? launch_scan_tf<T, ST, TO, true>(g, CB, x, C, cs, dtc, states, D, z, out, yoff,
-                                               st_trans, x_div, s)
-             : launch_scan_tf<T, ST, TO, false>(g, CB, x, C, cs, dtc, states, D, z, out, yoff,
-                                                st_trans, x_div, s);
+                                TArg out, float* yoff, int st_trans, int x_div, int split,
+                                hipStream_t s) {
+  if (split)
+    return dtc ? launch_scan_tf<T, ST, TO, true, true>(g, CB, x, C, cs, dtc, states, D, z, out,
+                                                       yoff, st_trans, x_div, s)
+               : launch_scan_tf<T, ST, TO, false, true>(g, CB, x, C, cs, dtc, states, D, z, out,
+                                                        yoff, st_trans, x_div, s);
+  return dtc ? launch_scan_tf<T, ST, TO, true, false>(g, CB, x, C, cs, dtc, states, D, z, out,
+                                                      yoff, st_trans, x_div, s)
+             : launch_scan_tf<T, ST, TO, false, false>(g, CB, x, C, cs, dtc, states, D, z, out,
+                                                       yoff, st_trans, x_div, s);
 }
 
 hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
                              const float* cs, const float* dtc, const void* states, int st_dtype,
                              const float* D, TArg z, TArg out, int out_dtype, hipStream_t s,
-                             float* yoff, int st_trans, int x_div) {
+                             float* yoff, int st_trans, int x_div, int split) {
   if (g.K == 0) return hipSuccess;
   const bool ib = in_dtype == DT_BF16, sb = st_dtype == DT_BF16, ob = out_dtype == DT_BF16;
   if (ib) {
-    // only the fp32 kernel reads transposed states or shares x between heads
-    if (st_trans || x_div != 1) return hipErrorInvalidValue;
+    // only the fp32 kernel reads transposed states, shares x between heads or
+    // splits fp32 operands
+    if (st_trans || x_div != 1 || split) return hipErrorInvalidValue;
     if (sb) return ob ? launch_scan_bf16<bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
                       : launch_scan_bf16<bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
     return ob ? launch_scan_bf16<float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s)
               : launch_scan_bf16<float, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, s);
   }
-  if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, s)
-                    : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, s);
-  return ob ? launch_scan_t<float, float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, s)
-            : launch_scan_t<float, float, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, s);
+  if (sb) return ob ? launch_scan_t<float, bf16, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, split, s)
+                    : launch_scan_t<float, bf16, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, split, s);
+  return ob ? launch_scan_t<float, float, bf16>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, split, s)
+            : launch_scan_t<float, float, float>(g, CB, x, C, cs, dtc, states, D, z, out, yoff, st_trans, x_div, split, s);
 }
 
 }  // namespace ssd

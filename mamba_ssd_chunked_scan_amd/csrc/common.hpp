@@ -170,6 +170,13 @@ __device__ __forceinline__ void mma(f32x4& acc, const FragBF& a, const FragSplit
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.hi, acc, 0, 0, 0);
   acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.lo, acc, 0, 0, 0);
 }
+// Both operands split: hi.hi + hi.lo + lo.hi (the lo.lo term is below fp32
+// rounding of the sum's leading terms), ~16 significant bits on each side.
+__device__ __forceinline__ void mma(f32x4& acc, const FragSplit& a, const FragSplit& b) {
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+  acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+}
 __device__ __forceinline__ void mma(f32x4& acc, const FragF32& a, const FragF32& b) {
 #pragma unroll
   for (int i = 0; i < 8; ++i)

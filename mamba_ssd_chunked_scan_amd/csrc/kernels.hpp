@@ -34,11 +34,14 @@ hipError_t launch_state_passing(const Geo& g, const void* states, int st_dtype,
 // the output, exp(cs_l) C_l . h_in, before the skip and the gate, as (tokens,
 // H, P) fp32 on the packed axis.  st_trans (fp32 inputs only): the carry-in
 // states are stored (K, H, N, P).  x_div (fp32 inputs only): head h reads row
-// h / x_div of x.
+// h / x_div of x.  split (fp32 inputs only): operands split into bf16 hi + lo,
+// three bf16 matrix instructions per product (~16 significant bits per
+// operand) instead of fp32 matrix instructions.
 hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int in_dtype,
                              const float* cs, const float* dtc, const void* states, int st_dtype,
                              const float* D, TArg z, TArg out, int out_dtype, hipStream_t s,
-                             float* yoff = nullptr, int st_trans = 0, int x_div = 1);
+                             float* yoff = nullptr, int st_trans = 0, int x_div = 1,
+                             int split = 0);
 
 // ---- fused forward (fused_fwd.hip)
 constexpr int kFusedChunk = 128;             // internal chunk length of the fused pass

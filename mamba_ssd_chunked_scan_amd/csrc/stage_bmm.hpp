@@ -9,10 +9,13 @@
 // global memory (16 B per lane for bf16).  One wavefront per (chunk, group,
 // 16-row l-tile) computes the l-tile's causal s-tiles four at a time: all
 // fragment loads of a batch are issued together (one memory round trip per
-// batch and 128 columns of N), rows past the chunk's end and columns past N are
-// zeroed by select when used, and every matrix instruction runs unconditionally.
+// batch of up to 128 columns of N), rows past the chunk's end and columns past
+// N are zeroed by select when used, and every matrix instruction runs outside
+// data-dependent branches.
 // Inputs are exact in their storage type, so the products need no hi/lo split.
 #pragma once
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace ssd {
@@ -38,48 +41,43 @@ __device__ __forceinline__ void bmm_wave(const Geo& g, const TArg& Cm, const TAr
     f32x4 acc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = zero4();
-    for (int n0 = 0; n0 < N; n0 += 128) {
-      Ex a[4], bf[4][4];
-      if (N - n0 >= 128) {
-        // a full 128-wide block: four k-blocks
+    // NB k-blocks of 32 starting at n0: every load first (addresses clamped
+    // into the rows and into N), then the matrix instructions, with rows past
+    // the chunk's end and k past N zeroed by select
+    auto batch = [&](auto nb, int n0) {
+      constexpr int NB = decltype(nb)::value;
+      Ex a[NB], bf[4][NB];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int k = n0 + kk * 32 + q * 8;
-          a[kk] = Pr::load_exact(crow + k);
+      for (int kk = 0; kk < NB; ++kk) {
+        const int k = min(n0 + kk * 32 + q * 8, N - 8);
+        a[kk] = Pr::load_exact(crow + k);
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int srow = min((st0 + b) * 16 + r16, c.len - 1);
-            bf[b][kk] = Pr::load_exact(row_ptr<T>(Bm, c.b, c.t0 + srow, grp) + k);
-          }
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const Ex av = lok ? a[kk] : Pr::zero_exact();
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const bool sok = (st0 + b) * 16 + r16 < c.len;
-            mma(acc[b], av, sok ? bf[b][kk] : Pr::zero_exact());
-          }
-        }
-      } else {
-        // the tail of N (a multiple of 16 below 128): only its k-blocks, a
-        // uniform trip count, so no matrix instruction sits under a
-        // data-dependent branch
-        const int nk = (N - n0 + 31) / 32;
-        for (int kk = 0; kk < nk; ++kk) {
-          const int k = n0 + kk * 32 + q * 8;
-          const Ex av0 = Pr::load_exact(crow + min(k, N - 8));
-          const Ex av = (lok && k < N) ? av0 : Pr::zero_exact();
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const int srow = min((st0 + b) * 16 + r16, c.len - 1);
-            const Ex bv = Pr::load_exact(row_ptr<T>(Bm, c.b, c.t0 + srow, grp) + min(k, N - 8));
-            const bool sok = (st0 + b) * 16 + r16 < c.len && k < N;
-            mma(acc[b], av, sok ? bv : Pr::zero_exact());
-          }
+        for (int b = 0; b < 4; ++b) {
+          const int srow = min((st0 + b) * 16 + r16, c.len - 1);
+          bf[b][kk] = Pr::load_exact(row_ptr<T>(Bm, c.b, c.t0 + srow, grp) + k);
         }
       }
+#pragma unroll
+      for (int kk = 0; kk < NB; ++kk) {
+        const bool kok = n0 + kk * 32 + q * 8 < N;
+        const Ex av = lok && kok ? a[kk] : Pr::zero_exact();
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const bool sok = (st0 + b) * 16 + r16 < c.len && kok;
+          mma(acc[b], av, sok ? bf[b][kk] : Pr::zero_exact());
+        }
+      }
+    };
+    // 128-wide blocks, then the tail of N (a multiple of 16) in blocks of 64
+    // and 32; all branches are uniform, so no matrix instruction sits under a
+    // data-dependent one
+    int n0 = 0;
+    for (; n0 + 128 <= N; n0 += 128) batch(std::integral_constant<int, 4>(), n0);
+    if (n0 + 64 <= N) {
+      batch(std::integral_constant<int, 2>(), n0);
+      n0 += 64;
     }
+    for (; n0 < N; n0 += 32) batch(std::integral_constant<int, 1>(), n0);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       if (st0 + b > lt) break;

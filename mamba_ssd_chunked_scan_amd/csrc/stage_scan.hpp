@@ -45,6 +45,13 @@ template <> struct HinLds<bf16, float> {  // fp32 state -> bf16 hi + lo
     f.lo = *reinterpret_cast<const bf16x8*>(&lo[prow * ld(N) + k]);
     return f;
   }
+  static __device__ void stage1(char* base, int N, int prow, int n, float v) {
+    bf16* hi = reinterpret_cast<bf16*>(base);
+    bf16* lo = hi + 64 * ld(N);
+    const bf16 h = (bf16)v;
+    hi[prow * ld(N) + n] = h;
+    lo[prow * ld(N) + n] = (bf16)(v - (float)h);
+  }
 };
 template <> struct HinLds<bf16, bf16> {  // bf16 state is exact
   static __host__ __device__ int ld(int N) { return N + 8; }
@@ -61,6 +68,9 @@ template <> struct HinLds<bf16, bf16> {  // bf16 state is exact
     FragBF f;
     f.v = *reinterpret_cast<const bf16x8*>(&hi[prow * ld(N) + k]);
     return f;
+  }
+  static __device__ void stage1(char* base, int N, int prow, int n, float v) {
+    reinterpret_cast<bf16*>(base)[prow * ld(N) + n] = (bf16)v;
   }
 };
 template <typename ST> struct HinLdsF32 {  // fp32 inputs: fp32 operands throughout
@@ -105,6 +115,23 @@ __host__ __device__ inline ScanLayout scan_layout(int C, int N) {
   const size_t xbytes = 64ull * L.ldx * sizeof(T);
   L.off_h = (L.off_x + xbytes + 15) & ~size_t(15);
   const size_t hb = HinLds<T, ST>::bytes(N);
+  const size_t yb = (size_t)C * L.ldy * sizeof(float);
+  L.bytes = L.off_h + (hb > yb ? hb : yb);
+  return L;
+}
+
+// fp32 inputs with every operand split into bf16 hi + lo (three bf16 matrix
+// instructions per product instead of eight fp32 ones): x^T is held as a hi
+// and a lo plane, the carry-in state as HinLds<bf16, ST>.
+template <typename ST>
+__host__ __device__ inline ScanLayout scan_layout_split(int C, int N) {
+  ScanLayout L;
+  L.ldx = C + 8;  // bf16 per x^T row, per plane
+  L.ldy = 64 + 4;
+  L.off_x = 8 * C;
+  const size_t xbytes = 2ull * 64 * L.ldx * sizeof(bf16);
+  L.off_h = (L.off_x + xbytes + 15) & ~size_t(15);
+  const size_t hb = HinLds<bf16, ST>::bytes(N);
   const size_t yb = (size_t)C * L.ldy * sizeof(float);
   L.bytes = L.off_h + (hb > yb ? hb : yb);
   return L;
