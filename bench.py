@@ -410,7 +410,7 @@ def time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu, fwd_ms):
             "fwd_bwd_ms": round(bms + fwd_ms, 5),
             "tokens_per_s": round(w.tokens / ((bms + fwd_ms) * 1e-3), 1),
             "workspace_MB": round(ws.numel() / 1e6, 1), "steps": len(times),
-            "note": "median of event-timed backward calls (fp32 staged scans), plus the "
+            "note": "median of event-timed backward calls, plus the "
                     "timed forward step"}
 
 

@@ -315,16 +315,18 @@ ssd_status ssd_backward_workspace_size(const ssd_problem* p, size_t* bytes);
  * backward contract": gradients of every input, exact for the forward).
  * The adjoint of the recurrence, dL/dh_t = exp(delta_{t+1} A) dL/dh_{t+1} +
  * dy_t (outer) C_t, is itself an SSD scan run backwards in time; the call
- * runs the staged forward four times on operands it prepares (the forward
- * recompute, then the adjoint read with B for dx and with x for dB, and the
+ * runs the staged kernels on operands it prepares: the forward recompute and
+ * the adjoint scan (read with B for dx) in full, then two chunk scans that
+ * reuse their chunk states transposed (the adjoint read with x for dB, the
  * forward state read with dy for dC).  The step-size gradient of a token is
  * the sum, over the later tokens of its chunk, of dL/dcs_l (cs the chunk's
  * cumulative log-decay): row minus column sums of the strictly lower triangle
  * of exp(cs_l - cs_s) (C_l . B_s) (dy_l . x_s), plus the terms of the states
  * entering and leaving the chunk; no two terms of it cancel, so it stays
- * accurate under strong decay.  Everything after the inputs is fp32 (fp32
- * chunk states, fp32 matrix products, fp64 sums where many terms meet), so
- * gradients are accurate to fp32 whatever the input dtype.  Packed mode is
+ * accurate under strong decay.  States and accumulations are fp32, sums of
+ * many terms fp64; products are fp32 for fp32 inputs and, for bf16 inputs,
+ * keep ~16 significant bits of each operand (bf16 hi + lo), well inside the
+ * bf16 tolerance.  Packed mode is
  * supported (each sequence runs backwards on its own).  initial_states,
  * dfinal_states and dinitial_states must be 16-byte aligned.
  * Results are bit-identical run to run (no atomics, fixed sum orders).
