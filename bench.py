@@ -61,9 +61,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--input-dt", action="store_true",
                     help="step size on the input term too (Mamba-2's discretised input)")
-    ap.add_argument("--backward", action="store_true",
-                    help="also time ssd_backward (upstream gradient ~ N(0,1)) and report the "
-                         "forward+backward rate in a 'fwd_bwd' object")
+    ap.add_argument("--no-backward", dest="backward", action="store_false",
+                    help="skip timing ssd_backward (by default it is timed with an upstream "
+                         "gradient ~ N(0,1) and the forward+backward rate is reported in a "
+                         "'fwd_bwd' object)")
+    ap.add_argument("--backward", dest="backward", action="store_true",
+                    help="time ssd_backward (the default)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle until this much CPU time has been spent (min 3 runs)")
     ap.add_argument("--cold-steps", type=int, default=10,
