@@ -27,6 +27,9 @@ Contents
                             recurrence's state at the chunk boundary).
 * ``state_passing``      -- the chunk-level recurrence applied to given chunk
                             states, SSD Reference "Inter-chunk propagation".
+* ``ssd_complex_fwd``    -- the fp64 sequential recurrence with a complex
+                            per-head A (``ssd_ref_complex.c``), SSD Reference
+                            "Math" with "_discretise" exp(softplus(dt) A).
 * ``ssd_bwd``            -- the reverse-mode gradient of ``ssd_fwd`` (every input,
                             the initial state included), the adjoint recurrence
                             taken token by token in reverse (``ssd_ref.c``,
@@ -49,12 +52,14 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ssd_ref.c")
+_SRC_COMPLEX = os.path.join(_HERE, "ssd_ref_complex.c")
 _LIB = os.path.join(_HERE, "libssd_ref.so")
 _lib = None
 
 
 def build(force: bool = True) -> str:
-    """Compile ``ssd_ref.c`` into ``libssd_ref.so`` with gcc (fp64, OpenMP).
+    """Compile ``ssd_ref.c`` and ``ssd_ref_complex.c`` into ``libssd_ref.so``
+    with gcc (fp64, OpenMP).
 
     ``-ffp-contract=off`` keeps every multiply and add separately rounded, as
     written; the portable ``-march=x86-64-v2`` lets the library built here run
@@ -64,7 +69,7 @@ def build(force: bool = True) -> str:
         return _LIB
     tmp = _LIB + ".tmp"
     cmd = ["gcc", "-O2", "-march=x86-64-v2", "-ffp-contract=off", "-fopenmp",
-           "-fPIC", "-shared", "-std=c99", _SRC, "-o", tmp, "-lm"]
+           "-fPIC", "-shared", "-std=c99", _SRC, _SRC_COMPLEX, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
@@ -443,3 +448,60 @@ def state_passing(S, cs, meta: ChunkMeta, initial_states=None):
             cur = np.exp(lam)[:, None, None] * cur + S[j]
         final[i] = cur
     return Hin, final
+
+
+# --------------------------------------------------------------------------
+# The complex-A scan (ssd_ref_complex.c).
+# --------------------------------------------------------------------------
+
+@dataclass
+class ComplexResult:
+    y: np.ndarray                 # complex128, like x
+    final_states: np.ndarray      # complex128, (nseq or b, H, D, N)
+
+
+def ssd_complex_fwd(x, B, C, dt, A, initial_states=None, cu_seqlens=None,
+                    threads=None) -> ComplexResult:
+    """Run the fp64 complex recurrence (SSD Reference, "Math" with complex A).
+
+    Batch mode: x (b, T, H, D), B and C (b, T, H, N) complex, dt (b, T, H) real,
+    A (H,) complex, initial_states (b, H, D, N) complex.  Packed mode: the same
+    without the batch axis plus ``cu_seqlens``.  Returns the full complex
+    output and the final states in the (D, N) layout.
+    """
+    x = np.asarray(x)
+    if cu_seqlens is None:
+        b, T = x.shape[0], x.shape[1]
+        cu = np.arange(b + 1, dtype=np.int64) * T
+        lead = 2
+    else:
+        cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+        lead = 1
+    H, D = x.shape[lead], x.shape[lead + 1]
+    N = np.shape(B)[lead + 1]
+
+    def cplx(a):
+        return None if a is None else np.ascontiguousarray(
+            np.asarray(a, dtype=np.complex128)).view(np.float64)
+
+    xs = cplx(np.reshape(x, (-1, H, D)))
+    Bs = cplx(np.reshape(B, (-1, H, N)))
+    Cs = cplx(np.reshape(C, (-1, H, N)))
+    dts = np.ascontiguousarray(np.reshape(np.asarray(dt, dtype=np.float64), (-1, H)))
+    A_ = cplx(np.broadcast_to(np.asarray(A, dtype=np.complex128), (H,)))
+    h0 = cplx(initial_states)
+    ntok = xs.shape[0]
+    nseq = len(cu) - 1
+    y = np.empty((ntok, H, D), dtype=np.complex128)
+    hfin = np.empty((nseq, H, D, N), dtype=np.complex128)
+    lib = _load()
+    f = lib.ssd_ref_complex_fwd
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), ctypes.c_int,
+                  ctypes.c_int, ctypes.c_int] + [ctypes.c_void_p] * 8 + [ctypes.c_int]
+    rc = f(ntok, nseq, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), H, D, N, _ptr(xs),
+           _ptr(Bs), _ptr(Cs), _ptr(dts), _ptr(A_), _ptr(h0), _ptr(y.view(np.float64)),
+           _ptr(hfin.view(np.float64)), int(threads or 0))
+    if rc != 0:
+        raise ValueError(f"ssd_ref_complex_fwd failed with code {rc}")
+    return ComplexResult(y.reshape(x.shape), hfin)

@@ -68,14 +68,33 @@ BWD_MUTANTS = {
 }
 
 
-CASES = [(n, MUTANTS[n], "tests/test_oracle_pins.py") for n in sorted(MUTANTS)] + \
-        [(n, BWD_MUTANTS[n], "tests/test_oracle_bwd_pins.py") for n in sorted(BWD_MUTANTS)]
+# slips in the complex-A scan (ssd_ref_complex.c), caught by tests/test_oracle_complex_pins.py
+COMPLEX_MUTANTS = {
+    "complex_C_conjugated": ("cx_mul(ct[2 * n], ct[2 * n + 1], sk[0], sk[1], &pr, &pi);",
+                             "cx_mul(ct[2 * n], -ct[2 * n + 1], sk[0], sk[1], &pr, &pi);"),
+    "complex_rotation_sign": ("ai = mag * sin(delta * Ai);", "ai = -mag * sin(delta * Ai);"),
+    "complex_no_softplus": ("const double delta = cx_softplus(dt[t * H + h]);",
+                            "const double delta = dt[t * H + h];"),
+    "complex_product_sign": ("*r = ar * br - ai * bi;", "*r = ar * br + ai * bi;"),
+    "complex_decay_after_add": ("sk[0] = dr + ur;\n          sk[1] = di + ui;",
+                                "sk[0] = ar * (sk[0] + ur) - ai * (sk[1] + ui);\n"
+                                "          sk[1] = ar * (sk[1] + ui) + ai * (sk[0] + ur);"),
+    "complex_initial_state_untransposed": (
+        "const double* src = h0 + ((((size_t)i * H + h) * D + d) * N + n) * 2;",
+        "const double* src = h0 + ((((size_t)i * H + h) * N + n) * D + d) * 2;"),
+}
+
+CASES = [(n, MUTANTS[n], "tests/test_oracle_pins.py", "ssd_ref.c") for n in sorted(MUTANTS)] + \
+        [(n, BWD_MUTANTS[n], "tests/test_oracle_bwd_pins.py", "ssd_ref.c")
+         for n in sorted(BWD_MUTANTS)] + \
+        [(n, COMPLEX_MUTANTS[n], "tests/test_oracle_complex_pins.py", "ssd_ref_complex.c")
+         for n in sorted(COMPLEX_MUTANTS)]
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("name,mutation,pins", CASES, ids=[c[0] for c in CASES])
-def test_pins_reject_mutant(name, mutation, pins, tmp_path):
-    src = open(os.path.join(ROOT, "oracle", "ssd_ref.c")).read()
+@pytest.mark.parametrize("name,mutation,pins,target", CASES, ids=[c[0] for c in CASES])
+def test_pins_reject_mutant(name, mutation, pins, target, tmp_path):
+    src = open(os.path.join(ROOT, "oracle", target)).read()
     before, after = mutation
     assert before in src, f"mutation site for {name} no longer in the oracle"
     work = tmp_path / "tree"
@@ -83,9 +102,10 @@ def test_pins_reject_mutant(name, mutation, pins, tmp_path):
                     ignore=shutil.ignore_patterns("*.so", "__pycache__", "*.tmp"))
     shutil.copytree(os.path.join(ROOT, "tests"), work / "tests",
                     ignore=shutil.ignore_patterns("__pycache__"))
-    (work / "oracle" / "ssd_ref.c").write_text(src.replace(before, after))
+    (work / "oracle" / target).write_text(src.replace(before, after))
     subprocess.run(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
-                    "-std=c99", str(work / "oracle" / "ssd_ref.c"), "-o",
+                    "-std=c99", str(work / "oracle" / "ssd_ref.c"),
+                    str(work / "oracle" / "ssd_ref_complex.c"), "-o",
                     str(work / "oracle" / "libssd_ref.so"), "-lm"], check=True)
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
                         pins], cwd=work, capture_output=True, text=True,
