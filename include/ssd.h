@@ -336,6 +336,70 @@ ssd_status ssd_backward_workspace_size(const ssd_problem* p, size_t* bytes);
 ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* workspace,
                         size_t ws_bytes, hipStream_t stream);
 
+/* ---------------------------------------------------------------- complex A */
+
+/* The complex-A SSD scan of Mamba-3-Lite (SSD Reference, "Math: the recurrence
+ * both functions implement", with "_discretise": abar_t = exp(softplus(dt_t) A_h)
+ * for a complex per-head A_h and a real step dt_t):
+ *
+ *     h_t = abar_t h_{t-1} + B_t (outer) x_t,     y_t = sum_n C_t[n] h_t[n, :]
+ *
+ * x (P), B and C (N) are complex and per head (SSD Reference, "Shape contract":
+ * B_t, C_t are (B, T, H, N)); nothing is conjugated.  There is no dt bias, no
+ * D skip and no gate.  Evaluated chunkwise as the page's production scan does
+ * ("Chunking and the discretized log-decay", "Intra-chunk outputs and
+ * per-chunk states", "Inter-chunk propagation" with decay_chunk[z, c] =
+ * exp(CD[z-1] - CD[c]) 1[z > c] and the init term exp(CD[z-1]) H_{-1},
+ * "Readout"), batch mode only.
+ *
+ * Complex tensors hold interleaved (re, im) float32 pairs (complex64); their
+ * ssd_tensor dtype is SSD_F32 and their strides count COMPLEX elements.
+ */
+typedef struct ssd_complex_problem {
+  int32_t batch;       /* b >= 1 */
+  int32_t seqlen;      /* T >= 0 */
+  int32_t nheads;      /* H >= 1, batch * nheads <= 65535 */
+  int32_t headdim;     /* P (the page's D): multiple of 16, <= 128 */
+  int32_t dstate;      /* N: multiple of 16, <= 128 */
+  int32_t chunk_size;  /* C: 32, 64, 128 or 256 (the result does not depend on it) */
+} ssd_complex_problem;
+
+typedef struct ssd_complex_fwd_args {
+  ssd_tensor x;        /* (b, T, H, P) complex; rows 16-byte aligned */
+  ssd_tensor B;        /* (b, T, H, N) complex; rows 16-byte aligned */
+  ssd_tensor C;        /* (b, T, H, N) complex; rows 16-byte aligned */
+  ssd_tensor dt;       /* (b, T, H) float32 real, raw (softplus is applied) */
+  const float* A;      /* (H) complex: 2H floats (re, im), device */
+  const float* initial_states; /* (b, H, P, N) complex, contiguous, 16-byte
+                                  aligned, or NULL (zero); the page's (D, N)
+                                  layout ("Shape contract") */
+  ssd_tensor out;      /* (b, T, H, P): out_complex = 0: float32, the real part
+                          of y (the page's chunkwise return contract); strides
+                          in floats.  out_complex = 1: complex y, strides in
+                          complex elements */
+  int32_t out_complex;
+  float* final_states; /* (b, H, P, N) complex, contiguous, 16-byte aligned, or NULL */
+} ssd_complex_fwd_args;
+
+/* Validate a complex problem (host only).  On failure sets the message. */
+ssd_status ssd_complex_problem_check(const ssd_complex_problem* p);
+
+/* Bytes of workspace ssd_complex_forward needs: the per-chunk complex states
+ * (b * ceil(T/C) * H * P * N * 8 bytes) and each chunk's step sum. */
+ssd_status ssd_complex_workspace_size(const ssd_complex_problem* p, size_t* bytes);
+
+/* The forward pass: three kernels on `stream` -- every chunk's end state from a
+ * zero start (SSD Reference "Algorithm and tensor-shape contract", step 6:
+ * state = Xc^T (decay_states * Bc)), the sequential pass over chunks
+ * ("Inter-chunk propagation"), and the output of every chunk (steps 3-5, Y_diag
+ * = (L * Cb) Xc, plus "Readout": Y_off = C . state . exp(A_cumsum)).  Products
+ * are fp32 matrix instructions, accumulation fp32.  workspace: at least
+ * ssd_complex_workspace_size bytes, 256-byte aligned, caller-owned, contents
+ * need not be initialised, not shared by calls that overlap in time.  Results
+ * are bit-identical run to run. */
+ssd_status ssd_complex_forward(const ssd_complex_problem* p, const ssd_complex_fwd_args* a,
+                               void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- errors */
 
 const char* ssd_status_string(ssd_status s);

@@ -833,3 +833,127 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- complex A
+
+static ssd_status check_cx_problem(const ssd_complex_problem* p) {
+  if (!p) return fail(SSD_ERR_NULL, "problem is NULL");
+  if (p->batch < 1) return fail(SSD_ERR_SHAPE, "batch = %d must be >= 1", p->batch);
+  if (p->seqlen < 0) return fail(SSD_ERR_SHAPE, "seqlen = %d must be >= 0", p->seqlen);
+  if (p->nheads < 1) return fail(SSD_ERR_SHAPE, "nheads = %d must be >= 1", p->nheads);
+  if ((int64_t)p->batch * p->nheads > 65535)
+    return fail(SSD_ERR_UNSUPPORTED, "batch * nheads = %lld exceeds 65535",
+                (long long)p->batch * p->nheads);
+  if (p->headdim < 16 || p->headdim > 128 || p->headdim % 16 != 0)
+    return fail(SSD_ERR_UNSUPPORTED, "headdim = %d: must be a multiple of 16 in [16, 128]",
+                p->headdim);
+  if (p->dstate < 16 || p->dstate > 128 || p->dstate % 16 != 0)
+    return fail(SSD_ERR_UNSUPPORTED, "dstate = %d: must be a multiple of 16 in [16, 128]",
+                p->dstate);
+  const int C = p->chunk_size;
+  if (C != 32 && C != 64 && C != 128 && C != 256)
+    return fail(SSD_ERR_UNSUPPORTED, "chunk_size = %d: must be 32, 64, 128 or 256", C);
+  if ((int64_t)p->batch * p->seqlen > INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "batch * seqlen exceeds 2^31 - 1 tokens");
+  return SSD_OK;
+}
+
+// A complex operand: float32 pairs, rows 16-byte aligned (strides even in
+// complex elements).
+static ssd_status check_cx_tensor(const ssd_tensor& t, const char* name, bool required) {
+  if (!t.data) {
+    if (required) return fail(SSD_ERR_NULL, "%s is NULL", name);
+    return SSD_OK;
+  }
+  if (t.dtype != SSD_F32) return fail(SSD_ERR_DTYPE, "%s must be complex64 (SSD_F32 pairs)", name);
+  if (reinterpret_cast<uintptr_t>(t.data) % 16 != 0)
+    return fail(SSD_ERR_STRIDE, "%s: data pointer is not 16-byte aligned", name);
+  for (int i = 0; i < 3; ++i) {
+    if (t.stride[i] < 0) return fail(SSD_ERR_STRIDE, "%s: stride[%d] is negative", name, i);
+    if (t.stride[i] % 2 != 0)
+      return fail(SSD_ERR_STRIDE,
+                  "%s: stride[%d] = %lld complex elements does not keep rows 16-byte aligned",
+                  name, i, (long long)t.stride[i]);
+  }
+  return SSD_OK;
+}
+
+struct CxWorkspace {
+  size_t states, lam, total;
+};
+
+static CxWorkspace cx_workspace(const ssd_complex_problem* p) {
+  const int64_t nc = cdiv(p->seqlen, p->chunk_size);
+  CxWorkspace w;
+  w.states = 0;
+  w.lam = align256((size_t)p->batch * nc * p->nheads * p->headdim * p->dstate * 8);
+  w.total = w.lam + align256((size_t)p->batch * p->nheads * nc * sizeof(float));
+  return w;
+}
+
+extern "C" {
+
+ssd_status ssd_complex_problem_check(const ssd_complex_problem* p) {
+  SSD_TRY(check_cx_problem(p));
+  return ok();
+}
+
+ssd_status ssd_complex_workspace_size(const ssd_complex_problem* p, size_t* bytes) {
+  SSD_TRY(check_cx_problem(p));
+  if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
+  *bytes = cx_workspace(p).total;
+  return ok();
+}
+
+ssd_status ssd_complex_forward(const ssd_complex_problem* p, const ssd_complex_fwd_args* a,
+                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  SSD_TRY(check_cx_problem(p));
+  if (!a) return fail(SSD_ERR_NULL, "args is NULL");
+  const bool tok = (int64_t)p->batch * p->seqlen > 0;
+  SSD_TRY(check_cx_tensor(a->x, "x", tok));
+  SSD_TRY(check_cx_tensor(a->B, "B", tok));
+  SSD_TRY(check_cx_tensor(a->C, "C", tok));
+  if (tok) {
+    if (!a->dt.data) return fail(SSD_ERR_NULL, "dt is NULL");
+    if (a->dt.dtype != SSD_F32) return fail(SSD_ERR_DTYPE, "dt must be float32");
+    if (reinterpret_cast<uintptr_t>(a->dt.data) % 4 != 0)
+      return fail(SSD_ERR_STRIDE, "dt: data pointer is not element aligned");
+    for (int i = 0; i < 3; ++i)
+      if (a->dt.stride[i] < 0) return fail(SSD_ERR_STRIDE, "dt: stride[%d] is negative", i);
+    if (!a->out.data) return fail(SSD_ERR_NULL, "out is NULL");
+    if (a->out.dtype != SSD_F32) return fail(SSD_ERR_DTYPE, "out must be float32 or complex64");
+    const size_t oal = a->out_complex ? 8 : 4;
+    if (reinterpret_cast<uintptr_t>(a->out.data) % oal != 0)
+      return fail(SSD_ERR_STRIDE, "out: data pointer is not element aligned");
+    for (int i = 0; i < 3; ++i)
+      if (a->out.stride[i] < 0) return fail(SSD_ERR_STRIDE, "out: stride[%d] is negative", i);
+  }
+  if (a->out_complex != 0 && a->out_complex != 1)
+    return fail(SSD_ERR_SHAPE, "out_complex = %d: must be 0 or 1", a->out_complex);
+  if (!a->A) return fail(SSD_ERR_NULL, "A is NULL");
+  if (reinterpret_cast<uintptr_t>(a->A) % 8 != 0)
+    return fail(SSD_ERR_STRIDE, "A: data pointer is not 8-byte aligned");
+  if (reinterpret_cast<uintptr_t>(a->initial_states) % 16 != 0)
+    return fail(SSD_ERR_STRIDE, "initial_states is not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(a->final_states) % 16 != 0)
+    return fail(SSD_ERR_STRIDE, "final_states is not 16-byte aligned");
+  const CxWorkspace w = cx_workspace(p);
+  if (w.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < w.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, w.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  ssd::CxGeo g;
+  g.b = p->batch; g.T = p->seqlen; g.H = p->nheads; g.P = p->headdim; g.N = p->dstate;
+  g.C = p->chunk_size;
+  g.nc = (int)cdiv(p->seqlen, p->chunk_size);
+  SSD_HIP(ssd::launch_complex_fwd(g, targ(a->x), targ(a->B), targ(a->C), targ(a->dt), a->A,
+                                  a->initial_states, targ(a->out), a->out_complex,
+                                  a->final_states, reinterpret_cast<float*>(ws + w.states),
+                                  reinterpret_cast<float*>(ws + w.lam), stream),
+          "complex forward launch");
+  return ok();
+}
+
+}  // extern "C"

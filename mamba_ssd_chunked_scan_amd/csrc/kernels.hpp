@@ -108,4 +108,16 @@ hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* CB
                                  TArg ddt, double* part, float* dA, float* ddt_bias, float* dD,
                                  float* dh0, hipStream_t s);
 
+// ---- complex-A forward (complex_fwd.hip): batch mode, per-head complex B, C
+struct CxGeo {
+  int b, T, H, P, N, C;
+  int nc;  // ceil(T / C)
+};
+// x, B, C, out (complex) strides in complex elements; dt, out (real) in floats.
+// states: b * nc * H * P * N complex (written, then overwritten in place by the
+// carry-in states); lam: b * H * nc floats (each chunk's step sum).
+hipError_t launch_complex_fwd(const CxGeo& g, TArg x, TArg B, TArg Cm, TArg dt, const float* A,
+                              const float* h0, TArg out, int out_complex, float* hfinal,
+                              float* states, float* lam, hipStream_t s);
+
 }  // namespace ssd

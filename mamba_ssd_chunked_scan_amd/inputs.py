@@ -144,3 +144,80 @@ def edge_seqlens(chunk_size: int, total: int) -> tuple:
         raise ValueError("total too small for the edge-length pattern")
     lens.append(total - s)
     return tuple(lens)
+
+
+# ------------------------------------------------------------------ complex A
+#
+# The complex-A scan of the Mamba-3-Lite SSD Reference page.  Its production
+# shape is the page's 434M configuration (batch 8, seq 2048, chunk 64, 16 heads,
+# head dim 64, state dim 64; complex64 throughout, dt float32).  The page's own
+# tests draw random complex A, B, C, x and dt; the recipe below keeps the real
+# workloads' step-size and decay-rate ranges (the complex call has no dt bias,
+# so the per-head offset is folded into dt).  One Generator(PCG64(seed)), in
+# this order:
+#   1. x  = N(0,1) + i N(0,1)                       (b, T, H, P)  (real part, then imaginary)
+#   2. B  = N(0,1) + i N(0,1)                       (b, T, H, N)
+#   3. C  = N(0,1) + i N(0,1)                       (b, T, H, N)
+#   4. dt = N(0,1) + log(expm1(u_h)),  u_h = exp(U(ln 1e-3, ln 0.1))   (b, T, H)
+#      so softplus of the per-head offset is u_h
+#   5. A_h = -exp(U(ln 1, ln 16)) + i U(-pi, pi)    (H)
+#   6. initial state N(0,1) + i N(0,1)              (b, H, P, N)  if asked
+# Values are rounded to complex64 / float32; the oracle consumes those values.
+
+@dataclass
+class ComplexWorkload:
+    name: str
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    dstate: int
+    chunk_size: int
+    seed: int = 0
+    initial_states: bool = False
+
+    @property
+    def tokens(self) -> int:
+        return self.batch * self.seqlen
+
+
+@dataclass
+class ComplexInputs:
+    x: np.ndarray        # complex64 (b, T, H, P)
+    B: np.ndarray        # complex64 (b, T, H, N)
+    C: np.ndarray        # complex64 (b, T, H, N)
+    dt: np.ndarray       # float32 (b, T, H)
+    A: np.ndarray        # complex64 (H,)
+    h0: np.ndarray | None  # complex64 (b, H, P, N)
+
+
+def _cnormal(rng, shape):
+    re = rng.standard_normal(shape, dtype=np.float32)
+    im = rng.standard_normal(shape, dtype=np.float32)
+    out = np.empty(shape, dtype=np.complex64)
+    out.real = re
+    out.imag = im
+    return out
+
+
+def make_complex_inputs(w: ComplexWorkload, seed: int | None = None) -> ComplexInputs:
+    rng = np.random.Generator(np.random.PCG64(w.seed if seed is None else seed))
+    b, T, H, P, N = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate
+    x = _cnormal(rng, (b, T, H, P))
+    B = _cnormal(rng, (b, T, H, N))
+    C = _cnormal(rng, (b, T, H, N))
+    dt = rng.standard_normal((b, T, H), dtype=np.float32)
+    u = np.exp(rng.uniform(np.log(1e-3), np.log(1e-1), H))
+    dt = (dt + np.log(np.expm1(u)).astype(np.float32)).astype(np.float32)
+    A = (-np.exp(rng.uniform(np.log(1.0), np.log(16.0), H))
+         + 1j * rng.uniform(-np.pi, np.pi, H)).astype(np.complex64)
+    h0 = _cnormal(rng, (b, H, P, N)) if w.initial_states else None
+    return ComplexInputs(x, B, C, dt, A, h0)
+
+
+COMPLEX_WORKLOADS = {
+    "complex_tiny": ComplexWorkload("complex_tiny", 2, 300, 3, 32, 32, 64, seed=2000,
+                                    initial_states=True),
+    # SSD Reference (Mamba-3-Lite) 434M configuration: B=8, T=2048, C=64, H=16, D=64, N=64
+    "complex_434m": ComplexWorkload("complex_434m", 8, 2048, 16, 64, 64, 64, seed=2001),
+}

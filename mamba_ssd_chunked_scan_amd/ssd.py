@@ -68,11 +68,25 @@ class SsdBwdArgs(ctypes.Structure):
                 ("dD", ctypes.c_void_p), ("dinitial_states", ctypes.c_void_p)]
 
 
+class SsdComplexProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
+                ("dstate", ctypes.c_int32), ("chunk_size", ctypes.c_int32)]
+
+
+class SsdComplexFwdArgs(ctypes.Structure):
+    _fields_ = [("x", SsdTensor), ("B", SsdTensor), ("C", SsdTensor), ("dt", SsdTensor),
+                ("A", ctypes.c_void_p), ("initial_states", ctypes.c_void_p),
+                ("out", SsdTensor), ("out_complex", ctypes.c_int32),
+                ("final_states", ctypes.c_void_p)]
+
+
 _lib = None
 EXPORTS = ("ssd_problem_check", "ssd_num_chunks", "ssd_varlen_meta_len", "ssd_workspace_size",
            "ssd_varlen_chunk_meta", "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum",
            "ssd_bmm_chunk", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
            "ssd_forward", "ssd_backward_workspace_size", "ssd_backward",
+           "ssd_complex_problem_check", "ssd_complex_workspace_size", "ssd_complex_forward",
            "ssd_status_string", "ssd_last_error_message", "ssd_version")
 
 
@@ -105,10 +119,16 @@ def lib():
                                   ctypes.c_size_t, vp]
         L.ssd_backward_workspace_size.argtypes = [P(SsdProblem), P(ctypes.c_size_t)]
         L.ssd_backward.argtypes = [P(SsdProblem), P(SsdBwdArgs), vp, ctypes.c_size_t, vp]
+        L.ssd_complex_problem_check.argtypes = [P(SsdComplexProblem)]
+        L.ssd_complex_workspace_size.argtypes = [P(SsdComplexProblem), P(ctypes.c_size_t)]
+        L.ssd_complex_forward.argtypes = [P(SsdComplexProblem), P(SsdComplexFwdArgs), vp,
+                                          ctypes.c_size_t, vp]
         for name in ("ssd_problem_check", "ssd_workspace_size", "ssd_varlen_chunk_meta",
                      "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum", "ssd_bmm_chunk",
                      "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
-                     "ssd_backward_workspace_size", "ssd_backward"):
+                     "ssd_backward_workspace_size", "ssd_backward",
+                     "ssd_complex_problem_check", "ssd_complex_workspace_size",
+                     "ssd_complex_forward"):
             getattr(L, name).restype = st
         L.ssd_status_string.argtypes = [ctypes.c_int]
         L.ssd_status_string.restype = ctypes.c_char_p
@@ -413,3 +433,95 @@ def ssd_backward(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_sta
     _check(lib().ssd_backward(ctypes.byref(prob.c()), ctypes.byref(a), workspace.data_ptr(),
                               workspace.numel(), _stream(stream)))
     return g
+
+
+# ------------------------------------------------------------------ complex A
+
+def _cx_tensor(t: torch.Tensor | None) -> SsdTensor:
+    """ssd_tensor of a complex64 (b, T, H, X) tensor: float32 pairs, strides in
+    complex elements (the innermost must be 1)."""
+    s = SsdTensor()
+    s.dtype = F32
+    if t is None or t.numel() == 0:
+        s.data = None
+        return s
+    if t.dtype != torch.complex64:
+        raise SSDError(3, f"expected complex64, got {t.dtype}")
+    if t.dim() != 4:
+        raise SSDError(2, f"expected a 4-D tensor, got shape {tuple(t.shape)}")
+    if t.stride(3) != 1 and t.shape[3] > 1:
+        raise SSDError(4, "innermost dimension must be contiguous")
+    s.data = t.data_ptr()
+    for i in range(3):
+        s.stride[i] = int(t.stride(i))
+    return s
+
+
+@dataclass
+class ComplexProblem:
+    batch: int
+    seqlen: int
+    nheads: int
+    headdim: int
+    dstate: int
+    chunk_size: int = 64
+
+    def c(self) -> SsdComplexProblem:
+        p = SsdComplexProblem()
+        p.batch, p.seqlen, p.nheads = self.batch, self.seqlen, self.nheads
+        p.headdim, p.dstate, p.chunk_size = self.headdim, self.dstate, self.chunk_size
+        return p
+
+    def check(self):
+        _check(lib().ssd_complex_problem_check(ctypes.byref(self.c())))
+
+    def workspace_size(self) -> int:
+        n = ctypes.c_size_t(0)
+        _check(lib().ssd_complex_workspace_size(ctypes.byref(self.c()), ctypes.byref(n)))
+        return int(n.value)
+
+
+def ssd_complex_forward(x, B, C, dt, A, initial_states=None, chunk_size=64,
+                        out_complex=False, out=None, final_states=None, workspace=None,
+                        stream=None):
+    """The complex-A SSD forward (ssd_complex_forward).
+
+    x (b, T, H, P), B and C (b, T, H, N) complex64; dt (b, T, H) float32; A (H,)
+    complex64; initial_states (b, H, P, N) complex64 or None.  Returns
+    (out, final_states): out is float32 (the real part) or, with out_complex,
+    complex64; final_states (b, H, P, N) complex64.
+    """
+    b, T, H, P = x.shape
+    N = B.shape[3]
+    prob = ComplexProblem(b, T, H, P, N, chunk_size)
+    dev = x.device
+    if out is None:
+        out = torch.empty((b, T, H, P), dtype=torch.complex64 if out_complex else torch.float32,
+                          device=dev)
+    if final_states is None:
+        final_states = torch.empty((b, H, P, N), dtype=torch.complex64, device=dev)
+    if initial_states is not None and not initial_states.is_contiguous():
+        raise SSDError(4, "initial_states must be contiguous")
+    if not final_states.is_contiguous():
+        raise SSDError(4, "final_states must be contiguous")
+    if A.dtype != torch.complex64 or not A.is_contiguous():
+        raise SSDError(3, "A must be a contiguous complex64 (H,) tensor")
+    if dt.dtype != torch.float32:
+        raise SSDError(3, "dt must be float32")
+    ws_bytes = prob.workspace_size()
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    a = SsdComplexFwdArgs()
+    a.x, a.B, a.C = _cx_tensor(x), _cx_tensor(B), _cx_tensor(C)
+    a.dt = tensor_arg(dt)
+    a.A = A.data_ptr()
+    a.initial_states = _ptr(initial_states)
+    if out_complex:
+        a.out = _cx_tensor(out)
+    else:
+        a.out = tensor_arg(out)
+    a.out_complex = 1 if out_complex else 0
+    a.final_states = final_states.data_ptr()
+    _check(lib().ssd_complex_forward(ctypes.byref(prob.c()), ctypes.byref(a),
+                                     workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out, final_states

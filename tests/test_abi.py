@@ -238,3 +238,58 @@ def test_host_chunk_table_rejects_bad_cu_seqlens():
         arr = (ctypes.c_int32 * len(cu))(*cu)
         out = (ctypes.c_int32 * n)()
         assert L.ssd_varlen_chunk_meta_host(ctypes.byref(c), arr, out, n) == 2
+
+
+# ------------------------------------------------------------------ complex A
+
+def cx_prob(**kw):
+    base = dict(batch=8, seqlen=2048, nheads=16, headdim=64, dstate=64, chunk_size=64)
+    base.update(kw)
+    return ssd.ComplexProblem(**base)
+
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(headdim=144), 5, "headdim"),
+    (dict(headdim=40), 5, "headdim"),
+    (dict(dstate=24), 5, "dstate"),
+    (dict(chunk_size=48), 5, "chunk_size"),
+    (dict(batch=0), 2, "batch"),
+    (dict(seqlen=-1), 2, "seqlen"),
+    (dict(nheads=0), 2, "nheads"),
+    (dict(batch=5000, nheads=16), 5, "nheads"),
+])
+def test_complex_problem_check_names_the_dim(kw, code, word):
+    L = ssd.lib()
+    rc = L.ssd_complex_problem_check(ctypes.byref(cx_prob(**kw).c()))
+    assert rc == code
+    assert word in L.ssd_last_error_message().decode()
+
+
+def test_complex_workspace_size():
+    p = cx_prob()
+    nc = 2048 // 64
+    states = 8 * nc * 16 * 64 * 64 * 8
+    lam = 8 * 16 * nc * 4
+    r256 = lambda v: (v + 255) // 256 * 256
+    assert p.workspace_size() == r256(states) + r256(lam)
+    assert cx_prob(seqlen=0).workspace_size() == 0
+
+
+def test_complex_forward_rejects_bad_arguments_before_launching():
+    L = ssd.lib()
+    p = cx_prob(batch=1, seqlen=64, nheads=2, headdim=16, dstate=16)
+    a = ssd.SsdComplexFwdArgs()
+    # x missing
+    rc = L.ssd_complex_forward(ctypes.byref(p.c()), ctypes.byref(a), None, 0, None)
+    assert rc == 1 and "x" in L.ssd_last_error_message().decode()
+    # x of the wrong dtype
+    buf = (ctypes.c_char * 4096)()
+    base = (ctypes.addressof(buf) + 255) // 256 * 256
+    a.x.data, a.x.dtype = base, 1
+    rc = L.ssd_complex_forward(ctypes.byref(p.c()), ctypes.byref(a), None, 0, None)
+    assert rc == 3 and "complex64" in L.ssd_last_error_message().decode()
+    # odd stride (rows not 16-byte aligned)
+    a.x.dtype = 0
+    a.x.stride[0], a.x.stride[1], a.x.stride[2] = 64 * 2 * 16, 2 * 16 + 1, 16
+    rc = L.ssd_complex_forward(ctypes.byref(p.c()), ctypes.byref(a), None, 0, None)
+    assert rc == 4 and "stride[1]" in L.ssd_last_error_message().decode()

@@ -1,0 +1,126 @@
+"""Parity of the complex-A forward (ssd_complex_forward) with the fp64 oracle.
+
+The oracle is the sequential complex recurrence (SSD Reference, "Math" with
+"_discretise"), pinned in test_oracle_complex_pins.py.  Inputs are complex64 /
+float32, so the gate is the fp32 one: max|gpu - ref| / RMS(ref) <= 1e-4, for
+the real output (the page's chunkwise return contract), the full complex
+output and the final state.  Every call goes through the C ABI.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import TOL_F32, err
+from mamba_ssd_chunked_scan_amd import ssd
+from mamba_ssd_chunked_scan_amd.inputs import (COMPLEX_WORKLOADS, ComplexWorkload,
+                                               make_complex_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+def dev(a):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def run(inp, C, out_complex=False, use_h0=True, views=None):
+    x, B, Cm = (dev(inp.x), dev(inp.B), dev(inp.C)) if views is None else views
+    y, fin = ssd.ssd_complex_forward(x, B, Cm, dev(inp.dt), dev(inp.A),
+                                     initial_states=dev(inp.h0) if use_h0 else None,
+                                     chunk_size=C, out_complex=out_complex)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), fin.cpu().numpy()
+
+
+def reference(inp, use_h0=True):
+    return oracle.ssd_complex_fwd(inp.x, inp.B, inp.C, inp.dt, inp.A,
+                                  initial_states=inp.h0 if use_h0 else None)
+
+
+def check(y, fin, r, out_complex):
+    ry = r.y if out_complex else r.y.real
+    e_y = err(y.view(np.float32), ry.view(np.float64)) if out_complex else err(y, ry)
+    e_f = err(fin.view(np.float32), r.final_states.view(np.float64))
+    print(f"complex forward: out err {e_y:.2e}, final-state err {e_f:.2e}")
+    assert e_y <= TOL_F32 and e_f <= TOL_F32, (e_y, e_f)
+
+
+@pytest.mark.parametrize("C", [32, 64, 128, 256])
+@pytest.mark.parametrize("out_complex", [False, True])
+def test_small_every_chunk_size(C, out_complex):
+    # several chunks, a ragged tail (300 = 4 x 64 + 44), an initial state
+    inp = make_complex_inputs(COMPLEX_WORKLOADS["complex_tiny"])
+    y, fin = run(inp, C, out_complex)
+    check(y, fin, reference(inp), out_complex)
+
+
+@pytest.mark.parametrize("shape", [
+    (1, 1, 2, 16, 16, 64),     # a single token
+    (1, 64, 2, 16, 16, 64),    # exactly one chunk
+    (2, 65, 2, 48, 80, 32),    # one token past a chunk edge; uneven tile counts
+    (1, 200, 5, 128, 128, 64), # the largest head and state dims
+    (3, 129, 1, 16, 128, 128),
+])
+def test_shapes(shape):
+    b, T, H, P, N, C = shape
+    w = ComplexWorkload("shape", b, T, H, P, N, C, seed=T * 7 + P, initial_states=True)
+    inp = make_complex_inputs(w)
+    for oc in (False, True):
+        y, fin = run(inp, C, oc)
+        check(y, fin, reference(inp), oc)
+
+
+def test_no_initial_state_and_no_tokens():
+    w = ComplexWorkload("noh0", 2, 190, 3, 32, 48, 64, seed=5)
+    inp = make_complex_inputs(w)
+    y, fin = run(inp, 64, use_h0=False)
+    check(y, fin, reference(inp, use_h0=False), False)
+    # T = 0: the final state is the initial state
+    w0 = ComplexWorkload("empty", 2, 0, 3, 16, 16, 64, seed=6, initial_states=True)
+    inp0 = make_complex_inputs(w0)
+    y0, fin0 = run(inp0, 64)
+    assert y0.shape == (2, 0, 3, 16)
+    assert np.array_equal(fin0, inp0.h0)
+
+
+def test_strided_views_of_one_buffer():
+    # x, B, C as views into one (b, T, H, P + 2N) complex buffer
+    w = ComplexWorkload("views", 2, 250, 4, 32, 16, 64, seed=9, initial_states=True)
+    inp = make_complex_inputs(w)
+    P, N = w.headdim, w.dstate
+    packed = np.concatenate([inp.x, inp.B, inp.C], axis=-1)
+    t = dev(packed)
+    views = (t[..., :P], t[..., P:P + N], t[..., P + N:])
+    y, fin = run(inp, 64, views=views)
+    check(y, fin, reference(inp), False)
+
+
+def test_decay_extremes_and_pure_rotation():
+    # very strong decay (memoryless), a pure rotation (Re A = 0: no decay at all)
+    w = ComplexWorkload("ext", 1, 300, 4, 16, 16, 64, seed=13, initial_states=True)
+    inp = make_complex_inputs(w)
+    inp.A = np.array([-1e4 + 0.5j, 0.0 + 2.0j, -1e-3 - 3.0j, 0.01 + 0.0j], dtype=np.complex64)
+    y, fin = run(inp, 64)
+    check(y, fin, reference(inp), False)
+
+
+def test_run_to_run_bit_identical():
+    inp = make_complex_inputs(COMPLEX_WORKLOADS["complex_tiny"])
+    a = run(inp, 64, True)
+    b = run(inp, 64, True)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_434m_config_sampled():
+    # the SSD Reference's 434M shape, on the GPU in full; the oracle on sampled
+    # (batch row, head) pairs (heads and rows are independent)
+    w = COMPLEX_WORKLOADS["complex_434m"]
+    inp = make_complex_inputs(w)
+    y, fin = run(inp, w.chunk_size, use_h0=False)
+    rows, heads = [0, 5], [0, 9, 15]
+    sub = lambda a: a[rows][:, :, heads]
+    r = oracle.ssd_complex_fwd(sub(inp.x), sub(inp.B), sub(inp.C), sub(inp.dt), inp.A[heads])
+    e_y = err(y[rows][:, :, heads], r.y.real)
+    e_f = err(fin[rows][:, heads].view(np.float32), r.final_states.view(np.float64))
+    print(f"434M sampled: out err {e_y:.2e}, final-state err {e_f:.2e}")
+    assert e_y <= TOL_F32 and e_f <= TOL_F32
