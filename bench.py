@@ -8,6 +8,9 @@ inputs already resident in HBM.  Prints ONE JSON line (rank 0).
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload nemotron]
                     [--algo staged|fused|auto] [--no-cpu-baseline] [--input-dt]
 
+--workload complex_434m times the complex-A scan of the Mamba-3-Lite SSD
+Reference at its 434M shape (three kernels; complex64 inputs, real output).
+
 --input-dt puts the step size on the input term as well (delta x (outer) B,
 the discretised input of the Mamba-2 models); the default is the recurrence
 as the pages write it.
@@ -46,6 +49,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA, published
+FP32_PEAK_TFLOPS = 157.3     # dense fp32 MFMA, published
 
 
 def parse():
@@ -186,11 +190,14 @@ def main():
         sys.exit(2)
     import torch
     from mamba_ssd_chunked_scan_amd import ssd
-    from mamba_ssd_chunked_scan_amd.inputs import WORKLOADS, make_inputs
+    from mamba_ssd_chunked_scan_amd.inputs import COMPLEX_WORKLOADS, WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.workload in COMPLEX_WORKLOADS:
+        bench_complex(args, COMPLEX_WORKLOADS[args.workload])
+        return
     w = WORKLOADS[args.workload]
     inp = make_inputs(w)
     dev = torch.device("cuda:0")
@@ -415,6 +422,151 @@ def time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu, fwd_ms):
             "workspace_MB": round(ws.numel() / 1e6, 1), "steps": len(times),
             "note": "median of event-timed backward calls, plus the "
                     "timed forward step"}
+
+
+def complex_stage_model(w):
+    """Algorithmic HBM bytes and useful matrix flops per launch of the three
+    complex-A kernels (complex64 = 8 bytes; a complex multiply-add is 8 real
+    flops, one whose imaginary part is not needed 4).  Each input is read once,
+    each output written once; C.B^T and the intra-chunk product count their
+    causal half only; the output is the real part (float32)."""
+    b, T, H, P, N, C = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk_size
+    nc = -(-T // C)
+    K = b * nc
+    tok = b * T
+    x, bc, dt = tok * H * P * 8, tok * H * N * 8, tok * H * 4
+    st, lam, fin, out = K * H * P * N * 8, K * H * 4, b * H * P * N * 8, tok * H * P * 4
+    tri = C * (C + 1) // 2
+    nb = {"cx_chunk_state": x + bc + dt + st + lam,
+          "cx_state_passing": 2 * st + lam + fin,
+          "cx_chunk_scan": x + 2 * bc + dt + st + out}
+    nf = {"cx_chunk_state": 8 * K * H * C * P * N,
+          "cx_state_passing": 8 * K * H * P * N,
+          "cx_chunk_scan": K * H * (8 * tri * N + 4 * tri * P + 4 * C * N * P)}
+    return nb, nf
+
+
+def bench_complex(args, w):
+    """The complex-A forward: ssd_complex_chunk_state, ssd_complex_state_passing,
+    ssd_complex_chunk_scan (what ssd_complex_forward launches), each bracketed
+    by HIP events on the stream it runs on."""
+    import torch
+    from mamba_ssd_chunked_scan_amd import ssd
+    from mamba_ssd_chunked_scan_amd.inputs import make_complex_inputs
+
+    inp = make_complex_inputs(w)
+    dev = torch.device("cuda:0")
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    x, B, C, dt, A = up(inp.x), up(inp.B), up(inp.C), up(inp.dt), up(inp.A)
+    h0 = up(inp.h0) if inp.h0 is not None else None
+    prob = ssd.ComplexProblem(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk_size)
+    nc = -(-w.seqlen // w.chunk_size)
+    st = torch.empty((w.batch * nc, w.nheads, w.headdim, w.dstate), dtype=torch.complex64,
+                     device=dev)
+    lam = torch.empty((w.batch, w.nheads, nc), dtype=torch.float32, device=dev)
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.complex64,
+                      device=dev)
+    out = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim), dtype=torch.float32, device=dev)
+    names = ["cx_chunk_state", "cx_state_passing", "cx_chunk_scan"]
+    calls = {
+        "cx_chunk_state": lambda: ssd.ssd_complex_chunk_state(prob, x, B, dt, A, st, lam),
+        "cx_state_passing": lambda: ssd.ssd_complex_state_passing(prob, A, lam, st, h0, fin),
+        "cx_chunk_scan": lambda: ssd.ssd_complex_chunk_scan(prob, x, B, C, dt, A, st, out),
+    }
+
+    def step(events=None):
+        for n in names:
+            if events is None:
+                calls[n]()
+                continue
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            calls[n]()
+            e1.record()
+            events.setdefault(n, []).append((e0, e1))
+
+    for _ in range(args.warmup):
+        step()
+    # the stage sequence is exactly ssd_complex_forward
+    ref_out, ref_fin = ssd.ssd_complex_forward(x, B, C, dt, A, initial_states=h0,
+                                               chunk_size=w.chunk_size)
+    torch.cuda.synchronize()
+    if not (torch.equal(ref_out, out) and torch.equal(ref_fin, fin)):
+        raise RuntimeError("stage sequence differs from ssd_complex_forward")
+    events = {}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in events[n]])) for n in names}
+    ms_per_step = wall * 1e3 / args.steps
+    nb, nf = complex_stage_model(w)
+
+    def roof(n):
+        t_hbm = nb[n] / (HBM_PEAK_GBS * 1e9)
+        t_mfma = nf[n] / (FP32_PEAK_TFLOPS * 1e12)
+        return ("hbm", t_hbm) if t_hbm >= t_mfma else ("mfma", t_mfma)
+
+    dom = max(names, key=lambda n: per_ms[n])
+    bound, _ = roof(dom)
+    if bound == "hbm":
+        achieved, peak, unit = nb[dom] / (per_ms[dom] * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = nf[dom] / (per_ms[dom] * 1e-3) / 1e12, FP32_PEAK_TFLOPS, "TFLOP/s"
+    stages = {n: {"ms": round(per_ms[n], 5),
+                  "GBps": round(nb[n] / (per_ms[n] * 1e-3) / 1e9, 1),
+                  "fp32_mfma_TFLOPs": round(nf[n] / (per_ms[n] * 1e-3) / 1e12, 1),
+                  "bound": roof(n)[0],
+                  "roofline_frac": round(roof(n)[1] / (per_ms[n] * 1e-3), 4)}
+              for n in names}
+    roof_ms = sum(roof(n)[1] for n in names) * 1e3
+    result = {
+        "metric": "complex-A SSD fwd tokens/s (Mamba-3-Lite SSD Reference, 434M shape)",
+        "value": round(w.tokens * args.steps / wall, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{w.name}: complex-A SSD forward, batch {w.batch}, seq "
+                               f"{w.seqlen}, {w.nheads} heads x {w.headdim}, d_state {w.dstate}, "
+                               f"chunk {w.chunk_size}, complex64 x/B/C/A, float32 dt, "
+                               "real output",
+                   "global_batch": w.batch, "seq_len": w.seqlen,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": bound, "kernel": dom, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": None, "bytes_per_launch": nb[dom], "flops_per_launch": nf[dom],
+                     "avg_launch_ms": round(per_ms[dom], 5)},
+        "stages": stages,
+        "path_roofline_frac": round(roof_ms / ms_per_step, 4),
+        "gpu": torch.cuda.get_device_name(0),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_complex(w, inp, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_complex(w, inp, seconds):
+    """The fp64 complex oracle on batch row 0 (all heads, all tokens), repeated
+    for about `seconds`; tokens/s of that sample."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or (os.cpu_count() or 1)
+    sl = lambda a: None if a is None else a[:1]
+    args = (sl(inp.x), sl(inp.B), sl(inp.C), sl(inp.dt), inp.A)
+    oracle.ssd_complex_fwd(*args, initial_states=sl(inp.h0), threads=threads)
+    times = []
+    while len(times) < 3 or (sum(times) < seconds and len(times) < 1000):
+        t0 = time.perf_counter()
+        oracle.ssd_complex_fwd(*args, initial_states=sl(inp.h0), threads=threads)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": w.seqlen / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": (f"batch row 0 of {w.name} ({w.seqlen} tokens, all {w.nheads} heads), "
+                       f"fp64 sequential complex recurrence, median of {len(times)} runs "
+                       f"({sum(times):.1f} s) after 1 warm-up"),
+            "seconds": t, "cpu": platform.processor() or platform.machine()}
 
 
 if __name__ == "__main__":

@@ -400,6 +400,40 @@ ssd_status ssd_complex_workspace_size(const ssd_complex_problem* p, size_t* byte
 ssd_status ssd_complex_forward(const ssd_complex_problem* p, const ssd_complex_fwd_args* a,
                                void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* The three stages ssd_complex_forward runs, for callers that keep the
+ * intermediates.  nc = ceil(T / C); chunk j = (batch row) * nc + c.
+ *   states        float32 complex (b * nc, H, P, N), 16-byte aligned: the page's
+ *                 internal states (B, n_chunks, H, D, N) ("Shape contract")
+ *   chunk_dt_sum  float32 (b, H, nc), 16-byte aligned: sum of softplus(dt) over
+ *                 each chunk's tokens (the chunk's total log-decay is this times A)
+ *
+ * ssd_complex_chunk_state: states[j] = sum_s exp(cs_last - cs_s) x_s (outer) B_s,
+ * each chunk from a zero start (SSD Reference "Algorithm and tensor-shape
+ * contract", step 6, decay_states = exp(A_cumsum[-1] - A_cumsum)); writes
+ * chunk_dt_sum too. */
+ssd_status ssd_complex_chunk_state(const ssd_complex_problem* p, ssd_tensor x, ssd_tensor B,
+                                   ssd_tensor dt, const float* A, float* states,
+                                   float* chunk_dt_sum, hipStream_t stream);
+
+/* ssd_complex_state_passing: in place over `states`, the carry-in state of every
+ * chunk, Hin[0] = initial_states (or 0), Hin[c+1] = exp(Lambda_c) Hin[c] + S_c
+ * with Lambda_c = chunk_dt_sum * A; final_states = the state after the last
+ * chunk (= initial_states when T = 0).  The SSD Reference's "Inter-chunk
+ * propagation": decay_chunk[z, c] = exp(CD[z-1] - CD[c]) 1[z > c] plus the init
+ * term exp(CD[z-1]) H_{-1}, evaluated as a sequential scan. */
+ssd_status ssd_complex_state_passing(const ssd_complex_problem* p, const float* A,
+                                     const float* chunk_dt_sum, const float* initial_states,
+                                     float* states, float* final_states, hipStream_t stream);
+
+/* ssd_complex_chunk_scan: the output of every token from the carry-in states,
+ * y_l = sum_{s <= l} exp(cs_l - cs_s) (C_l . B_s) x_s + exp(cs_l) C_l . Hin
+ * (SSD Reference "Algorithm and tensor-shape contract", steps 3-5, and
+ * "Readout"); out as in ssd_complex_fwd_args. */
+ssd_status ssd_complex_chunk_scan(const ssd_complex_problem* p, ssd_tensor x, ssd_tensor B,
+                                  ssd_tensor C, ssd_tensor dt, const float* A,
+                                  const float* states_in, ssd_tensor out, int32_t out_complex,
+                                  hipStream_t stream);
+
 /* ---------------------------------------------------------------- errors */
 
 const char* ssd_status_string(ssd_status s);

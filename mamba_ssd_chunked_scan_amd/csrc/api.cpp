@@ -878,6 +878,59 @@ static ssd_status check_cx_tensor(const ssd_tensor& t, const char* name, bool re
   return SSD_OK;
 }
 
+static ssd_status check_cx_dt(const ssd_tensor& t, bool required) {
+  if (!t.data) {
+    if (required) return fail(SSD_ERR_NULL, "dt is NULL");
+    return SSD_OK;
+  }
+  if (t.dtype != SSD_F32) return fail(SSD_ERR_DTYPE, "dt must be float32");
+  if (reinterpret_cast<uintptr_t>(t.data) % 4 != 0)
+    return fail(SSD_ERR_STRIDE, "dt: data pointer is not element aligned");
+  for (int i = 0; i < 3; ++i)
+    if (t.stride[i] < 0) return fail(SSD_ERR_STRIDE, "dt: stride[%d] is negative", i);
+  return SSD_OK;
+}
+
+static ssd_status check_cx_out(const ssd_tensor& t, int out_complex, bool required) {
+  if (out_complex != 0 && out_complex != 1)
+    return fail(SSD_ERR_SHAPE, "out_complex = %d: must be 0 or 1", out_complex);
+  if (!t.data) {
+    if (required) return fail(SSD_ERR_NULL, "out is NULL");
+    return SSD_OK;
+  }
+  if (t.dtype != SSD_F32) return fail(SSD_ERR_DTYPE, "out must be float32 or complex64");
+  if (reinterpret_cast<uintptr_t>(t.data) % (out_complex ? 8 : 4) != 0)
+    return fail(SSD_ERR_STRIDE, "out: data pointer is not element aligned");
+  for (int i = 0; i < 3; ++i)
+    if (t.stride[i] < 0) return fail(SSD_ERR_STRIDE, "out: stride[%d] is negative", i);
+  return SSD_OK;
+}
+
+static ssd_status check_cx_A(const float* A) {
+  if (!A) return fail(SSD_ERR_NULL, "A is NULL");
+  if (reinterpret_cast<uintptr_t>(A) % 8 != 0)
+    return fail(SSD_ERR_STRIDE, "A: data pointer is not 8-byte aligned");
+  return SSD_OK;
+}
+
+static ssd_status check_aligned16(const void* ptr, const char* name, bool required) {
+  if (!ptr) {
+    if (required) return fail(SSD_ERR_NULL, "%s is NULL", name);
+    return SSD_OK;
+  }
+  if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+    return fail(SSD_ERR_STRIDE, "%s is not 16-byte aligned", name);
+  return SSD_OK;
+}
+
+static ssd::CxGeo cx_geo(const ssd_complex_problem* p) {
+  ssd::CxGeo g;
+  g.b = p->batch; g.T = p->seqlen; g.H = p->nheads; g.P = p->headdim; g.N = p->dstate;
+  g.C = p->chunk_size;
+  g.nc = (int)cdiv(p->seqlen, p->chunk_size);
+  return g;
+}
+
 struct CxWorkspace {
   size_t states, lam, total;
 };
@@ -913,30 +966,11 @@ ssd_status ssd_complex_forward(const ssd_complex_problem* p, const ssd_complex_f
   SSD_TRY(check_cx_tensor(a->x, "x", tok));
   SSD_TRY(check_cx_tensor(a->B, "B", tok));
   SSD_TRY(check_cx_tensor(a->C, "C", tok));
-  if (tok) {
-    if (!a->dt.data) return fail(SSD_ERR_NULL, "dt is NULL");
-    if (a->dt.dtype != SSD_F32) return fail(SSD_ERR_DTYPE, "dt must be float32");
-    if (reinterpret_cast<uintptr_t>(a->dt.data) % 4 != 0)
-      return fail(SSD_ERR_STRIDE, "dt: data pointer is not element aligned");
-    for (int i = 0; i < 3; ++i)
-      if (a->dt.stride[i] < 0) return fail(SSD_ERR_STRIDE, "dt: stride[%d] is negative", i);
-    if (!a->out.data) return fail(SSD_ERR_NULL, "out is NULL");
-    if (a->out.dtype != SSD_F32) return fail(SSD_ERR_DTYPE, "out must be float32 or complex64");
-    const size_t oal = a->out_complex ? 8 : 4;
-    if (reinterpret_cast<uintptr_t>(a->out.data) % oal != 0)
-      return fail(SSD_ERR_STRIDE, "out: data pointer is not element aligned");
-    for (int i = 0; i < 3; ++i)
-      if (a->out.stride[i] < 0) return fail(SSD_ERR_STRIDE, "out: stride[%d] is negative", i);
-  }
-  if (a->out_complex != 0 && a->out_complex != 1)
-    return fail(SSD_ERR_SHAPE, "out_complex = %d: must be 0 or 1", a->out_complex);
-  if (!a->A) return fail(SSD_ERR_NULL, "A is NULL");
-  if (reinterpret_cast<uintptr_t>(a->A) % 8 != 0)
-    return fail(SSD_ERR_STRIDE, "A: data pointer is not 8-byte aligned");
-  if (reinterpret_cast<uintptr_t>(a->initial_states) % 16 != 0)
-    return fail(SSD_ERR_STRIDE, "initial_states is not 16-byte aligned");
-  if (reinterpret_cast<uintptr_t>(a->final_states) % 16 != 0)
-    return fail(SSD_ERR_STRIDE, "final_states is not 16-byte aligned");
+  SSD_TRY(check_cx_dt(a->dt, tok));
+  SSD_TRY(check_cx_out(a->out, a->out_complex, tok));
+  SSD_TRY(check_cx_A(a->A));
+  SSD_TRY(check_aligned16(a->initial_states, "initial_states", false));
+  SSD_TRY(check_aligned16(a->final_states, "final_states", false));
   const CxWorkspace w = cx_workspace(p);
   if (w.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < w.total)
@@ -944,15 +978,70 @@ ssd_status ssd_complex_forward(const ssd_complex_problem* p, const ssd_complex_f
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(SSD_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
-  ssd::CxGeo g;
-  g.b = p->batch; g.T = p->seqlen; g.H = p->nheads; g.P = p->headdim; g.N = p->dstate;
-  g.C = p->chunk_size;
-  g.nc = (int)cdiv(p->seqlen, p->chunk_size);
-  SSD_HIP(ssd::launch_complex_fwd(g, targ(a->x), targ(a->B), targ(a->C), targ(a->dt), a->A,
-                                  a->initial_states, targ(a->out), a->out_complex,
-                                  a->final_states, reinterpret_cast<float*>(ws + w.states),
-                                  reinterpret_cast<float*>(ws + w.lam), stream),
-          "complex forward launch");
+  const ssd::CxGeo g = cx_geo(p);
+  float* states = reinterpret_cast<float*>(ws + w.states);
+  float* lam = reinterpret_cast<float*>(ws + w.lam);
+  SSD_HIP(ssd::launch_cx_chunk_state(g, targ(a->x), targ(a->B), targ(a->dt), a->A, states, lam,
+                                     stream),
+          "complex chunk state launch");
+  SSD_HIP(ssd::launch_cx_state_pass(g, a->A, lam, a->initial_states, states, a->final_states,
+                                    stream),
+          "complex state passing launch");
+  SSD_HIP(ssd::launch_cx_chunk_scan(g, targ(a->x), targ(a->B), targ(a->C), targ(a->dt), a->A,
+                                    states, targ(a->out), a->out_complex, stream),
+          "complex chunk scan launch");
+  return ok();
+}
+
+ssd_status ssd_complex_chunk_state(const ssd_complex_problem* p, ssd_tensor x, ssd_tensor B,
+                                   ssd_tensor dt, const float* A, float* states,
+                                   float* chunk_dt_sum, hipStream_t stream) {
+  SSD_TRY(check_cx_problem(p));
+  const bool tok = (int64_t)p->batch * p->seqlen > 0;
+  SSD_TRY(check_cx_tensor(x, "x", tok));
+  SSD_TRY(check_cx_tensor(B, "B", tok));
+  SSD_TRY(check_cx_dt(dt, tok));
+  SSD_TRY(check_cx_A(A));
+  SSD_TRY(check_aligned16(states, "states", tok));
+  SSD_TRY(check_aligned16(chunk_dt_sum, "chunk_dt_sum", tok));
+  SSD_HIP(ssd::launch_cx_chunk_state(cx_geo(p), targ(x), targ(B), targ(dt), A, states,
+                                     chunk_dt_sum, stream),
+          "complex chunk state launch");
+  return ok();
+}
+
+ssd_status ssd_complex_state_passing(const ssd_complex_problem* p, const float* A,
+                                     const float* chunk_dt_sum, const float* initial_states,
+                                     float* states, float* final_states, hipStream_t stream) {
+  SSD_TRY(check_cx_problem(p));
+  const bool tok = (int64_t)p->batch * p->seqlen > 0;
+  SSD_TRY(check_cx_A(A));
+  SSD_TRY(check_aligned16(chunk_dt_sum, "chunk_dt_sum", tok));
+  SSD_TRY(check_aligned16(states, "states", tok));
+  SSD_TRY(check_aligned16(initial_states, "initial_states", false));
+  SSD_TRY(check_aligned16(final_states, "final_states", false));
+  SSD_HIP(ssd::launch_cx_state_pass(cx_geo(p), A, chunk_dt_sum, initial_states, states,
+                                    final_states, stream),
+          "complex state passing launch");
+  return ok();
+}
+
+ssd_status ssd_complex_chunk_scan(const ssd_complex_problem* p, ssd_tensor x, ssd_tensor B,
+                                  ssd_tensor C, ssd_tensor dt, const float* A,
+                                  const float* states_in, ssd_tensor out, int32_t out_complex,
+                                  hipStream_t stream) {
+  SSD_TRY(check_cx_problem(p));
+  const bool tok = (int64_t)p->batch * p->seqlen > 0;
+  SSD_TRY(check_cx_tensor(x, "x", tok));
+  SSD_TRY(check_cx_tensor(B, "B", tok));
+  SSD_TRY(check_cx_tensor(C, "C", tok));
+  SSD_TRY(check_cx_dt(dt, tok));
+  SSD_TRY(check_cx_A(A));
+  SSD_TRY(check_aligned16(states_in, "states_in", tok));
+  SSD_TRY(check_cx_out(out, out_complex, tok));
+  SSD_HIP(ssd::launch_cx_chunk_scan(cx_geo(p), targ(x), targ(B), targ(C), targ(dt), A,
+                                    states_in, targ(out), out_complex, stream),
+          "complex chunk scan launch");
   return ok();
 }
 

@@ -361,43 +361,43 @@ hipError_t launch_scan_pt(const CxGeo& g, TArg x, TArg B, TArg Cm, TArg dt, cons
 
 }  // namespace
 
-hipError_t launch_complex_fwd(const CxGeo& g, TArg x, TArg B, TArg Cm, TArg dt, const float* A,
-                              const float* h0, TArg out, int out_complex, float* hfinal,
-                              float* states, float* lam, hipStream_t s) {
-  hipError_t e = hipSuccess;
-  if (g.b * g.nc > 0) {
-    switch (g.N / 16) {
-      case 1: e = launch_state_nt<1>(g, x, B, dt, A, states, lam, s); break;
-      case 2: e = launch_state_nt<2>(g, x, B, dt, A, states, lam, s); break;
-      case 3: e = launch_state_nt<3>(g, x, B, dt, A, states, lam, s); break;
-      case 4: e = launch_state_nt<4>(g, x, B, dt, A, states, lam, s); break;
-      case 5: e = launch_state_nt<5>(g, x, B, dt, A, states, lam, s); break;
-      case 6: e = launch_state_nt<6>(g, x, B, dt, A, states, lam, s); break;
-      case 7: e = launch_state_nt<7>(g, x, B, dt, A, states, lam, s); break;
-      default: e = launch_state_nt<8>(g, x, B, dt, A, states, lam, s); break;
-    }
-    if (e != hipSuccess) return e;
+hipError_t launch_cx_chunk_state(const CxGeo& g, TArg x, TArg B, TArg dt, const float* A,
+                                 float* states, float* lam, hipStream_t s) {
+  if (g.b * g.nc == 0) return hipSuccess;
+  switch (g.N / 16) {
+    case 1: return launch_state_nt<1>(g, x, B, dt, A, states, lam, s);
+    case 2: return launch_state_nt<2>(g, x, B, dt, A, states, lam, s);
+    case 3: return launch_state_nt<3>(g, x, B, dt, A, states, lam, s);
+    case 4: return launch_state_nt<4>(g, x, B, dt, A, states, lam, s);
+    case 5: return launch_state_nt<5>(g, x, B, dt, A, states, lam, s);
+    case 6: return launch_state_nt<6>(g, x, B, dt, A, states, lam, s);
+    case 7: return launch_state_nt<7>(g, x, B, dt, A, states, lam, s);
+    default: return launch_state_nt<8>(g, x, B, dt, A, states, lam, s);
   }
-  {
-    const int64_t PN = (int64_t)g.P * g.N;
-    dim3 grid((unsigned)((PN + 511) / 512), g.b * g.H);
-    hipLaunchKernelGGL(k_cx_state_pass, grid, dim3(256), 0, s, g, A, lam, h0, states, hfinal);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+}
+
+hipError_t launch_cx_state_pass(const CxGeo& g, const float* A, const float* lam,
+                                const float* h0, float* states, float* hfinal, hipStream_t s) {
+  const int64_t PN = (int64_t)g.P * g.N;
+  dim3 grid((unsigned)((PN + 511) / 512), g.b * g.H);
+  hipLaunchKernelGGL(k_cx_state_pass, grid, dim3(256), 0, s, g, A, lam, h0, states, hfinal);
+  return hipGetLastError();
+}
+
+hipError_t launch_cx_chunk_scan(const CxGeo& g, TArg x, TArg B, TArg Cm, TArg dt,
+                                const float* A, const float* states, TArg out, int out_complex,
+                                hipStream_t s) {
+  if (g.b * g.nc == 0) return hipSuccess;
+  switch (g.P / 16) {
+    case 1: return launch_scan_pt<1>(g, x, B, Cm, dt, A, states, out, out_complex, s);
+    case 2: return launch_scan_pt<2>(g, x, B, Cm, dt, A, states, out, out_complex, s);
+    case 3: return launch_scan_pt<3>(g, x, B, Cm, dt, A, states, out, out_complex, s);
+    case 4: return launch_scan_pt<4>(g, x, B, Cm, dt, A, states, out, out_complex, s);
+    case 5: return launch_scan_pt<5>(g, x, B, Cm, dt, A, states, out, out_complex, s);
+    case 6: return launch_scan_pt<6>(g, x, B, Cm, dt, A, states, out, out_complex, s);
+    case 7: return launch_scan_pt<7>(g, x, B, Cm, dt, A, states, out, out_complex, s);
+    default: return launch_scan_pt<8>(g, x, B, Cm, dt, A, states, out, out_complex, s);
   }
-  if (g.b * g.nc > 0) {
-    switch (g.P / 16) {
-      case 1: e = launch_scan_pt<1>(g, x, B, Cm, dt, A, states, out, out_complex, s); break;
-      case 2: e = launch_scan_pt<2>(g, x, B, Cm, dt, A, states, out, out_complex, s); break;
-      case 3: e = launch_scan_pt<3>(g, x, B, Cm, dt, A, states, out, out_complex, s); break;
-      case 4: e = launch_scan_pt<4>(g, x, B, Cm, dt, A, states, out, out_complex, s); break;
-      case 5: e = launch_scan_pt<5>(g, x, B, Cm, dt, A, states, out, out_complex, s); break;
-      case 6: e = launch_scan_pt<6>(g, x, B, Cm, dt, A, states, out, out_complex, s); break;
-      case 7: e = launch_scan_pt<7>(g, x, B, Cm, dt, A, states, out, out_complex, s); break;
-      default: e = launch_scan_pt<8>(g, x, B, Cm, dt, A, states, out, out_complex, s); break;
-    }
-  }
-  return e;
 }
 
 }  // namespace ssd

@@ -114,10 +114,14 @@ struct CxGeo {
   int nc;  // ceil(T / C)
 };
 // x, B, C, out (complex) strides in complex elements; dt, out (real) in floats.
-// states: b * nc * H * P * N complex (written, then overwritten in place by the
-// carry-in states); lam: b * H * nc floats (each chunk's step sum).
-hipError_t launch_complex_fwd(const CxGeo& g, TArg x, TArg B, TArg Cm, TArg dt, const float* A,
-                              const float* h0, TArg out, int out_complex, float* hfinal,
-                              float* states, float* lam, hipStream_t s);
+// states: b * nc * H * P * N complex; lam: b * H * nc floats (each chunk's step sum).
+hipError_t launch_cx_chunk_state(const CxGeo& g, TArg x, TArg B, TArg dt, const float* A,
+                                 float* states, float* lam, hipStream_t s);
+// in place: the chunk states become the carry-in states
+hipError_t launch_cx_state_pass(const CxGeo& g, const float* A, const float* lam,
+                                const float* h0, float* states, float* hfinal, hipStream_t s);
+hipError_t launch_cx_chunk_scan(const CxGeo& g, TArg x, TArg B, TArg Cm, TArg dt,
+                                const float* A, const float* states, TArg out, int out_complex,
+                                hipStream_t s);
 
 }  // namespace ssd

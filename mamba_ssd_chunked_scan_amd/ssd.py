@@ -87,6 +87,7 @@ EXPORTS = ("ssd_problem_check", "ssd_num_chunks", "ssd_varlen_meta_len", "ssd_wo
            "ssd_bmm_chunk", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
            "ssd_forward", "ssd_backward_workspace_size", "ssd_backward",
            "ssd_complex_problem_check", "ssd_complex_workspace_size", "ssd_complex_forward",
+           "ssd_complex_chunk_state", "ssd_complex_state_passing", "ssd_complex_chunk_scan",
            "ssd_status_string", "ssd_last_error_message", "ssd_version")
 
 
@@ -123,12 +124,19 @@ def lib():
         L.ssd_complex_workspace_size.argtypes = [P(SsdComplexProblem), P(ctypes.c_size_t)]
         L.ssd_complex_forward.argtypes = [P(SsdComplexProblem), P(SsdComplexFwdArgs), vp,
                                           ctypes.c_size_t, vp]
+        L.ssd_complex_chunk_state.argtypes = [P(SsdComplexProblem), SsdTensor, SsdTensor,
+                                              SsdTensor, vp, vp, vp, vp]
+        L.ssd_complex_state_passing.argtypes = [P(SsdComplexProblem), vp, vp, vp, vp, vp, vp]
+        L.ssd_complex_chunk_scan.argtypes = [P(SsdComplexProblem), SsdTensor, SsdTensor,
+                                             SsdTensor, SsdTensor, vp, vp, SsdTensor,
+                                             ctypes.c_int32, vp]
         for name in ("ssd_problem_check", "ssd_workspace_size", "ssd_varlen_chunk_meta",
                      "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum", "ssd_bmm_chunk",
                      "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
                      "ssd_backward_workspace_size", "ssd_backward",
                      "ssd_complex_problem_check", "ssd_complex_workspace_size",
-                     "ssd_complex_forward"):
+                     "ssd_complex_forward", "ssd_complex_chunk_state",
+                     "ssd_complex_state_passing", "ssd_complex_chunk_scan"):
             getattr(L, name).restype = st
         L.ssd_status_string.argtypes = [ctypes.c_int]
         L.ssd_status_string.restype = ctypes.c_char_p
@@ -525,3 +533,33 @@ def ssd_complex_forward(x, B, C, dt, A, initial_states=None, chunk_size=64,
     _check(lib().ssd_complex_forward(ctypes.byref(prob.c()), ctypes.byref(a),
                                      workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return out, final_states
+
+
+def ssd_complex_chunk_state(prob: ComplexProblem, x, B, dt, A, states, chunk_dt_sum,
+                            stream=None):
+    """Every chunk's end state from a zero start; states (b * nc, H, P, N)
+    complex64, chunk_dt_sum (b, H, nc) float32, both written."""
+    _check(lib().ssd_complex_chunk_state(ctypes.byref(prob.c()), _cx_tensor(x), _cx_tensor(B),
+                                         tensor_arg(dt), A.data_ptr(), _ptr(states),
+                                         _ptr(chunk_dt_sum), _stream(stream)))
+    return states, chunk_dt_sum
+
+
+def ssd_complex_state_passing(prob: ComplexProblem, A, chunk_dt_sum, states,
+                              initial_states=None, final_states=None, stream=None):
+    """In place: chunk states -> carry-in states; also the final states."""
+    _check(lib().ssd_complex_state_passing(ctypes.byref(prob.c()), A.data_ptr(),
+                                           _ptr(chunk_dt_sum), _ptr(initial_states),
+                                           _ptr(states), _ptr(final_states), _stream(stream)))
+    return states, final_states
+
+
+def ssd_complex_chunk_scan(prob: ComplexProblem, x, B, C, dt, A, states_in, out,
+                           stream=None):
+    """The output from the carry-in states; out float32 (real part) or complex64."""
+    oc = out.dtype == torch.complex64
+    _check(lib().ssd_complex_chunk_scan(ctypes.byref(prob.c()), _cx_tensor(x), _cx_tensor(B),
+                                        _cx_tensor(C), tensor_arg(dt), A.data_ptr(),
+                                        _ptr(states_in), _cx_tensor(out) if oc else tensor_arg(out),
+                                        1 if oc else 0, _stream(stream)))
+    return out

@@ -124,3 +124,42 @@ def test_434m_config_sampled():
     e_f = err(fin[rows][:, heads].view(np.float32), r.final_states.view(np.float64))
     print(f"434M sampled: out err {e_y:.2e}, final-state err {e_f:.2e}")
     assert e_y <= TOL_F32 and e_f <= TOL_F32
+
+
+def test_stage_intermediates():
+    # chunk states = the recurrence run on each chunk alone from zero; after the
+    # pass, carry-in states = the recurrence's state at each chunk's start
+    w = ComplexWorkload("stages", 2, 150, 2, 16, 32, 64, seed=21, initial_states=True)
+    inp = make_complex_inputs(w)
+    prob = ssd.ComplexProblem(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.chunk_size)
+    nc = -(-w.seqlen // w.chunk_size)
+    x, B, C, dt, A, h0 = (dev(inp.x), dev(inp.B), dev(inp.C), dev(inp.dt), dev(inp.A),
+                          dev(inp.h0))
+    st = torch.empty((w.batch * nc, w.nheads, w.headdim, w.dstate), dtype=torch.complex64,
+                     device="cuda")
+    lam = torch.empty((w.batch, w.nheads, nc), dtype=torch.float32, device="cuda")
+    ssd.ssd_complex_chunk_state(prob, x, B, dt, A, st, lam)
+    torch.cuda.synchronize()
+    S = st.cpu().numpy().reshape(w.batch, nc, w.nheads, w.headdim, w.dstate)
+    for c in range(nc):
+        t0, t1 = c * 64, min(150, c * 64 + 64)
+        sl = lambda a: a[:, t0:t1]
+        r = oracle.ssd_complex_fwd(sl(inp.x), sl(inp.B), sl(inp.C), sl(inp.dt), inp.A)
+        assert err(S[:, c].view(np.float32), r.final_states.view(np.float64)) <= TOL_F32
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.complex64,
+                      device="cuda")
+    ssd.ssd_complex_state_passing(prob, A, lam, st, h0, fin)
+    torch.cuda.synchronize()
+    Hin = st.cpu().numpy().reshape(w.batch, nc, w.nheads, w.headdim, w.dstate)
+    assert np.array_equal(Hin[:, 0], inp.h0)
+    for c in range(1, nc):
+        sl = lambda a: a[:, :c * 64]
+        r = oracle.ssd_complex_fwd(sl(inp.x), sl(inp.B), sl(inp.C), sl(inp.dt), inp.A,
+                                   initial_states=inp.h0)
+        assert err(Hin[:, c].view(np.float32), r.final_states.view(np.float64)) <= TOL_F32
+    out = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim), dtype=torch.complex64,
+                      device="cuda")
+    ssd.ssd_complex_chunk_scan(prob, x, B, C, dt, A, st, out)
+    torch.cuda.synchronize()
+    y, f2 = run(inp, 64, out_complex=True)
+    assert np.array_equal(out.cpu().numpy(), y) and np.array_equal(fin.cpu().numpy(), f2)
