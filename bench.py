@@ -135,7 +135,10 @@ KERNEL_SOURCES = {"chunk_cumsum": ("chunk_cumsum.hip", "stage_cumsum.hpp"),
                   "chunk_state": ("chunk_state.hip", "stage_state.hpp"),
                   "state_passing": ("state_passing.hip", "stage_passing.hpp"),
                   "chunk_scan": ("chunk_scan.hip", "stage_scan.hpp"),
-                  "fused_fwd": ("fused_fwd.hip", "stage_varlen.hpp")}
+                  "fused_fwd": ("fused_fwd.hip", "stage_varlen.hpp"),
+                  "cx_chunk_state": ("complex_fwd.hip",),
+                  "cx_state_passing": ("complex_fwd.hip",),
+                  "cx_chunk_scan": ("complex_fwd.hip",)}
 
 
 def measured_traffic(stage, key):
@@ -456,6 +459,12 @@ def bench_complex(args, w):
 
     inp = make_complex_inputs(w)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     x, B, C, dt, A = up(inp.x), up(inp.B), up(inp.C), up(inp.dt), up(inp.A)
     h0 = up(inp.h0) if inp.h0 is not None else None
@@ -488,7 +497,9 @@ def bench_complex(args, w):
 
     for _ in range(args.warmup):
         step()
-    # the stage sequence is exactly ssd_complex_forward
+    # the stage sequence is exactly ssd_complex_forward (one more untimed step, so
+    # that the check also holds with no warm-up)
+    step()
     ref_out, ref_fin = ssd.ssd_complex_forward(x, B, C, dt, A, initial_states=h0,
                                                chunk_size=w.chunk_size)
     torch.cuda.synchronize()
@@ -537,7 +548,8 @@ def bench_complex(args, w):
                    "parallelism": "none (1 GPU)"},
         "roofline": {"bound": bound, "kernel": dom, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
-                     "traffic": None, "bytes_per_launch": nb[dom], "flops_per_launch": nf[dom],
+                     "traffic": measured_traffic(dom, w.name), "bytes_per_launch": nb[dom],
+                     "flops_per_launch": nf[dom],
                      "avg_launch_ms": round(per_ms[dom], 5)},
         "stages": stages,
         "path_roofline_frac": round(roof_ms / ms_per_step, 4),
