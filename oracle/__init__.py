@@ -37,6 +37,10 @@ Contents
                             "Measurements", SSD Reference section 6 "The autograd
                             backward contract".
 
+* ``gated_rmsnorm_fwd`` / ``gated_rmsnorm_bwd`` -- the gated RMSNorm after the
+                            scan (mamba PR 1012's "gated-LayerNorm"; formula:
+                            Mamba-2's gated RMSNorm, gate first), numpy fp64.
+
 All floating-point work is fp64.  Every function here is pinned by the
 ``-m "not gpu"`` tests against closed forms, special cases and brute force.
 """
@@ -505,3 +509,80 @@ def ssd_complex_fwd(x, B, C, dt, A, initial_states=None, cu_seqlens=None,
     if rc != 0:
         raise ValueError(f"ssd_ref_complex_fwd failed with code {rc}")
     return ComplexResult(y.reshape(x.shape), hfin)
+
+
+# ------------------------------------------------------------------ gated RMSNorm
+#
+# The step after the scan in the Mamba-2 mixer: the "gated-LayerNorm" whose
+# backward mamba PR 1012 times ("Summary", "Measurements": layer_norm_bwd).  The
+# pages do not write its formula; the reading taken is Mamba-2's gated RMSNorm
+# with the gate applied before the norm, over contiguous channel groups of the
+# flattened (H, P) axis:
+#     g   = y * silu(z)                 (z absent: g = y)
+#     r   = 1 / sqrt(mean_group(g^2) + eps)
+#     out = g * r * weight
+
+@dataclass
+class NormResult:
+    out: np.ndarray      # float64, shaped like y
+    rstd: np.ndarray     # float64, (..., H * P // group_size)
+
+
+def _norm_groups(a, group_size):
+    lead = a.shape[:-2]
+    width = a.shape[-2] * a.shape[-1]
+    if width % group_size != 0:
+        raise ValueError("group_size must divide H * P")
+    return a.reshape(lead + (width // group_size, group_size))
+
+
+def gated_rmsnorm_fwd(y, z, weight, group_size, eps=1e-5) -> NormResult:
+    """fp64 forward of the gated RMSNorm.  y, z (..., H, P); weight (H * P,)."""
+    y = np.asarray(y, dtype=np.float64)
+    g = y if z is None else y * (np.asarray(z, dtype=np.float64) /
+                                 (1.0 + np.exp(-np.asarray(z, dtype=np.float64))))
+    gg = _norm_groups(g, group_size)
+    ms = np.mean(gg * gg, axis=-1)
+    r = 1.0 / np.sqrt(ms + eps)
+    xhat = gg * r[..., None]
+    w = _norm_groups(np.asarray(weight, dtype=np.float64).reshape(y.shape[-2:]), group_size)
+    out = (xhat * w).reshape(y.shape)
+    return NormResult(out, r)
+
+
+@dataclass
+class NormGrads:
+    dy: np.ndarray
+    dz: np.ndarray | None
+    dweight: np.ndarray   # (H * P,)
+
+
+def gated_rmsnorm_bwd(y, z, weight, dout, group_size, eps=1e-5) -> NormGrads:
+    """fp64 gradient of sum(dout * out) with respect to y, z and weight.
+
+    With xhat = g r:  dxhat = dout w;  dg = r (dxhat - xhat mean_group(dxhat xhat));
+    dy = dg silu(z);  dz = dg y sigma(z) (1 + z (1 - sigma(z)));  dweight = sum over
+    tokens of dout xhat.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    shape = y.shape
+    if z is not None:
+        z = np.asarray(z, dtype=np.float64)
+        sig = 1.0 / (1.0 + np.exp(-z))
+        g = y * z * sig
+    else:
+        g = y
+    gg = _norm_groups(g, group_size)
+    r = 1.0 / np.sqrt(np.mean(gg * gg, axis=-1) + eps)
+    xhat = gg * r[..., None]
+    w = _norm_groups(np.asarray(weight, dtype=np.float64).reshape(shape[-2:]), group_size)
+    do = _norm_groups(np.asarray(dout, dtype=np.float64), group_size)
+    dxhat = do * w
+    dg = r[..., None] * (dxhat - xhat * np.mean(dxhat * xhat, axis=-1, keepdims=True))
+    dg = dg.reshape(shape)
+    dweight = np.sum((do * xhat).reshape((-1,) + shape[-2:]), axis=0).reshape(-1)
+    if z is None:
+        return NormGrads(dg, None, dweight)
+    dy = dg * z * sig
+    dz = dg * y * sig * (1.0 + z * (1.0 - sig))
+    return NormGrads(dy, dz, dweight)
