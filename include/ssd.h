@@ -434,6 +434,50 @@ ssd_status ssd_complex_chunk_scan(const ssd_complex_problem* p, ssd_tensor x, ss
                                   const float* states_in, ssd_tensor out, int32_t out_complex,
                                   hipStream_t stream);
 
+/* ---------------------------------------------------------------- gated RMSNorm */
+
+/* The normalisation that follows the scan in the Mamba-2 mixer: the
+ * "gated-LayerNorm" of mamba PR 1012 ("Summary"; its backward is the
+ * layer_norm_bwd stage of "Measurements").  The pages do not write its formula;
+ * this is Mamba-2's gated RMSNorm with the gate applied before the norm, over
+ * contiguous groups of group_size channels of each token's flattened (H, P) axis:
+ *
+ *     g = y silu(z)   (g = y when z is absent)
+ *     out = g / sqrt(mean_group(g^2) + eps) * weight
+ *
+ * y is typically the ungated scan output (ssd_forward with z absent).  It is a
+ * separate pass because a group spans several heads while the scan's
+ * workgroups each own one head.  Tokens: (b, T, H, P) strided views as for the
+ * scan (innermost contiguous, rows 16-byte aligned). */
+typedef struct ssd_norm_problem {
+  int32_t batch;       /* b >= 1 */
+  int32_t seqlen;      /* T >= 0 */
+  int32_t nheads;      /* H >= 1 */
+  int32_t headdim;     /* P: a multiple of 8 */
+  int32_t group_size;  /* divides H * P; a power of two in [8, 512] or a multiple of 512 */
+  float eps;           /* >= 0 */
+} ssd_norm_problem;
+
+/* Forward.  y, z: F32 or BF16, same dtype (z may be absent); weight: float32
+ * (H * P), 16-byte aligned; out: F32 or BF16; rstd: float32 (b * T, H * P /
+ * group_size) or NULL: 1 / sqrt(mean_group(g^2) + eps) per token and group. */
+ssd_status ssd_gated_rmsnorm_fwd(const ssd_norm_problem* p, ssd_tensor y, ssd_tensor z,
+                                 const float* weight, ssd_tensor out, float* rstd,
+                                 hipStream_t stream);
+
+/* Bytes of workspace ssd_gated_rmsnorm_bwd needs. */
+ssd_status ssd_gated_rmsnorm_bwd_workspace_size(const ssd_norm_problem* p, size_t* bytes);
+
+/* Gradient of sum(dout * out) with respect to y, z and weight.  dout has y's
+ * dtype; dy and dz are float32 (dz required when z is given); dweight: float32
+ * (H * P), written (summed over all tokens in a fixed order: bit-identical run to
+ * run).  workspace: at least ssd_gated_rmsnorm_bwd_workspace_size bytes, 256-byte
+ * aligned, caller-owned, contents need not be initialised. */
+ssd_status ssd_gated_rmsnorm_bwd(const ssd_norm_problem* p, ssd_tensor y, ssd_tensor z,
+                                 const float* weight, ssd_tensor dout, ssd_tensor dy,
+                                 ssd_tensor dz, float* dweight, void* workspace,
+                                 size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- errors */
 
 const char* ssd_status_string(ssd_status s);

@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cmath>
 #include <cstring>
 #include <string>
 
@@ -1042,6 +1043,123 @@ ssd_status ssd_complex_chunk_scan(const ssd_complex_problem* p, ssd_tensor x, ss
   SSD_HIP(ssd::launch_cx_chunk_scan(cx_geo(p), targ(x), targ(B), targ(C), targ(dt), A,
                                     states_in, targ(out), out_complex, stream),
           "complex chunk scan launch");
+  return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- gated RMSNorm
+
+static ssd_status check_norm_problem(const ssd_norm_problem* p) {
+  if (!p) return fail(SSD_ERR_NULL, "problem is NULL");
+  if (p->batch < 1) return fail(SSD_ERR_SHAPE, "batch = %d must be >= 1", p->batch);
+  if (p->seqlen < 0) return fail(SSD_ERR_SHAPE, "seqlen = %d must be >= 0", p->seqlen);
+  if (p->nheads < 1) return fail(SSD_ERR_SHAPE, "nheads = %d must be >= 1", p->nheads);
+  if (p->headdim < 8 || p->headdim % 8 != 0)
+    return fail(SSD_ERR_UNSUPPORTED, "headdim = %d: must be a positive multiple of 8", p->headdim);
+  const int64_t W = (int64_t)p->nheads * p->headdim;
+  if (W > (1 << 24)) return fail(SSD_ERR_UNSUPPORTED, "nheads * headdim exceeds 2^24");
+  const int gs = p->group_size;
+  if (gs < 1 || W % gs != 0)
+    return fail(SSD_ERR_SHAPE, "group_size = %d must divide nheads * headdim = %lld", gs,
+                (long long)W);
+  const bool pow2 = (gs & (gs - 1)) == 0;
+  if (!((pow2 && gs >= 8 && gs <= 512) || gs % 512 == 0))
+    return fail(SSD_ERR_UNSUPPORTED,
+                "group_size = %d: must be a power of two in [8, 512] or a multiple of 512", gs);
+  if (!(p->eps >= 0.0f) || p->eps == INFINITY)
+    return fail(SSD_ERR_SHAPE, "eps = %g must be finite and >= 0", (double)p->eps);
+  if ((int64_t)p->batch * p->seqlen > INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED, "batch * seqlen exceeds 2^31 - 1 tokens");
+  return SSD_OK;
+}
+
+static ssd::NormGeo norm_geo(const ssd_norm_problem* p) {
+  ssd::NormGeo g;
+  g.ntok = p->batch * p->seqlen;
+  g.T = p->seqlen > 0 ? p->seqlen : 1;
+  g.H = p->nheads; g.P = p->headdim; g.gs = p->group_size; g.eps = p->eps;
+  return g;
+}
+
+struct NormWorkspace {
+  size_t part, stats, total;
+};
+
+static NormWorkspace norm_workspace(const ssd_norm_problem* p) {
+  const ssd::NormGeo g = norm_geo(p);
+  const size_t W = (size_t)p->nheads * p->headdim;
+  NormWorkspace w;
+  w.part = 0;
+  w.stats = align256((size_t)ssd::norm_tiles(g) * W * sizeof(float));
+  const size_t st = p->group_size > 512 ? (size_t)g.ntok * (W / p->group_size) * 8 : 0;
+  w.total = w.stats + align256(st);
+  return w;
+}
+
+static ssd_status check_norm_io(const ssd_norm_problem* p, const ssd_tensor& y,
+                                const ssd_tensor& z, const float* weight) {
+  const bool tok = (int64_t)p->batch * p->seqlen > 0;
+  SSD_TRY(check_vec_tensor(y, "y", tok));
+  SSD_TRY(check_vec_tensor(z, "z", false));
+  if (z.data && y.data && z.dtype != y.dtype)
+    return fail(SSD_ERR_DTYPE, "z must have the dtype of y");
+  if (!weight) return fail(SSD_ERR_NULL, "weight is NULL");
+  if (reinterpret_cast<uintptr_t>(weight) % 16 != 0)
+    return fail(SSD_ERR_STRIDE, "weight is not 16-byte aligned");
+  return SSD_OK;
+}
+
+extern "C" {
+
+ssd_status ssd_gated_rmsnorm_fwd(const ssd_norm_problem* p, ssd_tensor y, ssd_tensor z,
+                                 const float* weight, ssd_tensor out, float* rstd,
+                                 hipStream_t stream) {
+  SSD_TRY(check_norm_problem(p));
+  SSD_TRY(check_norm_io(p, y, z, weight));
+  const bool tok = (int64_t)p->batch * p->seqlen > 0;
+  SSD_TRY(check_vec_tensor(out, "out", tok));
+  if (reinterpret_cast<uintptr_t>(rstd) % 4 != 0)
+    return fail(SSD_ERR_STRIDE, "rstd is not 4-byte aligned");
+  if (!tok) return ok();
+  SSD_HIP(ssd::launch_norm_fwd(norm_geo(p), targ(y), targ(z), dcode(y.dtype), weight, targ(out),
+                               dcode(out.dtype), rstd, stream),
+          "gated rmsnorm forward launch");
+  return ok();
+}
+
+ssd_status ssd_gated_rmsnorm_bwd_workspace_size(const ssd_norm_problem* p, size_t* bytes) {
+  SSD_TRY(check_norm_problem(p));
+  if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
+  *bytes = norm_workspace(p).total;
+  return ok();
+}
+
+ssd_status ssd_gated_rmsnorm_bwd(const ssd_norm_problem* p, ssd_tensor y, ssd_tensor z,
+                                 const float* weight, ssd_tensor dout, ssd_tensor dy,
+                                 ssd_tensor dz, float* dweight, void* workspace,
+                                 size_t ws_bytes, hipStream_t stream) {
+  SSD_TRY(check_norm_problem(p));
+  SSD_TRY(check_norm_io(p, y, z, weight));
+  const bool tok = (int64_t)p->batch * p->seqlen > 0;
+  SSD_TRY(check_vec_tensor(dout, "dout", tok));
+  if (dout.data && y.data && dout.dtype != y.dtype)
+    return fail(SSD_ERR_DTYPE, "dout must have the dtype of y");
+  SSD_TRY(check_vec_tensor(dy, "dy", tok, true, false));
+  SSD_TRY(check_vec_tensor(dz, "dz", tok && z.data != nullptr, true, false));
+  if (!dweight) return fail(SSD_ERR_NULL, "dweight is NULL");
+  const NormWorkspace w = norm_workspace(p);
+  if (w.total > 0 && !workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < w.total)
+    return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, w.total);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  SSD_HIP(ssd::launch_norm_bwd(norm_geo(p), targ(y), targ(z), dcode(y.data ? y.dtype : SSD_F32),
+                               weight, targ(dout), targ(dy), targ(dz), dweight,
+                               reinterpret_cast<float*>(ws + w.part),
+                               reinterpret_cast<float2*>(ws + w.stats), stream),
+          "gated rmsnorm backward launch");
   return ok();
 }
 

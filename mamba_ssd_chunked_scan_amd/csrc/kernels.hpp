@@ -124,4 +124,18 @@ hipError_t launch_cx_chunk_scan(const CxGeo& g, TArg x, TArg B, TArg Cm, TArg dt
                                 const float* A, const float* states, TArg out, int out_complex,
                                 hipStream_t s);
 
+// ---- gated RMSNorm after the scan (gated_norm.hip); tokens on the packed axis
+// ntok = b * T, T tokens per batch row; groups of gs channels of the (H, P) axis
+struct NormGeo {
+  int ntok, T, H, P, gs;
+  float eps;
+};
+int norm_tiles(const NormGeo& g);  // rows of weight-gradient partials
+hipError_t launch_norm_fwd(const NormGeo& g, TArg y, TArg z, int in_dtype, const float* w,
+                           TArg out, int out_dtype, float* rstd, hipStream_t s);
+// part: norm_tiles * H * P floats; stats: ntok * (H P / gs) float2 (gs > 512 only)
+hipError_t launch_norm_bwd(const NormGeo& g, TArg y, TArg z, int in_dtype, const float* w,
+                           TArg dout, TArg dy, TArg dz, float* dw, float* part, float2* stats,
+                           hipStream_t s);
+
 }  // namespace ssd

@@ -81,6 +81,12 @@ class SsdComplexFwdArgs(ctypes.Structure):
                 ("final_states", ctypes.c_void_p)]
 
 
+class SsdNormProblem(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
+                ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
+                ("group_size", ctypes.c_int32), ("eps", ctypes.c_float)]
+
+
 _lib = None
 EXPORTS = ("ssd_problem_check", "ssd_num_chunks", "ssd_varlen_meta_len", "ssd_workspace_size",
            "ssd_varlen_chunk_meta", "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum",
@@ -88,6 +94,8 @@ EXPORTS = ("ssd_problem_check", "ssd_num_chunks", "ssd_varlen_meta_len", "ssd_wo
            "ssd_forward", "ssd_backward_workspace_size", "ssd_backward",
            "ssd_complex_problem_check", "ssd_complex_workspace_size", "ssd_complex_forward",
            "ssd_complex_chunk_state", "ssd_complex_state_passing", "ssd_complex_chunk_scan",
+           "ssd_gated_rmsnorm_fwd", "ssd_gated_rmsnorm_bwd_workspace_size",
+           "ssd_gated_rmsnorm_bwd",
            "ssd_status_string", "ssd_last_error_message", "ssd_version")
 
 
@@ -126,6 +134,12 @@ def lib():
                                           ctypes.c_size_t, vp]
         L.ssd_complex_chunk_state.argtypes = [P(SsdComplexProblem), SsdTensor, SsdTensor,
                                               SsdTensor, vp, vp, vp, vp]
+        L.ssd_gated_rmsnorm_fwd.argtypes = [P(SsdNormProblem), SsdTensor, SsdTensor, vp,
+                                            SsdTensor, vp, vp]
+        L.ssd_gated_rmsnorm_bwd_workspace_size.argtypes = [P(SsdNormProblem), P(ctypes.c_size_t)]
+        L.ssd_gated_rmsnorm_bwd.argtypes = [P(SsdNormProblem), SsdTensor, SsdTensor, vp,
+                                            SsdTensor, SsdTensor, SsdTensor, vp, vp,
+                                            ctypes.c_size_t, vp]
         L.ssd_complex_state_passing.argtypes = [P(SsdComplexProblem), vp, vp, vp, vp, vp, vp]
         L.ssd_complex_chunk_scan.argtypes = [P(SsdComplexProblem), SsdTensor, SsdTensor,
                                              SsdTensor, SsdTensor, vp, vp, SsdTensor,
@@ -136,7 +150,9 @@ def lib():
                      "ssd_backward_workspace_size", "ssd_backward",
                      "ssd_complex_problem_check", "ssd_complex_workspace_size",
                      "ssd_complex_forward", "ssd_complex_chunk_state",
-                     "ssd_complex_state_passing", "ssd_complex_chunk_scan"):
+                     "ssd_complex_state_passing", "ssd_complex_chunk_scan",
+                     "ssd_gated_rmsnorm_fwd", "ssd_gated_rmsnorm_bwd_workspace_size",
+                     "ssd_gated_rmsnorm_bwd"):
             getattr(L, name).restype = st
         L.ssd_status_string.argtypes = [ctypes.c_int]
         L.ssd_status_string.restype = ctypes.c_char_p
@@ -563,3 +579,44 @@ def ssd_complex_chunk_scan(prob: ComplexProblem, x, B, C, dt, A, states_in, out,
                                         _ptr(states_in), _cx_tensor(out) if oc else tensor_arg(out),
                                         1 if oc else 0, _stream(stream)))
     return out
+
+
+# ------------------------------------------------------------------ gated RMSNorm
+
+def norm_problem(y, group_size, eps=1e-5) -> SsdNormProblem:
+    b, T, H, P = y.shape
+    p = SsdNormProblem()
+    p.batch, p.seqlen, p.nheads, p.headdim = b, T, H, P
+    p.group_size, p.eps = int(group_size), float(eps)
+    return p
+
+
+def ssd_gated_rmsnorm_fwd(y, z, weight, group_size, eps=1e-5, out=None, out_dtype=None,
+                          rstd=None, stream=None):
+    """out = g / sqrt(mean_group(g^2) + eps) * weight, g = y silu(z); y, z (b, T, H, P).
+    Returns (out, rstd); rstd is written only when a tensor is passed."""
+    if out is None:
+        out = torch.empty(y.shape, dtype=out_dtype or y.dtype, device=y.device)
+    p = norm_problem(y, group_size, eps)
+    _check(lib().ssd_gated_rmsnorm_fwd(ctypes.byref(p), tensor_arg(y), tensor_arg(z),
+                                       weight.data_ptr(), tensor_arg(out), _ptr(rstd),
+                                       _stream(stream)))
+    return out, rstd
+
+
+def ssd_gated_rmsnorm_bwd(y, z, weight, dout, group_size, eps=1e-5, workspace=None,
+                          stream=None):
+    """Gradients (dy, dz, dweight) of sum(dout * out); float32."""
+    p = norm_problem(y, group_size, eps)
+    n = ctypes.c_size_t(0)
+    _check(lib().ssd_gated_rmsnorm_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    if workspace is None:
+        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=y.device)
+    dy = torch.empty(y.shape, dtype=torch.float32, device=y.device)
+    dz = torch.empty(y.shape, dtype=torch.float32, device=y.device) if z is not None else None
+    dw = torch.empty(weight.shape, dtype=torch.float32, device=y.device)
+    _check(lib().ssd_gated_rmsnorm_bwd(ctypes.byref(p), tensor_arg(y), tensor_arg(z),
+                                       weight.data_ptr(), tensor_arg(dout), tensor_arg(dy),
+                                       tensor_arg(dz), dw.data_ptr(), workspace.data_ptr(),
+                                       workspace.numel(), _stream(stream)))
+    return dy, dz, dw

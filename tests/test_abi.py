@@ -293,3 +293,37 @@ def test_complex_forward_rejects_bad_arguments_before_launching():
     a.x.stride[0], a.x.stride[1], a.x.stride[2] = 64 * 2 * 16, 2 * 16 + 1, 16
     rc = L.ssd_complex_forward(ctypes.byref(p.c()), ctypes.byref(a), None, 0, None)
     assert rc == 4 and "stride[1]" in L.ssd_last_error_message().decode()
+
+
+# ------------------------------------------------------------------ gated RMSNorm
+
+@pytest.mark.parametrize("kw,code,word", [
+    (dict(nheads=6, group_size=96), 5, "group_size"),
+    (dict(group_size=1000), 2, "group_size"),
+    (dict(headdim=12), 5, "headdim"),
+    (dict(eps=-1.0), 2, "eps"),
+    (dict(batch=0), 2, "batch"),
+])
+def test_norm_problem_check(kw, code, word):
+    L = ssd.lib()
+    p = ssd.SsdNormProblem()
+    base = dict(batch=1, seqlen=16, nheads=8, headdim=64, group_size=512, eps=1e-5)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    ws = ctypes.c_size_t(0)
+    rc = L.ssd_gated_rmsnorm_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws))
+    assert rc == code
+    assert word in L.ssd_last_error_message().decode()
+
+
+def test_norm_workspace_size():
+    L = ssd.lib()
+    p = ssd.SsdNormProblem()
+    p.batch, p.seqlen, p.nheads, p.headdim, p.group_size, p.eps = 1, 8192, 64, 64, 512, 1e-5
+    ws = ctypes.c_size_t(0)
+    assert L.ssd_gated_rmsnorm_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws)) == 0
+    assert ws.value == 128 * 4096 * 4           # 64-token tiles x channels, no statistics
+    p.group_size = 1024
+    assert L.ssd_gated_rmsnorm_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws)) == 0
+    assert ws.value == 128 * 4096 * 4 + 8192 * 4 * 8
