@@ -71,6 +71,10 @@ def parse():
                          "'fwd_bwd' object)")
     ap.add_argument("--backward", dest="backward", action="store_true",
                     help="time ssd_backward (the default)")
+    ap.add_argument("--no-norm", dest="norm", action="store_false",
+                    help="skip timing the gated RMSNorm after the scan (by default its forward "
+                         "and backward are timed at the workload's shape in a 'gated_norm' "
+                         "object)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle until this much CPU time has been spent (min 3 runs)")
     ap.add_argument("--cold-steps", type=int, default=10,
@@ -387,9 +391,67 @@ def main():
     if args.backward:
         result["fwd_bwd"] = time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu,
                                           ms_per_step)
+    if args.norm:
+        result["gated_norm"] = time_norm(args, w, ssd, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def time_norm(args, w, ssd, dev):
+    """HIP-event times of the gated RMSNorm forward and backward at the workload's
+    output shape (bf16 y, z, dout; fp32 dy, dz; norm groups of H P / G channels,
+    Mamba-2's d_inner / ngroups), against their algorithmic bytes."""
+    import torch
+    H, P = w.nheads, w.headdim
+    gs = H * P // w.ngroups
+    shape = (w.batch, w.seqlen, H, P)
+    g = torch.Generator(device=dev).manual_seed(5)
+    y = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    z = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    dout = torch.randn(shape, generator=g, device=dev).to(torch.bfloat16)
+    wt = torch.ones(H * P, device=dev)
+    out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+    ntok = w.batch * w.seqlen
+    el = ntok * H * P
+    fwd_bytes = 3 * 2 * el + 4 * H * P
+    ntile = -(-ntok // 64)
+    bwd_bytes = 3 * 2 * el + 2 * 4 * el + 4 * H * P * 2 + 2 * 4 * ntile * H * P
+
+    dy = torch.empty(shape, dtype=torch.float32, device=dev)
+    dz = torch.empty(shape, dtype=torch.float32, device=dev)
+    dw = torch.empty(H * P, dtype=torch.float32, device=dev)
+    ws = torch.empty(max(ssd.gated_rmsnorm_bwd_workspace_size(y, gs), 1), dtype=torch.uint8,
+                     device=dev)
+
+    def timed(fn, n):
+        # n calls back to back between two events: the queue stays ahead of the GPU
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    fwd = lambda: ssd.ssd_gated_rmsnorm_fwd(y, z, wt, gs, out=out)
+    bwd = lambda: ssd.ssd_gated_rmsnorm_bwd(y, z, wt, dout, gs, workspace=ws, dy=dy, dz=dz, dw=dw)
+    for _ in range(3):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    n = max(10, args.steps // 2)
+    fm, bm = timed(fwd, n), timed(bwd, n)
+    return {"group_size": gs, "fwd_ms": round(fm, 5), "bwd_ms": round(bm, 5),
+            "fwd_GBps": round(fwd_bytes / (fm * 1e-3) / 1e9, 1),
+            "bwd_GBps": round(bwd_bytes / (bm * 1e-3) / 1e9, 1),
+            "fwd_hbm_frac": round(fwd_bytes / (fm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bwd_hbm_frac": round(bwd_bytes / (bm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "fwd_bytes": fwd_bytes, "bwd_bytes": bwd_bytes,
+            "calls": n,
+            "note": "average over calls issued back to back between two HIP events; the "
+                    "backward includes its weight-gradient partials and their reduction"}
 
 
 def time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu, fwd_ms):

@@ -8,9 +8,10 @@
 //     dg = r (dout w - xhat mean_group(dout w xhat)),  dy = dg silu(z),
 //     dz = dg y sigma(z) (1 + z (1 - sigma(z))),        dweight = sum_tokens dout xhat
 //
-// Both passes are HBM streams (each input read once, each output written once): one
-// wave per (token, group); a lane holds 8 consecutive channels per 512-channel strip,
-// so every access is a 16-byte (bf16) or 32-byte (fp32) vector.  The weight gradient is
+// Both passes are HBM streams (each input read once, each output written once).  A lane
+// holds 8 consecutive channels of a 512-channel strip, so every access is a 16-byte
+// (bf16) or 32-byte (fp32) vector; groups of up to 512 channels reduce over their lanes
+// within the wave, wider groups take a statistics pass first.  The weight gradient is
 // reduced deterministically: per 64-token tile into a partial row (fixed order), then
 // over tiles by a second kernel (fixed order, fp64).
 #include "common.hpp"
@@ -217,12 +218,33 @@ __global__ __launch_bounds__(256) void k_norm_bwd(NormGeo g, TArg y, TArg z, con
     if (blockIdx.y * kStrip + e < W) prow[e] = ((red[0][e] + red[1][e]) + red[2][e]) + red[3][e];
 }
 
+// dweight[c] = sum over tiles of part[tile][c]: a workgroup takes 16 channels; thread
+// (slice, channel) sums tiles slice, slice + 16, ... in fp64, then the 16 slices are
+// added in slice order.  Fixed order throughout.
 __global__ __launch_bounds__(256) void k_norm_dw(int W, const float* part, int ntile, float* dw) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= W) return;
+  __shared__ double red[16][17];
+  const int cl = threadIdx.x % 16, sl = threadIdx.x / 16;
+  const int c = blockIdx.x * 16 + cl;
   double acc = 0.0;
-  for (int t = 0; t < ntile; ++t) acc += (double)part[(int64_t)t * W + c];
-  dw[c] = (float)acc;
+  if (c < W) {
+    int t = sl;
+    for (; t + 48 < ntile; t += 64) {
+      const float a = part[(int64_t)t * W + c], b = part[(int64_t)(t + 16) * W + c];
+      const float d = part[(int64_t)(t + 32) * W + c], e = part[(int64_t)(t + 48) * W + c];
+      acc += (double)a;
+      acc += (double)b;
+      acc += (double)d;
+      acc += (double)e;
+    }
+    for (; t < ntile; t += 16) acc += (double)part[(int64_t)t * W + c];
+  }
+  red[sl][cl] = acc;
+  __syncthreads();
+  if (sl == 0 && c < W) {
+    double s = 0.0;
+    for (int i = 0; i < 16; ++i) s += red[i][cl];
+    dw[c] = (float)s;
+  }
 }
 
 }  // namespace
@@ -277,7 +299,7 @@ hipError_t launch_norm_bwd(const NormGeo& g, TArg y, TArg z, int in_dtype, const
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(k_norm_dw, dim3((W + 255) / 256), dim3(256), 0, s, W, part, ntile, dw);
+  hipLaunchKernelGGL(k_norm_dw, dim3((W + 15) / 16), dim3(256), 0, s, W, part, ntile, dw);
   return hipGetLastError();
 }
 

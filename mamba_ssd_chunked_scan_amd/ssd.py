@@ -604,17 +604,27 @@ def ssd_gated_rmsnorm_fwd(y, z, weight, group_size, eps=1e-5, out=None, out_dtyp
     return out, rstd
 
 
-def ssd_gated_rmsnorm_bwd(y, z, weight, dout, group_size, eps=1e-5, workspace=None,
-                          stream=None):
-    """Gradients (dy, dz, dweight) of sum(dout * out); float32."""
+def gated_rmsnorm_bwd_workspace_size(y, group_size, eps=1e-5) -> int:
     p = norm_problem(y, group_size, eps)
     n = ctypes.c_size_t(0)
     _check(lib().ssd_gated_rmsnorm_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)))
+    return int(n.value)
+
+
+def ssd_gated_rmsnorm_bwd(y, z, weight, dout, group_size, eps=1e-5, workspace=None,
+                          dy=None, dz=None, dw=None, stream=None):
+    """Gradients (dy, dz, dweight) of sum(dout * out); float32.  Output tensors and
+    the workspace are allocated when not given."""
+    p = norm_problem(y, group_size, eps)
     if workspace is None:
-        workspace = torch.empty(max(int(n.value), 1), dtype=torch.uint8, device=y.device)
-    dy = torch.empty(y.shape, dtype=torch.float32, device=y.device)
-    dz = torch.empty(y.shape, dtype=torch.float32, device=y.device) if z is not None else None
-    dw = torch.empty(weight.shape, dtype=torch.float32, device=y.device)
+        n = gated_rmsnorm_bwd_workspace_size(y, group_size, eps)
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=y.device)
+    if dy is None:
+        dy = torch.empty(y.shape, dtype=torch.float32, device=y.device)
+    if dz is None and z is not None:
+        dz = torch.empty(y.shape, dtype=torch.float32, device=y.device)
+    if dw is None:
+        dw = torch.empty(weight.shape, dtype=torch.float32, device=y.device)
     _check(lib().ssd_gated_rmsnorm_bwd(ctypes.byref(p), tensor_arg(y), tensor_arg(z),
                                        weight.data_ptr(), tensor_arg(dout), tensor_arg(dy),
                                        tensor_arg(dz), dw.data_ptr(), workspace.data_ptr(),
