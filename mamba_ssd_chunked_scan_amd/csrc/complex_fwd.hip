@@ -87,7 +87,7 @@ __device__ __forceinline__ void cx_delta_cumsum(const CxGeo& g, const TArg& dt, 
 
 // state[j, h, p, n] = sum_{s < len} w_s x[s, p] B[s, n],  w_s = exp((sd_last - sd_s) A).
 // Wave w computes p-tiles w, w + 4, ...; each p-tile holds all NT n-tiles.
-// Contraction over tokens: k-slot q of a 4-token step is token s0 + q.
+// Contraction over tokens: k-slot q of the 4-token step u is token s0 + 4u + q.
 template <int NT>
 __global__ __launch_bounds__(256) void k_cx_chunk_state(CxGeo g, TArg x, TArg B, TArg dt,
                                                         const float* A, float* states,
@@ -113,26 +113,30 @@ __global__ __launch_bounds__(256) void k_cx_chunk_state(CxGeo g, TArg x, TArg B,
 #pragma unroll
     for (int t = 0; t < NT; ++t) { are[t] = zero4(); aim[t] = zero4(); }
     const int p = pt * 16 + r16;
-    for (int s0 = 0; s0 < len; s0 += 4) {
-      const int s = s0 + q;  // < C: C is a multiple of 4
-      float2 xv = make_float2(0.0f, 0.0f);
-      float2 bv[NT];
+    // 16 tokens per pass: all their x and B values are requested before the products
+    for (int s0 = 0; s0 < len; s0 += 16) {
+      float2 xv[4], bv[4][NT];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) bv[t] = make_float2(0.0f, 0.0f);
-      if (s < len) {
-        xv = cx_row<float2>(x, bb, t0 + s, h)[p];
-        const float2* br = cx_row<float2>(B, bb, t0 + s, h);
+      for (int u = 0; u < 4; ++u) {
+        const int s = s0 + 4 * u + q;  // < C: C is a multiple of 16
+        const bool sv = s < len;
+        const float2* xr = cx_row<float2>(x, bb, t0 + (sv ? s : 0), h);
+        const float2* br = cx_row<float2>(B, bb, t0 + (sv ? s : 0), h);
+        xv[u] = sv ? xr[p] : make_float2(0.0f, 0.0f);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) bv[t] = br[t * 16 + r16];
+        for (int t = 0; t < NT; ++t) bv[u][t] = sv ? br[t * 16 + r16] : make_float2(0.0f, 0.0f);
       }
-      const float2 ws = w[s];
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        const float2 bw = cmul(ws, bv[t]);
-        are[t] = mfma4(xv.x, bw.x, are[t]);
-        are[t] = mfma4(-xv.y, bw.y, are[t]);
-        aim[t] = mfma4(xv.x, bw.y, aim[t]);
-        aim[t] = mfma4(xv.y, bw.x, aim[t]);
+      for (int u = 0; u < 4; ++u) {
+        const float2 ws = w[s0 + 4 * u + q];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const float2 bw = cmul(ws, bv[u][t]);
+          are[t] = mfma4(xv[u].x, bw.x, are[t]);
+          are[t] = mfma4(-xv[u].y, bw.y, are[t]);
+          aim[t] = mfma4(xv[u].x, bw.y, aim[t]);
+          aim[t] = mfma4(xv[u].y, bw.x, aim[t]);
+        }
       }
     }
 #pragma unroll
@@ -262,6 +266,18 @@ __global__ __launch_bounds__(256) void k_cx_chunk_scan(CxGeo g, TArg x, TArg B, 
       const int srow = st * 16 + r16;
       const bool sval = srow < len;
       const float2* brow = cx_row<float2>(B, bb, t0 + (sval ? srow : 0), h);
+      // this source tile's x rows (s = 16 st + 4q + r), requested before the C.B^T
+      // products so that they have arrived when Y_diag needs them
+      float2 xv[4][PT];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int s = st * 16 + 4 * q + r;
+        const bool xs = s < len;
+        const float2* xrow = cx_row<float2>(x, bb, t0 + (xs ? s : 0), h);
+#pragma unroll
+        for (int t = 0; t < PT; ++t)
+          xv[r][t] = xs ? xrow[t * 16 + r16] : make_float2(0.0f, 0.0f);
+      }
       f32x4 cbr = zero4(), cbi = zero4();
       for (int kb = 0; kb < nkb; ++kb) {
         const int n0 = kb * 16 + 4 * q;
@@ -300,22 +316,16 @@ __global__ __launch_bounds__(256) void k_cx_chunk_scan(CxGeo g, TArg x, TArg B, 
         }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int s = st * 16 + 4 * q + r;
-        const bool xs = s < len;
-        const float2* xrow = cx_row<float2>(x, bb, t0 + (xs ? s : 0), h);
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int t = 0; t < PT; ++t) {
-          float2 xv = make_float2(0.0f, 0.0f);
-          if (xs) xv = xrow[t * 16 + r16];
-          yre[t] = mfma4(mr[r], xv.x, yre[t]);
-          yre[t] = mfma4(-mi[r], xv.y, yre[t]);
+          yre[t] = mfma4(mr[r], xv[r][t].x, yre[t]);
+          yre[t] = mfma4(-mi[r], xv[r][t].y, yre[t]);
           if (CPLX) {
-            yim[t] = mfma4(mr[r], xv.y, yim[t]);
-            yim[t] = mfma4(mi[r], xv.x, yim[t]);
+            yim[t] = mfma4(mr[r], xv[r][t].y, yim[t]);
+            yim[t] = mfma4(mi[r], xv[r][t].x, yim[t]);
           }
         }
-      }
     }
 
     // lane holds y[l = 16 lt + 4q + i, p = 16 t + r16]
