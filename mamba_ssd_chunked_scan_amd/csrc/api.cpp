@@ -1071,6 +1071,10 @@ static ssd_status check_norm_problem(const ssd_norm_problem* p) {
     return fail(SSD_ERR_SHAPE, "eps = %g must be finite and >= 0", (double)p->eps);
   if ((int64_t)p->batch * p->seqlen > INT32_MAX)
     return fail(SSD_ERR_UNSUPPORTED, "batch * seqlen exceeds 2^31 - 1 tokens");
+  // the kernels number (token, 8-channel vector) items in 32 bits
+  if ((int64_t)p->batch * p->seqlen * (W / 8) > INT32_MAX)
+    return fail(SSD_ERR_UNSUPPORTED,
+                "batch * seqlen * nheads * headdim / 8 exceeds 2^31 - 1 (split the tokens)");
   return SSD_OK;
 }
 

@@ -327,3 +327,12 @@ def test_norm_workspace_size():
     p.group_size = 1024
     assert L.ssd_gated_rmsnorm_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws)) == 0
     assert ws.value == 128 * 4096 * 4 + 8192 * 4 * 8
+
+
+def test_norm_rejects_too_many_vectors():
+    L = ssd.lib()
+    p = ssd.SsdNormProblem()
+    p.batch, p.seqlen, p.nheads, p.headdim, p.group_size, p.eps = 64, 65536, 64, 64, 512, 1e-5
+    ws = ctypes.c_size_t(0)
+    assert L.ssd_gated_rmsnorm_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws)) == 5
+    assert "2^31" in L.ssd_last_error_message().decode()
