@@ -8,8 +8,10 @@ inputs already resident in HBM.  Prints ONE JSON line (rank 0).
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload nemotron]
                     [--algo staged|fused|auto] [--no-cpu-baseline] [--input-dt]
 
---workload complex_434m times the complex-A scan of the Mamba-3-Lite SSD
-Reference at its 434M shape (three kernels; complex64 inputs, real output).
+--workload complex_434m prints the complex-A scan's own line (the Mamba-3-Lite
+SSD Reference's 434M shape: three kernels; complex64 inputs, real output); the
+default line carries a 20-step measurement of it in 'complex_fwd' (--no-complex
+skips it), and the gated RMSNorm after the scan in 'gated_norm' (--no-norm).
 
 --input-dt puts the step size on the input term as well (delta x (outer) B,
 the discretised input of the Mamba-2 models); the default is the recurrence
@@ -75,6 +77,9 @@ def parse():
                     help="skip timing the gated RMSNorm after the scan (by default its forward "
                          "and backward are timed at the workload's shape in a 'gated_norm' "
                          "object)")
+    ap.add_argument("--no-complex", dest="complex", action="store_false",
+                    help="skip the complex-A forward at the SSD Reference's 434M shape (by "
+                         "default timed for 20 steps in a 'complex_fwd' object)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle until this much CPU time has been spent (min 3 runs)")
     ap.add_argument("--cold-steps", type=int, default=10,
@@ -393,6 +398,13 @@ def main():
                                           ms_per_step)
     if args.norm:
         result["gated_norm"] = time_norm(args, w, ssd, dev)
+    if args.complex:
+        from mamba_ssd_chunked_scan_amd.inputs import COMPLEX_WORKLOADS
+        cx = measure_complex(args, COMPLEX_WORKLOADS["complex_434m"], steps=20,
+                             warmup=min(args.warmup, 5))
+        result["complex_fwd"] = {k: cx[k] for k in ("metric", "value", "unit", "ms_per_step",
+                                                    "steps", "config", "roofline", "stages",
+                                                    "path_roofline_frac")}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
     print(json.dumps(result), flush=True)
@@ -512,9 +524,21 @@ def complex_stage_model(w):
 
 
 def bench_complex(args, w):
+    """Print the complex-A forward's own JSON line (bench.py --workload complex_434m)."""
+    result = measure_complex(args, w)
+    if not args.no_cpu_baseline:
+        from mamba_ssd_chunked_scan_amd.inputs import make_complex_inputs
+        result["cpu_baseline"] = cpu_baseline_complex(w, make_complex_inputs(w),
+                                                      args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def measure_complex(args, w, steps=None, warmup=None):
     """The complex-A forward: ssd_complex_chunk_state, ssd_complex_state_passing,
     ssd_complex_chunk_scan (what ssd_complex_forward launches), each bracketed
-    by HIP events on the stream it runs on."""
+    by HIP events on the stream it runs on.  Returns the result dict."""
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
     import torch
     from mamba_ssd_chunked_scan_amd import ssd
     from mamba_ssd_chunked_scan_amd.inputs import make_complex_inputs
@@ -557,7 +581,7 @@ def bench_complex(args, w):
             e1.record()
             events.setdefault(n, []).append((e0, e1))
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     # the stage sequence is exactly ssd_complex_forward (one more untimed step, so
     # that the check also holds with no warm-up)
@@ -570,12 +594,12 @@ def bench_complex(args, w):
     events = {}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step(events)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     per_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in events[n]])) for n in names}
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step = wall * 1e3 / steps
     nb, nf = complex_stage_model(w)
 
     def roof(n):
@@ -598,8 +622,8 @@ def bench_complex(args, w):
     roof_ms = sum(roof(n)[1] for n in names) * 1e3
     result = {
         "metric": "complex-A SSD fwd tokens/s (Mamba-3-Lite SSD Reference, 434M shape)",
-        "value": round(w.tokens * args.steps / wall, 1),
-        "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "value": round(w.tokens * steps / wall, 1),
+        "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{w.name}: complex-A SSD forward, batch {w.batch}, seq "
@@ -617,9 +641,8 @@ def bench_complex(args, w):
         "path_roofline_frac": round(roof_ms / ms_per_step, 4),
         "gpu": torch.cuda.get_device_name(0),
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline_complex(w, inp, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
+    del x, B, C, dt, A, st, lam, fin, out, ref_out, ref_fin
+    return result
 
 
 def cpu_baseline_complex(w, inp, seconds):
