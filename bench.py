@@ -493,7 +493,17 @@ def time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu, fwd_ms):
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
     bms = float(np.median(times))
+    # the backward's algorithmic bytes: read x, B, C, dt, z (input dtype) and dout
+    # (fp32); write dx, dB, dC, ddt, dz (fp32); per-head vectors are negligible
+    tok = w.batch * w.seqlen
+    H, P, G, N = w.nheads, w.headdim, w.ngroups, w.dstate
+    e = 2 if w.dtype == "bf16" else 4
+    zb = tok * H * P if w.has_z else 0
+    alg = (e * (tok * H * P + 2 * tok * G * N + tok * H + zb) + 4 * tok * H * P
+           + 4 * (tok * H * P + 2 * tok * G * N + tok * H + zb))
     return {"bwd_ms": round(bms, 5), "fwd_ms": round(fwd_ms, 5),
+            "bwd_algorithmic_bytes": alg,
+            "bwd_hbm_frac": round(alg / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "fwd_bwd_ms": round(bms + fwd_ms, 5),
             "tokens_per_s": round(w.tokens / ((bms + fwd_ms) * 1e-3), 1),
             "workspace_MB": round(ws.numel() / 1e6, 1), "steps": len(times),
