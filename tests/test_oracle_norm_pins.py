@@ -93,3 +93,71 @@ def test_backward_finite_differences():
         fd = (L(plus["y"], plus["z"], plus["w"]) - L(minus["y"], minus["z"], minus["w"])) / (2 * h)
         an = float(np.sum(grad * d))
         assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, fd, an)
+
+
+# ------------------------------------------------------------------ planted slips
+#
+# Each mutant is the oracle's forward or gradient with one plausible slip; the
+# library composition (torch rms_norm / silu / autograd) must reject every one.
+
+def _mut_fwd(kind, y, z, w, gs, eps):
+    y = np.asarray(y, dtype=np.float64)
+    s = 1.0 / (1.0 + np.exp(-z))
+    g = {"sigmoid_gate": y * s, "norm_before_gate": y}.get(kind, y * z * s)
+    lead = y.shape[:-2]
+    gg = g.reshape(lead + (-1, gs))
+    if kind == "group_over_heads_axis":
+        gg = g.reshape(lead + (gs, -1)).swapaxes(-1, -2)
+    ms = np.mean(gg * gg, axis=-1)
+    if kind == "no_eps":
+        eps = 0.0
+    r = 1.0 / np.sqrt(ms + eps) if kind != "std_not_rms" else 1.0 / np.sqrt(
+        np.var(gg, axis=-1) + eps)
+    xh = gg * r[..., None]
+    if kind == "group_over_heads_axis":
+        xh = xh.swapaxes(-1, -2)
+    out = xh.reshape(y.shape)
+    if kind == "norm_before_gate":
+        out = out * z * s
+    return out * np.asarray(w).reshape(y.shape[-2:])
+
+
+@pytest.mark.parametrize("kind", ["sigmoid_gate", "norm_before_gate", "no_eps",
+                                  "std_not_rms", "group_over_heads_axis"])
+def test_forward_slips_are_caught(kind):
+    y, z, w = case(8)
+    y = y * 1e-3  # small activations make a dropped eps visible
+    ref = library_forward(y, z, w, 16, 1e-5).numpy()
+    bad = _mut_fwd(kind, y, z, w, 16, 1e-5)
+    assert np.max(np.abs(bad - ref)) > 1e-6 * np.max(np.abs(ref))
+
+
+def _mut_bwd(kind, y, z, w, dout, gs, eps):
+    g = oracle.gated_rmsnorm_bwd(y, z, w, dout, gs, eps)
+    sig = 1.0 / (1.0 + np.exp(-z))
+    if kind == "dz_without_product_rule":
+        dg = g.dy / (z * sig)
+        return g.dy, dg * y * sig, g.dweight
+    if kind == "dy_without_gate":
+        return g.dy / (z * sig), g.dz, g.dweight
+    if kind == "dweight_on_gated_not_normalised":
+        gg = (y * z * sig)
+        return g.dy, g.dz, np.sum((dout * gg).reshape(-1, w.size), axis=0)
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["dz_without_product_rule", "dy_without_gate",
+                                  "dweight_on_gated_not_normalised"])
+def test_gradient_slips_are_caught(kind):
+    y, z, w = case(9)
+    dout = np.random.default_rng(10).standard_normal(y.shape)
+    dy, dz, dw = _mut_bwd(kind, y, z, w, dout, 16, 1e-5)
+    yt = torch.tensor(y, requires_grad=True)
+    zt = torch.tensor(z, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    n = torch.nn.functional.rms_norm((yt * torch.nn.functional.silu(zt)).reshape(2, 5, -1, 16),
+                                     (16,), eps=1e-5)
+    (n.reshape(yt.shape) * wt.reshape(4, 8) * torch.tensor(dout)).sum().backward()
+    bad = max(np.max(np.abs(dy - yt.grad.numpy())), np.max(np.abs(dz - zt.grad.numpy())),
+              np.max(np.abs(dw - wt.grad.numpy())))
+    assert bad > 1e-6
