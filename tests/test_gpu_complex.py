@@ -163,3 +163,58 @@ def test_stage_intermediates():
     torch.cuda.synchronize()
     y, f2 = run(inp, 64, out_complex=True)
     assert np.array_equal(out.cpu().numpy(), y) and np.array_equal(fin.cpu().numpy(), f2)
+
+
+def test_graph_capture_replays_match_eager():
+    # the complex forward and the gated RMSNorm (forward and backward) are
+    # stream-ordered device work with caller-owned buffers, so they can be
+    # captured in a HIP graph; every replay, with eager work in between, must
+    # reproduce the eager results exactly
+    inp = make_complex_inputs(COMPLEX_WORKLOADS["complex_tiny"])
+    x, B, C, dt, A, h0 = (dev(inp.x), dev(inp.B), dev(inp.C), dev(inp.dt), dev(inp.A),
+                          dev(inp.h0))
+    prob = ssd.ComplexProblem(*inp.x.shape[:1], inp.x.shape[1], inp.x.shape[2], inp.x.shape[3],
+                              inp.B.shape[3], 64)
+    ws = torch.empty(max(prob.workspace_size(), 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty(inp.x.shape, dtype=torch.complex64, device="cuda")
+    fin = torch.empty(inp.h0.shape, dtype=torch.complex64, device="cuda")
+    rng = np.random.default_rng(3)
+    ny, nz, ndo = (torch.from_numpy(rng.standard_normal((1, 80, 4, 64)).astype(np.float32)).cuda()
+                   for _ in range(3))
+    nw = torch.from_numpy((1.0 + 0.2 * rng.standard_normal(256)).astype(np.float32)).cuda()
+    nout = torch.empty_like(ny)
+    ndy, ndz, ndw = torch.empty_like(ny), torch.empty_like(ny), torch.empty_like(nw)
+    nws = torch.empty(max(ssd.gated_rmsnorm_bwd_workspace_size(ny, 128), 1), dtype=torch.uint8,
+                      device="cuda")
+
+    def work():
+        ssd.ssd_complex_forward(x, B, C, dt, A, initial_states=h0, chunk_size=64,
+                                out_complex=True, out=out, final_states=fin, workspace=ws)
+        ssd.ssd_gated_rmsnorm_fwd(ny, nz, nw, 128, out=nout)
+        ssd.ssd_gated_rmsnorm_bwd(ny, nz, nw, ndo, 128, workspace=nws, dy=ndy, dz=ndz, dw=ndw)
+
+    bufs = (out, fin, nout, ndy, ndz, ndw)
+    work()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in bufs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        work()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        work()
+    for _ in range(4):
+        for t in bufs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, r in zip(bufs, refs):
+            assert torch.equal(t, r)
+        work()  # eager work between replays
+        torch.cuda.synchronize()
+        for t, r in zip(bufs, refs):
+            assert torch.equal(t, r)
