@@ -568,7 +568,7 @@ def measure_complex(args, w, steps=None, warmup=None):
     nc = -(-w.seqlen // w.chunk_size)
     st = torch.empty((w.batch * nc, w.nheads, w.headdim, w.dstate), dtype=torch.complex64,
                      device=dev)
-    lam = torch.empty((w.batch, w.nheads, nc), dtype=torch.float32, device=dev)
+    lam = torch.empty((w.nheads, w.batch * nc), dtype=torch.float32, device=dev)
     fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.complex64,
                       device=dev)
     out = torch.empty((w.batch, w.seqlen, w.nheads, w.headdim), dtype=torch.float32, device=dev)

@@ -356,14 +356,22 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
  * ssd_tensor dtype is SSD_F32 and their strides count COMPLEX elements.
  */
 typedef struct ssd_complex_problem {
-  int32_t batch;       /* b >= 1 */
-  int32_t seqlen;      /* T >= 0 */
-  int32_t nheads;      /* H >= 1, batch * nheads <= 65535 */
+  int32_t batch;       /* b >= 1 (1 in packed mode) */
+  int32_t seqlen;      /* T >= 0: tokens per sequence, or total packed tokens */
+  int32_t nheads;      /* H >= 1, (batch or nseq) * nheads <= 65535 */
   int32_t headdim;     /* P (the page's D): multiple of 16, <= 128 */
   int32_t dstate;      /* N: multiple of 16, <= 128 */
   int32_t chunk_size;  /* C: 32, 64, 128 or 256 (the result does not depend on it) */
+  int32_t nseq;        /* packed mode: number of sequences; 0 = batch mode */
+  const int32_t* cu_seqlens; /* packed mode: device, nseq + 1 offsets, cu[0] = 0,
+                                non-decreasing, cu[nseq] = seqlen; each sequence is
+                                chunked from its own first token and starts from its
+                                initial state (or zero), as in the real scan's packed
+                                mode.  Only ssd_complex_forward takes packed problems. */
 } ssd_complex_problem;
 
+/* Packed mode drops the batch axis of every token tensor ((T, H, P) etc., the
+ * batch stride ignored) and indexes initial and final states by sequence. */
 typedef struct ssd_complex_fwd_args {
   ssd_tensor x;        /* (b, T, H, P) complex; rows 16-byte aligned */
   ssd_tensor B;        /* (b, T, H, N) complex; rows 16-byte aligned */
@@ -385,7 +393,8 @@ typedef struct ssd_complex_fwd_args {
 ssd_status ssd_complex_problem_check(const ssd_complex_problem* p);
 
 /* Bytes of workspace ssd_complex_forward needs: the per-chunk complex states
- * (b * ceil(T/C) * H * P * N * 8 bytes) and each chunk's step sum. */
+ * (K * H * P * N * 8 bytes, K = b * ceil(T/C), or ceil(T/C) + nseq when packed),
+ * each chunk's step sum and, when packed, the chunk table. */
 ssd_status ssd_complex_workspace_size(const ssd_complex_problem* p, size_t* bytes);
 
 /* The forward pass: three kernels on `stream` -- every chunk's end state from a
@@ -401,10 +410,11 @@ ssd_status ssd_complex_forward(const ssd_complex_problem* p, const ssd_complex_f
                                void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* The three stages ssd_complex_forward runs, for callers that keep the
- * intermediates.  nc = ceil(T / C); chunk j = (batch row) * nc + c.
+ * intermediates (batch mode only: a packed problem returns SSD_ERR_UNSUPPORTED).
+ * nc = ceil(T / C); chunk j = (batch row) * nc + c.
  *   states        float32 complex (b * nc, H, P, N), 16-byte aligned: the page's
  *                 internal states (B, n_chunks, H, D, N) ("Shape contract")
- *   chunk_dt_sum  float32 (b, H, nc), 16-byte aligned: sum of softplus(dt) over
+ *   chunk_dt_sum  float32 (H, b * nc), 16-byte aligned: sum of softplus(dt) over
  *                 each chunk's tokens (the chunk's total log-decay is this times A)
  *
  * ssd_complex_chunk_state: states[j] = sum_s exp(cs_last - cs_s) x_s (outer) B_s,

@@ -842,9 +842,17 @@ static ssd_status check_cx_problem(const ssd_complex_problem* p) {
   if (p->batch < 1) return fail(SSD_ERR_SHAPE, "batch = %d must be >= 1", p->batch);
   if (p->seqlen < 0) return fail(SSD_ERR_SHAPE, "seqlen = %d must be >= 0", p->seqlen);
   if (p->nheads < 1) return fail(SSD_ERR_SHAPE, "nheads = %d must be >= 1", p->nheads);
-  if ((int64_t)p->batch * p->nheads > 65535)
-    return fail(SSD_ERR_UNSUPPORTED, "batch * nheads = %lld exceeds 65535",
-                (long long)p->batch * p->nheads);
+  if (p->nseq < 0) return fail(SSD_ERR_SHAPE, "nseq = %d must be >= 0", p->nseq);
+  if (p->nseq > 0) {
+    if (p->batch != 1)
+      return fail(SSD_ERR_SHAPE, "packed mode (nseq = %d) requires batch == 1, got %d", p->nseq,
+                  p->batch);
+    if (!p->cu_seqlens) return fail(SSD_ERR_NULL, "packed mode requires cu_seqlens");
+  }
+  const int64_t nsq = p->nseq > 0 ? p->nseq : p->batch;
+  if (nsq * p->nheads > 65535)
+    return fail(SSD_ERR_UNSUPPORTED, "(batch or nseq) * nheads = %lld exceeds 65535",
+                (long long)(nsq * p->nheads));
   if (p->headdim < 16 || p->headdim > 128 || p->headdim % 16 != 0)
     return fail(SSD_ERR_UNSUPPORTED, "headdim = %d: must be a multiple of 16 in [16, 128]",
                 p->headdim);
@@ -924,24 +932,36 @@ static ssd_status check_aligned16(const void* ptr, const char* name, bool requir
   return SSD_OK;
 }
 
-static ssd::CxGeo cx_geo(const ssd_complex_problem* p) {
-  ssd::CxGeo g;
+static int64_t cx_num_chunks(const ssd_complex_problem* p) {
+  const int64_t nc = cdiv(p->seqlen, p->chunk_size);
+  return p->nseq > 0 ? nc + p->nseq : (int64_t)p->batch * nc;
+}
+
+// The complex scan on the shared chunk geometry: one "group" per head.
+static ssd::Geo cx_geo(const ssd_complex_problem* p, const int32_t* meta) {
+  ssd::Geo g;
   g.b = p->batch; g.T = p->seqlen; g.H = p->nheads; g.P = p->headdim; g.N = p->dstate;
+  g.G = p->nheads; g.hpg = 1;
   g.C = p->chunk_size;
   g.nc = (int)cdiv(p->seqlen, p->chunk_size);
+  g.K = (int)cx_num_chunks(p);
+  g.nseq = p->nseq > 0 ? p->nseq : p->batch;
+  g.meta = p->nseq > 0 ? meta : nullptr;
   return g;
 }
 
 struct CxWorkspace {
-  size_t states, lam, total;
+  size_t states, lam, meta, total;
 };
 
 static CxWorkspace cx_workspace(const ssd_complex_problem* p) {
-  const int64_t nc = cdiv(p->seqlen, p->chunk_size);
+  const int64_t K = cx_num_chunks(p);
   CxWorkspace w;
   w.states = 0;
-  w.lam = align256((size_t)p->batch * nc * p->nheads * p->headdim * p->dstate * 8);
-  w.total = w.lam + align256((size_t)p->batch * p->nheads * nc * sizeof(float));
+  w.lam = align256((size_t)K * p->nheads * p->headdim * p->dstate * 8);
+  w.meta = w.lam + align256((size_t)p->nheads * K * sizeof(float));
+  const size_t meta_len = p->nseq > 0 ? (size_t)(ssd::kMetaHeader + 3 * K + p->nseq + 1) : 0;
+  w.total = w.meta + align256(meta_len * sizeof(int32_t));
   return w;
 }
 
@@ -979,7 +999,10 @@ ssd_status ssd_complex_forward(const ssd_complex_problem* p, const ssd_complex_f
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
     return fail(SSD_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   char* ws = static_cast<char*>(workspace);
-  const ssd::CxGeo g = cx_geo(p);
+  int32_t* meta = reinterpret_cast<int32_t*>(ws + w.meta);
+  const ssd::Geo g = cx_geo(p, meta);
+  if (p->nseq > 0)
+    SSD_HIP(ssd::launch_varlen_meta(g, p->cu_seqlens, meta, stream), "chunk table launch");
   float* states = reinterpret_cast<float*>(ws + w.states);
   float* lam = reinterpret_cast<float*>(ws + w.lam);
   SSD_HIP(ssd::launch_cx_chunk_state(g, targ(a->x), targ(a->B), targ(a->dt), a->A, states, lam,
@@ -998,6 +1021,8 @@ ssd_status ssd_complex_chunk_state(const ssd_complex_problem* p, ssd_tensor x, s
                                    ssd_tensor dt, const float* A, float* states,
                                    float* chunk_dt_sum, hipStream_t stream) {
   SSD_TRY(check_cx_problem(p));
+  if (p->nseq > 0)
+    return fail(SSD_ERR_UNSUPPORTED, "packed problems run through ssd_complex_forward only");
   const bool tok = (int64_t)p->batch * p->seqlen > 0;
   SSD_TRY(check_cx_tensor(x, "x", tok));
   SSD_TRY(check_cx_tensor(B, "B", tok));
@@ -1005,7 +1030,7 @@ ssd_status ssd_complex_chunk_state(const ssd_complex_problem* p, ssd_tensor x, s
   SSD_TRY(check_cx_A(A));
   SSD_TRY(check_aligned16(states, "states", tok));
   SSD_TRY(check_aligned16(chunk_dt_sum, "chunk_dt_sum", tok));
-  SSD_HIP(ssd::launch_cx_chunk_state(cx_geo(p), targ(x), targ(B), targ(dt), A, states,
+  SSD_HIP(ssd::launch_cx_chunk_state(cx_geo(p, nullptr), targ(x), targ(B), targ(dt), A, states,
                                      chunk_dt_sum, stream),
           "complex chunk state launch");
   return ok();
@@ -1015,13 +1040,15 @@ ssd_status ssd_complex_state_passing(const ssd_complex_problem* p, const float* 
                                      const float* chunk_dt_sum, const float* initial_states,
                                      float* states, float* final_states, hipStream_t stream) {
   SSD_TRY(check_cx_problem(p));
+  if (p->nseq > 0)
+    return fail(SSD_ERR_UNSUPPORTED, "packed problems run through ssd_complex_forward only");
   const bool tok = (int64_t)p->batch * p->seqlen > 0;
   SSD_TRY(check_cx_A(A));
   SSD_TRY(check_aligned16(chunk_dt_sum, "chunk_dt_sum", tok));
   SSD_TRY(check_aligned16(states, "states", tok));
   SSD_TRY(check_aligned16(initial_states, "initial_states", false));
   SSD_TRY(check_aligned16(final_states, "final_states", false));
-  SSD_HIP(ssd::launch_cx_state_pass(cx_geo(p), A, chunk_dt_sum, initial_states, states,
+  SSD_HIP(ssd::launch_cx_state_pass(cx_geo(p, nullptr), A, chunk_dt_sum, initial_states, states,
                                     final_states, stream),
           "complex state passing launch");
   return ok();
@@ -1032,6 +1059,8 @@ ssd_status ssd_complex_chunk_scan(const ssd_complex_problem* p, ssd_tensor x, ss
                                   const float* states_in, ssd_tensor out, int32_t out_complex,
                                   hipStream_t stream) {
   SSD_TRY(check_cx_problem(p));
+  if (p->nseq > 0)
+    return fail(SSD_ERR_UNSUPPORTED, "packed problems run through ssd_complex_forward only");
   const bool tok = (int64_t)p->batch * p->seqlen > 0;
   SSD_TRY(check_cx_tensor(x, "x", tok));
   SSD_TRY(check_cx_tensor(B, "B", tok));
@@ -1040,7 +1069,7 @@ ssd_status ssd_complex_chunk_scan(const ssd_complex_problem* p, ssd_tensor x, ss
   SSD_TRY(check_cx_A(A));
   SSD_TRY(check_aligned16(states_in, "states_in", tok));
   SSD_TRY(check_cx_out(out, out_complex, tok));
-  SSD_HIP(ssd::launch_cx_chunk_scan(cx_geo(p), targ(x), targ(B), targ(C), targ(dt), A,
+  SSD_HIP(ssd::launch_cx_chunk_scan(cx_geo(p, nullptr), targ(x), targ(B), targ(C), targ(dt), A,
                                     states_in, targ(out), out_complex, stream),
           "complex chunk scan launch");
   return ok();

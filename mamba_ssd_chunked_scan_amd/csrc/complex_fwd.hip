@@ -67,7 +67,7 @@ __device__ __forceinline__ const T* cx_row(const TArg& a, int b, int t, int h) {
 
 // Inclusive cumsum of delta = softplus(dt) over the chunk's positions into sd[0..C);
 // positions past the chunk's end add 0 (their step is neutral).  Ends with a barrier.
-__device__ __forceinline__ void cx_delta_cumsum(const CxGeo& g, const TArg& dt, int b, int t0,
+__device__ __forceinline__ void cx_delta_cumsum(const Geo& g, const TArg& dt, int b, int t0,
                                                 int len, int h, float* sd) {
   if (threadIdx.x < kWave) {
     float carry = 0.0f;
@@ -89,20 +89,21 @@ __device__ __forceinline__ void cx_delta_cumsum(const CxGeo& g, const TArg& dt, 
 // Wave w computes p-tiles w, w + 4, ...; each p-tile holds all NT n-tiles.
 // Contraction over tokens: k-slot q of the 4-token step u is token s0 + 4u + q.
 template <int NT>
-__global__ __launch_bounds__(256) void k_cx_chunk_state(CxGeo g, TArg x, TArg B, TArg dt,
+__global__ __launch_bounds__(256) void k_cx_chunk_state(Geo g, TArg x, TArg B, TArg dt,
                                                         const float* A, float* states,
                                                         float* lam) {
   __shared__ float sd[kCxMaxChunk];
   __shared__ float2 w[kCxMaxChunk];
   const int j = blockIdx.x, h = blockIdx.y;
-  const int bb = j / g.nc, c = j - bb * g.nc;
-  const int t0 = c * g.C, len = min(g.C, g.T - t0);
+  Chunk ch;
+  if (!get_chunk(g, j, ch)) return;  // a packed batch's unused chunk slots
+  const int bb = ch.b, t0 = ch.t0, len = ch.len;
   cx_delta_cumsum(g, dt, bb, t0, len, h, sd);
   const float ar = A[2 * h], ai = A[2 * h + 1];
   const float last = sd[len - 1];
   for (int s = threadIdx.x; s < g.C; s += 256)
     w[s] = s < len ? cexp_step(last - sd[s], ar, ai) : make_float2(0.0f, 0.0f);
-  if (threadIdx.x == 0) lam[((int64_t)bb * g.H + h) * g.nc + c] = last;
+  if (threadIdx.x == 0) lam[(int64_t)h * g.K + j] = last;
   __syncthreads();
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -150,25 +151,29 @@ __global__ __launch_bounds__(256) void k_cx_chunk_state(CxGeo g, TArg x, TArg B,
 
 // ---------------------------------------------------------------- state passing
 
-// Hin[c] for every chunk of (b, h), in place over the chunk states, and the final
-// state.  Thread: complex elements e, e + 1 of the P x N state (one 16-byte word).
-__global__ __launch_bounds__(256) void k_cx_state_pass(CxGeo g, const float* A,
+// Hin[j] for every chunk j of (sequence i, head h), in place over the chunk states, and
+// the final state; each sequence starts from its initial state (or zero).  Thread:
+// complex elements e, e + 1 of the P x N state (one 16-byte word).
+__global__ __launch_bounds__(256) void k_cx_state_pass(Geo g, const float* A,
                                                        const float* lam, const float* h0,
                                                        float* states, float* hfinal) {
   __shared__ float2 dec[256];
-  const int bh = blockIdx.y;
-  const int bb = bh / g.H, h = bh - bb * g.H;
+  const int ih = blockIdx.y;
+  const int i = ih / g.H, h = ih - i * g.H;
+  int first, last;
+  seq_chunks(g, i, first, last);
+  const int nch = last - first;
   const int64_t PN = (int64_t)g.P * g.N;
   const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 2;
   const bool act = e < PN;
   float4 run = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-  if (act && h0) run = *reinterpret_cast<const float4*>(h0 + (bh * PN + e) * 2);
+  if (act && h0) run = *reinterpret_cast<const float4*>(h0 + (ih * PN + e) * 2);
   const float ar = A[2 * h], ai = A[2 * h + 1];
-  for (int cb = 0; cb < g.nc; cb += 256) {
-    const int nb = min(256, g.nc - cb);
+  for (int cb = 0; cb < nch; cb += 256) {
+    const int nb = min(256, nch - cb);
     __syncthreads();
     if ((int)threadIdx.x < nb)
-      dec[threadIdx.x] = cexp_step(lam[(int64_t)bh * g.nc + cb + threadIdx.x], ar, ai);
+      dec[threadIdx.x] = cexp_step(lam[(int64_t)h * g.K + first + cb + threadIdx.x], ar, ai);
     __syncthreads();
     if (!act) continue;
     for (int k = 0; k < nb; k += 8) {
@@ -177,12 +182,12 @@ __global__ __launch_bounds__(256) void k_cx_state_pass(CxGeo g, const float* A,
       for (int u = 0; u < 8; ++u)
         if (k + u < nb)
           sv[u] = *reinterpret_cast<const float4*>(
-              states + ((((int64_t)bb * g.nc + cb + k + u) * g.H + h) * PN + e) * 2);
+              states + ((((int64_t)first + cb + k + u) * g.H + h) * PN + e) * 2);
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
         if (k + u >= nb) break;
         float4* dst = reinterpret_cast<float4*>(
-            states + ((((int64_t)bb * g.nc + cb + k + u) * g.H + h) * PN + e) * 2);
+            states + ((((int64_t)first + cb + k + u) * g.H + h) * PN + e) * 2);
         *dst = run;
         const float2 d = dec[k + u];
         const float2 r0 = cmul(d, make_float2(run.x, run.y));
@@ -191,7 +196,7 @@ __global__ __launch_bounds__(256) void k_cx_state_pass(CxGeo g, const float* A,
       }
     }
   }
-  if (act && hfinal) *reinterpret_cast<float4*>(hfinal + (bh * PN + e) * 2) = run;
+  if (act && hfinal) *reinterpret_cast<float4*>(hfinal + (ih * PN + e) * 2) = run;
 }
 
 // ---------------------------------------------------------------- chunk scan
@@ -204,14 +209,15 @@ __global__ __launch_bounds__(256) void k_cx_state_pass(CxGeo g, const float* A,
 //           Y_diag (row l, k-slot q, instruction r <-> s = 4q + r).
 //   Y_diag: B operand x[s, p] for the same s of each (q, r).
 template <int PT, bool CPLX>
-__global__ __launch_bounds__(256) void k_cx_chunk_scan(CxGeo g, TArg x, TArg B, TArg Cm,
+__global__ __launch_bounds__(256) void k_cx_chunk_scan(Geo g, TArg x, TArg B, TArg Cm,
                                                        TArg dt, const float* A,
                                                        const float* states, TArg out) {
   __shared__ float sd[kCxMaxChunk];
   __shared__ float2 ecs[kCxMaxChunk];
   const int j = blockIdx.x, h = blockIdx.y;
-  const int bb = j / g.nc, c = j - bb * g.nc;
-  const int t0 = c * g.C, len = min(g.C, g.T - t0);
+  Chunk ch;
+  if (!get_chunk(g, j, ch)) return;  // a packed batch's unused chunk slots
+  const int bb = ch.b, t0 = ch.t0, len = ch.len;
   cx_delta_cumsum(g, dt, bb, t0, len, h, sd);
   const float ar = A[2 * h], ai = A[2 * h + 1];
   for (int l = threadIdx.x; l < g.C; l += 256) ecs[l] = cexp_step(sd[l], ar, ai);
@@ -349,17 +355,17 @@ __global__ __launch_bounds__(256) void k_cx_chunk_scan(CxGeo g, TArg x, TArg B, 
 }
 
 template <int NT>
-hipError_t launch_state_nt(const CxGeo& g, TArg x, TArg B, TArg dt, const float* A,
+hipError_t launch_state_nt(const Geo& g, TArg x, TArg B, TArg dt, const float* A,
                            float* states, float* lam, hipStream_t s) {
-  dim3 grid(g.b * g.nc, g.H);
+  dim3 grid(g.K, g.H);
   hipLaunchKernelGGL(k_cx_chunk_state<NT>, grid, dim3(256), 0, s, g, x, B, dt, A, states, lam);
   return hipGetLastError();
 }
 
 template <int PT>
-hipError_t launch_scan_pt(const CxGeo& g, TArg x, TArg B, TArg Cm, TArg dt, const float* A,
+hipError_t launch_scan_pt(const Geo& g, TArg x, TArg B, TArg Cm, TArg dt, const float* A,
                           const float* states, TArg out, int cplx, hipStream_t s) {
-  dim3 grid(g.b * g.nc, g.H);
+  dim3 grid(g.K, g.H);
   if (cplx)
     hipLaunchKernelGGL((k_cx_chunk_scan<PT, true>), grid, dim3(256), 0, s, g, x, B, Cm, dt, A,
                        states, out);
@@ -371,9 +377,9 @@ hipError_t launch_scan_pt(const CxGeo& g, TArg x, TArg B, TArg Cm, TArg dt, cons
 
 }  // namespace
 
-hipError_t launch_cx_chunk_state(const CxGeo& g, TArg x, TArg B, TArg dt, const float* A,
+hipError_t launch_cx_chunk_state(const Geo& g, TArg x, TArg B, TArg dt, const float* A,
                                  float* states, float* lam, hipStream_t s) {
-  if (g.b * g.nc == 0) return hipSuccess;
+  if (g.K == 0) return hipSuccess;
   switch (g.N / 16) {
     case 1: return launch_state_nt<1>(g, x, B, dt, A, states, lam, s);
     case 2: return launch_state_nt<2>(g, x, B, dt, A, states, lam, s);
@@ -386,18 +392,18 @@ hipError_t launch_cx_chunk_state(const CxGeo& g, TArg x, TArg B, TArg dt, const 
   }
 }
 
-hipError_t launch_cx_state_pass(const CxGeo& g, const float* A, const float* lam,
+hipError_t launch_cx_state_pass(const Geo& g, const float* A, const float* lam,
                                 const float* h0, float* states, float* hfinal, hipStream_t s) {
   const int64_t PN = (int64_t)g.P * g.N;
-  dim3 grid((unsigned)((PN + 511) / 512), g.b * g.H);
+  dim3 grid((unsigned)((PN + 511) / 512), g.nseq * g.H);
   hipLaunchKernelGGL(k_cx_state_pass, grid, dim3(256), 0, s, g, A, lam, h0, states, hfinal);
   return hipGetLastError();
 }
 
-hipError_t launch_cx_chunk_scan(const CxGeo& g, TArg x, TArg B, TArg Cm, TArg dt,
+hipError_t launch_cx_chunk_scan(const Geo& g, TArg x, TArg B, TArg Cm, TArg dt,
                                 const float* A, const float* states, TArg out, int out_complex,
                                 hipStream_t s) {
-  if (g.b * g.nc == 0) return hipSuccess;
+  if (g.K == 0) return hipSuccess;
   switch (g.P / 16) {
     case 1: return launch_scan_pt<1>(g, x, B, Cm, dt, A, states, out, out_complex, s);
     case 2: return launch_scan_pt<2>(g, x, B, Cm, dt, A, states, out, out_complex, s);

@@ -108,19 +108,16 @@ hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* CB
                                  TArg ddt, double* part, float* dA, float* ddt_bias, float* dD,
                                  float* dh0, hipStream_t s);
 
-// ---- complex-A forward (complex_fwd.hip): batch mode, per-head complex B, C
-struct CxGeo {
-  int b, T, H, P, N, C;
-  int nc;  // ceil(T / C)
-};
-// x, B, C, out (complex) strides in complex elements; dt, out (real) in floats.
-// states: b * nc * H * P * N complex; lam: b * H * nc floats (each chunk's step sum).
-hipError_t launch_cx_chunk_state(const CxGeo& g, TArg x, TArg B, TArg dt, const float* A,
+// ---- complex-A forward (complex_fwd.hip): per-head complex B, C (g.G = g.H),
+// batch or packed mode (g.meta); x, B, C, out (complex) strides in complex elements,
+// dt and out (real) in floats.  states: K * H * P * N complex; lam: H * K floats (each
+// chunk's step sum).
+hipError_t launch_cx_chunk_state(const Geo& g, TArg x, TArg B, TArg dt, const float* A,
                                  float* states, float* lam, hipStream_t s);
 // in place: the chunk states become the carry-in states
-hipError_t launch_cx_state_pass(const CxGeo& g, const float* A, const float* lam,
+hipError_t launch_cx_state_pass(const Geo& g, const float* A, const float* lam,
                                 const float* h0, float* states, float* hfinal, hipStream_t s);
-hipError_t launch_cx_chunk_scan(const CxGeo& g, TArg x, TArg B, TArg Cm, TArg dt,
+hipError_t launch_cx_chunk_scan(const Geo& g, TArg x, TArg B, TArg Cm, TArg dt,
                                 const float* A, const float* states, TArg out, int out_complex,
                                 hipStream_t s);
 

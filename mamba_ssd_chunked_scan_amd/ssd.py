@@ -71,7 +71,8 @@ class SsdBwdArgs(ctypes.Structure):
 class SsdComplexProblem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
                 ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
-                ("dstate", ctypes.c_int32), ("chunk_size", ctypes.c_int32)]
+                ("dstate", ctypes.c_int32), ("chunk_size", ctypes.c_int32),
+                ("nseq", ctypes.c_int32), ("cu_seqlens", ctypes.c_void_p)]
 
 
 class SsdComplexFwdArgs(ctypes.Structure):
@@ -461,9 +462,9 @@ def ssd_backward(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_sta
 
 # ------------------------------------------------------------------ complex A
 
-def _cx_tensor(t: torch.Tensor | None) -> SsdTensor:
-    """ssd_tensor of a complex64 (b, T, H, X) tensor: float32 pairs, strides in
-    complex elements (the innermost must be 1)."""
+def _cx_tensor(t: torch.Tensor | None, packed: bool = False) -> SsdTensor:
+    """ssd_tensor of a complex64 (b, T, H, X) tensor, or (T, H, X) when packed:
+    float32 pairs, strides in complex elements (the innermost must be 1)."""
     s = SsdTensor()
     s.dtype = F32
     if t is None or t.numel() == 0:
@@ -471,13 +472,15 @@ def _cx_tensor(t: torch.Tensor | None) -> SsdTensor:
         return s
     if t.dtype != torch.complex64:
         raise SSDError(3, f"expected complex64, got {t.dtype}")
-    if t.dim() != 4:
-        raise SSDError(2, f"expected a 4-D tensor, got shape {tuple(t.shape)}")
-    if t.stride(3) != 1 and t.shape[3] > 1:
+    want = 3 if packed else 4
+    if t.dim() != want:
+        raise SSDError(2, f"expected a {want}-D tensor, got shape {tuple(t.shape)}")
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
         raise SSDError(4, "innermost dimension must be contiguous")
     s.data = t.data_ptr()
+    st = ([0] if packed else []) + [int(v) for v in t.stride()]
     for i in range(3):
-        s.stride[i] = int(t.stride(i))
+        s.stride[i] = st[i]
     return s
 
 
@@ -489,11 +492,15 @@ class ComplexProblem:
     headdim: int
     dstate: int
     chunk_size: int = 64
+    nseq: int = 0
+    cu_seqlens: torch.Tensor | None = None   # device int32 (nseq + 1), packed mode
 
     def c(self) -> SsdComplexProblem:
         p = SsdComplexProblem()
         p.batch, p.seqlen, p.nheads = self.batch, self.seqlen, self.nheads
         p.headdim, p.dstate, p.chunk_size = self.headdim, self.dstate, self.chunk_size
+        p.nseq = self.nseq
+        p.cu_seqlens = _ptr(self.cu_seqlens)
         return p
 
     def check(self):
@@ -507,23 +514,33 @@ class ComplexProblem:
 
 def ssd_complex_forward(x, B, C, dt, A, initial_states=None, chunk_size=64,
                         out_complex=False, out=None, final_states=None, workspace=None,
-                        stream=None):
+                        cu_seqlens=None, stream=None):
     """The complex-A SSD forward (ssd_complex_forward).
 
     x (b, T, H, P), B and C (b, T, H, N) complex64; dt (b, T, H) float32; A (H,)
-    complex64; initial_states (b, H, P, N) complex64 or None.  Returns
-    (out, final_states): out is float32 (the real part) or, with out_complex,
-    complex64; final_states (b, H, P, N) complex64.
+    complex64; initial_states (b, H, P, N) complex64 or None.  Packed mode
+    (cu_seqlens: device int32, nseq + 1 offsets): the token tensors have no batch
+    axis and the states are per sequence.  Returns (out, final_states): out is
+    float32 (the real part) or, with out_complex, complex64.
     """
-    b, T, H, P = x.shape
-    N = B.shape[3]
-    prob = ComplexProblem(b, T, H, P, N, chunk_size)
+    packed = cu_seqlens is not None
+    if packed:
+        T, H, P = x.shape
+        N = B.shape[2]
+        nseq = cu_seqlens.numel() - 1
+        prob = ComplexProblem(1, T, H, P, N, chunk_size, nseq=nseq, cu_seqlens=cu_seqlens)
+        lead, ns = (T,), nseq
+    else:
+        b, T, H, P = x.shape
+        N = B.shape[3]
+        prob = ComplexProblem(b, T, H, P, N, chunk_size)
+        lead, ns = (b, T), b
     dev = x.device
     if out is None:
-        out = torch.empty((b, T, H, P), dtype=torch.complex64 if out_complex else torch.float32,
+        out = torch.empty(lead + (H, P), dtype=torch.complex64 if out_complex else torch.float32,
                           device=dev)
     if final_states is None:
-        final_states = torch.empty((b, H, P, N), dtype=torch.complex64, device=dev)
+        final_states = torch.empty((ns, H, P, N), dtype=torch.complex64, device=dev)
     if initial_states is not None and not initial_states.is_contiguous():
         raise SSDError(4, "initial_states must be contiguous")
     if not final_states.is_contiguous():
@@ -536,14 +553,14 @@ def ssd_complex_forward(x, B, C, dt, A, initial_states=None, chunk_size=64,
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     a = SsdComplexFwdArgs()
-    a.x, a.B, a.C = _cx_tensor(x), _cx_tensor(B), _cx_tensor(C)
-    a.dt = tensor_arg(dt)
+    a.x, a.B, a.C = (_cx_tensor(x, packed), _cx_tensor(B, packed), _cx_tensor(C, packed))
+    a.dt = tensor_arg(dt, packed)
     a.A = A.data_ptr()
     a.initial_states = _ptr(initial_states)
     if out_complex:
-        a.out = _cx_tensor(out)
+        a.out = _cx_tensor(out, packed)
     else:
-        a.out = tensor_arg(out)
+        a.out = tensor_arg(out, packed)
     a.out_complex = 1 if out_complex else 0
     a.final_states = final_states.data_ptr()
     _check(lib().ssd_complex_forward(ctypes.byref(prob.c()), ctypes.byref(a),

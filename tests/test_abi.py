@@ -336,3 +336,33 @@ def test_norm_rejects_too_many_vectors():
     ws = ctypes.c_size_t(0)
     assert L.ssd_gated_rmsnorm_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws)) == 5
     assert "2^31" in L.ssd_last_error_message().decode()
+
+
+def test_complex_packed_checks():
+    L = ssd.lib()
+    p = cx_prob(batch=2, seqlen=100, nseq=3)
+    assert L.ssd_complex_problem_check(ctypes.byref(p.c())) == 2
+    assert "batch == 1" in L.ssd_last_error_message().decode()
+    p = cx_prob(batch=1, seqlen=100, nseq=3)
+    assert L.ssd_complex_problem_check(ctypes.byref(p.c())) == 1
+    assert "cu_seqlens" in L.ssd_last_error_message().decode()
+    # the stage calls take batch problems only
+    c = p.c()
+    buf = (ctypes.c_int32 * 4)(0, 10, 50, 100)
+    c.cu_seqlens = ctypes.cast(buf, ctypes.c_void_p)
+    rc = L.ssd_complex_chunk_state(ctypes.byref(c), ssd.SsdTensor(), ssd.SsdTensor(),
+                                   ssd.SsdTensor(), None, None, None, None)
+    assert rc == 5 and "ssd_complex_forward" in L.ssd_last_error_message().decode()
+
+
+def test_complex_packed_workspace_includes_chunk_table():
+    L = ssd.lib()
+    p = cx_prob(batch=1, seqlen=1000, nseq=5, chunk_size=64)
+    c = p.c()
+    buf = (ctypes.c_int32 * 6)(0, 100, 200, 300, 400, 1000)
+    c.cu_seqlens = ctypes.cast(buf, ctypes.c_void_p)
+    ws = ctypes.c_size_t(0)
+    assert L.ssd_complex_workspace_size(ctypes.byref(c), ctypes.byref(ws)) == 0
+    K = 16 + 5
+    r256 = lambda v: (v + 255) // 256 * 256
+    assert ws.value == r256(K * 16 * 64 * 64 * 8) + r256(16 * K * 4) + r256((4 + 3 * K + 6) * 4)

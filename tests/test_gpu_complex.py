@@ -137,7 +137,7 @@ def test_stage_intermediates():
                           dev(inp.h0))
     st = torch.empty((w.batch * nc, w.nheads, w.headdim, w.dstate), dtype=torch.complex64,
                      device="cuda")
-    lam = torch.empty((w.batch, w.nheads, nc), dtype=torch.float32, device="cuda")
+    lam = torch.empty((w.nheads, w.batch * nc), dtype=torch.float32, device="cuda")
     ssd.ssd_complex_chunk_state(prob, x, B, dt, A, st, lam)
     torch.cuda.synchronize()
     S = st.cpu().numpy().reshape(w.batch, nc, w.nheads, w.headdim, w.dstate)
@@ -218,3 +218,40 @@ def test_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for t, r in zip(bufs, refs):
             assert torch.equal(t, r)
+
+
+@pytest.mark.parametrize("C", [32, 64, 256])
+def test_packed_sequences(C):
+    # sequences packed on one token axis (cu_seqlens): an empty one, a single
+    # token, exact multiples of the chunk and ragged tails; each starts from its
+    # own initial state
+    lens = [1, 0, C - 1, C, C + 1, 2 * C + 3, 37]
+    T = sum(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    w = ComplexWorkload("packed", 1, T, 3, 32, 16, C, seed=31 + C)
+    inp = make_complex_inputs(w)
+    x, B, Cm, dt = inp.x[0], inp.B[0], inp.C[0], inp.dt[0]
+    rng = np.random.default_rng(C)
+    h0 = (rng.standard_normal((len(lens), 3, 32, 16))
+          + 1j * rng.standard_normal((len(lens), 3, 32, 16))).astype(np.complex64)
+    cu_dev = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    y, fin = ssd.ssd_complex_forward(dev(x), dev(B), dev(Cm), dev(dt), dev(inp.A),
+                                     initial_states=dev(h0), chunk_size=C, out_complex=True,
+                                     cu_seqlens=cu_dev)
+    torch.cuda.synchronize()
+    y, fin = y.cpu().numpy(), fin.cpu().numpy()
+    ref = oracle.ssd_complex_fwd(x, B, Cm, dt, inp.A, initial_states=h0, cu_seqlens=cu)
+    check(y, fin, ref, True)
+    # every sequence run on its own in batch mode gives the same bits
+    for i, L in enumerate(lens):
+        a, b_ = int(cu[i]), int(cu[i + 1])
+        if L == 0:
+            assert np.array_equal(fin[i], h0[i])
+            continue
+        yi, fi = ssd.ssd_complex_forward(dev(x[None, a:b_]), dev(B[None, a:b_]),
+                                         dev(Cm[None, a:b_]), dev(dt[None, a:b_]), dev(inp.A),
+                                         initial_states=dev(h0[i:i + 1]), chunk_size=C,
+                                         out_complex=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(yi.cpu().numpy()[0], y[a:b_])
+        assert np.array_equal(fi.cpu().numpy()[0], fin[i])
