@@ -255,3 +255,23 @@ def test_packed_sequences(C):
         torch.cuda.synchronize()
         assert np.array_equal(yi.cpu().numpy()[0], y[a:b_])
         assert np.array_equal(fi.cpu().numpy()[0], fin[i])
+
+
+def test_long_sequence_more_than_256_chunks():
+    # 300 chunks in one sequence: the pass over chunks takes its decays in blocks of
+    # 256, so the second block is exercised (and a packed batch around it)
+    T = 64 * 300 - 17
+    w = ComplexWorkload("long", 1, T, 2, 16, 16, 64, seed=77, initial_states=True)
+    inp = make_complex_inputs(w)
+    y, fin = run(inp, 64, out_complex=True)
+    check(y, fin, reference(inp), True)
+    lens = [5, T - 5 - 64, 64]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    x, B, Cm, dt = inp.x[0], inp.B[0], inp.C[0], inp.dt[0]
+    h0 = np.repeat(inp.h0, 3, axis=0)
+    yp, fp = ssd.ssd_complex_forward(dev(x), dev(B), dev(Cm), dev(dt), dev(inp.A),
+                                     initial_states=dev(h0), chunk_size=64, out_complex=True,
+                                     cu_seqlens=torch.tensor(cu, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    ref = oracle.ssd_complex_fwd(x, B, Cm, dt, inp.A, initial_states=h0, cu_seqlens=cu)
+    check(yp.cpu().numpy(), fp.cpu().numpy(), ref, True)
