@@ -41,6 +41,7 @@ def dev(a, dt):
     ((1, 50, 6, 32), 64),        # groups spanning two heads
     ((1, 40, 16, 64), 1024),     # wider than a strip (statistics pass)
     ((1, 33, 12, 16), 8),
+    ((1, 20, 128, 64), 8192),    # Granite's one group of d_inner = 8192 channels
 ])
 @pytest.mark.parametrize("bf16", [False, True])
 @pytest.mark.parametrize("gated", [True, False])
@@ -118,3 +119,14 @@ def test_nemotron_size_sampled():
     assert err(dy.cpu().numpy(), g.dy) <= TOL
     assert err(dz.cpu().numpy(), g.dz) <= TOL
     assert err(dw.cpu().numpy(), g.dweight) <= TOL
+
+
+def test_no_tokens():
+    # an empty batch: nothing is written except the weight gradient, which is zero
+    y = torch.empty((1, 0, 4, 16), dtype=torch.float32, device="cuda")
+    w = torch.ones(64, dtype=torch.float32, device="cuda")
+    out, _ = ssd.ssd_gated_rmsnorm_fwd(y, y, w, 16)
+    dy, dz, dw = ssd.ssd_gated_rmsnorm_bwd(y, y, w, y, 16)
+    torch.cuda.synchronize()
+    assert out.shape == y.shape and dy.shape == y.shape
+    assert torch.equal(dw, torch.zeros_like(dw))
