@@ -193,6 +193,27 @@ def cpu_baseline(w, inp, seconds):
             "seconds": t, "cpu": platform.processor() or platform.machine()}
 
 
+def environment(torch, ssd):
+    """Provenance of a measurement: device, compute units, software versions and the
+    source revision when a git checkout is present."""
+    import subprocess
+    props = torch.cuda.get_device_properties(0)
+    commit = None
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short", "HEAD"],
+                           capture_output=True, text=True, timeout=5)
+        commit = r.stdout.strip() or None
+    except Exception:
+        commit = None
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None),
+            "compute_units": props.multi_processor_count,
+            "hbm_GB": round(props.total_memory / 1e9, 1),
+            "hip": torch.version.hip, "torch": torch.__version__,
+            "libssd": ssd.lib().ssd_version().decode(), "commit": commit,
+            "host_cpu": platform.processor() or platform.machine(),
+            "host_cores": os.cpu_count()}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -392,6 +413,7 @@ def main():
                   "note": "median of event-timed forwards, each after a 512 MB cache flush"}
                  if cold_ms else None),
         "gpu": torch.cuda.get_device_name(0),
+        "env": environment(torch, ssd),
     }
     if args.backward:
         result["fwd_bwd"] = time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu,
@@ -650,6 +672,7 @@ def measure_complex(args, w, steps=None, warmup=None):
         "stages": stages,
         "path_roofline_frac": round(roof_ms / ms_per_step, 4),
         "gpu": torch.cuda.get_device_name(0),
+        "env": environment(torch, ssd),
     }
     del x, B, C, dt, A, st, lam, fin, out, ref_out, ref_fin
     return result
