@@ -352,6 +352,17 @@ def main():
     tokens = w.tokens
     value = tokens * args.steps / wall
 
+    # host submission: the time one whole forward call takes to return on the host
+    # (every launch is asynchronous), each timed on an idle queue
+    submit_us = []
+    for _ in range(20):
+        torch.cuda.synchronize()
+        h0 = time.perf_counter()
+        for _name, fn in launches():
+            fn()
+        submit_us.append((time.perf_counter() - h0) * 1e6)
+    torch.cuda.synchronize()
+
     sbytes = 4 if sdt == torch.float32 else 2
     obytes = 2 if odt == torch.bfloat16 else 4
     ibytes = 2 if w.dtype == "bf16" else 4
@@ -407,6 +418,7 @@ def main():
         },
         "stages": stages,
         "path_roofline_frac": round(roof_time_ms / ms_per_step, 4),
+        "host_submit_us": round(float(np.median(submit_us)), 1),
         "cold": ({"ms_median": round(float(np.median(cold_ms)), 5),
                   "value": round(tokens / (float(np.median(cold_ms)) * 1e-3), 1),
                   "steps": len(cold_ms),
