@@ -73,6 +73,12 @@ WORKLOADS = {
                                 seed=1002, nseq=8),
     "longctx": Workload("longctx", 1, 65536, 80, 64, 1, 128, 256, has_z=False,
                         seed=1003),
+    # the forward + backward shape of cudnn-frontend PR 1133 (batch 2, seq 2048,
+    # 64 heads, head and state dim 64, one group), gated and ungated; timed with
+    # 128-token chunks (the result does not depend on the chunk length)
+    "cudnn_gated": Workload("cudnn_gated", 2, 2048, 64, 64, 1, 64, 128, seed=1004),
+    "cudnn_ungated": Workload("cudnn_ungated", 2, 2048, 64, 64, 1, 64, 128, has_z=False,
+                              seed=1005),
 }
 
 
