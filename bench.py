@@ -60,6 +60,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="nemotron")
+    ap.add_argument("--seqlen", type=int, default=None,
+                    help="override the workload's sequence length (e.g. a sweep over the "
+                         "vLLM microbenchmark's 1k-64k tokens at granite dims)")
     ap.add_argument("--algo", default="auto", choices=["auto", "staged", "fused"])
     ap.add_argument("--state-dtype", default="f32", choices=["f32", "bf16"])
     ap.add_argument("--out-dtype", default="bf16", choices=["f32", "bf16"])
@@ -232,6 +235,9 @@ def main():
         bench_complex(args, COMPLEX_WORKLOADS[args.workload])
         return
     w = WORKLOADS[args.workload]
+    if args.seqlen is not None:
+        import dataclasses
+        w = dataclasses.replace(w, seqlen=args.seqlen)
     inp = make_inputs(w)
     dev = torch.device("cuda:0")
     if args.copy_calibration:
