@@ -218,7 +218,7 @@ FusedWs fused_layout(const ssd_problem* p) {
   if (p->nseq > 0)
     off += align256((size_t)(ssd::kMetaHeader + 3 * w.K + p->nseq + 1) * sizeof(int32_t));
   w.sync = off;
-  off += align256((size_t)(2 + slots) * sizeof(uint32_t));
+  off += align256((size_t)(ssd::kFusedSyncHeader + slots) * sizeof(uint32_t));
   w.edec = off;
   off += align256((size_t)slots * sizeof(float));
   w.agg = off;

@@ -30,9 +30,16 @@
 //      Y_off + Y_diag (with the D skip on its diagonal), SiLU gate, store;
 //      then H_{j+1} = exp(Lambda_j)
 //      H_j + S_j in registers, and the final state at a sequence's last chunk.
-// Workgroups take (unit, range) in order from an atomic ticket counter, so a
-// workgroup only ever waits for work that a running or finished workgroup
-// owns: no residency assumption, no deadlock.  Every wait is bounded; on
+// Work queues.  There is one queue of (unit, range) items per XCD: queue x
+// holds the units [x U / 8, (x + 1) U / 8) -- consecutive heads, so the heads
+// of a group, which read the same B and C, meet in one XCD's L2 -- range
+// first.  A workgroup takes the next ticket of its own XCD's queue (the XCC_ID
+// hardware register), and once that queue is exhausted, of the others in turn.
+// A workgroup only waits for lower ranges of its own unit, which sit earlier
+// in the same queue and were therefore taken by running or finished
+// workgroups: no residency assumption, no deadlock.  Items never outnumber
+// workgroups, and a workgroup leaves without an item only when every queue is
+// exhausted, so every item is taken whatever the XCD placement.  Every wait is bounded; on
 // timeout an error bit is set in the workspace and the kernel still finishes.
 //
 // Hand-off.  Aggregates, decays and flags are written with agent-scope atomic
@@ -131,8 +138,10 @@ struct FusedArgs {
   float* hfinal;
   int softplus, clamp, input_dt;
   float dt_min, dt_max;
-  int U, PS, R;           // units, P slabs per head, chunks per range
-  uint32_t* sync;         // [0] ticket counter, [1] error bits, [2 + r * U + u] flags
+  int U, PS, R, nr;       // units, P slabs per head, chunks per range, ranges
+  // [0, kFusedQueues) queue counters, [kFusedQueues] error bits,
+  // [kFusedSyncHeader + r * U + u] flags
+  uint32_t* sync;
   float* edec;            // [r * U + u] total decay of the range's aggregate
   float* agg;             // [r * U + u][64][NMAX] aggregates
 };
@@ -156,11 +165,34 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int r16 = lane % 16, q = lane / 16;
 
-  if (tid == 0)
-    s_misc[0] = __hip_atomic_fetch_add(a.sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  // units [queue_lo(x), queue_lo(x + 1)) belong to queue x
+  auto queue_lo = [&](int x) { return x * a.U / kFusedQueues; };
+  if (tid == 0) {
+    // hwreg 20 (XCC_ID), bits [3:0]: the XCD this workgroup runs on
+    const int xcd = (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 15u) % kFusedQueues;
+    int item = -1, qsel = 0;
+    for (int i = 0; i < kFusedQueues && item < 0; ++i) {
+      const int qx = (xcd + i) % kFusedQueues;
+      const int n = (queue_lo(qx + 1) - queue_lo(qx)) * a.nr;
+      if (n == 0 || (int)__hip_atomic_load(a.sync + qx, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT) >= n)
+        continue;
+      const int t =
+          (int)__hip_atomic_fetch_add(a.sync + qx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (t < n) {
+        item = t;
+        qsel = qx;
+      }
+    }
+    s_misc[0] = (uint32_t)item;
+    s_misc[2] = (uint32_t)qsel;
+  }
   __syncthreads();
-  const int ticket = (int)s_misc[0];
-  const int r = ticket / a.U, u = ticket % a.U;
+  const int item = (int)s_misc[0];
+  if (item < 0) return;
+  const int qlo = queue_lo((int)s_misc[2]);
+  const int qn = queue_lo((int)s_misc[2] + 1) - qlo;
+  const int r = item / qn, u = qlo + item % qn;
   const int h = u / a.PS, p0 = (u % a.PS) * 64;
   const int grp = h / g.hpg;
   const int pw = min(64, g.P - p0);
@@ -443,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (tid == 0)
-      __hip_atomic_store(a.sync + 2 + r * a.U + u, reset ? kFlagReset : kFlagAgg,
+      __hip_atomic_store(a.sync + kFusedSyncHeader + r * a.U + u, reset ? kFlagReset : kFlagAgg,
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
@@ -474,7 +506,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     int next = f0 / a.R, spins = 0;
     while (next < r) {
       const int rr = next + lane;
-      const uint32_t f = rr < r ? __hip_atomic_load(a.sync + 2 + rr * a.U + u, __ATOMIC_RELAXED,
+      const uint32_t f = rr < r ? __hip_atomic_load(a.sync + kFusedSyncHeader + rr * a.U + u, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT)
                                 : 1u;
       const uint64_t waiting = ~__ballot(f != 0u);
@@ -482,7 +514,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       if (n == 0) {
         if (++spins > kSpinLimit) {
           if (lane == 0)
-            __hip_atomic_fetch_or(a.sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(a.sync + kFusedQueues, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           break;
         }
         __builtin_amdgcn_s_sleep(2);
@@ -788,7 +820,7 @@ FusedPlan fused_plan(int64_t K, int H, int P, int N) {
 hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s) {
   const Geo& g = f.g;
   const FusedPlan& pl = f.plan;
-  const int nsync = 2 + pl.nr * pl.U;
+  const int nsync = kFusedSyncHeader + pl.nr * pl.U;
   const int nflag_blocks = min((nsync + 255) / 256, 64);
   const int nfinal = f.hfinal ? g.nseq : 0;
   hipLaunchKernelGGL(k_fused_prep, dim3(1 + nflag_blocks + nfinal), dim3(256), 0, s, g, f.cu,
@@ -802,7 +834,7 @@ hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s) {
   a.A = f.A; a.dt_bias = f.dt_bias; a.D = f.D; a.h0 = f.h0; a.hfinal = f.hfinal;
   a.softplus = f.softplus; a.clamp = f.clamp; a.dt_min = f.dt_min; a.dt_max = f.dt_max;
   a.input_dt = f.input_dt;
-  a.U = pl.U; a.PS = pl.PS; a.R = pl.R;
+  a.U = pl.U; a.PS = pl.PS; a.R = pl.R; a.nr = pl.nr;
   a.sync = f.sync; a.edec = f.edec; a.agg = f.agg;
   const dim3 grid((unsigned)(pl.nr * pl.U));
   const bool ob = f.out_dtype == DT_BF16, db = f.dt_dtype == DT_BF16;

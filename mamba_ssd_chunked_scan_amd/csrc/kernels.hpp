@@ -46,6 +46,9 @@ hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int 
 // ---- fused forward (fused_fwd.hip)
 constexpr int kFusedChunk = 128;             // internal chunk length of the fused pass
 constexpr int kFusedTargetWorkgroups = 512;  // (unit, range) workgroups aimed for
+constexpr int kFusedQueues = 8;              // work queues of the fused pass, one per XCD
+// synchronisation words before the flags: the queue counters, then the error bits
+constexpr int kFusedSyncHeader = kFusedQueues + 1;
 
 // Work decomposition of the fused pass: P slabs of 64 rows per head, units =
 // heads x slabs, n-tiles of the d_state capacity, chunks per range, ranges.
@@ -68,7 +71,7 @@ struct FusedLaunch {
   int softplus, clamp, input_dt;
   float dt_min, dt_max;
   FusedPlan plan;
-  uint32_t* sync;          // 2 + nr * U words
+  uint32_t* sync;          // kFusedSyncHeader + nr * U words
   float* edec;             // nr * U
   float* agg;              // nr * U * 64 * 16 * NT
 };
