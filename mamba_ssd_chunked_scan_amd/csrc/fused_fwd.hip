@@ -609,6 +609,11 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     for (int ui = 0; ui < 2; ++ui)
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[ui][pt] = zero4();
+    // The matrix phases (B and D) run at raised wave priority: the SIMD's
+    // other wave, from another workgroup, is then more often in its VALU,
+    // LDS or load phases while this one keeps the matrix unit fed (measured
+    // 2.5% faster at the Nemotron-Nano size).
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       FragBF cf0, cf1;
@@ -635,6 +640,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
         for (int pt = 0; pt < 4; ++pt) acc[ui][pt][i] *= ex;
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // the carry-in rows are dead: the B tile takes their space
 
     // ---- C
@@ -658,6 +664,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     const float e = fast_exp2(__uint_as_float(s_misc[1]));
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) carry[nt] *= e;
+    __builtin_amdgcn_s_setprio(1);
     state_mma(carry);
     if (j == lj - 1 && a.hfinal && p_ok) {
 #pragma unroll
@@ -722,6 +729,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     // A sequence that starts at the next chunk starts from its initial
     // state (carry is dead here: its final state was stored above).  Issued
     // before the C fragments, so that waiting for it does not wait for them.
+    __builtin_amdgcn_s_setprio(0);
     if (more && fn == j + 1) load_h0(carry, cn.seq);
     load_cfr(cn);  // unconditional, as in pass 1
     __syncthreads();  // the B tile is dead: its space takes y
