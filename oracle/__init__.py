@@ -27,6 +27,10 @@ Contents
                             recurrence's state at the chunk boundary).
 * ``state_passing``      -- the chunk-level recurrence applied to given chunk
                             states, SSD Reference "Inter-chunk propagation".
+* ``ssd_fwd_stored_states`` -- the chunked forward with its per-chunk states
+                            stored in a narrower type (bf16), rounded where they
+                            are stored (vLLM PR 27299 "Purpose": the state dtype).
+* ``round_to_bf16``      -- round to the nearest bfloat16, ties to even.
 * ``ssd_complex_fwd``    -- the fp64 sequential recurrence with a complex
                             per-head A (``ssd_ref_complex.c``), SSD Reference
                             "Math" with "_discretise" exp(softplus(dt) A).
@@ -452,6 +456,83 @@ def state_passing(S, cs, meta: ChunkMeta, initial_states=None):
             cur = np.exp(lam)[:, None, None] * cur + S[j]
         final[i] = cur
     return Hin, final
+
+
+def round_to_bf16(a):
+    """Round to the nearest bfloat16 value, ties to even, returned as fp64.
+
+    The value is first rounded to the nearest float32 (numpy's conversion), then
+    its 16 low bits are rounded off: add 0x7FFF plus the lowest kept bit, clear
+    the low half.  Infinities and NaN are passed through unchanged.
+    """
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    keep = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + keep) & np.uint64(0xFFFF0000)).astype(np.uint32)
+    out = r.view(np.float32).astype(np.float64)
+    special = ~np.isfinite(f)
+    out[special] = f[special]
+    return out
+
+
+def ssd_fwd_stored_states(x, B, C, dt, A, dt_bias=None, D=None, z=None,
+                          initial_states=None, cu_seqlens=None, chunk_size=128,
+                          dt_softplus=True, dt_limit=None, input_dt=False,
+                          state_dtype="bf16", threads=None) -> FwdResult:
+    """The chunked forward with its per-chunk states stored in ``state_dtype``.
+
+    vLLM PR 27299 ("Purpose") names the state dtype as an axis of the SSD
+    stages: the states the chunk-state stage writes and the state-passing
+    stage reads and writes are held in that type.  With a narrow type the
+    result is no longer the plain recurrence's, so this follows the chunked
+    algorithm's steps (SSD Reference, "Intra-chunk outputs and per-chunk
+    states", "Inter-chunk propagation", "Readout") and rounds exactly where a
+    value is stored:
+      1. every chunk's end state from a zero start, S_j (fp64), stored rounded;
+      2. the inter-chunk recurrence Hin[j+1] = exp(Lambda_j) Hin[j] + S_j over
+         the stored S_j, carried in full precision (a register value); each
+         carry-in Hin[j] is stored rounded; the final state is the carried
+         value, not rounded (final states are float32 outputs);
+      3. every chunk's outputs from its stored carry-in: the recurrence run on
+         the chunk alone from that state (= the intra-chunk part plus the
+         readout of the carried state, by linearity).
+    ``state_dtype`` is "bf16" (round to nearest even) or "f32" (round to the
+    nearest float32).  Arguments and layouts as ``ssd_fwd``.
+    """
+    if state_dtype == "bf16":
+        rnd = round_to_bf16
+    elif state_dtype == "f32":
+        rnd = lambda a: np.asarray(a, dtype=np.float64).astype(np.float32).astype(np.float64)
+    else:
+        raise ValueError(f"state_dtype {state_dtype!r}")
+    x = _f64(x)
+    if cu_seqlens is None:
+        b, T = x.shape[0], x.shape[1]
+        cu = np.arange(b + 1, dtype=np.int64) * T
+        lead = 2
+    else:
+        cu = np.asarray(cu_seqlens, dtype=np.int64)
+        lead = 1
+    xs, Bs, Cs = _packed(x, lead), _packed(_f64(B), lead), _packed(_f64(C), lead)
+    dts = _packed(_f64(dt), lead)
+    zs = _packed(_f64(z), lead) if z is not None else None
+    meta = varlen_chunk_meta(cu, chunk_size)
+    S = chunk_states(xs, Bs, dts, A, meta, dt_bias=dt_bias, dt_softplus=dt_softplus,
+                     dt_limit=dt_limit, threads=threads, input_dt=input_dt)
+    cs = chunk_cumsum(dts, A, meta, chunk_size, dt_bias=dt_bias, dt_softplus=dt_softplus,
+                      dt_limit=dt_limit)
+    Hin, final = state_passing(rnd(S), cs, meta, initial_states)
+    H, P = xs.shape[1], xs.shape[2]
+    y = np.zeros((xs.shape[0], H, P))
+    if meta.nchunks:
+        cut = _chunk_cut(meta)
+        lo, hi = int(cut[0]), int(cut[-1])
+        r = ssd_fwd(xs[lo:hi], Bs[lo:hi], Cs[lo:hi], dts[lo:hi], A, dt_bias=dt_bias, D=D,
+                    z=None if zs is None else zs[lo:hi], initial_states=rnd(Hin),
+                    cu_seqlens=cut - lo, dt_softplus=dt_softplus, dt_limit=dt_limit,
+                    threads=threads, input_dt=input_dt)
+        y[lo:hi] = r.y
+    return FwdResult(y.reshape(x.shape), final, None)
 
 
 # --------------------------------------------------------------------------

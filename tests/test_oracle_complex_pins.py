@@ -11,11 +11,11 @@ than itself.
   y_t = e^{i phi_t} sum_{s<=t} e^{-i phi_s} x_s with phi = w cumsum(delta).
 * The recurrence is holomorphic in its inputs (no conjugation anywhere), so
   conjugating x, B, C and A conjugates y.
-* The pages' own chunkwise algorithm (SSD Reference: padding rule, A_cumsum,
-  L = exp(segsum) masked, Y_diag, states, decay_chunk[z, c] =
-  exp(CD[z-1] - CD[c]) 1[z > c], the init term exp(CD[z-1]) H_{-1}, Y_off),
-  written out here with numpy, agrees with it for time-varying dt, a ragged
-  last chunk and an initial state in the (D, N) layout.
+* A chunked evaluation worked out here chunk by chunk (SSD Reference: the
+  within-chunk cumulative log-decay, the intra-chunk outputs and chunk end
+  states, the inter-chunk window exp(CD[z-1] - CD[c]) with the init term
+  exp(CD[z-1]) H_{-1}, the readout) agrees with it for time-varying dt, a
+  ragged last chunk and an initial state in the (D, N) layout.
 * Split and resume, and packed sequences run one by one, agree bit for bit.
 """
 import numpy as np
@@ -108,43 +108,71 @@ def test_conjugation_symmetry():
     assert rel(c.final_states, a.final_states.conj()) < 1e-14
 
 
-def pages_chunkwise(x, B, C, dt, A, chunk, initial_states=None, window_off_by_one=False):
-    """The chunkwise evaluation the SSD Reference page describes, in numpy."""
-    b, T, H, D = x.shape
+def chunkwise_eval(x, B, C, dt, A, chunk, initial_states=None, window_shift=1):
+    """A chunked evaluation of the complex recurrence, chunk by chunk.
+
+    x (b, T, H, D), B and C (b, T, H, N) complex, dt (b, T, H) real, A (H)
+    complex.  Each chunk of ``chunk`` tokens (the last one shorter) with
+    per-token complex log-decays a_t = softplus(dt_t) A_h:
+      * cs[l] = a_0 + ... + a_l (SSD Reference, "Chunking and the discretized
+        log-decay");
+      * intra-chunk output y_l = sum_{s<=l} exp(cs[l] - cs[s]) (C_l . B_s) x_s
+        and the end state from zero S = sum_s exp(cs[L-1] - cs[s]) x_s (outer) B_s
+        in the (D, N) layout ("Intra-chunk outputs and per-chunk states");
+      * the state entering chunk z, sum_{c<z} exp(CD[z-1] - CD[c]) S_c plus
+        exp(CD[z-1]) H_-1, CD the running sum of the chunks' total log-decays,
+        CD[-1] = 0 ("Inter-chunk propagation"); ``window_shift=0`` uses the
+        off-by-one window CD[z] - CD[c] instead;
+      * the readout y_l += exp(cs[l]) sum_n C_l[n] Hin[:, n] ("Readout").
+    Nothing is conjugated.  Returns y (b, T, H, D) complex.
+    """
+    b, T, H, Dm = x.shape
     N = B.shape[-1]
-    pad = (chunk - T % chunk) % chunk
-    padt = lambda a: np.concatenate([a, np.zeros((b, pad) + a.shape[2:], dtype=a.dtype)], 1)
-    x, B, C, dt = padt(x), padt(B), padt(C), padt(dt)
-    nc = (T + pad) // chunk
-    A_log = softplus(dt) * A[None, None, :]
-    ch = lambda a: a.reshape((b, nc, chunk) + a.shape[2:])
-    Xc, Bc, Cc, Ac = ch(x), ch(B), ch(C), ch(A_log)
-    A_cumsum = np.cumsum(Ac, axis=2)                                   # (b, c, l, h)
-    decay_states = np.exp(A_cumsum[:, :, -1:, :] - A_cumsum)
-    seg = A_cumsum[:, :, :, None, :] - A_cumsum[:, :, None, :, :]     # (b, c, l, s, h)
-    mask = np.tril(np.ones((chunk, chunk), dtype=bool))[None, None, :, :, None]
-    L = np.where(mask, np.exp(np.where(mask, seg, 0.0)), 0.0)
-    Y_diag = np.einsum("bclhn,bcshn,bclsh,bcshp->bclhp", Cc, Bc, L, Xc)
-    states = np.einsum("bclhn,bclh,bclhp->bchpn", Bc, decay_states, Xc)  # (b, c, h, D, N)
-    lam = A_cumsum[:, :, -1, :]                                        # (b, c, h)
-    CD = np.cumsum(lam, axis=1)
-    CDm1 = np.concatenate([np.zeros_like(CD[:, :1]), CD[:, :-1]], 1)   # CD[z-1], CD[-1] = 0
-    Gz = np.zeros((b, nc, H, D, N), dtype=np.complex128)
-    for z in range(nc):
-        for c in range(z):
-            top = CD[:, z] if window_off_by_one else CDm1[:, z]
-            Gz[:, z] += np.exp(top - CD[:, c])[:, :, None, None] * states[:, c]
-        if initial_states is not None:
-            Gz[:, z] += np.exp(CDm1[:, z])[:, :, None, None] * initial_states
-    Y_off = np.einsum("bclhn,bchpn,bclh->bclhp", Cc, Gz, np.exp(A_cumsum))
-    return (Y_diag + Y_off).reshape(b, nc * chunk, H, D)[:, :T]
+    starts = list(range(0, T, chunk))
+    nc = len(starts)
+    y = np.zeros((b, T, H, Dm), dtype=np.complex128)
+    for bi in range(b):
+        a = softplus(dt[bi]) * A[None, :]                        # (T, H) complex
+        S = np.zeros((nc, H, Dm, N), dtype=np.complex128)
+        lam = np.zeros((nc, H), dtype=np.complex128)
+        css = []
+        for c, t0 in enumerate(starts):
+            L = min(chunk, T - t0)
+            cs = np.cumsum(a[t0:t0 + L], axis=0)
+            css.append(cs)
+            lam[c] = cs[L - 1]
+            for h in range(H):
+                xh, Bh, Ch = x[bi, t0:t0 + L, h], B[bi, t0:t0 + L, h], C[bi, t0:t0 + L, h]
+                for l in range(L):
+                    for s_ in range(l + 1):
+                        y[bi, t0 + l, h] += (np.exp(cs[l, h] - cs[s_, h])
+                                             * np.sum(Ch[l] * Bh[s_]) * xh[s_])
+                for s_ in range(L):
+                    S[c, h] += np.exp(cs[L - 1, h] - cs[s_, h]) * np.outer(xh[s_], Bh[s_])
+        CD = np.cumsum(lam, axis=0)
+        for zc in range(nc):
+            if window_shift:
+                top = CD[zc - 1] if zc > 0 else np.zeros(H, dtype=np.complex128)
+            else:
+                top = CD[zc]
+            Hin = np.zeros((H, Dm, N), dtype=np.complex128)
+            for c in range(zc):
+                Hin += np.exp(top - CD[c])[:, None, None] * S[c]
+            if initial_states is not None:
+                Hin += np.exp(top)[:, None, None] * initial_states[bi]
+            t0 = starts[zc]
+            cs = css[zc]
+            for l in range(cs.shape[0]):
+                for h in range(H):
+                    y[bi, t0 + l, h] += np.exp(cs[l, h]) * (Hin[h] @ C[bi, t0 + l, h])
+    return y
 
 
 @pytest.mark.parametrize("T,chunk", [(16, 4), (23, 4), (20, 8), (5, 8)])
-def test_matches_pages_chunkwise_algorithm(T, chunk):
+def test_matches_chunkwise_evaluation(T, chunk):
     x, B, C, dt, A, h0 = problem(5, T=T, h0=True)
     r = oracle.ssd_complex_fwd(x, B, C, dt, A, initial_states=h0)
-    ref = pages_chunkwise(x, B, C, dt, A, chunk, initial_states=h0)
+    ref = chunkwise_eval(x, B, C, dt, A, chunk, initial_states=h0)
     assert rel(r.y, ref) < 1e-11
     assert rel(r.y.real, ref.real) < 1e-11
 
@@ -154,8 +182,8 @@ def test_propagation_window_matters():
     # different function for time-varying dt, and the oracle is not it
     x, B, C, dt, A, _ = problem(6, T=16)
     r = oracle.ssd_complex_fwd(x, B, C, dt, A)
-    assert rel(r.y, pages_chunkwise(x, B, C, dt, A, 4)) < 1e-11
-    wrong = pages_chunkwise(x, B, C, dt, A, 4, window_off_by_one=True)
+    assert rel(r.y, chunkwise_eval(x, B, C, dt, A, 4)) < 1e-11
+    wrong = chunkwise_eval(x, B, C, dt, A, 4, window_shift=0)
     assert rel(wrong, r.y) > 1e-3
 
 

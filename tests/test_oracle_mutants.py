@@ -84,11 +84,26 @@ COMPLEX_MUTANTS = {
         "const double* src = h0 + ((((size_t)i * H + h) * N + n) * D + d) * 2;"),
 }
 
+# slips in the stored-state forward (oracle/__init__.py), caught by
+# tests/test_oracle_state_dtype_pins.py
+STATE_MUTANTS = {
+    "stored_chunk_states_not_rounded": (
+        "Hin, final = state_passing(rnd(S), cs, meta, initial_states)",
+        "Hin, final = state_passing(S, cs, meta, initial_states)"),
+    "stored_carry_in_not_rounded": ("initial_states=rnd(Hin),", "initial_states=Hin,"),
+    "final_state_rounded": ("return FwdResult(y.reshape(x.shape), final, None)",
+                            "return FwdResult(y.reshape(x.shape), rnd(final), None)"),
+    "bf16_truncated": ("r = ((u + np.uint64(0x7FFF) + keep)", "r = ((u)"),
+    "bf16_ties_away": ("r = ((u + np.uint64(0x7FFF) + keep)", "r = ((u + np.uint64(0x8000))"),
+}
+
 CASES = [(n, MUTANTS[n], "tests/test_oracle_pins.py", "ssd_ref.c") for n in sorted(MUTANTS)] + \
         [(n, BWD_MUTANTS[n], "tests/test_oracle_bwd_pins.py", "ssd_ref.c")
          for n in sorted(BWD_MUTANTS)] + \
         [(n, COMPLEX_MUTANTS[n], "tests/test_oracle_complex_pins.py", "ssd_ref_complex.c")
-         for n in sorted(COMPLEX_MUTANTS)]
+         for n in sorted(COMPLEX_MUTANTS)] + \
+        [(n, STATE_MUTANTS[n], "tests/test_oracle_state_dtype_pins.py", "__init__.py")
+         for n in sorted(STATE_MUTANTS)]
 
 
 @pytest.mark.slow

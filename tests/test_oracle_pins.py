@@ -3,8 +3,10 @@
 Each test ties the oracle to something the pages or the mathematics fix:
 a hand-derived example, the closed form of the recurrence, special cases
 that reduce to library routines, invariants (split/resume, packing, group
-expansion, linearity, causality), and the pages' own chunkwise
-decomposition written out here independently with numpy.
+expansion, linearity, causality), and a chunked evaluation worked out
+here from the recurrence chunk by chunk (the pages' chunkwise decomposition:
+intra-chunk outputs, chunk end states, the decay_chunk window of the
+inter-chunk propagation, the readout).
 
 A plausible slip in the oracle -- a dropped term, a sign, an index off by
 one, transposed operands, the decay applied after instead of before the
@@ -344,54 +346,78 @@ def test_linearity_and_causality():
 
 # ---------------------------------------------------------------- chunkwise decomposition
 
-def chunkwise_from_pages(x, B, C, dt, A, dt_bias, D, z, h0, Cs):
-    """The SSD Reference's chunkwise algorithm, written out with numpy, real A.
+def chunkwise_eval(x, B, C, dt, A, dt_bias, D, z, h0, Cs, window_shift=1):
+    """A chunked evaluation of the recurrence, worked out from it chunk by chunk.
 
-    Sections "Chunking and the discretized log-decay" (A_cumsum, decay_states),
-    "Intra-chunk outputs and per-chunk states" (L, Y_diag, states),
-    "Inter-chunk propagation" (decay_chunk[z,c] = exp(CD[z-1] - CD[c]) 1[z>c]
-    and the init term exp(CD[z-1]) H_-1), "Readout" (Y_off, Y = Y_diag + Y_off),
-    for one batch row, right-padding T to a multiple of the chunk size with
-    a = 0 and x = 0.  Groups expand to heads; the skip and gate come last.
+    For one batch row, real A, groups mapped to heads as g = h // (H/G).  The
+    token axis is cut into chunks of Cs tokens (the last one shorter).  Inside
+    chunk c with local positions 0..L-1 and per-head log-decays a_t:
+      * cs[l] = a_0 + ... + a_l, the chunk's cumulative log-decay (SSD
+        Reference, "Chunking and the discretized log-decay");
+      * the intra-chunk output y_l += sum_{s<=l} exp(cs[l] - cs[s]) (C_l.B_s) x_s,
+        and the chunk's end state from a zero start
+        S_c = sum_s exp(cs[L-1] - cs[s]) x_s (outer) B_s ("Intra-chunk outputs
+        and per-chunk states"); the exponent is selected before it is taken,
+        so masked pairs never reach exp;
+      * the state entering chunk z is the sum over earlier chunks c of
+        exp(CD[z-1] - CD[c]) S_c plus exp(CD[z-1]) h0, CD being the running
+        sum of the chunks' total log-decays and CD[-1] = 0 ("Inter-chunk
+        propagation", the decay_chunk window); ``window_shift=0`` evaluates
+        the off-by-one window CD[z] - CD[c] the page warns about instead;
+      * the readout y_l += exp(cs[l]) C_l . Hin_z ("Readout").
+    The skip D x and the gate silu(z) are applied last.  Returns
+    (y, final state, chunk end states, carry-in states).
     """
     T, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
     hpg = H // G
-    nc = -(-T // Cs)
-    pad = nc * Cs - T
-    a = plain_softplus(dt + dt_bias[None]) * A[None]
-    padt = lambda v: np.concatenate([v, np.zeros((pad,) + v.shape[1:])], 0)
-    Xc = padt(x).reshape(nc, Cs, H, P)
-    Bh = np.repeat(B, hpg, axis=1); Ch = np.repeat(C, hpg, axis=1)
-    Bc = padt(Bh).reshape(nc, Cs, H, N); Cc = padt(Ch).reshape(nc, Cs, H, N)
-    Ac = padt(a).reshape(nc, Cs, H)
-    Acs = np.cumsum(Ac, axis=1)                                     # (nc, Cs, H)
-    decay_states = np.exp(Acs[:, -1:, :] - Acs)
-    seg = Acs[:, :, None, :] - Acs[:, None, :, :]                   # (nc, l, s, H)
-    mask = np.tril(np.ones((Cs, Cs), dtype=bool))[None, :, :, None]
-    L = np.where(mask, np.exp(np.where(mask, seg, 0.0)), 0.0)
-    Y_diag = np.einsum("clhn,cshn,clsh,cshp->clhp", Cc, Bc, L, Xc)
-    states = np.einsum("clhn,clh,clhp->chpn", Bc, decay_states, Xc)
-    Lam = Acs[:, -1, :]                                             # (nc, H)
-    CD = np.cumsum(Lam, axis=0)
-    CDm1 = np.concatenate([np.zeros((1, H)), CD[:-1]], 0)          # CD[z-1], CD[-1] = 0
-    dc = np.exp(CDm1[:, None, :] - CD[None, :, :])                  # (z, c, H)
-    dc = dc * (np.arange(nc)[:, None] > np.arange(nc)[None, :])[:, :, None]
-    carry = np.einsum("zch,chpn->zhpn", dc, states)
-    if h0 is not None:
-        carry = carry + np.exp(CDm1)[:, :, None, None] * h0[None]
-    Y_off = np.einsum("clhn,chpn,clh->clhp", Cc, carry, np.exp(Acs))
-    Y = (Y_diag + Y_off).reshape(nc * Cs, H, P)[:T]
+    starts = list(range(0, T, Cs))
+    nc = len(starts)
+    a = plain_softplus(dt + dt_bias[None]) * A[None]          # (T, H)
+    y = np.zeros((T, H, P))
+    S = np.zeros((nc, H, P, N))
+    lam = np.zeros((nc, H))
+    css = []
+    for c, t0 in enumerate(starts):
+        L = min(Cs, T - t0)
+        cs = np.zeros((L, H))
+        run = np.zeros(H)
+        for l in range(L):
+            run = run + a[t0 + l]
+            cs[l] = run
+        css.append(cs)
+        lam[c] = cs[L - 1]
+        for h in range(H):
+            g = h // hpg
+            Cg, Bg, xh = C[t0:t0 + L, g], B[t0:t0 + L, g], x[t0:t0 + L, h]
+            for l in range(L):
+                for s_ in range(l + 1):
+                    y[t0 + l, h] += np.exp(cs[l, h] - cs[s_, h]) * np.dot(Cg[l], Bg[s_]) * xh[s_]
+            for s_ in range(L):
+                S[c, h] += np.exp(cs[L - 1, h] - cs[s_, h]) * np.outer(xh[s_], Bg[s_])
+    CD = np.cumsum(lam, axis=0)                               # (nc, H)
+    Hin = np.zeros((nc, H, P, N))
+    for zc in range(nc):
+        top = CD[zc - 1] if (window_shift and zc > 0) else (np.zeros(H) if window_shift else CD[zc])
+        for c in range(zc):
+            Hin[zc] += np.exp(top - CD[c])[:, None, None] * S[c]
+        if h0 is not None:
+            Hin[zc] += np.exp(top)[:, None, None] * h0
+    for c, t0 in enumerate(starts):
+        cs = css[c]
+        for l in range(cs.shape[0]):
+            for h in range(H):
+                y[t0 + l, h] += np.exp(cs[l, h]) * (Hin[c, h] @ C[t0 + l, h // hpg])
     if D is not None:
-        Y = Y + D[None, :, None] * x
+        y = y + D[None, :, None] * x
     if z is not None:
-        Y = Y * z / (1.0 + np.exp(-z))
-    final = np.exp(Lam[-1])[:, None, None] * carry[-1] + states[-1]
-    return Y, final, states, carry
+        y = y * z / (1.0 + np.exp(-z))
+    final = np.exp(lam[-1])[:, None, None] * Hin[-1] + S[-1]
+    return y, final, S, Hin
 
 
 @pytest.mark.parametrize("T,Cs", [(64, 16), (61, 16), (16, 16), (5, 16), (47, 8)])
-def test_oracle_matches_pages_chunkwise_algorithm(T, Cs):
+def test_oracle_matches_chunkwise_evaluation(T, Cs):
     rng = np.random.default_rng(20 + T)
     H, P, N, G = 4, 3, 5, 2
     x = rng.standard_normal((T, H, P)); B = rng.standard_normal((T, G, N))
@@ -401,7 +427,7 @@ def test_oracle_matches_pages_chunkwise_algorithm(T, Cs):
     h0 = rng.standard_normal((1, H, P, N))
     r = oracle.ssd_fwd(x[None], B[None], C[None], dt[None], A, bias, D, z[None], h0,
                        chunk_size=Cs)
-    Y, final, states, carry = chunkwise_from_pages(x, B, C, dt, A, bias, D, z, h0[0], Cs)
+    Y, final, states, carry = chunkwise_eval(x, B, C, dt, A, bias, D, z, h0[0], Cs)
     assert rel(r.y[0], Y) < 1e-12
     assert rel(r.final_states[0], final) < 1e-12
     # the oracle's stage helpers agree with the pages' per-chunk quantities
@@ -453,7 +479,12 @@ def test_wrong_propagation_window_is_detected():
     Hin = oracle.carry_in_states(oracle.ssd_fwd(x[None], B[None], C[None], dt[None], A, bias,
                                                 chunk_size=Cs).chunk_end_states, meta)
     assert rel(wrong, Hin) > 1e-3
-    del r
+    # the chunked evaluation with that window is a different function, and
+    # the oracle is not it (while the correct window matches, above)
+    yw = chunkwise_eval(x, B, C, dt, A, bias, None, None, None, Cs, window_shift=0)[0]
+    assert rel(yw, r.y[0]) > 1e-3
+    yr = chunkwise_eval(x, B, C, dt, A, bias, None, None, None, Cs)[0]
+    assert rel(yr, r.y[0]) < 1e-12
 
 
 def test_state_passing_packed_with_empty_sequence():
@@ -472,3 +503,39 @@ def test_state_passing_packed_with_empty_sequence():
     assert rel(Hin, oracle.carry_in_states(r.chunk_end_states, meta, h0)) < 1e-12
     assert rel(fin, r.final_states) < 1e-12
     assert np.array_equal(fin[1], h0[1])
+
+
+# ---------------------------------------------------------------- the step-size clamp (numpy helpers)
+
+def test_numpy_clamp_pinned_to_constant_step_and_to_the_c_oracle():
+    # oracle.step_size / oracle.chunk_cumsum (numpy) are the references of the
+    # GPU's chunk cumsum; their clamp is tied here to a closed form and to the
+    # C oracle's clamp.
+    rng = np.random.default_rng(51)
+    T, H, Cs = 45, 3, 16
+    dt = rng.standard_normal((T, H)) * 3.0
+    bias = rng.uniform(-2, 1, H)
+    A = -np.exp(rng.uniform(-1, 1, H))
+    meta = oracle.batch_chunk_meta(1, T, Cs)
+    # a degenerate limit [d, d] makes every step d: the cumsum is l * d * A
+    d = 0.0375
+    cs = oracle.chunk_cumsum(dt, A, meta, Cs, dt_bias=bias, dt_limit=(d, d))
+    for j in range(meta.nchunks):
+        L = meta.length[j]
+        ref = np.outer(A, np.arange(1, Cs + 1).clip(max=L)) * d
+        np.testing.assert_allclose(cs[j], ref, rtol=1e-13, atol=0)
+    # the clamp bounds the softplus value from both sides and leaves the rest
+    lo, hi = 0.3, 1.1
+    sp = plain_softplus(dt + bias)
+    st = oracle.step_size(dt, bias, dt_limit=(lo, hi))
+    assert np.max(np.abs(st - np.clip(sp, lo, hi))) < 1e-15
+    assert np.any(sp < lo) and np.any(sp > hi) and np.any((sp > lo) & (sp < hi))
+    # the C oracle with its clamp equals the C oracle fed the numpy steps
+    # directly (no softplus, no bias)
+    P, N = 2, 3
+    x = rng.standard_normal((1, T, H, P)); B = rng.standard_normal((1, T, 1, N))
+    C = rng.standard_normal((1, T, 1, N))
+    rc = oracle.ssd_fwd(x, B, C, dt[None], A, dt_bias=bias, dt_limit=(lo, hi))
+    rn = oracle.ssd_fwd(x, B, C, st[None], A, dt_softplus=False)
+    assert rel(rc.y, rn.y) < 1e-13
+    assert rel(rc.final_states, rn.final_states) < 1e-13
