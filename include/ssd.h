@@ -53,8 +53,11 @@
  *   so a call that returns an error has launched nothing (except SSD_ERR_HIP,
  *   returned when a launch itself fails).  ssd_last_error_message() names the
  *   offending argument (thread-local).
- * - Determinism: no atomics in the forward or backward pass; results are
- *   bitwise identical run to run.
+ * - Determinism: results are bitwise identical run to run.  The staged
+ *   forward, the backward, the complex-A and the norm calls use no atomics.
+ *   The fused forward uses atomics only to schedule and hand off work (queue
+ *   tickets, ready flags, an error word); the values it sums are folded in a
+ *   fixed order that never depends on timing.
  */
 #ifndef LIBSSD_SSD_H
 #define LIBSSD_SSD_H
@@ -269,7 +272,9 @@ typedef struct ssd_fwd_args {
  * intermediates), preceded by a small reset kernel; it always works on
  * 128-token chunks (the result does not depend on the chunk length), takes
  * bf16 x, B, C (and z) and dstate <= 128, and returns SSD_ERR_UNSUPPORTED
- * otherwise; with input_dt it also needs delta > 0 by construction (softplus,
+ * otherwise; it stores no per-chunk states (the carried state stays in
+ * float32 registers and hand-off buffers), so p->state_dtype does not apply
+ * to it; with input_dt it also needs delta > 0 by construction (softplus,
  * or a clamp with dt_min >= 0), since it folds log2(delta) into the decay
  * exponent.  initial_states and final_states must be 16-byte aligned for
  * it.  Its results are bit-identical run to run for a given problem shape;
@@ -278,9 +283,35 @@ typedef struct ssd_fwd_args {
  * In packed mode the chunk table is built inside the workspace.  workspace:
  * device memory of at least ssd_workspace_size(p, algo) bytes, 256-byte
  * aligned, owned by the caller, contents need not be initialised; it must not
- * be shared by calls that overlap in time. */
+ * be shared by calls that overlap in time.  The fused path's waits for
+ * another workgroup's state are bounded: one that gives up sets bit 0
+ * (SSD_STATUS_LOOKBACK_TIMEOUT) of the workspace's error word and writes NaN
+ * to every output and final state that depends on the missing state (the
+ * SSD Reference's contract: named failures, nothing degrades silently); read
+ * the word with ssd_forward_status. */
 ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* a,
                        void* workspace, size_t ws_bytes, hipStream_t stream);
+
+#define SSD_STATUS_LOOKBACK_TIMEOUT 1u
+
+/* Device-side status of the last ssd_forward that used `workspace` (same
+ * problem and algo): enqueues on `stream` a write of its error word to
+ * *status (device memory, or host memory the device can write), after
+ * whatever precedes it on the stream.  0 = no error; SSD_ALGO_STAGED always
+ * writes 0.  Graph-capturable (a one-thread kernel, no copy or fill). */
+ssd_status ssd_forward_status(const ssd_problem* p, ssd_algo algo, const void* workspace,
+                              size_t ws_bytes, uint32_t* status, hipStream_t stream);
+
+/* Failure-path test hook for the fused forward, not for production use: the
+ * same call as ssd_forward(p, SSD_ALGO_FUSED, ...) with the bound of every
+ * look-back wait set to spin_limit polls (>= 1) and, when publish_flags == 0,
+ * no ready flag ever raised, so every wait that needs another workgroup's
+ * state gives up after spin_limit polls.  Every kernel still exits normally;
+ * the test then reads SSD_STATUS_LOOKBACK_TIMEOUT and the NaN outputs. */
+ssd_status ssd_forward_fused_lookback_test(const ssd_problem* p, const ssd_fwd_args* a,
+                                           void* workspace, size_t ws_bytes,
+                                           int32_t spin_limit, int32_t publish_flags,
+                                           hipStream_t stream);
 
 /* ---------------------------------------------------------------- backward */
 

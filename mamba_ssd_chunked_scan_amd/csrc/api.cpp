@@ -236,7 +236,8 @@ ssd_status check_state_ptr(const float* ptr, const char* name) {
 // The single-pass forward (SSD_ALGO_FUSED); arguments common to both paths
 // were validated by ssd_forward.
 ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* workspace,
-                         size_t ws_bytes, hipStream_t stream) {
+                         size_t ws_bytes, hipStream_t stream, int spin_limit = 0,
+                         int publish_flags = 1) {
   if (has_tokens(p) && a->x.dtype != SSD_BF16)
     return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED takes bf16 x, B, C (use SSD_ALGO_STAGED)");
   if (p->dstate > 128)
@@ -274,6 +275,8 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
   f.sync = reinterpret_cast<uint32_t*>(ws + w.sync);
   f.edec = reinterpret_cast<float*>(ws + w.edec);
   f.agg = reinterpret_cast<float*>(ws + w.agg);
+  f.spin_limit = spin_limit;
+  f.publish_flags = publish_flags;
   SSD_HIP(ssd::launch_fused_fwd(f, stream), "fused forward launch");
   return ok();
 }
@@ -459,6 +462,23 @@ ssd_status check_grad_tensor(const ssd_tensor& t, const char* name, bool require
   return SSD_OK;
 }
 
+// Arguments common to both forward paths.
+ssd_status check_fwd_args(const ssd_problem* p, const ssd_fwd_args* a) {
+  SSD_TRY(check_problem(p));
+  if (!a) return fail(SSD_ERR_NULL, "args is NULL");
+  SSD_TRY(check_vec_tensor(a->x, "x", has_tokens(p)));
+  SSD_TRY(check_vec_tensor(a->B, "B", has_tokens(p)));
+  SSD_TRY(check_vec_tensor(a->C, "C", has_tokens(p)));
+  SSD_TRY(check_dt(a->dt, has_tokens(p)));
+  SSD_TRY(check_vec_tensor(a->z, "z", false));
+  SSD_TRY(check_vec_tensor(a->out, "out", has_tokens(p)));
+  if (has_tokens(p) && (a->x.dtype != a->B.dtype || a->x.dtype != a->C.dtype))
+    return fail(SSD_ERR_DTYPE, "x, B and C must share a dtype");
+  if (a->z.data && a->z.dtype != a->x.dtype) return fail(SSD_ERR_DTYPE, "z must have x's dtype");
+  if (!a->A) return fail(SSD_ERR_NULL, "A is NULL");
+  return SSD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -639,22 +659,38 @@ ssd_status ssd_chunk_scan(const ssd_problem* p, const float* CB, ssd_tensor x, s
 
 ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* a,
                        void* workspace, size_t ws_bytes, hipStream_t stream) {
-  SSD_TRY(check_problem(p));
-  if (!a) return fail(SSD_ERR_NULL, "args is NULL");
-  SSD_TRY(check_vec_tensor(a->x, "x", has_tokens(p)));
-  SSD_TRY(check_vec_tensor(a->B, "B", has_tokens(p)));
-  SSD_TRY(check_vec_tensor(a->C, "C", has_tokens(p)));
-  SSD_TRY(check_dt(a->dt, has_tokens(p)));
-  SSD_TRY(check_vec_tensor(a->z, "z", false));
-  SSD_TRY(check_vec_tensor(a->out, "out", has_tokens(p)));
-  if (has_tokens(p) && (a->x.dtype != a->B.dtype || a->x.dtype != a->C.dtype))
-    return fail(SSD_ERR_DTYPE, "x, B and C must share a dtype");
-  if (a->z.data && a->z.dtype != a->x.dtype) return fail(SSD_ERR_DTYPE, "z must have x's dtype");
-  if (!a->A) return fail(SSD_ERR_NULL, "A is NULL");
+  SSD_TRY(check_fwd_args(p, a));
   if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
   if (algo == SSD_ALGO_FUSED) return fused_forward(p, a, workspace, ws_bytes, stream);
   return staged_run(p, a, nullptr, workspace, ws_bytes, stream);
+}
+
+ssd_status ssd_forward_status(const ssd_problem* p, ssd_algo algo, const void* workspace,
+                              size_t ws_bytes, uint32_t* status, hipStream_t stream) {
+  SSD_TRY(check_problem(p));
+  if (!status) return fail(SSD_ERR_NULL, "status is NULL");
+  if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED)
+    return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
+  const uint32_t* sync = nullptr;
+  if (algo == SSD_ALGO_FUSED) {
+    const FusedWs w = fused_layout(p);
+    if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+    if (ws_bytes < w.total)
+      return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, w.total);
+    sync = reinterpret_cast<const uint32_t*>(static_cast<const char*>(workspace) + w.sync);
+  }
+  SSD_HIP(ssd::launch_fused_status(sync, status, stream), "forward status launch");
+  return ok();
+}
+
+ssd_status ssd_forward_fused_lookback_test(const ssd_problem* p, const ssd_fwd_args* a,
+                                           void* workspace, size_t ws_bytes,
+                                           int32_t spin_limit, int32_t publish_flags,
+                                           hipStream_t stream) {
+  SSD_TRY(check_fwd_args(p, a));
+  if (spin_limit < 1) return fail(SSD_ERR_SHAPE, "spin_limit = %d must be >= 1", spin_limit);
+  return fused_forward(p, a, workspace, ws_bytes, stream, spin_limit, publish_flags ? 1 : 0);
 }
 
 ssd_status ssd_backward_workspace_size(const ssd_problem* p, size_t* bytes) {

@@ -103,7 +103,6 @@ constexpr int FXV = (FC * 8) / 256;     // 16-byte x (and z, out) vectors per th
 constexpr int FYLD = 64 + SSD_FUSED_YPAD;  // floats per staged output row
 constexpr uint32_t kFlagAgg = 1;        // aggregate of a range that continues a sequence
 constexpr uint32_t kFlagReset = 2;      // aggregate of a range where the sequence starts
-constexpr int kSpinLimit = 1 << 18;     // polls (~1 us each) before giving up
 
 template <int NT> struct FCfg {
   static constexpr int NMAX = 16 * NT;         // d_state capacity
@@ -142,6 +141,8 @@ struct FusedArgs {
   // [0, kFusedQueues) queue counters, [kFusedQueues] error bits,
   // [kFusedSyncHeader + r * U + u] flags
   uint32_t* sync;
+  int spin_limit;         // polls of a flag before the wait gives up
+  int publish_flags;      // 0 only in the failure-path test: no flag is raised
   float* edec;            // [r * U + u] total decay of the range's aggregate
   float* agg;             // [r * U + u][64][NMAX] aggregates
 };
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       for (int e = 0; e < 2; ++e) {
         const float uu = from_bits<TDt>(st.dt[e]) + bias;
         float d = uu;
-        if (a.softplus) d = fmaxf(uu, 0.0f) + __logf(1.0f + __expf(-fabsf(uu)));
+        if (a.softplus) d = fmaxf(uu, 0.0f) + log1pf(__expf(-fabsf(uu)));
         if (a.clamp) d = fminf(fmaxf(d, a.dt_min), a.dt_max);
         const bool in = 2 * lane + e < c.len;
         av[e] = in ? d * Ah2 : 0.0f;
@@ -474,7 +475,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       __hip_atomic_store(a.edec + r * a.U + u, E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (tid == 0)
+    if (tid == 0 && a.publish_flags)
       __hip_atomic_store(a.sync + kFusedSyncHeader + r * a.U + u, reset ? kFlagReset : kFlagAgg,
                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -512,9 +513,15 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       const uint64_t waiting = ~__ballot(f != 0u);
       const int n = min(waiting ? (int)__builtin_ctzll(waiting) : 64, r - next);
       if (n == 0) {
-        if (++spins > kSpinLimit) {
+        if (++spins > a.spin_limit) {
+          // Give up: report it in the error word and poison this wave's
+          // carry, so that every output and final state that depends on it
+          // is NaN instead of silently wrong.
           if (lane == 0)
-            __hip_atomic_fetch_or(a.sync + kFusedQueues, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(a.sync + kFusedQueues, kFusedErrLookback, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) carry[nt] = f32x4{NAN, NAN, NAN, NAN};
           break;
         }
         __builtin_amdgcn_s_sleep(2);
@@ -808,6 +815,21 @@ __global__ __launch_bounds__(256) void k_fused_prep(Geo g, const int32_t* cu, in
   for (int64_t i = threadIdx.x; i < n; i += 256) dst[i] = src ? src[i] : 0.0f;
 }
 
+// Copies the error word of a fused workspace (or 0) to the caller's status
+// word: a kernel rather than a copy or a fill, so the call can sit inside a
+// captured graph.
+__global__ void k_fused_status(const uint32_t* sync, uint32_t* status) {
+  if (threadIdx.x == 0)
+    *status = sync ? __hip_atomic_load(sync + kFusedQueues, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)
+                   : 0u;
+}
+
+hipError_t launch_fused_status(const uint32_t* sync, uint32_t* status, hipStream_t s) {
+  hipLaunchKernelGGL(k_fused_status, dim3(1), dim3(64), 0, s, sync, status);
+  return hipGetLastError();
+}
+
 FusedPlan fused_plan(int64_t K, int H, int P, int N) {
   FusedPlan pl;
   pl.PS = (P + 63) / 64;
@@ -844,6 +866,8 @@ hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s) {
   a.input_dt = f.input_dt;
   a.U = pl.U; a.PS = pl.PS; a.R = pl.R; a.nr = pl.nr;
   a.sync = f.sync; a.edec = f.edec; a.agg = f.agg;
+  a.spin_limit = f.spin_limit > 0 ? f.spin_limit : kFusedSpinLimit;
+  a.publish_flags = f.publish_flags;
   const dim3 grid((unsigned)(pl.nr * pl.U));
   const bool ob = f.out_dtype == DT_BF16, db = f.dt_dtype == DT_BF16;
 #define SSD_FUSED(TO, NT)                                                                   \

@@ -49,6 +49,8 @@ constexpr int kFusedTargetWorkgroups = 512;  // (unit, range) workgroups aimed f
 constexpr int kFusedQueues = 8;              // work queues of the fused pass, one per XCD
 // synchronisation words before the flags: the queue counters, then the error bits
 constexpr int kFusedSyncHeader = kFusedQueues + 1;
+constexpr uint32_t kFusedErrLookback = 1u;    // error bit: a look-back wait gave up
+constexpr int kFusedSpinLimit = 1 << 18;      // flag polls (~1 us each) before giving up
 
 // Work decomposition of the fused pass: P slabs of 64 rows per head, units =
 // heads x slabs, n-tiles of the d_state capacity, chunks per range, ranges.
@@ -74,10 +76,15 @@ struct FusedLaunch {
   uint32_t* sync;          // kFusedSyncHeader + nr * U words
   float* edec;             // nr * U
   float* agg;              // nr * U * 64 * 16 * NT
+  int spin_limit = 0;      // 0: kFusedSpinLimit
+  int publish_flags = 1;   // 0 only to test the failure path
 };
 
 // Two launches: a small reset/table kernel, then the fused forward.
 hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s);
+// *status = the error word of the fused workspace whose sync words are `sync`
+// (0 when sync is NULL).
+hipError_t launch_fused_status(const uint32_t* sync, uint32_t* status, hipStream_t s);
 
 // ---- backward (bwd.hip): tokens on the packed axis, ntok = b * T (batch) or
 // T (packed, cu != NULL); scratch tensors are contiguous fp32 (ntok, rows, width)

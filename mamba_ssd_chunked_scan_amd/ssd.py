@@ -12,6 +12,7 @@ tensors and returns the tensors it wrote.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -92,7 +93,8 @@ _lib = None
 EXPORTS = ("ssd_problem_check", "ssd_num_chunks", "ssd_varlen_meta_len", "ssd_workspace_size",
            "ssd_varlen_chunk_meta", "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum",
            "ssd_bmm_chunk", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
-           "ssd_forward", "ssd_backward_workspace_size", "ssd_backward",
+           "ssd_forward", "ssd_forward_status", "ssd_forward_fused_lookback_test",
+           "ssd_backward_workspace_size", "ssd_backward",
            "ssd_complex_problem_check", "ssd_complex_workspace_size", "ssd_complex_forward",
            "ssd_complex_chunk_state", "ssd_complex_state_passing", "ssd_complex_chunk_scan",
            "ssd_gated_rmsnorm_fwd", "ssd_gated_rmsnorm_bwd_workspace_size",
@@ -127,6 +129,11 @@ def lib():
                                      SsdTensor, SsdTensor, vp]
         L.ssd_forward.argtypes = [P(SsdProblem), ctypes.c_int, P(SsdFwdArgs), vp,
                                   ctypes.c_size_t, vp]
+        L.ssd_forward_status.argtypes = [P(SsdProblem), ctypes.c_int, vp, ctypes.c_size_t, vp,
+                                         vp]
+        L.ssd_forward_fused_lookback_test.argtypes = [P(SsdProblem), P(SsdFwdArgs), vp,
+                                                      ctypes.c_size_t, ctypes.c_int32,
+                                                      ctypes.c_int32, vp]
         L.ssd_backward_workspace_size.argtypes = [P(SsdProblem), P(ctypes.c_size_t)]
         L.ssd_backward.argtypes = [P(SsdProblem), P(SsdBwdArgs), vp, ctypes.c_size_t, vp]
         L.ssd_complex_problem_check.argtypes = [P(SsdComplexProblem)]
@@ -148,6 +155,7 @@ def lib():
         for name in ("ssd_problem_check", "ssd_workspace_size", "ssd_varlen_chunk_meta",
                      "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum", "ssd_bmm_chunk",
                      "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
+                     "ssd_forward_status", "ssd_forward_fused_lookback_test",
                      "ssd_backward_workspace_size", "ssd_backward",
                      "ssd_complex_problem_check", "ssd_complex_workspace_size",
                      "ssd_complex_forward", "ssd_complex_chunk_state",
@@ -216,6 +224,86 @@ def _stream(stream=None):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on(stream):
+    """Context under which temporaries are allocated: the stream the kernels
+    run on, so that torch's caching allocator never hands a block that is still
+    in use by those kernels to work on another stream."""
+    return torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _bad(status, msg):
+    raise SSDError(status, msg)
+
+
+def _check_vec(name, t, n, device, dtype=torch.float32, required=True):
+    """A per-head parameter: contiguous, ``dtype``, n elements, on ``device``."""
+    if t is None:
+        if required:
+            _bad(1, f"{name} is None")
+        return
+    if t.dtype != dtype:
+        _bad(3, f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 1 or t.numel() != n:
+        _bad(2, f"{name} must have shape ({n},), got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        _bad(4, f"{name} must be contiguous")
+    if t.device != device:
+        _bad(2, f"{name} is on {t.device}, expected {device}")
+
+
+def _check_state(name, t, shape, device):
+    """An initial/final state or its gradient: contiguous float32 of ``shape``."""
+    if t is None:
+        return
+    if t.dtype != torch.float32:
+        _bad(3, f"{name} must be float32, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        _bad(2, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        _bad(4, f"{name} must be contiguous")
+    if t.device != device:
+        _bad(2, f"{name} is on {t.device}, expected {device}")
+
+
+def _check_like(name, t, shape, device):
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        _bad(2, f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        _bad(2, f"{name} is on {t.device}, expected {device}")
+
+
+def _check_fwd_inputs(prob, x, B, C, dt, A, dt_bias, D, z, initial_states, out=None,
+                      final_states=None):
+    dev = x.device
+    _check_like("C", C, B.shape, dev)
+    _check_like("B", B, tuple(x.shape[:-2]) + tuple(B.shape[-2:]), dev)
+    _check_like("dt", dt, tuple(x.shape[:-1]), dev)
+    _check_like("z", z, x.shape, dev)
+    _check_like("out", out, x.shape, dev)
+    H = prob.nheads
+    _check_vec("A", A, H, dev)
+    _check_vec("dt_bias", dt_bias, H, dev, required=False)
+    _check_vec("D", D, H, dev, required=False)
+    nseq = prob.nseq if prob.packed else prob.batch
+    shp = (nseq, H, prob.headdim, prob.dstate)
+    _check_state("initial_states", initial_states, shp, dev)
+    _check_state("final_states", final_states, shp, dev)
+
+
+def _workspace(need, workspace, device):
+    """The caller's workspace if it is large enough, else a new one."""
+    if workspace is not None:
+        if workspace.dtype != torch.uint8 or not workspace.is_contiguous():
+            _bad(6, "workspace must be a contiguous uint8 tensor")
+        if workspace.device != device:
+            _bad(6, f"workspace is on {workspace.device}, expected {device}")
+        if workspace.numel() >= need:
+            return workspace
+    return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
 
 
 @dataclass
@@ -370,28 +458,7 @@ def ssd_chunk_scan(prob: Problem, CB, x, C, dA_cumsum, states_in, D=None, z=None
     return out
 
 
-def ssd_forward(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=None,
-                cu_seqlens=None, chunk_size=128, dt_softplus=True, dt_limit=None,
-                state_dtype=torch.float32, out=None, out_dtype=None, final_states=None,
-                algo="staged", workspace=None, stream=None, input_dt=False):
-    """The whole forward pass; returns (out, final_states).
-
-    Batch mode: x (b, T, H, P), B and C (b, T, G, N), dt (b, T, H), z like x,
-    initial_states (b, H, P, N) float32.  Packed mode: the same without the batch
-    axis plus ``cu_seqlens`` (device int32, nseq + 1).  ``input_dt`` puts the
-    step size on the input term as well (delta x (outer) B).
-    """
-    prob = problem_from(x, B, chunk_size, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
-                        dt_limit=dt_limit, state_dtype=state_dtype, input_dt=input_dt)
-    if out is None:
-        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
-    if final_states is None:
-        nseq = prob.nseq if prob.packed else prob.batch
-        final_states = torch.empty((nseq, prob.nheads, prob.headdim, prob.dstate),
-                                   dtype=torch.float32, device=x.device)
-    need = prob.workspace_size(algo)
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+def _fwd_args(prob, x, B, C, dt, A, dt_bias, D, z, initial_states, out, final_states):
     a = SsdFwdArgs()
     pk = prob.packed
     a.x, a.B, a.C = tensor_arg(x, pk), tensor_arg(B, pk), tensor_arg(C, pk)
@@ -401,9 +468,75 @@ def ssd_forward(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=Non
     a.initial_states = _ptr(initial_states)
     a.out = tensor_arg(out, pk)
     a.final_states = _ptr(final_states)
+    return a
+
+
+def _forward_setup(x, B, C, dt, A, dt_bias, D, z, initial_states, cu_seqlens, chunk_size,
+                   dt_softplus, dt_limit, state_dtype, out, out_dtype, final_states, algo,
+                   workspace, stream, input_dt):
+    prob = problem_from(x, B, chunk_size, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
+                        dt_limit=dt_limit, state_dtype=state_dtype, input_dt=input_dt)
+    _check_fwd_inputs(prob, x, B, C, dt, A, dt_bias, D, z, initial_states, out, final_states)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+        if final_states is None:
+            nseq = prob.nseq if prob.packed else prob.batch
+            final_states = torch.empty((nseq, prob.nheads, prob.headdim, prob.dstate),
+                                       dtype=torch.float32, device=x.device)
+        workspace = _workspace(prob.workspace_size(algo), workspace, x.device)
+    a = _fwd_args(prob, x, B, C, dt, A, dt_bias, D, z, initial_states, out, final_states)
+    return prob, a, out, final_states, workspace
+
+
+def ssd_forward(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=None,
+                cu_seqlens=None, chunk_size=128, dt_softplus=True, dt_limit=None,
+                state_dtype=torch.float32, out=None, out_dtype=None, final_states=None,
+                algo="staged", workspace=None, stream=None, input_dt=False):
+    """The whole forward pass; returns (out, final_states).
+
+    Batch mode: x (b, T, H, P), B and C (b, T, G, N), dt (b, T, H), z like x,
+    initial_states (b, H, P, N) float32.  Packed mode: the same without the batch
+    axis plus ``cu_seqlens`` (device int32, nseq + 1).  ``input_dt`` puts the
+    step size on the input term as well (delta x (outer) B).  Temporaries are
+    allocated on ``stream`` (the kernels' stream).
+    """
+    prob, a, out, final_states, workspace = _forward_setup(
+        x, B, C, dt, A, dt_bias, D, z, initial_states, cu_seqlens, chunk_size, dt_softplus,
+        dt_limit, state_dtype, out, out_dtype, final_states, algo, workspace, stream, input_dt)
     _check(lib().ssd_forward(ctypes.byref(prob.c()), ALGO[algo], ctypes.byref(a),
                              workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return out, final_states
+
+
+def ssd_forward_status(prob: Problem, algo, workspace, status=None, stream=None):
+    """Enqueue a read of the error word of the forward that last used
+    ``workspace`` (ssd_forward_status); returns a 1-element int32 device tensor
+    holding it (0 = no error, bit 0 = a look-back wait gave up)."""
+    with _on(stream):
+        if status is None:
+            status = torch.empty(1, dtype=torch.int32, device=workspace.device)
+    _check(lib().ssd_forward_status(ctypes.byref(prob.c()), ALGO[algo], workspace.data_ptr(),
+                                    workspace.numel(), status.data_ptr(), _stream(stream)))
+    return status
+
+
+def ssd_forward_fused_lookback_test(x, B, C, dt, A, dt_bias=None, D=None, z=None,
+                                    initial_states=None, cu_seqlens=None, spin_limit=1,
+                                    publish_flags=False, out_dtype=None, workspace=None,
+                                    stream=None):
+    """The failure-path test hook (ssd_forward_fused_lookback_test): a fused
+    forward whose look-back waits give up after ``spin_limit`` polls and, with
+    ``publish_flags=False``, never see a flag.  Returns (out, final_states,
+    workspace, problem)."""
+    prob, a, out, final_states, workspace = _forward_setup(
+        x, B, C, dt, A, dt_bias, D, z, initial_states, cu_seqlens, 128, True, None,
+        torch.float32, None, out_dtype, None, "fused", workspace, stream, False)
+    _check(lib().ssd_forward_fused_lookback_test(ctypes.byref(prob.c()), ctypes.byref(a),
+                                                 workspace.data_ptr(), workspace.numel(),
+                                                 int(spin_limit), 1 if publish_flags else 0,
+                                                 _stream(stream)))
+    return out, final_states, workspace, prob
 
 
 @dataclass
@@ -419,16 +552,8 @@ class Grads:
     dinitial_states: torch.Tensor
 
 
-def ssd_backward(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_states=None,
-                 dfinal_states=None, cu_seqlens=None, chunk_size=128, dt_softplus=True,
-                 dt_limit=None, workspace=None, stream=None, input_dt=False) -> Grads:
-    """Gradients of sum(dout * out) + sum(dfinal_states * final_states) with
-    respect to every input of ``ssd_forward`` (same arguments and layouts);
-    all gradients are float32."""
-    prob = problem_from(x, B, chunk_size, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
-                        dt_limit=dt_limit, input_dt=input_dt)
+def _bwd_alloc(prob, x, B, C, dt, D, z, nseq, workspace):
     dev, f32 = x.device, torch.float32
-    nseq = prob.nseq if prob.packed else prob.batch
     g = Grads(dx=torch.empty(x.shape, dtype=f32, device=dev),
               dB=torch.empty(B.shape, dtype=f32, device=dev),
               dC=torch.empty(C.shape, dtype=f32, device=dev),
@@ -439,9 +564,24 @@ def ssd_backward(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_sta
               dz=torch.empty(x.shape, dtype=f32, device=dev) if z is not None else None,
               dinitial_states=torch.empty((nseq, prob.nheads, prob.headdim, prob.dstate),
                                           dtype=f32, device=dev))
-    need = prob.backward_workspace_size()
-    if workspace is None or workspace.numel() < need:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    return g, _workspace(prob.backward_workspace_size(), workspace, dev)
+
+
+def ssd_backward(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_states=None,
+                 dfinal_states=None, cu_seqlens=None, chunk_size=128, dt_softplus=True,
+                 dt_limit=None, workspace=None, stream=None, input_dt=False) -> Grads:
+    """Gradients of sum(dout * out) + sum(dfinal_states * final_states) with
+    respect to every input of ``ssd_forward`` (same arguments and layouts);
+    all gradients are float32, allocated on ``stream`` like the workspace."""
+    prob = problem_from(x, B, chunk_size, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
+                        dt_limit=dt_limit, input_dt=input_dt)
+    _check_fwd_inputs(prob, x, B, C, dt, A, dt_bias, D, z, initial_states)
+    _check_like("dout", dout, x.shape, x.device)
+    nseq = prob.nseq if prob.packed else prob.batch
+    _check_state("dfinal_states", dfinal_states, (nseq, prob.nheads, prob.headdim, prob.dstate),
+                 x.device)
+    with _on(stream):
+        g, workspace = _bwd_alloc(prob, x, B, C, dt, D, z, nseq, workspace)
     a = SsdBwdArgs()
     pk = prob.packed
     a.x, a.B, a.C = tensor_arg(x, pk), tensor_arg(B, pk), tensor_arg(C, pk)
@@ -536,22 +676,27 @@ def ssd_complex_forward(x, B, C, dt, A, initial_states=None, chunk_size=64,
         prob = ComplexProblem(b, T, H, P, N, chunk_size)
         lead, ns = (b, T), b
     dev = x.device
-    if out is None:
-        out = torch.empty(lead + (H, P), dtype=torch.complex64 if out_complex else torch.float32,
-                          device=dev)
-    if final_states is None:
-        final_states = torch.empty((ns, H, P, N), dtype=torch.complex64, device=dev)
-    if initial_states is not None and not initial_states.is_contiguous():
-        raise SSDError(4, "initial_states must be contiguous")
-    if not final_states.is_contiguous():
-        raise SSDError(4, "final_states must be contiguous")
-    if A.dtype != torch.complex64 or not A.is_contiguous():
-        raise SSDError(3, "A must be a contiguous complex64 (H,) tensor")
+    _check_like("B", B, lead + (H, N), dev)
+    _check_like("C", C, lead + (H, N), dev)
+    _check_like("dt", dt, lead + (H,), dev)
+    _check_vec("A", A, H, dev, dtype=torch.complex64)
     if dt.dtype != torch.float32:
         raise SSDError(3, "dt must be float32")
-    ws_bytes = prob.workspace_size()
-    if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    for name, t in (("initial_states", initial_states), ("final_states", final_states)):
+        if t is None:
+            continue
+        if t.dtype != torch.complex64 or tuple(t.shape) != (ns, H, P, N):
+            raise SSDError(2, f"{name} must be complex64 of shape {(ns, H, P, N)}")
+        if not t.is_contiguous():
+            raise SSDError(4, f"{name} must be contiguous")
+    with _on(stream):
+        if out is None:
+            out = torch.empty(lead + (H, P),
+                              dtype=torch.complex64 if out_complex else torch.float32,
+                              device=dev)
+        if final_states is None:
+            final_states = torch.empty((ns, H, P, N), dtype=torch.complex64, device=dev)
+        workspace = _workspace(prob.workspace_size(), workspace, dev)
     a = SsdComplexFwdArgs()
     a.x, a.B, a.C = (_cx_tensor(x, packed), _cx_tensor(B, packed), _cx_tensor(C, packed))
     a.dt = tensor_arg(dt, packed)
@@ -612,8 +757,12 @@ def ssd_gated_rmsnorm_fwd(y, z, weight, group_size, eps=1e-5, out=None, out_dtyp
                           rstd=None, stream=None):
     """out = g / sqrt(mean_group(g^2) + eps) * weight, g = y silu(z); y, z (b, T, H, P).
     Returns (out, rstd); rstd is written only when a tensor is passed."""
-    if out is None:
-        out = torch.empty(y.shape, dtype=out_dtype or y.dtype, device=y.device)
+    _check_like("z", z, y.shape, y.device)
+    _check_like("out", out, y.shape, y.device)
+    _check_vec("weight", weight, y.shape[2] * y.shape[3], y.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(y.shape, dtype=out_dtype or y.dtype, device=y.device)
     p = norm_problem(y, group_size, eps)
     _check(lib().ssd_gated_rmsnorm_fwd(ctypes.byref(p), tensor_arg(y), tensor_arg(z),
                                        weight.data_ptr(), tensor_arg(out), _ptr(rstd),
@@ -633,15 +782,18 @@ def ssd_gated_rmsnorm_bwd(y, z, weight, dout, group_size, eps=1e-5, workspace=No
     """Gradients (dy, dz, dweight) of sum(dout * out); float32.  Output tensors and
     the workspace are allocated when not given."""
     p = norm_problem(y, group_size, eps)
-    if workspace is None:
-        n = gated_rmsnorm_bwd_workspace_size(y, group_size, eps)
-        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=y.device)
-    if dy is None:
-        dy = torch.empty(y.shape, dtype=torch.float32, device=y.device)
-    if dz is None and z is not None:
-        dz = torch.empty(y.shape, dtype=torch.float32, device=y.device)
-    if dw is None:
-        dw = torch.empty(weight.shape, dtype=torch.float32, device=y.device)
+    _check_like("z", z, y.shape, y.device)
+    _check_like("dout", dout, y.shape, y.device)
+    _check_vec("weight", weight, y.shape[2] * y.shape[3], y.device)
+    with _on(stream):
+        workspace = _workspace(gated_rmsnorm_bwd_workspace_size(y, group_size, eps), workspace,
+                               y.device)
+        if dy is None:
+            dy = torch.empty(y.shape, dtype=torch.float32, device=y.device)
+        if dz is None and z is not None:
+            dz = torch.empty(y.shape, dtype=torch.float32, device=y.device)
+        if dw is None:
+            dw = torch.empty(weight.shape, dtype=torch.float32, device=y.device)
     _check(lib().ssd_gated_rmsnorm_bwd(ctypes.byref(p), tensor_arg(y), tensor_arg(z),
                                        weight.data_ptr(), tensor_arg(dout), tensor_arg(dy),
                                        tensor_arg(dz), dw.data_ptr(), workspace.data_ptr(),

@@ -98,6 +98,55 @@ def oracle_run(inp: Inputs, chunk_size=0, dt_limit=None, dt_softplus=True, threa
                           input_dt=input_dt)
 
 
+def oracle_stored_states_run(inp: Inputs, chunk_size, state_dtype="bf16", threads=None):
+    """The chunked forward with its per-chunk states stored in ``state_dtype``."""
+    return oracle.ssd_fwd_stored_states(inp.x, inp.B, inp.C, inp.dt, inp.A, inp.dt_bias, inp.D,
+                                        inp.z, inp.initial_states, cu_seqlens=inp.cu_seqlens,
+                                        chunk_size=chunk_size, state_dtype=state_dtype,
+                                        threads=threads)
+
+
+def stored_state_allowance(inp: Inputs, chunk_size):
+    """Per-element allowance of a result whose per-chunk states are stored in bf16.
+
+    A stored state is a rounding of a computed one; the GPU computes its chunk
+    states in fp32 where the oracle does fp64, so a value within that small
+    difference of a bf16 rounding boundary lands on the other neighbour: one
+    bf16 step, at most 2^-7 of its size (8 significant bits).  Such a step in
+    a stored chunk state travels through the inter-chunk recurrence, and the
+    stored carry-in adds a step of its own, so a stored carry-in can differ by
+    at most 2^-7 of the carry built from |S_j| and |h0| (the same recurrence
+    on magnitudes, M_j) plus 2^-7 |Hin_j| <= 2^-7 M_j.  Its readout then
+    moves an output by at most 2^-6 exp(cs_l) sum_n |C_ln| M_j[p, n] (times
+    |silu(z)| when gated).  The final state is not stored in bf16: only the
+    chunk-state steps reach it, 2^-7 M_final.  Returns (per-output allowance
+    shaped like y, per-final-state allowance).
+    """
+    x = np.asarray(inp.x, dtype=np.float64)
+    packed = inp.cu_seqlens is not None
+    lead = 1 if packed else 2
+    pk = lambda a: None if a is None else np.asarray(a, np.float64).reshape((-1,) + a.shape[lead:])
+    xs, Bs, Cs, dts, zs = pk(x), pk(inp.B), pk(inp.C), pk(inp.dt), pk(inp.z)
+    cu = (np.asarray(inp.cu_seqlens, np.int64) if packed
+          else np.arange(x.shape[0] + 1, dtype=np.int64) * x.shape[1])
+    meta = oracle.varlen_chunk_meta(cu, chunk_size)
+    S = oracle.chunk_states(xs, Bs, dts, inp.A, meta, dt_bias=inp.dt_bias)
+    cs = oracle.chunk_cumsum(dts, inp.A, meta, chunk_size, dt_bias=inp.dt_bias)
+    h0 = None if inp.initial_states is None else np.abs(inp.initial_states)
+    M, Mfin = oracle.state_passing(np.abs(oracle.round_to_bf16(S)), cs, meta, h0)
+    ry = np.zeros_like(xs)
+    if meta.nchunks:
+        starts = [meta.start[j] for j in range(meta.nchunks)]
+        cut = np.asarray(starts + [meta.start[-1] + meta.length[-1]], dtype=np.int64)
+        lo, hi = int(cut[0]), int(cut[-1])
+        r = oracle.ssd_fwd(np.zeros_like(xs[lo:hi]), Bs[lo:hi], np.abs(Cs[lo:hi]), dts[lo:hi],
+                           inp.A, dt_bias=inp.dt_bias, initial_states=M, cu_seqlens=cut - lo)
+        ry[lo:hi] = np.abs(r.y)
+    if zs is not None:
+        ry = ry * np.abs(zs / (1.0 + np.exp(-zs)))
+    return 2.0 ** -6 * ry.reshape(x.shape), 2.0 ** -7 * Mfin
+
+
 def small_workload(name="small", batch=1, seqlen=300, nheads=4, headdim=32, ngroups=2,
                    dstate=32, chunk_size=64, dtype="bf16", has_D=True, has_z=True, seed=5,
                    nseq=0, seqlens=None):
@@ -135,5 +184,6 @@ def head_slice(inp: Inputs, heads, packed=False) -> Inputs:
 
 
 __all__ = ["err", "bf16_out_ok", "to_dev", "to_np", "device_inputs", "oracle_run",
+           "oracle_stored_states_run", "stored_state_allowance",
            "small_workload", "make_inputs", "with_initial_states", "head_slice", "in_dtype",
            "TOL_F32", "TOL_BF16", "TOL_BF16_DESIGN"]
