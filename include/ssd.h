@@ -302,6 +302,24 @@ ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* 
 ssd_status ssd_forward_status(const ssd_problem* p, ssd_algo algo, const void* workspace,
                               size_t ws_bytes, uint32_t* status, hipStream_t stream);
 
+/* Bytes of the device array behind ssd_forward_fused_static (one per GPU). */
+#define SSD_FUSED_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * computation as ssd_forward(p, SSD_ALGO_FUSED, a, ...) with the fused pass's
+ * scratch (synchronisation words, hand-off aggregates, packed-mode chunk table)
+ * in a file-scope device array of SSD_FUSED_STATIC_SCRATCH_BYTES bytes, one per
+ * GPU, held until the process ends.  It calls no allocator.  The caller still
+ * passes inputs and outputs.  A problem whose fused workspace
+ * (ssd_workspace_size(p, SSD_ALGO_FUSED)) exceeds the array returns
+ * SSD_ERR_WORKSPACE.  Every call on one GPU uses that GPU's one array (the
+ * look-up of its address is the only set-up, once per device): calls that
+ * overlap in time on one GPU, on any streams, race and must not be made.
+ * ssd_forward_status(p, SSD_ALGO_FUSED, ...) does not see this array. */
+ssd_status ssd_forward_fused_static(const ssd_problem* p, const ssd_fwd_args* a,
+                                    hipStream_t stream);
+
 /* Failure-path test hook for the fused forward, not for production use: the
  * same call as ssd_forward(p, SSD_ALGO_FUSED, ...) with the bound of every
  * look-back wait set to spin_limit polls (>= 1) and, when publish_flags == 0,

@@ -481,6 +481,10 @@ ssd_status check_fwd_args(const ssd_problem* p, const ssd_fwd_args* a) {
 
 }  // namespace
 
+namespace ssd {
+ssd_status api_fail(ssd_status s, const char* msg) { return fail(s, "%s", msg); }
+}  // namespace ssd
+
 extern "C" {
 
 const char* ssd_version(void) { return "libssd 0.1 (gfx950)"; }

@@ -94,6 +94,7 @@ EXPORTS = ("ssd_problem_check", "ssd_num_chunks", "ssd_varlen_meta_len", "ssd_wo
            "ssd_varlen_chunk_meta", "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum",
            "ssd_bmm_chunk", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
            "ssd_forward", "ssd_forward_status", "ssd_forward_fused_lookback_test",
+           "ssd_forward_fused_static",
            "ssd_backward_workspace_size", "ssd_backward",
            "ssd_complex_problem_check", "ssd_complex_workspace_size", "ssd_complex_forward",
            "ssd_complex_chunk_state", "ssd_complex_state_passing", "ssd_complex_chunk_scan",
@@ -131,6 +132,7 @@ def lib():
                                   ctypes.c_size_t, vp]
         L.ssd_forward_status.argtypes = [P(SsdProblem), ctypes.c_int, vp, ctypes.c_size_t, vp,
                                          vp]
+        L.ssd_forward_fused_static.argtypes = [P(SsdProblem), P(SsdFwdArgs), vp]
         L.ssd_forward_fused_lookback_test.argtypes = [P(SsdProblem), P(SsdFwdArgs), vp,
                                                       ctypes.c_size_t, ctypes.c_int32,
                                                       ctypes.c_int32, vp]
@@ -156,6 +158,7 @@ def lib():
                      "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum", "ssd_bmm_chunk",
                      "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
                      "ssd_forward_status", "ssd_forward_fused_lookback_test",
+                     "ssd_forward_fused_static",
                      "ssd_backward_workspace_size", "ssd_backward",
                      "ssd_complex_problem_check", "ssd_complex_workspace_size",
                      "ssd_complex_forward", "ssd_complex_chunk_state",
@@ -506,6 +509,30 @@ def ssd_forward(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=Non
         dt_limit, state_dtype, out, out_dtype, final_states, algo, workspace, stream, input_dt)
     _check(lib().ssd_forward(ctypes.byref(prob.c()), ALGO[algo], ctypes.byref(a),
                              workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out, final_states
+
+
+def ssd_forward_fused_static(x, B, C, dt, A, dt_bias=None, D=None, z=None,
+                             initial_states=None, cu_seqlens=None, dt_softplus=True,
+                             dt_limit=None, out=None, out_dtype=None, final_states=None,
+                             stream=None, input_dt=False):
+    """The fused forward with the library's static scratch array
+    (ssd_forward_fused_static): no workspace is allocated.  With ``out`` and
+    ``final_states`` given, nothing is allocated at all.  Returns (out,
+    final_states)."""
+    prob = problem_from(x, B, 128, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
+                        dt_limit=dt_limit, input_dt=input_dt)
+    _check_fwd_inputs(prob, x, B, C, dt, A, dt_bias, D, z, initial_states, out, final_states)
+    with _on(stream):
+        if out is None:
+            out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+        if final_states is None:
+            nseq = prob.nseq if prob.packed else prob.batch
+            final_states = torch.empty((nseq, prob.nheads, prob.headdim, prob.dstate),
+                                       dtype=torch.float32, device=x.device)
+    a = _fwd_args(prob, x, B, C, dt, A, dt_bias, D, z, initial_states, out, final_states)
+    _check(lib().ssd_forward_fused_static(ctypes.byref(prob.c()), ctypes.byref(a),
+                                          _stream(stream)))
     return out, final_states
 
 
