@@ -55,9 +55,8 @@
  *   offending argument (thread-local).
  * - Determinism: results are bitwise identical run to run.  The staged
  *   forward, the backward, the complex-A and the norm calls use no atomics.
- *   The fused forward uses atomics only to schedule and hand off work (queue
- *   tickets, ready flags, an error word); the values it sums are folded in a
- *   fixed order that never depends on timing.
+ *   The fused forward uses none either: it hands states between its two
+ *   launches through memory, and every sum has a fixed order.
  */
 #ifndef LIBSSD_SSD_H
 #define LIBSSD_SSD_H
@@ -266,10 +265,12 @@ typedef struct ssd_fwd_args {
 
 /* The whole forward pass.  SSD_ALGO_STAGED runs chunk cumsum, BMM, chunk
  * state, state passing and chunk scan (vLLM PR 27299 "Purpose", the five
- * stages).  SSD_ALGO_FUSED computes the same result in one fused kernel (the
- * same page: one kernel that recomputes the cumsum and C.B^T per tile and
- * hands the chunk state between workgroups instead of storing the
- * intermediates), preceded by a small reset kernel; it always works on
+ * stages).  SSD_ALGO_FUSED computes the same result in one pass over the
+ * inputs (the same page: the cumsum and C.B^T are recomputed per tile and the
+ * state is handed between workgroups instead of storing the per-chunk
+ * intermediates): a launch that sums each range of chunks into one state,
+ * then the output launch, which folds those per range and walks its chunks
+ * (plus a small chunk-table kernel in packed mode); it always works on
  * 128-token chunks (the result does not depend on the chunk length), takes
  * bf16 x, B, C (and z) and dstate <= 128, and returns SSD_ERR_UNSUPPORTED
  * otherwise; it stores no per-chunk states (the carried state stays in
@@ -283,24 +284,11 @@ typedef struct ssd_fwd_args {
  * In packed mode the chunk table is built inside the workspace.  workspace:
  * device memory of at least ssd_workspace_size(p, algo) bytes, 256-byte
  * aligned, owned by the caller, contents need not be initialised; it must not
- * be shared by calls that overlap in time.  The fused path's waits for
- * another workgroup's state are bounded: one that gives up sets bit 0
- * (SSD_STATUS_LOOKBACK_TIMEOUT) of the workspace's error word and writes NaN
- * to every output and final state that depends on the missing state (the
- * SSD Reference's contract: named failures, nothing degrades silently); read
- * the word with ssd_forward_status. */
+ * be shared by calls that overlap in time.  The fused path hands the state
+ * from one range of chunks to the next through the workspace between two
+ * launches, so no workgroup ever waits for another. */
 ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* a,
                        void* workspace, size_t ws_bytes, hipStream_t stream);
-
-#define SSD_STATUS_LOOKBACK_TIMEOUT 1u
-
-/* Device-side status of the last ssd_forward that used `workspace` (same
- * problem and algo): enqueues on `stream` a write of its error word to
- * *status (device memory, or host memory the device can write), after
- * whatever precedes it on the stream.  0 = no error; SSD_ALGO_STAGED always
- * writes 0.  Graph-capturable (a one-thread kernel, no copy or fill). */
-ssd_status ssd_forward_status(const ssd_problem* p, ssd_algo algo, const void* workspace,
-                              size_t ws_bytes, uint32_t* status, hipStream_t stream);
 
 /* Bytes of the device array behind ssd_forward_fused_static (one per GPU). */
 #define SSD_FUSED_STATIC_SCRATCH_BYTES (32u << 20)
@@ -308,28 +296,16 @@ ssd_status ssd_forward_status(const ssd_problem* p, ssd_algo algo, const void* w
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation): the same
  * computation as ssd_forward(p, SSD_ALGO_FUSED, a, ...) with the fused pass's
- * scratch (synchronisation words, hand-off aggregates, packed-mode chunk table)
+ * scratch (hand-off aggregates, packed-mode chunk table)
  * in a file-scope device array of SSD_FUSED_STATIC_SCRATCH_BYTES bytes, one per
  * GPU, held until the process ends.  It calls no allocator.  The caller still
  * passes inputs and outputs.  A problem whose fused workspace
  * (ssd_workspace_size(p, SSD_ALGO_FUSED)) exceeds the array returns
  * SSD_ERR_WORKSPACE.  Every call on one GPU uses that GPU's one array (the
  * look-up of its address is the only set-up, once per device): calls that
- * overlap in time on one GPU, on any streams, race and must not be made.
- * ssd_forward_status(p, SSD_ALGO_FUSED, ...) does not see this array. */
+ * overlap in time on one GPU, on any streams, race and must not be made. */
 ssd_status ssd_forward_fused_static(const ssd_problem* p, const ssd_fwd_args* a,
                                     hipStream_t stream);
-
-/* Failure-path test hook for the fused forward, not for production use: the
- * same call as ssd_forward(p, SSD_ALGO_FUSED, ...) with the bound of every
- * look-back wait set to spin_limit polls (>= 1) and, when publish_flags == 0,
- * no ready flag ever raised, so every wait that needs another workgroup's
- * state gives up after spin_limit polls.  Every kernel still exits normally;
- * the test then reads SSD_STATUS_LOOKBACK_TIMEOUT and the NaN outputs. */
-ssd_status ssd_forward_fused_lookback_test(const ssd_problem* p, const ssd_fwd_args* a,
-                                           void* workspace, size_t ws_bytes,
-                                           int32_t spin_limit, int32_t publish_flags,
-                                           hipStream_t stream);
 
 /* ---------------------------------------------------------------- backward */
 

@@ -35,9 +35,9 @@ def sources():
     return sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, bdir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -48,21 +48,29 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(jobs: int | None = None) -> str:
-    """Compile all HIP sources for gfx950 and link libssd.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(jobs: int | None = None, variant: str = "") -> str:
+    """Compile all HIP sources for gfx950 and link libssd.so; returns its path.
+
+    ``variant="trace"`` builds the profiling library libssd_trace.so instead:
+    the same sources with -DSSD_FUSED_TRACE (the fused forward stores per-item
+    phase timestamps at the end of its workspace; see fused_trace.py).
+    """
+    bdir = BUILD if not variant else BUILD + "_" + variant
+    lib = LIB if not variant else os.path.join(HERE, f"libssd_{variant}.so")
+    extra = [] if not variant else ["-DSSD_FUSED_TRACE"]
+    os.makedirs(bdir, exist_ok=True)
     srcs = sources()
     jobs = jobs or min(8, os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda f: _compile(f, bdir, extra), srcs))
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build())
+    print(build(variant=sys.argv[1] if len(sys.argv) > 1 else ""))

@@ -198,7 +198,7 @@ StagedWs staged_layout(const ssd_problem* p) {
 struct FusedWs {
   ssd::FusedPlan plan;
   int64_t K;  // 128-token chunk slots
-  size_t meta, sync, edec, agg, total;
+  size_t meta, edec, agg, trace = 0, total;
 };
 
 // Chunk slots at the fused pass's own chunk length.
@@ -217,12 +217,15 @@ FusedWs fused_layout(const ssd_problem* p) {
   w.meta = off;
   if (p->nseq > 0)
     off += align256((size_t)(ssd::kMetaHeader + 3 * w.K + p->nseq + 1) * sizeof(int32_t));
-  w.sync = off;
-  off += align256((size_t)(ssd::kFusedSyncHeader + slots) * sizeof(uint32_t));
   w.edec = off;
   off += align256((size_t)slots * sizeof(float));
   w.agg = off;
   off += align256((size_t)slots * 64 * 16 * w.plan.NT * sizeof(float));
+#ifdef SSD_FUSED_TRACE
+  // profiling build only: per-item phase timestamps at the end of the workspace
+  w.trace = off;
+  off += align256((size_t)slots * ssd::kFusedTraceSlots * sizeof(unsigned long long));
+#endif
   w.total = off;
   return w;
 }
@@ -236,8 +239,7 @@ ssd_status check_state_ptr(const float* ptr, const char* name) {
 // The single-pass forward (SSD_ALGO_FUSED); arguments common to both paths
 // were validated by ssd_forward.
 ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* workspace,
-                         size_t ws_bytes, hipStream_t stream, int spin_limit = 0,
-                         int publish_flags = 1) {
+                         size_t ws_bytes, hipStream_t stream) {
   if (has_tokens(p) && a->x.dtype != SSD_BF16)
     return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED takes bf16 x, B, C (use SSD_ALGO_STAGED)");
   if (p->dstate > 128)
@@ -272,11 +274,11 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
   f.softplus = p->dt_softplus; f.clamp = p->dt_clamp; f.input_dt = p->input_dt;
   f.dt_min = p->dt_min; f.dt_max = p->dt_max;
   f.plan = w.plan;
-  f.sync = reinterpret_cast<uint32_t*>(ws + w.sync);
   f.edec = reinterpret_cast<float*>(ws + w.edec);
   f.agg = reinterpret_cast<float*>(ws + w.agg);
-  f.spin_limit = spin_limit;
-  f.publish_flags = publish_flags;
+#ifdef SSD_FUSED_TRACE
+  f.trace = reinterpret_cast<unsigned long long*>(ws + w.trace);
+#endif
   SSD_HIP(ssd::launch_fused_fwd(f, stream), "fused forward launch");
   return ok();
 }
@@ -668,33 +670,6 @@ ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* 
     return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
   if (algo == SSD_ALGO_FUSED) return fused_forward(p, a, workspace, ws_bytes, stream);
   return staged_run(p, a, nullptr, workspace, ws_bytes, stream);
-}
-
-ssd_status ssd_forward_status(const ssd_problem* p, ssd_algo algo, const void* workspace,
-                              size_t ws_bytes, uint32_t* status, hipStream_t stream) {
-  SSD_TRY(check_problem(p));
-  if (!status) return fail(SSD_ERR_NULL, "status is NULL");
-  if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED)
-    return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
-  const uint32_t* sync = nullptr;
-  if (algo == SSD_ALGO_FUSED) {
-    const FusedWs w = fused_layout(p);
-    if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
-    if (ws_bytes < w.total)
-      return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, w.total);
-    sync = reinterpret_cast<const uint32_t*>(static_cast<const char*>(workspace) + w.sync);
-  }
-  SSD_HIP(ssd::launch_fused_status(sync, status, stream), "forward status launch");
-  return ok();
-}
-
-ssd_status ssd_forward_fused_lookback_test(const ssd_problem* p, const ssd_fwd_args* a,
-                                           void* workspace, size_t ws_bytes,
-                                           int32_t spin_limit, int32_t publish_flags,
-                                           hipStream_t stream) {
-  SSD_TRY(check_fwd_args(p, a));
-  if (spin_limit < 1) return fail(SSD_ERR_SHAPE, "spin_limit = %d must be >= 1", spin_limit);
-  return fused_forward(p, a, workspace, ws_bytes, stream, spin_limit, publish_flags ? 1 : 0);
 }
 
 ssd_status ssd_backward_workspace_size(const ssd_problem* p, size_t* bytes) {

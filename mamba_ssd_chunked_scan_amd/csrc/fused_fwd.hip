@@ -8,49 +8,37 @@
 // cudnn-frontend PR 1133, organised the way vLLM PR 27299 ("Purpose")
 // describes its fused kernel: the log-decay cumsum and C.B^T are recomputed
 // where they are consumed instead of being stored, and the chunk-to-chunk state
-// is handed between workgroups through memory with inter-workgroup
-// synchronisation.
+// is handed between workgroups through memory (here: per range of chunks,
+// between two launches, so that no workgroup waits for another).
 //
 // Work split.  The internal chunk is 128 tokens (the chunked result does not
 // depend on the chunk length, so the problem's chunk_size only matters to the
 // staged path).  A unit is (head h, 64-row slab of P); its chunks are cut into
 // `nr` ranges of R consecutive chunks, and one workgroup owns one (unit,
-// range).  A workgroup
-//   1. (pass 1, only if a later range continues its last sequence) runs the
-//      chunk-state recurrence over its range from a zero state -- or from the
-//      sequence's initial state when the sequence starts inside the range --
-//      and publishes that aggregate with the range's total decay E;
-//   2. if its first chunk continues a sequence, waits for the aggregates of
-//      the preceding ranges back to the one where the sequence starts and sums
-//      them, decayed, in a fixed order: the carry-in state (a decoupled
-//      look-back that never depends on timing, so results are bit-identical
-//      run to run);
-//   3. (pass 2) walks its chunks: cumsum from dt, chunk state S_j, the carry-in
+// range).  Two launches of the same kernel template (after a small table /
+// empty-sequence kernel in packed mode):
+//   1. the aggregate launch: every range whose last sequence continues into
+//      the next range runs the chunk-state recurrence over its chunks from a
+//      zero state -- or from the sequence's initial state when the sequence
+//      starts inside the range -- and stores that aggregate with the range's
+//      total decay E;
+//   2. the output launch: a range whose first chunk continues a sequence
+//      folds the aggregates of the preceding ranges back to the one where the
+//      sequence starts, oldest first (carry = E carry + agg): its carry-in.
+//      Then it walks its chunks: cumsum from dt, chunk state S_j, the carry-in
 //      H_j of the chunk staged in LDS as bf16 hi + lo, C.B^T tile by tile,
 //      Y_off + Y_diag (with the D skip on its diagonal), SiLU gate, store;
-//      then H_{j+1} = exp(Lambda_j)
-//      H_j + S_j in registers, and the final state at a sequence's last chunk.
-// Work queues.  There is one queue of (unit, range) items per XCD: queue x
-// holds the units [x U / 8, (x + 1) U / 8) -- consecutive heads, so the heads
-// of a group, which read the same B and C, meet in one XCD's L2 -- range
-// first.  A workgroup takes the next ticket of its own XCD's queue (the XCC_ID
-// hardware register), and once that queue is exhausted, of the others in turn.
-// A workgroup only waits for lower ranges of its own unit, which sit earlier
-// in the same queue and were therefore taken by running or finished
-// workgroups: no residency assumption, no deadlock.  Items never outnumber
-// workgroups, and a workgroup leaves without an item only when every queue is
-// exhausted, so every item is taken whatever the XCD placement.  Every wait is bounded; on
-// timeout an error bit is set in the workspace and the kernel still finishes.
-//
-// Hand-off.  Aggregates, decays and flags are written with agent-scope atomic
-// stores, which on gfx950 are plain stores that go through to the level of
-// the memory system all XCDs share (the L2 of each XCD is not coherent with
-// the others).  A publisher stores its aggregate, waits until all its stores
-// have completed (s_waitcnt), passes a workgroup barrier and only then stores
-// the flag; a reader polls the flag with agent-scope loads and issues its
-// aggregate loads only after it has seen it.  Release/acquire fences would do
-// the same job through a write-back and an invalidation of the whole L2 of the
-// XCD, which costs far more than the few aggregates involved.
+//      H_{j+1} = exp(Lambda_j) H_j + S_j in registers, and the final state at
+//      a sequence's last chunk.
+// The hand-off between the two is the launch boundary: no workgroup ever
+// waits for another, so no wait can stall or time out, and the order of every
+// sum is fixed (results are bit-identical run to run).  The aggregate launch
+// has the output launch's work split, without its register and LDS demands
+// beyond the chunk-state product.
+// Placement.  Workgroup ids go to the 8 XCDs in turn; ids are mapped so that
+// XCD x holds the units [x U / 8, (x + 1) U / 8) -- consecutive heads, so the
+// heads of a group, which read the same B and C chunks, meet in one XCD's L2
+// -- range first.
 //
 // Per chunk, per workgroup (4 waves, wave w).  x and B are staged in LDS in
 // their natural layout (tokens x columns); operands that need the token axis
@@ -80,12 +68,20 @@ namespace ssd {
 namespace {
 
 constexpr int FC = 128;                 // internal chunk length
-constexpr int kLookback = 3;            // aggregates loaded per look-back round trip
-// buffer resource word 3 for raw (untyped, 32-bit format) buffer access
-constexpr int kBufWord3 = 0x00020000;
-// cache-policy operand of the buffer builtins: sc1, the policy of an
-// agent-scope atomic store
-constexpr int kCachePolicySc1 = 16;
+constexpr int kLookback = 4;            // aggregates loaded per round trip of the fold
+
+// softplus(u) = max(u, 0) + log1p(exp(-|u|)).  log1p(e) for e in (0, 1] as
+// log(1 + e) * e / ((1 + e) - 1): the quotient corrects the rounding of 1 + e
+// (an exact identity in real arithmetic; a few ulp in fp32, also for e far
+// below the fp32 spacing at 1, where 1 + e rounds to 1 and the result is e).
+__device__ __forceinline__ float softplus_fast(float u) {
+  const float e = __expf(-fabsf(u));
+  const float t = 1.0f + e;
+  const float d = t - 1.0f;
+  const float l1p = d == 0.0f ? e : __logf(t) * (e * __builtin_amdgcn_rcpf(d));
+  return fmaxf(u, 0.0f) + l1p;
+}
+
 #ifndef SSD_FUSED_XPAD
 #define SSD_FUSED_XPAD 8
 #endif
@@ -101,8 +97,6 @@ constexpr int kCachePolicySc1 = 16;
 constexpr int FXLD = 64 + SSD_FUSED_XPAD;   // bf16 per row of the x tile in LDS
 constexpr int FXV = (FC * 8) / 256;     // 16-byte x (and z, out) vectors per thread
 constexpr int FYLD = 64 + SSD_FUSED_YPAD;  // floats per staged output row
-constexpr uint32_t kFlagAgg = 1;        // aggregate of a range that continues a sequence
-constexpr uint32_t kFlagReset = 2;      // aggregate of a range where the sequence starts
 
 template <int NT> struct FCfg {
   static constexpr int NMAX = 16 * NT;         // d_state capacity
@@ -138,14 +132,28 @@ struct FusedArgs {
   int softplus, clamp, input_dt;
   float dt_min, dt_max;
   int U, PS, R, nr;       // units, P slabs per head, chunks per range, ranges
-  // [0, kFusedQueues) queue counters, [kFusedQueues] error bits,
-  // [kFusedSyncHeader + r * U + u] flags
-  uint32_t* sync;
-  int spin_limit;         // polls of a flag before the wait gives up
-  int publish_flags;      // 0 only in the failure-path test: no flag is raised
+  int nmax;               // d_state capacity (16 NT): row pitch of an aggregate
+  unsigned long long* trace;  // per-item phase timestamps (SSD_FUSED_TRACE builds only)
   float* edec;            // [r * U + u] total decay of the range's aggregate
   float* agg;             // [r * U + u][64][NMAX] aggregates
 };
+
+// Phase timestamps, compiled in only with -DSSD_FUSED_TRACE (the profiling
+// build of mamba_ssd_chunked_scan_amd/fused_trace.py): lane 0 of wave 0 of the
+// item's workgroup stores the 100 MHz device clock (s_memrealtime) into slot
+// `k` of the item's kFusedTraceSlots words.
+#ifdef SSD_FUSED_TRACE
+#define SSD_TRACE(k)                                                                   \
+  do {                                                                                 \
+    if (tid == 0 && a.trace)                                                           \
+      a.trace[(size_t)(r * a.U + u) * kFusedTraceSlots + (k)] =                        \
+          __builtin_amdgcn_s_memrealtime();                                            \
+  } while (0)
+#else
+#define SSD_TRACE(k) \
+  do {               \
+  } while (0)
+#endif
 
 template <typename TO, typename TDt, int NT>
 __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
@@ -166,34 +174,25 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   const int r16 = lane % 16, q = lane / 16;
 
-  // units [queue_lo(x), queue_lo(x + 1)) belong to queue x
-  auto queue_lo = [&](int x) { return x * a.U / kFusedQueues; };
-  if (tid == 0) {
-    // hwreg 20 (XCC_ID), bits [3:0]: the XCD this workgroup runs on
-    const int xcd = (int)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 15u) % kFusedQueues;
-    int item = -1, qsel = 0;
-    for (int i = 0; i < kFusedQueues && item < 0; ++i) {
-      const int qx = (xcd + i) % kFusedQueues;
-      const int n = (queue_lo(qx + 1) - queue_lo(qx)) * a.nr;
-      if (n == 0 || (int)__hip_atomic_load(a.sync + qx, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT) >= n)
-        continue;
-      const int t =
-          (int)__hip_atomic_fetch_add(a.sync + qx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (t < n) {
-        item = t;
-        qsel = qx;
-      }
-    }
-    s_misc[0] = (uint32_t)item;
-    s_misc[2] = (uint32_t)qsel;
+  // (unit, range) of this workgroup: with U a multiple of 8, XCD x (which
+  // runs ids x, x + 8, ...) holds units [x U / 8, (x + 1) U / 8), range first
+  int r, u;
+  if (a.U % kNumXcd == 0) {
+    const int qn = a.U / kNumXcd, per = a.nr * qn;
+    const int it = xcd_remap((int)blockIdx.x, a.nr * a.U);
+    const int xq = it / per, rem = it - xq * per;
+    r = rem / qn;
+    u = xq * qn + rem % qn;
+  } else {
+    r = (int)blockIdx.x / a.U;
+    u = (int)blockIdx.x % a.U;
   }
-  __syncthreads();
-  const int item = (int)s_misc[0];
-  if (item < 0) return;
-  const int qlo = queue_lo((int)s_misc[2]);
-  const int qn = queue_lo((int)s_misc[2] + 1) - qlo;
-  const int r = item / qn, u = qlo + item % qn;
+#ifdef SSD_FUSED_TRACE
+  if (tid == 0 && a.trace) {
+    a.trace[(size_t)(r * a.U + u) * kFusedTraceSlots + kFusedTraceSlots - 1] =
+        (unsigned long long)(__builtin_amdgcn_s_getreg((15 << 11) | 20) & 15u);
+  }
+#endif
   const int h = u / a.PS, p0 = (u % a.PS) * 64;
   const int grp = h / g.hpg;
   const int pw = min(64, g.P - p0);
@@ -319,7 +318,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   // Within-chunk cumsum by wave 0, branch-free: lane l holds positions 2l and
   // 2l + 1.  fp32 with a DPP wave scan (the bf16 inputs of this path leave
   // ample room for fp32 rounding of cs; no LDS round trips).  softplus as
-  // max(u, 0) + log(1 + exp(-|u|)) with the hardware exp/log.  The cumsum is
+  // softplus_fast (hardware exp/log, log1p corrected).  The cumsum is
   // kept in base-2 units (cs * log2 e), so every decay factor below is one
   // hardware 2^x of a difference.
   auto stage_cs = [&](const Stage& st, const Chunk& c) {
@@ -329,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       for (int e = 0; e < 2; ++e) {
         const float uu = from_bits<TDt>(st.dt[e]) + bias;
         float d = uu;
-        if (a.softplus) d = fmaxf(uu, 0.0f) + log1pf(__expf(-fabsf(uu)));
+        if (a.softplus) d = softplus_fast(uu);
         if (a.clamp) d = fminf(fmaxf(d, a.dt_min), a.dt_max);
         const bool in = 2 * lane + e < c.len;
         av[e] = in ? d * Ah2 : 0.0f;
@@ -406,156 +405,60 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   };
 
   // ---- sequence structure of the range
-  Chunk cfirst, clast;
+  Chunk cfirst;
   get_chunk(g, j0, cfirst);
-  get_chunk(g, j1 - 1, clast);
-  int f0, l0, fs, ls;
+  int f0, l0;
   seq_chunks(g, cfirst.seq, f0, l0);
-  seq_chunks(g, clast.seq, fs, ls);
   const bool need_lb = f0 < j0;        // the first chunk continues a sequence
-  const bool publish = j1 < ls;        // the next range continues the last sequence
-  const bool reset = fs >= j0;         // the last sequence starts inside the range
 
   f32x4 carry[NT];
 
-  // ---- pass 1: the range's aggregate
-  if (publish) {
-    const int js = reset ? fs : j0;
-    if (reset) load_h0(carry, clast.seq);
-    else {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) carry[nt] = zero4();
-    }
-    float E = 1.0f;
-    // two register sets alternate, so chunk j + 2 is in flight while chunk j
-    // is multiplied
-    Stage sa, sb;
-    Chunk ca, cb;
-    // Every prefetch below is unconditional: with loads under a branch the
-    // compiler can no longer count which loads a wait has to cover, and waits
-    // for all of them.  Past the range's end they re-read its last chunk,
-    // which is never used.
-    get_chunk(g, js, ca);
-    load_chunk(sa, ca, false);
-    get_chunk(g, min(js + 1, j1 - 1), cb);
-    load_chunk(sb, cb, false);
-    auto step = [&](Stage& st, Chunk& c, int j) {
-      __syncthreads();  // the previous chunk's matrix phase is done with LDS
-      stage_cs(st, c);
-      stage_xb(st, c);
-      // the registers are in LDS now: refill them with chunk j + 2
-      get_chunk(g, min(j + 2, j1 - 1), c);
-      load_chunk(st, c, false);
-      __syncthreads();
-      const float e = fast_exp2(__uint_as_float(s_misc[1]));
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) carry[nt] *= e;
-      state_mma(carry);
-      E *= e;
-    };
-    for (int j = js; j < j1; j += 2) {
-      step(sa, ca, j);
-      if (j + 1 < j1) step(sb, cb, j + 1);
-    }
-    // Publish: agent-coherent stores, wait until every one has completed, then
-    // raise the flag.  The aggregate never sits in a non-coherent cache, so no
-    // cache-wide write-back is needed (see "Hand-off" above).
-    // 16-byte stores with the cache policy of an agent-scope atomic store
-    // (sc1: written through to the level all XCDs share).
-    {
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc(slot_base(r), 0, 64 * NMAX * 4, kBufWord3);
-      const uint32_t lo = slot_lane();
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, carry[nt]), rs,
-                                               (lo + nt * 16) * 4, 0, kCachePolicySc1);
-    }
-    if (tid == 0)
-      __hip_atomic_store(a.edec + r * a.U + u, E, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0 && a.publish_flags)
-      __hip_atomic_store(a.sync + kFusedSyncHeader + r * a.U + u, reset ? kFlagReset : kFlagAgg,
-                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  SSD_TRACE(2);
 
-  // the first chunk's loads go out before the wait for the carry-in
+  // ---- carry-in: the aggregates of the preceding ranges back to the one
+  // where the sequence starts (whose aggregate starts from the initial
+  // state), folded oldest first: carry = E_rr carry + agg_rr, kLookback
+  // aggregates per round trip to memory.  They were written by the aggregate
+  // launch, which has ended, so nothing is waited for.
+  if (need_lb) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) carry[nt] = zero4();
+    const int first = f0 / a.R, n = r - first;
+    for (int b = 0; b < n; b += kLookback) {
+      // (loads past the n available repeat the last one, unused: loads under
+      // a branch would leave the compiler's wait counts conservative)
+      f32x4 v[kLookback][NT];
+      float e[kLookback];
+#pragma unroll
+      for (int m = 0; m < kLookback; ++m) {
+        const int rm = first + min(b + m, n - 1);
+        const float* src = slot_base(rm);
+        const uint32_t lo = slot_lane();
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          v[m][nt] = *reinterpret_cast<const f32x4*>(at(src, lo + nt * 16));
+        e[m] = a.edec[rm * a.U + u];
+      }
+#pragma unroll
+      for (int m = 0; m < kLookback; ++m) {
+        // an unused term folds as carry * 1 + 0, which leaves carry as it is
+        const bool ok = b + m < n;
+        const float em = ok ? e[m] : 1.0f, wm = ok ? 1.0f : 0.0f;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(em, carry[nt][i], wm * v[m][nt][i]);
+      }
+    }
+  }
+  // the first chunk's loads (after the fold's: a wait for those then covers
+  // none of these)
   Chunk c;
   get_chunk(g, j0, c);
   Stage st;
   load_chunk(st, c, false);
 
-  // ---- carry-in: the aggregates of the preceding ranges back to the one
-  // where the sequence starts (rstop, whose aggregate starts from the
-  // initial state), folded oldest first: carry = E_rr carry + agg_rr.  Each
-  // wave polls the flags itself (one lane per range) and folds every
-  // aggregate as soon as it and all older ones are published, kLookback per
-  // round trip to memory.  The folds happen in the same order whatever the
-  // timing, so results are bit-identical run to run.  Aggregate data is read
-  // with ordinary (cacheable) loads, issued only after this wave has seen the
-  // flag: no cache can hold an older copy from this launch, launch boundaries
-  // leave no stale lines behind, and each aggregate occupies whole cache
-  // lines.  The decays share cache lines across ranges and the flags change
-  // during the launch, so both are read coherently.
-  if (need_lb) {
-    auto ld = [&](const float* p) {
-      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    };
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) carry[nt] = zero4();
-    int next = f0 / a.R, spins = 0;
-    while (next < r) {
-      const int rr = next + lane;
-      const uint32_t f = rr < r ? __hip_atomic_load(a.sync + kFusedSyncHeader + rr * a.U + u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT)
-                                : 1u;
-      const uint64_t waiting = ~__ballot(f != 0u);
-      const int n = min(waiting ? (int)__builtin_ctzll(waiting) : 64, r - next);
-      if (n == 0) {
-        if (++spins > a.spin_limit) {
-          // Give up: report it in the error word and poison this wave's
-          // carry, so that every output and final state that depends on it
-          // is NaN instead of silently wrong.
-          if (lane == 0)
-            __hip_atomic_fetch_or(a.sync + kFusedQueues, kFusedErrLookback, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) carry[nt] = f32x4{NAN, NAN, NAN, NAN};
-          break;
-        }
-        __builtin_amdgcn_s_sleep(2);
-        continue;
-      }
-      for (int b = 0; b < n; b += kLookback) {
-        // (loads past the n available repeat the last one, unused: loads
-        // under a branch would leave the compiler's wait counts conservative)
-        f32x4 v[kLookback][NT];
-        float e[kLookback];
-#pragma unroll
-        for (int m = 0; m < kLookback; ++m) {
-          const int rm = next + min(b + m, n - 1);
-          const float* src = slot_base(rm);
-          const uint32_t lo = slot_lane();
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) v[m][nt] = *reinterpret_cast<const f32x4*>(at(src, lo + nt * 16));
-          e[m] = ld(a.edec + rm * a.U + u);
-        }
-#pragma unroll
-        for (int m = 0; m < kLookback; ++m) {
-          // an unused term folds as carry * 1 + 0, which leaves carry as it is
-          const bool ok = b + m < n;
-          const float em = ok ? e[m] : 1.0f, wm = ok ? 1.0f : 0.0f;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(em, carry[nt][i], wm * v[m][nt][i]);
-        }
-      }
-      next += n;
-    }
-  }
-
+  SSD_TRACE(3);
   // ---- pass 2: outputs, chunk by chunk.  Per chunk:
   //   A  the carry-in H_j (the initial state at a sequence's first chunk,
   //      loaded during the previous chunk) to LDS as bf16 hi + lo (the cumsum
@@ -609,6 +512,8 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     }
     __syncthreads();
 
+    const int kk = j - j0;  // (phase stamps of the profiling build)
+    if (kk < 4) SSD_TRACE(4 + 5 * kk);
     // ---- B  (each carry-in fragment is read from LDS once and serves both
     // l-tiles)
     f32x4 acc[2][4];
@@ -649,6 +554,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     }
     __builtin_amdgcn_s_setprio(0);
     __syncthreads();  // the carry-in rows are dead: the B tile takes their space
+    if (kk < 4) SSD_TRACE(5 + 5 * kk);
 
     // ---- C
     stage_xb(st, c);
@@ -667,6 +573,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     load_chunk(st, cn, false);  // unconditional, as in pass 1
     __syncthreads();
 
+    if (kk < 4) SSD_TRACE(6 + 5 * kk);
     // ---- D
     const float e = fast_exp2(__uint_as_float(s_misc[1]));
 #pragma unroll
@@ -740,6 +647,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     if (more && fn == j + 1) load_h0(carry, cn.seq);
     load_cfr(cn);  // unconditional, as in pass 1
     __syncthreads();  // the B tile is dead: its space takes y
+    if (kk < 4) SSD_TRACE(7 + 5 * kk);
 
     // ---- E
 #pragma unroll
@@ -781,13 +689,16 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     fj = fn;
     lj = ln;
     __syncthreads();  // y and x are dead before the next chunk's staging
+    if (kk < 4) SSD_TRACE(8 + 5 * kk);
+    else if (kk < 10) SSD_TRACE(24 + (kk - 4));
   }
+  SSD_TRACE(kFusedTraceSlots - 2);
 }
 
-// Resets the synchronisation words, builds the 128-token chunk table of a
-// packed batch and writes the final state of every sequence without tokens.
+// Builds the 128-token chunk table of a packed batch and writes the final
+// state of every sequence without tokens (launched only when there is one of
+// the two to do).
 __global__ __launch_bounds__(256) void k_fused_prep(Geo g, const int32_t* cu, int32_t* meta,
-                                                    uint32_t* sync, int nsync, int nflag_blocks,
                                                     const float* h0, float* hfinal) {
   __shared__ int lds_waves[4];
   const int bid = blockIdx.x;
@@ -795,11 +706,7 @@ __global__ __launch_bounds__(256) void k_fused_prep(Geo g, const int32_t* cu, in
     if (cu) varlen_meta_block(cu, g.nseq, g.T, g.C, g.K, meta, lds_waves);
     return;
   }
-  if (bid <= nflag_blocks) {
-    for (int i = (bid - 1) * 256 + threadIdx.x; i < nsync; i += nflag_blocks * 256) sync[i] = 0u;
-    return;
-  }
-  const int seq = bid - 1 - nflag_blocks;
+  const int seq = bid - 1;
   bool empty;
   if (cu) {
     int st, L;
@@ -815,19 +722,222 @@ __global__ __launch_bounds__(256) void k_fused_prep(Geo g, const int32_t* cu, in
   for (int64_t i = threadIdx.x; i < n; i += 256) dst[i] = src ? src[i] : 0.0f;
 }
 
-// Copies the error word of a fused workspace (or 0) to the caller's status
-// word: a kernel rather than a copy or a fill, so the call can sit inside a
-// captured graph.
-__global__ void k_fused_status(const uint32_t* sync, uint32_t* status) {
-  if (threadIdx.x == 0)
-    *status = sync ? __hip_atomic_load(sync + kFusedQueues, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT)
-                   : 0u;
-}
+// ---- The aggregate launch: one workgroup of 4 waves per (unit, range).  It
+// sums its range's chunks into one state, exactly what the output launch's own
+// recurrence would carry across the range: carry = exp(Lambda_j) carry + S_j
+// from a zero state (or from the sequence's initial state when it starts
+// inside the range), S_j = sum_s exp(Lambda_j - cs_s) x_s (outer) B_s (SSD
+// Reference, "Intra-chunk outputs and per-chunk states").  Wave w owns rows
+// p-tile w and every d_state column.  Each wave computes the chunk's cumsum
+// and decay weights itself (no wave waits for another's), x and B go through
+// LDS, and the chunk state is the product B^T (w x) on the matrix cores with
+// the decay-weighted x split into bf16 hi + lo (each element split once).  Two
+// register sets alternate, so chunk j + 2 is in flight while chunk j is
+// multiplied.  Measured at the Nemotron-Nano size: this shape, at two
+// workgroups per CU, is faster than eight waves per workgroup (each wave half
+// the columns: every x element split twice) and than d_state split across
+// workgroups at three or four per CU.
+constexpr int kAggThreads = 256;
+template <typename TDt, int NT>
+__global__ __launch_bounds__(kAggThreads, 2) void k_fused_agg(FusedArgs a) {
+  constexpr int NMAX = 16 * NT;
+  constexpr int NTS = NT;                 // n-tiles per wave
+  constexpr int XLD = 64 + SSD_FUSED_XPAD;  // bf16 per x row in LDS
+  constexpr int BLD = NMAX + SSD_FUSED_BPAD;  // bf16 per B row in LDS
+  constexpr int XV = FC * 8 / kAggThreads;  // 16-byte x pieces per thread
+  constexpr int BPR = NMAX / 8;           // 16-byte pieces per B row
+  constexpr int BROWS = kAggThreads / BPR;  // B rows per pass of the workgroup
+  constexpr int BV = FC / BROWS;          // B pieces per thread
+  constexpr int NW = kAggThreads / kWave;
+  __shared__ __align__(16) bf16 s_x[FC * XLD];
+  __shared__ __align__(16) bf16 s_b[FC * BLD];
+  __shared__ __align__(16) float s_w[NW][FC];
 
-hipError_t launch_fused_status(const uint32_t* sync, uint32_t* status, hipStream_t s) {
-  hipLaunchKernelGGL(k_fused_status, dim3(1), dim3(64), 0, s, sync, status);
-  return hipGetLastError();
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int r16 = lane % 16, q = lane / 16;
+  const int pt = wave, nh = 0;
+
+  // (unit, range): XCD x holds units [x U / 8, (x + 1) U / 8), range first
+  int r, u;
+  if (a.U % kNumXcd == 0) {
+    const int qn = a.U / kNumXcd, per = a.nr * qn;
+    const int it = xcd_remap((int)blockIdx.x, a.nr * a.U);
+    const int xq = it / per, rem = it - xq * per;
+    r = rem / qn;
+    u = xq * qn + rem % qn;
+  } else {
+    r = (int)blockIdx.x / a.U;
+    u = (int)blockIdx.x % a.U;
+  }
+  const int h = u / a.PS, p0 = (u % a.PS) * 64;
+  const int grp = h / g.hpg;
+  const int pw = min(64, g.P - p0);
+  const int Kr = g.meta ? meta_word(g.meta, 0) : g.K;
+  const int j0 = r * a.R, j1 = min(j0 + a.R, Kr);
+  if (j0 >= j1) return;
+  Chunk clast;
+  get_chunk(g, j1 - 1, clast);
+  int fs, ls;
+  seq_chunks(g, clast.seq, fs, ls);
+  if (!(j1 < ls)) return;                  // the next range does not continue it
+  const bool reset = fs >= j0;             // the last sequence starts inside the range
+#ifdef SSD_FUSED_TRACE
+  if (tid == 0 && a.trace)
+    a.trace[(size_t)(r * a.U + u) * kFusedTraceSlots + 0] = __builtin_amdgcn_s_memrealtime();
+#endif
+
+  const int pl = pt * 16 + r16;           // this lane's state row (p0 + pl)
+  const int64_t PN = (int64_t)g.P * g.N;
+  f32x4 carry[NTS];
+#pragma unroll
+  for (int nt = 0; nt < NTS; ++nt) {
+    const int n = (nh * NTS + nt) * 16;
+    carry[nt] = zero4();
+    if (reset && a.h0 && pl < pw && n < g.N)
+      carry[nt] = *reinterpret_cast<const f32x4*>(
+          a.h0 + ((int64_t)clast.seq * g.H + h) * PN + (int64_t)(p0 + pl) * g.N + n + q * 4);
+  }
+  const float Ah2 = a.A[h] * 1.4426950408889634f;
+  const float bias = a.dt_bias ? a.dt_bias[h] : 0.0f;
+
+  struct Stage {
+    u32x4 x[XV], b[BV];
+    uint32_t dt[2];
+  };
+  const bool dims_full = pw == 64 && g.N == NMAX;
+  auto load = [&](Stage& st, const Chunk& c) {
+    const TDt* dbase = row_ptr<TDt>(a.dt, c.b, c.t0, h);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      st.dt[e] = raw_bits(*at(dbase, (uint32_t)(min(2 * lane + e, c.len - 1) * a.dt.s1)));
+    const int t = opaque_tid();
+    const bf16* xbase = row_ptr<bf16>(a.x, c.b, c.t0, h) + p0;
+    const int xrow = t / 8, xcol = (t % 8) * 8;
+    const bf16* bbase = row_ptr<bf16>(a.B, c.b, c.t0, grp);
+    const int brow = t / BPR, bcol = (t % BPR) * 8;
+    constexpr int XROWS = kAggThreads / 8;
+    if (dims_full && c.len == FC) {
+#pragma unroll
+      for (int k = 0; k < XV; ++k)
+        st.x[k] = *reinterpret_cast<const u32x4*>(
+            at(xbase, (uint32_t)((xrow + XROWS * k) * a.x.s1 + xcol)));
+#pragma unroll
+      for (int k = 0; k < BV; ++k)
+        st.b[k] = *reinterpret_cast<const u32x4*>(
+            at(bbase, (uint32_t)((brow + BROWS * k) * a.B.s1 + bcol)));
+    } else {
+#pragma unroll
+      for (int k = 0; k < XV; ++k)
+        st.x[k] = *reinterpret_cast<const u32x4*>(at(
+            xbase, (uint32_t)(min(xrow + XROWS * k, c.len - 1) * a.x.s1 + min(xcol, pw - 8))));
+#pragma unroll
+      for (int k = 0; k < BV; ++k)
+        st.b[k] = *reinterpret_cast<const u32x4*>(at(
+            bbase, (uint32_t)(min(brow + BROWS * k, c.len - 1) * a.B.s1 + min(bcol, g.N - 8))));
+    }
+  };
+  auto stage = [&](const Stage& st, const Chunk& c) {
+    const int t = opaque_tid();
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    constexpr int XROWS = kAggThreads / 8;
+    const int xrow = t / 8, xcol = (t % 8) * 8;
+    const int brow = t / BPR, bcol = (t % BPR) * 8;
+#pragma unroll
+    for (int k = 0; k < XV; ++k)
+      *reinterpret_cast<u32x4*>(&s_x[(xrow + XROWS * k) * XLD + xcol]) =
+          (xrow + XROWS * k < c.len && xcol < pw) ? st.x[k] : zero;
+#pragma unroll
+    for (int k = 0; k < BV; ++k)
+      *reinterpret_cast<u32x4*>(&s_b[(brow + BROWS * k) * BLD + bcol]) =
+          (brow + BROWS * k < c.len && bcol < g.N) ? st.b[k] : zero;
+  };
+  // every wave: the chunk's decay weights into its own row of s_w; returns
+  // the chunk's total log-decay (base 2)
+  auto weights = [&](const Stage& st, const Chunk& c) {
+    float av[2], dv[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float uu = from_bits<TDt>(st.dt[e]) + bias;
+      float d = a.softplus ? softplus_fast(uu) : uu;
+      if (a.clamp) d = fminf(fmaxf(d, a.dt_min), a.dt_max);
+      const bool in = 2 * lane + e < c.len;
+      av[e] = in ? d * Ah2 : 0.0f;
+      dv[e] = in && a.input_dt ? d : 1.0f;
+    }
+    const float pair = av[0] + av[1];
+    const float incl = wave_inclusive_sum_dpp(pair);
+    const float c0 = incl - pair + av[0], c1 = incl;
+    const int ll = c.len - 1;
+    const float lam = __int_as_float(
+        __builtin_amdgcn_readlane(__float_as_int((ll & 1) ? c1 : c0), ll >> 1));
+    s_w[wave][2 * lane] = 2 * lane < c.len ? fast_exp2(lam - c0) * dv[0] : 0.0f;
+    s_w[wave][2 * lane + 1] = 2 * lane + 1 < c.len ? fast_exp2(lam - c1) * dv[1] : 0.0f;
+    return lam;
+  };
+  auto state_mma = [&]() {
+#pragma unroll
+    for (int kb = 0; kb < FC / 32; ++kb) {
+      const int k0 = kb * 32 + q * 8;
+      const u32x4 xv = __builtin_bit_cast(u32x4, lds_frag_tr(s_x, XLD, k0, k0 + 4, pt * 16));
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&s_w[wave][k0]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&s_w[wave][k0 + 4]);
+      f32x8 xw;
+#pragma unroll
+      for (int d = 0; d < 2; ++d) {
+        xw[2 * d] = bf16_lo_f32(xv[d]) * w0[2 * d];
+        xw[2 * d + 1] = bf16_hi_f32(xv[d]) * w0[2 * d + 1];
+        xw[4 + 2 * d] = bf16_lo_f32(xv[2 + d]) * w1[2 * d];
+        xw[4 + 2 * d + 1] = bf16_hi_f32(xv[2 + d]) * w1[2 * d + 1];
+      }
+      const FragSplit b = split_f32x8(xw);
+#pragma unroll
+      for (int nt = 0; nt < NTS; ++nt) {
+        FragBF av;
+        av.v = lds_frag_tr(s_b, BLD, k0, k0 + 4, (nh * NTS + nt) * 16);
+        mma(carry[nt], av, b);
+      }
+    }
+  };
+
+  const int js = reset ? fs : j0;
+  float E = 1.0f;
+  Stage sa, sb;
+  Chunk ca, cb;
+  get_chunk(g, js, ca);
+  load(sa, ca);
+  get_chunk(g, min(js + 1, j1 - 1), cb);
+  load(sb, cb);
+  auto step = [&](Stage& st, Chunk& c, int j) {
+    __syncthreads();  // every wave is done with the previous chunk's tiles
+    stage(st, c);
+    const float lam = weights(st, c);
+    get_chunk(g, min(j + 2, j1 - 1), c);  // refill with chunk j + 2 (or the last, unused)
+    load(st, c);
+    __syncthreads();
+    const float e = fast_exp2(lam);
+#pragma unroll
+    for (int nt = 0; nt < NTS; ++nt) carry[nt] *= e;
+    E *= e;
+    state_mma();
+  };
+  for (int j = js; j < j1; j += 2) {
+    step(sa, ca, j);
+    if (j + 1 < j1) step(sb, cb, j + 1);
+  }
+  if (pl < pw) {
+    float* dst = a.agg + ((int64_t)r * a.U + u) * 64 * NMAX + (int64_t)pl * NMAX + q * 4;
+#pragma unroll
+    for (int nt = 0; nt < NTS; ++nt) {
+      const int n = (nh * NTS + nt) * 16;
+      if (n < g.N) *reinterpret_cast<f32x4*>(dst + n) = carry[nt];
+    }
+  }
+  if (tid == 0) a.edec[r * a.U + u] = E;
+#ifdef SSD_FUSED_TRACE
+  if (tid == 0 && a.trace)
+    a.trace[(size_t)(r * a.U + u) * kFusedTraceSlots + 1] = __builtin_amdgcn_s_memrealtime();
+#endif
 }
 
 FusedPlan fused_plan(int64_t K, int H, int P, int N) {
@@ -850,13 +960,16 @@ FusedPlan fused_plan(int64_t K, int H, int P, int N) {
 hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s) {
   const Geo& g = f.g;
   const FusedPlan& pl = f.plan;
-  const int nsync = kFusedSyncHeader + pl.nr * pl.U;
-  const int nflag_blocks = min((nsync + 255) / 256, 64);
-  const int nfinal = f.hfinal ? g.nseq : 0;
-  hipLaunchKernelGGL(k_fused_prep, dim3(1 + nflag_blocks + nfinal), dim3(256), 0, s, g, f.cu,
-                     f.meta, f.sync, nsync, nflag_blocks, f.h0, f.hfinal);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.nr == 0) return e;
+  // the chunk table (packed mode), and final states of sequences without
+  // tokens (only packed mode, or a batch without tokens, has any)
+  if (f.cu || g.T == 0) {
+    const int nfinal = f.hfinal ? g.nseq : 0;
+    hipLaunchKernelGGL(k_fused_prep, dim3(1 + nfinal), dim3(256), 0, s, g, f.cu, f.meta, f.h0,
+                       f.hfinal);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (pl.nr == 0) return hipSuccess;
 
   FusedArgs a;
   a.g = g;
@@ -865,11 +978,27 @@ hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s) {
   a.softplus = f.softplus; a.clamp = f.clamp; a.dt_min = f.dt_min; a.dt_max = f.dt_max;
   a.input_dt = f.input_dt;
   a.U = pl.U; a.PS = pl.PS; a.R = pl.R; a.nr = pl.nr;
-  a.sync = f.sync; a.edec = f.edec; a.agg = f.agg;
-  a.spin_limit = f.spin_limit > 0 ? f.spin_limit : kFusedSpinLimit;
-  a.publish_flags = f.publish_flags;
+  a.edec = f.edec; a.agg = f.agg;
+  a.trace = f.trace;
   const dim3 grid((unsigned)(pl.nr * pl.U));
   const bool ob = f.out_dtype == DT_BF16, db = f.dt_dtype == DT_BF16;
+  a.nmax = 16 * pl.NT;
+  // the aggregate launch (only when some range hands a state to the next)
+  if (pl.nr > 1) {
+#define SSD_FUSED_AGG(NT)                                                                    \
+  do {                                                                                       \
+    if (db) hipLaunchKernelGGL((k_fused_agg<bf16, NT>), grid, dim3(kAggThreads), 0, s, a);   \
+    else hipLaunchKernelGGL((k_fused_agg<float, NT>), grid, dim3(kAggThreads), 0, s, a);     \
+  } while (0)
+    switch (pl.NT) {
+      case 2: SSD_FUSED_AGG(2); break;
+      case 4: SSD_FUSED_AGG(4); break;
+      default: SSD_FUSED_AGG(8); break;
+    }
+#undef SSD_FUSED_AGG
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 #define SSD_FUSED(TO, NT)                                                                   \
   do {                                                                                      \
     if (db) hipLaunchKernelGGL((k_fused_fwd<TO, bf16, NT>), grid, dim3(256), 0, s, a);       \

@@ -46,12 +46,6 @@ hipError_t launch_chunk_scan(const Geo& g, const float* CB, TArg x, TArg C, int 
 // ---- fused forward (fused_fwd.hip)
 constexpr int kFusedChunk = 128;             // internal chunk length of the fused pass
 constexpr int kFusedTargetWorkgroups = 512;  // (unit, range) workgroups aimed for
-constexpr int kFusedQueues = 8;              // work queues of the fused pass, one per XCD
-// synchronisation words before the flags: the queue counters, then the error bits
-constexpr int kFusedSyncHeader = kFusedQueues + 1;
-constexpr uint32_t kFusedErrLookback = 1u;    // error bit: a look-back wait gave up
-constexpr int kFusedSpinLimit = 1 << 18;      // flag polls (~1 us each) before giving up
-
 // Work decomposition of the fused pass: P slabs of 64 rows per head, units =
 // heads x slabs, n-tiles of the d_state capacity, chunks per range, ranges.
 struct FusedPlan {
@@ -73,18 +67,22 @@ struct FusedLaunch {
   int softplus, clamp, input_dt;
   float dt_min, dt_max;
   FusedPlan plan;
-  uint32_t* sync;          // kFusedSyncHeader + nr * U words
   float* edec;             // nr * U
   float* agg;              // nr * U * 64 * 16 * NT
-  int spin_limit = 0;      // 0: kFusedSpinLimit
-  int publish_flags = 1;   // 0 only to test the failure path
+  unsigned long long* trace = nullptr;  // SSD_FUSED_TRACE builds: kFusedTraceSlots per item
 };
+// Phase timestamps per (unit, range) item in SSD_FUSED_TRACE builds: [0] and
+// [1] the aggregate launch's start and end for the item; the output launch's
+// [2] start, [3] carry-in folded; for chunks k < 4 five stamps [4 + 5k ..
+// 8 + 5k] after its phases A (carry-in to LDS), B (Y_off), C (x and B to
+// LDS), D (state, C.B^T, Y_diag) and E (gate, store); for chunks 4 <= k < 10
+// the end of the chunk at [20 + k]; [slots - 2] end and [slots - 1] the XCD
+// the item ran on.
+constexpr int kFusedTraceSlots = 32;
 
-// Two launches: a small reset/table kernel, then the fused forward.
+// Up to three launches: the chunk table / empty sequences (packed mode or no
+// tokens), the range aggregates (more than one range), the outputs.
 hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s);
-// *status = the error word of the fused workspace whose sync words are `sync`
-// (0 when sync is NULL).
-hipError_t launch_fused_status(const uint32_t* sync, uint32_t* status, hipStream_t s);
 
 // ---- backward (bwd.hip): tokens on the packed axis, ntok = b * T (batch) or
 // T (packed, cu != NULL); scratch tensors are contiguous fp32 (ntok, rows, width)

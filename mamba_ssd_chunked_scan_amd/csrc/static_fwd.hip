@@ -1,7 +1,7 @@
 // static_fwd.hip -- ssd_forward_fused_static: the fused forward for callers
 // that cannot allocate device memory (code under HIP graph capture, tight
 // serving loops, harnesses that forbid allocation).  The fused pass's
-// synchronisation words, hand-off aggregates and (packed mode) chunk table live
+// hand-off aggregates and (packed mode) chunk table live
 // in a file-scope device array instead of a caller-provided workspace; the
 // kernels are those of ssd_forward(SSD_ALGO_FUSED).
 #include <hip/hip_runtime.h>

@@ -93,8 +93,7 @@ _lib = None
 EXPORTS = ("ssd_problem_check", "ssd_num_chunks", "ssd_varlen_meta_len", "ssd_workspace_size",
            "ssd_varlen_chunk_meta", "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum",
            "ssd_bmm_chunk", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
-           "ssd_forward", "ssd_forward_status", "ssd_forward_fused_lookback_test",
-           "ssd_forward_fused_static",
+           "ssd_forward", "ssd_forward_fused_static",
            "ssd_backward_workspace_size", "ssd_backward",
            "ssd_complex_problem_check", "ssd_complex_workspace_size", "ssd_complex_forward",
            "ssd_complex_chunk_state", "ssd_complex_state_passing", "ssd_complex_chunk_scan",
@@ -130,12 +129,7 @@ def lib():
                                      SsdTensor, SsdTensor, vp]
         L.ssd_forward.argtypes = [P(SsdProblem), ctypes.c_int, P(SsdFwdArgs), vp,
                                   ctypes.c_size_t, vp]
-        L.ssd_forward_status.argtypes = [P(SsdProblem), ctypes.c_int, vp, ctypes.c_size_t, vp,
-                                         vp]
         L.ssd_forward_fused_static.argtypes = [P(SsdProblem), P(SsdFwdArgs), vp]
-        L.ssd_forward_fused_lookback_test.argtypes = [P(SsdProblem), P(SsdFwdArgs), vp,
-                                                      ctypes.c_size_t, ctypes.c_int32,
-                                                      ctypes.c_int32, vp]
         L.ssd_backward_workspace_size.argtypes = [P(SsdProblem), P(ctypes.c_size_t)]
         L.ssd_backward.argtypes = [P(SsdProblem), P(SsdBwdArgs), vp, ctypes.c_size_t, vp]
         L.ssd_complex_problem_check.argtypes = [P(SsdComplexProblem)]
@@ -157,7 +151,6 @@ def lib():
         for name in ("ssd_problem_check", "ssd_workspace_size", "ssd_varlen_chunk_meta",
                      "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum", "ssd_bmm_chunk",
                      "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
-                     "ssd_forward_status", "ssd_forward_fused_lookback_test",
                      "ssd_forward_fused_static",
                      "ssd_backward_workspace_size", "ssd_backward",
                      "ssd_complex_problem_check", "ssd_complex_workspace_size",
@@ -534,36 +527,6 @@ def ssd_forward_fused_static(x, B, C, dt, A, dt_bias=None, D=None, z=None,
     _check(lib().ssd_forward_fused_static(ctypes.byref(prob.c()), ctypes.byref(a),
                                           _stream(stream)))
     return out, final_states
-
-
-def ssd_forward_status(prob: Problem, algo, workspace, status=None, stream=None):
-    """Enqueue a read of the error word of the forward that last used
-    ``workspace`` (ssd_forward_status); returns a 1-element int32 device tensor
-    holding it (0 = no error, bit 0 = a look-back wait gave up)."""
-    with _on(stream):
-        if status is None:
-            status = torch.empty(1, dtype=torch.int32, device=workspace.device)
-    _check(lib().ssd_forward_status(ctypes.byref(prob.c()), ALGO[algo], workspace.data_ptr(),
-                                    workspace.numel(), status.data_ptr(), _stream(stream)))
-    return status
-
-
-def ssd_forward_fused_lookback_test(x, B, C, dt, A, dt_bias=None, D=None, z=None,
-                                    initial_states=None, cu_seqlens=None, spin_limit=1,
-                                    publish_flags=False, out_dtype=None, workspace=None,
-                                    stream=None):
-    """The failure-path test hook (ssd_forward_fused_lookback_test): a fused
-    forward whose look-back waits give up after ``spin_limit`` polls and, with
-    ``publish_flags=False``, never see a flag.  Returns (out, final_states,
-    workspace, problem)."""
-    prob, a, out, final_states, workspace = _forward_setup(
-        x, B, C, dt, A, dt_bias, D, z, initial_states, cu_seqlens, 128, True, None,
-        torch.float32, None, out_dtype, None, "fused", workspace, stream, False)
-    _check(lib().ssd_forward_fused_lookback_test(ctypes.byref(prob.c()), ctypes.byref(a),
-                                                 workspace.data_ptr(), workspace.numel(),
-                                                 int(spin_limit), 1 if publish_flags else 0,
-                                                 _stream(stream)))
-    return out, final_states, workspace, prob
 
 
 @dataclass
