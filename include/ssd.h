@@ -290,6 +290,38 @@ typedef struct ssd_fwd_args {
 ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* a,
                        void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* The gated RMSNorm that follows the scan in the Mamba-2 mixer (mamba PR 1012,
+ * "Summary": the gated-LayerNorm after the SSD; its formula is not on the
+ * pages: Mamba-2's gated RMSNorm, gate first), fused into the forward:
+ *     g = y silu(z)  (g = y when z is absent),   y = the scan output,
+ *     out = g / sqrt(mean_group(g^2) + eps) * weight
+ * over contiguous groups of group_size channels of each token's flattened
+ * (H, P) axis, as ssd_gated_rmsnorm_fwd computes it from y and z. */
+typedef struct ssd_norm_args {
+  const float* weight;   /* (H * P) float32, 16-byte aligned */
+  int32_t group_size;    /* a multiple of 64 dividing H * P, at most 256 groups per token */
+  float eps;             /* >= 0 */
+  float* rstd;           /* (b * T, H * P / group_size) float32, or NULL:
+                            1 / sqrt(mean_group(g^2) + eps) per token and group */
+} ssd_norm_args;
+
+/* Bytes of workspace ssd_forward_gated_norm needs. */
+ssd_status ssd_forward_gated_norm_workspace_size(const ssd_problem* p, const ssd_norm_args* n,
+                                                 size_t* bytes);
+
+/* The fused forward (SSD_ALGO_FUSED, same inputs and restrictions) with the
+ * gated RMSNorm in its epilogue: the output launch gates its outputs, writes
+ * g to `out` and, per token and 64-channel block, the sum of g^2 (from the
+ * fp32 values); a last pass scales `out` in place by the group factor and the
+ * weight.  Against ssd_forward followed by ssd_gated_rmsnorm_fwd this reads
+ * neither y nor z a second time.  Needs headdim a multiple of 64 (the
+ * channel blocks are the fused pass's 64-row units); returns
+ * SSD_ERR_UNSUPPORTED otherwise.  With a bf16 `out`, g is rounded to bf16
+ * once before the scaling (one more rounding than the two-call path's y). */
+ssd_status ssd_forward_gated_norm(const ssd_problem* p, const ssd_fwd_args* a,
+                                  const ssd_norm_args* n, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream);
+
 /* Bytes of the device array behind ssd_forward_fused_static (one per GPU). */
 #define SSD_FUSED_STATIC_SCRATCH_BYTES (32u << 20)
 

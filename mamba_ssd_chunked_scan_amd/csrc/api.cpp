@@ -198,7 +198,7 @@ StagedWs staged_layout(const ssd_problem* p) {
 struct FusedWs {
   ssd::FusedPlan plan;
   int64_t K;  // 128-token chunk slots
-  size_t meta, edec, agg, trace = 0, total;
+  size_t meta, edec, agg, psum = 0, trace = 0, total;
 };
 
 // Chunk slots at the fused pass's own chunk length.
@@ -208,7 +208,7 @@ int64_t fused_chunks(const ssd_problem* p) {
   return (int64_t)p->batch * nc;
 }
 
-FusedWs fused_layout(const ssd_problem* p) {
+FusedWs fused_layout(const ssd_problem* p, bool norm = false) {
   FusedWs w;
   w.K = fused_chunks(p);
   w.plan = ssd::fused_plan(w.K, p->nheads, p->headdim, p->dstate);
@@ -221,6 +221,8 @@ FusedWs fused_layout(const ssd_problem* p) {
   off += align256((size_t)slots * sizeof(float));
   w.agg = off;
   off += align256((size_t)slots * 64 * 16 * w.plan.NT * sizeof(float));
+  w.psum = off;  // gated RMSNorm fused in: per token and 64-channel block, sum(g^2)
+  if (norm) off += align256((size_t)p->batch * p->seqlen * (p->nheads * p->headdim / 64) * sizeof(float));
 #ifdef SSD_FUSED_TRACE
   // profiling build only: per-item phase timestamps at the end of the workspace
   w.trace = off;
@@ -239,7 +241,7 @@ ssd_status check_state_ptr(const float* ptr, const char* name) {
 // The single-pass forward (SSD_ALGO_FUSED); arguments common to both paths
 // were validated by ssd_forward.
 ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* workspace,
-                         size_t ws_bytes, hipStream_t stream) {
+                         size_t ws_bytes, hipStream_t stream, const ssd_norm_args* norm = nullptr) {
   if (has_tokens(p) && a->x.dtype != SSD_BF16)
     return fail(SSD_ERR_UNSUPPORTED, "SSD_ALGO_FUSED takes bf16 x, B, C (use SSD_ALGO_STAGED)");
   if (p->dstate > 128)
@@ -251,7 +253,7 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
                 "dt_min >= 0); use SSD_ALGO_STAGED");
   SSD_TRY(check_state_ptr(a->initial_states, "initial_states"));
   SSD_TRY(check_state_ptr(a->final_states, "final_states"));
-  const FusedWs w = fused_layout(p);
+  const FusedWs w = fused_layout(p, norm != nullptr);
   if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < w.total)
     return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, w.total);
@@ -279,7 +281,20 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
 #ifdef SSD_FUSED_TRACE
   f.trace = reinterpret_cast<unsigned long long*>(ws + w.trace);
 #endif
+  if (norm) f.psum = reinterpret_cast<float*>(ws + w.psum);
   SSD_HIP(ssd::launch_fused_fwd(f, stream), "fused forward launch");
+  if (norm) {
+    ssd::NormGeo ng;
+    ng.ntok = (int)((int64_t)p->batch * p->seqlen);
+    ng.T = p->seqlen;
+    ng.H = p->nheads;
+    ng.P = p->headdim;
+    ng.gs = norm->group_size;
+    ng.eps = norm->eps;
+    SSD_HIP(ssd::launch_norm_finish(ng, f.psum, norm->weight, targ(a->out), dcode(a->out.dtype),
+                                    norm->rstd, stream),
+            "gated rmsnorm finish launch");
+  }
   return ok();
 }
 
@@ -481,6 +496,30 @@ ssd_status check_fwd_args(const ssd_problem* p, const ssd_fwd_args* a) {
   return SSD_OK;
 }
 
+// The forward with the gated RMSNorm fused in: checks of the norm arguments.
+ssd_status check_norm_args(const ssd_problem* p, const ssd_norm_args* n) {
+  if (!n) return fail(SSD_ERR_NULL, "norm args is NULL");
+  if (!n->weight) return fail(SSD_ERR_NULL, "norm weight is NULL");
+  if (reinterpret_cast<uintptr_t>(n->weight) % 16 != 0)
+    return fail(SSD_ERR_STRIDE, "norm weight is not 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(n->rstd) % 4 != 0)
+    return fail(SSD_ERR_STRIDE, "rstd is not 4-byte aligned");
+  if (!(n->eps >= 0.0f)) return fail(SSD_ERR_SHAPE, "eps = %g must be >= 0", n->eps);
+  if (p->headdim % 64 != 0)
+    return fail(SSD_ERR_UNSUPPORTED,
+                "the fused gated norm needs headdim a multiple of 64, got %d (use ssd_forward "
+                "and ssd_gated_rmsnorm_fwd)", p->headdim);
+  const int W = p->nheads * p->headdim;
+  const int gs = n->group_size;
+  if (gs < 64 || gs % 64 != 0 || W % gs != 0)
+    return fail(SSD_ERR_SHAPE, "group_size = %d must be a multiple of 64 dividing H * P = %d",
+                gs, W);
+  if (W / gs > ssd::kNormFinishGroups)
+    return fail(SSD_ERR_UNSUPPORTED, "H * P / group_size = %d groups per token exceeds %d",
+                W / gs, ssd::kNormFinishGroups);
+  return SSD_OK;
+}
+
 }  // namespace
 
 namespace ssd {
@@ -670,6 +709,23 @@ ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* 
     return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
   if (algo == SSD_ALGO_FUSED) return fused_forward(p, a, workspace, ws_bytes, stream);
   return staged_run(p, a, nullptr, workspace, ws_bytes, stream);
+}
+
+ssd_status ssd_forward_gated_norm_workspace_size(const ssd_problem* p, const ssd_norm_args* n,
+                                                 size_t* bytes) {
+  SSD_TRY(check_problem(p));
+  SSD_TRY(check_norm_args(p, n));
+  if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
+  *bytes = fused_layout(p, true).total;
+  return ok();
+}
+
+ssd_status ssd_forward_gated_norm(const ssd_problem* p, const ssd_fwd_args* a,
+                                  const ssd_norm_args* n, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream) {
+  SSD_TRY(check_fwd_args(p, a));
+  SSD_TRY(check_norm_args(p, n));
+  return fused_forward(p, a, workspace, ws_bytes, stream, n);
 }
 
 ssd_status ssd_backward_workspace_size(const ssd_problem* p, size_t* bytes) {

@@ -133,6 +133,9 @@ struct FusedArgs {
   float dt_min, dt_max;
   int U, PS, R, nr;       // units, P slabs per head, chunks per range, ranges
   int nmax;               // d_state capacity (16 NT): row pitch of an aggregate
+  // gated RMSNorm fused in (NULL: off): per (token, unit) sum of the squares
+  // of the unit's gated outputs, [token][U] (P a multiple of 64)
+  float* psum;
   unsigned long long* trace;  // per-item phase timestamps (SSD_FUSED_TRACE builds only)
   float* edec;            // [r * U + u] total decay of the range's aggregate
   float* agg;             // [r * U + u][64][NMAX] aggregates
@@ -684,6 +687,19 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
         }
       }
       if (efull || (l < c.len && pp < pw)) Vec8<TO>::store(at(obase, eoff + k * estep), y);
+      if (a.psum) {
+        // the gated RMSNorm after the scan: sum(g^2) of this row's 64
+        // channels (8 lanes of 8), one partial per (token, 64-channel block)
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ss += y[i] * y[i];
+        ss = (l < c.len && pp < pw) ? ss : 0.0f;
+        ss += __shfl_xor(ss, 1, kWave);
+        ss += __shfl_xor(ss, 2, kWave);
+        ss += __shfl_xor(ss, 4, kWave);
+        if (ecol == 0 && l < c.len)
+          a.psum[((int64_t)c.b * g.T + c.t0 + l) * a.U + u] = ss;
+      }
     }
     c = cn;
     fj = fn;
@@ -979,6 +995,7 @@ hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s) {
   a.input_dt = f.input_dt;
   a.U = pl.U; a.PS = pl.PS; a.R = pl.R; a.nr = pl.nr;
   a.edec = f.edec; a.agg = f.agg;
+  a.psum = f.psum;
   a.trace = f.trace;
   const dim3 grid((unsigned)(pl.nr * pl.U));
   const bool ob = f.out_dtype == DT_BF16, db = f.dt_dtype == DT_BF16;

@@ -120,6 +120,55 @@ __global__ __launch_bounds__(256) void k_norm_fwd(NormGeo g, TArg y, TArg z, con
   if (rstd && lane == 0) rstd[item] = r;
 }
 
+// The normalisation of the forward with the gated RMSNorm fused in: the scan's
+// epilogue has written g = y silu(z) to `out` and, per token and 64-channel
+// block, sum(g^2) (from the fp32 g) to psum; this pass scales `out` in place,
+// out = g r weight with r = 1 / sqrt(sum over the group's blocks / gs + eps).
+// One wave per token: the group factors first (into LDS), then the token's
+// channels in 16-byte (bf16) or 32-byte (fp32) vectors.
+template <typename TO>
+__global__ __launch_bounds__(256) void k_norm_finish(NormGeo g, const float* psum,
+                                                     const float* w, TArg out, float* rstd) {
+  __shared__ float s_r[4][kNormFinishGroups];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int tok = blockIdx.x * 4 + wave;
+  if (tok >= g.ntok) return;
+  const int W = g.H * g.P, U = W / 64, gu = g.gs / 64, ngr = W / g.gs;
+  const float* ps = psum + (int64_t)tok * U;
+  if (gu >= kWave) {
+    // wide groups: the wave sums each group's blocks
+    for (int j = 0; j < ngr; ++j) {
+      float ss = 0.0f;
+      for (int k = lane; k < gu; k += kWave) ss += ps[j * gu + k];
+      ss = seg_sum(ss, kWave);
+      const float r = 1.0f / sqrtf(ss / (float)g.gs + g.eps);
+      if (lane == 0) {
+        s_r[wave][j] = r;
+        if (rstd) rstd[(int64_t)tok * ngr + j] = r;
+      }
+    }
+  } else {
+    for (int j = lane; j < ngr; j += kWave) {
+      float ss = 0.0f;
+      for (int k = 0; k < gu; ++k) ss += ps[j * gu + k];
+      const float r = 1.0f / sqrtf(ss / (float)g.gs + g.eps);
+      s_r[wave][j] = r;
+      if (rstd) rstd[(int64_t)tok * ngr + j] = r;
+    }
+  }
+  // (a wave's LDS accesses are performed in order: its reads below see its
+  // writes above)
+  for (int c = lane * 8; c < W; c += kStrip) {
+    const float r = s_r[wave][c / g.gs];
+    const f32x8 gv = load8<TO>(g, out, tok, c);
+    const f32x8 wv = Vec8<float>::load(w + c);
+    f32x8 ov;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ov[i] = gv[i] * r * wv[i];
+    store8<TO>(g, out, tok, c, ov);
+  }
+}
+
 // Backward statistics of groups wider than a strip: per (token, group), r and
 // mean(dxhat xhat) = r mean(dout w g).  One wave per (token, group).
 template <typename TI>
@@ -270,6 +319,17 @@ hipError_t launch_norm_fwd(const NormGeo& g, TArg y, TArg z, int in_dtype, const
       hipLaunchKernelGGL((k_norm_fwd<float, float>), grid, dim3(256), 0, s, g, y, z, w, out,
                          rstd);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_finish(const NormGeo& g, const float* psum, const float* w, TArg out,
+                              int out_dtype, float* rstd, hipStream_t s) {
+  if (g.ntok == 0) return hipSuccess;
+  dim3 grid((unsigned)((g.ntok + 3) / 4));
+  if (out_dtype == DT_BF16)
+    hipLaunchKernelGGL((k_norm_finish<bf16>), grid, dim3(256), 0, s, g, psum, w, out, rstd);
+  else
+    hipLaunchKernelGGL((k_norm_finish<float>), grid, dim3(256), 0, s, g, psum, w, out, rstd);
   return hipGetLastError();
 }
 

@@ -69,6 +69,7 @@ struct FusedLaunch {
   FusedPlan plan;
   float* edec;             // nr * U
   float* agg;              // nr * U * 64 * 16 * NT
+  float* psum = nullptr;   // gated RMSNorm fused in: ntok * U partial sums of g^2
   unsigned long long* trace = nullptr;  // SSD_FUSED_TRACE builds: kFusedTraceSlots per item
 };
 // Phase timestamps per (unit, range) item in SSD_FUSED_TRACE builds: [0] and
@@ -138,6 +139,12 @@ struct NormGeo {
 int norm_tiles(const NormGeo& g);  // rows of weight-gradient partials
 hipError_t launch_norm_fwd(const NormGeo& g, TArg y, TArg z, int in_dtype, const float* w,
                            TArg out, int out_dtype, float* rstd, hipStream_t s);
+// In place: out = g r weight, g the gated scan output already in `out`, r from
+// psum (ntok x (H P / 64) sums of g^2 per 64-channel block).  gs a multiple of
+// 64, H P / gs <= kNormFinishGroups.
+constexpr int kNormFinishGroups = 256;
+hipError_t launch_norm_finish(const NormGeo& g, const float* psum, const float* w, TArg out,
+                              int out_dtype, float* rstd, hipStream_t s);
 // part: norm_tiles * H * P floats; stats: ntok * (H P / gs) float2 (gs > 512 only)
 hipError_t launch_norm_bwd(const NormGeo& g, TArg y, TArg z, int in_dtype, const float* w,
                            TArg dout, TArg dy, TArg dz, float* dw, float* part, float2* stats,

@@ -83,6 +83,11 @@ class SsdComplexFwdArgs(ctypes.Structure):
                 ("final_states", ctypes.c_void_p)]
 
 
+class SsdNormArgs(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("group_size", ctypes.c_int32),
+                ("eps", ctypes.c_float), ("rstd", ctypes.c_void_p)]
+
+
 class SsdNormProblem(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32),
                 ("nheads", ctypes.c_int32), ("headdim", ctypes.c_int32),
@@ -93,7 +98,8 @@ _lib = None
 EXPORTS = ("ssd_problem_check", "ssd_num_chunks", "ssd_varlen_meta_len", "ssd_workspace_size",
            "ssd_varlen_chunk_meta", "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum",
            "ssd_bmm_chunk", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
-           "ssd_forward", "ssd_forward_fused_static",
+           "ssd_forward", "ssd_forward_fused_static", "ssd_forward_gated_norm",
+           "ssd_forward_gated_norm_workspace_size",
            "ssd_backward_workspace_size", "ssd_backward",
            "ssd_complex_problem_check", "ssd_complex_workspace_size", "ssd_complex_forward",
            "ssd_complex_chunk_state", "ssd_complex_state_passing", "ssd_complex_chunk_scan",
@@ -130,6 +136,10 @@ def lib():
         L.ssd_forward.argtypes = [P(SsdProblem), ctypes.c_int, P(SsdFwdArgs), vp,
                                   ctypes.c_size_t, vp]
         L.ssd_forward_fused_static.argtypes = [P(SsdProblem), P(SsdFwdArgs), vp]
+        L.ssd_forward_gated_norm_workspace_size.argtypes = [P(SsdProblem), P(SsdNormArgs),
+                                                            P(ctypes.c_size_t)]
+        L.ssd_forward_gated_norm.argtypes = [P(SsdProblem), P(SsdFwdArgs), P(SsdNormArgs), vp,
+                                             ctypes.c_size_t, vp]
         L.ssd_backward_workspace_size.argtypes = [P(SsdProblem), P(ctypes.c_size_t)]
         L.ssd_backward.argtypes = [P(SsdProblem), P(SsdBwdArgs), vp, ctypes.c_size_t, vp]
         L.ssd_complex_problem_check.argtypes = [P(SsdComplexProblem)]
@@ -151,7 +161,8 @@ def lib():
         for name in ("ssd_problem_check", "ssd_workspace_size", "ssd_varlen_chunk_meta",
                      "ssd_varlen_chunk_meta_host", "ssd_chunk_cumsum", "ssd_bmm_chunk",
                      "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan", "ssd_forward",
-                     "ssd_forward_fused_static",
+                     "ssd_forward_fused_static", "ssd_forward_gated_norm",
+                     "ssd_forward_gated_norm_workspace_size",
                      "ssd_backward_workspace_size", "ssd_backward",
                      "ssd_complex_problem_check", "ssd_complex_workspace_size",
                      "ssd_complex_forward", "ssd_complex_chunk_state",
@@ -502,6 +513,36 @@ def ssd_forward(x, B, C, dt, A, dt_bias=None, D=None, z=None, initial_states=Non
         dt_limit, state_dtype, out, out_dtype, final_states, algo, workspace, stream, input_dt)
     _check(lib().ssd_forward(ctypes.byref(prob.c()), ALGO[algo], ctypes.byref(a),
                              workspace.data_ptr(), workspace.numel(), _stream(stream)))
+    return out, final_states
+
+
+def ssd_forward_gated_norm(x, B, C, dt, A, weight, group_size, dt_bias=None, D=None, z=None,
+                           initial_states=None, cu_seqlens=None, eps=1e-5, dt_softplus=True,
+                           dt_limit=None, out=None, out_dtype=None, final_states=None,
+                           rstd=None, workspace=None, stream=None, input_dt=False):
+    """The fused forward with the gated RMSNorm in its epilogue
+    (ssd_forward_gated_norm): out = RMSNorm_group(y silu(z)) * weight.  Returns
+    (out, final_states)."""
+    prob = problem_from(x, B, 128, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
+                        dt_limit=dt_limit, input_dt=input_dt)
+    _check_fwd_inputs(prob, x, B, C, dt, A, dt_bias, D, z, initial_states, out, final_states)
+    _check_vec("weight", weight, prob.nheads * prob.headdim, x.device)
+    n = SsdNormArgs()
+    n.weight, n.group_size, n.eps, n.rstd = weight.data_ptr(), int(group_size), float(eps), _ptr(rstd)
+    need = ctypes.c_size_t(0)
+    _check(lib().ssd_forward_gated_norm_workspace_size(ctypes.byref(prob.c()), ctypes.byref(n),
+                                                       ctypes.byref(need)))
+    with _on(stream):
+        if out is None:
+            out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+        if final_states is None:
+            nseq = prob.nseq if prob.packed else prob.batch
+            final_states = torch.empty((nseq, prob.nheads, prob.headdim, prob.dstate),
+                                       dtype=torch.float32, device=x.device)
+        workspace = _workspace(int(need.value), workspace, x.device)
+    a = _fwd_args(prob, x, B, C, dt, A, dt_bias, D, z, initial_states, out, final_states)
+    _check(lib().ssd_forward_gated_norm(ctypes.byref(prob.c()), ctypes.byref(a), ctypes.byref(n),
+                                        workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return out, final_states
 
 
