@@ -19,15 +19,21 @@ as the pages write it.
 
 Only one GPU is used: --gpus above 1 exits with a message.
 
-Timing: W untimed steps, then K steps bracketed by torch.cuda.synchronize();
-wall time over the K steps gives `value`.  Inside the same timed region every
-kernel is bracketed by HIP events on the stream it runs on, which gives each
-kernel's average duration; the dominant one is reported against its roofline
-(algorithmic bytes per launch / average duration vs 8 TB/s HBM).
+Timing: W untimed steps, then K timed steps bracketed by torch.cuda.synchronize().
+Each timed step is preceded, outside its events, by a 512 MB write that evicts
+the inputs from L2 and the 256 MB MALL (they stay resident in HBM); the step
+and each launch in it are bracketed by HIP events on the stream they run on.
+`value` and `ms_per_step` come from the median step (cold); the same K steps
+back to back without the flush are reported as `warm`.  The dominant launch is
+reported against its roofline (algorithmic bytes per launch / median cold
+duration vs 8 TB/s HBM, and vs the achievable bandwidth of a 1 GiB copy
+measured in the same run: `measured_peaks`).  The fused forward is one call of
+two launches (range aggregates, then outputs); its call is the timed unit.
 
-Cold: after the timed region, --cold-steps forwards are timed one by one with
-HIP events, each preceded (outside the events) by a 512 MB write that evicts
-the inputs from L2 and the 256 MB MALL; their median is reported as `cold`.
+'configs' carries the other workloads (Granite dims, the packed batch, long
+context fused and staged with fp32 / bf16 states, staged Nemotron-Nano with
+both state dtypes), each cold and warm; 'gated_norm_fused' the forward with
+the gated RMSNorm fused in against the two calls it replaces.
 
 cpu_baseline: the fp64 oracle (C, OpenMP) on the host's cores over the same
 workload, timed separately (a reported baseline, not the target).
@@ -85,8 +91,9 @@ def parse():
                          "default timed for 20 steps in a 'complex_fwd' object)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="repeat the oracle until this much CPU time has been spent (min 3 runs)")
-    ap.add_argument("--cold-steps", type=int, default=10,
-                    help="event-timed forwards each preceded by a 512 MB cache flush")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the other workloads (Granite, packed, long context, staged "
+                         "state dtypes) reported in a 'configs' object")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="copy a 512 MiB device buffer once first (HBM counter calibration)")
     return ap.parse_args()
@@ -217,6 +224,165 @@ def environment(torch, ssd):
             "host_cores": os.cpu_count()}
 
 
+def measure_peaks(torch, dev):
+    """Achievable peaks on this device: HBM bandwidth of a 1 GiB device-to-device
+    copy (read + write bytes / time) and the dense bf16 matrix rate of an
+    8192^3 GEMM through torch (hipBLASLt).  Medians of 10 event-timed runs."""
+    src = torch.ones(2**28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+
+    def med(fn, n=10):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return float(np.median(ts))
+
+    copy_ms = med(lambda: dst.copy_(src))
+    gemm_ms = med(lambda: torch.matmul(a, b))
+    res = {"hbm_copy_GBps": round(2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1),
+           "bf16_gemm_TFLOPs": round(2 * 8192**3 / (gemm_ms * 1e-3) / 1e12, 1),
+           "note": "1 GiB device-to-device copy (read + write bytes); 8192^3 bf16 GEMM "
+                   "(torch.matmul); medians of 10 event-timed runs"}
+    del src, dst, a, b
+    return res
+
+
+class Forward:
+    """One forward configuration: inputs resident in HBM, preallocated outputs and
+    workspace, and the launches ssd_forward makes (the staged path's five stage
+    calls one by one, so each can be bracketed by events; the fused path as its
+    one call)."""
+
+    def __init__(self, torch, ssd, w, algo, state_dtype="f32", out_dtype="bf16", layout="xbc",
+                 input_dt=False, dev=None):
+        from mamba_ssd_chunked_scan_amd.inputs import make_inputs
+        self.w, self.algo, self.state_dtype, self.out_dtype = w, algo, state_dtype, out_dtype
+        self.input_dt = input_dt
+        dev = dev or torch.device("cuda:0")
+        inp = self.inp = make_inputs(w)
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        sdt = torch.float32 if state_dtype == "f32" else torch.bfloat16
+        odt = torch.bfloat16 if out_dtype == "bf16" else torch.float32
+
+        def up(a, dt=tdt):
+            return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
+
+        if layout == "xbc":
+            lead = inp.x.shape[:-2]
+            H, P, G, N = w.nheads, w.headdim, w.ngroups, w.dstate
+            buf = up(np.concatenate([inp.x.reshape(lead + (H * P,)),
+                                     inp.B.reshape(lead + (G * N,)),
+                                     inp.C.reshape(lead + (G * N,))], axis=-1))
+            x = buf[..., :H * P].unflatten(-1, (H, P))
+            B = buf[..., H * P:H * P + G * N].unflatten(-1, (G, N))
+            C = buf[..., H * P + G * N:].unflatten(-1, (G, N))
+        else:
+            x, B, C = up(inp.x), up(inp.B), up(inp.C)
+        dt, z = up(inp.dt), up(inp.z)
+        A, bias = up(inp.A, torch.float32), up(inp.dt_bias, torch.float32)
+        D = up(inp.D, torch.float32)
+        cu = (torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
+              if inp.cu_seqlens is not None else None)
+        self.t = dict(x=x, B=B, C=C, dt=dt, z=z, A=A, bias=bias, D=D, cu=cu)
+        prob = self.prob = ssd.problem_from(x, B, w.chunk_size, cu_seqlens=cu, state_dtype=sdt,
+                                            input_dt=input_dt)
+        K = self.K = prob.num_chunks()
+        out = self.out = torch.empty(x.shape, dtype=odt, device=dev)
+        nseq = prob.nseq if prob.packed else prob.batch
+        fin = self.fin = torch.empty((nseq, w.nheads, w.headdim, w.dstate), dtype=torch.float32,
+                                     device=dev)
+        self.ws = ws = torch.empty(max(prob.workspace_size(algo), 1), dtype=torch.uint8,
+                                   device=dev)
+        if algo == "staged":
+            cs = torch.empty((K, w.nheads, w.chunk_size), dtype=torch.float32, device=dev)
+            dtc = torch.empty_like(cs) if input_dt else None
+            cb = torch.empty((K, w.ngroups, w.chunk_size, w.chunk_size), dtype=torch.float32,
+                             device=dev)
+            st = torch.empty((K, w.nheads, w.headdim, w.dstate), dtype=sdt, device=dev)
+            if prob.packed:
+                prob.chunk_meta = torch.empty(prob.meta_len(), dtype=torch.int32, device=dev)
+            self.names = (["varlen_meta"] if prob.packed else []) + [
+                "chunk_cumsum", "bmm_chunk", "chunk_state", "state_passing", "chunk_scan"]
+            calls = {
+                "varlen_meta": lambda: ssd.ssd_varlen_chunk_meta(prob, prob.chunk_meta),
+                "chunk_cumsum": lambda: ssd.ssd_chunk_cumsum(prob, dt, A, bias, cs, dtc),
+                "bmm_chunk": lambda: ssd.ssd_bmm_chunk(prob, C, B, cb),
+                "chunk_state": lambda: ssd.ssd_chunk_state(prob, x, B, cs, st, dt_chunk=dtc),
+                "state_passing": lambda: ssd.ssd_state_passing(prob, st, cs, None, st, fin),
+                "chunk_scan": lambda: ssd.ssd_chunk_scan(prob, cb, x, C, cs, st, D, z, out,
+                                                         dt_chunk=dtc),
+            }
+            self.calls = [(n, calls[n]) for n in self.names]
+        else:
+            self.names = ["fused_fwd"]
+            self.calls = [("fused_fwd", lambda: ssd.ssd_forward(
+                x, B, C, dt, A, bias, D, z, None, cu, w.chunk_size, state_dtype=sdt, out=out,
+                final_states=fin, algo="fused", workspace=ws, input_dt=input_dt))]
+        sb = 4 if state_dtype == "f32" else 2
+        ob = 2 if out_dtype == "bf16" else 4
+        ib = 2 if w.dtype == "bf16" else 4
+        self.nb = stage_bytes(w, K, sb, ob, ib, input_dt)
+        self.nf = stage_flops(w, K)
+        self.path_bytes = sum(self.nb[n] for n in self.names)
+
+    def run(self, torch, steps, flush=None):
+        """`steps` forwards; each launch bracketed by HIP events, and the whole step
+        too.  With `flush` (a large device buffer), every step is preceded, outside
+        the events, by a write of it.  Returns (per-launch ms lists, step ms list)."""
+        per = {n: [] for n in self.names}
+        step_ms = []
+        for _ in range(steps):
+            if flush is not None:
+                flush.fill_(1.0)
+            evs = []
+            s0 = torch.cuda.Event(enable_timing=True)
+            s1 = torch.cuda.Event(enable_timing=True)
+            s0.record()
+            for n, fn in self.calls:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                evs.append((n, e0, e1))
+            s1.record()
+            torch.cuda.synchronize()
+            for n, e0, e1 in evs:
+                per[n].append(e0.elapsed_time(e1))
+            step_ms.append(s0.elapsed_time(s1))
+        return per, step_ms
+
+    def summary(self, torch, steps, warmup, flush):
+        for _ in range(warmup):
+            for _n, fn in self.calls:
+                fn()
+        torch.cuda.synchronize()
+        cper, cstep = self.run(torch, steps, flush)
+        wper, wstep = self.run(torch, steps, None)
+        med = lambda v: float(np.median(v))
+        cold, warm = med(cstep), med(wstep)
+        tok = self.w.tokens
+        res = {"algo": self.algo, "state_dtype": self.state_dtype, "out_dtype": self.out_dtype,
+               "cold_ms": round(cold, 5), "warm_ms": round(warm, 5),
+               "tokens_per_s": round(tok / (cold * 1e-3), 1),
+               "warm_tokens_per_s": round(tok / (warm * 1e-3), 1),
+               "algorithmic_bytes": self.path_bytes,
+               "hbm_frac": round(self.path_bytes / (cold * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        if len(self.names) > 1:
+            res["stages_cold_ms"] = {n: round(med(cper[n]), 5) for n in self.names}
+        return res, cper, wper, cstep, wstep
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -226,7 +392,7 @@ def main():
         sys.exit(2)
     import torch
     from mamba_ssd_chunked_scan_amd import ssd
-    from mamba_ssd_chunked_scan_amd.inputs import COMPLEX_WORKLOADS, WORKLOADS, make_inputs
+    from mamba_ssd_chunked_scan_amd.inputs import COMPLEX_WORKLOADS, WORKLOADS
 
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
@@ -238,7 +404,6 @@ def main():
     if args.seqlen is not None:
         import dataclasses
         w = dataclasses.replace(w, seqlen=args.seqlen)
-    inp = make_inputs(w)
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         src = torch.ones(512 * 2**20 // 4, dtype=torch.float32, device=dev)
@@ -246,117 +411,33 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
-    sdt = torch.float32 if args.state_dtype == "f32" else torch.bfloat16
-    odt = torch.bfloat16 if args.out_dtype == "bf16" else torch.float32
-
-    def up(a, dt=tdt):
-        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev, dt)
-
-    if args.layout == "xbc":
-        lead = inp.x.shape[:-2]
-        H, P, G, N = w.nheads, w.headdim, w.ngroups, w.dstate
-        buf = up(np.concatenate([inp.x.reshape(lead + (H * P,)), inp.B.reshape(lead + (G * N,)),
-                                 inp.C.reshape(lead + (G * N,))], axis=-1))
-        x = buf[..., :H * P].unflatten(-1, (H, P))
-        B = buf[..., H * P:H * P + G * N].unflatten(-1, (G, N))
-        C = buf[..., H * P + G * N:].unflatten(-1, (G, N))
-    else:
-        x, B, C = up(inp.x), up(inp.B), up(inp.C)
-    dt, z = up(inp.dt), up(inp.z)
-    A, bias = up(inp.A, torch.float32), up(inp.dt_bias, torch.float32)
-    D = up(inp.D, torch.float32)
-    cu = (torch.from_numpy(inp.cu_seqlens.astype(np.int32)).to(dev)
-          if inp.cu_seqlens is not None else None)
-
-    prob = ssd.problem_from(x, B, w.chunk_size, cu_seqlens=cu, state_dtype=sdt,
-                            input_dt=args.input_dt)
     algo = args.algo
     if algo == "auto":
         # the single-pass forward where it applies (bf16 inputs, d_state <= 128),
         # the staged one otherwise
         algo = "fused" if (w.dtype == "bf16" and w.dstate <= 128) else "staged"
-    K = prob.num_chunks()
-    out = torch.empty(x.shape, dtype=odt, device=dev)
-    nseq = prob.nseq if prob.packed else prob.batch
-    fin = torch.empty((nseq, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device=dev)
-    ws = torch.empty(max(prob.workspace_size(algo), 1), dtype=torch.uint8, device=dev)
+    fw = Forward(torch, ssd, w, algo, args.state_dtype, args.out_dtype, args.layout,
+                 args.input_dt, dev)
+    # a 512 MB write before each cold step evicts the inputs from L2 and the 256 MB MALL
+    flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
 
-    # stage buffers for the instrumented staged step (same kernels ssd_forward launches)
-    cs = torch.empty((K, w.nheads, w.chunk_size), dtype=torch.float32, device=dev)
-    dtc = torch.empty_like(cs) if args.input_dt else None
-    cb = torch.empty((K, w.ngroups, w.chunk_size, w.chunk_size), dtype=torch.float32, device=dev)
-    st = torch.empty((K, w.nheads, w.headdim, w.dstate), dtype=sdt, device=dev)
-    if prob.packed:
-        prob.chunk_meta = torch.empty(prob.meta_len(), dtype=torch.int32, device=dev)
-
-    if algo == "staged":
-        names = (["varlen_meta"] if prob.packed else []) + [
-            "chunk_cumsum", "bmm_chunk", "chunk_state", "state_passing", "chunk_scan"]
-
-        def launches():
-            if prob.packed:
-                yield "varlen_meta", lambda: ssd.ssd_varlen_chunk_meta(prob, prob.chunk_meta)
-            yield "chunk_cumsum", lambda: ssd.ssd_chunk_cumsum(prob, dt, A, bias, cs, dtc)
-            yield "bmm_chunk", lambda: ssd.ssd_bmm_chunk(prob, C, B, cb)
-            yield "chunk_state", lambda: ssd.ssd_chunk_state(prob, x, B, cs, st, dt_chunk=dtc)
-            yield "state_passing", lambda: ssd.ssd_state_passing(prob, st, cs, None, st, fin)
-            yield "chunk_scan", lambda: ssd.ssd_chunk_scan(prob, cb, x, C, cs, st, D, z, out,
-                                                           dt_chunk=dtc)
-    else:
-        names = ["fused_fwd"]
-
-        def launches():
-            yield "fused_fwd", lambda: ssd.ssd_forward(x, B, C, dt, A, bias, D, z, None, cu,
-                                                       w.chunk_size, state_dtype=sdt, out=out,
-                                                       final_states=fin, algo="fused",
-                                                       workspace=ws, input_dt=args.input_dt)
-
-    def step(events=None):
-        for name, fn in launches():
-            if events is not None:
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn()
-                e1.record()
-                events.setdefault(name, []).append((e0, e1))
-            else:
-                fn()
-
-    # correctness smoke of the timed configuration against ssd_forward (same kernels)
+    # warm-up, then K timed steps (each after a flush, outside the events),
+    # bracketed by synchronisation; then K warm steps back to back
     for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    events = {}
+        for _n, fn in fw.calls:
+            fn()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(events)
+    cper, cstep = fw.run(torch, args.steps, flush)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-
-    per_kernel_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in events[n]])) for n in names}
-
-    # cold: a 512 MB write before each forward evicts L2 and the MALL
-    cold_ms = []
-    if args.cold_steps > 0:
-        flush = torch.empty(512 * 2**20 // 4, dtype=torch.float32, device=dev)
-        for _ in range(args.cold_steps):
-            flush.fill_(1.0)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            for _name, fn in launches():
-                fn()
-            e1.record()
-            torch.cuda.synchronize()
-            cold_ms.append(e0.elapsed_time(e1))
-        del flush
-    ms_per_step = wall * 1e3 / args.steps
+    wper, wstep = fw.run(torch, args.steps, None)
+    med = lambda v: float(np.median(v))
+    cold_ms, warm_ms = med(cstep), med(wstep)
+    per_cold = {n: med(cper[n]) for n in fw.names}
+    per_warm = {n: med(wper[n]) for n in fw.names}
     tokens = w.tokens
-    value = tokens * args.steps / wall
+    value = tokens / (cold_ms * 1e-3)
 
     # host submission: the time one whole forward call takes to return on the host
     # (every launch is asynchronous), each timed on an idle queue
@@ -364,26 +445,23 @@ def main():
     for _ in range(20):
         torch.cuda.synchronize()
         h0 = time.perf_counter()
-        for _name, fn in launches():
+        for _n, fn in fw.calls:
             fn()
         submit_us.append((time.perf_counter() - h0) * 1e6)
     torch.cuda.synchronize()
 
-    sbytes = 4 if sdt == torch.float32 else 2
-    obytes = 2 if odt == torch.bfloat16 else 4
-    ibytes = 2 if w.dtype == "bf16" else 4
-    nb = stage_bytes(w, K, sbytes, obytes, ibytes, args.input_dt)
-    nf = stage_flops(w, K)
-    dom = max((n for n in names if n in nb), key=lambda n: per_kernel_ms[n])
-    achieved = nb[dom] / (per_kernel_ms[dom] * 1e-3) / 1e9
-    stages = {n: {"ms": round(per_kernel_ms[n], 5),
-                  "GBps": (round(nb[n] / (per_kernel_ms[n] * 1e-3) / 1e9, 1) if n in nb else None),
-                  "hbm_frac": (round(nb[n] / (per_kernel_ms[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    peaks = measure_peaks(torch, dev)
+    nb, nf = fw.nb, fw.nf
+    dom = max((n for n in fw.names if n in nb), key=lambda n: per_cold[n])
+    achieved = nb[dom] / (per_cold[dom] * 1e-3) / 1e9
+    stages = {n: {"cold_ms": round(per_cold[n], 5), "warm_ms": round(per_warm[n], 5),
+                  "GBps": (round(nb[n] / (per_cold[n] * 1e-3) / 1e9, 1) if n in nb else None),
+                  "hbm_frac": (round(nb[n] / (per_cold[n] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
                                if n in nb else None),
-                  "mfma_TFLOPs": (round(nf[n] / (per_kernel_ms[n] * 1e-3) / 1e12, 1)
+                  "mfma_TFLOPs": (round(nf[n] / (per_cold[n] * 1e-3) / 1e12, 1)
                                   if nf.get(n) else None)}
-              for n in names}
-    roof_time_ms = sum(nb[n] for n in names if n in nb) / (HBM_PEAK_GBS * 1e9) * 1e3
+              for n in fw.names}
+    roof_time_ms = fw.path_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
 
     traffic_key = (f"{w.name}_{algo}_{args.state_dtype}state_{args.out_dtype}out_{args.layout}"
                    + ("_inputdt" if args.input_dt else ""))
@@ -394,12 +472,17 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(cold_ms, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic",
+        "timing": ("value and ms_per_step: median of K event-timed forwards, each preceded "
+                   "(outside the events) by a 512 MB write that evicts L2 and the MALL; the "
+                   "inputs stay resident in HBM.  'warm': the same K forwards back to back "
+                   f"without the flush.  Wall time of the K cold steps: {wall:.3f} s"),
+        "warm": {"ms_median": round(warm_ms, 5), "value": round(tokens / (warm_ms * 1e-3), 1)},
         "config": {
             "workload": f"{w.name}: SSD forward, batch {w.batch}, seq {w.seqlen}, "
                         f"{w.nheads} heads x {w.headdim}, d_state {w.dstate}, "
@@ -413,31 +496,46 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": dom,
+            "kernel": dom + (" (the call: range-aggregate and output launches)"
+                             if dom == "fused_fwd" else ""),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(dom, traffic_key),
             "bytes_per_launch": nb[dom],
-            "avg_launch_ms": round(per_kernel_ms[dom], 5),
+            "avg_launch_ms": round(per_cold[dom], 5),
+            "achievable_peak": peaks["hbm_copy_GBps"],
+            "frac_of_achievable": round(achieved / peaks["hbm_copy_GBps"], 4),
         },
         "stages": stages,
-        "path_roofline_frac": round(roof_time_ms / ms_per_step, 4),
+        "path_roofline_frac": round(roof_time_ms / cold_ms, 4),
+        "measured_peaks": peaks,
+        "mfma": {"useful_TFLOPs": round(nf[dom] / (per_cold[dom] * 1e-3) / 1e12, 1),
+                 "frac_of_published": round(nf[dom] / (per_cold[dom] * 1e-3) / 1e12
+                                            / BF16_PEAK_TFLOPS, 4),
+                 "frac_of_achievable": round(nf[dom] / (per_cold[dom] * 1e-3) / 1e12
+                                             / peaks["bf16_gemm_TFLOPs"], 4),
+                 "note": "useful causal matrix flops (no hi/lo second pass); a diagnostic: "
+                         "the path is bound by HBM bytes at these shapes"} if nf.get(dom) else None,
         "host_submit_us": round(float(np.median(submit_us)), 1),
-        "cold": ({"ms_median": round(float(np.median(cold_ms)), 5),
-                  "value": round(tokens / (float(np.median(cold_ms)) * 1e-3), 1),
-                  "steps": len(cold_ms),
-                  "note": "median of event-timed forwards, each after a 512 MB cache flush"}
-                 if cold_ms else None),
         "gpu": torch.cuda.get_device_name(0),
         "env": environment(torch, ssd),
     }
-    if args.backward:
-        result["fwd_bwd"] = time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu,
-                                          ms_per_step)
+    del fw
+    if args.configs and args.workload == "nemotron" and args.seqlen is None:
+        result["configs"] = other_configs(args, torch, ssd, flush)
     if args.norm:
         result["gated_norm"] = time_norm(args, w, ssd, dev)
+        if w.dtype == "bf16" and w.dstate <= 128 and w.headdim % 64 == 0:
+            result["gated_norm_fused"] = time_norm_fused(args, w, ssd, torch, flush)
+    if args.backward:
+        fw2 = Forward(torch, ssd, w, algo, args.state_dtype, args.out_dtype, args.layout,
+                      args.input_dt, dev)
+        t = fw2.t
+        result["fwd_bwd"] = time_backward(args, w, ssd, t["x"], t["B"], t["C"], t["dt"], t["A"],
+                                          t["bias"], t["D"], t["z"], t["cu"], cold_ms)
+        del fw2
     if args.complex:
         from mamba_ssd_chunked_scan_amd.inputs import COMPLEX_WORKLOADS
         cx = measure_complex(args, COMPLEX_WORKLOADS["complex_434m"], steps=20,
@@ -446,8 +544,90 @@ def main():
                                                     "steps", "config", "roofline", "stages",
                                                     "path_roofline_frac")}
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_seconds)
+        from mamba_ssd_chunked_scan_amd.inputs import make_inputs
+        result["cpu_baseline"] = cpu_baseline(w, make_inputs(w), args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def other_configs(args, torch, ssd, flush):
+    """The other workloads the pages time, each cold (median of 10 forwards after a
+    flush) and warm: Granite-style (vLLM PR 27299's SSD microbenchmark dims, seq
+    4096), the packed 8-sequence Nemotron-Nano batch, long context (seq 65536,
+    chunk 256; fused, and staged with fp32 and bf16 per-chunk states), and the
+    staged Nemotron-Nano path with both state dtypes."""
+    from mamba_ssd_chunked_scan_amd.inputs import WORKLOADS
+    out = {}
+    for key, name, algo, sd in [("granite_fused", "granite", "fused", "f32"),
+                                ("nemotron_varlen_fused", "nemotron_varlen", "fused", "f32"),
+                                ("longctx_fused", "longctx", "fused", "f32"),
+                                ("longctx_staged_f32state", "longctx", "staged", "f32"),
+                                ("longctx_staged_bf16state", "longctx", "staged", "bf16"),
+                                ("nemotron_staged_f32state", "nemotron", "staged", "f32"),
+                                ("nemotron_staged_bf16state", "nemotron", "staged", "bf16")]:
+        w = WORKLOADS[name]
+        fw = Forward(torch, ssd, w, algo, sd, "bf16", "xbc", False)
+        res = fw.summary(torch, 10, 3, flush)[0]
+        res["workload"] = (f"{w.name}: batch {w.batch}, seq {w.seqlen}, {w.nheads} heads x "
+                           f"{w.headdim}, d_state {w.dstate}, {w.ngroups} groups, chunk "
+                           f"{w.chunk_size}" + (f", {w.nseq} packed sequences" if w.nseq else ""))
+        out[key] = res
+        del fw
+        torch.cuda.empty_cache()
+    return out
+
+
+def time_norm_fused(args, w, ssd, torch, flush):
+    """The forward with the gated RMSNorm fused in (ssd_forward_gated_norm, groups of
+    H P / G channels) against the two calls it replaces (ssd_forward without the
+    gate, then ssd_gated_rmsnorm_fwd), cold (each after a flush) and warm."""
+    fw = Forward(torch, ssd, w, "fused", "f32", "bf16", "xbc", False)
+    t = fw.t
+    H, P = w.nheads, w.headdim
+    gs = H * P // w.ngroups
+    wt = torch.ones(H * P, device=t["x"].device)
+    # the fused workspace plus the per-(token, 64-channel block) sums of squares
+    ws_n = torch.empty(fw.prob.workspace_size("fused") + 4 * w.tokens * (H * P // 64) + 256,
+                       dtype=torch.uint8, device=t["x"].device)
+    y = torch.empty_like(fw.out)
+
+    def fused():
+        ssd.ssd_forward_gated_norm(t["x"], t["B"], t["C"], t["dt"], t["A"], wt, gs, t["bias"],
+                                   t["D"], t["z"], None, t["cu"], out=fw.out,
+                                   final_states=fw.fin, workspace=ws_n)
+
+    def two_calls():
+        ssd.ssd_forward(t["x"], t["B"], t["C"], t["dt"], t["A"], t["bias"], t["D"], None, None,
+                        t["cu"], w.chunk_size, out=y, final_states=fw.fin, algo="fused",
+                        workspace=fw.ws)
+        ssd.ssd_gated_rmsnorm_fwd(y, t["z"], wt, gs, out=fw.out)
+
+    def timed(fn, n, cold):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            if cold:
+                flush.fill_(1.0)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return round(float(np.median(ts)), 5)
+
+    n = max(10, args.steps // 5)
+    res = {"group_size": gs,
+           "fused_cold_ms": timed(fused, n, True), "fused_warm_ms": timed(fused, n, False),
+           "two_calls_cold_ms": timed(two_calls, n, True),
+           "two_calls_warm_ms": timed(two_calls, n, False),
+           "bytes_not_moved": 2 * 2 * w.tokens * H * P,
+           "note": "fused: ssd_forward_gated_norm; two calls: ssd_forward (no gate) then "
+                   "ssd_gated_rmsnorm_fwd (y and z read again); medians of event-timed calls"}
+    del fw
+    return res
 
 
 def time_norm(args, w, ssd, dev):
