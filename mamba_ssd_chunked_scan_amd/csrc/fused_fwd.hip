@@ -768,6 +768,7 @@ __global__ __launch_bounds__(kAggThreads, 2) void k_fused_agg(FusedArgs a) {
   __shared__ __align__(16) bf16 s_x[FC * XLD];
   __shared__ __align__(16) bf16 s_b[FC * BLD];
   __shared__ __align__(16) float s_w[NW][FC];
+  __shared__ __align__(16) uint32_t s_dt[FC];
 
   const Geo& g = a.g;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -819,39 +820,45 @@ __global__ __launch_bounds__(kAggThreads, 2) void k_fused_agg(FusedArgs a) {
 
   struct Stage {
     u32x4 x[XV], b[BV];
-    uint32_t dt[2];
+    uint32_t dt;            // raw bits of token (thread % 128)'s dt
   };
   const bool dims_full = pw == 64 && g.N == NMAX;
+  // Offsets are 32-bit element counts on a uniform base (scalar-base loads);
+  // dt goes last, so that no address register of the x and B loads is ever
+  // paired with a pending dt load (which would make the wave wait for it, and
+  // with it for every older load: the prefetch would be lost).
+  const uint32_t xs1 = (uint32_t)a.x.s1, bs1 = (uint32_t)a.B.s1, ds1 = (uint32_t)a.dt.s1;
   auto load = [&](Stage& st, const Chunk& c) {
-    const TDt* dbase = row_ptr<TDt>(a.dt, c.b, c.t0, h);
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-      st.dt[e] = raw_bits(*at(dbase, (uint32_t)(min(2 * lane + e, c.len - 1) * a.dt.s1)));
     const int t = opaque_tid();
     const bf16* xbase = row_ptr<bf16>(a.x, c.b, c.t0, h) + p0;
-    const int xrow = t / 8, xcol = (t % 8) * 8;
+    const uint32_t xrow = (uint32_t)t / 8, xcol = ((uint32_t)t % 8) * 8;
     const bf16* bbase = row_ptr<bf16>(a.B, c.b, c.t0, grp);
-    const int brow = t / BPR, bcol = (t % BPR) * 8;
-    constexpr int XROWS = kAggThreads / 8;
+    const uint32_t brow = (uint32_t)t / BPR, bcol = ((uint32_t)t % BPR) * 8;
+    constexpr uint32_t XROWS = kAggThreads / 8;
     if (dims_full && c.len == FC) {
+      const uint32_t xo = xrow * xs1 + xcol, bo = brow * bs1 + bcol;
+#pragma unroll
+      for (int k = 0; k < XV; ++k)
+        st.x[k] = *reinterpret_cast<const u32x4*>(at(xbase, xo + (uint32_t)k * XROWS * xs1));
+#pragma unroll
+      for (int k = 0; k < BV; ++k)
+        st.b[k] = *reinterpret_cast<const u32x4*>(at(bbase, bo + (uint32_t)k * BROWS * bs1));
+    } else {
+      const uint32_t lm = (uint32_t)c.len - 1;
+      const uint32_t xc = min(xcol, (uint32_t)pw - 8), bc = min(bcol, (uint32_t)g.N - 8);
 #pragma unroll
       for (int k = 0; k < XV; ++k)
         st.x[k] = *reinterpret_cast<const u32x4*>(
-            at(xbase, (uint32_t)((xrow + XROWS * k) * a.x.s1 + xcol)));
+            at(xbase, min(xrow + (uint32_t)k * XROWS, lm) * xs1 + xc));
 #pragma unroll
       for (int k = 0; k < BV; ++k)
         st.b[k] = *reinterpret_cast<const u32x4*>(
-            at(bbase, (uint32_t)((brow + BROWS * k) * a.B.s1 + bcol)));
-    } else {
-#pragma unroll
-      for (int k = 0; k < XV; ++k)
-        st.x[k] = *reinterpret_cast<const u32x4*>(at(
-            xbase, (uint32_t)(min(xrow + XROWS * k, c.len - 1) * a.x.s1 + min(xcol, pw - 8))));
-#pragma unroll
-      for (int k = 0; k < BV; ++k)
-        st.b[k] = *reinterpret_cast<const u32x4*>(at(
-            bbase, (uint32_t)(min(brow + BROWS * k, c.len - 1) * a.B.s1 + min(bcol, g.N - 8))));
+            at(bbase, min(brow + (uint32_t)k * BROWS, lm) * bs1 + bc));
     }
+    // dt travels with x and B (through LDS): it is consumed where they are,
+    // so no load of it is ever waited for on its own
+    const TDt* dbase = row_ptr<TDt>(a.dt, c.b, c.t0, h);
+    st.dt = raw_bits(*at(dbase, min((uint32_t)t % FC, (uint32_t)c.len - 1) * ds1));
   };
   auto stage = [&](const Stage& st, const Chunk& c) {
     const int t = opaque_tid();
@@ -867,14 +874,16 @@ __global__ __launch_bounds__(kAggThreads, 2) void k_fused_agg(FusedArgs a) {
     for (int k = 0; k < BV; ++k)
       *reinterpret_cast<u32x4*>(&s_b[(brow + BROWS * k) * BLD + bcol]) =
           (brow + BROWS * k < c.len && bcol < g.N) ? st.b[k] : zero;
+    if (t < FC) s_dt[t] = st.dt;
   };
   // every wave: the chunk's decay weights into its own row of s_w; returns
   // the chunk's total log-decay (base 2)
-  auto weights = [&](const Stage& st, const Chunk& c) {
+  auto weights = [&](const Chunk& c) {
     float av[2], dv[2];
+    const uint2 draw = *reinterpret_cast<const uint2*>(&s_dt[2 * lane]);
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-      const float uu = from_bits<TDt>(st.dt[e]) + bias;
+      const float uu = from_bits<TDt>(e ? draw.y : draw.x) + bias;
       float d = a.softplus ? softplus_fast(uu) : uu;
       if (a.clamp) d = fminf(fmaxf(d, a.dt_min), a.dt_max);
       const bool in = 2 * lane + e < c.len;
@@ -927,20 +936,27 @@ __global__ __launch_bounds__(kAggThreads, 2) void k_fused_agg(FusedArgs a) {
   auto step = [&](Stage& st, Chunk& c, int j) {
     __syncthreads();  // every wave is done with the previous chunk's tiles
     stage(st, c);
-    const float lam = weights(st, c);
+    const Chunk cur = c;
     get_chunk(g, min(j + 2, j1 - 1), c);  // refill with chunk j + 2 (or the last, unused)
     load(st, c);
     __syncthreads();
+    const float lam = weights(cur);
     const float e = fast_exp2(lam);
 #pragma unroll
     for (int nt = 0; nt < NTS; ++nt) carry[nt] *= e;
     E *= e;
     state_mma();
   };
-  for (int j = js; j < j1; j += 2) {
+  // whole pairs, then an odd last chunk: the loop is only ever re-entered
+  // after the second register set's step, so the wait counts at its head are
+  // exact (with the second step conditional inside the loop, the compiler
+  // drains every load there and the prefetch is lost)
+  int j = js;
+  for (; j + 1 < j1; j += 2) {
     step(sa, ca, j);
-    if (j + 1 < j1) step(sb, cb, j + 1);
+    step(sb, cb, j + 1);
   }
+  if (j < j1) step(sa, ca, j);
   if (pl < pw) {
     float* dst = a.agg + ((int64_t)r * a.U + u) * 64 * NMAX + (int64_t)pl * NMAX + q * 4;
 #pragma unroll
