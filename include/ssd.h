@@ -85,7 +85,10 @@ typedef enum ssd_dtype { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
 
 typedef enum ssd_algo {
   SSD_ALGO_STAGED = 0, /* the five stage kernels in sequence */
-  SSD_ALGO_FUSED = 1   /* one pass over the inputs: a reset kernel + one fused kernel */
+  SSD_ALGO_FUSED = 1,  /* one pass over the inputs (range aggregates, then outputs) */
+  SSD_ALGO_AUTO = 2    /* FUSED where it applies (bf16 x, B, C; dstate <= 128; with
+                          input_dt, delta >= 0 by construction), STAGED otherwise;
+                          its workspace size is the larger of the two */
 } ssd_algo;
 
 /* A strided tensor view.  Shape is implied by the argument's role. */

@@ -238,6 +238,14 @@ ssd_status check_state_ptr(const float* ptr, const char* name) {
   return SSD_OK;
 }
 
+// What the fused path takes (the rest of its checks are in fused_forward).
+bool fused_applies(const ssd_problem* p, const ssd_fwd_args* a) {
+  if (has_tokens(p) && a->x.dtype != SSD_BF16) return false;
+  if (p->dstate > 128) return false;
+  if (p->input_dt && !p->dt_softplus && !(p->dt_clamp && p->dt_min >= 0.0f)) return false;
+  return true;
+}
+
 // The single-pass forward (SSD_ALGO_FUSED); arguments common to both paths
 // were validated by ssd_forward.
 ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* workspace,
@@ -564,9 +572,10 @@ size_t ssd_varlen_meta_len(const ssd_problem* p) {
 ssd_status ssd_workspace_size(const ssd_problem* p, ssd_algo algo, size_t* bytes) {
   SSD_TRY(check_problem(p));
   if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
-  if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED)
+  if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED && algo != SSD_ALGO_AUTO)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
-  *bytes = algo == SSD_ALGO_FUSED ? fused_layout(p).total : staged_layout(p).total;
+  const size_t fu = fused_layout(p).total, st = staged_layout(p).total;
+  *bytes = algo == SSD_ALGO_FUSED ? fu : (algo == SSD_ALGO_STAGED ? st : (fu > st ? fu : st));
   return ok();
 }
 
@@ -705,8 +714,9 @@ ssd_status ssd_chunk_scan(const ssd_problem* p, const float* CB, ssd_tensor x, s
 ssd_status ssd_forward(const ssd_problem* p, ssd_algo algo, const ssd_fwd_args* a,
                        void* workspace, size_t ws_bytes, hipStream_t stream) {
   SSD_TRY(check_fwd_args(p, a));
-  if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED)
+  if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED && algo != SSD_ALGO_AUTO)
     return fail(SSD_ERR_UNSUPPORTED, "unknown algo %d", (int)algo);
+  if (algo == SSD_ALGO_AUTO) algo = fused_applies(p, a) ? SSD_ALGO_FUSED : SSD_ALGO_STAGED;
   if (algo == SSD_ALGO_FUSED) return fused_forward(p, a, workspace, ws_bytes, stream);
   return staged_run(p, a, nullptr, workspace, ws_bytes, stream);
 }

@@ -27,7 +27,7 @@ SSD_OK = 0
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_DTYPE",
           4: "SSD_ERR_STRIDE", 5: "SSD_ERR_UNSUPPORTED", 6: "SSD_ERR_WORKSPACE", 7: "SSD_ERR_HIP"}
 F32, BF16 = 0, 1
-ALGO = {"staged": 0, "fused": 1}
+ALGO = {"staged": 0, "fused": 1, "auto": 2}
 
 
 class SSDError(RuntimeError):

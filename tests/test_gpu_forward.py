@@ -21,16 +21,26 @@ ALGOS = ["staged", "fused"]
 
 
 def run_gpu(inp, w, algo="staged", out_dtype=torch.float32, packed_xbc=False, **kw):
-    if algo == "fused" and w.dtype == "f32":
-        pytest.skip("the fused forward takes bf16 inputs (fp32 is rejected, tested below)")
-    if algo == "fused" and w.dstate > 128:
-        pytest.skip("the fused forward takes dstate <= 128 (larger is rejected, tested in "
-                    "test_gpu_fused.py)")
+    """One forward through the C ABI.  The fused path takes bf16 inputs and
+    dstate <= 128: for anything else it must refuse with SSD_ERR_UNSUPPORTED,
+    and SSD_ALGO_AUTO must then run the staged path (its result is returned and
+    checked like any other)."""
     dev = device_inputs(inp, in_dtype(w), packed_xbc=packed_xbc)
-    out, fin = ssd.ssd_forward(dev["x"], dev["B"], dev["C"], dev["dt"], dev["A"],
-                               dev["dt_bias"], dev["D"], dev["z"], dev["initial_states"],
-                               cu_seqlens=dev["cu_seqlens"], chunk_size=w.chunk_size,
-                               out_dtype=out_dtype, algo=algo, **kw)
+    call = lambda a: ssd.ssd_forward(dev["x"], dev["B"], dev["C"], dev["dt"], dev["A"],
+                                     dev["dt_bias"], dev["D"], dev["z"], dev["initial_states"],
+                                     cu_seqlens=dev["cu_seqlens"], chunk_size=w.chunk_size,
+                                     out_dtype=out_dtype, algo=a, **kw)
+    if algo == "fused" and (w.dtype == "f32" or w.dstate > 128):
+        with pytest.raises(ssd.SSDError) as e:
+            call("fused")
+        assert e.value.status == 5
+        out, fin = call("auto")
+        torch.cuda.synchronize()
+        ys, fs = call("staged")
+        torch.cuda.synchronize()
+        assert torch.equal(out, ys) and torch.equal(fin, fs)   # auto ran the staged path
+        return out, fin
+    out, fin = call(algo)
     torch.cuda.synchronize()
     return out, fin
 

@@ -120,11 +120,11 @@ def run_fwd(w, inp, algo, out_dtype=torch.float32, **kw):
 
 
 @pytest.mark.parametrize("name", sorted(CASES))
-@pytest.mark.parametrize("algo", ["staged", "fused"])
+@pytest.mark.parametrize("algo", ["staged", "fused", "auto"])
 def test_forward(name, algo):
     w = CASES[name]
     if algo == "fused" and w.dtype == "f32":
-        pytest.skip("the fused forward takes bf16 inputs")
+        algo = "auto"   # fused refuses fp32 inputs (tested in test_gpu_forward.py); auto routes
     inp = with_initial_states(make_inputs(w))
     ref = oracle_run(inp, input_dt=True)
     y, fin = run_fwd(w, inp, algo)
