@@ -687,32 +687,44 @@ def time_norm(args, w, ssd, dev):
 
 
 def time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu, fwd_ms):
-    """HIP-event time of ssd_backward (all gradients) on the same inputs, with
-    an upstream gradient drawn from N(0, 1); the forward+backward rate adds
-    the forward step time measured above."""
+    """HIP-event time of the backward (all gradients) on the same inputs, with
+    an upstream gradient drawn from N(0, 1): ssd_backward_ex with AUTO (the
+    per-chunk path where it applies) as the headline, the staged backward
+    beside it; the forward+backward rate adds the forward step time measured
+    above."""
     import torch
     g = torch.Generator(device=x.device).manual_seed(4)
     dout = torch.randn(x.shape, generator=g, device=x.device, dtype=torch.float32)
     prob = ssd.problem_from(x, B, w.chunk_size, cu_seqlens=cu, input_dt=args.input_dt)
-    ws = torch.empty(prob.backward_workspace_size(), dtype=torch.uint8, device=x.device)
+    fused = x.dtype == torch.bfloat16 and w.headdim == 64 and w.dstate <= 128
 
-    def bwd():
-        return ssd.ssd_backward(x, B, C, dt, A, dout, dt_bias=bias, D=D, z=z, cu_seqlens=cu,
-                                chunk_size=w.chunk_size, workspace=ws, input_dt=args.input_dt)
+    def timed(algo):
+        ws = torch.empty(max(prob.backward_workspace_size(algo, x.dtype), 1), dtype=torch.uint8,
+                         device=x.device)
 
-    for _ in range(max(2, args.warmup // 5)):
-        bwd()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(max(5, args.steps // 5)):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        bwd()
-        e1.record()
+        def bwd():
+            return ssd.ssd_backward(x, B, C, dt, A, dout, dt_bias=bias, D=D, z=z, cu_seqlens=cu,
+                                    chunk_size=w.chunk_size, workspace=ws,
+                                    input_dt=args.input_dt, algo=algo)
+
+        for _ in range(max(2, args.warmup // 5)):
+            bwd()
         torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    bms = float(np.median(times))
+        times = []
+        for _ in range(max(5, args.steps // 5)):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bwd()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        n = ws.numel()
+        del ws
+        return float(np.median(times)), n, len(times)
+
+    bms, wsb, nst = timed("auto")
+    sms, swsb, _ = timed("staged") if fused else (bms, wsb, nst)
     # the backward's algorithmic bytes: read x, B, C, dt, z (input dtype) and dout
     # (fp32); write dx, dB, dC, ddt, dz (fp32); per-head vectors are negligible
     tok = w.batch * w.seqlen
@@ -721,14 +733,17 @@ def time_backward(args, w, ssd, x, B, C, dt, A, bias, D, z, cu, fwd_ms):
     zb = tok * H * P if w.has_z else 0
     alg = (e * (tok * H * P + 2 * tok * G * N + tok * H + zb) + 4 * tok * H * P
            + 4 * (tok * H * P + 2 * tok * G * N + tok * H + zb))
-    return {"bwd_ms": round(bms, 5), "fwd_ms": round(fwd_ms, 5),
+    return {"algo": "fused (per-chunk)" if fused else "staged",
+            "bwd_ms": round(bms, 5), "fwd_ms": round(fwd_ms, 5),
             "bwd_algorithmic_bytes": alg,
             "bwd_hbm_frac": round(alg / (bms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "fwd_bwd_ms": round(bms + fwd_ms, 5),
             "tokens_per_s": round(w.tokens / ((bms + fwd_ms) * 1e-3), 1),
-            "workspace_MB": round(ws.numel() / 1e6, 1), "steps": len(times),
-            "note": "median of event-timed backward calls, plus the "
-                    "timed forward step"}
+            "workspace_MB": round(wsb / 1e6, 1),
+            "staged_bwd_ms": round(sms, 5), "staged_workspace_MB": round(swsb / 1e6, 1),
+            "steps": nst,
+            "note": "median of event-timed backward calls (gradients allocated by the "
+                    "binding inside the events), plus the timed forward step"}
 
 
 def complex_stage_model(w):

@@ -396,6 +396,36 @@ ssd_status ssd_backward_workspace_size(const ssd_problem* p, size_t* bytes);
 ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* workspace,
                         size_t ws_bytes, hipStream_t stream);
 
+/* Bytes of workspace ssd_backward_ex needs for `algo` with inputs x, B, C of
+ * `in_dtype` (AUTO resolves exactly as the call does).  The per-chunk path
+ * (FUSED) needs ~450 MB at Nemotron-Nano size (8192 tokens, 64 heads x 64,
+ * d_state 128) against ~2.2 GB for STAGED. */
+ssd_status ssd_backward_ex_workspace_size(const ssd_problem* p, ssd_algo algo,
+                                          ssd_dtype in_dtype, size_t* bytes);
+
+/* ssd_backward with a choice of algorithm: the same gradients, arguments and
+ * conventions.
+ *   SSD_ALGO_STAGED  the staged backward above (every supported problem);
+ *   SSD_ALGO_FUSED   the per-chunk backward: two state passes at 128-token
+ *                    chunks give the state entering every chunk (forward
+ *                    recompute) and the gradient of the state leaving it (the
+ *                    adjoint scan); then one kernel per (chunk, head) forms y
+ *                    (for dz), dx and the step-size gradient, and one per
+ *                    (chunk, group, 64 state columns) forms dB and dC summed
+ *                    over the group's heads (the chunkwise forward of the SSD
+ *                    Reference, "Intra-chunk outputs and per-chunk states" and
+ *                    "Inter-chunk propagation", differentiated factor by
+ *                    factor).  Takes bf16 x, B, C, headdim 64 and dstate <= 128
+ *                    (a multiple of 8), with at least one token; returns
+ *                    SSD_ERR_UNSUPPORTED otherwise.  Same precision design
+ *                    (bf16 hi + lo operands, fp32 states and accumulation, fp64
+ *                    cumsum and step-size sums) and bit-identical results run to
+ *                    run.  In packed mode, tokens past cu_seqlens[nseq] belong
+ *                    to no sequence and get no gradient written.
+ *   SSD_ALGO_AUTO    FUSED where it applies, STAGED otherwise. */
+ssd_status ssd_backward_ex(const ssd_problem* p, const ssd_bwd_args* a, ssd_algo algo,
+                           void* workspace, size_t ws_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------- complex A */
 
 /* The complex-A SSD scan of Mamba-3-Lite (SSD Reference, "Math: the recurrence

@@ -745,8 +745,12 @@ ssd_status ssd_backward_workspace_size(const ssd_problem* p, size_t* bytes) {
   return ok();
 }
 
-ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* workspace,
-                        size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Arguments of both backward paths.
+ssd_status check_bwd_args(const ssd_problem* p, const ssd_bwd_args* a) {
   SSD_TRY(check_problem(p));
   if (!a) return fail(SSD_ERR_NULL, "args is NULL");
   const bool tok = has_tokens(p);
@@ -772,6 +776,21 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
   SSD_TRY(check_state_ptr(a->dinitial_states, "dinitial_states"));
   if (bwd_tokens(p) * (p->nheads > p->ngroups ? p->nheads : p->ngroups) > INT32_MAX)
     return fail(SSD_ERR_UNSUPPORTED, "backward: tokens x heads exceeds 2^31 - 1");
+  return SSD_OK;
+}
+
+ssd_status workspace_ok(const void* workspace, size_t ws_bytes, size_t need) {
+  if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
+  if (ws_bytes < need)
+    return fail(SSD_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SSD_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  return SSD_OK;
+}
+
+// The staged backward (SSD_ALGO_STAGED); arguments validated by the caller.
+ssd_status staged_backward(const ssd_problem* p, const ssd_bwd_args* a, void* workspace,
+                           size_t ws_bytes, hipStream_t stream) {
   const BwdWs w = bwd_layout(p);
   if (!workspace) return fail(SSD_ERR_WORKSPACE, "workspace is NULL");
   if (ws_bytes < w.total)
@@ -912,6 +931,219 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
               a->dA, a->ddt_bias, a->D ? a->dD : nullptr, a->dinitial_states, stream),
           "backward step gradients launch");
   return ok();
+}
+
+// ---- the per-chunk backward (SSD_ALGO_FUSED): the forward's carry-in states
+// and the adjoint's (two state passes at 128-token chunks), then the per-chunk
+// gradient kernels of bwd_chunk.hip
+
+bool bwd_fused_applies(const ssd_problem* p, ssd_dtype in_dtype) {
+  return has_tokens(p) && in_dtype == SSD_BF16 && p->headdim == 64 && p->dstate <= 128 &&
+         p->dstate % 8 == 0;
+}
+
+struct BwdChunkWs {
+  size_t fmeta, cs, dtc, st, delta, gd, dtr, dyr, Cr, mmeta, mcu, mcs, mst, gfirst, part, pdb,
+      pdc, total;
+};
+
+// The two problems of the per-chunk backward: the forward recompute at 128-token
+// chunks with fp32 states, and the adjoint scan (mirrored, packed form).
+ssd_problem chunk_fwd_problem(const ssd_problem* p) {
+  ssd_problem f = *p;
+  f.chunk_size = ssd::kBwdChunk;
+  f.state_dtype = SSD_F32;
+  f.chunk_meta = nullptr;
+  return f;
+}
+ssd_problem chunk_adj_problem(const ssd_problem* p) {
+  ssd_problem d = chunk_fwd_problem(p);
+  d.dt_softplus = 0;
+  d.dt_clamp = 0;
+  d.input_dt = 0;
+  return mirrored(d, p);
+}
+
+BwdChunkWs bwd_chunk_layout(const ssd_problem* p) {
+  BwdChunkWs w;
+  const ssd_problem fp = chunk_fwd_problem(p), mp = chunk_adj_problem(p);
+  const size_t nt = (size_t)bwd_tokens(p), H = p->nheads, P = p->headdim, N = p->dstate,
+               G = p->ngroups, ns = (size_t)bwd_nseq(p);
+  const size_t K = (size_t)num_chunks(&fp), Km = (size_t)num_chunks(&mp);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align256(bytes);
+    return o;
+  };
+  w.fmeta = take(p->nseq > 0 ? (ssd::kMetaHeader + 3 * K + p->nseq + 1) * sizeof(int32_t) : 0);
+  w.cs = take(K * H * ssd::kBwdChunk * sizeof(float));
+  w.dtc = take(p->input_dt ? K * H * ssd::kBwdChunk * sizeof(float) : 0);
+  w.st = take(K * H * P * N * sizeof(float));
+  w.delta = take(nt * H * sizeof(float));
+  w.gd = take(nt * H * sizeof(float));
+  w.dtr = take(nt * H * sizeof(float));
+  w.dyr = take(nt * H * P * sizeof(float));
+  w.Cr = take(nt * G * N * sizeof(float));
+  w.mmeta = take((ssd::kMetaHeader + 3 * Km + mp.nseq + 1) * sizeof(int32_t));
+  w.mcu = take((ns + 1) * sizeof(int32_t));
+  w.mcs = take(Km * H * ssd::kBwdChunk * sizeof(float));
+  w.mst = take(Km * H * P * N * sizeof(float));
+  w.gfirst = take(ns * H * P * N * sizeof(float));
+  w.part = take(K * H * 3 * sizeof(double));
+  const int splits = ssd::bwd_chunk_splits(p->nheads / p->ngroups);
+  w.pdb = take(splits > 1 ? (size_t)splits * nt * G * N * sizeof(float) : 0);
+  w.pdc = take(splits > 1 ? (size_t)splits * nt * G * N * sizeof(float) : 0);
+  w.total = off;
+  return w;
+}
+
+ssd_status chunk_backward(const ssd_problem* p, const ssd_bwd_args* a, void* workspace,
+                          size_t ws_bytes, hipStream_t stream) {
+  const BwdChunkWs w = bwd_chunk_layout(p);
+  SSD_TRY(workspace_ok(workspace, ws_bytes, w.total));
+  char* ws = static_cast<char*>(workspace);
+  auto f = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  const int H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups;
+  ssd_problem fp = chunk_fwd_problem(p), mp = chunk_adj_problem(p);
+  ssd::BwdGeo bg;
+  bg.ntok = (int)bwd_tokens(p);
+  bg.T = p->seqlen;
+  bg.nseq = bwd_nseq(p);
+  bg.H = H;
+  bg.P = P;
+  bg.G = G;
+  bg.N = N;
+  bg.hpg = H / G;
+  bg.cu = p->nseq > 0 ? p->cu_seqlens : nullptr;
+  const int in = dcode(a->x.dtype);
+  const ssd_tensor none = {nullptr, SSD_F32, {0, 0, 0}};
+
+  // 1. forward recompute at 128-token chunks: chunk table (packed), cumsum,
+  // chunk states, carry-in states (fp32)
+  int32_t* fmeta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws + w.fmeta) : nullptr;
+  const ssd::Geo gf = make_geo(&fp, fmeta);
+  if (fmeta)
+    SSD_HIP(ssd::launch_varlen_meta(gf, p->cu_seqlens, fmeta, stream), "chunk table launch");
+  float* dtc = p->input_dt ? f(w.dtc) : nullptr;
+  SSD_HIP(ssd::launch_chunk_cumsum(gf, targ(a->dt), dcode(a->dt.dtype), a->A, a->dt_bias,
+                                   p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, f(w.cs), dtc,
+                                   stream),
+          "backward cumsum launch");
+  SSD_HIP(ssd::launch_chunk_state(gf, targ(a->x), targ(a->B), in, f(w.cs), dtc, f(w.st),
+                                  ssd::DT_F32, stream),
+          "backward chunk state launch");
+  SSD_HIP(ssd::launch_state_passing(gf, f(w.st), ssd::DT_F32, f(w.cs), a->initial_states, f(w.st),
+                                    nullptr, stream),
+          "backward state passing launch");
+
+  // 2. step sizes, their derivatives and the adjoint's shifted, mirrored steps;
+  // dy = dout silu(z) mirrored; C mirrored
+  SSD_HIP(ssd::launch_bwd_steps(bg, targ(a->dt), dcode(a->dt.dtype), a->A, a->dt_bias,
+                                p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, f(w.delta),
+                                f(w.gd), f(w.dtr), stream),
+          "backward steps launch");
+  SSD_HIP(ssd::launch_bwd_gate(bg, targ(a->dout), dcode(a->dout.dtype), targ(a->z), in, nullptr,
+                               nullptr, f(w.dyr), targ(none), stream),
+          "backward gate launch");
+  SSD_HIP(ssd::launch_bwd_gather(bg, targ(a->C), in, G, N, 1, 1, f(w.Cr), stream),
+          "backward gather launch");
+
+  // 3. the adjoint scan's carry-in states: cumsum, chunk states, state passing
+  // on the mirrored sequences (dfinal as the initial state; its final state is
+  // G at each sequence's first token)
+  int32_t* mmeta = reinterpret_cast<int32_t*>(ws + w.mmeta);
+  int32_t* mcu = p->nseq > 0 ? const_cast<int32_t*>(p->cu_seqlens)
+                             : reinterpret_cast<int32_t*>(ws + w.mcu);
+  SSD_HIP(ssd::launch_bwd_mirror_meta(bg, ssd::kBwdChunk, (int)num_chunks(&mp), mmeta,
+                                      p->nseq > 0 ? nullptr : mcu, stream),
+          "backward chunk table launch");
+  mp.cu_seqlens = mcu;
+  const ssd::Geo gm = make_geo(&mp, mmeta);
+  ssd_tensor dtr;
+  dtr.data = f(w.dtr);
+  dtr.dtype = SSD_F32;
+  dtr.stride[0] = (int64_t)mp.seqlen * H;
+  dtr.stride[1] = H;
+  dtr.stride[2] = 1;
+  SSD_HIP(ssd::launch_chunk_cumsum(gm, targ(dtr), ssd::DT_F32, a->A, nullptr, 0, 0, 0.0f, 0.0f,
+                                   f(w.mcs), nullptr, stream),
+          "backward adjoint cumsum launch");
+  SSD_HIP(ssd::launch_chunk_state(gm, targ(scratch_view(f(w.dyr), &mp, H, P)),
+                                  targ(scratch_view(f(w.Cr), &mp, G, N)), ssd::DT_F32, f(w.mcs),
+                                  nullptr, f(w.mst), ssd::DT_F32, stream),
+          "backward adjoint chunk state launch");
+  SSD_HIP(ssd::launch_state_passing(gm, f(w.mst), ssd::DT_F32, f(w.mcs), a->dfinal_states,
+                                    f(w.mst), f(w.gfirst), stream),
+          "backward adjoint state passing launch");
+
+  // 4. the per-chunk gradients, then the per-head sums
+  ssd::BwdChunkLaunch l;
+  l.g = gf;
+  l.ntok = bg.ntok;
+  l.x = targ(a->x); l.B = targ(a->B); l.C = targ(a->C); l.z = targ(a->z);
+  l.dout = targ(a->dout);
+  l.dx = targ(a->dx); l.dz = targ(a->dz); l.dB = targ(a->dB); l.dC = targ(a->dC);
+  l.ddt = targ(a->ddt);
+  l.dout_dtype = dcode(a->dout.dtype);
+  l.A = a->A; l.D = a->D;
+  l.delta = f(w.delta); l.gd = f(w.gd);
+  l.hin = f(w.st); l.gmir = f(w.mst); l.gfirst = f(w.gfirst); l.dfinal = a->dfinal_states;
+  l.dyr = f(w.dyr);
+  l.part = reinterpret_cast<double*>(ws + w.part);
+  l.dh0 = a->dinitial_states;
+  l.input_dt = p->input_dt;
+  l.pdb = f(w.pdb);
+  l.pdc = f(w.pdc);
+  SSD_HIP(ssd::launch_bwd_chunk(l, stream), "backward chunk kernels launch");
+  SSD_HIP(ssd::launch_bwd_step_heads(bg, gf.K, reinterpret_cast<double*>(ws + w.part),
+                                     f(w.gfirst), a->dA, a->ddt_bias, a->D ? a->dD : nullptr,
+                                     a->dinitial_states, stream),
+          "backward per-head sums launch");
+  return ok();
+}
+
+size_t bwd_workspace(const ssd_problem* p, ssd_algo algo, ssd_dtype in_dtype) {
+  if (algo == SSD_ALGO_FUSED || (algo == SSD_ALGO_AUTO && bwd_fused_applies(p, in_dtype)))
+    return bwd_chunk_layout(p).total;
+  return bwd_layout(p).total;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* workspace,
+                        size_t ws_bytes, hipStream_t stream) {
+  SSD_TRY(check_bwd_args(p, a));
+  return staged_backward(p, a, workspace, ws_bytes, stream);
+}
+
+ssd_status ssd_backward_ex_workspace_size(const ssd_problem* p, ssd_algo algo,
+                                          ssd_dtype in_dtype, size_t* bytes) {
+  SSD_TRY(check_problem(p));
+  if (!bytes) return fail(SSD_ERR_NULL, "bytes is NULL");
+  if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED && algo != SSD_ALGO_AUTO)
+    return fail(SSD_ERR_SHAPE, "algo = %d is not STAGED, FUSED or AUTO", (int)algo);
+  if (!valid_dtype(in_dtype)) return fail(SSD_ERR_DTYPE, "in_dtype is not F32 or BF16");
+  *bytes = bwd_workspace(p, algo, in_dtype);
+  return ok();
+}
+
+ssd_status ssd_backward_ex(const ssd_problem* p, const ssd_bwd_args* a, ssd_algo algo,
+                           void* workspace, size_t ws_bytes, hipStream_t stream) {
+  SSD_TRY(check_bwd_args(p, a));
+  if (algo != SSD_ALGO_STAGED && algo != SSD_ALGO_FUSED && algo != SSD_ALGO_AUTO)
+    return fail(SSD_ERR_SHAPE, "algo = %d is not STAGED, FUSED or AUTO", (int)algo);
+  const ssd_dtype in = has_tokens(p) ? a->x.dtype : SSD_F32;
+  if (algo == SSD_ALGO_FUSED && !bwd_fused_applies(p, in))
+    return fail(SSD_ERR_UNSUPPORTED,
+                "the per-chunk backward takes bf16 x, B, C with tokens, headdim 64 and dstate "
+                "<= 128 (a multiple of 8); got headdim %d, dstate %d (use SSD_ALGO_STAGED)",
+                p->headdim, p->dstate);
+  if (algo == SSD_ALGO_FUSED || (algo == SSD_ALGO_AUTO && bwd_fused_applies(p, in)))
+    return chunk_backward(p, a, workspace, ws_bytes, stream);
+  return staged_backward(p, a, workspace, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -137,7 +137,8 @@ __global__ __launch_bounds__(256) void k_gather(BwdGeo q, TArg src, int dtype, i
 }
 
 // ---- the gate: dy = dout silu(z), dz = dout y silu'(z) (dy = dout without a
-// gate); dy is written in token order and mirrored
+// gate); dy is written in token order (when dy is given) and mirrored; dz only
+// when y is given
 __global__ __launch_bounds__(256) void k_gate(BwdGeo q, TArg dout, int dout_dtype, TArg z,
                                               int z_dtype, const float* y, float* dy,
                                               float* dy_rev, TArg dz) {
@@ -149,17 +150,20 @@ __global__ __launch_bounds__(256) void k_gate(BwdGeo q, TArg dout, int dout_dtyp
   f32x4 g = go;
   if (z.p) {
     const f32x4 zz = load4(z, z_dtype, q, tp, h, rw.c);
-    const f32x4 yy = *reinterpret_cast<const f32x4*>(y + o);
-    f32x4 d;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float s = sigmoid(zz[i]);
-      g[i] = go[i] * zz[i] * s;
-      d[i] = go[i] * yy[i] * (s * (1.0f + zz[i] * (1.0f - s)));
+    for (int i = 0; i < 4; ++i) g[i] = go[i] * zz[i] * sigmoid(zz[i]);
+    if (y) {
+      const f32x4 yy = *reinterpret_cast<const f32x4*>(y + o);
+      f32x4 d;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float s = sigmoid(zz[i]);
+        d[i] = go[i] * yy[i] * (s * (1.0f + zz[i] * (1.0f - s)));
+      }
+      *reinterpret_cast<f32x4*>(tok_row_f32(dz, q, tp, h) + rw.c) = d;
     }
-    *reinterpret_cast<f32x4*>(tok_row_f32(dz, q, tp, h) + rw.c) = d;
   }
-  *reinterpret_cast<f32x4*>(dy + o) = g;
+  if (dy) *reinterpret_cast<f32x4*>(dy + o) = g;
   *reinterpret_cast<f32x4*>(dy_rev + ((int64_t)mirror(q, tp) * q.H + h) * q.P + rw.c) = g;
 }
 
@@ -664,6 +668,14 @@ hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* CB
     if (e != hipSuccess) return e;
   }
   hipLaunchKernelGGL(k_step_heads, dim3(q.H), dim3(256), 0, s, q, gf.K, part, gfirst, dA,
+                     ddt_bias, dD, dh0);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_step_heads(const BwdGeo& q, int K, const double* part,
+                                 const float* gfirst, float* dA, float* ddt_bias, float* dD,
+                                 float* dh0, hipStream_t s) {
+  hipLaunchKernelGGL(k_step_heads, dim3(q.H), dim3(256), 0, s, q, K, part, gfirst, dA,
                      ddt_bias, dD, dh0);
   return hipGetLastError();
 }

@@ -117,6 +117,39 @@ hipError_t launch_bwd_step_grads(const BwdGeo& q, const Geo& gf, const float* CB
                                  TArg ddt, double* part, float* dA, float* ddt_bias, float* dD,
                                  float* dh0, hipStream_t s);
 
+// per head: dA, ddt_bias, dD from the chunks' shares in chunk order, and dh0 =
+// G_first for sequences without tokens
+hipError_t launch_bwd_step_heads(const BwdGeo& q, int K, const double* part,
+                                 const float* gfirst, float* dA, float* ddt_bias, float* dD,
+                                 float* dh0, hipStream_t s);
+
+// ---- per-chunk backward (bwd_chunk.hip): 128-token chunks, bf16 x, B, C,
+// headdim 64, d_state <= 128 (a multiple of 8)
+constexpr int kBwdChunk = 128;
+constexpr int kBwdHeadsPerSplit = 8;  // heads of a group per dB/dC workgroup
+int bwd_chunk_splits(int hpg);        // head splits of a group (partials when > 1)
+struct BwdChunkLaunch {
+  Geo g;                    // chunk geometry at 128 tokens (meta: its chunk table)
+  int ntok;
+  TArg x, B, C, z, dout, dx, dz, dB, dC, ddt;
+  int dout_dtype;
+  const float* A;
+  const float* D;
+  const float* delta;       // (ntok, H)
+  const float* gd;          // (ntok, H)
+  const float* hin;         // (K, H, P, N) forward carry-in states
+  const float* gmir;        // (K, H, P, N) adjoint carry-in states by mirrored chunk
+  const float* gfirst;      // (nseq, H, P, N)
+  const float* dfinal;      // or NULL
+  const float* dyr;         // (ntok, H, P) mirrored dy
+  double* part;             // (K, H, 3)
+  float* dh0;               // or NULL
+  int input_dt;
+  float* pdb;               // (splits, ntok, G, N) when bwd_chunk_splits(hpg) > 1
+  float* pdc;
+};
+hipError_t launch_bwd_chunk(const BwdChunkLaunch& l, hipStream_t s);
+
 // ---- complex-A forward (complex_fwd.hip): per-head complex B, C (g.G = g.H),
 // batch or packed mode (g.meta); x, B, C, out (complex) strides in complex elements,
 // dt and out (real) in floats.  states: K * H * P * N complex; lam: H * K floats (each

@@ -101,6 +101,7 @@ EXPORTS = ("ssd_problem_check", "ssd_num_chunks", "ssd_varlen_meta_len", "ssd_wo
            "ssd_forward", "ssd_forward_fused_static", "ssd_forward_gated_norm",
            "ssd_forward_gated_norm_workspace_size",
            "ssd_backward_workspace_size", "ssd_backward",
+           "ssd_backward_ex_workspace_size", "ssd_backward_ex",
            "ssd_complex_problem_check", "ssd_complex_workspace_size", "ssd_complex_forward",
            "ssd_complex_chunk_state", "ssd_complex_state_passing", "ssd_complex_chunk_scan",
            "ssd_gated_rmsnorm_fwd", "ssd_gated_rmsnorm_bwd_workspace_size",
@@ -142,6 +143,10 @@ def lib():
                                              ctypes.c_size_t, vp]
         L.ssd_backward_workspace_size.argtypes = [P(SsdProblem), P(ctypes.c_size_t)]
         L.ssd_backward.argtypes = [P(SsdProblem), P(SsdBwdArgs), vp, ctypes.c_size_t, vp]
+        L.ssd_backward_ex_workspace_size.argtypes = [P(SsdProblem), ctypes.c_int, ctypes.c_int,
+                                                     P(ctypes.c_size_t)]
+        L.ssd_backward_ex.argtypes = [P(SsdProblem), P(SsdBwdArgs), ctypes.c_int, vp,
+                                      ctypes.c_size_t, vp]
         L.ssd_complex_problem_check.argtypes = [P(SsdComplexProblem)]
         L.ssd_complex_workspace_size.argtypes = [P(SsdComplexProblem), P(ctypes.c_size_t)]
         L.ssd_complex_forward.argtypes = [P(SsdComplexProblem), P(SsdComplexFwdArgs), vp,
@@ -164,6 +169,7 @@ def lib():
                      "ssd_forward_fused_static", "ssd_forward_gated_norm",
                      "ssd_forward_gated_norm_workspace_size",
                      "ssd_backward_workspace_size", "ssd_backward",
+                     "ssd_backward_ex_workspace_size", "ssd_backward_ex",
                      "ssd_complex_problem_check", "ssd_complex_workspace_size",
                      "ssd_complex_forward", "ssd_complex_chunk_state",
                      "ssd_complex_state_passing", "ssd_complex_chunk_scan",
@@ -366,9 +372,16 @@ class Problem:
         _check(lib().ssd_workspace_size(ctypes.byref(self.c()), ALGO[algo], ctypes.byref(n)))
         return int(n.value)
 
-    def backward_workspace_size(self) -> int:
+    def backward_workspace_size(self, algo="staged", in_dtype=torch.bfloat16) -> int:
+        """Workspace bytes of ssd_backward (staged) or, with another algo, of
+        ssd_backward_ex for inputs of ``in_dtype``."""
         n = ctypes.c_size_t(0)
-        _check(lib().ssd_backward_workspace_size(ctypes.byref(self.c()), ctypes.byref(n)))
+        if algo == "staged":
+            _check(lib().ssd_backward_workspace_size(ctypes.byref(self.c()), ctypes.byref(n)))
+        else:
+            _check(lib().ssd_backward_ex_workspace_size(
+                ctypes.byref(self.c()), ALGO[algo], BF16 if in_dtype == torch.bfloat16 else F32,
+                ctypes.byref(n)))
         return int(n.value)
 
 
@@ -583,7 +596,7 @@ class Grads:
     dinitial_states: torch.Tensor
 
 
-def _bwd_alloc(prob, x, B, C, dt, D, z, nseq, workspace):
+def _bwd_alloc(prob, x, B, C, dt, D, z, nseq, workspace, algo):
     dev, f32 = x.device, torch.float32
     g = Grads(dx=torch.empty(x.shape, dtype=f32, device=dev),
               dB=torch.empty(B.shape, dtype=f32, device=dev),
@@ -595,15 +608,18 @@ def _bwd_alloc(prob, x, B, C, dt, D, z, nseq, workspace):
               dz=torch.empty(x.shape, dtype=f32, device=dev) if z is not None else None,
               dinitial_states=torch.empty((nseq, prob.nheads, prob.headdim, prob.dstate),
                                           dtype=f32, device=dev))
-    return g, _workspace(prob.backward_workspace_size(), workspace, dev)
+    return g, _workspace(prob.backward_workspace_size(algo, x.dtype), workspace, dev)
 
 
 def ssd_backward(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_states=None,
                  dfinal_states=None, cu_seqlens=None, chunk_size=128, dt_softplus=True,
-                 dt_limit=None, workspace=None, stream=None, input_dt=False) -> Grads:
+                 dt_limit=None, workspace=None, stream=None, input_dt=False,
+                 algo="auto") -> Grads:
     """Gradients of sum(dout * out) + sum(dfinal_states * final_states) with
     respect to every input of ``ssd_forward`` (same arguments and layouts);
-    all gradients are float32, allocated on ``stream`` like the workspace."""
+    all gradients are float32, allocated on ``stream`` like the workspace.
+    ``algo``: "staged" (ssd_backward), "fused" (the per-chunk backward of
+    ssd_backward_ex) or "auto" (fused where it applies)."""
     prob = problem_from(x, B, chunk_size, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
                         dt_limit=dt_limit, input_dt=input_dt)
     _check_fwd_inputs(prob, x, B, C, dt, A, dt_bias, D, z, initial_states)
@@ -612,7 +628,7 @@ def ssd_backward(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_sta
     _check_state("dfinal_states", dfinal_states, (nseq, prob.nheads, prob.headdim, prob.dstate),
                  x.device)
     with _on(stream):
-        g, workspace = _bwd_alloc(prob, x, B, C, dt, D, z, nseq, workspace)
+        g, workspace = _bwd_alloc(prob, x, B, C, dt, D, z, nseq, workspace, algo)
     a = SsdBwdArgs()
     pk = prob.packed
     a.x, a.B, a.C = tensor_arg(x, pk), tensor_arg(B, pk), tensor_arg(C, pk)
@@ -626,8 +642,12 @@ def ssd_backward(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_sta
     a.ddt, a.dz = tensor_arg(g.ddt, pk), tensor_arg(g.dz, pk)
     a.dA, a.ddt_bias, a.dD = g.dA.data_ptr(), g.ddt_bias.data_ptr(), _ptr(g.dD)
     a.dinitial_states = g.dinitial_states.data_ptr()
-    _check(lib().ssd_backward(ctypes.byref(prob.c()), ctypes.byref(a), workspace.data_ptr(),
-                              workspace.numel(), _stream(stream)))
+    if algo == "staged":
+        _check(lib().ssd_backward(ctypes.byref(prob.c()), ctypes.byref(a), workspace.data_ptr(),
+                                  workspace.numel(), _stream(stream)))
+    else:
+        _check(lib().ssd_backward_ex(ctypes.byref(prob.c()), ctypes.byref(a), ALGO[algo],
+                                     workspace.data_ptr(), workspace.numel(), _stream(stream)))
     return g
 
 
