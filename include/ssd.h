@@ -398,8 +398,9 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
 
 /* Bytes of workspace ssd_backward_ex needs for `algo` with inputs x, B, C of
  * `in_dtype` (AUTO resolves exactly as the call does).  The per-chunk path
- * (FUSED) needs ~450 MB at Nemotron-Nano size (8192 tokens, 64 heads x 64,
- * d_state 128) against ~2.2 GB for STAGED. */
+ * (FUSED) needs ~275 MB at Nemotron-Nano size (8192 tokens, 64 heads x 64,
+ * d_state 128: two fp32 states per chunk and head) against ~2.2 GB for
+ * STAGED. */
 ssd_status ssd_backward_ex_workspace_size(const ssd_problem* p, ssd_algo algo,
                                           ssd_dtype in_dtype, size_t* bytes);
 
@@ -408,8 +409,10 @@ ssd_status ssd_backward_ex_workspace_size(const ssd_problem* p, ssd_algo algo,
  *   SSD_ALGO_STAGED  the staged backward above (every supported problem);
  *   SSD_ALGO_FUSED   the per-chunk backward: two state passes at 128-token
  *                    chunks give the state entering every chunk (forward
- *                    recompute) and the gradient of the state leaving it (the
- *                    adjoint scan); then one kernel per (chunk, head) forms y
+ *                    recompute) and the gradient of the state leaving it (each
+ *                    chunk's own gradient of its entering state, then the
+ *                    state passing run backwards); then one kernel per (chunk,
+ *                    head) forms y
  *                    (for dz), dx and the step-size gradient, and one per
  *                    (chunk, group, 64 state columns) forms dB and dC summed
  *                    over the group's heads (the chunkwise forward of the SSD

@@ -934,8 +934,9 @@ ssd_status staged_backward(const ssd_problem* p, const ssd_bwd_args* a, void* wo
 }
 
 // ---- the per-chunk backward (SSD_ALGO_FUSED): the forward's carry-in states
-// and the adjoint's (two state passes at 128-token chunks), then the per-chunk
-// gradient kernels of bwd_chunk.hip
+// and the gradients of the states leaving every chunk (two state passes, the
+// second backwards, at 128-token chunks), then the per-chunk gradient kernels of
+// bwd_chunk.hip
 
 bool bwd_fused_applies(const ssd_problem* p, ssd_dtype in_dtype) {
   return has_tokens(p) && in_dtype == SSD_BF16 && p->headdim == 64 && p->dstate <= 128 &&
@@ -943,12 +944,10 @@ bool bwd_fused_applies(const ssd_problem* p, ssd_dtype in_dtype) {
 }
 
 struct BwdChunkWs {
-  size_t fmeta, cs, dtc, st, delta, gd, dtr, dyr, Cr, mmeta, mcu, mcs, mst, gfirst, part, pdb,
-      pdc, total;
+  size_t fmeta, cs, dtc, st, adj, delta, gd, part, pdb, pdc, total;
 };
 
-// The two problems of the per-chunk backward: the forward recompute at 128-token
-// chunks with fp32 states, and the adjoint scan (mirrored, packed form).
+// The forward recompute of the per-chunk backward: 128-token chunks, fp32 states.
 ssd_problem chunk_fwd_problem(const ssd_problem* p) {
   ssd_problem f = *p;
   f.chunk_size = ssd::kBwdChunk;
@@ -956,20 +955,13 @@ ssd_problem chunk_fwd_problem(const ssd_problem* p) {
   f.chunk_meta = nullptr;
   return f;
 }
-ssd_problem chunk_adj_problem(const ssd_problem* p) {
-  ssd_problem d = chunk_fwd_problem(p);
-  d.dt_softplus = 0;
-  d.dt_clamp = 0;
-  d.input_dt = 0;
-  return mirrored(d, p);
-}
 
 BwdChunkWs bwd_chunk_layout(const ssd_problem* p) {
   BwdChunkWs w;
-  const ssd_problem fp = chunk_fwd_problem(p), mp = chunk_adj_problem(p);
+  const ssd_problem fp = chunk_fwd_problem(p);
   const size_t nt = (size_t)bwd_tokens(p), H = p->nheads, P = p->headdim, N = p->dstate,
-               G = p->ngroups, ns = (size_t)bwd_nseq(p);
-  const size_t K = (size_t)num_chunks(&fp), Km = (size_t)num_chunks(&mp);
+               G = p->ngroups;
+  const size_t K = (size_t)num_chunks(&fp);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;
@@ -980,16 +972,9 @@ BwdChunkWs bwd_chunk_layout(const ssd_problem* p) {
   w.cs = take(K * H * ssd::kBwdChunk * sizeof(float));
   w.dtc = take(p->input_dt ? K * H * ssd::kBwdChunk * sizeof(float) : 0);
   w.st = take(K * H * P * N * sizeof(float));
+  w.adj = take(K * H * P * N * sizeof(float));
   w.delta = take(nt * H * sizeof(float));
   w.gd = take(nt * H * sizeof(float));
-  w.dtr = take(nt * H * sizeof(float));
-  w.dyr = take(nt * H * P * sizeof(float));
-  w.Cr = take(nt * G * N * sizeof(float));
-  w.mmeta = take((ssd::kMetaHeader + 3 * Km + mp.nseq + 1) * sizeof(int32_t));
-  w.mcu = take((ns + 1) * sizeof(int32_t));
-  w.mcs = take(Km * H * ssd::kBwdChunk * sizeof(float));
-  w.mst = take(Km * H * P * N * sizeof(float));
-  w.gfirst = take(ns * H * P * N * sizeof(float));
   w.part = take(K * H * 3 * sizeof(double));
   const int splits = ssd::bwd_chunk_splits(p->nheads / p->ngroups);
   w.pdb = take(splits > 1 ? (size_t)splits * nt * G * N * sizeof(float) : 0);
@@ -1004,20 +989,19 @@ ssd_status chunk_backward(const ssd_problem* p, const ssd_bwd_args* a, void* wor
   SSD_TRY(workspace_ok(workspace, ws_bytes, w.total));
   char* ws = static_cast<char*>(workspace);
   auto f = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  const int H = p->nheads, P = p->headdim, N = p->dstate, G = p->ngroups;
-  ssd_problem fp = chunk_fwd_problem(p), mp = chunk_adj_problem(p);
+  const int H = p->nheads, G = p->ngroups;
+  const ssd_problem fp = chunk_fwd_problem(p);
   ssd::BwdGeo bg;
   bg.ntok = (int)bwd_tokens(p);
   bg.T = p->seqlen;
   bg.nseq = bwd_nseq(p);
   bg.H = H;
-  bg.P = P;
+  bg.P = p->headdim;
   bg.G = G;
-  bg.N = N;
+  bg.N = p->dstate;
   bg.hpg = H / G;
   bg.cu = p->nseq > 0 ? p->cu_seqlens : nullptr;
   const int in = dcode(a->x.dtype);
-  const ssd_tensor none = {nullptr, SSD_F32, {0, 0, 0}};
 
   // 1. forward recompute at 128-token chunks: chunk table (packed), cumsum,
   // chunk states, carry-in states (fp32)
@@ -1037,47 +1021,14 @@ ssd_status chunk_backward(const ssd_problem* p, const ssd_bwd_args* a, void* wor
                                     nullptr, stream),
           "backward state passing launch");
 
-  // 2. step sizes, their derivatives and the adjoint's shifted, mirrored steps;
-  // dy = dout silu(z) mirrored; C mirrored
+  // 2. step sizes and their derivatives
   SSD_HIP(ssd::launch_bwd_steps(bg, targ(a->dt), dcode(a->dt.dtype), a->A, a->dt_bias,
                                 p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, f(w.delta),
-                                f(w.gd), f(w.dtr), stream),
+                                f(w.gd), nullptr, stream),
           "backward steps launch");
-  SSD_HIP(ssd::launch_bwd_gate(bg, targ(a->dout), dcode(a->dout.dtype), targ(a->z), in, nullptr,
-                               nullptr, f(w.dyr), targ(none), stream),
-          "backward gate launch");
-  SSD_HIP(ssd::launch_bwd_gather(bg, targ(a->C), in, G, N, 1, 1, f(w.Cr), stream),
-          "backward gather launch");
 
-  // 3. the adjoint scan's carry-in states: cumsum, chunk states, state passing
-  // on the mirrored sequences (dfinal as the initial state; its final state is
-  // G at each sequence's first token)
-  int32_t* mmeta = reinterpret_cast<int32_t*>(ws + w.mmeta);
-  int32_t* mcu = p->nseq > 0 ? const_cast<int32_t*>(p->cu_seqlens)
-                             : reinterpret_cast<int32_t*>(ws + w.mcu);
-  SSD_HIP(ssd::launch_bwd_mirror_meta(bg, ssd::kBwdChunk, (int)num_chunks(&mp), mmeta,
-                                      p->nseq > 0 ? nullptr : mcu, stream),
-          "backward chunk table launch");
-  mp.cu_seqlens = mcu;
-  const ssd::Geo gm = make_geo(&mp, mmeta);
-  ssd_tensor dtr;
-  dtr.data = f(w.dtr);
-  dtr.dtype = SSD_F32;
-  dtr.stride[0] = (int64_t)mp.seqlen * H;
-  dtr.stride[1] = H;
-  dtr.stride[2] = 1;
-  SSD_HIP(ssd::launch_chunk_cumsum(gm, targ(dtr), ssd::DT_F32, a->A, nullptr, 0, 0, 0.0f, 0.0f,
-                                   f(w.mcs), nullptr, stream),
-          "backward adjoint cumsum launch");
-  SSD_HIP(ssd::launch_chunk_state(gm, targ(scratch_view(f(w.dyr), &mp, H, P)),
-                                  targ(scratch_view(f(w.Cr), &mp, G, N)), ssd::DT_F32, f(w.mcs),
-                                  nullptr, f(w.mst), ssd::DT_F32, stream),
-          "backward adjoint chunk state launch");
-  SSD_HIP(ssd::launch_state_passing(gm, f(w.mst), ssd::DT_F32, f(w.mcs), a->dfinal_states,
-                                    f(w.mst), f(w.gfirst), stream),
-          "backward adjoint state passing launch");
-
-  // 4. the per-chunk gradients, then the per-head sums
+  // 3. the adjoint: each chunk's own gradient of its entering state, then the
+  // reverse state passing (dfinal in, the initial states' gradient out)
   ssd::BwdChunkLaunch l;
   l.g = gf;
   l.ntok = bg.ntok;
@@ -1088,17 +1039,20 @@ ssd_status chunk_backward(const ssd_problem* p, const ssd_bwd_args* a, void* wor
   l.dout_dtype = dcode(a->dout.dtype);
   l.A = a->A; l.D = a->D;
   l.delta = f(w.delta); l.gd = f(w.gd);
-  l.hin = f(w.st); l.gmir = f(w.mst); l.gfirst = f(w.gfirst); l.dfinal = a->dfinal_states;
-  l.dyr = f(w.dyr);
+  l.cs = f(w.cs); l.hin = f(w.st); l.adj = f(w.adj);
   l.part = reinterpret_cast<double*>(ws + w.part);
-  l.dh0 = a->dinitial_states;
   l.input_dt = p->input_dt;
   l.pdb = f(w.pdb);
   l.pdc = f(w.pdc);
+  SSD_HIP(ssd::launch_bwd_adj_state(l, stream), "backward adjoint chunk state launch");
+  SSD_HIP(ssd::launch_state_passing_rev(gf, f(w.adj), f(w.cs), a->dfinal_states,
+                                        a->dinitial_states, stream),
+          "backward reverse state passing launch");
+
+  // 4. the per-chunk gradients, then the per-head sums
   SSD_HIP(ssd::launch_bwd_chunk(l, stream), "backward chunk kernels launch");
-  SSD_HIP(ssd::launch_bwd_step_heads(bg, gf.K, reinterpret_cast<double*>(ws + w.part),
-                                     f(w.gfirst), a->dA, a->ddt_bias, a->D ? a->dD : nullptr,
-                                     a->dinitial_states, stream),
+  SSD_HIP(ssd::launch_bwd_step_heads(bg, gf.K, reinterpret_cast<double*>(ws + w.part), nullptr,
+                                     a->dA, a->ddt_bias, a->D ? a->dD : nullptr, nullptr, stream),
           "backward per-head sums launch");
   return ok();
 }

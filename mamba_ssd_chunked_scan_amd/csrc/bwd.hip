@@ -182,6 +182,7 @@ __global__ __launch_bounds__(256) void k_steps(BwdGeo q, TArg dt, int dt_dtype, 
     step_size(load_any(dt, dt_dtype, q, tp, h, 0) + bias, softplus, clamp, dt_min, dt_max, d, g);
     delta[i] = d;
     gd[i] = g;
+    if (!dt_rev) continue;
     int s0, s1;
     seq_of(q, tp, s0, s1);
     float dn = 0.0f;

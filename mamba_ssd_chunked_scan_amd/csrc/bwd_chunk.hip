@@ -2,10 +2,13 @@
 // (SSD_ALGO_FUSED of ssd_backward_ex).
 //
 // Once the state entering every 128-token chunk (Hin: the forward recompute's
-// carry-in) and the gradient of the state leaving it through later tokens (dS:
-// the adjoint scan's carry-in for the next chunk, decayed by the next token's
-// step, or dfinal at a sequence's last chunk) are known, what a chunk adds to
-// each gradient depends on that chunk alone.  The chunked forward of the SSD
+// carry-in) and the gradient of the state leaving it through later tokens (dS)
+// are known, what a chunk adds to each gradient depends on that chunk alone.
+// dS comes from the adjoint of the state passing: k_bwd_adj_state forms, per
+// chunk, the gradient its own tokens send to the state entering it,
+// U_j = sum_l exp(cs_l) dy_l (outer) C_l, and the reverse scan (state_passing.hip)
+// turns those into dS_j = exp(Lambda_{j+1}) dS_{j+1} + U_{j+1} (dfinal at a
+// sequence's last chunk) and the initial state's gradient.  The chunked forward of the SSD
 // Reference ("Intra-chunk outputs and per-chunk states", "Inter-chunk
 // propagation", "Readout"), differentiated factor by factor (section 6 asks for
 // exact gradients of every input), gives, with cs the chunk's inclusive cumsum
@@ -26,9 +29,9 @@
 // holds them; no two remaining terms cancel, so the step-size gradient stays
 // accurate under strong decay).
 //
-//   k_bwd_dx   one workgroup per (chunk, head): y and dz, dx, dcs -> ddt, the
-//              chunk's shares of dA, ddt_bias and dD, and dh0 at a sequence's
-//              first chunk;
+//   k_bwd_adj_state  one workgroup per (chunk, head): U_j;
+//   k_bwd_dx   one workgroup per (chunk, head): y and dz, dx, dcs -> ddt, and
+//              the chunk's shares of dA, ddt_bias and dD;
 //   k_bwd_dbc  one workgroup per (chunk, group, 64-column slab of N): dB and
 //              dC of the slab, summed over the group's heads in registers in
 //              head order (groups of more than 8 heads are split into runs of
@@ -144,13 +147,10 @@ struct BwdChunkArgs {
   const float* D;
   const float* delta;     // (ntok, H) step size
   const float* gd;        // (ntok, H) d(step)/du, 0 where the clamp is active
+  const float* cs;        // (K, H, 128) the forward's chunk cumsum (fp32)
   const float* hin;       // (K, H, P, N) forward carry-in states
-  const float* gmir;      // (K, H, P, N) adjoint carry-in states, by mirrored chunk
-  const float* gfirst;    // (nseq, H, P, N) adjoint state at each sequence's first token
-  const float* dfinal;    // (nseq, H, P, N) or NULL
-  const float* dyr;       // (ntok, H, P) dy, each sequence mirrored in time
+  float* adj;             // (K, H, P, N) U_j (k_bwd_adj_state), then dS_j
   double* part;           // (K, H, 3): the chunk's shares of dA, ddt_bias, dD
-  float* dh0;             // (nseq, H, P, N) or NULL
   int input_dt;
   int nsl;                // 64-column slabs of N
   int ntok;               // tokens on the packed axis
@@ -159,16 +159,12 @@ struct BwdChunkArgs {
   float* pdc;             // (nsplit, ntok, G, N) partial dC
 };
 
-// The chunk's sequence, its chunks [fi, li), and the gradient of the state
-// leaving chunk j through later tokens: exp(a_next) G_next (G_next the
-// adjoint carry-in of the mirrored chunk that mirrors chunk j: the adjoint
-// scan cuts each mirrored sequence so that its chunk boundaries fall on the
-// forward ones) or dfinal at the sequence's last chunk (NULL: zero).
+// The chunk, its sequence's chunks [fi, li), and the gradient of the state
+// leaving it through later tokens (dS_j, from the reverse state passing).
 struct ChunkCtx {
   Chunk c;
   int fi, li, jl, tp0;
-  const float* ds;        // (P, N) state gradient source, or NULL
-  float dscale;
+  const float* ds;        // (P, N)
 };
 __device__ __forceinline__ bool chunk_ctx(const BwdChunkArgs& a, int j, int h, ChunkCtx& x) {
   const Geo& g = a.g;
@@ -176,15 +172,7 @@ __device__ __forceinline__ bool chunk_ctx(const BwdChunkArgs& a, int j, int h, C
   seq_chunks(g, x.c.seq, x.fi, x.li);
   x.jl = j - x.fi;
   x.tp0 = x.c.b * g.T + x.c.t0;
-  const int64_t PN = (int64_t)g.P * g.N;
-  x.ds = nullptr;
-  x.dscale = 1.0f;
-  if (j < x.li - 1) {
-    x.ds = a.gmir + ((int64_t)(x.li - 1 - x.jl) * g.H + h) * PN;
-    x.dscale = fast_exp(a.delta[(int64_t)(x.tp0 + x.c.len) * g.H + h] * a.A[h]);
-  } else if (a.dfinal) {
-    x.ds = a.dfinal + ((int64_t)x.c.seq * g.H + h) * PN;
-  }
+  x.ds = a.adj + ((int64_t)j * g.H + h) * g.P * g.N;
   return true;
 }
 
@@ -205,6 +193,92 @@ __device__ __forceinline__ void stage_cumsum(const BwdChunkArgs& a, const ChunkC
   __syncthreads();
   if (tid >= kWave && tid < BC) s_cs[tid] += s_tmp[0];
   __syncthreads();
+}
+
+// ---------------------------------------------------------------- k_bwd_adj_state
+
+// U_j (P x N) = sum_l exp(cs_l) dy_l (outer) C_l: wave w owns p-tile w, all
+// n-tiles; exp(cs) dy (split hi + lo) and C staged in LDS in their natural
+// layout (tokens x columns) and read with the transpose read, as the token is
+// the reduction axis.
+template <int NT>
+__global__ __launch_bounds__(256, 2) void k_bwd_adj_state(BwdChunkArgs a) {
+  constexpr int NMAX = 16 * NT, CLD = NMAX + 8, BPR = NMAX / 8, ROWS = 256 / BPR;
+  __shared__ __align__(16) float s_e[BC];
+  __shared__ __align__(16) bf16 s_dyh[BC * TLD];
+  __shared__ __align__(16) bf16 s_dyl[BC * TLD];
+  __shared__ __align__(16) bf16 s_c[BC * CLD];
+  const Geo& g = a.g;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int r16 = lane % 16, q = lane / 16;
+  const int item = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int j = item / g.H, h = item % g.H, grp = h / g.hpg;
+  Chunk c;
+  if (!get_chunk(g, j, c)) return;
+  const int len = c.len;
+  if (tid < BC) s_e[tid] = tid < len ? fast_exp(a.cs[((int64_t)j * g.H + h) * BC + tid]) : 0.0f;
+  __syncthreads();
+  {
+    const int row0 = tid / 8, col = (tid % 8) * 8;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int l = row0 + 32 * k, lc = min(l, len - 1);
+      f32x8 v;
+      if (a.dout_bf16) {
+        const bf16* db = row_ptr<bf16>(a.dout, c.b, c.t0, h);
+        v = bf8_to_f32(*reinterpret_cast<const u32x4*>(at(db, (uint32_t)(lc * a.dout.s1 + col))));
+      } else {
+        v = load8f(at(row_ptr<float>(a.dout, c.b, c.t0, h), (uint32_t)(lc * a.dout.s1 + col)));
+      }
+      if (a.z.p) {
+        const f32x8 zz = bf8_to_f32(*reinterpret_cast<const u32x4*>(
+            at(row_ptr<bf16>(a.z, c.b, c.t0, h), (uint32_t)(lc * a.z.s1 + col))));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] *= zz[i] * sigmoidf(zz[i]);
+      }
+      const float e = s_e[l];  // (0 past the chunk's end)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] *= e;
+      const FragSplit sp = split_f32x8(v);
+      *reinterpret_cast<bf16x8*>(&s_dyh[l * TLD + col]) = sp.hi;
+      *reinterpret_cast<bf16x8*>(&s_dyl[l * TLD + col]) = sp.lo;
+    }
+    const bf16* cb = row_ptr<bf16>(a.C, c.b, c.t0, grp);
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < BC / ROWS; ++k) {
+      const int l = tid / BPR + ROWS * k, cc = (tid % BPR) * 8;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(
+          at(cb, (uint32_t)(min(l, len - 1) * a.C.s1 + min(cc, g.N - 8))));
+      *reinterpret_cast<u32x4*>(&s_c[l * CLD + cc]) = (l < len && cc < g.N) ? v : zero;
+    }
+  }
+  __syncthreads();
+  f32x4 acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = zero4();
+#pragma unroll
+  for (int kb = 0; kb < BC / 32; ++kb) {
+    const int k0 = kb * 32 + q * 8;
+    FragSplit af;
+    af.hi = lds_frag_tr(s_dyh, TLD, k0, k0 + 4, wave * 16);
+    af.lo = lds_frag_tr(s_dyl, TLD, k0, k0 + 4, wave * 16);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      FragBF bf;
+      bf.v = lds_frag_tr(s_c, CLD, k0, k0 + 4, nt * 16);
+      mma(acc[nt], af, bf);
+    }
+  }
+  float* dst = a.adj + ((int64_t)j * g.H + h) * g.P * g.N;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int n = nt * 16 + r16;
+    if (n < g.N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[(wave * 16 + q * 4 + i) * g.N + n] = acc[nt][i];
+    }
+  }
 }
 
 // ---------------------------------------------------------------- k_bwd_dx
@@ -309,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdChunkArgs a) {
   // <dS, Hin> (for the last token's Lambda term), fp64
   const float* hin = a.hin + ((int64_t)j * g.H + h) * PN;
   double ip = 0.0;
-  if (cx.ds) {
+  {
     for (int k = tid * 4; k < PN; k += 256 * 4) {
       const f32x4 u = *reinterpret_cast<const f32x4*>(cx.ds + k);
       const f32x4 v = *reinterpret_cast<const f32x4*>(hin + k);
@@ -467,11 +541,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdChunkArgs a) {
     f32x4 go_[8];
 #pragma unroll
     for (int st = 0; st < 8; ++st) go_[st] = zero4();
-    if (cx.ds) {
+    {
       const int pr = wave * 16 + r16;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const FragSplit df = state_frag(cx.ds, pr, kb, cx.dscale);
+        const FragSplit df = state_frag(cx.ds, pr, kb, 1.0f);
 #pragma unroll
         for (int st = 0; st < 8; ++st)
           mma(go_[st], df, as_frag(nrow_frag(bbase, a.B.s1, st * 16 + r16, kb)));
@@ -636,7 +710,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdChunkArgs a) {
   }
   __syncthreads();
   if (tid == 0)
-    s_dcs[len - 1] += (double)cx.dscale * exp_d(lam) * sip + s_tmp[4] + s_tmp[5];
+    s_dcs[len - 1] += (double)exp_d(lam) * sip + s_tmp[4] + s_tmp[5];
   __syncthreads();
   double sa = 0.0, sb = 0.0, suf = 0.0;
   if (tid < BC) {
@@ -663,14 +737,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdChunkArgs a) {
     pj[0] = sa;
     pj[1] = sb;
     pj[2] = dyx;
-  }
-  // ---- dh0 = exp(a_first) G_first at a sequence's first chunk
-  if (cx.jl == 0 && a.dh0) {
-    const float* gf = a.gfirst + ((int64_t)c.seq * g.H + h) * PN;
-    float* dst = a.dh0 + ((int64_t)c.seq * g.H + h) * PN;
-    const float e = fast_exp(a.delta[(int64_t)cx.tp0 * g.H + h] * Ah);
-    for (int64_t k = tid * 4; k < PN; k += 256 * 4)
-      *reinterpret_cast<f32x4*>(dst + k) = e * *reinterpret_cast<const f32x4*>(gf + k);
   }
 }
 
@@ -721,19 +787,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dbc(BwdChunkArgs a) {
   const int nw = min(64, g.N - n0);  // columns of this slab
   const int64_t PN = (int64_t)g.P * g.N;
   const int tp0 = c.b * g.T + c.t0;
-  // the sequence's span on the packed axis (for the mirrored rows of dy)
-  int s0, s1;
-  {
-    int fi, li;
-    seq_chunks(g, c.seq, fi, li);
-    Chunk cf, cl;
-    get_chunk(g, fi, cf);
-    get_chunk(g, li - 1, cl);
-    s0 = cf.b * g.T + cf.t0;
-    s1 = cl.b * g.T + cl.t0 + cl.len;
-  }
-  const int mir = s0 + s1 - 1;  // token tp's mirror: mir - tp
-
   // ---- B and C slabs of the chunk (rows past the chunk, columns past N: 0)
   {
     const bf16* bb = row_ptr<bf16>(a.B, c.b, c.t0, grp) + n0;
@@ -762,11 +815,23 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dbc(BwdChunkArgs a) {
       db[ui][nt] = zero4();
     }
 
-  // dy row fragment (8 consecutive p) of token l of the chunk, fp32, from the
-  // mirrored dy; rows past the chunk read as zero
+  // dy = dout silu(z): row fragment (8 consecutive p) of token l of the chunk;
+  // rows past the chunk read as zero
   auto dy_row = [&](int h, int l, int kp) -> f32x8 {
-    const int tm = mir - (tp0 + min(l, len - 1));
-    f32x8 v = load8f(a.dyr + ((int64_t)tm * g.H + h) * g.P + kp * 32 + q * 8);
+    const int lc = min(l, len - 1), col = kp * 32 + q * 8;
+    f32x8 v;
+    if (a.dout_bf16) {
+      const bf16* db = row_ptr<bf16>(a.dout, c.b, c.t0, h);
+      v = bf8_to_f32(*reinterpret_cast<const u32x4*>(at(db, (uint32_t)(lc * a.dout.s1 + col))));
+    } else {
+      v = load8f(at(row_ptr<float>(a.dout, c.b, c.t0, h), (uint32_t)(lc * a.dout.s1 + col)));
+    }
+    if (a.z.p) {
+      const f32x8 zz = bf8_to_f32(*reinterpret_cast<const u32x4*>(
+          at(row_ptr<bf16>(a.z, c.b, c.t0, h), (uint32_t)(lc * a.z.s1 + col))));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] *= zz[i] * sigmoidf(zz[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = l < len ? v[i] : 0.0f;
     return v;
@@ -867,7 +932,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dbc(BwdChunkArgs a) {
       }
     }
     __syncthreads();  // the Hin slab is dead: dS takes its place
-    stage_state(cx.ds, cx.dscale);
+    stage_state(cx.ds, 1.0f);
     __syncthreads();
 
     // ---- dB for s-tiles ltA, ltB: intra f_s sum_l (L o dy.x^T)_ls C_l (layout
@@ -974,18 +1039,17 @@ __global__ __launch_bounds__(256) void k_bwd_dbc_sum(BwdChunkArgs a) {
 
 int bwd_chunk_splits(int hpg) { return (hpg + kBwdHeadsPerSplit - 1) / kBwdHeadsPerSplit; }
 
-hipError_t launch_bwd_chunk(const BwdChunkLaunch& l, hipStream_t s) {
+namespace {
+BwdChunkArgs chunk_args(const BwdChunkLaunch& l) {
   const Geo& g = l.g;
-  const int Kr = g.K;  // chunk slots (dead slots in packed mode exit at once)
-  if (Kr <= 0) return hipSuccess;
   BwdChunkArgs a;
   a.g = g;
   a.x = l.x; a.B = l.B; a.C = l.C; a.z = l.z; a.dout = l.dout;
   a.dx = l.dx; a.dz = l.dz; a.dB = l.dB; a.dC = l.dC; a.ddt = l.ddt;
   a.dout_bf16 = l.dout_dtype == DT_BF16;
   a.A = l.A; a.D = l.D; a.delta = l.delta; a.gd = l.gd;
-  a.hin = l.hin; a.gmir = l.gmir; a.gfirst = l.gfirst; a.dfinal = l.dfinal; a.dyr = l.dyr;
-  a.part = l.part; a.dh0 = l.dh0;
+  a.cs = l.cs; a.hin = l.hin; a.adj = l.adj;
+  a.part = l.part;
   a.input_dt = l.input_dt;
   a.nsl = (g.N + 63) / 64;
   a.ntok = l.ntok;
@@ -993,6 +1057,24 @@ hipError_t launch_bwd_chunk(const BwdChunkLaunch& l, hipStream_t s) {
   a.hps = (g.hpg + a.nsplit - 1) / a.nsplit;
   a.pdb = l.pdb;
   a.pdc = l.pdc;
+  return a;
+}
+}  // namespace
+
+hipError_t launch_bwd_adj_state(const BwdChunkLaunch& l, hipStream_t s) {
+  const Geo& g = l.g;
+  if (g.K <= 0) return hipSuccess;
+  const BwdChunkArgs a = chunk_args(l);
+  const unsigned nx = (unsigned)((int64_t)g.K * g.H);
+  if (g.N <= 64) hipLaunchKernelGGL(k_bwd_adj_state<4>, dim3(nx), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_bwd_adj_state<8>, dim3(nx), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_chunk(const BwdChunkLaunch& l, hipStream_t s) {
+  const Geo& g = l.g;
+  if (g.K <= 0) return hipSuccess;  // (dead chunk slots in packed mode exit at once)
+  const BwdChunkArgs a = chunk_args(l);
   const unsigned nx = (unsigned)((int64_t)g.K * g.H);
   if (g.N <= 64) hipLaunchKernelGGL(k_bwd_dx<4>, dim3(nx), dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_bwd_dx<8>, dim3(nx), dim3(256), 0, s, a);

@@ -30,6 +30,13 @@ hipError_t launch_state_passing(const Geo& g, const void* states, int st_dtype,
                                 const float* cs, const float* h0, void* states_out,
                                 float* hfinal, hipStream_t s);
 
+// The adjoint of the state passing, chunks last to first, in place on adj (fp32
+// (K, H, P, N)): U_j (the gradient chunk j's tokens send to its entering state)
+// becomes dHout_j (the gradient of the state leaving chunk j through later
+// tokens); dh0 (nseq, H, P, N) or NULL receives the initial state's gradient.
+hipError_t launch_state_passing_rev(const Geo& g, float* adj, const float* cs,
+                                    const float* dfinal, float* dh0, hipStream_t s);
+
 // yoff (NULL to skip): also writes the inter-chunk part of
 // the output, exp(cs_l) C_l . h_in, before the skip and the gate, as (tokens,
 // H, P) fp32 on the packed axis.  st_trans (fp32 inputs only): the carry-in
@@ -137,17 +144,18 @@ struct BwdChunkLaunch {
   const float* D;
   const float* delta;       // (ntok, H)
   const float* gd;          // (ntok, H)
+  const float* cs;          // (K, H, 128) the forward's chunk cumsum
   const float* hin;         // (K, H, P, N) forward carry-in states
-  const float* gmir;        // (K, H, P, N) adjoint carry-in states by mirrored chunk
-  const float* gfirst;      // (nseq, H, P, N)
-  const float* dfinal;      // or NULL
-  const float* dyr;         // (ntok, H, P) mirrored dy
+  float* adj;               // (K, H, P, N): U_j, then (after the reverse state
+                            // passing) dS_j, the gradient of the state leaving chunk j
   double* part;             // (K, H, 3)
-  float* dh0;               // or NULL
   int input_dt;
   float* pdb;               // (splits, ntok, G, N) when bwd_chunk_splits(hpg) > 1
   float* pdc;
 };
+// U_j = sum_l exp(cs_l) dy_l (outer) C_l per (chunk, head) into adj
+hipError_t launch_bwd_adj_state(const BwdChunkLaunch& l, hipStream_t s);
+// dz, dx, ddt, the per-chunk shares of dA, ddt_bias, dD; then dB, dC
 hipError_t launch_bwd_chunk(const BwdChunkLaunch& l, hipStream_t s);
 
 // ---- complex-A forward (complex_fwd.hip): per-head complex B, C (g.G = g.H),
