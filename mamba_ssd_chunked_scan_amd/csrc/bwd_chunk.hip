@@ -63,7 +63,6 @@ namespace {
 
 constexpr int BC = 128;     // chunk length of these kernels
 constexpr int TLD = 72;     // bf16 per row of the x, dy, B, C and state tiles (64 + 8)
-constexpr int SLD = 68;     // floats per row of the staging tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ float exp_d(double v) { return fast_exp2((float)v * kLog2e); }
@@ -94,15 +93,6 @@ __device__ __forceinline__ float across_groups(float v) {
   v += __shfl_xor(v, 16, kWave);
   v += __shfl_xor(v, 32, kWave);
   return v;
-}
-
-__device__ __forceinline__ double block_sum4(double v, double* lds) {
-  v = wave_sum_f64(v);
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  __syncthreads();
-  if (lane == 0) lds[wave] = v;
-  __syncthreads();
-  return lds[0] + lds[1] + lds[2] + lds[3];
 }
 
 __device__ __forceinline__ float sigmoidf(float v) {
@@ -176,20 +166,24 @@ __device__ __forceinline__ bool chunk_ctx(const BwdChunkArgs& a, int j, int h, C
   return true;
 }
 
-// fp64 inclusive cumsum of a = delta A over the chunk (waves 0 and 1, one
-// token per thread; constant past the chunk's end), and f.
-__device__ __forceinline__ void stage_cumsum(const BwdChunkArgs& a, const ChunkCtx& x, int h,
-                                             double* s_cs, float* s_f, double* s_tmp) {
+// The cumsum of stage_cumsum in two halves, for a workgroup that stages other
+// tiles in between: waves 0 and 1 scan their 64 tokens each (partial), then,
+// after every thread has called finish (it holds barriers), wave 1's tokens
+// get wave 0's total.
+__device__ __forceinline__ void stage_cumsum_partial(const BwdChunkArgs& a, const ChunkCtx& x,
+                                                     int h, double* s_cs, float* s_f) {
   const int tid = threadIdx.x;
-  const float Ah = a.A[h];
   if (tid < BC) {
     const bool in = tid < x.c.len;
     const float d = in ? a.delta[(int64_t)(x.tp0 + tid) * a.g.H + h] : 0.0f;
-    const double v = wave_inclusive_sum_f64(in ? (double)d * (double)Ah : 0.0);
-    s_cs[tid] = v;
+    s_cs[tid] = wave_inclusive_sum_f64(in ? (double)d * (double)a.A[h] : 0.0);
     s_f[tid] = in ? (a.input_dt ? d : 1.0f) : 0.0f;
-    if (tid == kWave - 1) s_tmp[0] = v;
   }
+}
+__device__ __forceinline__ void stage_cumsum_finish(double* s_cs, double* s_tmp) {
+  const int tid = threadIdx.x;
+  __syncthreads();
+  if (tid == 0) s_tmp[0] = s_cs[kWave - 1];
   __syncthreads();
   if (tid >= kWave && tid < BC) s_cs[tid] += s_tmp[0];
   __syncthreads();
@@ -283,41 +277,66 @@ __global__ __launch_bounds__(256, 2) void k_bwd_adj_state(BwdChunkArgs a) {
 
 // ---------------------------------------------------------------- k_bwd_dx
 
+// One workgroup of 8 waves per (chunk, head); x, dy (bf16 hi + lo), B and C
+// staged in LDS.  Waves 0-3 form y^T (rows p, columns l; wave w: l-tiles w and
+// 7 - w): Y_off^T = Hin C^T scaled by exp(cs_l), then Q_l, then Y_diag^T =
+// x^T (L o C.B^T + D I)^T (the C.B^T tiles computed as [s][l], whose
+// accumulator layout is directly the B operand), then dz.  Waves 4-7 form g^T
+// (rows p, columns s; s-tiles w - 4 and 11 - w): the inter part exp(Lambda -
+// cs_s) dS B_s and R_s, then the intra part dy^T (L o C.B^T) with the row and
+// column sums of M = (L o C.B^T) o (dy.x^T) f, then dx.  Every output row
+// (l or s) is complete in one wave: no staging tile.
+template <int NT>
 struct DxLds {
+  static constexpr int NMAX = 16 * NT, CLD = NMAX + 8;
   static constexpr int OFF_CS = 0;                  // double[128]
-  static constexpr int OFF_F = 1024;                // float[128]
-  static constexpr int OFF_TMP = 1536;              // double[8]
-  static constexpr int OFF_ROWP = 1600;             // double[4][128] row sums of M per wave
+  static constexpr int OFF_RED = 1024;              // double[16]
+  static constexpr int OFF_ROWP = 1152;             // double[4][128] row sums of M per g-wave
   static constexpr int OFF_COL = OFF_ROWP + 4096;   // double[128] column sums of M
-  static constexpr int OFF_Q = OFF_COL + 1024;      // float[128]
-  static constexpr int OFF_R = OFF_Q + 512;         // float[4][128] R partials per wave (p-tile)
-  static constexpr int OFF_XG = OFF_R + 2048;       // float[128]
-  static constexpr int OFF_DYH = OFF_XG + 512;      // bf16[128][TLD]
-  static constexpr int OFF_DYL = OFF_DYH + BC * TLD * 2;
-  static constexpr int OFF_X = OFF_DYL + BC * TLD * 2;   // bf16[128][TLD]; then staging
-  static constexpr int STAGE_BYTES = BC * SLD * 4;
-  static constexpr int X_BYTES = BC * TLD * 2;
-  static constexpr int TOTAL = OFF_X + (STAGE_BYTES > X_BYTES ? STAGE_BYTES : X_BYTES);
+  static constexpr int OFF_F = OFF_COL + 1024;      // float[128]
+  static constexpr int OFF_Q = OFF_F + 512;         // float[128]
+  static constexpr int OFF_R = OFF_Q + 512;         // float[128]
+  static constexpr int OFF_XG = OFF_R + 512;        // float[128]
+  static constexpr int OFF_X = OFF_XG + 512;        // bf16[128][TLD]
+  static constexpr int OFF_YH = OFF_X + BC * TLD * 2;
+  static constexpr int OFF_YL = OFF_YH + BC * TLD * 2;
+  static constexpr int OFF_B = OFF_YL + BC * TLD * 2;   // bf16[128][CLD]
+  static constexpr int OFF_C = OFF_B + BC * CLD * 2;
+  static constexpr int TOTAL = OFF_C + BC * CLD * 2;
 };
-static_assert(DxLds::TOTAL <= 81920, "two workgroups per CU");
+static_assert(DxLds<8>::TOTAL <= 163840, "one workgroup per CU");
+
+__device__ __forceinline__ double block_sum8(double v, double* red) {
+  v = wave_sum_f64(v);
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) t += red[w];
+  return t;
+}
 
 template <int NT>
-__global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdChunkArgs a) {
-  constexpr int NKB = NT / 2;
-  __shared__ __align__(16) char smem[DxLds::TOTAL];
-  double* s_cs = reinterpret_cast<double*>(smem + DxLds::OFF_CS);
-  float* s_f = reinterpret_cast<float*>(smem + DxLds::OFF_F);
-  double* s_tmp = reinterpret_cast<double*>(smem + DxLds::OFF_TMP);
-  double* s_rowp = reinterpret_cast<double*>(smem + DxLds::OFF_ROWP);
-  double* s_col = reinterpret_cast<double*>(smem + DxLds::OFF_COL);
-  float* s_q = reinterpret_cast<float*>(smem + DxLds::OFF_Q);
-  float* s_r = reinterpret_cast<float*>(smem + DxLds::OFF_R);
-  float* s_xg = reinterpret_cast<float*>(smem + DxLds::OFF_XG);
+__global__ __launch_bounds__(512, 1) void k_bwd_dx(BwdChunkArgs a) {
+  using L = DxLds<NT>;
+  constexpr int NKB = NT / 2, CLD = L::CLD, NMAX = L::NMAX;
+  __shared__ __align__(16) char smem[L::TOTAL];
+  double* s_cs = reinterpret_cast<double*>(smem + L::OFF_CS);
+  double* s_red = reinterpret_cast<double*>(smem + L::OFF_RED);
+  double* s_rowp = reinterpret_cast<double*>(smem + L::OFF_ROWP);
+  double* s_col = reinterpret_cast<double*>(smem + L::OFF_COL);
+  float* s_f = reinterpret_cast<float*>(smem + L::OFF_F);
+  float* s_q = reinterpret_cast<float*>(smem + L::OFF_Q);
+  float* s_r = reinterpret_cast<float*>(smem + L::OFF_R);
+  float* s_xg = reinterpret_cast<float*>(smem + L::OFF_XG);
+  bf16* s_x = reinterpret_cast<bf16*>(smem + L::OFF_X);
+  bf16* s_yh = reinterpret_cast<bf16*>(smem + L::OFF_YH);
+  bf16* s_yl = reinterpret_cast<bf16*>(smem + L::OFF_YL);
+  bf16* s_b = reinterpret_cast<bf16*>(smem + L::OFF_B);
+  bf16* s_c = reinterpret_cast<bf16*>(smem + L::OFF_C);
   double* s_dcs = s_rowp;  // (dcs_l replaces the row sums of token l, read by the same thread)
-  bf16* s_dyh = reinterpret_cast<bf16*>(smem + DxLds::OFF_DYH);
-  bf16* s_dyl = reinterpret_cast<bf16*>(smem + DxLds::OFF_DYL);
-  bf16* s_x = reinterpret_cast<bf16*>(smem + DxLds::OFF_X);
-  float* s_st = reinterpret_cast<float*>(smem + DxLds::OFF_X);
 
   const Geo& g = a.g;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -337,21 +356,19 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdChunkArgs a) {
   const int64_t PN = (int64_t)g.P * g.N;
   const float Ah = a.A[h];
   const float Dh = a.D ? a.D[h] : 0.0f;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  stage_cumsum(a, cx, h, s_cs, s_f, s_tmp);
-  const double lam = s_cs[len - 1];
-
-  // ---- x and dy = dout silu(z) to LDS (dy as bf16 hi + lo); D's gradient
-  // share sum(dy . x) on the way
+  // ---- stage: cumsum (waves 0-1), x and dy = dout silu(z) (hi + lo) rows, the
+  // B and C tiles; D's gradient share sum(dy . x) on the way
+  stage_cumsum_partial(a, cx, h, s_cs, s_f);
   const bf16* xb = row_ptr<bf16>(a.x, c.b, c.t0, h);
   const bf16* zb = a.z.p ? row_ptr<bf16>(a.z, c.b, c.t0, h) : nullptr;
   double dyx = 0.0;
   {
     const int row0 = tid / 8, col = (tid % 8) * 8;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int l = row0 + 32 * k;
-      const int lc = min(l, len - 1);
+    for (int k = 0; k < 2; ++k) {
+      const int l = row0 + 64 * k, lc = min(l, len - 1);
       const bool in = l < len;
       const u32x4 xv = *reinterpret_cast<const u32x4*>(at(xb, (uint32_t)(lc * a.x.s1 + col)));
       f32x8 go;
@@ -359,8 +376,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdChunkArgs a) {
         const bf16* db = row_ptr<bf16>(a.dout, c.b, c.t0, h);
         go = bf8_to_f32(*reinterpret_cast<const u32x4*>(at(db, (uint32_t)(lc * a.dout.s1 + col))));
       } else {
-        const float* db = row_ptr<float>(a.dout, c.b, c.t0, h);
-        go = load8f(at(db, (uint32_t)(lc * a.dout.s1 + col)));
+        go = load8f(at(row_ptr<float>(a.dout, c.b, c.t0, h), (uint32_t)(lc * a.dout.s1 + col)));
       }
       if (zb) {
         const f32x8 zz = bf8_to_f32(*reinterpret_cast<const u32x4*>(at(zb, (uint32_t)(lc * a.z.s1 + col))));
@@ -374,354 +390,335 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdChunkArgs a) {
         dyx += (double)(go[i] * xf[i]);
       }
       const FragSplit sp = split_f32x8(go);
-      const u32x4 zero = {0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4*>(&s_x[l * TLD + col]) = in ? xv : zero;
-      *reinterpret_cast<bf16x8*>(&s_dyh[l * TLD + col]) = sp.hi;
-      *reinterpret_cast<bf16x8*>(&s_dyl[l * TLD + col]) = sp.lo;
+      *reinterpret_cast<bf16x8*>(&s_yh[l * TLD + col]) = sp.hi;
+      *reinterpret_cast<bf16x8*>(&s_yl[l * TLD + col]) = sp.lo;
     }
-  }
-  // <dS, Hin> (for the last token's Lambda term), fp64
-  const float* hin = a.hin + ((int64_t)j * g.H + h) * PN;
-  double ip = 0.0;
-  {
-    for (int k = tid * 4; k < PN; k += 256 * 4) {
-      const f32x4 u = *reinterpret_cast<const f32x4*>(cx.ds + k);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(hin + k);
+    constexpr int BPR = NMAX / 8, ROWS = 512 / BPR;
+    const bf16* bbase = row_ptr<bf16>(a.B, c.b, c.t0, grp);
+    const bf16* cbase = row_ptr<bf16>(a.C, c.b, c.t0, grp);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ip += (double)u[i] * (double)v[i];
+    for (int k = 0; k < BC / ROWS; ++k) {
+      const int l = tid / BPR + ROWS * k, cc = (tid % BPR) * 8;
+      const uint32_t off = (uint32_t)(min(l, len - 1) * a.B.s1 + min(cc, g.N - 8));
+      const uint32_t offc = (uint32_t)(min(l, len - 1) * a.C.s1 + min(cc, g.N - 8));
+      const bool ok = l < len && cc < g.N;
+      const u32x4 vb = *reinterpret_cast<const u32x4*>(at(bbase, off));
+      const u32x4 vc = *reinterpret_cast<const u32x4*>(at(cbase, offc));
+      *reinterpret_cast<u32x4*>(&s_b[l * CLD + cc]) = ok ? vb : zero;
+      *reinterpret_cast<u32x4*>(&s_c[l * CLD + cc]) = ok ? vc : zero;
     }
+    for (int i = tid; i < 4 * BC; i += 512) s_rowp[i] = 0.0;
   }
-  __syncthreads();
-
-  // C and B row fragments (n contiguous): rows past the chunk and columns past
-  // N read as zero
-  const bf16* cbase = row_ptr<bf16>(a.C, c.b, c.t0, grp);
-  const bf16* bbase = row_ptr<bf16>(a.B, c.b, c.t0, grp);
-  auto nrow_frag = [&](const bf16* base, int64_t s1, int row, int kb) -> u32x4 {
-    const int n = kb * 32 + q * 8;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(
-        at(base, (uint32_t)(min(row, len - 1) * s1 + min(n, g.N - 8))));
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    return (row < len && n < g.N) ? v : zero;
-  };
-  // a state row (P x N fp32, row p) as an operand fragment of 8 n, split
-  auto state_frag = [&](const float* st, int p, int kb, float scale) -> FragSplit {
+  stage_cumsum_finish(s_cs, s_red + 15);
+  const double lam = s_cs[len - 1];
+  const float* hin = a.hin + ((int64_t)j * g.H + h) * PN;
+  // a state row (P x N fp32, row p) as 8 fp32 n of k-block kb (0 past N)
+  auto state8 = [&](const float* st, int p, int kb) -> f32x8 {
     const int n = kb * 32 + q * 8;
     f32x8 v = load8f(st + (int64_t)p * g.N + min(n, g.N - 8));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = n < g.N ? v[i] * scale : 0.0f;
-    return split_f32x8(v);
+    for (int i = 0; i < 8; ++i) v[i] = n < g.N ? v[i] : 0.0f;
+    return v;
   };
+  const int w4 = wave & 3;
+  const int tA = w4, tB = 7 - w4;
 
-  const int ltA = wave, ltB = 7 - wave;
-
-  // ---- Y_diag = (L o C.B^T + D I) x for l-tiles ltA, ltB (layout A tiles, as
-  // in the fused forward): rows l, all four p-tiles
-  f32x4 yd[2][4];
+  if (wave < 4) {
+    // ==== y side: l-tiles tA, tB
+    f32x4 yt[2][4];
 #pragma unroll
-  for (int ui = 0; ui < 2; ++ui)
+    for (int ui = 0; ui < 2; ++ui)
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) yd[ui][pt] = zero4();
+      for (int pt = 0; pt < 4; ++pt) yt[ui][pt] = zero4();
+    FragBF cf[2][NKB];
 #pragma unroll
-  for (int ui = 0; ui < 2; ++ui) {
-    const int lt = ui ? ltB : ltA;
-    const int lrow = lt * 16 + r16;
-    u32x4 cf[NKB];
+    for (int ui = 0; ui < 2; ++ui) {
+      const int l = (ui ? tB : tA) * 16 + r16;
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) cf[kb] = nrow_frag(cbase, a.C.s1, lrow, kb);
-    const double csl = s_cs[lrow];
-    for (int kp = 0; kp <= lt / 2; ++kp) {
-      const int sa = 2 * kp, sb = 2 * kp + 1;
-      f32x4 va = zero4(), vb = zero4();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        mma(va, as_frag(nrow_frag(bbase, a.B.s1, sa * 16 + r16, kb)), as_frag(cf[kb]));
-        mma(vb, as_frag(nrow_frag(bbase, a.B.s1, sb * 16 + r16, kb)), as_frag(cf[kb]));
-      }
-      f32x8 m;
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int s_a = sa * 16 + q * 4 + e4, s_b = sb * 16 + q * 4 + e4;
-        const float ma = exp_d(csl - s_cs[s_a]) * s_f[s_a] * va[e4];
-        const float mb = exp_d(csl - s_cs[s_b]) * s_f[s_b] * vb[e4];
-        m[e4] = s_a < lrow ? ma : (s_a == lrow ? ma + Dh : 0.0f);
-        m[4 + e4] = s_b < lrow ? mb : (s_b == lrow ? mb + Dh : 0.0f);
-      }
-      const FragSplit mf = split_f32x8(m);
-#pragma unroll
-      for (int pt = 0; pt < 4; ++pt) {
-        FragBF xf;
-        xf.v = lds_frag_tr(s_x, TLD, sa * 16 + q * 4, sb * 16 + q * 4, pt * 16);
-        mma(yd[ui][pt], mf, xf);
-      }
+      for (int kb = 0; kb < NKB; ++kb)
+        cf[ui][kb].v = *reinterpret_cast<const bf16x8*>(&s_c[l * CLD + kb * 32 + q * 8]);
     }
-  }
-
-  // ---- Y_off = exp(cs_l) C_l . Hin for p-tile `wave`, all l-tiles (each wave
-  // splits only its own 16 rows of Hin)
-  f32x4 yo[8];
-#pragma unroll
-  for (int lt = 0; lt < 8; ++lt) yo[lt] = zero4();
-  {
-    const int pr = wave * 16 + r16;
+    // Y_off^T = Hin C^T (rows p, columns l); <dS, Hin> over p-tile w on the way
+    double ip = 0.0;
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const FragSplit hf = state_frag(hin, pr, kb, 1.0f);
-#pragma unroll
-      for (int lt = 0; lt < 8; ++lt)
-        mma(yo[lt], as_frag(nrow_frag(cbase, a.C.s1, lt * 16 + r16, kb)), hf);
-    }
-#pragma unroll
-    for (int lt = 0; lt < 8; ++lt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) yo[lt][i] *= exp_d(s_cs[lt * 16 + q * 4 + i]);
-  }
-  __syncthreads();  // the x tile is dead: its space takes the staging tile
-  // stage Y_off; Q_l = dy_l . Y_off_l; then add Y_diag: y
-#pragma unroll
-  for (int lt = 0; lt < 8; ++lt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s_st[(lt * 16 + q * 4 + i) * SLD + wave * 16 + r16] = yo[lt][i];
-  __syncthreads();
-  {
-    const int l = tid / 2, p0 = (tid % 2) * 32;
-    float qs = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const u32x4 hv = *reinterpret_cast<const u32x4*>(&s_dyh[l * TLD + p0 + 8 * k]);
-      const u32x4 lv = *reinterpret_cast<const u32x4*>(&s_dyl[l * TLD + p0 + 8 * k]);
-      const f32x8 hf = bf8_to_f32(hv), lf = bf8_to_f32(lv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qs += (hf[i] + lf[i]) * s_st[l * SLD + p0 + 8 * k + i];
-    }
-    qs += __shfl_xor(qs, 1, kWave);
-    if ((tid % 2) == 0) s_q[l] = qs;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int ui = 0; ui < 2; ++ui) {
-    const int lt = ui ? ltB : ltA;
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) s_st[(lt * 16 + q * 4 + i) * SLD + pt * 16 + r16] += yd[ui][pt][i];
-  }
-  __syncthreads();
-  // ---- dz = dout y silu'(z), silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
-  if (zb) {
-    const int row0 = tid / 8, col = (tid % 8) * 8;
-    float* dzb = row_ptr_mut<float>(a.dz, c.b, c.t0, h);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int l = row0 + 32 * k;
-      const int lc = min(l, len - 1);
-      f32x8 go;
-      if (a.dout_bf16) {
-        const bf16* db = row_ptr<bf16>(a.dout, c.b, c.t0, h);
-        go = bf8_to_f32(*reinterpret_cast<const u32x4*>(at(db, (uint32_t)(lc * a.dout.s1 + col))));
-      } else {
-        const float* db = row_ptr<float>(a.dout, c.b, c.t0, h);
-        go = load8f(at(db, (uint32_t)(lc * a.dout.s1 + col)));
-      }
-      const f32x8 zz = bf8_to_f32(*reinterpret_cast<const u32x4*>(at(zb, (uint32_t)(lc * a.z.s1 + col))));
-      f32x8 o;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float sg = sigmoidf(zz[i]);
-        o[i] = go[i] * s_st[l * SLD + col + i] * (sg * (1.0f + zz[i] * (1.0f - sg)));
-      }
-      if (l < len) Vec8<float>::store(at(dzb, (uint32_t)(l * a.dz.s1 + col)), o);
-    }
-  }
-  __syncthreads();  // y is dead: the staging tile takes g
-
-  // ---- inter-chunk part of g: exp(Lambda - cs_s) dS B_s, as g^T tiles (rows
-  // p of p-tile `wave`, columns s of every s-tile); R partials on the way
-  {
-    f32x4 go_[8];
-#pragma unroll
-    for (int st = 0; st < 8; ++st) go_[st] = zero4();
-    {
-      const int pr = wave * 16 + r16;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const FragSplit df = state_frag(cx.ds, pr, kb, 1.0f);
-#pragma unroll
-        for (int st = 0; st < 8; ++st)
-          mma(go_[st], df, as_frag(nrow_frag(bbase, a.B.s1, st * 16 + r16, kb)));
-      }
-    }
-#pragma unroll
-    for (int st = 0; st < 8; ++st) {
-      const int s = st * 16 + r16;
-      const float e = s < len ? exp_d(lam - s_cs[s]) : 0.0f;
-      // x[s][p] for p = 16 wave + 4 q + 0..3
-      const uint2 xv = *reinterpret_cast<const uint2*>(
-          at(xb, (uint32_t)(min(s, len - 1) * a.x.s1 + wave * 16 + q * 4)));
-      const float x4[4] = {bf16_lo_f32(xv.x), bf16_hi_f32(xv.x), bf16_lo_f32(xv.y),
-                           bf16_hi_f32(xv.y)};
-      float rp = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        go_[st][i] *= e;
-        rp += x4[i] * go_[st][i];
-      }
-      rp = across_groups(rp);
-      if (q == 0) s_r[wave * BC + s] = s < len ? rp : 0.0f;
-      *reinterpret_cast<f32x4*>(&s_st[s * SLD + wave * 16 + q * 4]) = go_[st];
-    }
-  }
-
-  // ---- intra-chunk part of g^T = dy^T (L o C.B^T) for s-tiles ltA, ltB
-  // (layout B tiles), with the row and column sums of M = (L o C.B^T) o
-  // (dy.x^T) f (strictly lower triangle) in fp64
-  f32x4 gd_[2][4];
-#pragma unroll
-  for (int ui = 0; ui < 2; ++ui)
-#pragma unroll
-    for (int pt = 0; pt < 4; ++pt) gd_[ui][pt] = zero4();
-  for (int i = tid; i < 4 * BC; i += 256) s_rowp[i] = 0.0;
-  __syncthreads();  // (the g^T staging above, and the row sums' zeroing, are done)
-#pragma unroll
-  for (int ui = 0; ui < 2; ++ui) {
-    const int sbt = ui ? ltB : ltA;
-    const int s = sbt * 16 + r16;
-    u32x4 bf[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) bf[kb] = nrow_frag(bbase, a.B.s1, s, kb);
-    u32x4 xr[2];
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(
-          at(xb, (uint32_t)(min(s, len - 1) * a.x.s1 + kp * 32 + q * 8)));
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      xr[kp] = s < len ? v : zero;
-    }
-    const double css = s_cs[s];
-    const float fs = s_f[s];
-    double colp = 0.0;
-    for (int lp = sbt / 2; lp < 4; ++lp) {
-      const int la = 2 * lp, lb = 2 * lp + 1;
-      f32x4 ca = zero4(), cb = zero4(), xa = zero4(), xb2 = zero4();
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        mma(ca, as_frag(nrow_frag(cbase, a.C.s1, la * 16 + r16, kb)), as_frag(bf[kb]));
-        mma(cb, as_frag(nrow_frag(cbase, a.C.s1, lb * 16 + r16, kb)), as_frag(bf[kb]));
-      }
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        const int pc = kp * 32 + q * 8;
-        mma(xa, lds_split(&s_dyh[(la * 16 + r16) * TLD + pc], &s_dyl[(la * 16 + r16) * TLD + pc]),
-            as_frag(xr[kp]));
-        mma(xb2, lds_split(&s_dyh[(lb * 16 + r16) * TLD + pc], &s_dyl[(lb * 16 + r16) * TLD + pc]),
-            as_frag(xr[kp]));
-      }
-      f32x8 m;
-      double rowa[4], rowb[4];
-#pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const int l_a = la * 16 + q * 4 + e4, l_b = lb * 16 + q * 4 + e4;
-        const float ea = exp_d(s_cs[l_a] - css), eb = exp_d(s_cs[l_b] - css);
-        const bool oka = s <= l_a && l_a < len && s < len;
-        const bool okb = s <= l_b && l_b < len && s < len;
-        m[e4] = oka ? ea * ca[e4] : 0.0f;
-        m[4 + e4] = okb ? eb * cb[e4] : 0.0f;
-        const double pa = (oka && s < l_a) ? (double)(m[e4] * xa[e4] * fs) : 0.0;
-        const double pb = (okb && s < l_b) ? (double)(m[4 + e4] * xb2[e4] * fs) : 0.0;
-        rowa[e4] = pa;
-        rowb[e4] = pb;
-        colp += pa + pb;
-      }
-      const FragSplit mf = split_f32x8(m);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        FragSplit dyt;
-        dyt.hi = lds_frag_tr(s_dyh, TLD, la * 16 + q * 4, lb * 16 + q * 4, pt * 16);
-        dyt.lo = lds_frag_tr(s_dyl, TLD, la * 16 + q * 4, lb * 16 + q * 4, pt * 16);
-        mma(gd_[ui][pt], dyt, mf);
-      }
-      // row sums of this pair of tiles: over the 16 columns s of the lane group
+        const f32x8 hv = state8(hin, pt * 16 + r16, kb);
+        if (pt == w4) {
+          const f32x8 dv = state8(cx.ds, pt * 16 + r16, kb);
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const double ra = group16_sum_f64(rowa[e4]);
-        const double rb = group16_sum_f64(rowb[e4]);
-        if (r16 == 0) {
-          s_rowp[wave * BC + la * 16 + q * 4 + e4] += ra;
-          s_rowp[wave * BC + lb * 16 + q * 4 + e4] += rb;
+          for (int i = 0; i < 8; ++i) ip += (double)hv[i] * (double)dv[i];
+        }
+        const FragSplit hf = split_f32x8(hv);
+        mma(yt[0][pt], hf, cf[0][kb]);
+        mma(yt[1][pt], hf, cf[1][kb]);
+      }
+    }
+    ip = wave_sum_f64(ip);
+    if (lane == 0) s_red[8 + w4] = ip;
+#pragma unroll
+    for (int ui = 0; ui < 2; ++ui) {
+      const int l = (ui ? tB : tA) * 16 + r16;
+      const float el = exp_d(s_cs[l]);
+      float qs = 0.0f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const uint2 hv = *reinterpret_cast<const uint2*>(&s_yh[l * TLD + pt * 16 + q * 4]);
+        const uint2 lv = *reinterpret_cast<const uint2*>(&s_yl[l * TLD + pt * 16 + q * 4]);
+        const float dy4[4] = {bf16_lo_f32(hv.x) + bf16_lo_f32(lv.x), bf16_hi_f32(hv.x) + bf16_hi_f32(lv.x),
+                              bf16_lo_f32(hv.y) + bf16_lo_f32(lv.y), bf16_hi_f32(hv.y) + bf16_hi_f32(lv.y)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          yt[ui][pt][i] *= el;
+          qs += dy4[i] * yt[ui][pt][i];
+        }
+      }
+      qs = across_groups(qs);
+      if (q == 0) s_q[l] = qs;
+    }
+    // Y_diag^T = x^T M^T, M = L o C.B^T (+ D on the diagonal)
+#pragma unroll
+    for (int ui = 0; ui < 2; ++ui) {
+      const int lt = ui ? tB : tA;
+      const int lrow = lt * 16 + r16;
+      const double csl = s_cs[lrow];
+      for (int kp = 0; kp <= lt / 2; ++kp) {
+        const int sa = 2 * kp, sb = 2 * kp + 1;
+        f32x4 va = zero4(), vb = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          FragBF ba, bb;
+          ba.v = *reinterpret_cast<const bf16x8*>(&s_b[(sa * 16 + r16) * CLD + kb * 32 + q * 8]);
+          bb.v = *reinterpret_cast<const bf16x8*>(&s_b[(sb * 16 + r16) * CLD + kb * 32 + q * 8]);
+          mma(va, ba, cf[ui][kb]);
+          mma(vb, bb, cf[ui][kb]);
+        }
+        f32x8 m;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int s_a = sa * 16 + q * 4 + e4, s_b2 = sb * 16 + q * 4 + e4;
+          const float ma = exp_d(csl - s_cs[s_a]) * s_f[s_a] * va[e4];
+          const float mb = exp_d(csl - s_cs[s_b2]) * s_f[s_b2] * vb[e4];
+          m[e4] = s_a < lrow ? ma : (s_a == lrow ? ma + Dh : 0.0f);
+          m[4 + e4] = s_b2 < lrow ? mb : (s_b2 == lrow ? mb + Dh : 0.0f);
+        }
+        const FragSplit mf = split_f32x8(m);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          FragBF xt;
+          xt.v = lds_frag_tr(s_x, TLD, sa * 16 + q * 4, sb * 16 + q * 4, pt * 16);
+          mma(yt[ui][pt], xt, mf);
         }
       }
     }
-    colp = across_groups_f64(colp);
-    if (q == 0) s_col[s] = colp;
-  }
-  // g = intra + inter in the staging tile (rows s, columns p)
+    // dz = dout y silu'(z), silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
+    if (zb) {
 #pragma unroll
-  for (int ui = 0; ui < 2; ++ui) {
-    const int sbt = ui ? ltB : ltA;
+      for (int ui = 0; ui < 2; ++ui) {
+        const int l = (ui ? tB : tA) * 16 + r16;
+        const int lc = min(l, len - 1);
+        float* dzr = row_ptr_mut<float>(a.dz, c.b, c.t0, h);
 #pragma unroll
-    for (int pt = 0; pt < 4; ++pt) {
-      f32x4* dst = reinterpret_cast<f32x4*>(&s_st[(sbt * 16 + r16) * SLD + pt * 16 + q * 4]);
-      *dst = *dst + gd_[ui][pt];
-    }
-  }
-  __syncthreads();
-  // ---- dx = f g + D dy; x . g for the step size on the input term
-  {
-    const int row0 = tid / 8, col = (tid % 8) * 8;
-    float* dxb = row_ptr_mut<float>(a.dx, c.b, c.t0, h);
+        for (int pt = 0; pt < 4; ++pt) {
+          const int p = pt * 16 + q * 4;
+          f32x4 go;
+          if (a.dout_bf16) {
+            const uint2 v = *reinterpret_cast<const uint2*>(
+                at(row_ptr<bf16>(a.dout, c.b, c.t0, h), (uint32_t)(lc * a.dout.s1 + p)));
+            go[0] = bf16_lo_f32(v.x); go[1] = bf16_hi_f32(v.x);
+            go[2] = bf16_lo_f32(v.y); go[3] = bf16_hi_f32(v.y);
+          } else {
+            go = *reinterpret_cast<const f32x4*>(
+                at(row_ptr<float>(a.dout, c.b, c.t0, h), (uint32_t)(lc * a.dout.s1 + p)));
+          }
+          const uint2 zv = *reinterpret_cast<const uint2*>(at(zb, (uint32_t)(lc * a.z.s1 + p)));
+          const float z4[4] = {bf16_lo_f32(zv.x), bf16_hi_f32(zv.x), bf16_lo_f32(zv.y),
+                               bf16_hi_f32(zv.y)};
+          f32x4 o;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int s = row0 + 32 * k;
-      const f32x8 gv = Vec8<float>::load(s_st + s * SLD + col);
-      const f32x8 hf = bf8_to_f32(*reinterpret_cast<const u32x4*>(&s_dyh[s * TLD + col]));
-      const f32x8 lf = bf8_to_f32(*reinterpret_cast<const u32x4*>(&s_dyl[s * TLD + col]));
-      const float fs = s_f[s];
-      f32x8 o;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[i] = fs * gv[i] + Dh * (hf[i] + lf[i]);
-      if (s < len) Vec8<float>::store(at(dxb, (uint32_t)(s * a.dx.s1 + col)), o);
-      if (a.input_dt) {
-        const f32x8 xf = bf8_to_f32(*reinterpret_cast<const u32x4*>(
-            at(xb, (uint32_t)(min(s, len - 1) * a.x.s1 + col))));
-        float e = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) e += xf[i] * gv[i];
-        e += __shfl_xor(e, 1, kWave);
-        e += __shfl_xor(e, 2, kWave);
-        e += __shfl_xor(e, 4, kWave);
-        if ((tid % 8) == 0) s_xg[s] = s < len ? e : 0.0f;
+          for (int i = 0; i < 4; ++i) {
+            const float sg = sigmoidf(z4[i]);
+            o[i] = go[i] * yt[ui][pt][i] * (sg * (1.0f + z4[i] * (1.0f - sg)));
+          }
+          if (l < len) *reinterpret_cast<f32x4*>(at(dzr, (uint32_t)(l * a.dz.s1 + p))) = o;
+        }
       }
     }
+  } else {
+    // ==== g side: s-tiles tA, tB
+    f32x4 gt[2][4];
+#pragma unroll
+    for (int ui = 0; ui < 2; ++ui)
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) gt[ui][pt] = zero4();
+    FragBF bf[2][NKB];
+#pragma unroll
+    for (int ui = 0; ui < 2; ++ui) {
+      const int s = (ui ? tB : tA) * 16 + r16;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+        bf[ui][kb].v = *reinterpret_cast<const bf16x8*>(&s_b[s * CLD + kb * 32 + q * 8]);
+    }
+    // inter part g^T += dS B^T, scaled by exp(Lambda - cs_s); R_s
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const FragSplit df = split_f32x8(state8(cx.ds, pt * 16 + r16, kb));
+        mma(gt[0][pt], df, bf[0][kb]);
+        mma(gt[1][pt], df, bf[1][kb]);
+      }
+    }
+#pragma unroll
+    for (int ui = 0; ui < 2; ++ui) {
+      const int s = (ui ? tB : tA) * 16 + r16;
+      const float e = s < len ? exp_d(lam - s_cs[s]) : 0.0f;
+      float rp = 0.0f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const uint2 xv = *reinterpret_cast<const uint2*>(&s_x[s * TLD + pt * 16 + q * 4]);
+        const float x4[4] = {bf16_lo_f32(xv.x), bf16_hi_f32(xv.x), bf16_lo_f32(xv.y),
+                             bf16_hi_f32(xv.y)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          gt[ui][pt][i] *= e;
+          rp += x4[i] * gt[ui][pt][i];
+        }
+      }
+      rp = across_groups(rp);
+      if (q == 0) s_r[s] = s_f[s] * rp;
+    }
+    // intra part g^T += dy^T (L o C.B^T) ([l][s] tiles: the B operand), with the
+    // row and column sums of M in fp64
+#pragma unroll
+    for (int ui = 0; ui < 2; ++ui) {
+      const int sbt = ui ? tB : tA;
+      const int s = sbt * 16 + r16;
+      FragBF xr[2];
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp)
+        xr[kp].v = *reinterpret_cast<const bf16x8*>(&s_x[s * TLD + kp * 32 + q * 8]);
+      const double css = s_cs[s];
+      const float fs = s_f[s];
+      double colp = 0.0;
+      for (int lp = sbt / 2; lp < 4; ++lp) {
+        const int la = 2 * lp, lb = 2 * lp + 1;
+        f32x4 ca = zero4(), cb = zero4(), xa = zero4(), xb2 = zero4();
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          FragBF c0, c1;
+          c0.v = *reinterpret_cast<const bf16x8*>(&s_c[(la * 16 + r16) * CLD + kb * 32 + q * 8]);
+          c1.v = *reinterpret_cast<const bf16x8*>(&s_c[(lb * 16 + r16) * CLD + kb * 32 + q * 8]);
+          mma(ca, c0, bf[ui][kb]);
+          mma(cb, c1, bf[ui][kb]);
+        }
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          const int pc = kp * 32 + q * 8;
+          mma(xa, lds_split(&s_yh[(la * 16 + r16) * TLD + pc], &s_yl[(la * 16 + r16) * TLD + pc]),
+              xr[kp]);
+          mma(xb2, lds_split(&s_yh[(lb * 16 + r16) * TLD + pc], &s_yl[(lb * 16 + r16) * TLD + pc]),
+              xr[kp]);
+        }
+        f32x8 m;
+        double rowa[4], rowb[4];
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const int l_a = la * 16 + q * 4 + e4, l_b = lb * 16 + q * 4 + e4;
+          const float ea = exp_d(s_cs[l_a] - css), eb = exp_d(s_cs[l_b] - css);
+          const bool oka = s <= l_a && l_a < len && s < len;
+          const bool okb = s <= l_b && l_b < len && s < len;
+          m[e4] = oka ? ea * ca[e4] : 0.0f;
+          m[4 + e4] = okb ? eb * cb[e4] : 0.0f;
+          const double pa = (oka && s < l_a) ? (double)(m[e4] * xa[e4] * fs) : 0.0;
+          const double pb = (okb && s < l_b) ? (double)(m[4 + e4] * xb2[e4] * fs) : 0.0;
+          rowa[e4] = pa;
+          rowb[e4] = pb;
+          colp += pa + pb;
+        }
+        const FragSplit mf = split_f32x8(m);
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          FragSplit dyt;
+          dyt.hi = lds_frag_tr(s_yh, TLD, la * 16 + q * 4, lb * 16 + q * 4, pt * 16);
+          dyt.lo = lds_frag_tr(s_yl, TLD, la * 16 + q * 4, lb * 16 + q * 4, pt * 16);
+          mma(gt[ui][pt], dyt, mf);
+        }
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const double ra = group16_sum_f64(rowa[e4]);
+          const double rb = group16_sum_f64(rowb[e4]);
+          if (r16 == 0) {
+            s_rowp[w4 * BC + la * 16 + q * 4 + e4] += ra;
+            s_rowp[w4 * BC + lb * 16 + q * 4 + e4] += rb;
+          }
+        }
+      }
+      colp = across_groups_f64(colp);
+      if (q == 0) s_col[s] = colp;
+    }
+    // dx = f g + D dy; x . g for the step size on the input term
+#pragma unroll
+    for (int ui = 0; ui < 2; ++ui) {
+      const int s = (ui ? tB : tA) * 16 + r16;
+      const float fs = s_f[s];
+      float* dxr = row_ptr_mut<float>(a.dx, c.b, c.t0, h);
+      float e = 0.0f;
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) {
+        const int p = pt * 16 + q * 4;
+        const uint2 hv = *reinterpret_cast<const uint2*>(&s_yh[s * TLD + p]);
+        const uint2 lv = *reinterpret_cast<const uint2*>(&s_yl[s * TLD + p]);
+        const uint2 xv = *reinterpret_cast<const uint2*>(&s_x[s * TLD + p]);
+        const float dy4[4] = {bf16_lo_f32(hv.x) + bf16_lo_f32(lv.x), bf16_hi_f32(hv.x) + bf16_hi_f32(lv.x),
+                              bf16_lo_f32(hv.y) + bf16_lo_f32(lv.y), bf16_hi_f32(hv.y) + bf16_hi_f32(lv.y)};
+        const float x4[4] = {bf16_lo_f32(xv.x), bf16_hi_f32(xv.x), bf16_lo_f32(xv.y),
+                             bf16_hi_f32(xv.y)};
+        f32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] = fs * gt[ui][pt][i] + Dh * dy4[i];
+          e += x4[i] * gt[ui][pt][i];
+        }
+        if (s < len) *reinterpret_cast<f32x4*>(at(dxr, (uint32_t)(s * a.dx.s1 + p))) = o;
+      }
+      e = across_groups(e);
+      if (q == 0) s_xg[s] = s < len ? e : 0.0f;
+    }
   }
+
   // ---- dcs, and its suffix sums: dL/da_t
-  const double sip = block_sum4(ip, s_tmp);  // (its barriers publish the sums above)
+  __syncthreads();
   if (tid < BC) {
     const int l = tid;
     double v = 0.0, rl = 0.0;
     if (l < len) {
-      rl = (double)s_f[l] * ((double)s_r[l] + s_r[BC + l] + s_r[2 * BC + l] + s_r[3 * BC + l]);
+      rl = (double)s_r[l];
       v = s_rowp[l] + s_rowp[BC + l] + s_rowp[2 * BC + l] + s_rowp[3 * BC + l] - s_col[l] +
           (double)s_q[l] - rl;
     }
     s_dcs[l] = v;
-    // sum of R over the chunk (wave 0 and 1 each hold 64 tokens)
     const double rs = wave_sum_f64(rl);
-    if (lane == 0) s_tmp[4 + wave] = rs;
+    if (lane == 0) s_red[12 + wave] = rs;
   }
   __syncthreads();
-  if (tid == 0)
-    s_dcs[len - 1] += (double)exp_d(lam) * sip + s_tmp[4] + s_tmp[5];
+  if (tid == 0) {
+    const double sip = s_red[8] + s_red[9] + s_red[10] + s_red[11];
+    s_dcs[len - 1] += (double)exp_d(lam) * sip + s_red[12] + s_red[13];
+  }
   __syncthreads();
   double sa = 0.0, sb = 0.0, suf = 0.0;
   if (tid < BC) {
     // suffix sums by a reversed inclusive scan: thread t holds token 127 - t
     suf = wave_inclusive_sum_f64(s_dcs[BC - 1 - tid]);
-    if (tid == kWave - 1) s_tmp[6] = suf;
+    if (tid == kWave - 1) s_red[14] = suf;
   }
   __syncthreads();
   if (tid < BC) {
     const int l = BC - 1 - tid;
-    const double da = suf + (tid >= kWave ? s_tmp[6] : 0.0);
+    const double da = suf + (tid >= kWave ? s_red[14] : 0.0);
     if (l < len) {
       const int64_t it = (int64_t)(cx.tp0 + l) * g.H + h;
       const double gg = (da * (double)Ah + (a.input_dt ? (double)s_xg[l] : 0.0)) * (double)a.gd[it];
@@ -730,9 +727,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdChunkArgs a) {
       sb = gg;
     }
   }
-  sa = block_sum4(sa, s_tmp);
-  sb = block_sum4(sb, s_tmp);
-  dyx = block_sum4(dyx, s_tmp);
+  sa = block_sum8(sa, s_red);
+  sb = block_sum8(sb, s_red);
+  dyx = block_sum8(dyx, s_red);
   if (tid == 0) {
     pj[0] = sa;
     pj[1] = sb;
@@ -742,21 +739,33 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dx(BwdChunkArgs a) {
 
 // ---------------------------------------------------------------- k_bwd_dbc
 
+// One workgroup of 8 waves per (chunk, group, head split, 64-column slab of N).
+// Per head, every operand is staged in LDS: dy (bf16 hi + lo), x, and the
+// slabs of Hin and dS (hi + lo); the chunk's B and C slabs once.  Waves 0-3
+// form dC (wave w: l-tiles w and 7 - w), waves 4-7 dB (s-tiles w - 4 and
+// 11 - w), each accumulating over the heads in registers.
 struct DbcLds {
   static constexpr int OFF_CS = 0;                   // double[128]
   static constexpr int OFF_F = 1024;                 // float[128]
   static constexpr int OFF_EL = 1536;                // float[128] exp(cs_l)
   static constexpr int OFF_ES = 2048;                // float[128] f_s exp(Lambda - cs_s)
   static constexpr int OFF_TMP = 2560;               // double[8]
-  static constexpr int OFF_BT = 2624;                // bf16[128][TLD] B slab
-  static constexpr int OFF_CT = OFF_BT + BC * TLD * 2;     // bf16[128][TLD] C slab
-  static constexpr int OFF_SH = OFF_CT + BC * TLD * 2;     // bf16[64][TLD] state slab hi
-  static constexpr int OFF_SL = OFF_SH + 64 * TLD * 2;     // bf16[64][TLD] state slab lo
-  static constexpr int TOTAL = OFF_SL + 64 * TLD * 2;
+  static constexpr int T128 = BC * TLD * 2;          // a [128][TLD] bf16 tile
+  static constexpr int T64 = 64 * TLD * 2;           // a [64][TLD] bf16 tile
+  static constexpr int OFF_BT = 2624;                // B slab
+  static constexpr int OFF_CT = OFF_BT + T128;       // C slab
+  static constexpr int OFF_YH = OFF_CT + T128;       // dy hi
+  static constexpr int OFF_YL = OFF_YH + T128;       // dy lo
+  static constexpr int OFF_X = OFF_YL + T128;        // x
+  static constexpr int OFF_HH = OFF_X + T128;        // Hin slab hi, lo
+  static constexpr int OFF_HL = OFF_HH + T64;
+  static constexpr int OFF_DH = OFF_HL + T64;        // dS slab hi, lo
+  static constexpr int OFF_DL = OFF_DH + T64;
+  static constexpr int TOTAL = OFF_DL + T64;
 };
-static_assert(DbcLds::TOTAL <= 81920, "two workgroups per CU");
+static_assert(DbcLds::TOTAL <= 163840, "one workgroup per CU");
 
-__global__ __launch_bounds__(256, 2) void k_bwd_dbc(BwdChunkArgs a) {
+__global__ __launch_bounds__(512, 1) void k_bwd_dbc(BwdChunkArgs a) {
   __shared__ __align__(16) char smem[DbcLds::TOTAL];
   double* s_cs = reinterpret_cast<double*>(smem + DbcLds::OFF_CS);
   float* s_f = reinterpret_cast<float*>(smem + DbcLds::OFF_F);
@@ -765,8 +774,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dbc(BwdChunkArgs a) {
   double* s_tmp = reinterpret_cast<double*>(smem + DbcLds::OFF_TMP);
   bf16* s_bt = reinterpret_cast<bf16*>(smem + DbcLds::OFF_BT);
   bf16* s_ct = reinterpret_cast<bf16*>(smem + DbcLds::OFF_CT);
-  bf16* s_sh = reinterpret_cast<bf16*>(smem + DbcLds::OFF_SH);
-  bf16* s_sl = reinterpret_cast<bf16*>(smem + DbcLds::OFF_SL);
+  bf16* s_yh = reinterpret_cast<bf16*>(smem + DbcLds::OFF_YH);
+  bf16* s_yl = reinterpret_cast<bf16*>(smem + DbcLds::OFF_YL);
+  bf16* s_x = reinterpret_cast<bf16*>(smem + DbcLds::OFF_X);
+  bf16* s_hh = reinterpret_cast<bf16*>(smem + DbcLds::OFF_HH);
+  bf16* s_hl = reinterpret_cast<bf16*>(smem + DbcLds::OFF_HL);
+  bf16* s_dh = reinterpret_cast<bf16*>(smem + DbcLds::OFF_DH);
+  bf16* s_dl = reinterpret_cast<bf16*>(smem + DbcLds::OFF_DL);
 
   const Geo& g = a.g;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -787,15 +801,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dbc(BwdChunkArgs a) {
   const int nw = min(64, g.N - n0);  // columns of this slab
   const int64_t PN = (int64_t)g.P * g.N;
   const int tp0 = c.b * g.T + c.t0;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+
   // ---- B and C slabs of the chunk (rows past the chunk, columns past N: 0)
   {
     const bf16* bb = row_ptr<bf16>(a.B, c.b, c.t0, grp) + n0;
     const bf16* cb = row_ptr<bf16>(a.C, c.b, c.t0, grp) + n0;
     const int row0 = tid / 8, col = (tid % 8) * 8;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int l = row0 + 32 * k;
+    for (int k = 0; k < 2; ++k) {
+      const int l = row0 + 64 * k;
       const int lc = min(l, len - 1), cc = min(col, nw - 8);
       const bool ok = l < len && col < nw;
       const u32x4 vb = *reinterpret_cast<const u32x4*>(at(bb, (uint32_t)(lc * a.B.s1 + cc)));
@@ -805,193 +820,196 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dbc(BwdChunkArgs a) {
     }
   }
 
-  const int ltA = wave, ltB = 7 - wave;
-  f32x4 dc[2][4], db[2][4];
+  const bool dc_side = wave < 4;
+  const int w4 = wave & 3;
+  const int tA = w4, tB = 7 - w4;  // l-tiles (dC side) or s-tiles (dB side)
+  f32x4 acc[2][4];
 #pragma unroll
   for (int ui = 0; ui < 2; ++ui)
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      dc[ui][nt] = zero4();
-      db[ui][nt] = zero4();
-    }
-
-  // dy = dout silu(z): row fragment (8 consecutive p) of token l of the chunk;
-  // rows past the chunk read as zero
-  auto dy_row = [&](int h, int l, int kp) -> f32x8 {
-    const int lc = min(l, len - 1), col = kp * 32 + q * 8;
-    f32x8 v;
-    if (a.dout_bf16) {
-      const bf16* db = row_ptr<bf16>(a.dout, c.b, c.t0, h);
-      v = bf8_to_f32(*reinterpret_cast<const u32x4*>(at(db, (uint32_t)(lc * a.dout.s1 + col))));
-    } else {
-      v = load8f(at(row_ptr<float>(a.dout, c.b, c.t0, h), (uint32_t)(lc * a.dout.s1 + col)));
-    }
-    if (a.z.p) {
-      const f32x8 zz = bf8_to_f32(*reinterpret_cast<const u32x4*>(
-          at(row_ptr<bf16>(a.z, c.b, c.t0, h), (uint32_t)(lc * a.z.s1 + col))));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] *= zz[i] * sigmoidf(zz[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = l < len ? v[i] : 0.0f;
-    return v;
-  };
-  auto x_row = [&](const bf16* xb, int s, int kp) -> u32x4 {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(
-        at(xb, (uint32_t)(min(s, len - 1) * a.x.s1 + kp * 32 + q * 8)));
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-    return s < len ? v : zero;
-  };
-  // stage rows p of a (P x N) fp32 state slab, times `scale`, as bf16 hi + lo
-  auto stage_state = [&](const float* st, float scale) {
-    const int p = tid / 4, cbase = (tid % 4) * 16;
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int col = cbase + 8 * k;
-      f32x8 v;
-      if (st) {
-        v = load8f(st + (int64_t)p * g.N + n0 + min(col, nw - 8));
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = col < nw ? v[i] * scale : 0.0f;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = 0.0f;
-      }
-      const FragSplit sp = split_f32x8(v);
-      *reinterpret_cast<bf16x8*>(&s_sh[p * TLD + col]) = sp.hi;
-      *reinterpret_cast<bf16x8*>(&s_sl[p * TLD + col]) = sp.lo;
-    }
-  };
+    for (int nt = 0; nt < 4; ++nt) acc[ui][nt] = zero4();
 
   for (int h = h_lo; h < h_hi; ++h) {
     ChunkCtx cx;
     chunk_ctx(a, j, h, cx);
-    __syncthreads();  // the previous head is done with the cumsum and the state slab
-    stage_cumsum(a, cx, h, s_cs, s_f, s_tmp);
-    const double lam = s_cs[len - 1];
+    __syncthreads();  // the previous head is done with every staged tile
+    // ---- stage: cumsum (waves 0-1), dy = dout silu(z) (hi + lo) and x rows,
+    // the Hin and dS slabs (hi + lo)
+    if (tid < 256) stage_cumsum_partial(a, cx, h, s_cs, s_f);
+    {
+      const int row0 = tid / 8, col = (tid % 8) * 8;
+      const bf16* xb = row_ptr<bf16>(a.x, c.b, c.t0, h);
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int l = row0 + 64 * k, lc = min(l, len - 1);
+        const bool in = l < len;
+        f32x8 v;
+        if (a.dout_bf16) {
+          const bf16* db = row_ptr<bf16>(a.dout, c.b, c.t0, h);
+          v = bf8_to_f32(*reinterpret_cast<const u32x4*>(at(db, (uint32_t)(lc * a.dout.s1 + col))));
+        } else {
+          v = load8f(at(row_ptr<float>(a.dout, c.b, c.t0, h), (uint32_t)(lc * a.dout.s1 + col)));
+        }
+        if (a.z.p) {
+          const f32x8 zz = bf8_to_f32(*reinterpret_cast<const u32x4*>(
+              at(row_ptr<bf16>(a.z, c.b, c.t0, h), (uint32_t)(lc * a.z.s1 + col))));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] *= zz[i] * sigmoidf(zz[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = in ? v[i] : 0.0f;
+        const FragSplit spl = split_f32x8(v);
+        *reinterpret_cast<bf16x8*>(&s_yh[l * TLD + col]) = spl.hi;
+        *reinterpret_cast<bf16x8*>(&s_yl[l * TLD + col]) = spl.lo;
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(at(xb, (uint32_t)(lc * a.x.s1 + col)));
+        *reinterpret_cast<u32x4*>(&s_x[l * TLD + col]) = in ? xv : zero;
+      }
+      // state slabs: 64 rows p x 64 columns, 8 per thread
+      const int p = tid / 8;
+      const float* hsrc = a.hin + ((int64_t)j * g.H + h) * PN + (int64_t)p * g.N + n0;
+      const float* dsrc = cx.ds + (int64_t)p * g.N + n0;
+      f32x8 hv = load8f(hsrc + min(col, nw - 8)), dv = load8f(dsrc + min(col, nw - 8));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        hv[i] = col < nw ? hv[i] : 0.0f;
+        dv[i] = col < nw ? dv[i] : 0.0f;
+      }
+      const FragSplit hs = split_f32x8(hv), ds = split_f32x8(dv);
+      *reinterpret_cast<bf16x8*>(&s_hh[p * TLD + col]) = hs.hi;
+      *reinterpret_cast<bf16x8*>(&s_hl[p * TLD + col]) = hs.lo;
+      *reinterpret_cast<bf16x8*>(&s_dh[p * TLD + col]) = ds.hi;
+      *reinterpret_cast<bf16x8*>(&s_dl[p * TLD + col]) = ds.lo;
+    }
+    stage_cumsum_finish(s_cs, s_tmp);
     if (tid < BC) {
       const bool in = tid < len;
+      const double lam = s_cs[len - 1];
       s_el[tid] = in ? exp_d(s_cs[tid]) : 0.0f;
       s_es[tid] = in ? s_f[tid] * exp_d(lam - s_cs[tid]) : 0.0f;
     }
-    stage_state(a.hin + ((int64_t)j * g.H + h) * PN, 1.0f);
-    __syncthreads();
-    const bf16* xb = row_ptr<bf16>(a.x, c.b, c.t0, h);
-
-    // ---- dC for l-tiles ltA, ltB: intra sum_s (L o dy.x^T f)_ls B_s (layout
-    // A tiles: dy.x^T computed as [s][l]) and inter exp(cs_l) dy_l Hin
-#pragma unroll
-    for (int ui = 0; ui < 2; ++ui) {
-      const int lt = ui ? ltB : ltA;
-      const int l = lt * 16 + r16;
-      FragSplit dyf[2];
-      f32x8 dyv[2];
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        dyv[kp] = dy_row(h, l, kp);
-        dyf[kp] = split_f32x8(dyv[kp]);
-      }
-      const double csl = s_cs[l];
-      for (int kp2 = 0; kp2 <= lt / 2; ++kp2) {
-        const int sa = 2 * kp2, sb = 2 * kp2 + 1;
-        f32x4 va = zero4(), vb = zero4();
-#pragma unroll
-        for (int kp = 0; kp < 2; ++kp) {
-          mma(va, as_frag(x_row(xb, sa * 16 + r16, kp)), dyf[kp]);
-          mma(vb, as_frag(x_row(xb, sb * 16 + r16, kp)), dyf[kp]);
-        }
-        f32x8 w;
-#pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int s_a = sa * 16 + q * 4 + e4, s_b = sb * 16 + q * 4 + e4;
-          w[e4] = s_a <= l ? exp_d(csl - s_cs[s_a]) * s_f[s_a] * va[e4] : 0.0f;
-          w[4 + e4] = s_b <= l ? exp_d(csl - s_cs[s_b]) * s_f[s_b] * vb[e4] : 0.0f;
-        }
-        const FragSplit wf = split_f32x8(w);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          FragBF bt;
-          bt.v = lds_frag_tr(s_bt, TLD, sa * 16 + q * 4, sb * 16 + q * 4, nt * 16);
-          mma(dc[ui][nt], wf, bt);
-        }
-      }
-      const float el = s_el[min(l, BC - 1)];
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        f32x8 v = dyv[kp];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] *= el;
-        const FragSplit af = split_f32x8(v);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          FragSplit hs;
-          hs.hi = lds_frag_tr(s_sh, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
-          hs.lo = lds_frag_tr(s_sl, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
-          mma(dc[ui][nt], af, hs);
-        }
-      }
-    }
-    __syncthreads();  // the Hin slab is dead: dS takes its place
-    stage_state(cx.ds, 1.0f);
     __syncthreads();
 
-    // ---- dB for s-tiles ltA, ltB: intra f_s sum_l (L o dy.x^T)_ls C_l (layout
-    // B tiles: dy.x^T as [l][s]) and inter f_s exp(Lambda - cs_s) x_s dS
+    if (dc_side) {
+      // ---- dC_l += sum_s (L o dy.x^T f)_ls B_s + exp(cs_l) dy_l Hin, for l-tiles
+      // tA, tB (dy.x^T as [s][l] tiles: the A operand of the product over s)
 #pragma unroll
-    for (int ui = 0; ui < 2; ++ui) {
-      const int sbt = ui ? ltB : ltA;
-      const int s = sbt * 16 + r16;
-      u32x4 xr[2];
+      for (int ui = 0; ui < 2; ++ui) {
+        const int lt = ui ? tB : tA;
+        const int l = lt * 16 + r16;
+        FragSplit dyf[2];
 #pragma unroll
-      for (int kp = 0; kp < 2; ++kp) xr[kp] = x_row(xb, s, kp);
-      const double css = s_cs[s];
-      const float fs = s_f[min(s, BC - 1)];
-      for (int lp = sbt / 2; lp < 4; ++lp) {
-        const int la = 2 * lp, lb = 2 * lp + 1;
-        f32x4 va = zero4(), vb = zero4();
+        for (int kp = 0; kp < 2; ++kp)
+          dyf[kp] = lds_split(&s_yh[l * TLD + kp * 32 + q * 8], &s_yl[l * TLD + kp * 32 + q * 8]);
+        const double csl = s_cs[l];
+        for (int kp2 = 0; kp2 <= lt / 2; ++kp2) {
+          const int sa = 2 * kp2, sb = 2 * kp2 + 1;
+          f32x4 va = zero4(), vb = zero4();
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp) {
+            FragBF xa, xb2;
+            xa.v = *reinterpret_cast<const bf16x8*>(&s_x[(sa * 16 + r16) * TLD + kp * 32 + q * 8]);
+            xb2.v = *reinterpret_cast<const bf16x8*>(&s_x[(sb * 16 + r16) * TLD + kp * 32 + q * 8]);
+            mma(va, xa, dyf[kp]);
+            mma(vb, xb2, dyf[kp]);
+          }
+          f32x8 w;
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int s_a = sa * 16 + q * 4 + e4, s_b = sb * 16 + q * 4 + e4;
+            w[e4] = s_a <= l ? exp_d(csl - s_cs[s_a]) * s_f[s_a] * va[e4] : 0.0f;
+            w[4 + e4] = s_b <= l ? exp_d(csl - s_cs[s_b]) * s_f[s_b] * vb[e4] : 0.0f;
+          }
+          const FragSplit wf = split_f32x8(w);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            FragBF bt;
+            bt.v = lds_frag_tr(s_bt, TLD, sa * 16 + q * 4, sb * 16 + q * 4, nt * 16);
+            mma(acc[ui][nt], wf, bt);
+          }
+        }
+        const float el = s_el[l];
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
-          mma(va, split_f32x8(dy_row(h, la * 16 + r16, kp)), as_frag(xr[kp]));
-          mma(vb, split_f32x8(dy_row(h, lb * 16 + r16, kp)), as_frag(xr[kp]));
-        }
-        f32x8 w;
+          f32x8 v = bf8_to_f32(__builtin_bit_cast(u32x4, dyf[kp].hi));
+          const f32x8 lo = bf8_to_f32(__builtin_bit_cast(u32x4, dyf[kp].lo));
 #pragma unroll
-        for (int e4 = 0; e4 < 4; ++e4) {
-          const int l_a = la * 16 + q * 4 + e4, l_b = lb * 16 + q * 4 + e4;
-          w[e4] = s <= l_a ? exp_d(s_cs[l_a] - css) * fs * va[e4] : 0.0f;
-          w[4 + e4] = s <= l_b ? exp_d(s_cs[l_b] - css) * fs * vb[e4] : 0.0f;
-        }
-        const FragSplit wf = split_f32x8(w);
+          for (int i = 0; i < 8; ++i) v[i] = (v[i] + lo[i]) * el;
+          const FragSplit af = split_f32x8(v);
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          FragBF ct;
-          ct.v = lds_frag_tr(s_ct, TLD, la * 16 + q * 4, lb * 16 + q * 4, nt * 16);
-          mma(db[ui][nt], wf, ct);
+          for (int nt = 0; nt < 4; ++nt) {
+            FragSplit hs;
+            hs.hi = lds_frag_tr(s_hh, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
+            hs.lo = lds_frag_tr(s_hl, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
+            mma(acc[ui][nt], af, hs);
+          }
         }
       }
-      const float es = s_es[min(s, BC - 1)];
+    } else {
+      // ---- dB_s += f_s sum_l (L o dy.x^T)_ls C_l + f_s exp(Lambda - cs_s) x_s dS,
+      // for s-tiles tA, tB (dy.x^T as [l][s] tiles: the A operand of the
+      // product over l)
 #pragma unroll
-      for (int kp = 0; kp < 2; ++kp) {
-        f32x8 v = bf8_to_f32(xr[kp]);
+      for (int ui = 0; ui < 2; ++ui) {
+        const int sbt = ui ? tB : tA;
+        const int s = sbt * 16 + r16;
+        FragBF xr[2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] *= es;
-        const FragSplit af = split_f32x8(v);
+        for (int kp = 0; kp < 2; ++kp)
+          xr[kp].v = *reinterpret_cast<const bf16x8*>(&s_x[s * TLD + kp * 32 + q * 8]);
+        const double css = s_cs[s];
+        const float fs = s_f[s];
+        for (int lp = sbt / 2; lp < 4; ++lp) {
+          const int la = 2 * lp, lb = 2 * lp + 1;
+          f32x4 va = zero4(), vb = zero4();
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          FragSplit ds;
-          ds.hi = lds_frag_tr(s_sh, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
-          ds.lo = lds_frag_tr(s_sl, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
-          mma(db[ui][nt], af, ds);
+          for (int kp = 0; kp < 2; ++kp) {
+            const int pc = kp * 32 + q * 8;
+            mma(va, lds_split(&s_yh[(la * 16 + r16) * TLD + pc], &s_yl[(la * 16 + r16) * TLD + pc]),
+                xr[kp]);
+            mma(vb, lds_split(&s_yh[(lb * 16 + r16) * TLD + pc], &s_yl[(lb * 16 + r16) * TLD + pc]),
+                xr[kp]);
+          }
+          f32x8 w;
+#pragma unroll
+          for (int e4 = 0; e4 < 4; ++e4) {
+            const int l_a = la * 16 + q * 4 + e4, l_b = lb * 16 + q * 4 + e4;
+            w[e4] = s <= l_a ? exp_d(s_cs[l_a] - css) * fs * va[e4] : 0.0f;
+            w[4 + e4] = s <= l_b ? exp_d(s_cs[l_b] - css) * fs * vb[e4] : 0.0f;
+          }
+          const FragSplit wf = split_f32x8(w);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            FragBF ct;
+            ct.v = lds_frag_tr(s_ct, TLD, la * 16 + q * 4, lb * 16 + q * 4, nt * 16);
+            mma(acc[ui][nt], wf, ct);
+          }
+        }
+        const float es = s_es[s];
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp) {
+          f32x8 v = bf8_to_f32(__builtin_bit_cast(u32x4, xr[kp].v));
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] *= es;
+          const FragSplit af = split_f32x8(v);
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            FragSplit ds;
+            ds.hi = lds_frag_tr(s_dh, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
+            ds.lo = lds_frag_tr(s_dl, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
+            mma(acc[ui][nt], af, ds);
+          }
         }
       }
     }
   }
 
   // ---- store: accumulator tile [row][n], lane: column n = 16 nt + r16, rows
-  // 4 q + 0..3
+  // 4 q + 0..3; dC from waves 0-3, dB from waves 4-7
+  const TArg& out = dc_side ? a.dC : a.dB;
+  float* part = dc_side ? a.pdc : a.pdb;
 #pragma unroll
   for (int ui = 0; ui < 2; ++ui) {
-    const int rt = ui ? ltB : ltA;
+    const int rt = ui ? tB : tA;
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
       const int n = nt * 16 + r16;
@@ -1001,12 +1019,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dbc(BwdChunkArgs a) {
         const int r = rt * 16 + q * 4 + i;
         if (r >= len) continue;
         if (a.nsplit == 1) {
-          row_ptr_mut<float>(a.dC, c.b, c.t0 + r, grp)[n0 + n] = dc[ui][nt][i];
-          row_ptr_mut<float>(a.dB, c.b, c.t0 + r, grp)[n0 + n] = db[ui][nt][i];
+          row_ptr_mut<float>(out, c.b, c.t0 + r, grp)[n0 + n] = acc[ui][nt][i];
         } else {
-          const int64_t o = (((int64_t)sp * a.ntok + tp0 + r) * g.G + grp) * g.N + n0 + n;
-          a.pdc[o] = dc[ui][nt][i];
-          a.pdb[o] = db[ui][nt][i];
+          part[(((int64_t)sp * a.ntok + tp0 + r) * g.G + grp) * g.N + n0 + n] = acc[ui][nt][i];
         }
       }
     }
@@ -1076,12 +1091,12 @@ hipError_t launch_bwd_chunk(const BwdChunkLaunch& l, hipStream_t s) {
   if (g.K <= 0) return hipSuccess;  // (dead chunk slots in packed mode exit at once)
   const BwdChunkArgs a = chunk_args(l);
   const unsigned nx = (unsigned)((int64_t)g.K * g.H);
-  if (g.N <= 64) hipLaunchKernelGGL(k_bwd_dx<4>, dim3(nx), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_bwd_dx<8>, dim3(nx), dim3(256), 0, s, a);
+  if (g.N <= 64) hipLaunchKernelGGL(k_bwd_dx<4>, dim3(nx), dim3(512), 0, s, a);
+  else hipLaunchKernelGGL(k_bwd_dx<8>, dim3(nx), dim3(512), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const unsigned nb = (unsigned)((int64_t)g.K * g.G * a.nsplit * a.nsl);
-  hipLaunchKernelGGL(k_bwd_dbc, dim3(nb), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(k_bwd_dbc, dim3(nb), dim3(512), 0, s, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.nsplit == 1) return e;
   hipLaunchKernelGGL(k_bwd_dbc_sum, dim3((unsigned)((int64_t)g.K * g.G)), dim3(256), 0, s, a);
