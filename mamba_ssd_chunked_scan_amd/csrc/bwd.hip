@@ -563,14 +563,29 @@ __global__ __launch_bounds__(256) void k_step_heads(BwdGeo q, int K, const doubl
                                                     const float* gfirst, float* dA,
                                                     float* ddt_bias, float* dD, float* dh0) {
   const int h = blockIdx.x, tid = threadIdx.x;
-  if (tid == 0) {
-    double a = 0.0, b = 0.0, x = 0.0;
-    for (int j = 0; j < K; ++j) {
-      const double* pj = part + ((int64_t)j * q.H + h) * 3;
-      a += pj[0];
-      b += pj[1];
-      x += pj[2];
+  // the chunks' shares are loaded 256 at a time by all threads and added by
+  // one, in chunk order
+  __shared__ double s_p[3][256];
+  double a = 0.0, b = 0.0, x = 0.0;
+  for (int j0 = 0; j0 < K; j0 += 256) {
+    if (j0 + tid < K) {
+      const double* pj = part + ((int64_t)(j0 + tid) * q.H + h) * 3;
+      s_p[0][tid] = pj[0];
+      s_p[1][tid] = pj[1];
+      s_p[2][tid] = pj[2];
     }
+    __syncthreads();
+    if (tid == 0) {
+      const int n = min(256, K - j0);
+      for (int k = 0; k < n; ++k) {
+        a += s_p[0][k];
+        b += s_p[1][k];
+        x += s_p[2][k];
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
     dA[h] = (float)a;
     ddt_bias[h] = (float)b;
     if (dD) dD[h] = (float)x;

@@ -829,30 +829,52 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dbc(BwdChunkArgs a) {
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) acc[ui][nt] = zero4();
 
+  // The next head's rows are loaded into registers while the current head is
+  // multiplied (the products read LDS only, so the loads overlap them): dout
+  // (or its bf16), z and x rows (2 x 8 columns each), and 8 columns of one row
+  // of the Hin and dS slabs.
+  const int row0 = tid / 8, col = (tid % 8) * 8;
+  struct Pre {
+    f32x8 go[2];
+    u32x4 zv[2], xv[2];
+    f32x8 hv, dv;
+  } pre;
+  auto issue = [&](int h) {
+    const bf16* xb = row_ptr<bf16>(a.x, c.b, c.t0, h);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int lc = min(row0 + 64 * k, len - 1);
+      if (a.dout_bf16) {
+        const bf16* db = row_ptr<bf16>(a.dout, c.b, c.t0, h);
+        pre.go[k] = bf8_to_f32(*reinterpret_cast<const u32x4*>(at(db, (uint32_t)(lc * a.dout.s1 + col))));
+      } else {
+        pre.go[k] = load8f(at(row_ptr<float>(a.dout, c.b, c.t0, h), (uint32_t)(lc * a.dout.s1 + col)));
+      }
+      pre.zv[k] = a.z.p ? *reinterpret_cast<const u32x4*>(
+                              at(row_ptr<bf16>(a.z, c.b, c.t0, h), (uint32_t)(lc * a.z.s1 + col)))
+                        : zero;
+      pre.xv[k] = *reinterpret_cast<const u32x4*>(at(xb, (uint32_t)(lc * a.x.s1 + col)));
+    }
+    const int p = tid / 8;
+    pre.hv = load8f(a.hin + ((int64_t)j * g.H + h) * PN + (int64_t)p * g.N + n0 + min(col, nw - 8));
+    pre.dv = load8f(a.adj + ((int64_t)j * g.H + h) * PN + (int64_t)p * g.N + n0 + min(col, nw - 8));
+  };
+  issue(h_lo);
   for (int h = h_lo; h < h_hi; ++h) {
     ChunkCtx cx;
     chunk_ctx(a, j, h, cx);
     __syncthreads();  // the previous head is done with every staged tile
     // ---- stage: cumsum (waves 0-1), dy = dout silu(z) (hi + lo) and x rows,
-    // the Hin and dS slabs (hi + lo)
-    if (tid < 256) stage_cumsum_partial(a, cx, h, s_cs, s_f);
+    // the Hin and dS slabs (hi + lo), from the registers loaded above
+    stage_cumsum_partial(a, cx, h, s_cs, s_f);
     {
-      const int row0 = tid / 8, col = (tid % 8) * 8;
-      const bf16* xb = row_ptr<bf16>(a.x, c.b, c.t0, h);
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const int l = row0 + 64 * k, lc = min(l, len - 1);
+        const int l = row0 + 64 * k;
         const bool in = l < len;
-        f32x8 v;
-        if (a.dout_bf16) {
-          const bf16* db = row_ptr<bf16>(a.dout, c.b, c.t0, h);
-          v = bf8_to_f32(*reinterpret_cast<const u32x4*>(at(db, (uint32_t)(lc * a.dout.s1 + col))));
-        } else {
-          v = load8f(at(row_ptr<float>(a.dout, c.b, c.t0, h), (uint32_t)(lc * a.dout.s1 + col)));
-        }
+        f32x8 v = pre.go[k];
         if (a.z.p) {
-          const f32x8 zz = bf8_to_f32(*reinterpret_cast<const u32x4*>(
-              at(row_ptr<bf16>(a.z, c.b, c.t0, h), (uint32_t)(lc * a.z.s1 + col))));
+          const f32x8 zz = bf8_to_f32(pre.zv[k]);
 #pragma unroll
           for (int i = 0; i < 8; ++i) v[i] *= zz[i] * sigmoidf(zz[i]);
         }
@@ -861,14 +883,10 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dbc(BwdChunkArgs a) {
         const FragSplit spl = split_f32x8(v);
         *reinterpret_cast<bf16x8*>(&s_yh[l * TLD + col]) = spl.hi;
         *reinterpret_cast<bf16x8*>(&s_yl[l * TLD + col]) = spl.lo;
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(at(xb, (uint32_t)(lc * a.x.s1 + col)));
-        *reinterpret_cast<u32x4*>(&s_x[l * TLD + col]) = in ? xv : zero;
+        *reinterpret_cast<u32x4*>(&s_x[l * TLD + col]) = in ? pre.xv[k] : zero;
       }
-      // state slabs: 64 rows p x 64 columns, 8 per thread
       const int p = tid / 8;
-      const float* hsrc = a.hin + ((int64_t)j * g.H + h) * PN + (int64_t)p * g.N + n0;
-      const float* dsrc = cx.ds + (int64_t)p * g.N + n0;
-      f32x8 hv = load8f(hsrc + min(col, nw - 8)), dv = load8f(dsrc + min(col, nw - 8));
+      f32x8 hv = pre.hv, dv = pre.dv;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         hv[i] = col < nw ? hv[i] : 0.0f;
@@ -888,6 +906,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dbc(BwdChunkArgs a) {
       s_es[tid] = in ? s_f[tid] * exp_d(lam - s_cs[tid]) : 0.0f;
     }
     __syncthreads();
+    // (past the last head this reloads it, unused)
+    issue(min(h + 1, h_hi - 1));
 
     if (dc_side) {
       // ---- dC_l += sum_s (L o dy.x^T f)_ls B_s + exp(cs_l) dy_l Hin, for l-tiles
