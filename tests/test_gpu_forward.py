@@ -169,6 +169,30 @@ def test_chunk_size_invariance(C, algo):
     check(w, y, f, ref)
 
 
+def test_fused_chunk_is_internal_and_matches_staged_at_every_chunk_size():
+    # The fused path always works on 128-token chunks (chunk invariance makes
+    # the chunk length a tiling choice): any chunk_size gives the same bits.
+    # Its result is then held against the staged path at each chunk size
+    # 32..256 (bf16 inputs, ragged tail, groups, initial states, gate), which
+    # is where the chunk length really changes the computation.
+    inp = None
+    outs = {}
+    for C in (32, 64, 128, 256):
+        w = small_workload("inv16", seqlen=700, nheads=4, headdim=64, ngroups=2, dstate=64,
+                           chunk_size=C)
+        if inp is None:
+            inp = with_initial_states(make_inputs(w))
+            ref = oracle_run(inp)
+        outs[C] = (run_gpu(inp, w, "fused"), run_gpu(inp, w, "staged"))
+    (fy, ff), _ = outs[128]
+    for C, ((y, f), (sy, sf)) in outs.items():
+        assert torch.equal(y, fy) and torch.equal(f, ff), C
+        check(w, sy, sf, ref)
+        assert err(to_np(y), to_np(sy)) <= TOL_BF16_DESIGN, C
+        assert err(to_np(f), to_np(sf)) <= TOL_BF16_DESIGN, C
+    check(w, fy, ff, ref)
+
+
 OPTION_CASES = {
     "no_D_no_z": dict(has_D=False, has_z=False),
     "z_only": dict(has_D=False, has_z=True),
