@@ -245,3 +245,17 @@ def test_bit_identical_repeats():
     g2 = gpu_bwd(w, inp, dout, dfin, "fused")
     for n in NAMES:
         assert torch.equal(getattr(g1, n), getattr(g2, n)), n
+
+
+def test_full_size_granite_every_gradient():
+    # granite-4.0-h-small dims (4096 tokens, 128 heads x 64 in one group,
+    # d_state 128): every gradient of the whole problem against the oracle,
+    # dB and dC summed over all 128 heads (16 head splits and their reduction)
+    from mamba_ssd_chunked_scan_amd.inputs import WORKLOADS
+    w = WORKLOADS["granite"]
+    inp = make_inputs(w)
+    dout, dfin = upstream(inp, seed=11)
+    ref = oracle.ssd_bwd(inp.x, inp.B, inp.C, inp.dt, inp.A, dout, dt_bias=inp.dt_bias, D=inp.D,
+                         z=inp.z, dfinal_states=dfin, threads=16)
+    g = gpu_bwd(w, inp, dout, dfin, "fused")
+    check(g, ref)
