@@ -54,6 +54,43 @@ def test_two_streams_at_once_match_serial_runs():
         assert torch.equal(ob[0], rb[0]) and torch.equal(ob[1], rb[1])
 
 
+def test_backward_paths_on_two_streams_match_serial_runs():
+    # the per-chunk and the staged backward at once on two streams (each call
+    # allocates its own workspace and gradients on its stream), against the
+    # same calls run one after the other
+    w = small_workload("bs", seqlen=1500, nheads=16, headdim=64, ngroups=2, dstate=128,
+                       chunk_size=128)
+    inp = with_initial_states(make_inputs(w))
+    dev = device_inputs(inp, torch.bfloat16)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    dout = torch.randn(dev["x"].shape, generator=g, device="cuda")
+
+    def bwd(algo, stream=None):
+        return ssd.ssd_backward(dev["x"], dev["B"], dev["C"], dev["dt"], dev["A"], dout,
+                                dt_bias=dev["dt_bias"], D=dev["D"], z=dev["z"],
+                                initial_states=dev["initial_states"], chunk_size=128,
+                                algo=algo, stream=stream)
+
+    rf, rs = bwd("fused"), bwd("staged")
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            of = bwd("fused", stream=s1)
+        with torch.cuda.stream(s2):
+            os_ = bwd("staged", stream=s2)
+        outs.append((of, os_))
+    torch.cuda.synchronize()
+    names = ("dx", "dB", "dC", "ddt", "dA", "ddt_bias", "dD", "dz", "dinitial_states")
+    for of, os_ in outs:
+        for n in names:
+            assert torch.equal(getattr(of, n), getattr(rf, n)), n
+            assert torch.equal(getattr(os_, n), getattr(rs, n)), n
+
+
 def test_side_stream_temporaries_are_not_reused_early():
     # the binding allocates the workspace and outputs on the stream it launches
     # on; a busy current stream allocating and freeing at the same time must
