@@ -68,7 +68,7 @@ namespace ssd {
 namespace {
 
 constexpr int FC = 128;                 // internal chunk length
-constexpr int kLookback = 4;            // aggregates loaded per round trip of the fold
+constexpr int kFoldBatch = 4;           // aggregates loaded per round trip of the fold
 
 // softplus(u) = max(u, 0) + log1p(exp(-|u|)).  log1p(e) for e in (0, 1] as
 // log(1 + e) * e / ((1 + e) - 1): the quotient corrects the rounding of 1 + e
@@ -412,7 +412,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   get_chunk(g, j0, cfirst);
   int f0, l0;
   seq_chunks(g, cfirst.seq, f0, l0);
-  const bool need_lb = f0 < j0;        // the first chunk continues a sequence
+  const bool need_fold = f0 < j0;        // the first chunk continues a sequence
 
   f32x4 carry[NT];
 
@@ -420,20 +420,20 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
 
   // ---- carry-in: the aggregates of the preceding ranges back to the one
   // where the sequence starts (whose aggregate starts from the initial
-  // state), folded oldest first: carry = E_rr carry + agg_rr, kLookback
+  // state), folded oldest first: carry = E_rr carry + agg_rr, kFoldBatch
   // aggregates per round trip to memory.  They were written by the aggregate
   // launch, which has ended, so nothing is waited for.
-  if (need_lb) {
+  if (need_fold) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) carry[nt] = zero4();
     const int first = f0 / a.R, n = r - first;
-    for (int b = 0; b < n; b += kLookback) {
+    for (int b = 0; b < n; b += kFoldBatch) {
       // (loads past the n available repeat the last one, unused: loads under
       // a branch would leave the compiler's wait counts conservative)
-      f32x4 v[kLookback][NT];
-      float e[kLookback];
+      f32x4 v[kFoldBatch][NT];
+      float e[kFoldBatch];
 #pragma unroll
-      for (int m = 0; m < kLookback; ++m) {
+      for (int m = 0; m < kFoldBatch; ++m) {
         const int rm = first + min(b + m, n - 1);
         const float* src = slot_base(rm);
         const uint32_t lo = slot_lane();
@@ -443,7 +443,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
         e[m] = a.edec[rm * a.U + u];
       }
 #pragma unroll
-      for (int m = 0; m < kLookback; ++m) {
+      for (int m = 0; m < kFoldBatch; ++m) {
         // an unused term folds as carry * 1 + 0, which leaves carry as it is
         const bool ok = b + m < n;
         const float em = ok ? e[m] : 1.0f, wm = ok ? 1.0f : 0.0f;
@@ -462,7 +462,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
   load_chunk(st, c, false);
 
   SSD_TRACE(3);
-  // ---- pass 2: outputs, chunk by chunk.  Per chunk:
+  // ---- the outputs, chunk by chunk.  Per chunk:
   //   A  the carry-in H_j (the initial state at a sequence's first chunk,
   //      loaded during the previous chunk) to LDS as bf16 hi + lo (the cumsum
   //      was staged at the end of the previous chunk)
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
       get_chunk(g, j + 1, cn);
       if (cn.seq != c.seq) seq_chunks(g, cn.seq, fn, ln);
     }
-    load_chunk(st, cn, false);  // unconditional, as in pass 1
+    load_chunk(st, cn, false);  // unconditional (past the range it reloads the last chunk)
     __syncthreads();
 
     if (kk < 4) SSD_TRACE(6 + 5 * kk);
@@ -648,7 +648,7 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
     // before the C fragments, so that waiting for it does not wait for them.
     __builtin_amdgcn_s_setprio(0);
     if (more && fn == j + 1) load_h0(carry, cn.seq);
-    load_cfr(cn);  // unconditional, as in pass 1
+    load_cfr(cn);  // unconditional (past the range it reloads the last chunk)
     __syncthreads();  // the B tile is dead: its space takes y
     if (kk < 4) SSD_TRACE(7 + 5 * kk);
 
