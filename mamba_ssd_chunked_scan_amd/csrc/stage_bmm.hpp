@@ -88,4 +88,87 @@ __device__ __forceinline__ void bmm_wave(const Geo& g, const TArg& Cm, const TAr
   }
 }
 
+// bf16 inputs, C <= 128: one workgroup of four waves per (chunk, group), the
+// whole causal half in one round.  Wave w owns l-tile w and, at C = 128, also
+// l-tile 7 - w, so every wave computes nine causal tiles (the causal triangle
+// split evenly).  s-tiles come in batches of four; the l-tile of slot u needs
+// batches 0..u, and batch 0 serves both slots, so each B fragment a wave needs
+// is loaded once.  Every load of a 128-wide block of N (the C fragments of
+// both l-tiles and the B fragments of both batches, 40 x 16 B per lane) is
+// issued before the first matrix instruction.  The k-blocks accumulate in the
+// same order as in bmm_wave, so both give the same bits.
+template <int C>
+__device__ __forceinline__ void bmm_group_bf16(const Geo& g, const TArg& Cm, const TArg& Bm,
+                                               float* CB, int j, int grp) {
+  constexpr int NLT = C / 16;
+  constexpr int LTW = NLT >= 8 ? 2 : 1;  // l-tile slots per wave
+  static_assert(C <= 128, "one workgroup covers at most eight l-tiles");
+  Chunk c;
+  if (!get_chunk(g, j, c)) return;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (wave >= NLT) return;  // C = 32: two l-tiles
+  const int r16 = lane % 16, q = lane / 16;
+  const int N = g.N;
+  float* out = CB + ((int64_t)j * g.G + grp) * C * C;
+  int lt[LTW];
+  lt[0] = wave;
+  if (LTW == 2) lt[LTW - 1] = NLT - 1 - wave;
+
+  f32x4 acc[LTW][LTW][4];  // [slot][s-batch][s-tile of the batch]; slot u uses batches 0..u
+#pragma unroll
+  for (int u = 0; u < LTW; ++u)
+#pragma unroll
+    for (int sb = 0; sb < LTW; ++sb)
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) acc[u][sb][bi] = zero4();
+
+  for (int n0 = 0; n0 < N; n0 += 128) {
+    FragBF a[LTW][4], b[LTW][4][4];
+#pragma unroll
+    for (int u = 0; u < LTW; ++u) {
+      const bf16* crow = row_ptr<bf16>(Cm, c.b, c.t0 + min(lt[u] * 16 + r16, c.len - 1), grp);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) a[u][kb].v = *reinterpret_cast<const bf16x8*>(crow + min(n0 + kb * 32 + q * 8, N - 8));
+    }
+#pragma unroll
+    for (int sb = 0; sb < LTW; ++sb)
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        const bf16* brow =
+            row_ptr<bf16>(Bm, c.b, c.t0 + min((4 * sb + bi) * 16 + r16, c.len - 1), grp);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          b[sb][bi][kb].v = *reinterpret_cast<const bf16x8*>(brow + min(n0 + kb * 32 + q * 8, N - 8));
+      }
+    const FragBF zf = Prec<bf16>::zero_exact();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      const bool kok = n0 + kb * 32 + q * 8 < N;
+#pragma unroll
+      for (int u = 0; u < LTW; ++u) {
+        const FragBF av = kok && lt[u] * 16 + r16 < c.len ? a[u][kb] : zf;
+#pragma unroll
+        for (int sb = 0; sb <= u; ++sb)
+#pragma unroll
+          for (int bi = 0; bi < 4; ++bi) {
+            const bool sok = kok && (4 * sb + bi) * 16 + r16 < c.len;
+            mma(acc[u][sb][bi], av, sok ? b[sb][bi][kb] : zf);
+          }
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < LTW; ++u)
+#pragma unroll
+    for (int sb = 0; sb <= u; ++sb)
+#pragma unroll
+      for (int bi = 0; bi < 4; ++bi) {
+        const int st = 4 * sb + bi;
+        if (st > lt[u]) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          out[(int64_t)(lt[u] * 16 + q * 4 + i) * C + st * 16 + r16] = acc[u][sb][bi][i];
+      }
+}
+
 }  // namespace ssd
