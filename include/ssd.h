@@ -398,9 +398,11 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
 
 /* Bytes of workspace ssd_backward_ex needs for `algo` with inputs x, B, C of
  * `in_dtype` (AUTO resolves exactly as the call does).  The per-chunk path
- * (FUSED) needs ~275 MB at Nemotron-Nano size (8192 tokens, 64 heads x 64,
- * d_state 128: two fp32 states per chunk and head) against ~2.2 GB for
- * STAGED. */
+ * (FUSED) keeps two fp32 states per chunk and head (the state entering the
+ * chunk and its gradient); it takes the heads in passes whose two state
+ * buffers hold at most 128 MiB by default: 137 MB at Nemotron-Nano size (8192
+ * tokens, 64 heads x 64, d_state 128: two passes of 32 heads) against ~2.2 GB
+ * for STAGED. */
 ssd_status ssd_backward_ex_workspace_size(const ssd_problem* p, ssd_algo algo,
                                           ssd_dtype in_dtype, size_t* bytes);
 
@@ -425,7 +427,14 @@ ssd_status ssd_backward_ex_workspace_size(const ssd_problem* p, ssd_algo algo,
  *                    cumsum and step-size sums) and bit-identical results run to
  *                    run.  In packed mode, tokens past cu_seqlens[nseq] belong
  *                    to no sequence and get no gradient written.
- *   SSD_ALGO_AUTO    FUSED where it applies, STAGED otherwise. */
+ *   SSD_ALGO_AUTO    FUSED where it applies, STAGED otherwise.
+ * Workspace: 256-byte aligned, contents need not be initialised, not shared by
+ * calls that overlap in time.  STAGED needs its full size.  FUSED takes any
+ * size down to that of its smallest head pass and then uses the largest
+ * passes that fit (equal sizes; whole groups of heads, or multiples of eight
+ * heads of one group when the group's heads are a multiple of eight: their dB
+ * and dC are then summed over the passes in the same order as in one pass,
+ * so every size gives the same bits); below that, SSD_ERR_WORKSPACE. */
 ssd_status ssd_backward_ex(const ssd_problem* p, const ssd_bwd_args* a, ssd_algo algo,
                            void* workspace, size_t ws_bytes, hipStream_t stream);
 

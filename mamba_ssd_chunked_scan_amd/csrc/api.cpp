@@ -10,6 +10,8 @@
 #include <cmath>
 #include <cstring>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "ssd.h"
 #include "kernels.hpp"
@@ -97,6 +99,7 @@ ssd::Geo make_geo(const ssd_problem* p, const int32_t* meta) {
   g.K = (int)num_chunks(p);
   g.nseq = p->nseq > 0 ? p->nseq : p->batch;
   g.hpg = p->nheads / p->ngroups;
+  g.Hs = p->nheads;
   g.meta = p->nseq > 0 ? meta : nullptr;
   return g;
 }
@@ -956,11 +959,23 @@ ssd_problem chunk_fwd_problem(const ssd_problem* p) {
   return f;
 }
 
-BwdChunkWs bwd_chunk_layout(const ssd_problem* p) {
+// A pass of the per-chunk backward covers `hb` heads: a whole number of groups,
+// or (when a group's heads split into dB/dC workgroups of eight) a multiple of
+// eight heads of one group, whose dB and dC are then summed over the group's
+// passes in split order.
+int pass_groups(const ssd_problem* p, int hb) {
+  const int hpg = p->nheads / p->ngroups;
+  return hb >= hpg ? hb / hpg : 1;
+}
+bool pass_in_group(const ssd_problem* p, int hb) { return hb < p->nheads / p->ngroups; }
+
+// Workspace of one pass over `hb` heads: everything per head is sized for the
+// pass, the chunk table for the problem.
+BwdChunkWs bwd_chunk_layout(const ssd_problem* p, int hb) {
   BwdChunkWs w;
   const ssd_problem fp = chunk_fwd_problem(p);
-  const size_t nt = (size_t)bwd_tokens(p), H = p->nheads, P = p->headdim, N = p->dstate,
-               G = p->ngroups;
+  const size_t nt = (size_t)bwd_tokens(p), H = (size_t)hb, P = p->headdim, N = p->dstate,
+               G = (size_t)pass_groups(p, hb);
   const size_t K = (size_t)num_chunks(&fp);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -976,90 +991,173 @@ BwdChunkWs bwd_chunk_layout(const ssd_problem* p) {
   w.delta = take(nt * H * sizeof(float));
   w.gd = take(nt * H * sizeof(float));
   w.part = take(K * H * 3 * sizeof(double));
-  const int splits = ssd::bwd_chunk_splits(p->nheads / p->ngroups);
-  w.pdb = take(splits > 1 ? (size_t)splits * nt * G * N * sizeof(float) : 0);
-  w.pdc = take(splits > 1 ? (size_t)splits * nt * G * N * sizeof(float) : 0);
+  const int splits = ssd::bwd_chunk_splits((int)(H / G));
+  const bool partials = splits > 1 || pass_in_group(p, hb);
+  w.pdb = take(partials ? (size_t)splits * nt * G * N * sizeof(float) : 0);
+  w.pdc = take(partials ? (size_t)splits * nt * G * N * sizeof(float) : 0);
   w.total = off;
   return w;
 }
 
+// Heads per pass.  The two fp32 state buffers (the state entering every chunk
+// and its gradient) grow with the heads of a pass; by default a pass holds at
+// most kBwdStateBudget bytes of them, in passes of equal size.  With a given
+// workspace: the largest passes that fit.  Pass sizes: multiples of the heads
+// per group, and below that multiples of eight (one dB/dC workgroup's heads)
+// when they divide a group evenly.
+constexpr size_t kBwdStateBudget = size_t(128) << 20;
+
+std::vector<int> pass_sizes(const ssd_problem* p) {
+  const int H = p->nheads, hpg = H / p->ngroups, u = ssd::kBwdHeadsPerSplit;
+  std::vector<int> v;
+  if (hpg > u && hpg % u == 0)
+    for (int h = u; h < hpg; h += u) v.push_back(h);
+  for (int h = hpg; h <= H; h += hpg) v.push_back(h);
+  return v;
+}
+
+// passes of equal size no larger than hmax (one of pass_sizes)
+int balanced_pass(const ssd_problem* p, int hmax) {
+  const int H = p->nheads, hpg = H / p->ngroups;
+  if (hmax >= H) return H;
+  if (hmax >= hpg) return (int)cdiv(cdiv(H, cdiv(H, hmax)), hpg) * hpg;
+  const int u = ssd::kBwdHeadsPerSplit;
+  return (int)cdiv(cdiv(hpg, cdiv(hpg, hmax)), u) * u;
+}
+
+int bwd_heads_default(const ssd_problem* p) {
+  const ssd_problem fp = chunk_fwd_problem(p);
+  const size_t per_head = 2 * (size_t)num_chunks(&fp) * p->headdim * p->dstate * sizeof(float);
+  const std::vector<int> v = pass_sizes(p);
+  int hb = v.front();
+  for (int h : v)
+    if ((size_t)h * per_head <= kBwdStateBudget) hb = h;
+  return balanced_pass(p, hb);
+}
+
+// 0 when not even the smallest pass fits in ws_bytes
+int bwd_heads_fit(const ssd_problem* p, size_t ws_bytes) {
+  int hb = 0;
+  for (int h : pass_sizes(p))
+    if (bwd_chunk_layout(p, h).total <= ws_bytes) hb = h;
+  return hb ? balanced_pass(p, hb) : 0;
+}
+
 ssd_status chunk_backward(const ssd_problem* p, const ssd_bwd_args* a, void* workspace,
                           size_t ws_bytes, hipStream_t stream) {
-  const BwdChunkWs w = bwd_chunk_layout(p);
-  SSD_TRY(workspace_ok(workspace, ws_bytes, w.total));
+  const int H = p->nheads, G = p->ngroups, hpg = H / G;
+  const int hb = bwd_heads_fit(p, ws_bytes);
+  SSD_TRY(workspace_ok(workspace, ws_bytes, bwd_chunk_layout(p, hb ? hb : pass_sizes(p).front()).total));
+  const BwdChunkWs w = bwd_chunk_layout(p, hb);
   char* ws = static_cast<char*>(workspace);
   auto f = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  const int H = p->nheads, G = p->ngroups;
   const ssd_problem fp = chunk_fwd_problem(p);
-  ssd::BwdGeo bg;
-  bg.ntok = (int)bwd_tokens(p);
-  bg.T = p->seqlen;
-  bg.nseq = bwd_nseq(p);
-  bg.H = H;
-  bg.P = p->headdim;
-  bg.G = G;
-  bg.N = p->dstate;
-  bg.hpg = H / G;
-  bg.cu = p->nseq > 0 ? p->cu_seqlens : nullptr;
   const int in = dcode(a->x.dtype);
+  const size_t PN = (size_t)p->headdim * p->dstate;
 
-  // 1. forward recompute at 128-token chunks: chunk table (packed), cumsum,
-  // chunk states, carry-in states (fp32)
+  // the chunk table at 128 tokens (packed mode), shared by every pass
   int32_t* fmeta = p->nseq > 0 ? reinterpret_cast<int32_t*>(ws + w.fmeta) : nullptr;
-  const ssd::Geo gf = make_geo(&fp, fmeta);
   if (fmeta)
-    SSD_HIP(ssd::launch_varlen_meta(gf, p->cu_seqlens, fmeta, stream), "chunk table launch");
-  float* dtc = p->input_dt ? f(w.dtc) : nullptr;
-  SSD_HIP(ssd::launch_chunk_cumsum(gf, targ(a->dt), dcode(a->dt.dtype), a->A, a->dt_bias,
-                                   p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, f(w.cs), dtc,
-                                   stream),
-          "backward cumsum launch");
-  SSD_HIP(ssd::launch_chunk_state(gf, targ(a->x), targ(a->B), in, f(w.cs), dtc, f(w.st),
-                                  ssd::DT_F32, stream),
-          "backward chunk state launch");
-  SSD_HIP(ssd::launch_state_passing(gf, f(w.st), ssd::DT_F32, f(w.cs), a->initial_states, f(w.st),
-                                    nullptr, stream),
-          "backward state passing launch");
+    SSD_HIP(ssd::launch_varlen_meta(make_geo(&fp, fmeta), p->cu_seqlens, fmeta, stream),
+            "chunk table launch");
 
-  // 2. step sizes and their derivatives
-  SSD_HIP(ssd::launch_bwd_steps(bg, targ(a->dt), dcode(a->dt.dtype), a->A, a->dt_bias,
-                                p->dt_softplus, p->dt_clamp, p->dt_min, p->dt_max, f(w.delta),
-                                f(w.gd), nullptr, stream),
-          "backward steps launch");
+  // a tensor or per-head array moved to head h0 (group h0 / hpg)
+  auto heads = [](ssd_tensor t, int64_t n) {
+    if (t.data) t.data = static_cast<char*>(t.data) + n * t.stride[2] * (int64_t)dsize(t.dtype);
+    return t;
+  };
+  auto at_head = [](auto* ptr, int64_t n) { return ptr ? ptr + n : ptr; };
 
-  // 3. the adjoint: each chunk's own gradient of its entering state, then the
-  // reverse state passing (dfinal in, the initial states' gradient out)
-  ssd::BwdChunkLaunch l;
-  l.g = gf;
-  l.ntok = bg.ntok;
-  l.x = targ(a->x); l.B = targ(a->B); l.C = targ(a->C); l.z = targ(a->z);
-  l.dout = targ(a->dout);
-  l.dx = targ(a->dx); l.dz = targ(a->dz); l.dB = targ(a->dB); l.dC = targ(a->dC);
-  l.ddt = targ(a->ddt);
-  l.dout_dtype = dcode(a->dout.dtype);
-  l.A = a->A; l.D = a->D;
-  l.delta = f(w.delta); l.gd = f(w.gd);
-  l.cs = f(w.cs); l.hin = f(w.st); l.adj = f(w.adj);
-  l.part = reinterpret_cast<double*>(ws + w.part);
-  l.input_dt = p->input_dt;
-  l.pdb = f(w.pdb);
-  l.pdc = f(w.pdc);
-  SSD_HIP(ssd::launch_bwd_adj_state(l, stream), "backward adjoint chunk state launch");
-  SSD_HIP(ssd::launch_state_passing_rev(gf, f(w.adj), f(w.cs), a->dfinal_states,
-                                        a->dinitial_states, stream),
-          "backward reverse state passing launch");
+  // the passes: (first head, heads), in head order
+  std::vector<std::pair<int, int>> passes;
+  if (!pass_in_group(p, hb)) {
+    for (int h0 = 0; h0 < H; h0 += hb) passes.emplace_back(h0, std::min(hb, H - h0));
+  } else {
+    for (int g = 0; g < G; ++g)
+      for (int k = 0; k < hpg; k += hb) passes.emplace_back(g * hpg + k, std::min(hb, hpg - k));
+  }
+  for (const auto& ps : passes) {
+    const int h0 = ps.first, hn = ps.second, g0 = h0 / hpg;
+    const bool in_group = pass_in_group(p, hb);
+    ssd_problem pp = fp;
+    pp.nheads = hn;
+    pp.ngroups = in_group ? 1 : hn / hpg;
+    ssd::Geo gf = make_geo(&pp, fmeta);
+    gf.Hs = H;  // initial and final states keep the problem's head axis
+    ssd::BwdGeo bg;
+    bg.ntok = (int)bwd_tokens(p);
+    bg.T = p->seqlen;
+    bg.nseq = bwd_nseq(p);
+    bg.H = hn;
+    bg.P = p->headdim;
+    bg.G = pp.ngroups;
+    bg.N = p->dstate;
+    bg.hpg = hn / pp.ngroups;
+    bg.cu = p->nseq > 0 ? p->cu_seqlens : nullptr;
+    const ssd_tensor x = heads(a->x, h0), B = heads(a->B, g0), C = heads(a->C, g0),
+                     dt = heads(a->dt, h0);
+    const float* A = a->A + h0;
+    const float* dt_bias = at_head(a->dt_bias, h0);
+    const float* h0s = at_head(a->initial_states, (int64_t)h0 * PN);
 
-  // 4. the per-chunk gradients, then the per-head sums
-  SSD_HIP(ssd::launch_bwd_chunk(l, stream), "backward chunk kernels launch");
-  SSD_HIP(ssd::launch_bwd_step_heads(bg, gf.K, reinterpret_cast<double*>(ws + w.part), nullptr,
-                                     a->dA, a->ddt_bias, a->D ? a->dD : nullptr, nullptr, stream),
-          "backward per-head sums launch");
+    // 1. forward recompute at 128-token chunks: cumsum, chunk states,
+    // carry-in states (fp32)
+    float* dtc = p->input_dt ? f(w.dtc) : nullptr;
+    SSD_HIP(ssd::launch_chunk_cumsum(gf, targ(dt), dcode(dt.dtype), A, dt_bias, p->dt_softplus,
+                                     p->dt_clamp, p->dt_min, p->dt_max, f(w.cs), dtc, stream),
+            "backward cumsum launch");
+    SSD_HIP(ssd::launch_chunk_state(gf, targ(x), targ(B), in, f(w.cs), dtc, f(w.st),
+                                    ssd::DT_F32, stream),
+            "backward chunk state launch");
+    SSD_HIP(ssd::launch_state_passing(gf, f(w.st), ssd::DT_F32, f(w.cs), h0s, f(w.st), nullptr,
+                                      stream),
+            "backward state passing launch");
+
+    // 2. step sizes and their derivatives
+    SSD_HIP(ssd::launch_bwd_steps(bg, targ(dt), dcode(dt.dtype), A, dt_bias, p->dt_softplus,
+                                  p->dt_clamp, p->dt_min, p->dt_max, f(w.delta), f(w.gd), nullptr,
+                                  stream),
+            "backward steps launch");
+
+    // 3. the adjoint: each chunk's own gradient of its entering state, then the
+    // reverse state passing (dfinal in, the initial states' gradient out)
+    ssd::BwdChunkLaunch l;
+    l.g = gf;
+    l.ntok = bg.ntok;
+    l.x = targ(x); l.B = targ(B); l.C = targ(C); l.z = targ(heads(a->z, h0));
+    l.dout = targ(heads(a->dout, h0));
+    l.dx = targ(heads(a->dx, h0)); l.dz = targ(heads(a->dz, h0));
+    l.dB = targ(heads(a->dB, g0)); l.dC = targ(heads(a->dC, g0));
+    l.ddt = targ(heads(a->ddt, h0));
+    l.dout_dtype = dcode(a->dout.dtype);
+    l.A = A; l.D = at_head(a->D, h0);
+    l.delta = f(w.delta); l.gd = f(w.gd);
+    l.cs = f(w.cs); l.hin = f(w.st); l.adj = f(w.adj);
+    l.part = reinterpret_cast<double*>(ws + w.part);
+    l.input_dt = p->input_dt;
+    l.pdb = f(w.pdb);
+    l.pdc = f(w.pdc);
+    l.partials = in_group;
+    l.accumulate = in_group && h0 % hpg != 0;
+    SSD_HIP(ssd::launch_bwd_adj_state(l, stream), "backward adjoint chunk state launch");
+    SSD_HIP(ssd::launch_state_passing_rev(gf, f(w.adj), f(w.cs),
+                                          at_head(a->dfinal_states, (int64_t)h0 * PN),
+                                          at_head(a->dinitial_states, (int64_t)h0 * PN), stream),
+            "backward reverse state passing launch");
+
+    // 4. the per-chunk gradients, then the per-head sums
+    SSD_HIP(ssd::launch_bwd_chunk(l, stream), "backward chunk kernels launch");
+    SSD_HIP(ssd::launch_bwd_step_heads(bg, gf.K, reinterpret_cast<double*>(ws + w.part), nullptr,
+                                       a->dA + h0, a->ddt_bias + h0,
+                                       a->D ? a->dD + h0 : nullptr, nullptr, stream),
+            "backward per-head sums launch");
+  }
   return ok();
 }
 
 size_t bwd_workspace(const ssd_problem* p, ssd_algo algo, ssd_dtype in_dtype) {
   if (algo == SSD_ALGO_FUSED || (algo == SSD_ALGO_AUTO && bwd_fused_applies(p, in_dtype)))
-    return bwd_chunk_layout(p).total;
+    return bwd_chunk_layout(p, bwd_heads_default(p)).total;
   return bwd_layout(p).total;
 }
 
@@ -1208,7 +1306,7 @@ static int64_t cx_num_chunks(const ssd_complex_problem* p) {
 static ssd::Geo cx_geo(const ssd_complex_problem* p, const int32_t* meta) {
   ssd::Geo g;
   g.b = p->batch; g.T = p->seqlen; g.H = p->nheads; g.P = p->headdim; g.N = p->dstate;
-  g.G = p->nheads; g.hpg = 1;
+  g.G = p->nheads; g.hpg = 1; g.Hs = p->nheads;
   g.C = p->chunk_size;
   g.nc = (int)cdiv(p->seqlen, p->chunk_size);
   g.K = (int)cx_num_chunks(p);

@@ -145,8 +145,10 @@ struct BwdChunkArgs {
   int nsl;                // 64-column slabs of N
   int ntok;               // tokens on the packed axis
   int nsplit, hps;        // k_bwd_dbc: head splits of a group, heads per split
-  float* pdb;             // (nsplit, ntok, G, N) partial dB of each head split (nsplit > 1)
+  float* pdb;             // (nsplit, ntok, G, N) partial dB of each head split (partials)
   float* pdc;             // (nsplit, ntok, G, N) partial dC
+  int partials;           // dB, dC go through pdb, pdc and k_bwd_dbc_sum
+  int accumulate;         // k_bwd_dbc_sum adds to dB, dC instead of starting at zero
 };
 
 // The chunk, its sequence's chunks [fi, li), and the gradient of the state
@@ -1038,7 +1040,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dbc(BwdChunkArgs a) {
       for (int i = 0; i < 4; ++i) {
         const int r = rt * 16 + q * 4 + i;
         if (r >= len) continue;
-        if (a.nsplit == 1) {
+        if (!a.partials) {
           row_ptr_mut<float>(out, c.b, c.t0 + r, grp)[n0 + n] = acc[ui][nt][i];
         } else {
           part[(((int64_t)sp * a.ntok + tp0 + r) * g.G + grp) * g.N + n0 + n] = acc[ui][nt][i];
@@ -1049,7 +1051,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dbc(BwdChunkArgs a) {
 }
 
 // ---- dB and dC of a chunk and group: the head splits' partial sums, added in
-// split order
+// split order (after what dB and dC hold when accumulating: an earlier pass's
+// splits of the same group, so the order is the same as in one pass)
 __global__ __launch_bounds__(256) void k_bwd_dbc_sum(BwdChunkArgs a) {
   const Geo& g = a.g;
   const int j = (int)blockIdx.x / g.G, grp = (int)blockIdx.x % g.G;
@@ -1060,6 +1063,10 @@ __global__ __launch_bounds__(256) void k_bwd_dbc_sum(BwdChunkArgs a) {
   for (int e = threadIdx.x; e < c.len * nv; e += 256) {
     const int r = e / nv, n = (e % nv) * 4;
     f32x4 sb = zero4(), sc = zero4();
+    if (a.accumulate) {
+      sb = *reinterpret_cast<const f32x4*>(row_ptr<float>(a.dB, c.b, c.t0 + r, grp) + n);
+      sc = *reinterpret_cast<const f32x4*>(row_ptr<float>(a.dC, c.b, c.t0 + r, grp) + n);
+    }
     for (int sp = 0; sp < a.nsplit; ++sp) {
       const int64_t o = (((int64_t)sp * a.ntok + tp0 + r) * g.G + grp) * g.N + n;
       sb += *reinterpret_cast<const f32x4*>(a.pdb + o);
@@ -1092,6 +1099,8 @@ BwdChunkArgs chunk_args(const BwdChunkLaunch& l) {
   a.hps = (g.hpg + a.nsplit - 1) / a.nsplit;
   a.pdb = l.pdb;
   a.pdc = l.pdc;
+  a.partials = a.nsplit > 1 || l.partials;
+  a.accumulate = l.accumulate;
   return a;
 }
 }  // namespace
@@ -1118,7 +1127,7 @@ hipError_t launch_bwd_chunk(const BwdChunkLaunch& l, hipStream_t s) {
   const unsigned nb = (unsigned)((int64_t)g.K * g.G * a.nsplit * a.nsl);
   hipLaunchKernelGGL(k_bwd_dbc, dim3(nb), dim3(512), 0, s, a);
   e = hipGetLastError();
-  if (e != hipSuccess || a.nsplit == 1) return e;
+  if (e != hipSuccess || !a.partials) return e;
   hipLaunchKernelGGL(k_bwd_dbc_sum, dim3((unsigned)((int64_t)g.K * g.G)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

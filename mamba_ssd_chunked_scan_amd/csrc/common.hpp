@@ -322,6 +322,8 @@ struct Geo {
   int K;         // logical chunk slots
   int nseq;      // sequences (batch mode: b)
   int hpg;       // heads per group
+  int Hs;        // heads of the (sequence, head, P, N) initial/final state tensors:
+                 // H, or more when a pass covers only some of the heads
   const int32_t* meta;  // packed-mode chunk table, NULL in batch mode
 };
 

@@ -151,7 +151,11 @@ struct BwdChunkLaunch {
   double* part;             // (K, H, 3)
   int input_dt;
   float* pdb;               // (splits, ntok, G, N) when bwd_chunk_splits(hpg) > 1
-  float* pdc;
+  float* pdc;               // or `partials`
+  int partials;             // dB, dC through the split partials even with one split
+                            // (a pass over part of a group's heads)
+  int accumulate;           // add the pass's sum to what dB and dC hold (a later
+                            // pass over the same group), in split order
 };
 // U_j = sum_l exp(cs_l) dy_l (outer) C_l per (chunk, head) into adj
 hipError_t launch_bwd_adj_state(const BwdChunkLaunch& l, hipStream_t s);

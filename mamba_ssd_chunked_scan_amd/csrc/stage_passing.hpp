@@ -43,7 +43,7 @@ __device__ __forceinline__ void state_passing_thread(const Geo& g, const ST* sta
 
   f32x8 cur;
   if (h0) {
-    cur = Vec8<float>::load(h0 + ((int64_t)seq * g.H + h) * PN + e0);
+    cur = Vec8<float>::load(h0 + ((int64_t)seq * g.Hs + h) * PN + e0);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) cur[i] = 0.0f;
@@ -72,7 +72,7 @@ __device__ __forceinline__ void state_passing_thread(const Geo& g, const ST* sta
       }
     }
   }
-  if (hfinal) Vec8<float>::store(hfinal + ((int64_t)seq * g.H + h) * PN + e0, cur);
+  if (hfinal) Vec8<float>::store(hfinal + ((int64_t)seq * g.Hs + h) * PN + e0, cur);
 }
 
 }  // namespace ssd

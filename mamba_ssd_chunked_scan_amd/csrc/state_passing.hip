@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void k_state_passing_rev(Geo g, float* adj,
   seq_chunks(g, seq, first, last);
   f32x8 cur;
   if (dfinal) {
-    cur = Vec8<float>::load(dfinal + ((int64_t)seq * g.H + h) * PN + e0);
+    cur = Vec8<float>::load(dfinal + ((int64_t)seq * g.Hs + h) * PN + e0);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) cur[i] = 0.0f;
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(256) void k_state_passing_rev(Geo g, float* adj,
       }
     }
   }
-  if (dh0) Vec8<float>::store(dh0 + ((int64_t)seq * g.H + h) * PN + e0, cur);
+  if (dh0) Vec8<float>::store(dh0 + ((int64_t)seq * g.Hs + h) * PN + e0, cur);
 }
 
 hipError_t launch_state_passing_rev(const Geo& g, float* adj, const float* cs,

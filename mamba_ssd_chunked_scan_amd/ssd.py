@@ -608,6 +608,11 @@ def _bwd_alloc(prob, x, B, C, dt, D, z, nseq, workspace, algo):
               dz=torch.empty(x.shape, dtype=f32, device=dev) if z is not None else None,
               dinitial_states=torch.empty((nseq, prob.nheads, prob.headdim, prob.dstate),
                                           dtype=f32, device=dev))
+    if workspace is not None and algo != "staged":
+        # the per-chunk backward takes any workspace down to its smallest head
+        # pass (fewer heads per pass in a smaller one); the library checks it
+        _workspace(0, workspace, dev)
+        return g, workspace
     return g, _workspace(prob.backward_workspace_size(algo, x.dtype), workspace, dev)
 
 
@@ -619,7 +624,10 @@ def ssd_backward(x, B, C, dt, A, dout, dt_bias=None, D=None, z=None, initial_sta
     respect to every input of ``ssd_forward`` (same arguments and layouts);
     all gradients are float32, allocated on ``stream`` like the workspace.
     ``algo``: "staged" (ssd_backward), "fused" (the per-chunk backward of
-    ssd_backward_ex) or "auto" (fused where it applies)."""
+    ssd_backward_ex) or "auto" (fused where it applies).  A ``workspace``
+    given for "fused" or "auto" is used as it is: one smaller than
+    ``Problem.backward_workspace_size`` makes the per-chunk backward take its
+    heads in more passes (down to one group, or eight heads of a group)."""
     prob = problem_from(x, B, chunk_size, cu_seqlens=cu_seqlens, dt_softplus=dt_softplus,
                         dt_limit=dt_limit, input_dt=input_dt)
     _check_fwd_inputs(prob, x, B, C, dt, A, dt_bias, D, z, initial_states)

@@ -236,6 +236,47 @@ def test_rejects_what_it_does_not_take():
     assert e.value.status == 5
 
 
+def _equal_grads(a, b):
+    for n in NAMES:
+        x, y = getattr(a, n), getattr(b, n)
+        assert (x is None) == (y is None), n
+        if x is not None:
+            assert torch.equal(x, y), f"{n} differs between head passes and one pass"
+
+
+@pytest.mark.parametrize("case", ["whole_groups", "within_a_group"])
+def test_head_passes_match_one_pass(case):
+    """A smaller workspace makes the backward take its heads in passes: four
+    passes of one group (two heads each), or one group of 24 heads in passes of
+    16 and 8 (dB and dC summed over the group's passes in split order).  Every
+    gradient equals the one-pass result bit for bit; packed sequences with
+    initial states and a final-state gradient exercise the state tensors'
+    head offsets."""
+    if case == "whole_groups":
+        H, G, hsmall, gsmall = 8, 4, 2, 1
+    else:
+        H, G, hsmall, gsmall = 24, 1, 16, 1
+    lens = (130, 0, 257, 64)
+    w = small_workload(f"bwdf_pass_{case}", seqlen=sum(lens), nheads=H, headdim=64, ngroups=G,
+                       dstate=64, chunk_size=128, seqlens=lens)
+    inp = with_initial_states(make_inputs(w))
+    dout, dfin = upstream(inp)
+    one = gpu_bwd(w, inp, dout, dfin, "fused")
+    cu = device_inputs(inp, torch.bfloat16)["cu_seqlens"]
+    small = ssd.Problem(1, w.seqlen, hsmall, 64, gsmall, 64, 128, nseq=len(lens), cu_seqlens=cu)
+    need = small.backward_workspace_size("fused")
+    full = ssd.Problem(1, w.seqlen, H, 64, G, 64, 128, nseq=len(lens), cu_seqlens=cu)
+    assert need < full.backward_workspace_size("fused")
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    passes = gpu_bwd(w, inp, dout, dfin, "fused", workspace=ws)
+    _equal_grads(passes, one)
+    check(passes, ref_bwd(inp, dout, dfin))
+    # below the smallest pass: an error, nothing launched
+    tiny = torch.empty(1024, dtype=torch.uint8, device="cuda")
+    with pytest.raises(ssd.SSDError):
+        gpu_bwd(w, inp, dout, dfin, "fused", workspace=tiny)
+
+
 def test_bit_identical_repeats():
     w = small_workload("bwdf_rep", seqlen=700, nheads=16, headdim=64, ngroups=1, dstate=128,
                        chunk_size=128)
