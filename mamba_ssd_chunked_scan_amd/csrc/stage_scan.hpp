@@ -278,7 +278,7 @@ __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, 
   const float* csr = cs + ((int64_t)j * g.H + h) * C;
   const float* dtr = dtc ? dtc + ((int64_t)j * g.H + h) * C : nullptr;
   for (int l = tid; l < C; l += 256) {
-    s_cs[l] = csr[l];
+    s_cs[l] = csr[l] * 1.4426950408889634f;  // base 2: every decay is one 2^x
     s_f[l] = dtr ? dtr[l] : 1.0f;
   }
 #pragma unroll
@@ -348,7 +348,7 @@ __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, 
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float e = fast_exp(s_cs[lt * 16 + q * 4 + i]);
+      const float e = fast_exp2(s_cs[lt * 16 + q * 4 + i]);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) acc[u][pt][i] *= e;
     }
@@ -386,12 +386,19 @@ __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, 
         const int s0 = (k0 + kk) * 32 + q * 8;
         const f32x8 csv = Vec8<float>::load(s_cs + s0);
         f32x8 m;
+        if (k0 + kk < nkd - 1 && c.len == C) {
+          // a k-block wholly below the diagonal of a full chunk: every
+          // (l, s) is kept, the exponent is <= 0 (or small for growth)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int s = s0 + e;
-          const bool keep = lok && (s <= lrow) && (s < c.len);
-          const float ex = fast_exp(keep ? csl - csv[e] : 0.0f);
-          m[e] = keep ? ex * cbv[kk][e] : 0.0f;
+          for (int e = 0; e < 8; ++e) m[e] = fast_exp2(csl - csv[e]) * cbv[kk][e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int s = s0 + e;
+            const bool keep = lok && (s <= lrow) && (s < c.len);
+            const float ex = fast_exp2(keep ? csl - csv[e] : 0.0f);
+            m[e] = keep ? ex * cbv[kk][e] : 0.0f;
+          }
         }
         if constexpr (F) {
           const f32x8 fv = Vec8<float>::load(s_f + s0);
