@@ -72,27 +72,68 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
   for (int d = kWave / 2; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
   return v;
 }
-// sum over the 16 lanes of a lane group (xor 1, 2, 4, 8 stay inside it)
+// A lane move within each row of 16 lanes (DPP: no LDS traffic), for the
+// sums below: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (lane i <-> 7 - i of its half row) and row_mirror (i <-> 15 -
+// i).  After the two quad steps every lane of a quad holds the quad's sum, so
+// the mirrors pair quad with quad and half with half exactly as lane ^ 4 and
+// lane ^ 8 would: the same additions in the same order.
+template <int CTRL>
+__device__ __forceinline__ double row_move_f64(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double(((long long)hi << 32) | (long long)(unsigned)lo);
+}
+template <int CTRL>
+__device__ __forceinline__ float row_move(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+// sum over the 16 lanes of a lane group
 __device__ __forceinline__ double group16_sum_f64(double v) {
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) v += __shfl_xor(v, d, kWave);
+  v += row_move_f64<kDppXor1>(v);
+  v += row_move_f64<kDppXor2>(v);
+  v += row_move_f64<kDppHalfMirror>(v);
+  v += row_move_f64<kDppMirror>(v);
   return v;
 }
 __device__ __forceinline__ float group16_sum(float v) {
-#pragma unroll
-  for (int d = 1; d < 16; d <<= 1) v += __shfl_xor(v, d, kWave);
+  v += row_move<kDppXor1>(v);
+  v += row_move<kDppXor2>(v);
+  v += row_move<kDppHalfMirror>(v);
+  v += row_move<kDppMirror>(v);
   return v;
 }
-// sum over the 4 lane groups (lanes l, l + 16, l + 32, l + 48)
-__device__ __forceinline__ double across_groups_f64(double v) {
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
-}
+// Sum over the 4 lane groups (lanes l, l + 16, l + 32, l + 48) with the gfx950
+// lane swaps: v_permlane16_swap exchanges rows 0 <-> 1 and 2 <-> 3 between its
+// two operands and v_permlane32_swap the wave halves, so with both operands
+// holding v, the two results add to v[l] + v[l ^ 16] (then ^ 32) in every lane
+// (no LDS traffic; the same pair sums as shuffles).
 __device__ __forceinline__ float across_groups(float v) {
-  v += __shfl_xor(v, 16, kWave);
-  v += __shfl_xor(v, 32, kWave);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ double across_groups_f64(double v) {
+  auto halves = [](double x, unsigned& lo, unsigned& hi) {
+    const unsigned long long u = (unsigned long long)__double_as_longlong(x);
+    lo = (unsigned)u;
+    hi = (unsigned)(u >> 32);
+  };
+  auto join = [](unsigned lo, unsigned hi) {
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+  };
+  unsigned lo, hi;
+  halves(v, lo, hi);
+  auto l16 = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  auto h16 = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  v = join(l16[0], h16[0]) + join(l16[1], h16[1]);
+  halves(v, lo, hi);
+  auto l32 = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  auto h32 = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  return join(l32[0], h32[0]) + join(l32[1], h32[1]);
 }
 
 __device__ __forceinline__ float sigmoidf(float v) {
