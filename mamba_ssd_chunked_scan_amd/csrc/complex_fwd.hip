@@ -208,16 +208,32 @@ __global__ __launch_bounds__(256) void k_cx_state_pass(Geo g, const float* A,
 //           accumulator (column l, rows s = 4q + r) is directly the A operand of
 //           Y_diag (row l, k-slot q, instruction r <-> s = 4q + r).
 //   Y_diag: B operand x[s, p] for the same s of each (q, r).
-template <int PT, bool CPLX>
+// With STAGE the carry-in state (P x N complex) is first copied into LDS
+// (dynamic shared memory, rows of N + 2 complex), so that the four waves, each
+// reading all of it for its l-tiles' readout, read it from there rather than
+// through the caches (chosen when it fits in 64 KB).
+template <int PT, bool CPLX, bool STAGE>
 __global__ __launch_bounds__(256) void k_cx_chunk_scan(Geo g, TArg x, TArg B, TArg Cm,
                                                        TArg dt, const float* A,
                                                        const float* states, TArg out) {
   __shared__ float sd[kCxMaxChunk];
   __shared__ float2 ecs[kCxMaxChunk];
+  extern __shared__ __align__(16) float2 s_hin[];
   const int j = blockIdx.x, h = blockIdx.y;
   Chunk ch;
   if (!get_chunk(g, j, ch)) return;  // a packed batch's unused chunk slots
   const int bb = ch.b, t0 = ch.t0, len = ch.len;
+  const float2* hsrc = reinterpret_cast<const float2*>(states) + ((int64_t)j * g.H + h) * g.P * g.N;
+  const int HLDc = g.N + 2;  // complex per staged row
+  if (STAGE) {
+    // issued before the cumsum, whose barrier then also orders these writes
+    const int rowv = g.N / 2;  // float4 (two complex) per row
+    for (int v = threadIdx.x; v < g.P * rowv; v += 256) {
+      const int p = v / rowv, n = (v % rowv) * 2;
+      *reinterpret_cast<float4*>(&s_hin[p * HLDc + n]) =
+          *reinterpret_cast<const float4*>(hsrc + (int64_t)p * g.N + n);
+    }
+  }
   cx_delta_cumsum(g, dt, bb, t0, len, h, sd);
   const float ar = A[2 * h], ai = A[2 * h + 1];
   for (int l = threadIdx.x; l < g.C; l += 256) ecs[l] = cexp_step(sd[l], ar, ai);
@@ -225,7 +241,8 @@ __global__ __launch_bounds__(256) void k_cx_chunk_scan(Geo g, TArg x, TArg B, TA
 
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int r16 = lane % 16, q = lane / 16;
-  const float2* hin = reinterpret_cast<const float2*>(states) + ((int64_t)j * g.H + h) * g.P * g.N;
+  const float2* hin = STAGE ? s_hin : hsrc;
+  const int hld = STAGE ? HLDc : g.N;  // complex per row of hin
   const int nkb = g.N / 16;
   for (int lt = wave; lt * 16 < len; lt += 4) {
     f32x4 yre[PT], yim[PT];
@@ -249,7 +266,7 @@ __global__ __launch_bounds__(256) void k_cx_chunk_scan(Geo g, TArg x, TArg B, TA
                         cmul(el, make_float2(c23.x, c23.y)), cmul(el, make_float2(c23.z, c23.w))};
 #pragma unroll
         for (int t = 0; t < PT; ++t) {
-          const float2* hr = hin + (int64_t)(t * 16 + r16) * g.N + n0;
+          const float2* hr = hin + (t * 16 + r16) * hld + n0;
           const float4 h01 = *reinterpret_cast<const float4*>(hr);
           const float4 h23 = *reinterpret_cast<const float4*>(hr + 2);
           const float2 hv[4] = {make_float2(h01.x, h01.y), make_float2(h01.z, h01.w),
@@ -366,12 +383,21 @@ template <int PT>
 hipError_t launch_scan_pt(const Geo& g, TArg x, TArg B, TArg Cm, TArg dt, const float* A,
                           const float* states, TArg out, int cplx, hipStream_t s) {
   dim3 grid(g.K, g.H);
-  if (cplx)
-    hipLaunchKernelGGL((k_cx_chunk_scan<PT, true>), grid, dim3(256), 0, s, g, x, B, Cm, dt, A,
-                       states, out);
-  else
-    hipLaunchKernelGGL((k_cx_chunk_scan<PT, false>), grid, dim3(256), 0, s, g, x, B, Cm, dt, A,
-                       states, out);
+  const size_t hbytes = (size_t)g.P * (g.N + 2) * sizeof(float2);
+  if (hbytes <= 64 * 1024) {
+    if (cplx)
+      hipLaunchKernelGGL((k_cx_chunk_scan<PT, true, true>), grid, dim3(256), hbytes, s, g, x, B,
+                         Cm, dt, A, states, out);
+    else
+      hipLaunchKernelGGL((k_cx_chunk_scan<PT, false, true>), grid, dim3(256), hbytes, s, g, x, B,
+                         Cm, dt, A, states, out);
+  } else if (cplx) {
+    hipLaunchKernelGGL((k_cx_chunk_scan<PT, true, false>), grid, dim3(256), 0, s, g, x, B, Cm, dt,
+                       A, states, out);
+  } else {
+    hipLaunchKernelGGL((k_cx_chunk_scan<PT, false, false>), grid, dim3(256), 0, s, g, x, B, Cm,
+                       dt, A, states, out);
+  }
   return hipGetLastError();
 }
 
