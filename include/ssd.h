@@ -281,7 +281,9 @@ typedef struct ssd_fwd_args {
  * to it; with input_dt it also needs delta > 0 by construction (softplus,
  * or a clamp with dt_min >= 0), since it folds log2(delta) into the decay
  * exponent.  initial_states and final_states must be 16-byte aligned for
- * it.  Its results are bit-identical run to run for a given problem shape;
+ * it, and 127 token strides plus one row of each token tensor must stay
+ * below 2 GiB (it addresses a chunk's rows as 32-bit offsets; AUTO takes
+ * STAGED otherwise).  Its results are bit-identical run to run for a given problem shape;
  * two different shapes of one computation (e.g. a sequence split in two and
  * resumed from the final state) agree to fp32 rounding of the states.
  * In packed mode the chunk table is built inside the workspace.  workspace:
@@ -421,8 +423,9 @@ ssd_status ssd_backward_ex_workspace_size(const ssd_problem* p, ssd_algo algo,
  *                    Reference, "Intra-chunk outputs and per-chunk states" and
  *                    "Inter-chunk propagation", differentiated factor by
  *                    factor).  Takes bf16 x, B, C, headdim 64 and dstate <= 128
- *                    (a multiple of 8), with at least one token; returns
- *                    SSD_ERR_UNSUPPORTED otherwise.  Same precision design
+ *                    (a multiple of 8), with at least one token, and 127
+ *                    token strides plus one row of each token tensor below
+ *                    2 GiB; returns SSD_ERR_UNSUPPORTED otherwise.  Same precision design
  *                    (bf16 hi + lo operands, fp32 states and accumulation, fp64
  *                    cumsum and step-size sums) and bit-identical results run to
  *                    run.  In packed mode, tokens past cu_seqlens[nseq] belong

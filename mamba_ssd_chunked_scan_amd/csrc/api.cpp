@@ -241,9 +241,32 @@ ssd_status check_state_ptr(const float* ptr, const char* name) {
   return SSD_OK;
 }
 
+// The fused forward and the per-chunk backward address a 128-token chunk's rows
+// of a token tensor as 32-bit byte offsets from its first row (so that the base
+// stays in scalar registers): 127 token strides plus one row must stay below
+// 2^31 bytes.
+bool chunk_rows_fit(const ssd_tensor& t, int64_t row_elems) {
+  if (!t.data) return true;
+  const int64_t s1 = t.stride[1] < 0 ? -t.stride[1] : t.stride[1];
+  return (s1 * 127 + row_elems) * (int64_t)dsize(t.dtype) < (int64_t(1) << 31);
+}
+bool fwd_rows_fit(const ssd_problem* p, const ssd_fwd_args* a) {
+  const int64_t P = p->headdim, N = p->dstate;
+  return chunk_rows_fit(a->x, P) && chunk_rows_fit(a->B, N) && chunk_rows_fit(a->C, N) &&
+         chunk_rows_fit(a->dt, 1) && chunk_rows_fit(a->z, P) && chunk_rows_fit(a->out, P);
+}
+bool bwd_rows_fit(const ssd_problem* p, const ssd_bwd_args* a) {
+  const int64_t P = p->headdim, N = p->dstate;
+  return chunk_rows_fit(a->x, P) && chunk_rows_fit(a->B, N) && chunk_rows_fit(a->C, N) &&
+         chunk_rows_fit(a->dt, 1) && chunk_rows_fit(a->z, P) && chunk_rows_fit(a->dout, P) &&
+         chunk_rows_fit(a->dx, P) && chunk_rows_fit(a->dB, N) && chunk_rows_fit(a->dC, N) &&
+         chunk_rows_fit(a->ddt, 1) && chunk_rows_fit(a->dz, P);
+}
+
 // What the fused path takes (the rest of its checks are in fused_forward).
 bool fused_applies(const ssd_problem* p, const ssd_fwd_args* a) {
   if (has_tokens(p) && a->x.dtype != SSD_BF16) return false;
+  if (!fwd_rows_fit(p, a)) return false;
   if (p->dstate > 128) return false;
   if (p->input_dt && !p->dt_softplus && !(p->dt_clamp && p->dt_min >= 0.0f)) return false;
   return true;
@@ -262,6 +285,10 @@ ssd_status fused_forward(const ssd_problem* p, const ssd_fwd_args* a, void* work
     return fail(SSD_ERR_UNSUPPORTED,
                 "SSD_ALGO_FUSED with input_dt needs delta >= 0 (softplus, or a clamp with "
                 "dt_min >= 0); use SSD_ALGO_STAGED");
+  if (!fwd_rows_fit(p, a))
+    return fail(SSD_ERR_UNSUPPORTED,
+                "SSD_ALGO_FUSED needs 127 token strides of every token tensor below 2 GiB; "
+                "use SSD_ALGO_STAGED");
   SSD_TRY(check_state_ptr(a->initial_states, "initial_states"));
   SSD_TRY(check_state_ptr(a->final_states, "final_states"));
   const FusedWs w = fused_layout(p, norm != nullptr);
@@ -1193,7 +1220,12 @@ ssd_status ssd_backward_ex(const ssd_problem* p, const ssd_bwd_args* a, ssd_algo
                 "the per-chunk backward takes bf16 x, B, C with tokens, headdim 64 and dstate "
                 "<= 128 (a multiple of 8); got headdim %d, dstate %d (use SSD_ALGO_STAGED)",
                 p->headdim, p->dstate);
-  if (algo == SSD_ALGO_FUSED || (algo == SSD_ALGO_AUTO && bwd_fused_applies(p, in)))
+  if (algo == SSD_ALGO_FUSED && !bwd_rows_fit(p, a))
+    return fail(SSD_ERR_UNSUPPORTED,
+                "the per-chunk backward needs 127 token strides of every token tensor below "
+                "2 GiB (use SSD_ALGO_STAGED)");
+  if (algo == SSD_ALGO_FUSED ||
+      (algo == SSD_ALGO_AUTO && bwd_fused_applies(p, in) && bwd_rows_fit(p, a)))
     return chunk_backward(p, a, workspace, ws_bytes, stream);
   return staged_backward(p, a, workspace, ws_bytes, stream);
 }

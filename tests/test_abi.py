@@ -148,6 +148,37 @@ def test_forward_validation_workspace_and_algo():
     assert L.ssd_forward(ctypes.byref(p), 0, ctypes.byref(a), 4096, 1 << 40, None) == 1
 
 
+def test_fused_paths_refuse_token_strides_past_32_bit_offsets():
+    # The fused forward and the per-chunk backward address a 128-token chunk's
+    # rows as 32-bit byte offsets; a token stride of 2^24 bf16 elements puts 127
+    # rows 4 GiB apart, so both refuse it on the host (nothing is launched).
+    L = ssd.lib()
+    p = prob().c()
+    huge = (0, 1 << 24, 64)
+    a = ssd.SsdFwdArgs()
+    a.x = fake_tensor(strides=huge)
+    a.B = fake_tensor()
+    a.C = fake_tensor()
+    a.dt = fake_tensor(strides=(8192 * 64, 64, 1))
+    a.out = fake_tensor(strides=(8192 * 4096, 4096, 64))
+    a.A = 4096
+    rc = L.ssd_forward(ctypes.byref(p), ssd.ALGO["fused"], ctypes.byref(a), 4096, 1 << 40, None)
+    assert rc == 5 and b"2 GiB" in L.ssd_last_error_message(), (rc, L.ssd_last_error_message())
+    b = ssd.SsdBwdArgs()
+    tok, grp, steps = (8192 * 4096, 4096, 64), (8192 * 1024, 1024, 128), (8192 * 64, 64, 1)
+    b.x = fake_tensor(strides=huge)
+    b.B, b.C = fake_tensor(strides=grp), fake_tensor(strides=grp)
+    b.dt = fake_tensor(strides=steps)
+    b.dout = fake_tensor(dtype=ssd.F32, strides=tok)
+    b.dx = fake_tensor(dtype=ssd.F32, strides=tok)
+    b.dB, b.dC = fake_tensor(dtype=ssd.F32, strides=grp), fake_tensor(dtype=ssd.F32, strides=grp)
+    b.ddt = fake_tensor(dtype=ssd.F32, strides=steps)
+    b.A = b.dA = b.ddt_bias = 4096
+    rc = L.ssd_backward_ex(ctypes.byref(p), ctypes.byref(b), ssd.ALGO["fused"], 4096, 1 << 40,
+                           None)
+    assert rc == 5 and b"2 GiB" in L.ssd_last_error_message(), (rc, L.ssd_last_error_message())
+
+
 def test_backward_validation_before_launch():
     # fake device addresses: every case fails on the host before any launch
     L = ssd.lib()
