@@ -1127,8 +1127,8 @@ ssd_status chunk_backward(const ssd_problem* p, const ssd_bwd_args* a, void* wor
     const float* dt_bias = at_head(a->dt_bias, h0);
     const float* h0s = at_head(a->initial_states, (int64_t)h0 * PN);
 
-    // 1. forward recompute at 128-token chunks: cumsum, chunk states,
-    // carry-in states (fp32)
+    // 1. forward recompute at 128-token chunks: cumsum, chunk states (the
+    // carry-in states come with the adjoint's scan, step 3)
     float* dtc = p->input_dt ? f(w.dtc) : nullptr;
     SSD_HIP(ssd::launch_chunk_cumsum(gf, targ(dt), dcode(dt.dtype), A, dt_bias, p->dt_softplus,
                                      p->dt_clamp, p->dt_min, p->dt_max, f(w.cs), dtc, stream),
@@ -1136,9 +1136,6 @@ ssd_status chunk_backward(const ssd_problem* p, const ssd_bwd_args* a, void* wor
     SSD_HIP(ssd::launch_chunk_state(gf, targ(x), targ(B), in, f(w.cs), dtc, f(w.st),
                                     ssd::DT_F32, stream),
             "backward chunk state launch");
-    SSD_HIP(ssd::launch_state_passing(gf, f(w.st), ssd::DT_F32, f(w.cs), h0s, f(w.st), nullptr,
-                                      stream),
-            "backward state passing launch");
 
     // 2. step sizes and their derivatives
     SSD_HIP(ssd::launch_bwd_steps(bg, targ(dt), dcode(dt.dtype), A, dt_bias, p->dt_softplus,
@@ -1146,8 +1143,10 @@ ssd_status chunk_backward(const ssd_problem* p, const ssd_bwd_args* a, void* wor
                                   stream),
             "backward steps launch");
 
-    // 3. the adjoint: each chunk's own gradient of its entering state, then the
-    // reverse state passing (dfinal in, the initial states' gradient out)
+    // 3. the adjoint: each chunk's own gradient of its entering state; then
+    // in one launch the forward state passing (chunk states -> carry-in
+    // states) and the reverse one (dfinal in, the initial states' gradient
+    // out), two independent scans over the chunks
     ssd::BwdChunkLaunch l;
     l.g = gf;
     l.ntok = bg.ntok;
@@ -1167,10 +1166,10 @@ ssd_status chunk_backward(const ssd_problem* p, const ssd_bwd_args* a, void* wor
     l.partials = in_group;
     l.accumulate = in_group && h0 % hpg != 0;
     SSD_HIP(ssd::launch_bwd_adj_state(l, stream), "backward adjoint chunk state launch");
-    SSD_HIP(ssd::launch_state_passing_rev(gf, f(w.adj), f(w.cs),
-                                          at_head(a->dfinal_states, (int64_t)h0 * PN),
-                                          at_head(a->dinitial_states, (int64_t)h0 * PN), stream),
-            "backward reverse state passing launch");
+    SSD_HIP(ssd::launch_state_passing_pair(gf, f(w.st), f(w.cs), h0s, f(w.adj),
+                                           at_head(a->dfinal_states, (int64_t)h0 * PN),
+                                           at_head(a->dinitial_states, (int64_t)h0 * PN), stream),
+            "backward state passing launch");
 
     // 4. the per-chunk gradients, then the per-head sums
     SSD_HIP(ssd::launch_bwd_chunk(l, stream), "backward chunk kernels launch");

@@ -30,12 +30,15 @@ hipError_t launch_state_passing(const Geo& g, const void* states, int st_dtype,
                                 const float* cs, const float* h0, void* states_out,
                                 float* hfinal, hipStream_t s);
 
-// The adjoint of the state passing, chunks last to first, in place on adj (fp32
-// (K, H, P, N)): U_j (the gradient chunk j's tokens send to its entering state)
-// becomes dHout_j (the gradient of the state leaving chunk j through later
-// tokens); dh0 (nseq, H, P, N) or NULL receives the initial state's gradient.
-hipError_t launch_state_passing_rev(const Geo& g, float* adj, const float* cs,
-                                    const float* dfinal, float* dh0, hipStream_t s);
+// Two independent scans over the chunks, side by side in one launch: the state
+// passing over fp32 states (in place, from h0, no final state), and its adjoint,
+// chunks last to first, in place on adj (fp32 (K, H, P, N)): U_j (the gradient
+// chunk j's tokens send to its entering state) becomes dHout_j (the gradient of
+// the state leaving chunk j through later tokens) from dfinal; dh0 (nseq, H, P,
+// N) or NULL receives the initial state's gradient.
+hipError_t launch_state_passing_pair(const Geo& g, float* states, const float* cs,
+                                     const float* h0, float* adj, const float* dfinal, float* dh0,
+                                     hipStream_t s);
 
 // yoff (NULL to skip): also writes the inter-chunk part of
 // the output, exp(cs_l) C_l . h_in, before the skip and the gate, as (tokens,

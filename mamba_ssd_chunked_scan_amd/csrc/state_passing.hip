@@ -21,13 +21,10 @@ __global__ __launch_bounds__(256) void k_state_passing(Geo g, const ST* states,
 // stores dHout[j] (the gradient of the state leaving chunk j through later
 // tokens) over U_j in place, and the gradient of the initial state, dHin of the
 // first chunk (dfinal itself for a sequence without tokens), into dh0.
-__global__ __launch_bounds__(256) void k_state_passing_rev(Geo g, float* adj,
-                                                           const float* __restrict__ cs,
-                                                           const float* __restrict__ dfinal,
-                                                           float* __restrict__ dh0) {
+__device__ __forceinline__ void state_passing_rev_thread(const Geo& g, float* adj,
+                                                         const float* cs, const float* dfinal,
+                                                         float* dh0, int64_t e0, int h, int seq) {
   const int64_t PN = (int64_t)g.P * g.N;
-  const int64_t e0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
-  const int h = blockIdx.y, seq = blockIdx.z;
   if (e0 >= PN) return;
   int first, last;
   seq_chunks(g, seq, first, last);
@@ -65,12 +62,33 @@ __global__ __launch_bounds__(256) void k_state_passing_rev(Geo g, float* adj,
   if (dh0) Vec8<float>::store(dh0 + ((int64_t)seq * g.Hs + h) * PN + e0, cur);
 }
 
-hipError_t launch_state_passing_rev(const Geo& g, float* adj, const float* cs,
-                                    const float* dfinal, float* dh0, hipStream_t s) {
+// Both scans of the per-chunk backward in one launch: sequences [0, nseq) of
+// the grid's z axis run the forward scan (fp32 states, in place, from h0; no
+// final state), [nseq, 2 nseq) the reverse one.  The two are independent and
+// each is a walk over the chunks bound by the latency of its loads, so running
+// them side by side overlaps the two walks.
+__global__ __launch_bounds__(256) void k_state_passing_pair(Geo g, float* states,
+                                                            const float* __restrict__ cs,
+                                                            const float* __restrict__ h0,
+                                                            float* adj,
+                                                            const float* __restrict__ dfinal,
+                                                            float* __restrict__ dh0) {
+  const int64_t e0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  const int h = blockIdx.y, z = blockIdx.z;
+  if (z < g.nseq)
+    state_passing_thread<float>(g, states, cs, h0, states, nullptr, e0, h, z);
+  else
+    state_passing_rev_thread(g, adj, cs, dfinal, dh0, e0, h, z - g.nseq);
+}
+
+hipError_t launch_state_passing_pair(const Geo& g, float* states, const float* cs,
+                                     const float* h0, float* adj, const float* dfinal, float* dh0,
+                                     hipStream_t s) {
   const int64_t PN = (int64_t)g.P * g.N;
-  dim3 grid((unsigned)((PN / 8 + 255) / 256), g.H, g.nseq);
+  dim3 grid((unsigned)((PN / 8 + 255) / 256), g.H, 2 * g.nseq);
   if (g.nseq == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_state_passing_rev, grid, dim3(256), 0, s, g, adj, cs, dfinal, dh0);
+  hipLaunchKernelGGL(k_state_passing_pair, grid, dim3(256), 0, s, g, states, cs, h0, adj, dfinal,
+                     dh0);
   return hipGetLastError();
 }
 
