@@ -27,9 +27,10 @@ __global__ __launch_bounds__(256, 4) void k_chunk_state_bf16(Geo g, TArg x, TArg
 // item is multiplied and stored, the next item's x, B, cumsum and step sizes
 // are already on their way into registers, so every workgroup keeps loads in
 // flight through its whole life instead of waiting on memory once per item.
-// Every item is valid and every store unconditional (straight-line code), so
-// the compiler's wait for an item's loads leaves the previous item's stores in
-// flight.  x and B go to LDS in their natural row-major layout (16-byte rows
+// An item's output block is read out of LDS at the end of its iteration and
+// stored at the start of the next one, after the wait for that next item's
+// loads: no store sits between a load and its wait, so the compiler's wait
+// counts stay exact (every item is valid, no load is conditional).  x and B go to LDS in their natural row-major layout (16-byte rows
 // as loaded) and the token-major operands come from the gfx950 LDS transpose
 // read; the decay weight multiplies x after that read and x w is split into
 // bf16 hi + lo there.  Items are ordered (chunk, head, block) -- the heads of a
