@@ -244,7 +244,7 @@ def _equal_grads(a, b):
             assert torch.equal(x, y), f"{n} differs between head passes and one pass"
 
 
-@pytest.mark.parametrize("case", ["whole_groups", "within_a_group"])
+@pytest.mark.parametrize("case", ["whole_groups", "within_a_group", "within_a_group_input_dt"])
 def test_head_passes_match_one_pass(case):
     """A smaller workspace makes the backward take its heads in passes: four
     passes of one group (two heads each), or one group of 24 heads in passes of
@@ -256,25 +256,27 @@ def test_head_passes_match_one_pass(case):
         H, G, hsmall, gsmall = 8, 4, 2, 1
     else:
         H, G, hsmall, gsmall = 24, 1, 16, 1
+    kw = {"input_dt": True} if case.endswith("input_dt") else {}
     lens = (130, 0, 257, 64)
     w = small_workload(f"bwdf_pass_{case}", seqlen=sum(lens), nheads=H, headdim=64, ngroups=G,
                        dstate=64, chunk_size=128, seqlens=lens)
     inp = with_initial_states(make_inputs(w))
     dout, dfin = upstream(inp)
-    one = gpu_bwd(w, inp, dout, dfin, "fused")
+    one = gpu_bwd(w, inp, dout, dfin, "fused", **kw)
     cu = device_inputs(inp, torch.bfloat16)["cu_seqlens"]
-    small = ssd.Problem(1, w.seqlen, hsmall, 64, gsmall, 64, 128, nseq=len(lens), cu_seqlens=cu)
+    small = ssd.Problem(1, w.seqlen, hsmall, 64, gsmall, 64, 128, nseq=len(lens), cu_seqlens=cu,
+                        **kw)
     need = small.backward_workspace_size("fused")
-    full = ssd.Problem(1, w.seqlen, H, 64, G, 64, 128, nseq=len(lens), cu_seqlens=cu)
+    full = ssd.Problem(1, w.seqlen, H, 64, G, 64, 128, nseq=len(lens), cu_seqlens=cu, **kw)
     assert need < full.backward_workspace_size("fused")
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    passes = gpu_bwd(w, inp, dout, dfin, "fused", workspace=ws)
+    passes = gpu_bwd(w, inp, dout, dfin, "fused", workspace=ws, **kw)
     _equal_grads(passes, one)
-    check(passes, ref_bwd(inp, dout, dfin))
+    check(passes, ref_bwd(inp, dout, dfin, **kw))
     # below the smallest pass: an error, nothing launched
     tiny = torch.empty(1024, dtype=torch.uint8, device="cuda")
     with pytest.raises(ssd.SSDError):
-        gpu_bwd(w, inp, dout, dfin, "fused", workspace=tiny)
+        gpu_bwd(w, inp, dout, dfin, "fused", workspace=tiny, **kw)
 
 
 def test_bit_identical_repeats():
