@@ -272,8 +272,9 @@ typedef struct ssd_fwd_args {
  * inputs (the same page: the cumsum and C.B^T are recomputed per tile and the
  * state is handed between workgroups instead of storing the per-chunk
  * intermediates): a launch that sums each range of chunks into one state,
- * then the output launch, which folds those per range and walks its chunks
- * (plus a small chunk-table kernel in packed mode); it always works on
+ * a small launch that turns those into each range's carry-in, then the
+ * output launch, which walks each range's chunks from its carry-in (plus a
+ * small chunk-table kernel in packed mode); it always works on
  * 128-token chunks (the result does not depend on the chunk length), takes
  * bf16 x, B, C (and z) and dstate <= 128, and returns SSD_ERR_UNSUPPORTED
  * otherwise; it stores no per-chunk states (the carried state stays in

@@ -15,22 +15,24 @@
 // depend on the chunk length, so the problem's chunk_size only matters to the
 // staged path).  A unit is (head h, 64-row slab of P); its chunks are cut into
 // `nr` ranges of R consecutive chunks, and one workgroup owns one (unit,
-// range).  Two launches of the same kernel template (after a small table /
-// empty-sequence kernel in packed mode):
+// range).  Three launches (after a small table / empty-sequence kernel in
+// packed mode):
 //   1. the aggregate launch: every range whose last sequence continues into
 //      the next range runs the chunk-state recurrence over its chunks from a
 //      zero state -- or from the sequence's initial state when the sequence
 //      starts inside the range -- and stores that aggregate with the range's
 //      total decay E;
-//   2. the output launch: a range whose first chunk continues a sequence
-//      folds the aggregates of the preceding ranges back to the one where the
-//      sequence starts, oldest first (carry = E carry + agg): its carry-in.
+//   2. the carry launch: per unit, the ranges in order turn each aggregate into
+//      the state at the end of its range (carry = E carry + agg, restarted
+//      where a sequence starts), in place;
+//   3. the output launch: a range whose first chunk continues a sequence
+//      loads the state its predecessor ends with: its carry-in.
 //      Then it walks its chunks: cumsum from dt, chunk state S_j, the carry-in
 //      H_j of the chunk staged in LDS as bf16 hi + lo, C.B^T tile by tile,
 //      Y_off + Y_diag (with the D skip on its diagonal), SiLU gate, store;
 //      H_{j+1} = exp(Lambda_j) H_j + S_j in registers, and the final state at
 //      a sequence's last chunk.
-// The hand-off between the two is the launch boundary: no workgroup ever
+// The hand-offs between them are launch boundaries: no workgroup ever
 // waits for another, so no wait can stall or time out, and the order of every
 // sum is fixed (results are bit-identical run to run).  The aggregate launch
 // has the output launch's work split, without its register and LDS demands
@@ -68,7 +70,7 @@ namespace ssd {
 namespace {
 
 constexpr int FC = 128;                 // internal chunk length
-constexpr int kFoldBatch = 4;           // aggregates loaded per round trip of the fold
+constexpr int kCarryBatch = 8;          // aggregates loaded per round trip of the carry launch
 
 // softplus(u) = max(u, 0) + log1p(exp(-|u|)).  log1p(e) for e in (0, 1] as
 // log(1 + e) * e / ((1 + e) - 1): the quotient corrects the rounding of 1 + e
@@ -418,44 +420,17 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
 
   SSD_TRACE(2);
 
-  // ---- carry-in: the aggregates of the preceding ranges back to the one
-  // where the sequence starts (whose aggregate starts from the initial
-  // state), folded oldest first: carry = E_rr carry + agg_rr, kFoldBatch
-  // aggregates per round trip to memory.  They were written by the aggregate
-  // launch, which has ended, so nothing is waited for.
+  // ---- carry-in: the state the preceding range ends with, left in its
+  // aggregate slot by the carry launch (which has ended, so nothing is waited
+  // for)
   if (need_fold) {
+    const float* src = slot_base(r - 1);
+    const uint32_t lo = slot_lane();
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) carry[nt] = zero4();
-    const int first = f0 / a.R, n = r - first;
-    for (int b = 0; b < n; b += kFoldBatch) {
-      // (loads past the n available repeat the last one, unused: loads under
-      // a branch would leave the compiler's wait counts conservative)
-      f32x4 v[kFoldBatch][NT];
-      float e[kFoldBatch];
-#pragma unroll
-      for (int m = 0; m < kFoldBatch; ++m) {
-        const int rm = first + min(b + m, n - 1);
-        const float* src = slot_base(rm);
-        const uint32_t lo = slot_lane();
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          v[m][nt] = *reinterpret_cast<const f32x4*>(at(src, lo + nt * 16));
-        e[m] = a.edec[rm * a.U + u];
-      }
-#pragma unroll
-      for (int m = 0; m < kFoldBatch; ++m) {
-        // an unused term folds as carry * 1 + 0, which leaves carry as it is
-        const bool ok = b + m < n;
-        const float em = ok ? e[m] : 1.0f, wm = ok ? 1.0f : 0.0f;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) carry[nt][i] = fmaf(em, carry[nt][i], wm * v[m][nt][i]);
-      }
-    }
+    for (int nt = 0; nt < NT; ++nt) carry[nt] = *reinterpret_cast<const f32x4*>(at(src, lo + nt * 16));
   }
-  // the first chunk's loads (after the fold's: a wait for those then covers
-  // none of these)
+  // the first chunk's loads (after the carry-in's: a wait for that then
+  // covers none of these)
   Chunk c;
   get_chunk(g, j0, c);
   Stage st;
@@ -972,6 +947,74 @@ __global__ __launch_bounds__(kAggThreads, 2) void k_fused_agg(FusedArgs a) {
 #endif
 }
 
+// ---- The carry launch: per unit, the ranges in order replace each stored
+// aggregate by the state at the end of its range (of the range's last
+// sequence, the one that continues into the next range): the aggregate itself
+// where that sequence starts inside the range (its aggregate already starts
+// from the sequence's initial state), else E times the state the previous
+// range ends with plus the aggregate -- the inter-chunk propagation of the SSD
+// Reference ("Inter-chunk propagation") taken a whole range at a time.  Each
+// thread owns four consecutive words of one unit's 64 x NMAX state; kCarryBatch
+// slots are loaded before the first of them is combined.  Unit u runs on the
+// XCD whose L2 holds its aggregates (the aggregate launch's placement).
+template <int NT>
+__global__ __launch_bounds__(256) void k_fused_carry(FusedArgs a) {
+  constexpr int NMAX = 16 * NT;
+  constexpr int PIECES = 64 * NMAX / 4;  // f32x4 pieces of one state
+  constexpr int WPU = PIECES / 256;      // workgroups per unit
+  static_assert(PIECES % 256 == 0, "a unit's state fills whole workgroups");
+  const Geo& g = a.g;
+  const int total = a.U * WPU;
+  const int it = a.U % kNumXcd == 0 ? xcd_remap((int)blockIdx.x, total) : (int)blockIdx.x;
+  const int u = it / WPU;
+  const uint32_t off = (uint32_t)((it % WPU) * 256 + (int)threadIdx.x) * 4;
+  const int Kr = g.meta ? meta_word(g.meta, 0) : g.K;
+  const int nlast = a.nr - 1;  // the last range hands nothing on
+  f32x4 prev = zero4();
+  for (int b = 0; b < nlast; b += kCarryBatch) {
+    // which slots take over the previous range's state: those of ranges
+    // whose last sequence continues into the next range (they have an
+    // aggregate) and came in from the previous range
+    bool take[kCarryBatch];
+#pragma unroll
+    for (int m = 0; m < kCarryBatch; ++m) {
+      const int rr = b + m;
+      const int j0 = rr * a.R, j1 = min(j0 + a.R, Kr);
+      take[m] = false;
+      if (rr < nlast && j0 < j1) {
+        Chunk clast;
+        get_chunk(g, j1 - 1, clast);
+        int fs, ls;
+        seq_chunks(g, clast.seq, fs, ls);
+        take[m] = j1 < ls && fs < j0;
+      }
+    }
+    // (slots past the last one repeat it, unused: loads under a branch would
+    // leave the compiler's wait counts conservative)
+    f32x4 v[kCarryBatch];
+    float e[kCarryBatch];
+#pragma unroll
+    for (int m = 0; m < kCarryBatch; ++m) {
+      const int rm = min(b + m, nlast - 1);
+      v[m] = *reinterpret_cast<const f32x4*>(
+          at(a.agg + ((int64_t)rm * a.U + u) * 64 * NMAX, off));
+      e[m] = a.edec[rm * a.U + u];
+    }
+    // where a sequence starts inside a range, its slot already holds the end
+    // state (or is never read)
+#pragma unroll
+    for (int m = 0; m < kCarryBatch; ++m) {
+      if (take[m]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[m][i] = fmaf(e[m], prev[i], v[m][i]);
+        *reinterpret_cast<f32x4*>(at(a.agg + ((int64_t)(b + m) * a.U + u) * 64 * NMAX, off)) =
+            v[m];
+      }
+      prev = v[m];
+    }
+  }
+}
+
 FusedPlan fused_plan(int64_t K, int H, int P, int N) {
   FusedPlan pl;
   pl.PS = (P + 63) / 64;
@@ -1029,8 +1072,20 @@ hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s) {
       default: SSD_FUSED_AGG(8); break;
     }
 #undef SSD_FUSED_AGG
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    // the carry launch (only when some range takes over a state that is not
+    // the first range's own aggregate)
+    if (pl.nr > 2) {
+      const dim3 cgrid((unsigned)(pl.U * (64 * 16 * pl.NT / 4 / 256)));
+      switch (pl.NT) {
+        case 2: hipLaunchKernelGGL(k_fused_carry<2>, cgrid, dim3(256), 0, s, a); break;
+        case 4: hipLaunchKernelGGL(k_fused_carry<4>, cgrid, dim3(256), 0, s, a); break;
+        default: hipLaunchKernelGGL(k_fused_carry<8>, cgrid, dim3(256), 0, s, a); break;
+      }
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
 #define SSD_FUSED(TO, NT)                                                                   \
   do {                                                                                      \

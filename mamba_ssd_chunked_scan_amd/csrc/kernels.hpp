@@ -84,15 +84,16 @@ struct FusedLaunch {
 };
 // Phase timestamps per (unit, range) item in SSD_FUSED_TRACE builds: [0] and
 // [1] the aggregate launch's start and end for the item; the output launch's
-// [2] start, [3] carry-in folded; for chunks k < 4 five stamps [4 + 5k ..
+// [2] start, [3] carry-in loaded; for chunks k < 4 five stamps [4 + 5k ..
 // 8 + 5k] after its phases A (carry-in to LDS), B (Y_off), C (x and B to
 // LDS), D (state, C.B^T, Y_diag) and E (gate, store); for chunks 4 <= k < 10
 // the end of the chunk at [20 + k]; [slots - 2] end and [slots - 1] the XCD
 // the item ran on.
 constexpr int kFusedTraceSlots = 32;
 
-// Up to three launches: the chunk table / empty sequences (packed mode or no
-// tokens), the range aggregates (more than one range), the outputs.
+// Up to four launches: the chunk table / empty sequences (packed mode or no
+// tokens), the range aggregates (more than one range), their carry scan (more
+// than two ranges), the outputs.
 hipError_t launch_fused_fwd(const FusedLaunch& f, hipStream_t s);
 
 // ---- backward (bwd.hip): tokens on the packed axis, ntok = b * T (batch) or

@@ -6,7 +6,7 @@
 The profiling library is libssd with -DSSD_FUSED_TRACE: every (unit, range)
 item stores the device's 100 MHz clock (s_memrealtime) at the start and end of
 its range aggregate (first launch), and at the start of the output launch,
-after its carry-in is folded, after each chunk and at its end, in a region at
+after its carry-in is loaded, after each chunk and at its end, in a region at
 the end of its workspace.  The report gives, over the items of the last of
 several forwards, the mean and spread of each phase and each launch's span.
 """
@@ -87,7 +87,7 @@ def main(argv=None):
     s2, s3, se = tr[:, 2], tr[:, 3], tr[:, SLOTS - 2]
     print(f"output launch: starts {rel(s2.min()):.1f} .. {rel(s2.max()):.1f} us, "
           f"ends {rel(se.min()):.1f} .. {rel(se.max()):.1f} us (span {us(se.max() - s2.min()):.1f})")
-    print(f"  carry-in fold   mean {us((s3 - s2).mean()):.2f}  max {us((s3 - s2).max()):.2f} us")
+    print(f"  carry-in        mean {us((s3 - s2).mean()):.2f}  max {us((s3 - s2).max()):.2f} us")
     ph = {n: [] for n in "ABCDE"}
     ck, k0 = [], []
     for i in range(items):
@@ -113,6 +113,12 @@ def main(argv=None):
           + " us  (A carry-in to LDS, B Y_off, C x/B to LDS, D state + C.B^T + Y_diag,"
           " E gate + store)")
     print(f"  item total      mean {us((se - s2).mean()):.1f}  max {us((se - s2).max()):.1f} us")
+    # per range
+    rix = np.arange(items) // U
+    for r_ in range(nr):
+        m = rix == r_
+        print(f"  range {r_}: carry-in {us((s3[m] - s2[m]).mean()):5.2f}  item {us((se[m] - s2[m]).mean()):6.1f}"
+              f"  ends mean {rel(se[m]).mean():6.1f} max {rel(se[m]).max():6.1f} us")
     return 0
 
 
