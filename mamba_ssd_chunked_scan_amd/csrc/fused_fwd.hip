@@ -93,6 +93,9 @@ __device__ __forceinline__ float softplus_fast(float u) {
 #ifndef SSD_FUSED_HPAD
 #define SSD_FUSED_HPAD 8
 #endif
+#ifndef SSD_FUSED_SG
+#define SSD_FUSED_SG 4
+#endif
 #ifndef SSD_FUSED_YPAD
 #define SSD_FUSED_YPAD 4
 #endif
@@ -399,11 +402,17 @@ __global__ __launch_bounds__(256, 2) void k_fused_fwd(FusedArgs a) {
         xw[4 + 2 * d + 1] = bf16_hi_f32(xv[2 + d]) * w1[2 * d + 1];
       }
       const FragSplit b = split_f32x8(xw);
+      // the B fragments in groups of SG, each group read before its products
+      // (one LDS round trip per group instead of one per n-tile)
+      constexpr int SG = SSD_FUSED_SG < NT ? SSD_FUSED_SG : NT;
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        FragBF av;
-        av.v = lds_frag_tr(s_b, BLD, k0, k0 + 4, nt * 16);
-        mma(acc[nt], av, b);
+      for (int n0 = 0; n0 < NT; n0 += SG) {
+        FragBF bt[SG];
+#pragma unroll
+        for (int i = 0; i < SG; ++i) bt[i].v = lds_frag_tr(s_b, BLD, k0, k0 + 4, (n0 + i) * 16);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < SG; ++i) mma(acc[n0 + i], bt[i], b);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -890,13 +899,16 @@ __global__ __launch_bounds__(kAggThreads, 2) void k_fused_agg(FusedArgs a) {
         xw[4 + 2 * d] = bf16_lo_f32(xv[2 + d]) * w1[2 * d];
         xw[4 + 2 * d + 1] = bf16_hi_f32(xv[2 + d]) * w1[2 * d + 1];
       }
-      const FragSplit b = split_f32x8(xw);
+      // every B fragment of the k-block is read before the first product:
+      // one LDS round trip per k-block instead of one per n-tile
+      FragBF bt[NTS];
 #pragma unroll
-      for (int nt = 0; nt < NTS; ++nt) {
-        FragBF av;
-        av.v = lds_frag_tr(s_b, BLD, k0, k0 + 4, (nh * NTS + nt) * 16);
-        mma(carry[nt], av, b);
-      }
+      for (int nt = 0; nt < NTS; ++nt) bt[nt].v = lds_frag_tr(s_b, BLD, k0, k0 + 4, (nh * NTS + nt) * 16);
+      const FragSplit b = split_f32x8(xw);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int nt = 0; nt < NTS; ++nt) mma(carry[nt], bt[nt], b);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
