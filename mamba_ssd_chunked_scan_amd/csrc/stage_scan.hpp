@@ -384,7 +384,15 @@ __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, 
       for (int kk = 0; kk < 4; ++kk) {
         if (k0 + kk >= nkd) break;
         const int s0 = (k0 + kk) * 32 + q * 8;
+        // the cumsum, then the x^T fragments, whose LDS latency runs under the
+        // decay weights below (LDS reads complete in order: waiting for the
+        // cumsum does not wait for them)
         const f32x8 csv = Vec8<float>::load(s_cs + s0);
+        FragBF xb[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          xb[pt].v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                    &s_xt[(pt * 16 + r16) * LDW + s0 / 2]));
         f32x8 m;
         if (k0 + kk < nkd - 1 && c.len == C) {
           // a k-block wholly below the diagonal of a full chunk: every
@@ -407,12 +415,7 @@ __device__ __forceinline__ void chunk_scan_block(const Geo& g, const float* CB, 
         }
         const FragSplit mf = split_f32x8(m);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          FragBF xb;
-          xb.v = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
-                                                &s_xt[(pt * 16 + r16) * LDW + s0 / 2]));
-          mma(acc[u][pt], mf, xb);
-        }
+        for (int pt = 0; pt < 4; ++pt) mma(acc[u][pt], mf, xb[pt]);
       }
     }
   }
