@@ -530,14 +530,25 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dx(BwdChunkArgs a) {
       for (int kp = 0; kp <= lt / 2; ++kp) {
         const int sa = 2 * kp, sb = 2 * kp + 1;
         f32x4 va = zero4(), vb = zero4();
+        // every B row fragment of the pair first (one LDS round trip), then
+        // the products
+        FragBF ba[NKB], bb[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          FragBF ba, bb;
-          ba.v = *reinterpret_cast<const bf16x8*>(&s_b[(sa * 16 + r16) * CLD + kb * 32 + q * 8]);
-          bb.v = *reinterpret_cast<const bf16x8*>(&s_b[(sb * 16 + r16) * CLD + kb * 32 + q * 8]);
-          mma(va, ba, cf[ui][kb]);
-          mma(vb, bb, cf[ui][kb]);
+          ba[kb].v = *reinterpret_cast<const bf16x8*>(&s_b[(sa * 16 + r16) * CLD + kb * 32 + q * 8]);
+          bb[kb].v = *reinterpret_cast<const bf16x8*>(&s_b[(sb * 16 + r16) * CLD + kb * 32 + q * 8]);
         }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          mma(va, ba[kb], cf[ui][kb]);
+          mma(vb, bb[kb], cf[ui][kb]);
+        }
+        // the x^T fragments go out before M is formed: their latency runs
+        // under its exponentials
+        FragBF xt[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt)
+          xt[pt].v = lds_frag_tr(s_x, TLD, sa * 16 + q * 4, sb * 16 + q * 4, pt * 16);
         f32x8 m;
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
@@ -549,11 +560,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dx(BwdChunkArgs a) {
         }
         const FragSplit mf = split_f32x8(m);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          FragBF xt;
-          xt.v = lds_frag_tr(s_x, TLD, sa * 16 + q * 4, sb * 16 + q * 4, pt * 16);
-          mma(yt[ui][pt], xt, mf);
-        }
+        for (int pt = 0; pt < 4; ++pt) mma(yt[ui][pt], xt[pt], mf);
       }
     }
     // dz = dout y silu'(z), silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z)))
@@ -649,13 +656,16 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dx(BwdChunkArgs a) {
       for (int lp = sbt / 2; lp < 4; ++lp) {
         const int la = 2 * lp, lb = 2 * lp + 1;
         f32x4 ca = zero4(), cb = zero4(), xa = zero4(), xb2 = zero4();
+        FragBF c0[NKB], c1[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-          FragBF c0, c1;
-          c0.v = *reinterpret_cast<const bf16x8*>(&s_c[(la * 16 + r16) * CLD + kb * 32 + q * 8]);
-          c1.v = *reinterpret_cast<const bf16x8*>(&s_c[(lb * 16 + r16) * CLD + kb * 32 + q * 8]);
-          mma(ca, c0, bf[ui][kb]);
-          mma(cb, c1, bf[ui][kb]);
+          c0[kb].v = *reinterpret_cast<const bf16x8*>(&s_c[(la * 16 + r16) * CLD + kb * 32 + q * 8]);
+          c1[kb].v = *reinterpret_cast<const bf16x8*>(&s_c[(lb * 16 + r16) * CLD + kb * 32 + q * 8]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          mma(ca, c0[kb], bf[ui][kb]);
+          mma(cb, c1[kb], bf[ui][kb]);
         }
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
@@ -664,6 +674,13 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dx(BwdChunkArgs a) {
               xr[kp]);
           mma(xb2, lds_split(&s_yh[(lb * 16 + r16) * TLD + pc], &s_yl[(lb * 16 + r16) * TLD + pc]),
               xr[kp]);
+        }
+        // the dy^T fragments go out before M is formed
+        FragSplit dyt[4];
+#pragma unroll
+        for (int pt = 0; pt < 4; ++pt) {
+          dyt[pt].hi = lds_frag_tr(s_yh, TLD, la * 16 + q * 4, lb * 16 + q * 4, pt * 16);
+          dyt[pt].lo = lds_frag_tr(s_yl, TLD, la * 16 + q * 4, lb * 16 + q * 4, pt * 16);
         }
         f32x8 m;
         double rowa[4], rowb[4];
@@ -683,12 +700,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dx(BwdChunkArgs a) {
         }
         const FragSplit mf = split_f32x8(m);
 #pragma unroll
-        for (int pt = 0; pt < 4; ++pt) {
-          FragSplit dyt;
-          dyt.hi = lds_frag_tr(s_yh, TLD, la * 16 + q * 4, lb * 16 + q * 4, pt * 16);
-          dyt.lo = lds_frag_tr(s_yl, TLD, la * 16 + q * 4, lb * 16 + q * 4, pt * 16);
-          mma(gt[ui][pt], dyt, mf);
-        }
+        for (int pt = 0; pt < 4; ++pt) mma(gt[ui][pt], dyt[pt], mf);
 #pragma unroll
         for (int e4 = 0; e4 < 4; ++e4) {
           const double ra = group16_sum_f64(rowa[e4]);
@@ -967,14 +979,23 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dbc(BwdChunkArgs a) {
         for (int kp2 = 0; kp2 <= lt / 2; ++kp2) {
           const int sa = 2 * kp2, sb = 2 * kp2 + 1;
           f32x4 va = zero4(), vb = zero4();
+          // operand reads ahead of their products: the x rows, then (under
+          // the decay weights) the B^T fragments
+          FragBF xa[2], xb2[2];
 #pragma unroll
           for (int kp = 0; kp < 2; ++kp) {
-            FragBF xa, xb2;
-            xa.v = *reinterpret_cast<const bf16x8*>(&s_x[(sa * 16 + r16) * TLD + kp * 32 + q * 8]);
-            xb2.v = *reinterpret_cast<const bf16x8*>(&s_x[(sb * 16 + r16) * TLD + kp * 32 + q * 8]);
-            mma(va, xa, dyf[kp]);
-            mma(vb, xb2, dyf[kp]);
+            xa[kp].v = *reinterpret_cast<const bf16x8*>(&s_x[(sa * 16 + r16) * TLD + kp * 32 + q * 8]);
+            xb2[kp].v = *reinterpret_cast<const bf16x8*>(&s_x[(sb * 16 + r16) * TLD + kp * 32 + q * 8]);
           }
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp) {
+            mma(va, xa[kp], dyf[kp]);
+            mma(vb, xb2[kp], dyf[kp]);
+          }
+          FragBF bt[4];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            bt[nt].v = lds_frag_tr(s_bt, TLD, sa * 16 + q * 4, sb * 16 + q * 4, nt * 16);
           f32x8 w;
 #pragma unroll
           for (int e4 = 0; e4 < 4; ++e4) {
@@ -984,27 +1005,24 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dbc(BwdChunkArgs a) {
           }
           const FragSplit wf = split_f32x8(w);
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            FragBF bt;
-            bt.v = lds_frag_tr(s_bt, TLD, sa * 16 + q * 4, sb * 16 + q * 4, nt * 16);
-            mma(acc[ui][nt], wf, bt);
-          }
+          for (int nt = 0; nt < 4; ++nt) mma(acc[ui][nt], wf, bt[nt]);
         }
         const float el = s_el[l];
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
+          FragSplit hs[4];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            hs[nt].hi = lds_frag_tr(s_hh, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
+            hs[nt].lo = lds_frag_tr(s_hl, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
+          }
           f32x8 v = bf8_to_f32(__builtin_bit_cast(u32x4, dyf[kp].hi));
           const f32x8 lo = bf8_to_f32(__builtin_bit_cast(u32x4, dyf[kp].lo));
 #pragma unroll
           for (int i = 0; i < 8; ++i) v[i] = (v[i] + lo[i]) * el;
           const FragSplit af = split_f32x8(v);
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            FragSplit hs;
-            hs.hi = lds_frag_tr(s_hh, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
-            hs.lo = lds_frag_tr(s_hl, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
-            mma(acc[ui][nt], af, hs);
-          }
+          for (int nt = 0; nt < 4; ++nt) mma(acc[ui][nt], af, hs[nt]);
         }
       }
     } else {
@@ -1024,14 +1042,24 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dbc(BwdChunkArgs a) {
         for (int lp = sbt / 2; lp < 4; ++lp) {
           const int la = 2 * lp, lb = 2 * lp + 1;
           f32x4 va = zero4(), vb = zero4();
+          // operand reads ahead of their products: the dy rows, then (under
+          // the decay weights) the C^T fragments
+          FragSplit ya[2], yb[2];
 #pragma unroll
           for (int kp = 0; kp < 2; ++kp) {
             const int pc = kp * 32 + q * 8;
-            mma(va, lds_split(&s_yh[(la * 16 + r16) * TLD + pc], &s_yl[(la * 16 + r16) * TLD + pc]),
-                xr[kp]);
-            mma(vb, lds_split(&s_yh[(lb * 16 + r16) * TLD + pc], &s_yl[(lb * 16 + r16) * TLD + pc]),
-                xr[kp]);
+            ya[kp] = lds_split(&s_yh[(la * 16 + r16) * TLD + pc], &s_yl[(la * 16 + r16) * TLD + pc]);
+            yb[kp] = lds_split(&s_yh[(lb * 16 + r16) * TLD + pc], &s_yl[(lb * 16 + r16) * TLD + pc]);
           }
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp) {
+            mma(va, ya[kp], xr[kp]);
+            mma(vb, yb[kp], xr[kp]);
+          }
+          FragBF ct[4];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            ct[nt].v = lds_frag_tr(s_ct, TLD, la * 16 + q * 4, lb * 16 + q * 4, nt * 16);
           f32x8 w;
 #pragma unroll
           for (int e4 = 0; e4 < 4; ++e4) {
@@ -1041,26 +1069,23 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dbc(BwdChunkArgs a) {
           }
           const FragSplit wf = split_f32x8(w);
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            FragBF ct;
-            ct.v = lds_frag_tr(s_ct, TLD, la * 16 + q * 4, lb * 16 + q * 4, nt * 16);
-            mma(acc[ui][nt], wf, ct);
-          }
+          for (int nt = 0; nt < 4; ++nt) mma(acc[ui][nt], wf, ct[nt]);
         }
         const float es = s_es[s];
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp) {
+          FragSplit ds[4];
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            ds[nt].hi = lds_frag_tr(s_dh, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
+            ds[nt].lo = lds_frag_tr(s_dl, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
+          }
           f32x8 v = bf8_to_f32(__builtin_bit_cast(u32x4, xr[kp].v));
 #pragma unroll
           for (int i = 0; i < 8; ++i) v[i] *= es;
           const FragSplit af = split_f32x8(v);
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            FragSplit ds;
-            ds.hi = lds_frag_tr(s_dh, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
-            ds.lo = lds_frag_tr(s_dl, TLD, kp * 32 + q * 8, kp * 32 + q * 8 + 4, nt * 16);
-            mma(acc[ui][nt], af, ds);
-          }
+          for (int nt = 0; nt < 4; ++nt) mma(acc[ui][nt], af, ds[nt]);
         }
       }
     }
