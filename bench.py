@@ -28,7 +28,8 @@ back to back without the flush are reported as `warm`.  The dominant launch is
 reported against its roofline (algorithmic bytes per launch / median cold
 duration vs 8 TB/s HBM, and vs the achievable bandwidth of a 1 GiB copy
 measured in the same run: `measured_peaks`).  The fused forward is one call of
-two launches (range aggregates, then outputs); its call is the timed unit.
+three launches (range aggregates, their carry-ins, then outputs); its call is the
+timed unit.
 
 'configs' carries the other workloads (Granite dims, the packed batch, long
 context fused and staged with fp32 / bf16 states, staged Nemotron-Nano with
@@ -496,7 +497,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": dom + (" (the call: range-aggregate and output launches)"
+            "kernel": dom + (" (the call: range-aggregate, carry and output launches)"
                              if dom == "fused_fwd" else ""),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,

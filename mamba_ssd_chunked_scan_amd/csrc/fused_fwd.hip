@@ -9,7 +9,7 @@
 // describes its fused kernel: the log-decay cumsum and C.B^T are recomputed
 // where they are consumed instead of being stored, and the chunk-to-chunk state
 // is handed between workgroups through memory (here: per range of chunks,
-// between two launches, so that no workgroup waits for another).
+// across launch boundaries, so that no workgroup waits for another).
 //
 // Work split.  The internal chunk is 128 tokens (the chunked result does not
 // depend on the chunk length, so the problem's chunk_size only matters to the
