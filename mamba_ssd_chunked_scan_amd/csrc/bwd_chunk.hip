@@ -482,19 +482,31 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dx(BwdChunkArgs a) {
       for (int kb = 0; kb < NKB; ++kb)
         cf[ui][kb].v = *reinterpret_cast<const bf16x8*>(&s_c[l * CLD + kb * 32 + q * 8]);
     }
-    // Y_off^T = Hin C^T (rows p, columns l); <dS, Hin> over p-tile w on the way
+    // <dS, Hin> over p-tile w (this wave's share of the decay gradient), every
+    // row load issued before the first product
     double ip = 0.0;
+    {
+      f32x8 hw[NKB], dw[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        hw[kb] = state8(hin, w4 * 16 + r16, kb);
+        dw[kb] = state8(cx.ds, w4 * 16 + r16, kb);
+      }
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) ip += (double)hw[kb][i] * (double)dw[kb][i];
+    }
+    // Y_off^T = Hin C^T (rows p, columns l): a k-block's four state rows are
+    // loaded together, then multiplied (one round trip to memory per k-block)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      f32x8 hv[4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) hv[pt] = state8(hin, pt * 16 + r16, kb);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const f32x8 hv = state8(hin, pt * 16 + r16, kb);
-        if (pt == w4) {
-          const f32x8 dv = state8(cx.ds, pt * 16 + r16, kb);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) ip += (double)hv[i] * (double)dv[i];
-        }
-        const FragSplit hf = split_f32x8(hv);
+        const FragSplit hf = split_f32x8(hv[pt]);
         mma(yt[0][pt], hf, cf[0][kb]);
         mma(yt[1][pt], hf, cf[1][kb]);
       }
@@ -611,12 +623,16 @@ __global__ __launch_bounds__(512, 1) void k_bwd_dx(BwdChunkArgs a) {
       for (int kb = 0; kb < NKB; ++kb)
         bf[ui][kb].v = *reinterpret_cast<const bf16x8*>(&s_b[s * CLD + kb * 32 + q * 8]);
     }
-    // inter part g^T += dS B^T, scaled by exp(Lambda - cs_s); R_s
+    // inter part g^T += dS B^T, scaled by exp(Lambda - cs_s); R_s.  A k-block's
+    // four state rows are loaded together, then multiplied.
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
+      f32x8 dv[4];
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt) dv[pt] = state8(cx.ds, pt * 16 + r16, kb);
 #pragma unroll
       for (int pt = 0; pt < 4; ++pt) {
-        const FragSplit df = split_f32x8(state8(cx.ds, pt * 16 + r16, kb));
+        const FragSplit df = split_f32x8(dv[pt]);
         mma(gt[0][pt], df, bf[0][kb]);
         mma(gt[1][pt], df, bf[1][kb]);
       }
