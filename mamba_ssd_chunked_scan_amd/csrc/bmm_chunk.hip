@@ -12,7 +12,8 @@ __global__ __launch_bounds__(256) void k_bmm_chunk(Geo g, TArg Cm, TArg Bm, floa
 template <int C>
 __global__ __launch_bounds__(256, 2) void k_bmm_group_bf16(Geo g, TArg Cm, TArg Bm,
                                                          float* __restrict__ CB) {
-  bmm_group_bf16<C>(g, Cm, Bm, CB, blockIdx.x, blockIdx.y);
+  __shared__ __align__(16) bf16 s_b[C * (128 + 8)];
+  bmm_group_bf16<C>(g, Cm, Bm, CB, blockIdx.x, blockIdx.y, s_b);
 }
 
 hipError_t launch_bmm_chunk(const Geo& g, TArg C, TArg B, int in_dtype, float* CB,
