@@ -300,12 +300,15 @@ __global__ __launch_bounds__(256, 2) void k_bwd_adj_state(BwdChunkArgs a) {
     FragSplit af;
     af.hi = lds_frag_tr(s_dyh, TLD, k0, k0 + 4, wave * 16);
     af.lo = lds_frag_tr(s_dyl, TLD, k0, k0 + 4, wave * 16);
+    // every C fragment of the k-block before the products (one LDS round trip
+    // per k-block instead of one per n-tile)
+    FragBF bf[NT];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      FragBF bf;
-      bf.v = lds_frag_tr(s_c, CLD, k0, k0 + 4, nt * 16);
-      mma(acc[nt], af, bf);
-    }
+    for (int nt = 0; nt < NT; ++nt) bf[nt].v = lds_frag_tr(s_c, CLD, k0, k0 + 4, nt * 16);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) mma(acc[nt], af, bf[nt]);
+    __builtin_amdgcn_sched_barrier(0);
   }
   float* dst = a.adj + ((int64_t)j * g.H + h) * g.P * g.N;
 #pragma unroll
