@@ -157,9 +157,19 @@ struct FusedArgs {
       a.trace[(size_t)(r * a.U + u) * kFusedTraceSlots + (k)] =                        \
           __builtin_amdgcn_s_memrealtime();                                            \
   } while (0)
+// the aggregate launch's chunk steps: stamp m of step ks (first four steps)
+#define SSD_TRACE_AGG(m)                                                               \
+  do {                                                                                 \
+    if (tid == 0 && a.trace && ks < 4)                                                 \
+      a.trace[(size_t)(r * a.U + u) * kFusedTraceSlots + 32 + 6 * ks + (m)] =          \
+          __builtin_amdgcn_s_memrealtime();                                            \
+  } while (0)
 #else
 #define SSD_TRACE(k) \
   do {               \
+  } while (0)
+#define SSD_TRACE_AGG(m) \
+  do {                   \
   } while (0)
 #endif
 
@@ -920,19 +930,31 @@ __global__ __launch_bounds__(kAggThreads, 2) void k_fused_agg(FusedArgs a) {
   load(sa, ca);
   get_chunk(g, min(js + 1, j1 - 1), cb);
   load(sb, cb);
+#ifdef SSD_FUSED_TRACE
+  int ks = 0;  // (the profiling build's step count)
+#endif
   auto step = [&](Stage& st, Chunk& c, int j) {
     __syncthreads();  // every wave is done with the previous chunk's tiles
+    SSD_TRACE_AGG(0);
     stage(st, c);
+    SSD_TRACE_AGG(1);
     const Chunk cur = c;
     get_chunk(g, min(j + 2, j1 - 1), c);  // refill with chunk j + 2 (or the last, unused)
     load(st, c);
+    SSD_TRACE_AGG(2);
     __syncthreads();
+    SSD_TRACE_AGG(3);
     const float lam = weights(cur);
+    SSD_TRACE_AGG(4);
     const float e = fast_exp2(lam);
 #pragma unroll
     for (int nt = 0; nt < NTS; ++nt) carry[nt] *= e;
     E *= e;
     state_mma();
+    SSD_TRACE_AGG(5);
+#ifdef SSD_FUSED_TRACE
+    ++ks;
+#endif
   };
   // whole pairs, then an odd last chunk: the loop is only ever re-entered
   // after the second register set's step, so the wait counts at its head are

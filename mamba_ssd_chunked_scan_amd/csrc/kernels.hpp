@@ -87,9 +87,12 @@ struct FusedLaunch {
 // [2] start, [3] carry-in loaded; for chunks k < 4 five stamps [4 + 5k ..
 // 8 + 5k] after its phases A (carry-in to LDS), B (Y_off), C (x and B to
 // LDS), D (state, C.B^T, Y_diag) and E (gate, store); for chunks 4 <= k < 10
-// the end of the chunk at [20 + k]; [slots - 2] end and [slots - 1] the XCD
-// the item ran on.
-constexpr int kFusedTraceSlots = 32;
+// the end of the chunk at [20 + k]; for the aggregate launch's first four
+// chunk steps k, six stamps [32 + 6k .. 37 + 6k]: after its first barrier, the
+// staging of x and B, the issue of the next loads, the second barrier, the
+// decay weights and the products' issue; [slots - 2] end and [slots - 1] the
+// XCD the item ran on.
+constexpr int kFusedTraceSlots = 64;
 
 // Up to four launches: the chunk table / empty sequences (packed mode or no
 // tokens), the range aggregates (more than one range), their carry scan (more

@@ -5,9 +5,9 @@
 
 The profiling library is libssd with -DSSD_FUSED_TRACE: every (unit, range)
 item stores the device's 100 MHz clock (s_memrealtime) at the start and end of
-its range aggregate (first launch), and at the start of the output launch,
-after its carry-in is loaded, after each chunk and at its end, in a region at
-the end of its workspace.  The report gives, over the items of the last of
+its range aggregate (first launch) and inside that launch's first four chunk
+steps, and at the start of the output launch, after its carry-in is loaded,
+after each chunk and at its end, in a region at the end of its workspace.  The report gives, over the items of the last of
 several forwards, the mean and spread of each phase and each launch's span.
 """
 from __future__ import annotations
@@ -18,7 +18,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 TRACE_LIB = os.path.join(HERE, "libssd_trace.so")
-SLOTS = 32          # kFusedTraceSlots
+SLOTS = 64          # kFusedTraceSlots
 TICK_NS = 10.0      # s_memrealtime runs at 100 MHz
 
 
@@ -84,6 +84,19 @@ def main(argv=None):
         print(f"aggregate launch: {has_agg.sum()} items, span {rel(a1.max()):.1f} us; "
               f"item mean {us((a1 - a0).mean()):.1f} max {us((a1 - a0).max()):.1f} us "
               f"({us((a1 - a0).mean()) / R:.2f} us per chunk)")
+        # the aggregate launch's chunk steps (first four): barrier, staging,
+        # load issue, barrier, decay weights, products
+        names = ["barrier", "stage x/B", "issue loads", "barrier", "weights", "products"]
+        ta = tr[has_agg]
+        for k in range(4):
+            prev = ta[:, 0] if k == 0 else ta[:, 32 + 6 * (k - 1) + 5]
+            parts = []
+            for m in range(6):
+                cur = ta[:, 32 + 6 * k + m]
+                parts.append(us(cur - prev).mean())
+                prev = cur
+            print(f"  step {k}: " + "  ".join(f"{n} {v:.2f}" for n, v in zip(names, parts))
+                  + f"  (total {sum(parts):.2f} us)")
     s2, s3, se = tr[:, 2], tr[:, 3], tr[:, SLOTS - 2]
     print(f"output launch: starts {rel(s2.min()):.1f} .. {rel(s2.max()):.1f} us, "
           f"ends {rel(se.min()):.1f} .. {rel(se.max()):.1f} us (span {us(se.max() - s2.min()):.1f})")
