@@ -76,6 +76,24 @@ def test_multi_chunk_ranges():
     check(y, f, ref)
 
 
+# The plan aims at 512 (unit, range) workgroups: 512 units give one range (no
+# aggregate launch), 256 give two (the second range takes the first one's
+# aggregate as it stands, no carry launch) and 160 give three (the carry launch
+# runs).  Six 128-token chunks; packed sequences start and end inside ranges.
+FEW_RANGES = [(512, None), (256, None), (160, None), (512, (100, 200, 90, 300)),
+              (256, (100, 200, 90, 300)), (160, (100, 200, 90, 300)), (160, (700, 0, 10))]
+
+
+@pytest.mark.parametrize("H,seqlens", FEW_RANGES)
+def test_one_two_three_ranges(H, seqlens):
+    w = small_workload(f"r{H}", seqlen=690 if seqlens is None else sum(seqlens), nheads=H,
+                       headdim=16, ngroups=4, dstate=16, chunk_size=128, seqlens=seqlens)
+    inp = with_initial_states(make_inputs(w))
+    ref = oracle_run(inp)
+    y, f = run(inp, w)
+    check(y, f, ref)
+
+
 VARLEN = (300, 0, 1, 127, 128, 129, 1000, 0, 1315)
 
 
