@@ -403,9 +403,10 @@ ssd_status ssd_backward(const ssd_problem* p, const ssd_bwd_args* a, void* works
  * `in_dtype` (AUTO resolves exactly as the call does).  The per-chunk path
  * (FUSED) keeps two fp32 states per chunk and head (the state entering the
  * chunk and its gradient); it takes the heads in passes whose two state
- * buffers hold at most 128 MiB by default: 137 MB at Nemotron-Nano size (8192
- * tokens, 64 heads x 64, d_state 128: two passes of 32 heads) against ~2.2 GB
- * for STAGED. */
+ * buffers hold at most 256 MiB by default: 275 MB at Nemotron-Nano size (8192
+ * tokens, 64 heads x 64, d_state 128: one pass), 342 MB at 65536 tokens x 80
+ * heads (ten passes of 8 heads), against ~2.2 GB for STAGED at Nemotron-Nano
+ * size. */
 ssd_status ssd_backward_ex_workspace_size(const ssd_problem* p, ssd_algo algo,
                                           ssd_dtype in_dtype, size_t* bytes);
 

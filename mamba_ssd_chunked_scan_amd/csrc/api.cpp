@@ -1032,7 +1032,7 @@ BwdChunkWs bwd_chunk_layout(const ssd_problem* p, int hb) {
 // workspace: the largest passes that fit.  Pass sizes: multiples of the heads
 // per group, and below that multiples of eight (one dB/dC workgroup's heads)
 // when they divide a group evenly.
-constexpr size_t kBwdStateBudget = size_t(128) << 20;
+constexpr size_t kBwdStateBudget = size_t(256) << 20;
 
 std::vector<int> pass_sizes(const ssd_problem* p) {
   const int H = p->nheads, hpg = H / p->ngroups, u = ssd::kBwdHeadsPerSplit;
